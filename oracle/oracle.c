@@ -1,0 +1,488 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the fused element-wise two-state
+ * optimizer step (AdamW and AdEMAMix with decoupled weight decay; fp32, BF16
+ * and 8-bit blockwise optimizer states; the update-norm pre-pass).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product links, loads or calls
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header, table or constant generator with the
+ * HIP path; both sides receive the same seeded inputs and nothing else.
+ *
+ * Arithmetic model.  Every + - * / sqrt below is one IEEE binary32 operation,
+ * rounded to nearest-even, with no contraction into fused multiply-add and no
+ * flush of subnormals (build: gcc -O2 -ffp-contract=off -fno-fast-math; on
+ * x86-64 SSE, FLT_EVAL_METHOD is 0).  The pages state the step in fp32 (the
+ * states are fp32 words; "Reading the stored value into FP32 is exact, so new
+ * error only enters when the result is written back", When Small Updates
+ * Disappear, Sec. 1.1), and the integer results that depend on it (quantized
+ * codes, stochastic-rounding bits) must be decided in that same precision.
+ * The bias-correction powers beta^t and the update-norm sums are binary64.
+ *
+ * Sources (page title, then section):
+ *  [PR]  bitsandbytes PR "Fix decoupled weight decay ordering in the CUDA
+ *        Adam/AdEMAMix kernels": intro (decay-first order, AdEMAMix rule
+ *        reference); "Why the current tests do not catch it" (step-1 closed
+ *        form, state zero quantizes exactly, 8-bit blockwise kernel).
+ *  [SU]  "When Small Updates Disappear": Sec. 1.1 (the two EMAs), Sec. 3
+ *        (stochastic rounding), Sec. 6 and 6.1 (the FP32->BF16 bit trick),
+ *        Sec. 7.3 (random number tied to the element).
+ *  [ISS] bitsandbytes fork issue "Investigate SM103 bias-correction broadcast
+ *        in 32-bit optimizers": Problem (bias-correction scalars, max_unorm
+ *        precondition kernel, unorm buffer), Result (the non-deterministic
+ *        atomic unorm sum).
+ *  [GN]  NeMo Automodel PR "perf(training): fused multi-tensor gradient-norm
+ *        reduction": Numerics and Correctness properties (fp64 accumulation,
+ *        NaN poisoning of a max).
+ *
+ * Readings where the pages are silent (each is restated at its use):
+ *  - eps is added to sqrt(v_hat), as in torch.optim.AdamW, which [PR] intro
+ *    says the fixed kernels match;
+ *  - AdEMAMix (Pagliardini et al., cited in [PR] intro): m1 and v are
+ *    bias-corrected, the slow EMA m2 is not; u = (m1_hat + alpha*m2)/(sqrt(v_hat)+eps);
+ *  - 8-bit codes: the nearest codebook entry, ties to the lower index; the
+ *    block absmax is the max |value| over a 256-element block, NaN poisons it
+ *    ([GN] Correctness properties); a zero absmax gives x = 0;
+ *  - stochastic rounding draws r from Philox4x32-10 (Salmon, Moraes, Dror,
+ *    Shaw, SC'11) keyed by the seed, with counter (j>>2, j>>34, t, k);
+ *    the low 16 bits of word j mod 4 round m, the high 16 bits round v.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* public enums and hyper-parameter record (oracle-private definitions) */
+
+enum { ORC_ADAMW = 0, ORC_ADEMAMIX = 1 };
+enum { ORC_F32 = 0, ORC_BF16_RN = 1, ORC_BF16_SR = 2, ORC_Q8 = 3 };
+
+typedef struct {
+    float lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm;
+    int64_t step;         /* t, 1-based                                        */
+    uint64_t seed;        /* Philox key for stochastic rounding                */
+    int64_t index_base;   /* element index j of the first element passed in    */
+    int32_t tensor_index; /* k: the tensor's position in the caller's list     */
+    int32_t decay_after;  /* 0: decay-first (the method).  1: the decay-after
+                             ordering that [PR] removes; a planted mistake that
+                             tests use to show their checks are not vacuous.  */
+} orc_hp;
+
+/* ------------------------------------------------------------------ */
+/* bit views                                                          */
+
+static uint32_t f2u(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float u2f(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+/* A bf16 word is the high half of a binary32 word, so widening is exact. */
+float orc_bf16_to_f32(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+/* ------------------------------------------------------------------ */
+/* BF16 rounding                                                      */
+
+/* Round-to-nearest-even FP32 -> BF16, written from the definition: of the two
+ * BF16 magnitudes that bracket |x| (the truncation toward zero and the next
+ * one up), take the nearer in exact (binary64) arithmetic; on a tie take the
+ * one whose last kept bit is 0.  Above the largest finite BF16 the "next one
+ * up" is infinity, which IEEE rounding treats as the value 2^128.  A NaN stays
+ * a NaN with its sign, made quiet.  ([SU] Sec. 6: the built-in nearest cast.) */
+uint16_t orc_bf16_rne(float x)
+{
+    uint32_t b = f2u(x);
+    uint16_t sign = (uint16_t)((b >> 16) & 0x8000u);
+    if (isnan(x)) return (uint16_t)((b >> 16) | 0x0040u);
+    uint32_t mag = b & 0x7FFFFFFFu;
+    uint16_t lo = (uint16_t)(mag >> 16);           /* |q-| <= |x|            */
+    if ((mag & 0xFFFFu) == 0) return sign | lo;     /* exactly representable  */
+    uint16_t hi = (uint16_t)(lo + 1);               /* |q+| >  |x|            */
+    double a = fabs((double)x);
+    double qlo = (double)orc_bf16_to_f32(lo);
+    double qhi = (hi == 0x7F80u) ? ldexp(1.0, 128) : (double)orc_bf16_to_f32(hi);
+    double dlo = a - qlo, dhi = qhi - a;
+    if (dlo < dhi) return sign | lo;
+    if (dhi < dlo) return sign | hi;
+    return sign | ((lo & 1u) ? hi : lo);
+}
+
+/* Stochastic rounding FP32 -> BF16 with a 16-bit random integer r ([SU]
+ * Sec. 3 and 6.1): l is the integer held by the 16 dropped bits; adding r to
+ * the word carries into the kept bits exactly when l + r >= 2^16, which moves
+ * the magnitude up one BF16 step (away from zero) with probability l/2^16.
+ * Infinities and NaNs are kept as they are (the page's special-value lines are
+ * lost in extraction; reading: use the nearest cast for them).  A finite value
+ * just below the largest float may carry into infinity, as the bit trick does. */
+uint16_t orc_bf16_sr(float x, uint32_t r)
+{
+    uint32_t b = f2u(x);
+    if (!isfinite(x)) return orc_bf16_rne(x);
+    uint32_t l = b & 0xFFFFu;
+    uint16_t kept = (uint16_t)(b >> 16);
+    return (l + (r & 0xFFFFu) >= 0x10000u) ? (uint16_t)(kept + 1) : kept;
+}
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC'11).  State: four 32-bit counter words and a two-word
+ * key.  One round multiplies counter words 0 and 2 by the two Philox
+ * multipliers into 64-bit products, then the new counter is
+ *   (hi(M1*c2) ^ c1 ^ k0,  lo(M1*c2),  hi(M0*c0) ^ c3 ^ k1,  lo(M0*c0));
+ * between rounds the key is bumped by the two Weyl constants (the golden
+ * ratio and sqrt(3)-1 in 32-bit fixed point).  Ten rounds.                 */
+
+#define PHILOX_M0 0xD2511F53u
+#define PHILOX_M1 0xCD9E8D57u
+#define PHILOX_W0 0x9E3779B9u
+#define PHILOX_W1 0xBB67AE85u
+
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) { k0 += PHILOX_W0; k1 += PHILOX_W1; }
+        uint64_t p0 = (uint64_t)PHILOX_M0 * c0;
+        uint64_t p1 = (uint64_t)PHILOX_M1 * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The 32-bit random word for element j of tensor k at step t.  The counter is
+ * tied to the element, not to any launch geometry ([SU] Sec. 7.3): one Philox
+ * block serves four consecutive elements.  `stream` selects the second call
+ * used for AdEMAMix's slow EMA (counter word 3 = k | 2^31).               */
+static uint32_t sr_word(uint64_t seed, int64_t t, int32_t k, int64_t j, int stream)
+{
+    uint32_t ctr[4], key[2], out[4];
+    uint64_t q = (uint64_t)j >> 2;
+    ctr[0] = (uint32_t)q;
+    ctr[1] = (uint32_t)(q >> 32);
+    ctr[2] = (uint32_t)(uint64_t)t;
+    ctr[3] = (uint32_t)k | (stream ? 0x80000000u : 0u);
+    key[0] = (uint32_t)seed;
+    key[1] = (uint32_t)(seed >> 32);
+    orc_philox4x32_10(ctr, key, out);
+    return out[(uint64_t)j & 3u];
+}
+
+/* Exported for tests: the word sr_word() draws. */
+uint32_t orc_sr_word(uint64_t seed, int64_t t, int32_t k, int64_t j, int32_t stream)
+{
+    return sr_word(seed, t, k, j, stream);
+}
+
+/* ------------------------------------------------------------------ */
+/* 8-bit codebook quantization                                        */
+
+/* Code of x against a strictly increasing 256-entry codebook T: the index of
+ * the nearest entry, ties to the lower index.  Written as a count of the
+ * midpoints x lies strictly above; each midpoint is formed in binary64, where
+ * (T[i] + T[i+1]) / 2 is exact for entries of similar size.  NaN lies above
+ * no midpoint and gets code 0.                                            */
+int orc_quantize(const float *T, float x)
+{
+    int code = 0;
+    for (int i = 0; i < 255; ++i) {
+        double mid = ((double)T[i] + (double)T[i + 1]) / 2.0;
+        if ((double)x > mid) ++code;
+    }
+    return code;
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-call scalars ([ISS] Problem: uniform across the whole launch).     */
+
+typedef struct {
+    float om1, om2, om3;   /* 1 - beta                           */
+    float c1, c2;          /* bias corrections 1 - beta^t        */
+    float d;               /* decay factor 1 - lr*wd             */
+    float lam;             /* lr, times the update-norm scale    */
+} scalars_t;
+
+static scalars_t make_scalars(const orc_hp *hp, float scale)
+{
+    scalars_t s;
+    s.om1 = 1.0f - hp->beta1;
+    s.om2 = 1.0f - hp->beta2;
+    s.om3 = 1.0f - hp->beta3;
+    s.c1 = (float)(1.0 - pow((double)hp->beta1, (double)hp->step));
+    s.c2 = (float)(1.0 - pow((double)hp->beta2, (double)hp->step));
+    float lrwd = hp->lr * hp->weight_decay;
+    s.d = 1.0f - lrwd;
+    s.lam = hp->lr * scale;   /* exact when scale is 1 */
+    return s;
+}
+
+/* Exported for tests. */
+void orc_scalars(const orc_hp *hp, float scale, float out[7])
+{
+    scalars_t s = make_scalars(hp, scale);
+    out[0] = s.om1; out[1] = s.om2; out[2] = s.om3;
+    out[3] = s.c1; out[4] = s.c2; out[5] = s.d; out[6] = s.lam;
+}
+
+/* ------------------------------------------------------------------ */
+/* One element.  Inputs are the fp32 values read from storage (exact for
+ * fp32 and BF16 storage; T[code]*absmax for 8-bit storage).              */
+
+typedef struct { float m, v, m2, u; } moments_t;
+
+static moments_t moments_and_direction(int opt, const orc_hp *hp, const scalars_t *s,
+                                       float g, float m, float v, float m2)
+{
+    moments_t r;
+    /* EMAs ([SU] Sec. 1.1):  m' = b1 m + (1-b1) g,  v' = b2 v + (1-b2) g^2,
+     * AdEMAMix adds the slow EMA m2' = b3 m2 + (1-b3) g.  g^2 is formed in
+     * fp32 from the widened gradient. */
+    float gg = g * g;
+    r.m = hp->beta1 * m + s->om1 * g;
+    r.v = hp->beta2 * v + s->om2 * gg;
+    r.m2 = 0.0f;
+    /* Bias-corrected direction; eps added to sqrt(v_hat) (reading above). */
+    float mh = r.m / s->c1;
+    float vh = r.v / s->c2;
+    float den = sqrtf(vh) + hp->eps;
+    if (opt == ORC_ADEMAMIX) {
+        r.m2 = hp->beta3 * m2 + s->om3 * g;
+        float num = mh + hp->alpha * r.m2;
+        r.u = num / den;
+    } else {
+        r.u = mh / den;
+    }
+    return r;
+}
+
+/* Decoupled weight decay.  Decay-first ([PR] intro): both the decay and the
+ * update are taken from the previous p,  p' = p (1 - lr wd) - lr u.
+ * Decay-after, the ordering the PR removes:  p' = (p - lr u)(1 - lr wd).  */
+static float apply_update(const orc_hp *hp, const scalars_t *s, float p, float u)
+{
+    float step = s->lam * u;
+    if (hp->decay_after) {
+        float q = p - step;
+        return q * s->d;
+    }
+    float decayed = p * s->d;
+    return decayed - step;
+}
+
+/* ------------------------------------------------------------------ */
+/* Whole-tensor steps.  Arrays hold n elements; g is the gradient widened to
+ * fp32.  `scale` is the update-norm scale s_k (1.0f when max_unorm is off).  */
+
+static int step_f32(int opt, const orc_hp *hp, float scale, int64_t n,
+                    float *p, const float *g, float *m, float *v, float *m2)
+{
+    scalars_t s = make_scalars(hp, scale);
+    for (int64_t j = 0; j < n; ++j) {
+        moments_t r = moments_and_direction(opt, hp, &s, g[j], m[j], v[j],
+                                            opt == ORC_ADEMAMIX ? m2[j] : 0.0f);
+        p[j] = apply_update(hp, &s, p[j], r.u);
+        m[j] = r.m;
+        v[j] = r.v;
+        if (opt == ORC_ADEMAMIX) m2[j] = r.m2;
+    }
+    return 0;
+}
+
+static int step_bf16(int opt, int stochastic, const orc_hp *hp, float scale, int64_t n,
+                     float *p, const float *g, uint16_t *m, uint16_t *v, uint16_t *m2)
+{
+    scalars_t s = make_scalars(hp, scale);
+    for (int64_t j = 0; j < n; ++j) {
+        float m_old = orc_bf16_to_f32(m[j]);
+        float v_old = orc_bf16_to_f32(v[j]);
+        float m2_old = (opt == ORC_ADEMAMIX) ? orc_bf16_to_f32(m2[j]) : 0.0f;
+        moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
+        /* The parameter update uses the unrounded fp32 moments; rounding
+         * happens only at write-back ([SU] Sec. 1.1). */
+        p[j] = apply_update(hp, &s, p[j], r.u);
+        if (stochastic) {
+            int64_t jj = hp->index_base + j;
+            uint32_t w = sr_word(hp->seed, hp->step, hp->tensor_index, jj, 0);
+            m[j] = orc_bf16_sr(r.m, w & 0xFFFFu);
+            v[j] = orc_bf16_sr(r.v, w >> 16);
+            if (opt == ORC_ADEMAMIX) {
+                uint32_t w2 = sr_word(hp->seed, hp->step, hp->tensor_index, jj, 1);
+                m2[j] = orc_bf16_sr(r.m2, w2 & 0xFFFFu);
+            }
+        } else {
+            m[j] = orc_bf16_rne(r.m);
+            v[j] = orc_bf16_rne(r.v);
+            if (opt == ORC_ADEMAMIX) m2[j] = orc_bf16_rne(r.m2);
+        }
+    }
+    return 0;
+}
+
+/* Largest |x| over a block; any NaN makes it NaN ([GN] Correctness
+ * properties: a maximum must not silently skip NaNs). */
+static float block_absmax(const float *x, int64_t len)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < len; ++i) {
+        if (isnan(x[i])) return NAN;
+        float ax = fabsf(x[i]);
+        if (ax > a) a = ax;
+    }
+    return a;
+}
+
+static void quantize_block(const float *T, const float *x, int64_t len, float amax, uint8_t *codes)
+{
+    for (int64_t i = 0; i < len; ++i) {
+        float q = (amax == 0.0f) ? 0.0f : x[i] / amax;
+        codes[i] = (uint8_t)orc_quantize(T, q);
+    }
+}
+
+#define Q8_BLOCK 256
+
+/* 8-bit blockwise states ([PR] intro: the 2-state branch of the blockwise
+ * 8-bit kernel; "Why the current tests do not catch it": a zero state
+ * quantizes exactly).  Blocks are 256 consecutive elements from element 0 of
+ * the tensor; the last block may be short.  m and m2 use the signed codebook
+ * qs, v the unsigned codebook qu; each state has its own absmax per block.
+ * A stored state reads back as T[code] * absmax.                          */
+static int step_q8(int opt, const orc_hp *hp, float scale, int64_t n,
+                   float *p, const float *g, uint8_t *c1, uint8_t *c2, uint8_t *c3,
+                   float *a1, float *a2, float *a3, const float *qs, const float *qu)
+{
+    scalars_t s = make_scalars(hp, scale);
+    float bm[Q8_BLOCK], bv[Q8_BLOCK], bm2[Q8_BLOCK];
+    for (int64_t b0 = 0, blk = 0; b0 < n; b0 += Q8_BLOCK, ++blk) {
+        int64_t len = (n - b0 < Q8_BLOCK) ? n - b0 : Q8_BLOCK;
+        for (int64_t i = 0; i < len; ++i) {
+            int64_t j = b0 + i;
+            float m_old = qs[c1[j]] * a1[blk];
+            float v_old = qu[c2[j]] * a2[blk];
+            float m2_old = (opt == ORC_ADEMAMIX) ? qs[c3[j]] * a3[blk] : 0.0f;
+            moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
+            p[j] = apply_update(hp, &s, p[j], r.u);
+            bm[i] = r.m; bv[i] = r.v; bm2[i] = r.m2;
+        }
+        float am = block_absmax(bm, len);
+        float av = block_absmax(bv, len);
+        quantize_block(qs, bm, len, am, c1 + b0);
+        quantize_block(qu, bv, len, av, c2 + b0);
+        a1[blk] = am;
+        a2[blk] = av;
+        if (opt == ORC_ADEMAMIX) {
+            float am2 = block_absmax(bm2, len);
+            quantize_block(qs, bm2, len, am2, c3 + b0);
+            a3[blk] = am2;
+        }
+    }
+    return 0;
+}
+
+/* One optimizer step over one tensor.  s1/s2/s3 are m (m1 for AdEMAMix), v,
+ * and m2, in the storage of `fmt`: float*, uint16_t* (BF16 bits) or uint8_t*
+ * (codes).  Returns 0, or -1 for an unknown optimizer or format.          */
+int orc_step(int opt, int fmt, const orc_hp *hp, float scale, int64_t n,
+             float *p, const float *g, void *s1, void *s2, void *s3,
+             float *a1, float *a2, float *a3, const float *qs, const float *qu)
+{
+    if (opt != ORC_ADAMW && opt != ORC_ADEMAMIX) return -1;
+    switch (fmt) {
+    case ORC_F32:
+        return step_f32(opt, hp, scale, n, p, g, (float *)s1, (float *)s2, (float *)s3);
+    case ORC_BF16_RN:
+        return step_bf16(opt, 0, hp, scale, n, p, g, (uint16_t *)s1, (uint16_t *)s2, (uint16_t *)s3);
+    case ORC_BF16_SR:
+        return step_bf16(opt, 1, hp, scale, n, p, g, (uint16_t *)s1, (uint16_t *)s2, (uint16_t *)s3);
+    case ORC_Q8:
+        return step_q8(opt, hp, scale, n, p, g, (uint8_t *)s1, (uint8_t *)s2, (uint8_t *)s3,
+                       a1, a2, a3, qs, qu);
+    }
+    return -1;
+}
+
+/* ------------------------------------------------------------------ */
+/* Update-norm pre-pass ([ISS] Problem: the precondition kernel used when
+ * max_unorm > 0 recomputes the would-be update and accumulates its norm).
+ * U2 = sum_j u_j^2 and P2 = sum_j p_j^2 for one tensor, with u the direction
+ * of the step (no lr, no decay) and p the parameter before the step, summed
+ * in element order in binary64 with Neumaier's compensation.             */
+
+typedef struct { double s, c; } nsum_t;
+
+static void nsum_add(nsum_t *a, double x)
+{
+    double t = a->s + x;
+    if (fabs(a->s) >= fabs(x)) a->c += (a->s - t) + x;
+    else a->c += (x - t) + a->s;
+    a->s = t;
+}
+
+int orc_unorm(int opt, int fmt, const orc_hp *hp, int64_t n, const float *p, const float *g,
+              const void *s1, const void *s2, const void *s3,
+              const float *a1, const float *a2, const float *a3,
+              const float *qs, const float *qu, double out[2])
+{
+    if (opt != ORC_ADAMW && opt != ORC_ADEMAMIX) return -1;
+    if (fmt < ORC_F32 || fmt > ORC_Q8) return -1;
+    scalars_t s = make_scalars(hp, 1.0f);
+    nsum_t su = {0.0, 0.0}, sp = {0.0, 0.0};
+    for (int64_t j = 0; j < n; ++j) {
+        float m, v, m2 = 0.0f;
+        if (fmt == ORC_F32) {
+            m = ((const float *)s1)[j];
+            v = ((const float *)s2)[j];
+            if (opt == ORC_ADEMAMIX) m2 = ((const float *)s3)[j];
+        } else if (fmt == ORC_Q8) {
+            int64_t blk = j / Q8_BLOCK;
+            m = qs[((const uint8_t *)s1)[j]] * a1[blk];
+            v = qu[((const uint8_t *)s2)[j]] * a2[blk];
+            if (opt == ORC_ADEMAMIX) m2 = qs[((const uint8_t *)s3)[j]] * a3[blk];
+        } else {
+            m = orc_bf16_to_f32(((const uint16_t *)s1)[j]);
+            v = orc_bf16_to_f32(((const uint16_t *)s2)[j]);
+            if (opt == ORC_ADEMAMIX) m2 = orc_bf16_to_f32(((const uint16_t *)s3)[j]);
+        }
+        moments_t r = moments_and_direction(opt, hp, &s, g[j], m, v, m2);
+        nsum_add(&su, (double)r.u * (double)r.u);
+        nsum_add(&sp, (double)p[j] * (double)p[j]);
+    }
+    out[0] = su.s + su.c;
+    out[1] = sp.s + sp.c;
+    return 0;
+}
+
+/* The update-norm scale: min(1, max_unorm * ||p|| / ||u||), rounded to fp32;
+ * 1 when max_unorm <= 0 (the precondition pass runs only when max_unorm > 0,
+ * [ISS] Problem) or when ||u|| does not exceed the bound.               */
+float orc_unorm_scale(float max_unorm, double u2, double p2)
+{
+    if (!(max_unorm > 0.0f)) return 1.0f;
+    double un = sqrt(u2), bound = (double)max_unorm * sqrt(p2);
+    if (un > bound) return (float)(bound / un);
+    return 1.0f;
+}
+
+/* ------------------------------------------------------------------ */
+/* Array forms of the element functions above, for exhaustive tests.    */
+
+void orc_bf16_rne_array(const float *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_rne(x[i]);
+}
+
+void orc_bf16_sr_array(const float *x, const uint32_t *r, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_sr(x[i], r[i]);
+}
+
+void orc_quantize_array(const float *T, const float *x, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_quantize(T, x[i]);
+}
+
+void orc_sr_words(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, int32_t stream,
+                  uint32_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = sr_word(seed, t, k, j0 + i, stream);
+}
