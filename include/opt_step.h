@@ -1,0 +1,201 @@
+/*
+ * opt_step.h -- C ABI of the MI355X (gfx950) fused element-wise two-state
+ * optimizer step: AdamW and AdEMAMix with decoupled weight decay applied in
+ * the decay-first order, optimizer states stored as fp32, BF16 (nearest or
+ * stochastic rounding) or 8-bit blockwise codes, and a deterministic
+ * update-norm pre-pass for max_unorm.
+ *
+ * The operation (sources are the four pages this library is built from):
+ *  - decay-first AdamW, p' = p*(1 - lr*wd) - lr*u with u = m_hat/(sqrt(v_hat)+eps):
+ *    bitsandbytes PR "Fix decoupled weight decay ordering in the CUDA
+ *    Adam/AdEMAMix kernels", intro (both terms from the same previous p);
+ *  - AdEMAMix (the rule that PR cites): a slow EMA m2 with beta3, mixed into
+ *    the numerator with alpha, u = (m1_hat + alpha*m2)/(sqrt(v_hat)+eps);
+ *  - the EMAs m' = b1*m + (1-b1)*g, v' = b2*v + (1-b2)*g^2 and BF16 storage
+ *    with nearest or stochastic rounding: "When Small Updates Disappear",
+ *    Sec. 1.1, 3, 6.1 and 8.1 (the fused step with BF16 moments);
+ *  - 8-bit blockwise states, one absmax per 256-element block: the blockwise
+ *    8-bit kernel of the bitsandbytes PR;
+ *  - the max_unorm precondition pass and its per-tensor norm buffer: issue
+ *    "Investigate SM103 bias-correction broadcast in 32-bit optimizers",
+ *    Problem and Result (here without atomics, so bit-reproducible).
+ *
+ * Arithmetic.  Each element's moments are formed in binary32 in the fixed
+ * order m' = fl(fl(b1*m) + fl((1-b1)*g)), v' = fl(fl(b2*v) + fl((1-b2)*fl(g*g))),
+ * m2' = fl(fl(b3*m2) + fl((1-b3)*g)), with no fused multiply-add, so BF16 and
+ * 8-bit results are bit-reproducible.  The update uses these unrounded fp32
+ * moments; rounding or quantization happens only when they are stored.
+ * Bias corrections c = 1 - beta^t are formed in binary64 and rounded once.
+ *
+ * Calls and memory.  Every call is asynchronous on `stream` (a hipStream_t
+ * passed as void*; NULL is the null stream).  All tensors, states and the
+ * unorm buffer are caller-owned device memory; the library keeps no pointer
+ * after a call returns.  The library owns a small per-device workspace
+ * (tensor tables, codebook search tables, norm partials) that it grows on
+ * demand and releases in opt_shutdown.  Calls from several host threads are
+ * serialized inside the library.
+ *
+ * Errors.  Every entry point returns OPT_OK (0) or a negative status and, on
+ * error, enqueues nothing; opt_last_error() then describes the failure.
+ */
+#ifndef OPT_STEP_H
+#define OPT_STEP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define OPT_OK            0
+#define OPT_EINVAL       (-1)  /* null pointer, negative size, step < 1, bad enum, bad codebook */
+#define OPT_EUNSUPPORTED (-2)  /* a dtype / format / optimizer combination not provided        */
+#define OPT_EALIGN       (-3)  /* a device pointer not aligned as required (see opt_tensor)    */
+#define OPT_EHIP         (-4)  /* a HIP runtime error; its text is in opt_last_error()         */
+
+/* ---- enumerations -------------------------------------------------------- */
+typedef enum { OPT_F32 = 0, OPT_BF16 = 1 } opt_dtype;
+
+typedef enum {
+    OPT_STATE_F32 = 0,      /* fp32 words                                          */
+    OPT_STATE_BF16_RN = 1,  /* BF16 words, round to nearest even on store          */
+    OPT_STATE_BF16_SR = 2,  /* BF16 words, stochastic rounding with Philox4x32-10  */
+    OPT_STATE_Q8 = 3        /* 8-bit codes + one fp32 absmax per 256 elements      */
+} opt_state_fmt;
+
+typedef enum { OPT_ADAMW = 0, OPT_ADEMAMIX = 1 } opt_optimizer;
+
+/* ---- one tensor of the multi-tensor list --------------------------------
+ * All pointers are device pointers owned by the caller.
+ *   p        numel fp32 parameters, read and written (p_dtype must be OPT_F32).
+ *   g        numel gradients in g_dtype, read.
+ *   s1       first moment m (AdamW) or fast EMA m1 (AdEMAMix), read and written.
+ *   s2       second moment v, read and written.
+ *   s3       AdEMAMix's slow EMA m2, read and written; NULL for AdamW.
+ *            State storage: OPT_STATE_F32 -> float[numel]; BF16 formats ->
+ *            uint16_t[numel] BF16 words; OPT_STATE_Q8 -> uint8_t[numel] codes.
+ *   absmax1..3  OPT_STATE_Q8 only: float[ceil(numel/256)] per-block absmax of
+ *            s1..s3; NULL otherwise.  Blocks are 256 consecutive elements from
+ *            element 0 of the tensor; the last block may be short.
+ *   numel    element count, >= 0 (0 is a no-op).
+ * Alignment: p, g, s1, s2, s3 must be 16-byte aligned (any PyTorch allocation
+ * is); absmax arrays 4-byte aligned.  Buffers of different tensors must not
+ * overlap.  The tensor's position k in the list keys its stochastic rounding.
+ * A fresh 8-bit state is every code set to the code of 0 (127 for a signed
+ * table whose entry 127 is 0, 0 for an unsigned table) and absmax 0.
+ */
+typedef struct {
+    void *p;
+    const void *g;
+    void *s1, *s2, *s3;
+    float *absmax1, *absmax2, *absmax3;
+    int64_t numel;
+    int32_t p_dtype;
+    int32_t g_dtype;
+} opt_tensor;
+
+/* ---- hyper-parameters -----------------------------------------------------
+ *   lr, weight_decay   decay-first: p' = p*(1 - lr*wd) - lr*s_k*u.
+ *   beta1, beta2, eps  AdamW moments, 0 <= beta < 1; eps is added to sqrt(v_hat).
+ *   beta3, alpha       AdEMAMix slow EMA (0 <= beta3 <= 1) and its mixing
+ *                      weight (both ignored by AdamW).
+ *   max_unorm          > 0: scale the update of tensor k by
+ *                      s_k = min(1, max_unorm*||p_k|| / ||u_k||), from the norms
+ *                      opt_precondition_unorm wrote; <= 0: off (s_k = 1).
+ *   step               t >= 1; the bias corrections are 1 - beta1^t, 1 - beta2^t.
+ *   seed               Philox key for OPT_STATE_BF16_SR: element j of tensor k
+ *                      at step t draws word j%4 of Philox4x32-10 with counter
+ *                      (j>>2 low, j>>34, t, k) [k | 2^31 for m2]; the low 16 bits
+ *                      round m (and m2), the high 16 bits round v.
+ *   qmap_signed        OPT_STATE_Q8 only: HOST pointer to 256 floats, strictly
+ *                      increasing, finite, within [-1, 1]; codebook of m and m2.
+ *   qmap_unsigned      OPT_STATE_Q8 only: HOST pointer to 256 floats as above,
+ *                      all >= 0; codebook of v.  The library copies both during
+ *                      the call.  A code is the index of the nearest entry to
+ *                      x = m'/absmax (ties to the lower index; NaN -> 0).
+ */
+typedef struct {
+    float lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm;
+    int64_t step;
+    uint64_t seed;
+    const float *qmap_signed;
+    const float *qmap_unsigned;
+} opt_hparams;
+
+/* One AdamW step over the n tensors of `tensors` (host array, read during the
+ * call only).  Tensors are grouped by gradient dtype and each group runs as
+ * one kernel launch over a host-built chunk table.
+ * unorm: device double[2*n] written by opt_precondition_unorm with the same
+ * tensors, format and hyper-parameters, on the same stream, before this call;
+ * required when hp->max_unorm > 0 and ignored otherwise. */
+int opt_step_adamw(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
+                   const opt_hparams *hp, const double *unorm, void *stream);
+
+/* One AdEMAMix step; arguments as opt_step_adamw, with s3 (and absmax3 for
+ * OPT_STATE_Q8) required for every tensor. */
+int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
+                      const opt_hparams *hp, const double *unorm, void *stream);
+
+/* The max_unorm pre-pass: for each tensor k, recompute the direction u of the
+ * coming step (no lr, no decay) from p, g and the states without writing them,
+ * and store unorm_out[2k] = sum u^2 and unorm_out[2k+1] = sum p^2, in binary64.
+ * Deterministic: per-chunk partials reduced in a fixed order, no atomics, so
+ * repeated calls give the same bits.  unorm_out is device double[2*n]. */
+int opt_precondition_unorm(int32_t optimizer, const opt_tensor *tensors, int64_t n,
+                           int32_t state_fmt, const opt_hparams *hp, double *unorm_out,
+                           void *stream);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char *opt_last_error(void);
+
+/* Wait for the library's outstanding work and free its workspace on every
+ * device.  Later calls re-create it. */
+int opt_shutdown(void);
+
+/* ---- test hooks (the same device functions the step kernels use) -------- */
+
+/* out[i] = Philox4x32-10 word (j0+i) % 4 of the block with counter
+ * ((j0+i)>>2 low, (j0+i)>>34, t, k) and key (seed low, seed high), for
+ * i < count.  out is device uint32_t[count]. */
+int opt_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t count,
+                     uint32_t *out, void *stream);
+
+/* out[i] = BF16 word of x[i]: round to nearest even if r is NULL, else
+ * stochastic rounding with the 16-bit integer r[i] & 0xFFFF.  Device arrays. */
+int opt_debug_round_bf16(const float *x, const uint32_t *r, uint16_t *out, int64_t n,
+                         void *stream);
+
+/* out[i] = code of x[i] against the host codebook qmap (256 floats, as
+ * qmap_signed; pass is_signed = 0 for a table of non-negative entries, which
+ * must hold 0 <= x <= 1), using the lookup tables the 8-bit step builds.
+ * x and out are device arrays of n entries. */
+int opt_debug_quantize(const float *qmap, int32_t is_signed, const float *x, uint8_t *out,
+                       int64_t n, void *stream);
+
+/* Host only, no device work: the number of chunks the planner gives each
+ * tensor of `numels` (n entries) at the library's chunk size, written to
+ * chunks_out[n]; returns the chunk size in elements, or a negative status. */
+int64_t opt_debug_plan(const int64_t *numels, int64_t n, int64_t *chunks_out);
+
+/* Host only: the lookup of opt_debug_quantize run on the CPU over host arrays
+ * (the same table builder and lookup source).  x[i] must be NaN or in [-1, 1]
+ * (OPT_EINVAL otherwise). */
+int opt_debug_quantize_host(const float *qmap, int32_t is_signed, const float *x, uint8_t *out,
+                            int64_t n);
+
+/* Host only: out[i] = a[i] / b[i] by the kernels' division with a reused
+ * reciprocal (two residual corrections of a[i] * RN(1/b[i])), on the CPU.
+ * Each b[i] must have |b|, 1/|b| in [2^-124, 2^124] (OPT_EINVAL otherwise). */
+int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n);
+
+/* Launch geometry for all later calls in this process: elements per chunk (a
+ * positive multiple of 1024) and persistent workgroups per compute unit
+ * (1..64).  Results do not depend on either. */
+int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPT_STEP_H */

@@ -1,0 +1,243 @@
+"""Python binding of the MI355X fused optimizer-step library (libopt_step.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/opt_step.h``; PyTorch supplies
+device memory and streams.  Function names match the C entry points.  If the
+library has not been built, every call raises (there is no other code path).
+
+Tensors are passed as a list of dicts with torch CUDA tensors under the keys
+``p``, ``g``, ``s1``, ``s2`` and, as the format and optimizer need, ``s3``,
+``absmax1``, ``absmax2``, ``absmax3`` (see ``opt_tensor`` in the header).
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libopt_step.so")
+
+OPT_OK, OPT_EINVAL, OPT_EUNSUPPORTED, OPT_EALIGN, OPT_EHIP = 0, -1, -2, -3, -4
+OPT_F32, OPT_BF16 = 0, 1
+STATE_F32, STATE_BF16_RN, STATE_BF16_SR, STATE_Q8 = 0, 1, 2, 3
+ADAMW, ADEMAMIX = 0, 1
+FORMATS = {"f32": STATE_F32, "bf16_rn": STATE_BF16_RN, "bf16_sr": STATE_BF16_SR, "q8": STATE_Q8}
+OPTIMIZERS = {"adamw": ADAMW, "ademamix": ADEMAMIX}
+BLOCK = 256
+
+
+class OptError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class OptTensor(ctypes.Structure):
+    _fields_ = [
+        ("p", ctypes.c_void_p), ("g", ctypes.c_void_p),
+        ("s1", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("s3", ctypes.c_void_p),
+        ("absmax1", ctypes.c_void_p), ("absmax2", ctypes.c_void_p), ("absmax3", ctypes.c_void_p),
+        ("numel", ctypes.c_int64), ("p_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32),
+    ]
+
+
+class OptHparams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+        ("beta3", ctypes.c_float), ("alpha", ctypes.c_float), ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float), ("max_unorm", ctypes.c_float),
+        ("step", ctypes.c_int64), ("seed", ctypes.c_uint64),
+        ("qmap_signed", ctypes.c_void_p), ("qmap_unsigned", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with optimizer_step_amd/build.py "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        T = ctypes.POINTER(OptTensor)
+        H = ctypes.POINTER(OptHparams)
+        sig = {
+            "opt_step_adamw": ([T, i64, i32, H, vp, vp], i32),
+            "opt_step_ademamix": ([T, i64, i32, H, vp, vp], i32),
+            "opt_precondition_unorm": ([i32, T, i64, i32, H, vp, vp], i32),
+            "opt_last_error": ([], ctypes.c_char_p),
+            "opt_shutdown": ([], i32),
+            "opt_debug_philox": ([ctypes.c_uint64, i64, i32, i64, i64, vp, vp], i32),
+            "opt_debug_round_bf16": ([vp, vp, vp, i64, vp], i32),
+            "opt_debug_quantize": ([vp, i32, vp, vp, i64, vp], i32),
+            "opt_debug_plan": ([vp, i64, vp], i64),
+            "opt_debug_quantize_host": ([vp, i32, vp, vp, i64], i32),
+            "opt_debug_div_by": ([vp, vp, vp, i64], i32),
+            "opt_debug_set_launch": ([i64, i32], i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != OPT_OK:
+        raise OptError(status, lib().opt_last_error().decode())
+    return status
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return OPT_F32
+    if t.dtype == torch.bfloat16:
+        return OPT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class TensorList:
+    """The C array of opt_tensor for a list of tensor dicts; build it once and
+    pass it to every step when the buffers do not change."""
+
+    def __init__(self, tensors):
+        self.keep = list(tensors)
+        self.arr = (OptTensor * max(1, len(self.keep)))()
+        for i, d in enumerate(self.keep):
+            p = d["p"]
+            self.arr[i] = OptTensor(
+                _ptr(p), _ptr(d["g"]), _ptr(d.get("s1")), _ptr(d.get("s2")), _ptr(d.get("s3")),
+                _ptr(d.get("absmax1")), _ptr(d.get("absmax2")), _ptr(d.get("absmax3")),
+                p.numel(), _dtype_code(p), _dtype_code(d["g"]))
+        self.n = len(self.keep)
+
+
+def _as_list(tensors):
+    return tensors if isinstance(tensors, TensorList) else TensorList(tensors)
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
+            weight_decay=0.0, max_unorm=0.0, step=1, seed=0, qmap_signed=None, qmap_unsigned=None):
+    """An OptHparams record.  qmap_* are host float32 arrays (numpy or CPU
+    torch tensors) of 256 entries; they are referenced, not copied, so keep
+    them alive for the call."""
+    h = OptHparams(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
+                   int(step), int(seed) & (2**64 - 1), None, None)
+    for field, q in (("qmap_signed", qmap_signed), ("qmap_unsigned", qmap_unsigned)):
+        if q is not None:
+            addr = q.ctypes.data if hasattr(q, "ctypes") else q.data_ptr()
+            setattr(h, field, addr)
+    h._keep = (qmap_signed, qmap_unsigned)
+    return h
+
+
+def opt_step_adamw(tensors, state_fmt, hp, unorm=None, stream=None):
+    tl = _as_list(tensors)
+    return _check(lib().opt_step_adamw(tl.arr, tl.n, FORMATS.get(state_fmt, state_fmt),
+                                       ctypes.byref(hp), _ptr(unorm), _stream(stream)))
+
+
+def opt_step_ademamix(tensors, state_fmt, hp, unorm=None, stream=None):
+    tl = _as_list(tensors)
+    return _check(lib().opt_step_ademamix(tl.arr, tl.n, FORMATS.get(state_fmt, state_fmt),
+                                          ctypes.byref(hp), _ptr(unorm), _stream(stream)))
+
+
+def opt_precondition_unorm(optimizer, tensors, state_fmt, hp, unorm_out, stream=None):
+    tl = _as_list(tensors)
+    return _check(lib().opt_precondition_unorm(OPTIMIZERS.get(optimizer, optimizer), tl.arr, tl.n,
+                                               FORMATS.get(state_fmt, state_fmt), ctypes.byref(hp),
+                                               _ptr(unorm_out), _stream(stream)))
+
+
+def opt_last_error():
+    return lib().opt_last_error().decode()
+
+
+def opt_shutdown():
+    return _check(lib().opt_shutdown())
+
+
+def opt_debug_philox(seed, t, k, j0, out, stream=None):
+    return _check(lib().opt_debug_philox(int(seed) & (2**64 - 1), t, k, j0, out.numel(), _ptr(out),
+                                         _stream(stream)))
+
+
+def opt_debug_round_bf16(x, r, out, stream=None):
+    return _check(lib().opt_debug_round_bf16(_ptr(x), _ptr(r), _ptr(out), x.numel(), _stream(stream)))
+
+
+def opt_debug_quantize(qmap, is_signed, x, out, stream=None):
+    return _check(lib().opt_debug_quantize(qmap.ctypes.data, int(is_signed), _ptr(x), _ptr(out),
+                                           x.numel(), _stream(stream)))
+
+
+def opt_debug_plan(numels):
+    import numpy as np
+    a = np.ascontiguousarray(numels, dtype=np.int64)
+    out = np.zeros(a.size, dtype=np.int64)
+    chunk = lib().opt_debug_plan(a.ctypes.data, a.size, out.ctypes.data)
+    if chunk < 0:
+        _check(int(chunk))
+    return int(chunk), out
+
+
+def opt_debug_quantize_host(qmap, is_signed, x):
+    import numpy as np
+    q = np.ascontiguousarray(qmap, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.size, dtype=np.uint8)
+    _check(lib().opt_debug_quantize_host(q.ctypes.data, int(is_signed), x.ctypes.data, out.ctypes.data,
+                                         x.size))
+    return out
+
+
+def opt_debug_div_by(a, b):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    out = np.zeros(a.size, dtype=np.float32)
+    _check(lib().opt_debug_div_by(a.ctypes.data, b.ctypes.data, out.ctypes.data, a.size))
+    return out
+
+
+def opt_debug_set_launch(chunk, wgs_per_cu):
+    return _check(lib().opt_debug_set_launch(int(chunk), int(wgs_per_cu)))
+
+
+def state_buffers(fmt, numel, optimizer="adamw", device="cuda", qmap_signed=None, qmap_unsigned=None):
+    """Fresh (zero) optimizer state on the device for one tensor, as a dict of
+    s1, s2[, s3][, absmax1, absmax2[, absmax3]].  8-bit codes start at the
+    code of 0 in each codebook (the index of its 0 entry) with absmax 0."""
+    import torch
+    import numpy as np
+    fmt = FORMATS.get(fmt, fmt)
+    nst = 3 if OPTIMIZERS.get(optimizer, optimizer) == ADEMAMIX else 2
+    out = {}
+    if fmt == STATE_Q8:
+        nb = (numel + BLOCK - 1) // BLOCK
+        zs = int(np.argmin(np.abs(np.asarray(qmap_signed, dtype=np.float64))))
+        zu = int(np.argmin(np.abs(np.asarray(qmap_unsigned, dtype=np.float64))))
+        for i in range(1, nst + 1):
+            out[f"s{i}"] = torch.full((numel,), zu if i == 2 else zs, dtype=torch.uint8, device=device)
+            out[f"absmax{i}"] = torch.zeros(nb, dtype=torch.float32, device=device)
+    else:
+        dt = torch.float32 if fmt == STATE_F32 else torch.bfloat16
+        for i in range(1, nst + 1):
+            out[f"s{i}"] = torch.zeros(numel, dtype=dt, device=device)
+    return out

@@ -1,0 +1,56 @@
+"""Build the HIP library libopt_step.so for gfx950, in-tree.
+
+hipcc flags: -O3, no FMA contraction (-ffp-contract=off) so the binary32
+recipe runs in the written order, packed-fp32 instructions disabled, and the
+default correctly rounded fp32 division and square root.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libopt_step.so")
+SOURCES = ["opt_api.cpp", "opt_kernels.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    "-I", CSRC, "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc():
+    return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def build(verbose=False, out=LIB, extra_flags=()):
+    tmpdir = tempfile.mkdtemp(prefix="optstep_build_")
+    try:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            lang = ["-x", "hip"]
+            cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            objs.append(obj)
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,648 @@
+// opt_api.cpp -- the C ABI declared in include/opt_step.h: argument checks,
+// dtype bucketing, the host-built chunk table, the per-device workspace, and
+// the 8-bit codebook lookup tables.  Device work is in opt_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "opt_device.h"
+#include "opt_step.h"
+
+namespace optstep {
+
+hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st);
+hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds, int ntens,
+                        double *out, hipStream_t st);
+hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, uint32_t *out,
+                               hipStream_t st);
+hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, int64_t n, hipStream_t st);
+hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, uint8_t *out, int64_t n,
+                                 hipStream_t st);
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(OPT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// launch configuration
+
+int64_t g_chunk = 32768;      // elements per chunk; multiple of 1024
+int g_wgs_per_cu = 8;         // persistent grid size per compute unit
+
+constexpr int kMaxDevices = 64;
+constexpr int kSlots = 16;
+constexpr uint32_t kMaxSearchWords = 15000;   // LDS budget of the search tables
+
+// ---------------------------------------------------------------------------
+// 8-bit codebook lookup tables
+
+struct BuiltTable {
+    std::vector<uint32_t> entries;
+    QTabParams P{};
+};
+
+static uint32_t fb(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float bf(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+// The code of x is the number of midpoints t_i = (T_i + T_{i+1})/2 (formed in
+// binary64) that x lies strictly above, i.e. the count of tau_i <= x with
+// tau_i the smallest float above t_i: the nearest entry, ties to the lower
+// index.  The table splits [lo, 1] into buckets of 2^shift ulps (one sign at
+// a time) holding at most one tau each, so one comparison finishes the code.
+int build_search(const float *T, bool is_signed, BuiltTable &out)
+{
+    for (int i = 0; i < 256; ++i) {
+        if (!std::isfinite(T[i]) || T[i] < -1.0f || T[i] > 1.0f)
+            return fail(OPT_EINVAL, "codebook entry %d (%g) is not a finite value in [-1, 1]", i, T[i]);
+        if (i > 0 && !(T[i] > T[i - 1]))
+            return fail(OPT_EINVAL, "codebook is not strictly increasing at entry %d", i);
+    }
+    if (!is_signed && T[0] < 0.0f) return fail(OPT_EINVAL, "unsigned codebook has a negative entry");
+    float tau[255];
+    float minmag = INFINITY;
+    for (int i = 0; i < 255; ++i) {
+        double t = ((double)T[i] + (double)T[i + 1]) / 2.0;
+        float f = (float)t;
+        if ((double)f <= t) f = nextafterf(f, INFINITY);
+        tau[i] = f;
+        // a midpoint of exactly 0 gives tau = the smallest positive float; the
+        // lookup sends +0 to the x < 0 half, so only the others bound lo
+        if (t != 0.0) minmag = std::min(minmag, std::fabs(f));
+    }
+    if (!(minmag > 0x1p-100f)) return fail(OPT_EUNSUPPORTED, "codebook midpoints too close to zero");
+    // lo: the largest power of two strictly below every |tau|.
+    uint32_t lo = fb(minmag) & 0x7F800000u;
+    if (lo == fb(minmag)) lo -= 0x00800000u;
+    const uint32_t one = 0x3F800000u;
+    for (uint32_t shift = 17; shift >= 10; --shift) {
+        const uint32_t nb = ((one - lo) >> shift) + 1;
+        const uint32_t sides = is_signed ? 2 : 1;
+        if (nb * sides > kMaxSearchWords) break;
+        std::vector<uint32_t> ent(nb * sides);
+        bool ok = true;
+        for (uint32_t b = 0; b < nb && ok; ++b) {
+            const uint32_t L = lo + (b << shift), H = L + (1u << shift) - 1u;
+            const float xl = bf(L), xh = bf(H);
+            // x >= 0 with magnitude bits in [L, H]
+            uint32_t base = 0, nin = 0, thr = 1u << shift;
+            for (int i = 0; i < 255; ++i) {
+                if (tau[i] <= xl) ++base;
+                else if (tau[i] <= xh) { ++nin; thr = fb(tau[i]) - L; }
+            }
+            ent[b] = base | (thr << 8);
+            ok = nin <= 1;
+            if (is_signed && ok) {
+                // x = -m, m in [xl, xh]
+                base = 0; nin = 0; thr = 1u << shift;
+                for (int i = 0; i < 255; ++i) {
+                    if (tau[i] <= -xh) ++base;
+                    else if (tau[i] <= -xl) { ++nin; thr = ((1u << shift) - 1u) - (fb(-tau[i]) - L); }
+                }
+                ent[nb + b] = base | (thr << 8);
+                ok = nin <= 1;
+            }
+        }
+        if (ok) {
+            out.entries.swap(ent);
+            out.P.lo = lo;
+            out.P.shift = shift;
+            out.P.nb = nb;
+            return OPT_OK;
+        }
+    }
+    return fail(OPT_EUNSUPPORTED, "codebook too dense for the lookup table");
+}
+
+// Packs [signed values | unsigned values | signed search | unsigned search].
+int build_qwords(const float *qs, const float *qu, std::vector<uint32_t> &words, QTabParams &ps,
+                 QTabParams &pu)
+{
+    BuiltTable S, U;
+    int rc;
+    if ((rc = build_search(qs, true, S)) != OPT_OK) return rc;
+    if ((rc = build_search(qu, false, U)) != OPT_OK) return rc;
+    if (S.entries.size() + U.entries.size() > kMaxSearchWords)
+        return fail(OPT_EUNSUPPORTED, "codebook lookup tables exceed the LDS budget");
+    words.resize(512 + S.entries.size() + U.entries.size());
+    memcpy(words.data(), qs, 1024);
+    memcpy(words.data() + 256, qu, 1024);
+    std::copy(S.entries.begin(), S.entries.end(), words.begin() + 512);
+    std::copy(U.entries.begin(), U.entries.end(), words.begin() + 512 + S.entries.size());
+    ps = S.P;
+    ps.offset = 512;
+    pu = U.P;
+    pu.offset = 512 + (uint32_t)S.entries.size();
+    return OPT_OK;
+}
+
+struct QCache {
+    float qs[256], qu[256];
+    std::vector<uint32_t> words;
+    QTabParams ps, pu;
+    bool valid = false;
+};
+
+// ---------------------------------------------------------------------------
+// per-device workspace
+
+struct Slot {
+    void *dev = nullptr;
+    void *host = nullptr;           // pinned staging copy
+    size_t cap = 0;
+    std::vector<unsigned char> content;
+    hipEvent_t ev = nullptr;
+    hipStream_t last_stream = nullptr;
+    bool multi_stream = false;
+    bool used = false;
+    uint64_t tick = 0;
+};
+
+struct Workspace {
+    bool init = false;
+    int ncu = 0;
+    Slot slots[kSlots];
+    uint64_t tick = 0;
+    double *partials = nullptr;
+    size_t partials_cap = 0;          // doubles
+    hipEvent_t partials_ev = nullptr;
+    hipStream_t partials_stream = nullptr;
+    bool partials_used = false;
+    QCache q;
+};
+
+std::mutex g_mu;
+Workspace g_ws[kMaxDevices];
+
+int workspace(Workspace *&out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(OPT_EUNSUPPORTED, "device %d out of range", dev);
+    Workspace &w = g_ws[dev];
+    if (!w.init) {
+        e = hipDeviceGetAttribute(&w.ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        for (Slot &s : w.slots) {
+            e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+            if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        }
+        e = hipEventCreateWithFlags(&w.partials_ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        w.init = true;
+    }
+    out = &w;
+    return OPT_OK;
+}
+
+// Wait until no queued kernel still reads the slot.
+int slot_quiesce(Slot &s)
+{
+    if (!s.used) return OPT_OK;
+    hipError_t e = s.multi_stream ? hipDeviceSynchronize() : hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return hip_fail(e, "waiting for a workspace slot");
+    s.used = false;
+    s.multi_stream = false;
+    return OPT_OK;
+}
+
+// Device copy of `blob`, reusing a slot that already holds the same bytes.
+int upload(Workspace &w, const std::vector<unsigned char> &blob, hipStream_t st, Slot *&out)
+{
+    ++w.tick;
+    for (Slot &s : w.slots) {
+        if (s.dev && s.content.size() == blob.size() && memcmp(s.content.data(), blob.data(), blob.size()) == 0) {
+            s.tick = w.tick;
+            out = &s;
+            return OPT_OK;
+        }
+    }
+    Slot *v = &w.slots[0];
+    for (Slot &s : w.slots) if (s.tick < v->tick) v = &s;
+    int rc = slot_quiesce(*v);
+    if (rc != OPT_OK) return rc;
+    hipError_t e;
+    if (v->cap < blob.size()) {
+        if (v->dev) { (void)hipFree(v->dev); v->dev = nullptr; }
+        if (v->host) { (void)hipHostFree(v->host); v->host = nullptr; }
+        v->cap = 0;
+        size_t cap = std::max<size_t>(blob.size(), 64 * 1024);
+        if ((e = hipMalloc(&v->dev, cap)) != hipSuccess) return hip_fail(e, "hipMalloc (workspace)");
+        if ((e = hipHostMalloc(&v->host, cap, hipHostMallocDefault)) != hipSuccess)
+            return hip_fail(e, "hipHostMalloc (workspace)");
+        v->cap = cap;
+    }
+    memcpy(v->host, blob.data(), blob.size());
+    v->content = blob;
+    if ((e = hipMemcpyAsync(v->dev, v->host, blob.size(), hipMemcpyHostToDevice, st)) != hipSuccess) {
+        v->content.clear();
+        return hip_fail(e, "hipMemcpyAsync (tables)");
+    }
+    v->tick = w.tick;
+    out = v;
+    return OPT_OK;
+}
+
+int slot_mark_used(Slot &s, hipStream_t st)
+{
+    if (s.used && s.last_stream != st) s.multi_stream = true;
+    s.used = true;
+    s.last_stream = st;
+    hipError_t e = hipEventRecord(s.ev, st);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return OPT_OK;
+}
+
+int partials_reserve(Workspace &w, size_t ndoubles, hipStream_t st)
+{
+    hipError_t e;
+    if (w.partials_cap < ndoubles) {
+        if (w.partials_used) {
+            if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            w.partials_used = false;
+        }
+        if (w.partials) (void)hipFree(w.partials);
+        w.partials = nullptr;
+        w.partials_cap = 0;
+        size_t cap = std::max<size_t>(ndoubles, 1 << 16);
+        if ((e = hipMalloc((void **)&w.partials, cap * sizeof(double))) != hipSuccess)
+            return hip_fail(e, "hipMalloc (norm partials)");
+        w.partials_cap = cap;
+    } else if (w.partials_used && w.partials_stream != st) {
+        // the previous pre-pass ran on another stream: order after it
+        if ((e = hipStreamWaitEvent(st, w.partials_ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    }
+    return OPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// argument checks and planning
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_hparams(const opt_hparams *hp, int fmt)
+{
+    if (!hp) return fail(OPT_EINVAL, "hp is NULL");
+    if (hp->step < 1) return fail(OPT_EINVAL, "step must be >= 1 (got %lld)", (long long)hp->step);
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(OPT_EINVAL, "beta1 and beta2 must lie in [0, 1)");
+    if (!(hp->beta3 >= 0.0f && hp->beta3 <= 1.0f)) return fail(OPT_EINVAL, "beta3 must lie in [0, 1]");
+    if (fmt == kQ8 && (!hp->qmap_signed || !hp->qmap_unsigned))
+        return fail(OPT_EINVAL, "8-bit states need qmap_signed and qmap_unsigned");
+    return OPT_OK;
+}
+
+int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
+{
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (n > 0 && !t) return fail(OPT_EINVAL, "tensors is NULL");
+    if (n > INT32_MAX) return fail(OPT_EINVAL, "too many tensors");
+    if (fmt < kF32 || fmt > kQ8) return fail(OPT_EINVAL, "unknown state format %d", fmt);
+    for (int64_t k = 0; k < n; ++k) {
+        const opt_tensor &x = t[k];
+        if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
+        if (x.p_dtype != OPT_F32 && x.p_dtype != OPT_BF16)
+            return fail(OPT_EINVAL, "tensor %lld: unknown p_dtype %d", (long long)k, x.p_dtype);
+        if (x.g_dtype != OPT_F32 && x.g_dtype != OPT_BF16)
+            return fail(OPT_EINVAL, "tensor %lld: unknown g_dtype %d", (long long)k, x.g_dtype);
+        if (x.p_dtype != OPT_F32)
+            return fail(OPT_EUNSUPPORTED, "tensor %lld: only fp32 parameters are provided", (long long)k);
+        if (x.numel == 0) continue;
+        const bool q8 = fmt == kQ8, m2 = opt == kAdEMAMix;
+        if (!x.p || !x.g || !x.s1 || !x.s2 || (m2 && !x.s3))
+            return fail(OPT_EINVAL, "tensor %lld: missing p, g or a state", (long long)k);
+        if (q8 && (!x.absmax1 || !x.absmax2 || (m2 && !x.absmax3)))
+            return fail(OPT_EINVAL, "tensor %lld: missing an absmax array", (long long)k);
+        if (!aligned(x.p, 16) || !aligned(x.g, 16) || !aligned(x.s1, 16) || !aligned(x.s2, 16) ||
+            (m2 && !aligned(x.s3, 16)))
+            return fail(OPT_EALIGN, "tensor %lld: p, g and states must be 16-byte aligned", (long long)k);
+        if (q8 && (!aligned(x.absmax1, 4) || !aligned(x.absmax2, 4) || (m2 && !aligned(x.absmax3, 4))))
+            return fail(OPT_EALIGN, "tensor %lld: absmax arrays must be 4-byte aligned", (long long)k);
+    }
+    return OPT_OK;
+}
+
+struct Bucket {
+    std::vector<DevTensor> tens;
+    std::vector<int32_t> chunk_tensor;
+};
+
+void plan_bucket(const opt_tensor *t, int64_t n, int gd, int64_t chunk, Bucket &b)
+{
+    int64_t next = 0;
+    for (int64_t k = 0; k < n; ++k) {
+        const opt_tensor &x = t[k];
+        // empty tensors ride in the first bucket with no chunks, so the norm
+        // pre-pass still writes {0, 0} for them
+        const bool mine = x.numel == 0 ? gd == kGradF32 : x.g_dtype == (gd == kGradF32 ? OPT_F32 : OPT_BF16);
+        if (!mine) continue;
+        DevTensor d{};
+        d.p = (float *)x.p;
+        d.g = x.g;
+        d.s1 = x.s1; d.s2 = x.s2; d.s3 = x.s3;
+        d.a1 = x.absmax1; d.a2 = x.absmax2; d.a3 = x.absmax3;
+        d.numel = x.numel;
+        d.chunk_begin = next;
+        d.k = (int32_t)k;
+        const int64_t nc = (x.numel + chunk - 1) / chunk;
+        const int32_t idx = (int32_t)b.tens.size();
+        b.tens.push_back(d);
+        b.chunk_tensor.insert(b.chunk_tensor.end(), (size_t)nc, idx);
+        next += nc;
+    }
+}
+
+size_t round16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Blob = DevTensor[] | int32 chunk_tensor[] | uint32 q-words[]; returns the
+// byte offsets of the second and third parts.
+void make_blob(const Bucket &b, const std::vector<uint32_t> *qw, std::vector<unsigned char> &blob,
+               size_t &off_ct, size_t &off_q)
+{
+    const size_t n0 = b.tens.size() * sizeof(DevTensor);
+    off_ct = round16(n0);
+    off_q = round16(off_ct + b.chunk_tensor.size() * 4);
+    const size_t total = off_q + (qw ? qw->size() * 4 : 0);
+    blob.assign(total, 0);
+    memcpy(blob.data(), b.tens.data(), n0);
+    memcpy(blob.data() + off_ct, b.chunk_tensor.data(), b.chunk_tensor.size() * 4);
+    if (qw) memcpy(blob.data() + off_q, qw->data(), qw->size() * 4);
+}
+
+int qtables(Workspace &w, const opt_hparams *hp)
+{
+    QCache &q = w.q;
+    if (q.valid && !memcmp(q.qs, hp->qmap_signed, 1024) && !memcmp(q.qu, hp->qmap_unsigned, 1024))
+        return OPT_OK;
+    q.valid = false;
+    int rc = build_qwords(hp->qmap_signed, hp->qmap_unsigned, q.words, q.ps, q.pu);
+    if (rc != OPT_OK) return rc;
+    memcpy(q.qs, hp->qmap_signed, 1024);
+    memcpy(q.qu, hp->qmap_unsigned, 1024);
+    q.valid = true;
+    return OPT_OK;
+}
+
+StepArgs base_args(const opt_hparams *hp, int64_t chunk)
+{
+    StepArgs a{};
+    a.chunk = chunk;
+    a.lr = hp->lr; a.beta1 = hp->beta1; a.beta2 = hp->beta2; a.beta3 = hp->beta3;
+    a.alpha = hp->alpha; a.eps = hp->eps; a.wd = hp->weight_decay; a.max_unorm = hp->max_unorm;
+    a.step = hp->step;
+    a.seed = hp->seed;
+    return a;
+}
+
+int grid_for(const Workspace &w, int64_t nchunks)
+{
+    int64_t cap = (int64_t)w.ncu * g_wgs_per_cu;
+    return (int)std::max<int64_t>(1, std::min(nchunks, cap));
+}
+
+// The shared body of the step and the pre-pass.
+int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp, const double *unorm,
+        double *unorm_out, void *stream)
+{
+    int rc;
+    if ((rc = check_hparams(hp, fmt)) != OPT_OK) return rc;
+    if ((rc = check_tensors(t, n, opt, fmt)) != OPT_OK) return rc;
+    const bool pre = unorm_out != nullptr;
+    if (!pre && hp->max_unorm > 0.0f && !unorm)
+        return fail(OPT_EINVAL, "max_unorm > 0 needs the norms from opt_precondition_unorm");
+    if (pre && !aligned(unorm_out, 8)) return fail(OPT_EALIGN, "unorm_out must be 8-byte aligned");
+    if (n == 0) return OPT_OK;
+
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace *w;
+    if ((rc = workspace(w)) != OPT_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const bool q8 = fmt == kQ8;
+    if (q8 && (rc = qtables(*w, hp)) != OPT_OK) return rc;
+    const int64_t chunk = g_chunk;
+
+    Bucket b[2];
+    plan_bucket(t, n, kGradF32, chunk, b[0]);
+    plan_bucket(t, n, kGradBF16, chunk, b[1]);
+
+    if (pre) {
+        size_t need = 0;
+        for (auto &bk : b) need = std::max(need, bk.chunk_tensor.size() * (size_t)(chunk / kUTile) * 2);
+        if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
+    }
+
+    for (int gd = 0; gd < 2; ++gd) {
+        Bucket &bk = b[gd];
+        if (bk.tens.empty() || (!pre && bk.chunk_tensor.empty())) continue;
+        std::vector<unsigned char> blob;
+        size_t off_ct, off_q;
+        make_blob(bk, q8 ? &w->q.words : nullptr, blob, off_ct, off_q);
+        Slot *s;
+        if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+        StepArgs a = base_args(hp, chunk);
+        a.tens = (const DevTensor *)s->dev;
+        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
+        a.nchunks = (int64_t)bk.chunk_tensor.size();
+        a.unorm = (!pre && hp->max_unorm > 0.0f) ? unorm : nullptr;
+        size_t lds = 0;
+        if (q8) {
+            a.q.words = (const uint32_t *)((unsigned char *)s->dev + off_q);
+            a.q.nwords = (uint32_t)w->q.words.size();
+            a.q.s = w->q.ps;
+            a.q.u = w->q.pu;
+            lds = (size_t)a.q.nwords * 4;
+        }
+        hipError_t e;
+        const int grid = grid_for(*w, a.nchunks);
+        if (pre) {
+            a.partials = w->partials;
+            e = launch_unorm(opt, gd, fmt, a, grid, q8 ? 2048 : 0, (int)bk.tens.size(), unorm_out, st);
+            if (e == hipSuccess) {
+                w->partials_used = true;
+                w->partials_stream = st;
+                e = hipEventRecord(w->partials_ev, st);
+            }
+        } else {
+            e = launch_step(opt, gd, fmt, a, grid, lds, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, pre ? "norm pre-pass launch" : "step launch");
+        if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
+    }
+    return OPT_OK;
+}
+
+}  // namespace
+}  // namespace optstep
+
+using namespace optstep;
+
+extern "C" {
+
+int opt_step_adamw(const opt_tensor *tensors, int64_t n, int32_t state_fmt, const opt_hparams *hp,
+                   const double *unorm, void *stream)
+{
+    return run(kAdamW, tensors, n, state_fmt, hp, unorm, nullptr, stream);
+}
+
+int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt, const opt_hparams *hp,
+                      const double *unorm, void *stream)
+{
+    return run(kAdEMAMix, tensors, n, state_fmt, hp, unorm, nullptr, stream);
+}
+
+int opt_precondition_unorm(int32_t optimizer, const opt_tensor *tensors, int64_t n, int32_t state_fmt,
+                           const opt_hparams *hp, double *unorm_out, void *stream)
+{
+    if (optimizer != kAdamW && optimizer != kAdEMAMix) return fail(OPT_EINVAL, "unknown optimizer %d", optimizer);
+    if (!unorm_out) return fail(OPT_EINVAL, "unorm_out is NULL");
+    return run(optimizer, tensors, n, state_fmt, hp, nullptr, unorm_out, stream);
+}
+
+const char *opt_last_error(void) { return g_err.c_str(); }
+
+int opt_shutdown(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (int d = 0; d < kMaxDevices; ++d) {
+        Workspace &w = g_ws[d];
+        if (!w.init) continue;
+        (void)hipSetDevice(d);
+        (void)hipDeviceSynchronize();
+        for (Slot &s : w.slots) {
+            if (s.dev) (void)hipFree(s.dev);
+            if (s.host) (void)hipHostFree(s.host);
+            if (s.ev) (void)hipEventDestroy(s.ev);
+            s = Slot();
+        }
+        if (w.partials) (void)hipFree(w.partials);
+        if (w.partials_ev) (void)hipEventDestroy(w.partials_ev);
+        w = Workspace();
+    }
+    (void)hipSetDevice(cur);
+    return OPT_OK;
+}
+
+int opt_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t count, uint32_t *out,
+                     void *stream)
+{
+    if (count < 0 || j0 < 0) return fail(OPT_EINVAL, "negative count or start");
+    if (count == 0) return OPT_OK;
+    if (!out) return fail(OPT_EINVAL, "out is NULL");
+    hipError_t e = launch_debug_philox(seed, t, k, j0, count, out, (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "debug philox launch");
+}
+
+int opt_debug_round_bf16(const float *x, const uint32_t *r, uint16_t *out, int64_t n, void *stream)
+{
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (n == 0) return OPT_OK;
+    if (!x || !out) return fail(OPT_EINVAL, "x or out is NULL");
+    hipError_t e = launch_debug_round(x, r, out, n, (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "debug round launch");
+}
+
+int opt_debug_quantize(const float *qmap, int32_t is_signed, const float *x, uint8_t *out, int64_t n,
+                       void *stream)
+{
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (!qmap) return fail(OPT_EINVAL, "qmap is NULL");
+    BuiltTable B;
+    int rc = build_search(qmap, is_signed != 0, B);
+    if (rc != OPT_OK) return rc;
+    if (n == 0) return OPT_OK;
+    if (!x || !out) return fail(OPT_EINVAL, "x or out is NULL");
+    std::vector<uint32_t> words(512 + B.entries.size());
+    memcpy(words.data() + (is_signed ? 0 : 256), qmap, 1024);
+    std::copy(B.entries.begin(), B.entries.end(), words.begin() + 512);
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace *w;
+    if ((rc = workspace(w)) != OPT_OK) return rc;
+    std::vector<unsigned char> blob(words.size() * 4);
+    memcpy(blob.data(), words.data(), blob.size());
+    Slot *s;
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+    QTabs q{};
+    q.words = (const uint32_t *)s->dev;
+    q.nwords = (uint32_t)words.size();
+    QTabParams P = B.P;
+    P.offset = 512;
+    if (is_signed) q.s = P; else q.u = P;
+    hipError_t e = launch_debug_quantize(q, is_signed, x, out, n, st);
+    if (e != hipSuccess) return hip_fail(e, "debug quantize launch");
+    return slot_mark_used(*s, st);
+}
+
+int opt_debug_quantize_host(const float *qmap, int32_t is_signed, const float *x, uint8_t *out, int64_t n)
+{
+    if (n < 0 || !qmap || (n > 0 && (!x || !out))) return fail(OPT_EINVAL, "bad arguments");
+    BuiltTable B;
+    int rc = build_search(qmap, is_signed != 0, B);
+    if (rc != OPT_OK) return rc;
+    QTabParams P = B.P;
+    P.offset = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = x[i];
+        if (v != v) { out[i] = 0; continue; }
+        if (!(std::fabs(v) <= 1.0f)) return fail(OPT_EINVAL, "x[%lld] is outside [-1, 1]", (long long)i);
+        out[i] = (uint8_t)q8_lookup(v, B.entries.data(), P, is_signed != 0);
+    }
+    return OPT_OK;
+}
+
+int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n)
+{
+    if (n < 0 || (n > 0 && (!a || !b || !out))) return fail(OPT_EINVAL, "bad arguments");
+    for (int64_t i = 0; i < n; ++i) {
+        if (!div_by_ok(b[i])) return fail(OPT_EINVAL, "divisor %lld outside the fast range", (long long)i);
+        out[i] = div_by(a[i], b[i], 1.0f / b[i]);
+    }
+    return OPT_OK;
+}
+
+int64_t opt_debug_plan(const int64_t *numels, int64_t n, int64_t *chunks_out)
+{
+    if (n < 0 || (n > 0 && (!numels || !chunks_out))) return fail(OPT_EINVAL, "bad arguments");
+    for (int64_t k = 0; k < n; ++k) {
+        if (numels[k] < 0) return fail(OPT_EINVAL, "numel < 0");
+        chunks_out[k] = (numels[k] + g_chunk - 1) / g_chunk;
+    }
+    return g_chunk;
+}
+
+int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu)
+{
+    if (chunk <= 0 || chunk % 1024 != 0) return fail(OPT_EINVAL, "chunk must be a positive multiple of 1024");
+    if (wgs_per_cu <= 0 || wgs_per_cu > 64) return fail(OPT_EINVAL, "wgs_per_cu must be in [1, 64]");
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_chunk = chunk;
+    g_wgs_per_cu = wgs_per_cu;
+    return OPT_OK;
+}
+
+}  // extern "C"

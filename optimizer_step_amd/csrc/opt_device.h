@@ -1,0 +1,279 @@
+// opt_device.h -- device building blocks of the optimizer-step kernels.
+//
+// Functions marked __host__ __device__ are also compiled into the host side
+// of the library so that the CPU tests exercise the very same source.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "opt_plan.h"
+
+namespace optstep {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// Accesses through the global address space, so the compiler emits global_*
+// (not flat_*) instructions for pointers it reads out of the tensor table.
+#define OPT_GLOBAL __attribute__((address_space(1)))
+
+template <class V>
+__device__ __forceinline__ V gld(const void *p) { return *(const OPT_GLOBAL V *)p; }
+
+template <class V>
+__device__ __forceinline__ void gst(void *p, V v) { *(OPT_GLOBAL V *)p = v; }
+
+__host__ __device__ inline uint32_t fbits(float x)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __float_as_uint(x);
+#else
+    uint32_t u; memcpy(&u, &x, 4); return u;
+#endif
+}
+
+__host__ __device__ inline float bitsf(uint32_t u)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __uint_as_float(u);
+#else
+    float x; memcpy(&x, &u, 4); return x;
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// BF16 words.  A BF16 word is the high half of a binary32 word.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bitsf(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bitsf(w & 0xFFFF0000u); }
+
+// Round to nearest even ("When Small Updates Disappear", Sec. 6: the built-in
+// cast): add 0x7FFF plus the last kept bit, keep the high half.  NaN keeps its
+// sign and becomes quiet.
+__host__ __device__ inline uint32_t bf16_rne(float x)
+{
+    uint32_t b = fbits(x);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x0040u;
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Stochastic rounding (same page, Sec. 6.1): add a 16-bit random integer to
+// the word and keep the high half; the carry reaches the kept bits with
+// probability (dropped bits)/2^16.  Infinities and NaNs round to nearest.
+__host__ __device__ inline uint32_t bf16_sr(float x, uint32_t r16)
+{
+    uint32_t b = fbits(x);
+    if ((b & 0x7F800000u) == 0x7F800000u) return bf16_rne(x);
+    return (b + r16) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies and a key-dependent exchange, the key bumped by the
+// Weyl constants between rounds.
+
+struct PhiloxOut { uint32_t w0, w1, w2, w3; };
+
+__host__ __device__ inline PhiloxOut philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                   uint32_t c3, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
+        k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+    }
+    return PhiloxOut{c0, c1, c2, c3};
+}
+
+// The block that serves elements 4q..4q+3 of tensor k at step t.
+__host__ __device__ inline PhiloxOut sr_block(uint64_t seed, int64_t t, int32_t k, uint64_t q,
+                                              bool slow_ema)
+{
+    return philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), (uint32_t)(uint64_t)t,
+                         (uint32_t)k | (slow_ema ? 0x80000000u : 0u),
+                         (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__host__ __device__ inline uint32_t philox_word(const PhiloxOut &o, int i)
+{
+    return i == 0 ? o.w0 : i == 1 ? o.w1 : i == 2 ? o.w2 : o.w3;
+}
+
+// ---------------------------------------------------------------------------
+// Division by a divisor b that is the same for many dividends, given
+// y = RN(1/b).  q0 = a*y is within 1.5 ulp of a/b; one residual correction
+// (r = a - b*q exactly by fma, q += r*y) makes it faithful, and a second
+// correction then yields the correctly rounded quotient (Markstein's theorem:
+// y within half an ulp of 1/b and q faithful => RN(q + r*y) = RN(a/b)).
+// Requires b and 1/b normal and a/b not below the normal range; callers check
+// b and treat tiny quotients as described where they use it.
+__host__ __device__ inline float div_by(float a, float b, float y)
+{
+    float q = a * y;
+    float r = fmaf(-b, q, a);
+    q = fmaf(r, y, q);
+    r = fmaf(-b, q, a);
+    return fmaf(r, y, q);
+}
+
+// b for which div_by is exact: b and 1/b both well inside the normal range.
+__host__ __device__ inline bool div_by_ok(float b)
+{
+    float ab = b < 0 ? -b : b;
+    return ab >= 0x1p-124f && ab <= 0x1p124f;
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit code of x against a codebook's lookup table (layout in opt_plan.h).
+// x must not be NaN (callers map NaN to code 0).  Magnitudes above 1 read as
+// 1, which keeps the nearest-entry code (entries lie in [-1, 1]); an unsigned
+// table gives code 0 to x <= 0 (every midpoint is above 0).
+__host__ __device__ inline uint32_t q8_lookup(float x, const uint32_t *tab, const QTabParams &P,
+                                              bool is_signed)
+{
+    uint32_t b = fbits(x);
+    if (!is_signed && (b >> 31)) return 0u;
+    uint32_t mag = b & 0x7FFFFFFFu;
+    mag = mag < P.lo ? P.lo : mag;                    // all |x| < lo share one code
+    mag = mag > 0x3F800000u ? 0x3F800000u : mag;
+    uint32_t off = mag - P.lo;
+    uint32_t mask = (1u << P.shift) - 1u;
+    uint32_t bucket = off >> P.shift;
+    uint32_t key = off & mask;
+    // +0 reads the x < 0 half: a midpoint of exactly 0 sits between +0 and
+    // the smallest positive float, and that half holds code(0) for m -> 0
+    const bool neg = is_signed && (int32_t)b <= 0;
+    uint32_t e = tab[P.offset + bucket + (neg ? P.nb : 0u)];
+    key = neg ? (mask - key) : key;
+    return (e & 0xFFu) + (key >= (e >> 8) ? 1u : 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Bias corrections and the other per-call scalars.  Formed once per
+// workgroup by one lane and published through LDS (the issue "Investigate
+// SM103 bias-correction broadcast in 32-bit optimizers", Problem: they are
+// uniform across the workgroup).
+
+struct Scalars {
+    float om1, om2, om3;   // 1 - beta
+    float c1, c2;          // 1 - beta^t, formed in binary64 and rounded once
+    float rc1, rc2;        // RN(1/c1), RN(1/c2)
+    float d;               // 1 - lr*wd
+    float lam;             // lr (the update-norm scale is applied per tensor)
+};
+
+__device__ inline double powi(double b, int64_t t)
+{
+    double r = 1.0;
+    while (t > 0) {
+        if (t & 1) r *= b;
+        b *= b;
+        t >>= 1;
+    }
+    return r;
+}
+
+__device__ inline Scalars make_scalars(const StepArgs &a)
+{
+    Scalars s;
+    s.om1 = 1.0f - a.beta1;
+    s.om2 = 1.0f - a.beta2;
+    s.om3 = 1.0f - a.beta3;
+    s.c1 = (float)(1.0 - powi((double)a.beta1, a.step));
+    s.c2 = (float)(1.0 - powi((double)a.beta2, a.step));
+    // 0 <= beta < 1 (checked by the host) keeps c in [2^-24, 1], where div_by
+    // by c is exact
+    s.rc1 = 1.0f / s.c1;
+    s.rc2 = 1.0f / s.c2;
+    float lrwd = a.lr * a.wd;
+    s.d = 1.0f - lrwd;
+    s.lam = a.lr;
+    return s;
+}
+
+// lr times the update-norm scale of tensor k: min(1, max_unorm*||p||/||u||).
+__device__ inline float lam_for(const StepArgs &a, int32_t k)
+{
+    if (!(a.max_unorm > 0.0f) || a.unorm == nullptr) return a.lr;
+    double u2 = a.unorm[2 * (int64_t)k], p2 = a.unorm[2 * (int64_t)k + 1];
+    double un = sqrt(u2), bound = (double)a.max_unorm * sqrt(p2);
+    float s = un > bound ? (float)(bound / un) : 1.0f;
+    return a.lr * s;
+}
+
+// ---------------------------------------------------------------------------
+// The per-element recipe (fixed binary32 order; built with -ffp-contract=off).
+
+struct Mom { float m, v, m2, u; };
+
+template <int OPT>
+__device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, float g, float m,
+                                       float v, float m2)
+{
+    Mom r;
+    float gg = g * g;
+    r.m = a.beta1 * m + s.om1 * g;
+    r.v = a.beta2 * v + s.om2 * gg;
+    float mh = div_by(r.m, s.c1, s.rc1);
+    float vh = div_by(r.v, s.c2, s.rc2);
+    float den = __builtin_sqrtf(vh) + a.eps;
+    if (OPT == kAdEMAMix) {
+        r.m2 = a.beta3 * m2 + s.om3 * g;
+        float num = mh + a.alpha * r.m2;
+        r.u = num / den;
+    } else {
+        r.m2 = 0.0f;
+        r.u = mh / den;
+    }
+    return r;
+}
+
+// Decay-first: both terms from the previous p (bitsandbytes PR "Fix decoupled
+// weight decay ordering in the CUDA Adam/AdEMAMix kernels", intro).
+__device__ __forceinline__ float apply_update(float p, float d, float lam, float u)
+{
+    float decayed = p * d;
+    float step = lam * u;
+    return decayed - step;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions.
+
+// Max over the 64 lanes (IEEE maxNum: NaN inputs are skipped; callers track
+// NaN separately).  DPP row exchanges within each 16-lane row, then the four
+// row results are read across.
+__device__ __forceinline__ float wave_max(float x)
+{
+    int v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+    v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+    v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false))); // row_ror 4
+    v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false))); // row_ror 8
+    v = __float_as_int(x);
+    float r0 = __int_as_float(__builtin_amdgcn_readlane(v, 0));
+    float r1 = __int_as_float(__builtin_amdgcn_readlane(v, 16));
+    float r2 = __int_as_float(__builtin_amdgcn_readlane(v, 32));
+    float r3 = __int_as_float(__builtin_amdgcn_readlane(v, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Sum over the 64 lanes in a fixed butterfly order; every lane ends with the
+// same bits (each level adds the same two partial sums, commutatively).
+__device__ __forceinline__ double wave_sum(double x)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace optstep

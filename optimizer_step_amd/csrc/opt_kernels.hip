@@ -1,0 +1,531 @@
+// opt_kernels.hip -- gfx950 kernels of the fused element-wise optimizer step.
+//
+// Layout of the work: the host flattens a dtype bucket of tensors into a
+// chunk space (each tensor split into chunks of `chunk` elements, a multiple
+// of 1024), and a persistent grid of 256-thread workgroups walks the chunks
+// with a grid stride.  Inside a chunk every lane owns groups of 4 consecutive
+// elements, so p, m, v (fp32) move as 128-bit accesses, bf16 gradients and
+// BF16 states as 64-bit ones, and 8-bit codes as 32-bit ones; consecutive
+// lanes own consecutive groups, so every access instruction of a wave64 is
+// fully coalesced.  The 8-bit format hands one 256-element block to one wave
+// (64 lanes x 4), which makes the block absmax a wave reduction.
+//
+// The step is HBM-bound (no dense contraction, so no MFMA): every byte is read
+// or written once per step and no intermediate leaves registers.
+#include "opt_device.h"
+
+namespace optstep {
+
+// ---------------------------------------------------------------------------
+// element groups of four
+
+template <int GD>
+__device__ __forceinline__ void load_grad4(const void *g, int64_t e, float out[4])
+{
+    if (GD == kGradF32) {
+        f4 x = gld<f4>((const float *)g + e);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        u2 w = gld<u2>((const uint16_t *)g + e);
+        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+        out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    }
+}
+
+template <int GD>
+__device__ __forceinline__ float load_grad1(const void *g, int64_t e)
+{
+    if (GD == kGradF32) return gld<float>((const float *)g + e);
+    return bf16_lo(gld<uint16_t>((const uint16_t *)g + e));
+}
+
+template <int SF>
+__device__ __forceinline__ void load_state4(const void *s, int64_t e, float out[4])
+{
+    if (SF == kF32) {
+        f4 x = gld<f4>((const float *)s + e);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        u2 w = gld<u2>((const uint16_t *)s + e);
+        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+        out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    }
+}
+
+template <int SF>
+__device__ __forceinline__ float load_state1(const void *s, int64_t e)
+{
+    if (SF == kF32) return gld<float>((const float *)s + e);
+    return bf16_lo(gld<uint16_t>((const uint16_t *)s + e));
+}
+
+// Store four fp32 moments in format SF; r[i] are the 16-bit random integers of
+// stochastic rounding (ignored otherwise).
+template <int SF>
+__device__ __forceinline__ void store_state4(void *s, int64_t e, const float x[4], const uint32_t r[4])
+{
+    if (SF == kF32) {
+        gst<f4>((float *)s + e, f4{x[0], x[1], x[2], x[3]});
+    } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = SF == kBF16SR ? bf16_sr(x[i], r[i]) : bf16_rne(x[i]);
+        gst<u2>((uint16_t *)s + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+    }
+}
+
+template <int SF>
+__device__ __forceinline__ void store_state1(void *s, int64_t e, float x, uint32_t r)
+{
+    if (SF == kF32) gst<float>((float *)s + e, x);
+    else gst<uint16_t>((uint16_t *)s + e, (uint16_t)(SF == kBF16SR ? bf16_sr(x, r) : bf16_rne(x)));
+}
+
+// ---------------------------------------------------------------------------
+// fp32 and BF16 states
+
+struct Group {
+    float p[4], g[4], m[4], v[4], m2[4];
+};
+
+template <int OPT, int GD, int SF>
+__device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, Group &x)
+{
+    f4 pv = gld<f4>(T.p + e);
+    x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
+    load_grad4<GD>(T.g, e, x.g);
+    load_state4<SF>(T.s1, e, x.m);
+    load_state4<SF>(T.s2, e, x.v);
+    if (OPT == kAdEMAMix) load_state4<SF>(T.s3, e, x.m2);
+    else x.m2[0] = x.m2[1] = x.m2[2] = x.m2[3] = 0.0f;
+}
+
+template <int OPT, int GD, int SF>
+__device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
+                                          int64_t e, float lam, Group &x)
+{
+    float mo[4], vo[4], m2o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        Mom r = moments<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
+        x.p[i] = apply_update(x.p[i], s.d, lam, r.u);
+        mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
+    }
+    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0};
+    if (SF == kBF16SR) {
+        PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
+        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
+        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
+        if (OPT == kAdEMAMix) {
+            PhiloxOut w2 = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true);
+            rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu;
+            rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
+        }
+    }
+    gst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
+    store_state4<SF>(T.s1, e, mo, rm);
+    store_state4<SF>(T.s2, e, vo, rv);
+    if (OPT == kAdEMAMix) store_state4<SF>(T.s3, e, m2o, rm2);
+}
+
+template <int OPT, int GD, int SF>
+__device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, const DevTensor &T,
+                                          int64_t e, float lam)
+{
+    float g = load_grad1<GD>(T.g, e);
+    float m = load_state1<SF>(T.s1, e), v = load_state1<SF>(T.s2, e);
+    float m2 = OPT == kAdEMAMix ? load_state1<SF>(T.s3, e) : 0.0f;
+    Mom r = moments<OPT>(s, a, g, m, v, m2);
+    gst<float>(T.p + e, apply_update(gld<float>(T.p + e), s.d, lam, r.u));
+    uint32_t rm = 0, rv = 0, rm2 = 0;
+    if (SF == kBF16SR) {
+        uint32_t w = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3));
+        rm = w & 0xFFFFu; rv = w >> 16;
+        if (OPT == kAdEMAMix)
+            rm2 = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true), (int)(e & 3)) & 0xFFFFu;
+    }
+    store_state1<SF>(T.s1, e, r.m, rm);
+    store_state1<SF>(T.s2, e, r.v, rv);
+    if (OPT == kAdEMAMix) store_state1<SF>(T.s3, e, r.m2, rm2);
+}
+
+template <int OPT, int GD, int SF>
+__global__ __launch_bounds__(kThreads) void step_ew_kernel(const DevTensor *__restrict__ tens,
+                                                           const int32_t *__restrict__ ctab, StepArgs a)
+{
+    __shared__ Scalars sh;
+    if (threadIdx.x == 0) sh = make_scalars(a);
+    __syncthreads();
+    const Scalars s = sh;
+    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
+        const DevTensor T = tens[ctab[c]];
+        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
+        const int64_t len = min(a.chunk, T.numel - e0);
+        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
+        const int64_t ngroups = len >> 2;
+        int64_t i = threadIdx.x;
+        // two groups per iteration: both groups' loads are issued before any math
+        for (; i + kThreads < ngroups; i += 2 * kThreads) {
+            Group x0, x1;
+            ew_load<OPT, GD, SF>(T, e0 + 4 * i, x0);
+            ew_load<OPT, GD, SF>(T, e0 + 4 * (i + kThreads), x1);
+            ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, lam, x0);
+            ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (i + kThreads), lam, x1);
+        }
+        if (i < ngroups) {
+            Group x0;
+            ew_load<OPT, GD, SF>(T, e0 + 4 * i, x0);
+            ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, lam, x0);
+        }
+        const int64_t tail = len & 3;
+        if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit blockwise states
+
+// Code of one fp32 moment against its block absmax A.  fast: A and 1/A are
+// normal, so div_by gives the correctly rounded m'/A and |x| <= 1; otherwise
+// x = 0 for A = 0, else the correctly rounded m'/A, and a NaN quotient (A NaN
+// or infinite) gets code 0.
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t quant(float x_num, float A, float yA, bool fast,
+                                          const uint32_t *lds, const QTabParams &P)
+{
+    if (fast) return q8_lookup(div_by(x_num, A, yA), lds, P, SIGNED);
+    float x = A == 0.0f ? 0.0f : x_num / A;
+    if (x != x) return 0u;
+    return q8_lookup(x, lds, P, SIGNED);
+}
+
+__device__ __forceinline__ float absmax_of(const float x[4], bool any_nan)
+{
+    float m = wave_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+    return any_nan ? __builtin_nanf("") : m;
+}
+
+template <int OPT, int GD>
+__global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__restrict__ tens,
+                                                           const int32_t *__restrict__ ctab,
+                                                           const uint32_t *__restrict__ qwords,
+                                                           StepArgs a)
+{
+    extern __shared__ uint32_t lds[];
+    __shared__ Scalars sh;
+    for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kThreads) lds[i] = qwords[i];
+    if (threadIdx.x == 0) sh = make_scalars(a);
+    __syncthreads();
+    const Scalars s = sh;
+    const float *TS = (const float *)lds;
+    const float *TU = TS + 256;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const QTabParams PS = a.q.s, PU = a.q.u;
+
+    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
+        const DevTensor T = tens[ctab[c]];
+        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
+        const int64_t len = min(a.chunk, T.numel - e0);
+        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
+        const int64_t nblk = (len + kQBlock - 1) / kQBlock;
+        for (int64_t b = wave; b < nblk; b += kWaves) {
+            const int64_t eb = e0 + b * kQBlock;           // first element of the block
+            const int64_t blk = eb / kQBlock;              // its absmax slot
+            const int nvalid = (int)min((int64_t)kQBlock, T.numel - eb);
+            const int i0 = lane * 4;
+            const int nmine = max(0, min(4, nvalid - i0));
+            const int64_t e = eb + i0;
+
+            float p[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f};
+            uint32_t cm = 0, cv = 0, cm2 = 0;
+            const uint8_t *S1 = (const uint8_t *)T.s1, *S2 = (const uint8_t *)T.s2,
+                          *S3 = (const uint8_t *)T.s3;
+            if (nmine == 4) {
+                f4 pv = gld<f4>(T.p + e);
+                p[0] = pv.x; p[1] = pv.y; p[2] = pv.z; p[3] = pv.w;
+                load_grad4<GD>(T.g, e, g);
+                cm = gld<uint32_t>(S1 + e);
+                cv = gld<uint32_t>(S2 + e);
+                if (OPT == kAdEMAMix) cm2 = gld<uint32_t>(S3 + e);
+            } else {
+                for (int i = 0; i < nmine; ++i) {
+                    p[i] = gld<float>(T.p + e + i);
+                    g[i] = load_grad1<GD>(T.g, e + i);
+                    cm |= (uint32_t)gld<uint8_t>(S1 + e + i) << (8 * i);
+                    cv |= (uint32_t)gld<uint8_t>(S2 + e + i) << (8 * i);
+                    if (OPT == kAdEMAMix) cm2 |= (uint32_t)gld<uint8_t>(S3 + e + i) << (8 * i);
+                }
+            }
+            const float A1 = gld<float>(T.a1 + blk), A2 = gld<float>(T.a2 + blk);
+            const float A3 = OPT == kAdEMAMix ? gld<float>(T.a3 + blk) : 0.0f;
+
+            float mo[4], vo[4], m2o[4];
+            bool nan_m = false, nan_v = false, nan_m2 = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = TS[(cm >> (8 * i)) & 0xFFu] * A1;
+                float v = TU[(cv >> (8 * i)) & 0xFFu] * A2;
+                float m2 = OPT == kAdEMAMix ? TS[(cm2 >> (8 * i)) & 0xFFu] * A3 : 0.0f;
+                Mom r = moments<OPT>(s, a, g[i], m, v, m2);
+                const bool valid = i < nmine;
+                p[i] = apply_update(p[i], s.d, lam, r.u);
+                mo[i] = valid ? r.m : 0.0f;
+                vo[i] = valid ? r.v : 0.0f;
+                m2o[i] = valid ? r.m2 : 0.0f;
+                nan_m |= mo[i] != mo[i];
+                nan_v |= vo[i] != vo[i];
+                nan_m2 |= m2o[i] != m2o[i];
+            }
+            // block absmax: wave max, poisoned by any NaN in the block
+            const float Am = absmax_of(mo, __any(nan_m));
+            const float Av = absmax_of(vo, __any(nan_v));
+            const bool fm = div_by_ok(Am), fv = div_by_ok(Av);
+            const float ym = fm ? 1.0f / Am : 0.0f, yv = fv ? 1.0f / Av : 0.0f;
+            uint32_t om = 0, ov = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                om |= quant<true>(mo[i], Am, ym, fm, lds, PS) << (8 * i);
+                ov |= quant<false>(vo[i], Av, yv, fv, lds, PU) << (8 * i);
+            }
+            uint32_t om2 = 0;
+            float Am2 = 0.0f;
+            if (OPT == kAdEMAMix) {
+                Am2 = absmax_of(m2o, __any(nan_m2));
+                const bool f2 = div_by_ok(Am2);
+                const float y2 = f2 ? 1.0f / Am2 : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) om2 |= quant<true>(m2o[i], Am2, y2, f2, lds, PS) << (8 * i);
+            }
+            uint8_t *W1 = (uint8_t *)T.s1, *W2 = (uint8_t *)T.s2, *W3 = (uint8_t *)T.s3;
+            if (nmine == 4) {
+                gst<f4>(T.p + e, f4{p[0], p[1], p[2], p[3]});
+                gst<uint32_t>(W1 + e, om);
+                gst<uint32_t>(W2 + e, ov);
+                if (OPT == kAdEMAMix) gst<uint32_t>(W3 + e, om2);
+            } else {
+                for (int i = 0; i < nmine; ++i) {
+                    gst<float>(T.p + e + i, p[i]);
+                    gst<uint8_t>(W1 + e + i, (uint8_t)(om >> (8 * i)));
+                    gst<uint8_t>(W2 + e + i, (uint8_t)(ov >> (8 * i)));
+                    if (OPT == kAdEMAMix) gst<uint8_t>(W3 + e + i, (uint8_t)(om2 >> (8 * i)));
+                }
+            }
+            if (lane == 0) {
+                gst<float>(T.a1 + blk, Am);
+                gst<float>(T.a2 + blk, Av);
+                if (OPT == kAdEMAMix) gst<float>(T.a3 + blk, Am2);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// max_unorm pre-pass.  The tensor is cut into tiles of kUTile elements from
+// element 0; one wave sums a tile ({sum u^2, sum p^2} in binary64: per lane in
+// element order, then a fixed butterfly) and writes one partial per tile, and
+// one workgroup per tensor then sums its tiles in a fixed order.  Nothing
+// depends on the chunk size, the grid or timing, and there are no atomics, so
+// repeated runs give identical bits.
+
+template <int SF>
+__device__ __forceinline__ float read_state(const uint32_t *lds, const void *s, const float *amax,
+                                            bool is_signed, int64_t e)
+{
+    if (SF == kQ8) {
+        const float *tab = (const float *)lds + (is_signed ? 0 : 256);
+        return tab[gld<uint8_t>((const uint8_t *)s + e)] * gld<float>(amax + e / kQBlock);
+    }
+    return load_state1<SF == kF32 ? kF32 : kBF16RN>(s, e);
+}
+
+template <int OPT, int GD, int SF>
+__global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTensor *__restrict__ tens,
+                                                                  const int32_t *__restrict__ ctab,
+                                                                  const uint32_t *__restrict__ qwords,
+                                                                  StepArgs a)
+{
+    extern __shared__ uint32_t lds[];
+    __shared__ Scalars sh;
+    if (SF == kQ8)
+        for (uint32_t i = threadIdx.x; i < 512; i += kThreads) lds[i] = qwords[i];
+    if (threadIdx.x == 0) sh = make_scalars(a);
+    __syncthreads();
+    const Scalars s = sh;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tiles_per_chunk = a.chunk / kUTile;
+    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
+        const DevTensor T = tens[ctab[c]];
+        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
+        const int64_t len = min(a.chunk, T.numel - e0);
+        const int64_t ntile = (len + kUTile - 1) / kUTile;
+        for (int64_t tt = wave; tt < ntile; tt += kWaves) {
+            double su = 0.0, sp = 0.0;
+            for (int q = 0; q < kUTile / 256; ++q) {
+                const int64_t i0 = tt * kUTile + q * 256 + lane * 4;   // within the chunk
+                const int n = (int)max((int64_t)0, min((int64_t)4, len - i0));
+                for (int j = 0; j < n; ++j) {
+                    const int64_t e = e0 + i0 + j;
+                    float g = load_grad1<GD>(T.g, e);
+                    float m = read_state<SF>(lds, T.s1, T.a1, true, e);
+                    float v = read_state<SF>(lds, T.s2, T.a2, false, e);
+                    float m2 = OPT == kAdEMAMix ? read_state<SF>(lds, T.s3, T.a3, true, e) : 0.0f;
+                    Mom r = moments<OPT>(s, a, g, m, v, m2);
+                    float p = gld<float>(T.p + e);
+                    su += (double)r.u * (double)r.u;
+                    sp += (double)p * (double)p;
+                }
+            }
+            su = wave_sum(su);
+            sp = wave_sum(sp);
+            if (lane == 0) {
+                const int64_t slot = c * tiles_per_chunk + tt;
+                gst<double>(a.partials + 2 * slot, su);
+                gst<double>(a.partials + 2 * slot + 1, sp);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void unorm_reduce_kernel(const DevTensor *__restrict__ tens,
+                                                              int64_t chunk, const double *partials,
+                                                              double *out)
+{
+    __shared__ double red[kWaves][2];
+    const DevTensor T = tens[blockIdx.x];
+    const int64_t first = T.chunk_begin * (chunk / kUTile);
+    const int64_t nt = (T.numel + kUTile - 1) / kUTile;
+    double su = 0.0, sp = 0.0;
+    for (int64_t i = threadIdx.x; i < nt; i += kThreads) {
+        su += gld<double>(partials + 2 * (first + i));
+        sp += gld<double>(partials + 2 * (first + i) + 1);
+    }
+    su = wave_sum(su);
+    sp = wave_sum(sp);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { red[wave][0] = su; red[wave][1] = sp; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double U = red[0][0], P = red[0][1];
+        for (int w = 1; w < kWaves; ++w) { U += red[w][0]; P += red[w][1]; }
+        gst<double>(out + 2 * (int64_t)T.k, U);
+        gst<double>(out + 2 * (int64_t)T.k + 1, P);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// test hooks
+
+__global__ void debug_philox_kernel(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n,
+                                    uint32_t *out)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        uint64_t j = (uint64_t)(j0 + i);
+        out[i] = philox_word(sr_block(seed, t, k, j >> 2, false), (int)(j & 3));
+    }
+}
+
+__global__ void debug_round_kernel(const float *x, const uint32_t *r, uint16_t *out, int64_t n)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        out[i] = (uint16_t)(r ? bf16_sr(x[i], r[i] & 0xFFFFu) : bf16_rne(x[i]));
+}
+
+__global__ void debug_quantize_kernel(QTabs q, int is_signed, const float *x, uint8_t *out, int64_t n)
+{
+    extern __shared__ uint32_t lds[];
+    for (uint32_t i = threadIdx.x; i < q.nwords; i += blockDim.x) lds[i] = q.words[i];
+    __syncthreads();
+    const QTabParams P = is_signed ? q.s : q.u;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float v = x[i];
+        out[i] = (uint8_t)(v != v ? 0u : q8_lookup(v, lds, P, is_signed != 0));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers (called by opt_api.cpp)
+
+template <int OPT, int GD>
+static hipError_t launch_step_t(int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st)
+{
+    const dim3 G(grid), B(kThreads);
+    switch (fmt) {
+    case kF32: hipLaunchKernelGGL((step_ew_kernel<OPT, GD, kF32>), G, B, 0, st, a.tens, a.chunk_tensor, a); break;
+    case kBF16RN: hipLaunchKernelGGL((step_ew_kernel<OPT, GD, kBF16RN>), G, B, 0, st, a.tens, a.chunk_tensor, a); break;
+    case kBF16SR: hipLaunchKernelGGL((step_ew_kernel<OPT, GD, kBF16SR>), G, B, 0, st, a.tens, a.chunk_tensor, a); break;
+    case kQ8: hipLaunchKernelGGL((step_q8_kernel<OPT, GD>), G, B, lds, st, a.tens, a.chunk_tensor, a.q.words, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st)
+{
+    if (opt == kAdamW) return gd == kGradF32 ? launch_step_t<kAdamW, kGradF32>(fmt, a, grid, lds, st)
+                                             : launch_step_t<kAdamW, kGradBF16>(fmt, a, grid, lds, st);
+    return gd == kGradF32 ? launch_step_t<kAdEMAMix, kGradF32>(fmt, a, grid, lds, st)
+                          : launch_step_t<kAdEMAMix, kGradBF16>(fmt, a, grid, lds, st);
+}
+
+template <int OPT, int GD>
+static hipError_t launch_unorm_t(int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st)
+{
+    const dim3 G(grid), B(kThreads);
+    switch (fmt) {
+    case kF32: hipLaunchKernelGGL((unorm_partials_kernel<OPT, GD, kF32>), G, B, 0, st, a.tens, a.chunk_tensor, a.q.words, a); break;
+    case kBF16RN:
+    case kBF16SR: hipLaunchKernelGGL((unorm_partials_kernel<OPT, GD, kBF16RN>), G, B, 0, st, a.tens, a.chunk_tensor, a.q.words, a); break;
+    case kQ8: hipLaunchKernelGGL((unorm_partials_kernel<OPT, GD, kQ8>), G, B, lds, st, a.tens, a.chunk_tensor, a.q.words, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds,
+                        int ntens, double *out, hipStream_t st)
+{
+    hipError_t e = hipSuccess;
+    if (a.nchunks > 0) {
+        if (opt == kAdamW) e = gd == kGradF32 ? launch_unorm_t<kAdamW, kGradF32>(fmt, a, grid, lds, st)
+                                              : launch_unorm_t<kAdamW, kGradBF16>(fmt, a, grid, lds, st);
+        else e = gd == kGradF32 ? launch_unorm_t<kAdEMAMix, kGradF32>(fmt, a, grid, lds, st)
+                                : launch_unorm_t<kAdEMAMix, kGradBF16>(fmt, a, grid, lds, st);
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(unorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
+                       (const double *)a.partials, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n,
+                               uint32_t *out, hipStream_t st)
+{
+    int64_t blocks = min((int64_t)4096, (n + 255) / 256);
+    hipLaunchKernelGGL(debug_philox_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st,
+                       seed, t, k, j0, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, int64_t n, hipStream_t st)
+{
+    int64_t blocks = min((int64_t)4096, (n + 255) / 256);
+    hipLaunchKernelGGL(debug_round_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st,
+                       x, r, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, uint8_t *out, int64_t n,
+                                 hipStream_t st)
+{
+    int64_t blocks = min((int64_t)1024, (n + 255) / 256);
+    hipLaunchKernelGGL(debug_quantize_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256),
+                       (size_t)q.nwords * 4, st, q, is_signed, x, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace optstep

@@ -1,0 +1,68 @@
+// opt_plan.h -- records shared by the host planner (opt_api.cpp) and the
+// kernels (opt_kernels.hip).  Plain data only.
+#pragma once
+
+#include <stdint.h>
+
+namespace optstep {
+
+constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kQBlock = 256;       // elements per 8-bit absmax block
+constexpr int kUTile = 1024;       // elements per update-norm partial
+
+enum Opt : int { kAdamW = 0, kAdEMAMix = 1 };
+enum Fmt : int { kF32 = 0, kBF16RN = 1, kBF16SR = 2, kQ8 = 3 };
+enum GradT : int { kGradF32 = 0, kGradBF16 = 1 };
+
+// One tensor of a dtype bucket, as the kernels see it (device memory).
+struct alignas(16) DevTensor {
+    float *p;
+    const void *g;
+    void *s1, *s2, *s3;
+    float *a1, *a2, *a3;
+    int64_t numel;
+    int64_t chunk_begin;   // first chunk of this tensor in the bucket's chunk space
+    int32_t k;             // position in the caller's list
+    int32_t pad_[3];
+};
+static_assert(sizeof(DevTensor) == 96, "DevTensor layout");
+
+// 8-bit codebook lookup-table parameters (see opt_qtable in opt_api.cpp).
+// For |x| <= 1 the magnitude bits a = bits(max(|x|, lo_f)) give the bucket
+// b = (a - lo) >> shift and the in-bucket key (a - lo) & mask; a signed table
+// holds nb buckets for x >= 0 followed by nb for x < 0.  Each 32-bit entry is
+// base | thr << 8: code = base + (key' >= thr), key' = key for x >= 0 and
+// mask - key for x < 0.
+struct QTabParams {
+    uint32_t lo;       // bit pattern of the smallest magnitude kept apart
+    uint32_t shift;    // log2 of the bucket width in ulps
+    uint32_t nb;       // buckets per sign
+    uint32_t offset;   // first entry of this table in the packed search area (words)
+};
+
+// Packed 8-bit tables in device memory and LDS (32-bit words):
+//   [0, 256)          signed codebook values (m, m2)
+//   [256, 512)        unsigned codebook values (v)
+//   [512, ...)        search entries: signed table (2*nb) then unsigned (nb)
+struct QTabs {
+    const uint32_t *words;   // device
+    uint32_t nwords;
+    QTabParams s, u;
+};
+
+// Kernel arguments (passed by value).
+struct StepArgs {
+    const DevTensor *tens;
+    const int32_t *chunk_tensor;   // bucket-local tensor of each chunk
+    int64_t nchunks;
+    int64_t chunk;                 // elements per chunk (multiple of 1024)
+    const double *unorm;           // caller's {sum u^2, sum p^2} per tensor k, or null
+    double *partials;              // pre-pass: {sum u^2, sum p^2} per kUTile elements
+    QTabs q;
+    float lr, beta1, beta2, beta3, alpha, eps, wd, max_unorm;
+    int64_t step;
+    uint64_t seed;
+};
+
+}  // namespace optstep

@@ -111,6 +111,19 @@ def device_normal_(tensor, seed, std, *stream):
     return tensor
 
 
+def device_grads(n, device, std, t, k=0, bf16=False, mask_scale=None):
+    """Gradient of tensor k at step t on the device: N(0, std) in fp32, a fixed
+    random subset scaled in fp32 if mask_scale=(frac, factor), then rounded to
+    BF16 by torch's cast if bf16."""
+    import torch
+    g = torch.empty(n, dtype=torch.float32, device=device)
+    device_normal_(g, GRAD_SEED, std, k, t)
+    if mask_scale is not None:
+        frac, factor = mask_scale
+        g[device_mask(n, device, frac, k)] *= factor
+    return g.to(torch.bfloat16) if bf16 else g
+
+
 def device_mask(n, device, frac, k=0):
     import torch
     gen = torch.Generator(device=device)
@@ -169,6 +182,9 @@ WORKLOADS = {
     "adamw_bf16_1g": dict(opt="adamw", fmt="bf16_rn", sizes=[2**30], grad_bf16=True,
                           p_std=0.02, g_std="decay", steps=200,
                           hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)),
+    "adamw_bf16_sr_1g": dict(opt="adamw", fmt="bf16_sr", sizes=[2**30], grad_bf16=True,
+                             p_std=0.02, g_std="decay", steps=200,
+                             hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)),
 }
 
 

@@ -1,0 +1,161 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every function include/opt_step.h declares, rejects bad arguments before any
+device work, plans chunks from sizes only, and its host-compiled helpers (the
+8-bit lookup tables and the reused-reciprocal division the kernels use) agree
+with the oracle and with correctly rounded arithmetic."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+QS, QU = synth.codebook_signed(), synth.codebook_unsigned()
+
+
+@pytest.fixture(scope="module")
+def L():
+    import optimizer_step_amd as osa
+    if not os.path.exists(osa.LIB_PATH):
+        from optimizer_step_amd import build
+        build.build()
+    return osa
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "opt_step.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(opt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert "opt_step_adamw" in names and "opt_precondition_unorm" in names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def _tensor(L, numel=16, p=4096, g=4096, s1=8192, s2=12288, s3=0, gd=0):
+    return [L.OptTensor(p, g, s1, s2, s3 or None, None, None, None, numel, 0, gd)]
+
+
+def _call(L, fn, tensors, fmt=0, hp=None, unorm=None):
+    arr = (L.OptTensor * len(tensors))(*tensors)
+    hp = hp or L.hparams()
+    return getattr(L.lib(), fn)(arr, len(tensors), fmt, hp, unorm, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(hp=dict(step=0)), -1),
+    (dict(hp=dict(beta1=1.0)), -1),
+    (dict(hp=dict(beta2=-0.1)), -1),
+    (dict(fmt=9), -1),
+    (dict(tensor=dict(p=0)), -1),
+    (dict(tensor=dict(numel=-1)), -1),
+    (dict(tensor=dict(p=4100)), -3),
+    (dict(tensor=dict(s2=12296)), -3),
+    (dict(tensor=dict(gd=7)), -1),
+    (dict(fmt=3), -1),                          # 8-bit without codebooks
+    (dict(hp=dict(max_unorm=1.0)), -1),         # bound without norms
+])
+def test_bad_arguments_are_rejected_before_device_work(L, case, status):
+    hp = L.hparams(**case.get("hp", {}))
+    rc = _call(L, "opt_step_adamw", _tensor(L, **case.get("tensor", {})), case.get("fmt", 0), hp)
+    assert rc == status
+    assert L.opt_last_error() != ""
+
+
+def test_ademamix_needs_slow_ema(L):
+    assert _call(L, "opt_step_ademamix", _tensor(L)) == -1
+
+
+def test_bad_codebooks_are_rejected(L):
+    bad = QS.copy()
+    bad[10] = bad[9]
+    for q in (bad, QS * 2):
+        hp = L.hparams(qmap_signed=q, qmap_unsigned=QU)
+        assert _call(L, "opt_step_adamw", _tensor(L), 3, hp) == -1
+    hp = L.hparams(qmap_signed=QS, qmap_unsigned=QS)       # negative entries in the v table
+    assert _call(L, "opt_step_adamw", _tensor(L), 3, hp) == -1
+
+
+def test_empty_call_is_a_no_op(L):
+    assert L.lib().opt_step_adamw(None, 0, 0, L.hparams(), None, None) == 0
+
+
+def test_plan_depends_on_sizes_only(L):
+    chunk, nc = L.opt_debug_plan([0, 1, 1023, 1024, 65537, 6 * 2**20])
+    assert chunk % 1024 == 0
+    assert list(nc) == [0, 1, 1, 1, -(-65537 // chunk), -(-6 * 2**20 // chunk)]
+
+
+def _probe(T):
+    mids = ((T[:-1].astype(np.float64) + T[1:].astype(np.float64)) / 2).astype(np.float32)
+    rng = np.random.default_rng(7)
+    pts = [T, mids, np.nextafter(mids, np.float32(2)), np.nextafter(mids, np.float32(-2)),
+           np.array([0.0, -0.0, 1.0, -1.0, 1e-30, -1e-30, 3e-8, -3e-8, np.nan], dtype=np.float32),
+           rng.uniform(-1, 1, 200000).astype(np.float32),
+           (rng.uniform(-1, 1, 200000) ** 9).astype(np.float32)]
+    x = np.concatenate(pts).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_host_lookup_matches_oracle(L, signed):
+    T = QS if signed else QU
+    x = _probe(T)
+    if not signed:
+        x = np.abs(x)
+    got = L.opt_debug_quantize_host(T, signed, x)
+    ref = oracle.quantize_array(T, x)
+    assert np.array_equal(got, ref)
+
+
+def test_host_lookup_other_codebooks(L):
+    """Other strictly increasing tables in [-1, 1]: uniform (with a midpoint
+    of exactly 0), and random gaps."""
+    rng = np.random.default_rng(3)
+    gaps = np.concatenate([[0.0], rng.uniform(0.5, 1.5, 255)])
+    rand = (-1 + 2 * np.cumsum(gaps) / gaps.sum()).astype(np.float32)
+    for T in (np.linspace(-1, 1, 256).astype(np.float32), rand):
+        assert np.all(np.diff(T.astype(np.float64)) > 0)
+        x = _probe(T)
+        assert np.array_equal(L.opt_debug_quantize_host(T, True, x), oracle.quantize_array(T, x))
+
+
+def test_codebook_too_dense_for_the_table_is_unsupported(L):
+    """Two midpoints closer than the finest bucket cannot share one
+    comparison: such a codebook is refused, not approximated."""
+    T = np.linspace(-1, 1, 256).astype(np.float32)
+    T[200] = np.nextafter(T[201], np.float32(-1))
+    T[199] = np.nextafter(T[200], np.float32(-1))
+    with pytest.raises(L.OptError) as e:
+        L.opt_debug_quantize_host(T, True, np.zeros(1, np.float32))
+    assert e.value.status == -2
+
+
+def test_reused_reciprocal_division_is_correctly_rounded(L):
+    """a / b by two residual corrections of a * RN(1/b) equals the correctly
+    rounded quotient (numpy float32 division), over random operands, divisors
+    with all-ones significands, and dividends next to the divisor."""
+    rng = np.random.default_rng(5)
+    n = 2_000_000
+    b = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(-30, 10, n)).astype(np.float32)
+    a = (b * rng.uniform(-1, 1, n)).astype(np.float32)
+    ones = (np.float32(2) - np.float32(2.0 ** -23)) * (2.0 ** rng.integers(-24, 1, n // 4)).astype(np.float32)
+    b = np.concatenate([b, ones.astype(np.float32), b[:n // 4]])
+    a = np.concatenate([a, (ones * rng.uniform(-1, 1, n // 4)).astype(np.float32),
+                        np.nextafter(b[:n // 4], np.float32(0))])
+    b = b.astype(np.float32)
+    a = a.astype(np.float32)
+    got = L.opt_debug_div_by(a, b)
+    ref = (a / b).astype(np.float32)
+    normal = np.abs(ref) >= np.float32(2.0 ** -126)
+    assert np.array_equal(got[normal].view(np.uint32), ref[normal].view(np.uint32))

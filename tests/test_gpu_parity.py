@@ -1,0 +1,264 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds: several chunks
+and ragged tails, every optimizer x state format x gradient dtype, multi-tensor
+lists with empty tensors, NaN/Inf gradients, determinism, chunk-size
+invariance, resume, and the device test hooks.
+
+Bars: fp32 values within 1e-6 * max(|x|, rms(x)) per element; BF16 nearest
+within one BF16 step per step; stochastic-rounding bits, 8-bit codes and
+absmax, and Philox words bit-exact; update norms within 1e-12 relative."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import Case, compare, fp32_close, nan_equal_bits, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 255, 256, 257, 4095, 4096, 4097, 8191, 8193, 65536, 1_000_003]
+FORMATS = ["f32", "bf16_rn", "bf16_sr", "q8"]
+HP_ADAMW = dict(lr=0.1, weight_decay=0.1, beta1=0.9, beta2=0.999, eps=1e-8)
+HP_ADEMAMIX = dict(lr=1e-2, weight_decay=0.1, beta1=0.9, beta2=0.999, beta3=0.99, alpha=5.0, eps=1e-8)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import optimizer_step_amd as osa
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    osa.lib()                      # raises if the HIP library is missing
+    print(f"device: {torch.cuda.get_device_name(0)}", flush=True)
+    yield
+    osa.opt_debug_set_launch(32768, 8)
+
+
+def _hp(opt):
+    return HP_ADAMW if opt == "adamw" else HP_ADEMAMIX
+
+
+def _run_and_compare(case, label):
+    print(f"case {label}", flush=True)
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    frac = compare(case, dev, ps, st)
+    assert frac >= 0.99, f"only {frac:.4f} of p words bit-identical"
+    return dev, ps, st
+
+
+def test_small_flat_fp32_ten_steps():
+    """One fp32 tensor of 2^16+1 elements, lr = wd = 0.1, 10 steps."""
+    w = synth.WORKLOADS["adamw_f32_small"]
+    case = Case("adamw", "f32", w["sizes"], False, w["steps"], w["hp"], g_std=w["g_std"])
+    _run_and_compare(case, "adamw f32 n=65537 x10")
+
+
+def test_step1_closed_form_on_gpu():
+    """The GPU's first step against p0 (1 - lr wd) - lr g/(|g|+eps) in binary64."""
+    n = 65537
+    case = Case("adamw", "f32", [n], False, 1, HP_ADAMW)
+    dev, _ = case.run_gpu()
+    p = to_host(dev[0]["p"]).astype(np.float64)
+    p0 = case.p0[0].astype(np.float64)
+    g = case.grad(1, 0).astype(np.float64)
+    lr, wd = np.float64(np.float32(0.1)), np.float64(np.float32(0.1))
+    ref = p0 * (1 - lr * wd) - lr * g / (np.abs(g) + np.float64(np.float32(1e-8)))
+    assert np.all(np.abs(p - ref) <= 8 * 2.0 ** -24 * (np.abs(p0) + lr))
+
+
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("grad_bf16", [False, True])
+def test_size_matrix(opt, fmt, grad_bf16):
+    """Every size of the matrix as one multi-tensor call, 3 steps."""
+    case = Case(opt, fmt, SIZES, grad_bf16, 3, _hp(opt))
+    _run_and_compare(case, f"{opt} {fmt} bf16grad={grad_bf16} sizes={SIZES}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_mixed_buckets_and_empty_tensors(fmt):
+    """fp32 and bf16 gradients in one call (two launches), with empty tensors;
+    the tensor position keys stochastic rounding."""
+    sizes = [1000, 0, 4097, 3, 70000, 0, 513]
+    bf = [False, True, True, False, True, False, False]
+    case = Case("adamw", fmt, sizes, bf, 4, HP_ADAMW)
+    _run_and_compare(case, f"mixed buckets {fmt}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_nonfinite_and_zero_gradients(fmt):
+    """NaN, +-Inf and zero gradients propagate as in the oracle (NaN payloads
+    are compared by position only); a NaN poisons its 8-bit block."""
+    def grads(t, k, n):
+        g = synth.grads(n, t, k)
+        if t == 2:
+            g[5] = np.nan
+            g[300] = np.inf
+            g[301] = -np.inf
+            g[600:900] = 0.0
+        return g
+    case = Case("adamw", fmt, [4097, 1500], False, 3, HP_ADAMW, grad_override=grads)
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_late_step_and_zero_decay(fmt):
+    """Step counts far from 1 (bias corrections near 1) and wd = 0."""
+    hp = dict(HP_ADAMW, weight_decay=0.0, lr=1e-3)
+    case = Case("adamw", fmt, [70001], True, 2, hp)
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+    case2 = Case("adamw", fmt, [5000], False, 3, hp)
+    start_t = 997
+    ps, st, _ = case2.run_oracle(start=([p.copy() for p in case2.p0],
+                                        [oracle.state_zeros(fmt, 5000, "adamw", case2.qs, case2.qu)], start_t))
+    dev, _ = case2.run_gpu(t0=start_t)
+    compare(case2, dev, ps, st)
+
+
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_update_norm_prepass(opt, fmt):
+    """max_unorm = 1: the pre-pass norms within 1e-12 relative of the oracle's
+    compensated sums, and the clipped steps within the bars."""
+    hp = dict(_hp(opt), max_unorm=1.0, lr=1e-3)
+    case = Case(opt, fmt, [65537, 0, 3000], [False, False, True], 4, hp)
+    ps, st, norms_o = case.run_oracle()
+    dev, norms_g = case.run_gpu()
+    compare(case, dev, ps, st)
+    for (t, k, u2, p2) in norms_o:
+        g = norms_g[t - 1]
+        assert abs(g[2 * k] - u2) <= 1e-12 * abs(u2), (t, k, g[2 * k], u2)
+        assert abs(g[2 * k + 1] - p2) <= 1e-12 * abs(p2), (t, k)
+    # clipping is active: the scale at step 1 is well below 1
+    s = oracle.unorm_scale(1.0, norms_o[0][2], norms_o[0][3])
+    assert s < 0.1
+
+
+def test_update_norm_is_deterministic():
+    """Ten pre-pass runs over a multi-chunk tensor give identical bits."""
+    import torch
+    import optimizer_step_amd as osa
+    n = 3 * 2**20 + 5
+    dev = [{"p": to_dev(synth.params(n)), "g": to_dev(synth.grads(n, 1)),
+            **osa.state_buffers("f32", n)}]
+    dev[0]["s1"].copy_(to_dev(synth.grads(n, 7)))
+    dev[0]["s2"].copy_(to_dev(np.abs(synth.grads(n, 8, std=1e-2)) ** 2))
+    hp = osa.hparams(step=5, max_unorm=1.0)
+    outs = []
+    for _ in range(10):
+        u = torch.empty(2, dtype=torch.float64, device="cuda")
+        osa.opt_precondition_unorm("adamw", dev, "f32", hp, u)
+        outs.append(u.cpu().numpy().view(np.uint64).copy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_repeat_runs_are_bit_identical(fmt):
+    case = Case("ademamix", fmt, [100_003, 777], True, 3, HP_ADEMAMIX)
+    a = Case.host(case.run_gpu()[0])
+    b = Case.host(case.run_gpu()[0])
+    for x, y in zip(a, b):
+        for key in x:
+            assert nan_equal_bits(x[key], y[key]), key
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_chunk_size_and_grid_do_not_change_results(fmt):
+    import optimizer_step_amd as osa
+    case = Case("adamw", fmt, [300_001, 4097], [False, True], 3, dict(HP_ADAMW, max_unorm=1.0))
+    try:
+        results = []
+        for chunk, wgs in ((32768, 8), (1024, 1), (65536, 3), (4096, 64)):
+            osa.opt_debug_set_launch(chunk, wgs)
+            results.append(Case.host(case.run_gpu()[0]))
+    finally:
+        osa.opt_debug_set_launch(32768, 8)
+    for r in results[1:]:
+        for x, y in zip(results[0], r):
+            for key in x:
+                assert nan_equal_bits(x[key], y[key]), key
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_resume_from_copied_state(fmt):
+    """6 steps equal 3 steps, a copy of every buffer out and back in, and 3
+    more steps: the state lives only in the caller's buffers."""
+    case = Case("ademamix", fmt, [50_001], True, 6, HP_ADEMAMIX)
+    full = Case.host(case.run_gpu(6)[0])
+    dev, _ = case.run_gpu(3)
+    snap = Case.host(dev)
+    dev2 = case.alloc_gpu(start=([s["p"] for s in snap], [{k: v for k, v in s.items() if k != "p"} for s in snap]))
+    part = Case.host(case.run_gpu(3, dev=dev2, t0=3)[0])
+    for x, y in zip(full, part):
+        for key in x:
+            assert nan_equal_bits(x[key], y[key]), key
+
+
+def test_streams_other_than_the_default():
+    import torch
+    case = Case("adamw", "bf16_sr", [20_000], True, 2, HP_ADAMW)
+    ps, st, _ = case.run_oracle()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dev, _ = case.run_gpu(stream=s)
+    compare(case, dev, ps, st)
+
+
+# ---------------------------------------------------------------------------
+# test hooks: the device functions the kernels use
+
+def test_philox_words_match_oracle():
+    import torch
+    import optimizer_step_amd as osa
+    for j0, n, k, t in ((0, 1 << 22, 0, 1), ((1 << 34) - (1 << 20), 1 << 21, 7, 123456), (12345, 1001, 3, 2**31 + 5)):
+        out = torch.empty(n, dtype=torch.int32, device="cuda")
+        osa.opt_debug_philox(synth.SR_SEED, t, k, j0, out)
+        got = out.cpu().numpy().view(np.uint32)
+        ref = oracle.sr_words(synth.SR_SEED, t, k, j0, n)
+        assert np.array_equal(got, ref)
+
+
+def test_bf16_rounding_matches_oracle():
+    import torch
+    import optimizer_step_amd as osa
+    rng = np.random.default_rng(17)
+    hi = (np.arange(65536, dtype=np.uint32) << 16)
+    words = np.concatenate([hi | np.uint32(lo) for lo in (0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF)] +
+                           [rng.integers(0, 2**32, 1 << 21, dtype=np.uint64).astype(np.uint32)])
+    x = words.view(np.float32)
+    r = rng.integers(0, 2**32, x.size, dtype=np.uint64).astype(np.uint32)
+    xd = to_dev(x)
+    rd = torch.from_numpy(r.view(np.int32)).cuda()
+    out = torch.empty(x.size, dtype=torch.int16, device="cuda")
+    osa.opt_debug_round_bf16(xd, None, out)
+    rne = out.cpu().numpy().view(np.uint16)
+    assert nan_equal_bits(rne, oracle.bf16_rne_array(x))
+    osa.opt_debug_round_bf16(xd, rd, out)
+    sr = out.cpu().numpy().view(np.uint16)
+    assert nan_equal_bits(sr, oracle.bf16_sr_array(x, r & 0xFFFF))
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_quantizer_matches_oracle(signed):
+    import torch
+    import optimizer_step_amd as osa
+    T = synth.codebook_signed() if signed else synth.codebook_unsigned()
+    mids = ((T[:-1].astype(np.float64) + T[1:].astype(np.float64)) / 2).astype(np.float32)
+    rng = np.random.default_rng(4)
+    x = np.concatenate([T, mids, np.nextafter(mids, np.float32(2)), np.nextafter(mids, np.float32(-2)),
+                        np.array([0.0, -0.0, 1.0, -1.0, np.nan, 1e-30], dtype=np.float32),
+                        rng.uniform(-1, 1, 1 << 20).astype(np.float32),
+                        (rng.uniform(-1, 1, 1 << 20) ** 9).astype(np.float32)]).astype(np.float32)
+    if not signed:
+        x = np.abs(x)
+    out = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    osa.opt_debug_quantize(T, signed, to_dev(x), out)
+    assert np.array_equal(out.cpu().numpy(), oracle.quantize_array(T, x))
