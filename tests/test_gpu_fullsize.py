@@ -1,0 +1,267 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  Every output the oracle can compute one element (or one
+8-bit block) at a time is checked on a seeded sample that always includes the
+first and last elements of every tensor; the update-norm workload, whose
+scale couples all elements, is replayed in full by the oracle.  Inputs are
+drawn on the device from seeded generators and the oracle is handed exactly
+the sampled input values (never a value the HIP path produced)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import FP32_REL, bf16_ulps, fp32_close, nan_equal_bits, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import optimizer_step_amd as osa
+    assert torch.cuda.is_available()
+    osa.lib()
+    osa.opt_debug_set_launch(32768, 8)      # the benchmark's geometry
+    yield
+    torch.cuda.empty_cache()
+
+
+def _sample_idx(n, count, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.concatenate([np.arange(min(4, n)), np.arange(max(0, n - 5), n),
+                          rng.integers(0, n, count)])
+    return np.unique(idx)
+
+
+def _flat_states(fmt, total, opt, qs, qu):
+    import optimizer_step_amd as osa
+    return osa.state_buffers(fmt, total, opt, qmap_signed=qs, qmap_unsigned=qu)
+
+
+def _views(P, G, states, sizes, fmt):
+    tensors, off = [], 0
+    for n in sizes:
+        d = {"p": P[off:off + n], "g": G[off:off + n]}
+        for key, buf in states.items():
+            d[key] = buf[off // 256:(off + n + 255) // 256] if key.startswith("absmax") else buf[off:off + n]
+        tensors.append(d)
+        off += n
+    return tensors
+
+
+def _gather(t, idx):
+    import torch
+    return to_host(t[torch.from_numpy(idx).cuda()])
+
+
+def test_llama7b_list_adamw_fp32_states():
+    """290 tensors, 6,738,411,520 elements, bf16 gradients, 5 steps, one launch
+    per step; 72 sampled elements per tensor against the oracle."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["adamw_f32_llama7b"]
+    sizes, hp, steps = w["sizes"], w["hp"], w["steps"]
+    total = sum(sizes)
+    offs = np.cumsum([0] + sizes[:-1])
+    print(f"llama7b list: {len(sizes)} tensors, {total} elements", flush=True)
+    P = torch.empty(total, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = _flat_states("f32", total, "adamw", None, None)
+    samples = [_sample_idx(n, 64, 100 + k) + offs[k] for k, n in enumerate(sizes)]
+    allidx = np.concatenate(samples)
+    p0 = _gather(P, allidx)
+    g_hist = []
+    G = None
+    tl = None
+    for t in range(1, steps + 1):
+        del G
+        G = synth.device_grads(total, "cuda", w["g_std"], t, bf16=True)
+        tensors = _views(P, G, st, sizes, "f32")
+        tl = osa.TensorList(tensors)
+        osa.opt_step_adamw(tl, "f32", osa.hparams(step=t, **hp))
+        g_hist.append(_gather(G, allidx))
+    torch.cuda.synchronize()
+    gp, gm, gv = _gather(P, allidx), _gather(st["s1"], allidx), _gather(st["s2"], allidx)
+    # the oracle on each tensor's sample (element-wise, so the sample is exact)
+    pos = 0
+    for k, idx in enumerate(samples):
+        m = idx.size
+        p = p0[pos:pos + m].copy()
+        s = oracle.state_zeros("f32", m)
+        for t in range(1, steps + 1):
+            oracle.step("adamw", "f32", oracle.make_hp(step=t, tensor_index=k, **hp), p,
+                        g_hist[t - 1][pos:pos + m], **s)
+        assert fp32_close(gp[pos:pos + m], p), f"tensor {k}: p"
+        assert fp32_close(gm[pos:pos + m], s["s1"]), f"tensor {k}: m"
+        assert fp32_close(gv[pos:pos + m], s["s2"]), f"tensor {k}: v"
+        pos += m
+    del P, G, st, tensors, tl
+    torch.cuda.empty_cache()
+
+
+def test_q8_one_billion_elements():
+    """2^30 elements, 8-bit blockwise m and v, 10% of gradients x100, 5 steps;
+    64 sampled blocks (first and last included): codes and absmax bit-exact,
+    p within the fp32 bar."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["adamw_q8_1g"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    qs, qu = synth.codebook_signed(), synth.codebook_unsigned()
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = _flat_states("q8", n, "adamw", qs, qu)
+    nb = n // 256
+    blocks = np.unique(np.concatenate([[0, 1, nb - 1], np.random.default_rng(9).integers(0, nb, 61)]))
+    idx = (blocks[:, None] * 256 + np.arange(256)[None, :]).reshape(-1)
+    p0 = _gather(P, idx)
+    g_hist = []
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", w["g_std"], t, bf16=True, mask_scale=w["mask_scale"])
+        tl = osa.TensorList(_views(P, G, st, [n], "q8"))
+        osa.opt_step_adamw(tl, "q8", osa.hparams(step=t, qmap_signed=qs, qmap_unsigned=qu, **hp))
+        g_hist.append(_gather(G, idx))
+        del G
+    torch.cuda.synchronize()
+    p = p0.copy()
+    s = oracle.state_zeros("q8", idx.size, "adamw", qs, qu)
+    for t in range(1, steps + 1):
+        oracle.step("adamw", "q8", oracle.make_hp(step=t, **hp), p, g_hist[t - 1], qs=qs, qu=qu, **s)
+    assert fp32_close(_gather(P, idx), p)
+    assert np.array_equal(_gather(st["s1"], idx), s["s1"])
+    assert np.array_equal(_gather(st["s2"], idx), s["s2"])
+    assert nan_equal_bits(_gather(st["absmax1"], blocks), s["a1"])
+    assert nan_equal_bits(_gather(st["absmax2"], blocks), s["a2"])
+    del P, st
+    torch.cuda.empty_cache()
+
+
+def test_ademamix_268m():
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["ademamix_f32_268m"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = _flat_states("f32", n, "ademamix", None, None)
+    idx = _sample_idx(n, 4096, 12)
+    p0 = _gather(P, idx)
+    g_hist = []
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", w["g_std"], t)
+        osa.opt_step_ademamix(osa.TensorList(_views(P, G, st, [n], "f32")), "f32", osa.hparams(step=t, **hp))
+        g_hist.append(_gather(G, idx))
+        del G
+    torch.cuda.synchronize()
+    p = p0.copy()
+    s = oracle.state_zeros("f32", idx.size, "ademamix")
+    for t in range(1, steps + 1):
+        oracle.step("ademamix", "f32", oracle.make_hp(step=t, **hp), p, g_hist[t - 1], **s)
+    assert fp32_close(_gather(P, idx), p)
+    for key in ("s1", "s2", "s3"):
+        assert fp32_close(_gather(st[key], idx), s[key]), key
+    del P, st
+    torch.cuda.empty_cache()
+
+
+def test_update_norm_268m_full_replay():
+    """AdamW with max_unorm = 1 on 2^28 elements for 10 steps.  The scale ties
+    every element to the norms, so the oracle replays the whole tensor: the
+    pre-pass norms within 1e-12 relative at every step, then p, m and v within
+    the fp32 bar at the end; a repeated pre-pass gives identical bits."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["adamw_f32_unorm_268m"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = _flat_states("f32", n, "adamw", None, None)
+    p = to_host(P).copy()
+    s = oracle.state_zeros("f32", n)
+    unorm = torch.empty(2, dtype=torch.float64, device="cuda")
+    again = torch.empty(2, dtype=torch.float64, device="cuda")
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", w["g_std"], t)
+        tl = osa.TensorList(_views(P, G, st, [n], "f32"))
+        h = osa.hparams(step=t, **hp)
+        osa.opt_precondition_unorm("adamw", tl, "f32", h, unorm)
+        osa.opt_precondition_unorm("adamw", tl, "f32", h, again)
+        osa.opt_step_adamw(tl, "f32", h, unorm)
+        g = to_host(G)
+        hpo = oracle.make_hp(step=t, **hp)
+        u2, p2 = oracle.unorm("adamw", "f32", hpo, p, g, **s)
+        gu = unorm.cpu().numpy()
+        assert np.array_equal(gu.view(np.uint64), again.cpu().numpy().view(np.uint64)), t
+        assert abs(gu[0] - u2) <= 1e-12 * u2 and abs(gu[1] - p2) <= 1e-12 * p2, (t, gu, u2, p2)
+        scale = oracle.unorm_scale(hp["max_unorm"], u2, p2)
+        if t == 1:
+            assert scale < 0.05
+        oracle.step("adamw", "f32", hpo, p, g, scale=scale, **s)
+        print(f"step {t}: scale {scale:.6f}", flush=True)
+        del G
+    torch.cuda.synchronize()
+    assert fp32_close(to_host(P), p)
+    assert fp32_close(to_host(st["s1"]), s["s1"])
+    assert fp32_close(to_host(st["s2"]), s["s2"])
+    del P, st
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["bf16_rn", "bf16_sr"])
+def test_bf16_states_one_billion_200_steps(fmt):
+    """2^30 elements, BF16 m/v, gradient scale decaying 1e-2 -> 1e-4 over 200
+    steps.  Sampled elements: SR bits exact, RN within one BF16 step per step;
+    per-step stalled fraction of v (stored word unchanged) over the whole
+    tensor; under RN with beta2 = 0.999 no stored v ever decreases."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["adamw_bf16_1g"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = _flat_states(fmt, n, "adamw", None, None)
+    idx = _sample_idx(n, 2048, 14)
+    p0 = _gather(P, idx)
+    g_hist = []
+    stalled = []
+    v_prev = st["s2"].clone()
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", synth.decaying_std(t, steps), t, bf16=True)
+        osa.opt_step_adamw(osa.TensorList(_views(P, G, st, [n], fmt)), fmt,
+                           osa.hparams(step=t, seed=synth.SR_SEED, **hp))
+        g_hist.append(_gather(G, idx))
+        v_new = st["s2"]
+        stalled.append(float((v_new.view(torch.int16) == v_prev.view(torch.int16)).float().mean()))
+        if fmt == "bf16_rn" and t > 1:
+            assert bool((v_new.float() >= v_prev.float()).all()), f"v fell at step {t}"
+        v_prev.copy_(v_new)
+        del G
+    torch.cuda.synchronize()
+    # oracle on the sample: contiguous runs keep their element index for SR
+    p = p0.copy()
+    s = oracle.state_zeros(fmt, idx.size)
+    so = []
+    for t in range(1, steps + 1):
+        v_before = s["s2"].copy()
+        hpo = oracle.make_hp(step=t, seed=synth.SR_SEED, **hp)
+        for i, j in enumerate(idx):
+            hpo.index_base = int(j)
+            sl = slice(i, i + 1)
+            sub = {k2: v2[sl] for k2, v2 in s.items()}
+            pp = p[sl]
+            oracle.step("adamw", fmt, hpo, pp, g_hist[t - 1][sl], **sub)
+        so.append(float(np.mean(s["s2"] == v_before)))
+    assert fp32_close(_gather(P, idx), p)
+    gm, gv = _gather(st["s1"], idx), _gather(st["s2"], idx)
+    if fmt == "bf16_sr":
+        assert np.array_equal(gm, s["s1"]) and np.array_equal(gv, s["s2"])
+    else:
+        assert bf16_ulps(gm, s["s1"]).max() <= steps and bf16_ulps(gv, s["s2"]).max() <= steps
+    print(f"{fmt} stalled v fraction (whole tensor) at steps 2,50,100,200: "
+          f"{stalled[1]:.4f} {stalled[49]:.4f} {stalled[99]:.4f} {stalled[199]:.4f}; "
+          f"oracle sample: {so[1]:.4f} {so[49]:.4f} {so[99]:.4f} {so[199]:.4f}", flush=True)
+    # the sample's stall fraction estimates the tensor's
+    for t in (49, 99, 199):
+        assert abs(stalled[t] - so[t]) < 0.05
+    del P, st, v_prev
+    torch.cuda.empty_cache()
