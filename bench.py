@@ -173,6 +173,100 @@ def cpu_baseline(budget_s=12.0):
             "bytes_per_element": 26, "GBps": done * 26 / dt / 1e9}
 
 
+def calibrate(torch, osa, n=1 << 30, reps=3):
+    """The calibration copy: n fp32 read and n written per launch."""
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty(n, dtype=torch.float32, device="cuda")
+    osa.opt_debug_stream([src], [dst])
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        osa.opt_debug_stream([src], [dst])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"kernel": "debug_stream_kernel (1 read, 1 write)", "bytes_read": 4 * n, "bytes_written": 4 * n,
+            "ms": ms, "GBps": 8 * n / ms / 1e6}
+
+
+# ---------------------------------------------------------------------------
+# profile summaries (from rocprofv3 csv output)
+
+HEADLINE_KERNEL = "step_ew_kernel<0, 1, 0>"
+CALIB_KERNEL = "debug_stream_kernel"
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd_trace, cmd_fetch, cmd_write):
+    """Write profiles/step_ew_adamw_llama7b_{trace,counters}.txt and
+    profiles/step_counters.json from the csv files of three rocprofv3 runs:
+    --kernel-trace --stats, --pmc FETCH_SIZE and --pmc WRITE_SIZE (counter
+    values are KiB per dispatch).  The calibration copy kernel moves a known
+    number of bytes, and its counter readings give the scale factors."""
+    import csv
+    import glob
+    import statistics
+
+    def one(pattern):
+        files = glob.glob(pattern, recursive=True)
+        if not files:
+            raise SystemExit(f"no file matches {pattern}")
+        return files[0]
+
+    stats = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    head = [r for r in stats if HEADLINE_KERNEL in r["Name"]][0]
+    calib = [r for r in stats if CALIB_KERNEL in r["Name"]][0]
+
+    def counters(d, name):
+        rows = list(csv.DictReader(open(one(os.path.join(d, "**", "*counter_collection.csv")))))
+        pick = lambda k: [float(r["Counter_Value"]) for r in rows if k in r["Kernel_Name"] and r["Counter_Name"] == name]
+        return pick(HEADLINE_KERNEL), pick(CALIB_KERNEL)
+
+    f_step, f_cal = counters(fetch_dir, "FETCH_SIZE")
+    w_step, w_cal = counters(write_dir, "WRITE_SIZE")
+    n_cal = 1 << 30
+    cal_bytes = 4 * n_cal                      # read and also written per launch
+    kib = 1024.0
+    fetch_scale = cal_bytes / (statistics.median(f_cal) * kib)
+    write_scale = cal_bytes / (statistics.median(w_cal) * kib)
+    rd = statistics.median(f_step) * kib * fetch_scale
+    wr = statistics.median(w_step) * kib * write_scale
+    elems = sum(n for _, n in __import__("synth").llama7b_shapes())
+    alg_r, alg_w = 14 * elems, 12 * elems
+    avg_ms = float(head["AverageNs"]) / 1e6
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_trace.txt"), "w") as f:
+        f.write("rocprofv3 kernel statistics: AdamW step over the Llama-7B-shaped list (290 tensors,\n"
+                f"6,738,411,520 elements; fp32 p/m/v, bf16 g), plus the calibration copy kernel.\n"
+                f"command: {cmd_trace}\n\n")
+        f.write(f"{'kernel':48s} {'calls':>6s} {'avg ms':>10s} {'min ms':>10s} {'max ms':>10s}\n")
+        for r in (head, calib):
+            nm = HEADLINE_KERNEL if r is head else CALIB_KERNEL
+            f.write(f"{nm:48s} {r['Calls']:>6s} {float(r['AverageNs'])/1e6:10.3f} "
+                    f"{float(r['MinNs'])/1e6:10.3f} {float(r['MaxNs'])/1e6:10.3f}\n")
+        f.write(f"\nstep kernel: {alg_r + alg_w:.4e} algorithmic bytes per launch / {avg_ms:.3f} ms = "
+                f"{(alg_r + alg_w) / avg_ms / 1e6:.0f} GB/s ({(alg_r + alg_w) / avg_ms / 1e6 / PEAK_GBPS:.1%} of 8 TB/s)\n")
+    with open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_counters.txt"), "w") as f:
+        f.write("rocprofv3 HBM byte counters (KiB per dispatch), one counter per run.\n"
+                f"commands:\n  {cmd_fetch}\n  {cmd_write}\n\n")
+        f.write(f"calibration copy (debug_stream_kernel, 2^30 fp32 read + written = {cal_bytes} B each way):\n"
+                f"  FETCH_SIZE {statistics.median(f_cal):.1f} KiB -> scale {fetch_scale:.4f}\n"
+                f"  WRITE_SIZE {statistics.median(w_cal):.1f} KiB -> scale {write_scale:.4f}\n")
+        f.write(f"step kernel ({HEADLINE_KERNEL}), per launch:\n"
+                f"  FETCH_SIZE {statistics.median(f_step):.1f} KiB x scale = {rd:.4e} B (algorithmic reads {alg_r:.4e} B, ratio {rd / alg_r:.4f})\n"
+                f"  WRITE_SIZE {statistics.median(w_step):.1f} KiB x scale = {wr:.4e} B (algorithmic writes {alg_w:.4e} B, ratio {wr / alg_w:.4f})\n"
+                f"  HBM traffic {rd + wr:.4e} B per launch vs {alg_r + alg_w:.4e} B algorithmic\n")
+    summary = {"kernel_source_hash": kernel_hash(), "fetch_scale": fetch_scale, "write_scale": write_scale,
+               "workloads": {"adamw_f32_llama7b": {"kernel": HEADLINE_KERNEL, "hbm_bytes_per_launch": rd + wr,
+                                                   "read_bytes": rd, "write_bytes": wr,
+                                                   "trace_avg_ms": avg_ms}},
+               "commands": [cmd_trace, cmd_fetch, cmd_write]}
+    with open(COUNTERS, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_counters.txt")).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,7 +274,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="all", help="'all', 'none', or comma-separated workload names")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run the plain copy kernel (2^30 fp32 read + written, 3 launches) whose "
+                         "HBM counters scale the step kernel's")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from three rocprofv3 output folders and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        base = "python bench.py --rows none --no-cpu --calibrate"
+        summarize_profiles(*args.summarize_profiles,
+                           cmd_trace="rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
+                                     f"{base} --steps 10 --warmup 3",
+                           cmd_fetch=f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- {base} --steps 2 --warmup 1",
+                           cmd_write=f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- {base} --steps 2 --warmup 1")
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the step shards with no exchange; see the design notes)", file=sys.stderr)
@@ -208,6 +315,7 @@ def main():
               file=sys.stderr, flush=True)
         rows.append(r)
 
+    calib = calibrate(torch, osa) if args.calibrate else None
     cpu = None if args.no_cpu else cpu_baseline()
     traffic = counter_traffic(head, main_row["elements"])
     gb_launch = main_row["bytes_per_element"] * main_row["elements"]
@@ -239,6 +347,8 @@ def main():
         "ms_median": main_row["ms_median"], "ms_p10": main_row["ms_p10"], "ms_p90": main_row["ms_p90"],
         "rows": rows,
     }
+    if calib is not None:
+        out["calibration"] = calib
     print(json.dumps(out), flush=True)
 
 

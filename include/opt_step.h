@@ -189,9 +189,17 @@ int opt_debug_quantize_host(const float *qmap, int32_t is_signed, const float *x
  * Each b[i] must have |b|, 1/|b| in [2^-124, 2^124] (OPT_EINVAL otherwise). */
 int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n);
 
+/* Calibration: dst[j][i] = sum_k src[k][i] for i < n over fp32 device arrays
+ * (0..6 sources, 1..6 destinations, 16-byte aligned, n a multiple of 4), a
+ * plain streaming kernel with the step's access pattern and no arithmetic,
+ * used to read the achievable bandwidth and to scale HBM byte counters. */
+int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, int32_t ndst, int64_t n,
+                     void *stream);
+
 /* Launch geometry for all later calls in this process: elements per chunk (a
  * positive multiple of 1024) and persistent workgroups per compute unit
- * (1..64).  Results do not depend on either. */
+ * (1..64, or 0 for as many as fit, the default).  Results do not depend on
+ * either. */
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);
 
 #ifdef __cplusplus

@@ -76,6 +76,7 @@ def lib():
             "opt_debug_quantize_host": ([vp, i32, vp, vp, i64], i32),
             "opt_debug_div_by": ([vp, vp, vp, i64], i32),
             "opt_debug_set_launch": ([i64, i32], i32),
+            "opt_debug_stream": ([vp, i32, vp, i32, i64, vp], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -214,6 +215,13 @@ def opt_debug_div_by(a, b):
     out = np.zeros(a.size, dtype=np.float32)
     _check(lib().opt_debug_div_by(a.ctypes.data, b.ctypes.data, out.ctypes.data, a.size))
     return out
+
+
+def opt_debug_stream(srcs, dsts, stream=None):
+    n = dsts[0].numel()
+    S = (ctypes.c_void_p * max(1, len(srcs)))(*[t.data_ptr() for t in srcs])
+    D = (ctypes.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
+    return _check(lib().opt_debug_stream(S, len(srcs), D, len(dsts), n, _stream(stream)))
 
 
 def opt_debug_set_launch(chunk, wgs_per_cu):

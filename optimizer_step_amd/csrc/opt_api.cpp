@@ -17,14 +17,17 @@
 
 namespace optstep {
 
-hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st);
-hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds, int ntens,
+hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds,
+                       hipStream_t st);
+hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, int ntens,
                         double *out, hipStream_t st);
 hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, uint32_t *out,
                                hipStream_t st);
 hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, int64_t n, hipStream_t st);
 hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, uint8_t *out, int64_t n,
                                  hipStream_t st);
+hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *dst, int ndst, int64_t n,
+                               const LaunchGeom &lg, hipStream_t st);
 
 namespace {
 
@@ -50,7 +53,7 @@ int hip_fail(hipError_t e, const char *what)
 // launch configuration
 
 int64_t g_chunk = 32768;      // elements per chunk; multiple of 1024
-int g_wgs_per_cu = 8;         // persistent grid size per compute unit
+int g_wgs_per_cu = 0;         // persistent workgroups per compute unit (0: occupancy)
 
 constexpr int kMaxDevices = 64;
 constexpr int kSlots = 16;
@@ -417,11 +420,7 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     return a;
 }
 
-int grid_for(const Workspace &w, int64_t nchunks)
-{
-    int64_t cap = (int64_t)w.ncu * g_wgs_per_cu;
-    return (int)std::max<int64_t>(1, std::min(nchunks, cap));
-}
+LaunchGeom geom(const Workspace &w) { return LaunchGeom{w.ncu, g_wgs_per_cu}; }
 
 // The shared body of the step and the pre-pass.
 int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp, const double *unorm,
@@ -476,17 +475,16 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
             lds = (size_t)a.q.nwords * 4;
         }
         hipError_t e;
-        const int grid = grid_for(*w, a.nchunks);
         if (pre) {
             a.partials = w->partials;
-            e = launch_unorm(opt, gd, fmt, a, grid, q8 ? 2048 : 0, (int)bk.tens.size(), unorm_out, st);
+            e = launch_unorm(opt, gd, fmt, a, geom(*w), q8 ? 2048 : 0, (int)bk.tens.size(), unorm_out, st);
             if (e == hipSuccess) {
                 w->partials_used = true;
                 w->partials_stream = st;
                 e = hipEventRecord(w->partials_ev, st);
             }
         } else {
-            e = launch_step(opt, gd, fmt, a, grid, lds, st);
+            e = launch_step(opt, gd, fmt, a, geom(*w), lds, st);
         }
         if (e != hipSuccess) return hip_fail(e, pre ? "norm pre-pass launch" : "step launch");
         if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
@@ -635,10 +633,31 @@ int64_t opt_debug_plan(const int64_t *numels, int64_t n, int64_t *chunks_out)
     return g_chunk;
 }
 
+int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, int32_t ndst, int64_t n,
+                     void *stream)
+{
+    if (nsrc < 0 || nsrc > 6 || ndst < 1 || ndst > 6 || n < 0 || n % 4 != 0)
+        return fail(OPT_EINVAL, "need 0..6 sources, 1..6 destinations and n a multiple of 4");
+    if ((nsrc > 0 && !src) || !dst) return fail(OPT_EINVAL, "NULL array list");
+    for (int k = 0; k < nsrc; ++k)
+        if (!src[k] || !aligned(src[k], 16)) return fail(OPT_EALIGN, "source %d not 16-byte aligned", k);
+    for (int k = 0; k < ndst; ++k)
+        if (!dst[k] || !aligned(dst[k], 16)) return fail(OPT_EALIGN, "destination %d not 16-byte aligned", k);
+    if (n == 0) return OPT_OK;
+    Workspace *w;
+    int rc;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if ((rc = workspace(w)) != OPT_OK) return rc;
+    }
+    hipError_t e = launch_debug_stream(src, nsrc, dst, ndst, n, geom(*w), (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "debug stream launch");
+}
+
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu)
 {
     if (chunk <= 0 || chunk % 1024 != 0) return fail(OPT_EINVAL, "chunk must be a positive multiple of 1024");
-    if (wgs_per_cu <= 0 || wgs_per_cu > 64) return fail(OPT_EINVAL, "wgs_per_cu must be in [1, 64]");
+    if (wgs_per_cu < 0 || wgs_per_cu > 64) return fail(OPT_EINVAL, "wgs_per_cu must be in [0, 64]");
     std::lock_guard<std::mutex> lock(g_mu);
     g_chunk = chunk;
     g_wgs_per_cu = wgs_per_cu;

@@ -25,6 +25,36 @@ __device__ __forceinline__ V gld(const void *p) { return *(const OPT_GLOBAL V *)
 template <class V>
 __device__ __forceinline__ void gst(void *p, V v) { *(OPT_GLOBAL V *)p = v; }
 
+// Streaming accesses of the per-element arrays (p, g, states): each byte is
+// touched once per step, so they carry the non-temporal hint (measured on
+// MI355X: +2-4% step bandwidth over plain accesses).
+#ifndef OPT_NT_LOAD
+#define OPT_NT_LOAD 1
+#endif
+#ifndef OPT_NT_STORE
+#define OPT_NT_STORE 1
+#endif
+
+template <class V>
+__device__ __forceinline__ V sld(const void *p)
+{
+#if OPT_NT_LOAD
+    return __builtin_nontemporal_load((const OPT_GLOBAL V *)p);
+#else
+    return *(const OPT_GLOBAL V *)p;
+#endif
+}
+
+template <class V>
+__device__ __forceinline__ void sst(void *p, V v)
+{
+#if OPT_NT_STORE
+    __builtin_nontemporal_store(v, (OPT_GLOBAL V *)p);
+#else
+    *(OPT_GLOBAL V *)p = v;
+#endif
+}
+
 __host__ __device__ inline uint32_t fbits(float x)
 {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -16,6 +16,27 @@
 
 namespace optstep {
 
+#ifndef OPT_EW_GROUPS
+#define OPT_EW_GROUPS 4
+#endif
+constexpr int kEwGroups = OPT_EW_GROUPS;   // groups of four in flight per lane
+
+#ifndef OPT_XCD_REMAP
+#define OPT_XCD_REMAP 0
+#endif
+
+// The chunk a workgroup starts at.  Workgroups are dealt to the 8 XCDs in
+// turn; with the remap, the workgroups of one XCD take a contiguous run of
+// each round's chunks instead of every 8th chunk.
+__device__ __forceinline__ int64_t first_chunk()
+{
+#if OPT_XCD_REMAP
+    const unsigned g = gridDim.x, b = blockIdx.x;
+    if (g % 8 == 0) return (int64_t)(b % 8) * (g / 8) + b / 8;
+#endif
+    return blockIdx.x;
+}
+
 // ---------------------------------------------------------------------------
 // element groups of four
 
@@ -23,10 +44,10 @@ template <int GD>
 __device__ __forceinline__ void load_grad4(const void *g, int64_t e, float out[4])
 {
     if (GD == kGradF32) {
-        f4 x = gld<f4>((const float *)g + e);
+        f4 x = sld<f4>((const float *)g + e);
         out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
     } else {
-        u2 w = gld<u2>((const uint16_t *)g + e);
+        u2 w = sld<u2>((const uint16_t *)g + e);
         out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
         out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
     }
@@ -43,10 +64,10 @@ template <int SF>
 __device__ __forceinline__ void load_state4(const void *s, int64_t e, float out[4])
 {
     if (SF == kF32) {
-        f4 x = gld<f4>((const float *)s + e);
+        f4 x = sld<f4>((const float *)s + e);
         out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
     } else {
-        u2 w = gld<u2>((const uint16_t *)s + e);
+        u2 w = sld<u2>((const uint16_t *)s + e);
         out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
         out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
     }
@@ -65,12 +86,12 @@ template <int SF>
 __device__ __forceinline__ void store_state4(void *s, int64_t e, const float x[4], const uint32_t r[4])
 {
     if (SF == kF32) {
-        gst<f4>((float *)s + e, f4{x[0], x[1], x[2], x[3]});
+        sst<f4>((float *)s + e, f4{x[0], x[1], x[2], x[3]});
     } else {
         uint32_t h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) h[i] = SF == kBF16SR ? bf16_sr(x[i], r[i]) : bf16_rne(x[i]);
-        gst<u2>((uint16_t *)s + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        sst<u2>((uint16_t *)s + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
     }
 }
 
@@ -91,7 +112,7 @@ struct Group {
 template <int OPT, int GD, int SF>
 __device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, Group &x)
 {
-    f4 pv = gld<f4>(T.p + e);
+    f4 pv = sld<f4>(T.p + e);
     x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
     load_grad4<GD>(T.g, e, x.g);
     load_state4<SF>(T.s1, e, x.m);
@@ -122,7 +143,7 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
             rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
         }
     }
-    gst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
+    sst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
     store_state4<SF>(T.s1, e, mo, rm);
     store_state4<SF>(T.s2, e, vo, rv);
     if (OPT == kAdEMAMix) store_state4<SF>(T.s3, e, m2o, rm2);
@@ -157,22 +178,22 @@ __global__ __launch_bounds__(kThreads) void step_ew_kernel(const DevTensor *__re
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
-    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
+    for (int64_t c = first_chunk(); c < a.nchunks; c += gridDim.x) {
         const DevTensor T = tens[ctab[c]];
         const int64_t e0 = (c - T.chunk_begin) * a.chunk;
         const int64_t len = min(a.chunk, T.numel - e0);
         const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
         const int64_t ngroups = len >> 2;
         int64_t i = threadIdx.x;
-        // two groups per iteration: both groups' loads are issued before any math
-        for (; i + kThreads < ngroups; i += 2 * kThreads) {
-            Group x0, x1;
-            ew_load<OPT, GD, SF>(T, e0 + 4 * i, x0);
-            ew_load<OPT, GD, SF>(T, e0 + 4 * (i + kThreads), x1);
-            ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, lam, x0);
-            ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (i + kThreads), lam, x1);
+        // kEwGroups groups per iteration: all their loads are issued before any math
+        for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
+            Group x[kEwGroups];
+#pragma unroll
+            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF>(T, e0 + 4 * (i + u * kThreads), x[u]);
+#pragma unroll
+            for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
         }
-        if (i < ngroups) {
+        for (; i < ngroups; i += kThreads) {
             Group x0;
             ew_load<OPT, GD, SF>(T, e0 + 4 * i, x0);
             ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, lam, x0);
@@ -242,12 +263,12 @@ __global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__re
             const uint8_t *S1 = (const uint8_t *)T.s1, *S2 = (const uint8_t *)T.s2,
                           *S3 = (const uint8_t *)T.s3;
             if (nmine == 4) {
-                f4 pv = gld<f4>(T.p + e);
+                f4 pv = sld<f4>(T.p + e);
                 p[0] = pv.x; p[1] = pv.y; p[2] = pv.z; p[3] = pv.w;
                 load_grad4<GD>(T.g, e, g);
-                cm = gld<uint32_t>(S1 + e);
-                cv = gld<uint32_t>(S2 + e);
-                if (OPT == kAdEMAMix) cm2 = gld<uint32_t>(S3 + e);
+                cm = sld<uint32_t>(S1 + e);
+                cv = sld<uint32_t>(S2 + e);
+                if (OPT == kAdEMAMix) cm2 = sld<uint32_t>(S3 + e);
             } else {
                 for (int i = 0; i < nmine; ++i) {
                     p[i] = gld<float>(T.p + e + i);
@@ -299,10 +320,10 @@ __global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__re
             }
             uint8_t *W1 = (uint8_t *)T.s1, *W2 = (uint8_t *)T.s2, *W3 = (uint8_t *)T.s3;
             if (nmine == 4) {
-                gst<f4>(T.p + e, f4{p[0], p[1], p[2], p[3]});
-                gst<uint32_t>(W1 + e, om);
-                gst<uint32_t>(W2 + e, ov);
-                if (OPT == kAdEMAMix) gst<uint32_t>(W3 + e, om2);
+                sst<f4>(T.p + e, f4{p[0], p[1], p[2], p[3]});
+                sst<uint32_t>(W1 + e, om);
+                sst<uint32_t>(W2 + e, ov);
+                if (OPT == kAdEMAMix) sst<uint32_t>(W3 + e, om2);
             } else {
                 for (int i = 0; i < nmine; ++i) {
                     gst<float>(T.p + e + i, p[i]);
@@ -339,6 +360,23 @@ __device__ __forceinline__ float read_state(const uint32_t *lds, const void *s, 
     return load_state1<SF == kF32 ? kF32 : kBF16RN>(s, e);
 }
 
+// Four consecutive state values starting at e (a multiple of 4, so one 8-bit
+// block holds all four).
+template <int SF>
+__device__ __forceinline__ void read_state4(const uint32_t *lds, const void *s, const float *amax,
+                                            bool is_signed, int64_t e, float out[4])
+{
+    if (SF == kQ8) {
+        const float *tab = (const float *)lds + (is_signed ? 0 : 256);
+        const uint32_t c = sld<uint32_t>((const uint8_t *)s + e);
+        const float A = gld<float>(amax + e / kQBlock);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = tab[(c >> (8 * i)) & 0xFFu] * A;
+    } else {
+        load_state4<SF == kF32 ? kF32 : kBF16RN>(s, e, out);
+    }
+}
+
 template <int OPT, int GD, int SF>
 __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTensor *__restrict__ tens,
                                                                   const int32_t *__restrict__ ctab,
@@ -362,19 +400,44 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
         const int64_t ntile = (len + kUTile - 1) / kUTile;
         for (int64_t tt = wave; tt < ntile; tt += kWaves) {
             double su = 0.0, sp = 0.0;
-            for (int q = 0; q < kUTile / 256; ++q) {
-                const int64_t i0 = tt * kUTile + q * 256 + lane * 4;   // within the chunk
-                const int n = (int)max((int64_t)0, min((int64_t)4, len - i0));
-                for (int j = 0; j < n; ++j) {
-                    const int64_t e = e0 + i0 + j;
-                    float g = load_grad1<GD>(T.g, e);
-                    float m = read_state<SF>(lds, T.s1, T.a1, true, e);
-                    float v = read_state<SF>(lds, T.s2, T.a2, false, e);
-                    float m2 = OPT == kAdEMAMix ? read_state<SF>(lds, T.s3, T.a3, true, e) : 0.0f;
-                    Mom r = moments<OPT>(s, a, g, m, v, m2);
-                    float p = gld<float>(T.p + e);
-                    su += (double)r.u * (double)r.u;
-                    sp += (double)p * (double)p;
+            const bool full = (tt + 1) * kUTile <= len;
+            if (full) {
+                // the whole tile is in range: 4 groups of 4 per lane, loads first
+                float p[4][4], g[4][4], m[4][4], v[4][4], m2[4][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t e = e0 + tt * kUTile + q * 256 + lane * 4;
+                    f4 pv = sld<f4>(T.p + e);
+                    p[q][0] = pv.x; p[q][1] = pv.y; p[q][2] = pv.z; p[q][3] = pv.w;
+                    load_grad4<GD>(T.g, e, g[q]);
+                    read_state4<SF>(lds, T.s1, T.a1, true, e, m[q]);
+                    read_state4<SF>(lds, T.s2, T.a2, false, e, v[q]);
+                    if (OPT == kAdEMAMix) read_state4<SF>(lds, T.s3, T.a3, true, e, m2[q]);
+                    else m2[q][0] = m2[q][1] = m2[q][2] = m2[q][3] = 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        Mom r = moments<OPT>(s, a, g[q][j], m[q][j], v[q][j], m2[q][j]);
+                        su += (double)r.u * (double)r.u;
+                        sp += (double)p[q][j] * (double)p[q][j];
+                    }
+            } else {
+                for (int q = 0; q < kUTile / 256; ++q) {
+                    const int64_t i0 = tt * kUTile + q * 256 + lane * 4;   // within the chunk
+                    const int n = (int)max((int64_t)0, min((int64_t)4, len - i0));
+                    for (int j = 0; j < n; ++j) {
+                        const int64_t e = e0 + i0 + j;
+                        float g = load_grad1<GD>(T.g, e);
+                        float m = read_state<SF>(lds, T.s1, T.a1, true, e);
+                        float v = read_state<SF>(lds, T.s2, T.a2, false, e);
+                        float m2 = OPT == kAdEMAMix ? read_state<SF>(lds, T.s3, T.a3, true, e) : 0.0f;
+                        Mom r = moments<OPT>(s, a, g, m, v, m2);
+                        float p = gld<float>(T.p + e);
+                        su += (double)r.u * (double)r.u;
+                        sp += (double)p * (double)p;
+                    }
                 }
             }
             su = wave_sum(su);
@@ -447,54 +510,143 @@ __global__ void debug_quantize_kernel(QTabs q, int is_signed, const float *x, ui
     }
 }
 
+template <class K>
+static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks);
+
+// Calibration stream: dst[j][i] = sum_k src[k][i] over fp32 arrays, 4 per
+// lane per access, grid-stride.  With nsrc reads and ndst writes it moves the
+// same mix of bytes as a step without the arithmetic.
+struct StreamArgs {
+    const float *src[6];
+    float *dst[6];
+    int nsrc, ndst;
+    int64_t n;   // elements, multiple of 4
+};
+
+#ifndef OPT_STREAM_UNROLL
+#define OPT_STREAM_UNROLL 4
+#endif
+
+__global__ __launch_bounds__(kThreads) void debug_stream_kernel(StreamArgs a)
+{
+    constexpr int U = OPT_STREAM_UNROLL;
+    const int64_t ng = a.n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+    for (; i + (U - 1) * stride < ng; i += U * stride) {
+        f4 acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (k < a.nsrc) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[u] += sld<f4>(a.src[k] + 4 * (i + u * stride));
+            }
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (k < a.ndst) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) sst<f4>(a.dst[k] + 4 * (i + u * stride), acc[u]);
+            }
+    }
+    for (; i < ng; i += stride) {
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (k < a.nsrc) acc += sld<f4>(a.src[k] + 4 * i);
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (k < a.ndst) sst<f4>(a.dst[k] + 4 * i, acc);
+    }
+}
+
+hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *dst, int ndst, int64_t n,
+                               const LaunchGeom &lg, hipStream_t st)
+{
+    StreamArgs a{};
+    for (int k = 0; k < nsrc; ++k) a.src[k] = src[k];
+    for (int k = 0; k < ndst; ++k) a.dst[k] = dst[k];
+    a.nsrc = nsrc;
+    a.ndst = ndst;
+    a.n = n;
+    const int64_t groups = (n / 4 + kThreads - 1) / kThreads;
+    const int grid = grid_size(debug_stream_kernel, 0, lg, groups);
+    hipLaunchKernelGGL(debug_stream_kernel, dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // launchers (called by opt_api.cpp)
 
-template <int OPT, int GD>
-static hipError_t launch_step_t(int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st)
+// Persistent grid: the workgroups that fit on the device at once (the
+// kernel's occupancy times the compute units), unless the caller fixed a
+// per-CU count; never more workgroups than chunks.
+template <class K>
+static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks)
 {
-    const dim3 G(grid), B(kThreads);
-    switch (fmt) {
-    case kF32: hipLaunchKernelGGL((step_ew_kernel<OPT, GD, kF32>), G, B, 0, st, a.tens, a.chunk_tensor, a); break;
-    case kBF16RN: hipLaunchKernelGGL((step_ew_kernel<OPT, GD, kBF16RN>), G, B, 0, st, a.tens, a.chunk_tensor, a); break;
-    case kBF16SR: hipLaunchKernelGGL((step_ew_kernel<OPT, GD, kBF16SR>), G, B, 0, st, a.tens, a.chunk_tensor, a); break;
-    case kQ8: hipLaunchKernelGGL((step_q8_kernel<OPT, GD>), G, B, lds, st, a.tens, a.chunk_tensor, a.q.words, a); break;
-    default: return hipErrorInvalidValue;
+    int per_cu = lg.wgs_per_cu;
+    if (per_cu <= 0) {
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, lds) != hipSuccess || occ < 1)
+            occ = 1;
+        per_cu = occ;
     }
+    return (int)std::max<int64_t>(1, std::min<int64_t>(nchunks, (int64_t)lg.ncu * per_cu));
+}
+
+template <class K, class... Args>
+static hipError_t launch_persistent(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, hipStream_t st,
+                                    Args... args)
+{
+    const int grid = grid_size(kernel, lds, lg, nchunks);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, st, args...);
     return hipGetLastError();
 }
 
-hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st)
+template <int OPT, int GD>
+static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
-    if (opt == kAdamW) return gd == kGradF32 ? launch_step_t<kAdamW, kGradF32>(fmt, a, grid, lds, st)
-                                             : launch_step_t<kAdamW, kGradBF16>(fmt, a, grid, lds, st);
-    return gd == kGradF32 ? launch_step_t<kAdEMAMix, kGradF32>(fmt, a, grid, lds, st)
-                          : launch_step_t<kAdEMAMix, kGradBF16>(fmt, a, grid, lds, st);
+    const int64_t nc = a.nchunks;
+    switch (fmt) {
+    case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kQ8: return launch_persistent(step_q8_kernel<OPT, GD>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
+{
+    if (opt == kAdamW) return gd == kGradF32 ? launch_step_t<kAdamW, kGradF32>(fmt, a, lg, lds, st)
+                                             : launch_step_t<kAdamW, kGradBF16>(fmt, a, lg, lds, st);
+    return gd == kGradF32 ? launch_step_t<kAdEMAMix, kGradF32>(fmt, a, lg, lds, st)
+                          : launch_step_t<kAdEMAMix, kGradBF16>(fmt, a, lg, lds, st);
 }
 
 template <int OPT, int GD>
-static hipError_t launch_unorm_t(int fmt, const StepArgs &a, int grid, size_t lds, hipStream_t st)
+static hipError_t launch_unorm_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
-    const dim3 G(grid), B(kThreads);
+    const int64_t nc = a.nchunks;
     switch (fmt) {
-    case kF32: hipLaunchKernelGGL((unorm_partials_kernel<OPT, GD, kF32>), G, B, 0, st, a.tens, a.chunk_tensor, a.q.words, a); break;
+    case kF32: return launch_persistent(unorm_partials_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     case kBF16RN:
-    case kBF16SR: hipLaunchKernelGGL((unorm_partials_kernel<OPT, GD, kBF16RN>), G, B, 0, st, a.tens, a.chunk_tensor, a.q.words, a); break;
-    case kQ8: hipLaunchKernelGGL((unorm_partials_kernel<OPT, GD, kQ8>), G, B, lds, st, a.tens, a.chunk_tensor, a.q.words, a); break;
+    case kBF16SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kQ8: return launch_persistent(unorm_partials_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
-hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, int grid, size_t lds,
+hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds,
                         int ntens, double *out, hipStream_t st)
 {
     hipError_t e = hipSuccess;
     if (a.nchunks > 0) {
-        if (opt == kAdamW) e = gd == kGradF32 ? launch_unorm_t<kAdamW, kGradF32>(fmt, a, grid, lds, st)
-                                              : launch_unorm_t<kAdamW, kGradBF16>(fmt, a, grid, lds, st);
-        else e = gd == kGradF32 ? launch_unorm_t<kAdEMAMix, kGradF32>(fmt, a, grid, lds, st)
-                                : launch_unorm_t<kAdEMAMix, kGradBF16>(fmt, a, grid, lds, st);
+        if (opt == kAdamW) e = gd == kGradF32 ? launch_unorm_t<kAdamW, kGradF32>(fmt, a, lg, lds, st)
+                                              : launch_unorm_t<kAdamW, kGradBF16>(fmt, a, lg, lds, st);
+        else e = gd == kGradF32 ? launch_unorm_t<kAdEMAMix, kGradF32>(fmt, a, lg, lds, st)
+                                : launch_unorm_t<kAdEMAMix, kGradBF16>(fmt, a, lg, lds, st);
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(unorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,

@@ -51,6 +51,13 @@ struct QTabs {
     QTabParams s, u;
 };
 
+// Launch geometry: compute units, and persistent workgroups per compute unit
+// (0: as many as the kernel's occupancy allows).
+struct LaunchGeom {
+    int ncu;
+    int wgs_per_cu;
+};
+
 // Kernel arguments (passed by value).
 struct StepArgs {
     const DevTensor *tens;

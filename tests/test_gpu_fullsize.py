@@ -21,7 +21,7 @@ def gpu():
     import optimizer_step_amd as osa
     assert torch.cuda.is_available()
     osa.lib()
-    osa.opt_debug_set_launch(32768, 8)      # the benchmark's geometry
+    osa.opt_debug_set_launch(32768, 0)      # the benchmark's geometry
     yield
     torch.cuda.empty_cache()
 

@@ -33,7 +33,7 @@ def gpu():
     osa.lib()                      # raises if the HIP library is missing
     print(f"device: {torch.cuda.get_device_name(0)}", flush=True)
     yield
-    osa.opt_debug_set_launch(32768, 8)
+    osa.opt_debug_set_launch(32768, 0)
 
 
 def _hp(opt):
@@ -176,11 +176,11 @@ def test_chunk_size_and_grid_do_not_change_results(fmt):
     case = Case("adamw", fmt, [300_001, 4097], [False, True], 3, dict(HP_ADAMW, max_unorm=1.0))
     try:
         results = []
-        for chunk, wgs in ((32768, 8), (1024, 1), (65536, 3), (4096, 64)):
+        for chunk, wgs in ((32768, 0), (1024, 1), (65536, 3), (4096, 64), (32768, 8)):
             osa.opt_debug_set_launch(chunk, wgs)
             results.append(Case.host(case.run_gpu()[0]))
     finally:
-        osa.opt_debug_set_launch(32768, 8)
+        osa.opt_debug_set_launch(32768, 0)
     for r in results[1:]:
         for x, y in zip(results[0], r):
             for key in x:
