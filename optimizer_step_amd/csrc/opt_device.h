@@ -160,28 +160,38 @@ __host__ __device__ inline bool div_by_ok(float b)
 }
 
 // ---------------------------------------------------------------------------
-// 8-bit code of x against a codebook's lookup table (layout in opt_plan.h).
-// x must not be NaN (callers map NaN to code 0).  Magnitudes above 1 read as
-// 1, which keeps the nearest-entry code (entries lie in [-1, 1]); an unsigned
-// table gives code 0 to x <= 0 (every midpoint is above 0).
+// 8-bit code of x against a codebook's lookup table (layout in opt_plan.h),
+// for x with |x| <= 1 that is not NaN (and, for an unsigned table, x >= 0 or
+// -0).  The magnitude max(|x|, lo) picks a bucket that holds at most one
+// threshold, so the code is the bucket's base plus one comparison.  +0 reads
+// the x < 0 half: a midpoint of exactly 0 sits between +0 and the smallest
+// positive float, and that half holds code(0) for m -> 0.
+__host__ __device__ inline uint32_t q8_code(float x, const uint32_t *tab, const QTabParams &P,
+                                            bool is_signed)
+{
+    const uint32_t b = fbits(x);
+    const float ax = fmaxf(fabsf(x), bitsf(P.lo));   // all |x| < lo share one code
+    const uint32_t off = fbits(ax) - P.lo;
+    const uint32_t mask = (1u << P.shift) - 1u;
+    const uint32_t bucket = off >> P.shift;
+    uint32_t key = off & mask;
+    const bool neg = is_signed && (int32_t)b <= 0;
+    const uint32_t e = tab[P.offset + bucket + (neg ? P.nb : 0u)];
+    key = neg ? mask - key : key;
+    return (e & 0xFFu) + (key >= (e >> 8) ? 1u : 0u);
+}
+
+// The same for any x that is not NaN (callers map NaN to code 0): magnitudes
+// above 1 read as 1, which keeps the nearest-entry code (entries lie in
+// [-1, 1]), and an unsigned table gives code 0 to every x <= 0 (all its
+// midpoints are above 0).
 __host__ __device__ inline uint32_t q8_lookup(float x, const uint32_t *tab, const QTabParams &P,
                                               bool is_signed)
 {
-    uint32_t b = fbits(x);
+    const uint32_t b = fbits(x);
     if (!is_signed && (b >> 31)) return 0u;
-    uint32_t mag = b & 0x7FFFFFFFu;
-    mag = mag < P.lo ? P.lo : mag;                    // all |x| < lo share one code
-    mag = mag > 0x3F800000u ? 0x3F800000u : mag;
-    uint32_t off = mag - P.lo;
-    uint32_t mask = (1u << P.shift) - 1u;
-    uint32_t bucket = off >> P.shift;
-    uint32_t key = off & mask;
-    // +0 reads the x < 0 half: a midpoint of exactly 0 sits between +0 and
-    // the smallest positive float, and that half holds code(0) for m -> 0
-    const bool neg = is_signed && (int32_t)b <= 0;
-    uint32_t e = tab[P.offset + bucket + (neg ? P.nb : 0u)];
-    key = neg ? (mask - key) : key;
-    return (e & 0xFFu) + (key >= (e >> 8) ? 1u : 0u);
+    if ((b & 0x7FFFFFFFu) > 0x3F800000u) x = bitsf((b & 0x80000000u) | 0x3F800000u);
+    return q8_code(x, tab, P, is_signed);
 }
 
 // ---------------------------------------------------------------------------
@@ -264,6 +274,34 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
     return r;
 }
 
+// The same moments, with the direction u (which only feeds the parameter
+// update, never a stored moment, code or rounding bit) formed with the
+// hardware reciprocal and square root (each within 1 ulp) instead of
+// correctly rounded division and square root: u is within a few ulp of the
+// exact recipe, far inside the parameter tolerance.  v_hat below 2^-96 (where
+// the hardware square root loses accuracy) or NaN falls back to the exact
+// recipe for the whole wave.
+template <int OPT>
+__device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a, float g, float m,
+                                            float v, float m2)
+{
+    Mom r;
+    float gg = g * g;
+    r.m = a.beta1 * m + s.om1 * g;
+    r.v = a.beta2 * v + s.om2 * gg;
+    const float mh = r.m * s.rc1;
+    const float vh = r.v * s.rc2;
+    const float rden = __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(vh) + a.eps);
+    if (OPT == kAdEMAMix) {
+        r.m2 = a.beta3 * m2 + s.om3 * g;
+        r.u = (mh + a.alpha * r.m2) * rden;
+    } else {
+        r.m2 = 0.0f;
+        r.u = mh * rden;
+    }
+    return r;
+}
+
 // Decay-first: both terms from the previous p (bitsandbytes PR "Fix decoupled
 // weight decay ordering in the CUDA Adam/AdEMAMix kernels", intro).
 __device__ __forceinline__ float apply_update(float p, float d, float lam, float u)
@@ -295,6 +333,20 @@ __device__ __forceinline__ float wave_max(float x)
     float r2 = __int_as_float(__builtin_amdgcn_readlane(v, 32));
     float r3 = __int_as_float(__builtin_amdgcn_readlane(v, 48));
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Max over the 64 lanes of unsigned words (for |x| bit patterns this is the
+// numeric max, and any NaN pattern beats every number, so a NaN anywhere
+// poisons the result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 // Sum over the 64 lanes in a fixed butterfly order; every lane ends with the

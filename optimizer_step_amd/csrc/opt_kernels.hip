@@ -214,16 +214,156 @@ template <bool SIGNED>
 __device__ __forceinline__ uint32_t quant(float x_num, float A, float yA, bool fast,
                                           const uint32_t *lds, const QTabParams &P)
 {
-    if (fast) return q8_lookup(div_by(x_num, A, yA), lds, P, SIGNED);
+    if (fast) return q8_code(div_by(x_num, A, yA), lds, P, SIGNED);
     float x = A == 0.0f ? 0.0f : x_num / A;
     if (x != x) return 0u;
     return q8_lookup(x, lds, P, SIGNED);
 }
 
-__device__ __forceinline__ float absmax_of(const float x[4], bool any_nan)
+#ifndef OPT_Q8_PAIR
+#define OPT_Q8_PAIR 0
+#endif
+
+// The block absmax from this lane's four values: max |x| as unsigned bit
+// patterns across the wave, so NaN poisons it.  Values of lanes past the end
+// of a short block are passed as 0.
+__device__ __forceinline__ float block_absmax(const float x[4])
 {
-    float m = wave_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
-    return any_nan ? __builtin_nanf("") : m;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+    return bitsf(wave_max_u32(m));
+}
+
+// One lane's four elements of a 256-element block, as loaded.
+struct QIn {
+    float p[4], g[4];
+    uint32_t cm, cv, cm2;
+    float A1, A2, A3;
+};
+
+template <int OPT, int GD, bool FULL>
+__device__ __forceinline__ void q8_load(const DevTensor &T, int64_t eb, int nmine, int lane, QIn &x)
+{
+    if (FULL) nmine = 4;
+    const int64_t e = eb + lane * 4;
+    const int64_t blk = eb / kQBlock;
+    const uint8_t *S1 = (const uint8_t *)T.s1, *S2 = (const uint8_t *)T.s2, *S3 = (const uint8_t *)T.s3;
+    if (nmine == 4) {
+        f4 pv = sld<f4>(T.p + e);
+        x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
+        load_grad4<GD>(T.g, e, x.g);
+        x.cm = sld<uint32_t>(S1 + e);
+        x.cv = sld<uint32_t>(S2 + e);
+        x.cm2 = OPT == kAdEMAMix ? sld<uint32_t>(S3 + e) : 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x.p[i] = 0.0f; x.g[i] = 0.0f; }
+        x.cm = x.cv = x.cm2 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < nmine) {
+                x.p[i] = gld<float>(T.p + e + i);
+                x.g[i] = load_grad1<GD>(T.g, e + i);
+                x.cm |= (uint32_t)gld<uint8_t>(S1 + e + i) << (8 * i);
+                x.cv |= (uint32_t)gld<uint8_t>(S2 + e + i) << (8 * i);
+                if (OPT == kAdEMAMix) x.cm2 |= (uint32_t)gld<uint8_t>(S3 + e + i) << (8 * i);
+            }
+        }
+    }
+    x.A1 = gld<float>(T.a1 + blk);
+    x.A2 = gld<float>(T.a2 + blk);
+    x.A3 = OPT == kAdEMAMix ? gld<float>(T.a3 + blk) : 0.0f;
+}
+
+// FULL: every lane holds four elements (all blocks but a tensor's short last one).
+template <int OPT, bool FULL>
+__device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
+                                          const uint32_t *lds, int64_t eb, int nmine, int lane, float lam,
+                                          const QIn &x)
+{
+    if (FULL) nmine = 4;
+    const float *TS = (const float *)lds;
+    const float *TU = TS + 256;
+    const int64_t e = eb + lane * 4;
+    const int64_t blk = eb / kQBlock;
+    float m_in[4], v_in[4], m2_in[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m_in[i] = TS[(x.cm >> (8 * i)) & 0xFFu] * x.A1;
+        v_in[i] = TU[(x.cv >> (8 * i)) & 0xFFu] * x.A2;
+        m2_in[i] = OPT == kAdEMAMix ? TS[(x.cm2 >> (8 * i)) & 0xFFu] * x.A3 : 0.0f;
+    }
+    // The stored moments are exact binary32; only the direction u (for p)
+    // takes the fast path, unless some v_hat in the wave is tiny or NaN.
+    float p[4], mo[4], vo[4], m2o[4];
+    float vmin = 1.0f;
+    Mom r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = moments_fast<OPT>(s, a, x.g[i], m_in[i], v_in[i], m2_in[i]);
+        vmin = fminf(vmin, r[i].v * s.rc2);
+    }
+    if (__any(!(vmin >= 0x1p-96f))) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = moments<OPT>(s, a, x.g[i], m_in[i], v_in[i], m2_in[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool valid = i < nmine;
+        p[i] = apply_update(x.p[i], s.d, lam, r[i].u);
+        mo[i] = valid ? r[i].m : 0.0f;
+        vo[i] = valid ? r[i].v : 0.0f;
+        m2o[i] = valid ? r[i].m2 : 0.0f;
+    }
+    const QTabParams PS = a.q.s, PU = a.q.u;
+    const float Am = block_absmax(mo), Av = block_absmax(vo);
+    const bool fm = div_by_ok(Am), fv = div_by_ok(Av);
+    const float ym = fm ? 1.0f / Am : 0.0f, yv = fv ? 1.0f / Av : 0.0f;
+    uint32_t om = 0, ov = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        om |= quant<true>(mo[i], Am, ym, fm, lds, PS) << (8 * i);
+        ov |= quant<false>(vo[i], Av, yv, fv, lds, PU) << (8 * i);
+    }
+    uint32_t om2 = 0;
+    float Am2 = 0.0f;
+    if (OPT == kAdEMAMix) {
+        Am2 = block_absmax(m2o);
+        const bool f2 = div_by_ok(Am2);
+        const float y2 = f2 ? 1.0f / Am2 : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) om2 |= quant<true>(m2o[i], Am2, y2, f2, lds, PS) << (8 * i);
+    }
+    uint8_t *W1 = (uint8_t *)T.s1, *W2 = (uint8_t *)T.s2, *W3 = (uint8_t *)T.s3;
+    if (nmine == 4) {
+        sst<f4>(T.p + e, f4{p[0], p[1], p[2], p[3]});
+        sst<uint32_t>(W1 + e, om);
+        sst<uint32_t>(W2 + e, ov);
+        if (OPT == kAdEMAMix) sst<uint32_t>(W3 + e, om2);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < nmine) {
+                gst<float>(T.p + e + i, p[i]);
+                gst<uint8_t>(W1 + e + i, (uint8_t)(om >> (8 * i)));
+                gst<uint8_t>(W2 + e + i, (uint8_t)(ov >> (8 * i)));
+                if (OPT == kAdEMAMix) gst<uint8_t>(W3 + e + i, (uint8_t)(om2 >> (8 * i)));
+            }
+        }
+    }
+    if (lane == 0) {
+        gst<float>(T.a1 + blk, Am);
+        gst<float>(T.a2 + blk, Av);
+        if (OPT == kAdEMAMix) gst<float>(T.a3 + blk, Am2);
+    }
+}
+
+// Lanes of this wave that hold elements of the block starting at eb.
+__device__ __forceinline__ int q8_mine(const DevTensor &T, int64_t eb, int lane)
+{
+    const int nvalid = (int)min((int64_t)kQBlock, T.numel - eb);
+    return max(0, min(4, nvalid - lane * 4));
 }
 
 template <int OPT, int GD>
@@ -238,11 +378,8 @@ __global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__re
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
-    const float *TS = (const float *)lds;
-    const float *TU = TS + 256;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const QTabParams PS = a.q.s, PU = a.q.u;
 
     for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
         const DevTensor T = tens[ctab[c]];
@@ -250,93 +387,29 @@ __global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__re
         const int64_t len = min(a.chunk, T.numel - e0);
         const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
         const int64_t nblk = (len + kQBlock - 1) / kQBlock;
-        for (int64_t b = wave; b < nblk; b += kWaves) {
-            const int64_t eb = e0 + b * kQBlock;           // first element of the block
-            const int64_t blk = eb / kQBlock;              // its absmax slot
-            const int nvalid = (int)min((int64_t)kQBlock, T.numel - eb);
-            const int i0 = lane * 4;
-            const int nmine = max(0, min(4, nvalid - i0));
-            const int64_t e = eb + i0;
-
-            float p[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f};
-            uint32_t cm = 0, cv = 0, cm2 = 0;
-            const uint8_t *S1 = (const uint8_t *)T.s1, *S2 = (const uint8_t *)T.s2,
-                          *S3 = (const uint8_t *)T.s3;
-            if (nmine == 4) {
-                f4 pv = sld<f4>(T.p + e);
-                p[0] = pv.x; p[1] = pv.y; p[2] = pv.z; p[3] = pv.w;
-                load_grad4<GD>(T.g, e, g);
-                cm = sld<uint32_t>(S1 + e);
-                cv = sld<uint32_t>(S2 + e);
-                if (OPT == kAdEMAMix) cm2 = sld<uint32_t>(S3 + e);
-            } else {
-                for (int i = 0; i < nmine; ++i) {
-                    p[i] = gld<float>(T.p + e + i);
-                    g[i] = load_grad1<GD>(T.g, e + i);
-                    cm |= (uint32_t)gld<uint8_t>(S1 + e + i) << (8 * i);
-                    cv |= (uint32_t)gld<uint8_t>(S2 + e + i) << (8 * i);
-                    if (OPT == kAdEMAMix) cm2 |= (uint32_t)gld<uint8_t>(S3 + e + i) << (8 * i);
-                }
-            }
-            const float A1 = gld<float>(T.a1 + blk), A2 = gld<float>(T.a2 + blk);
-            const float A3 = OPT == kAdEMAMix ? gld<float>(T.a3 + blk) : 0.0f;
-
-            float mo[4], vo[4], m2o[4];
-            bool nan_m = false, nan_v = false, nan_m2 = false;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m = TS[(cm >> (8 * i)) & 0xFFu] * A1;
-                float v = TU[(cv >> (8 * i)) & 0xFFu] * A2;
-                float m2 = OPT == kAdEMAMix ? TS[(cm2 >> (8 * i)) & 0xFFu] * A3 : 0.0f;
-                Mom r = moments<OPT>(s, a, g[i], m, v, m2);
-                const bool valid = i < nmine;
-                p[i] = apply_update(p[i], s.d, lam, r.u);
-                mo[i] = valid ? r.m : 0.0f;
-                vo[i] = valid ? r.v : 0.0f;
-                m2o[i] = valid ? r.m2 : 0.0f;
-                nan_m |= mo[i] != mo[i];
-                nan_v |= vo[i] != vo[i];
-                nan_m2 |= m2o[i] != m2o[i];
-            }
-            // block absmax: wave max, poisoned by any NaN in the block
-            const float Am = absmax_of(mo, __any(nan_m));
-            const float Av = absmax_of(vo, __any(nan_v));
-            const bool fm = div_by_ok(Am), fv = div_by_ok(Av);
-            const float ym = fm ? 1.0f / Am : 0.0f, yv = fv ? 1.0f / Av : 0.0f;
-            uint32_t om = 0, ov = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                om |= quant<true>(mo[i], Am, ym, fm, lds, PS) << (8 * i);
-                ov |= quant<false>(vo[i], Av, yv, fv, lds, PU) << (8 * i);
-            }
-            uint32_t om2 = 0;
-            float Am2 = 0.0f;
-            if (OPT == kAdEMAMix) {
-                Am2 = absmax_of(m2o, __any(nan_m2));
-                const bool f2 = div_by_ok(Am2);
-                const float y2 = f2 ? 1.0f / Am2 : 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) om2 |= quant<true>(m2o[i], Am2, y2, f2, lds, PS) << (8 * i);
-            }
-            uint8_t *W1 = (uint8_t *)T.s1, *W2 = (uint8_t *)T.s2, *W3 = (uint8_t *)T.s3;
-            if (nmine == 4) {
-                sst<f4>(T.p + e, f4{p[0], p[1], p[2], p[3]});
-                sst<uint32_t>(W1 + e, om);
-                sst<uint32_t>(W2 + e, ov);
-                if (OPT == kAdEMAMix) sst<uint32_t>(W3 + e, om2);
-            } else {
-                for (int i = 0; i < nmine; ++i) {
-                    gst<float>(T.p + e + i, p[i]);
-                    gst<uint8_t>(W1 + e + i, (uint8_t)(om >> (8 * i)));
-                    gst<uint8_t>(W2 + e + i, (uint8_t)(ov >> (8 * i)));
-                    if (OPT == kAdEMAMix) gst<uint8_t>(W3 + e + i, (uint8_t)(om2 >> (8 * i)));
-                }
-            }
-            if (lane == 0) {
-                gst<float>(T.a1 + blk, Am);
-                gst<float>(T.a2 + blk, Av);
-                if (OPT == kAdEMAMix) gst<float>(T.a3 + blk, Am2);
-            }
+        const int64_t nfull = len / kQBlock;
+        int64_t b = wave;
+#if OPT_Q8_PAIR
+        // two full blocks per wave per iteration: both blocks' loads first
+        for (; b + kWaves < nfull; b += 2 * kWaves) {
+            QIn x0, x1;
+            q8_load<OPT, GD, true>(T, e0 + b * kQBlock, 4, lane, x0);
+            q8_load<OPT, GD, true>(T, e0 + (b + kWaves) * kQBlock, 4, lane, x1);
+            q8_finish<OPT, true>(a, s, T, lds, e0 + b * kQBlock, 4, lane, lam, x0);
+            q8_finish<OPT, true>(a, s, T, lds, e0 + (b + kWaves) * kQBlock, 4, lane, lam, x1);
+        }
+#endif
+        for (; b < nfull; b += kWaves) {
+            QIn x0;
+            q8_load<OPT, GD, true>(T, e0 + b * kQBlock, 4, lane, x0);
+            q8_finish<OPT, true>(a, s, T, lds, e0 + b * kQBlock, 4, lane, lam, x0);
+        }
+        if (b < nblk) {   // the tensor's short last block
+            const int64_t eb = e0 + b * kQBlock;
+            const int nm = q8_mine(T, eb, lane);
+            QIn x0;
+            q8_load<OPT, GD, false>(T, eb, nm, lane, x0);
+            q8_finish<OPT, false>(a, s, T, lds, eb, nm, lane, lam, x0);
         }
     }
 }
