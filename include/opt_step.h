@@ -197,7 +197,7 @@ int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, i
                      void *stream);
 
 /* Launch geometry for all later calls in this process: elements per chunk (a
- * positive multiple of 1024) and persistent workgroups per compute unit
+ * positive multiple of 1024, at most 2^24) and persistent workgroups per compute unit
  * (1..64, or 0 for as many as fit, the default).  Results do not depend on
  * either. */
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);

@@ -656,7 +656,8 @@ int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, i
 
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu)
 {
-    if (chunk <= 0 || chunk % 1024 != 0) return fail(OPT_EINVAL, "chunk must be a positive multiple of 1024");
+    if (chunk <= 0 || chunk % 1024 != 0 || chunk > (1 << 24))
+        return fail(OPT_EINVAL, "chunk must be a positive multiple of 1024, at most 2^24");
     if (wgs_per_cu < 0 || wgs_per_cu > 64) return fail(OPT_EINVAL, "wgs_per_cu must be in [0, 64]");
     std::lock_guard<std::mutex> lock(g_mu);
     g_chunk = chunk;

@@ -165,20 +165,20 @@ __host__ __device__ inline bool div_by_ok(float b)
 // -0).  The magnitude max(|x|, lo) picks a bucket that holds at most one
 // threshold, so the code is the bucket's base plus one comparison.  +0 reads
 // the x < 0 half: a midpoint of exactly 0 sits between +0 and the smallest
-// positive float, and that half holds code(0) for m -> 0.
+// positive float, and that half holds code(0) for m -> 0.  For x < 0 the
+// in-bucket key is mirrored (xor with the bucket mask flips only the low
+// bits, so the bucket index is unchanged).
 __host__ __device__ inline uint32_t q8_code(float x, const uint32_t *tab, const QTabParams &P,
                                             bool is_signed)
 {
     const uint32_t b = fbits(x);
-    const float ax = fmaxf(fabsf(x), bitsf(P.lo));   // all |x| < lo share one code
-    const uint32_t off = fbits(ax) - P.lo;
+    uint32_t mag = b & 0x7FFFFFFFu;
+    mag = mag > P.lo ? mag : P.lo;                     // all |x| < lo share one code
     const uint32_t mask = (1u << P.shift) - 1u;
-    const uint32_t bucket = off >> P.shift;
-    uint32_t key = off & mask;
     const bool neg = is_signed && (int32_t)b <= 0;
-    const uint32_t e = tab[P.offset + bucket + (neg ? P.nb : 0u)];
-    key = neg ? mask - key : key;
-    return (e & 0xFFu) + (key >= (e >> 8) ? 1u : 0u);
+    const uint32_t off = (mag - P.lo) ^ (neg ? mask : 0u);
+    const uint32_t e = tab[(neg ? P.offset + P.nb : P.offset) + (off >> P.shift)];
+    return (e & 0xFFu) + ((off & mask) >= (e >> 8) ? 1u : 0u);
 }
 
 // The same for any x that is not NaN (callers map NaN to code 0): magnitudes
@@ -314,39 +314,20 @@ __device__ __forceinline__ float apply_update(float p, float d, float lam, float
 // ---------------------------------------------------------------------------
 // Wave64 reductions.
 
-// Max over the 64 lanes (IEEE maxNum: NaN inputs are skipped; callers track
-// NaN separately).  DPP row exchanges within each 16-lane row, then the four
-// row results are read across.
-__device__ __forceinline__ float wave_max(float x)
-{
-    int v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
-    v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
-    v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false))); // row_ror 4
-    v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false))); // row_ror 8
-    v = __float_as_int(x);
-    float r0 = __int_as_float(__builtin_amdgcn_readlane(v, 0));
-    float r1 = __int_as_float(__builtin_amdgcn_readlane(v, 16));
-    float r2 = __int_as_float(__builtin_amdgcn_readlane(v, 32));
-    float r3 = __int_as_float(__builtin_amdgcn_readlane(v, 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 // Max over the 64 lanes of unsigned words (for |x| bit patterns this is the
 // numeric max, and any NaN pattern beats every number, so a NaN anywhere
 // poisons the result).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+    // each step is one v_max_u32 with a DPP source: quad_perm [1,0,3,2], [2,3,0,1],
+    // then row_ror 4 and 8 leave every lane of a 16-lane row with the row max
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));
     const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
     const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    return max(max(r0, r1), max(r2, r3));
+    return __builtin_amdgcn_readfirstlane(max(max(r0, r1), max(r2, r3)));
 }
 
 // Sum over the 64 lanes in a fixed butterfly order; every lane ends with the

@@ -206,23 +206,27 @@ __global__ __launch_bounds__(kThreads) void step_ew_kernel(const DevTensor *__re
 // ---------------------------------------------------------------------------
 // 8-bit blockwise states
 
-// Code of one fp32 moment against its block absmax A.  fast: A and 1/A are
-// normal, so div_by gives the correctly rounded m'/A and |x| <= 1; otherwise
-// x = 0 for A = 0, else the correctly rounded m'/A, and a NaN quotient (A NaN
-// or infinite) gets code 0.
+// Codes of this lane's four fp32 moments against their block absmax A (a
+// wave-uniform value).  When A and 1/A are normal, div_by gives the correctly
+// rounded x = m'/A (|x| <= 1); otherwise x = 0 for A = 0, else the correctly
+// rounded m'/A, and a NaN quotient (A NaN or infinite) gets code 0.
 template <bool SIGNED>
-__device__ __forceinline__ uint32_t quant(float x_num, float A, float yA, bool fast,
-                                          const uint32_t *lds, const QTabParams &P)
+__device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint32_t *lds, const QTabParams &P)
 {
-    if (fast) return q8_code(div_by(x_num, A, yA), lds, P, SIGNED);
-    float x = A == 0.0f ? 0.0f : x_num / A;
-    if (x != x) return 0u;
-    return q8_lookup(x, lds, P, SIGNED);
+    uint32_t out = 0;
+    if (div_by_ok(A)) {
+        const float y = 1.0f / A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out |= q8_code(div_by(x[i], A, y), lds, P, SIGNED) << (8 * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float q = A == 0.0f ? 0.0f : x[i] / A;
+            out |= (q != q ? 0u : q8_lookup(q, lds, P, SIGNED)) << (8 * i);
+        }
+    }
+    return out;
 }
-
-#ifndef OPT_Q8_PAIR
-#define OPT_Q8_PAIR 0
-#endif
 
 // The block absmax from this lane's four values: max |x| as unsigned bit
 // patterns across the wave, so NaN poisons it.  Values of lanes past the end
@@ -235,6 +239,30 @@ __device__ __forceinline__ float block_absmax(const float x[4])
     return bitsf(wave_max_u32(m));
 }
 
+// One chunk's arrays, offset to the chunk's first element (absmax to its
+// first block): wave-uniform base pointers, indexed with 32-bit offsets.
+struct QChunk {
+    float *p;
+    const uint8_t *g;      // bytes
+    uint8_t *s1, *s2, *s3;
+    float *a1, *a2, *a3;
+};
+
+template <int GD>
+__device__ __forceinline__ QChunk q8_chunk(const DevTensor &T, int64_t e0)
+{
+    QChunk c;
+    c.p = T.p + e0;
+    c.g = (const uint8_t *)T.g + e0 * (GD == kGradF32 ? 4 : 2);
+    c.s1 = (uint8_t *)T.s1 + e0;
+    c.s2 = (uint8_t *)T.s2 + e0;
+    c.s3 = (uint8_t *)T.s3 + e0;
+    c.a1 = T.a1 + e0 / kQBlock;
+    c.a2 = T.a2 + e0 / kQBlock;
+    c.a3 = T.a3 + e0 / kQBlock;
+    return c;
+}
+
 // One lane's four elements of a 256-element block, as loaded.
 struct QIn {
     float p[4], g[4];
@@ -242,20 +270,25 @@ struct QIn {
     float A1, A2, A3;
 };
 
+// Block b of the chunk (elements 256*b ..); lanes own 4 elements each.
 template <int OPT, int GD, bool FULL>
-__device__ __forceinline__ void q8_load(const DevTensor &T, int64_t eb, int nmine, int lane, QIn &x)
+__device__ __forceinline__ void q8_load(const QChunk &C, uint32_t b, int nmine, int lane, QIn &x)
 {
     if (FULL) nmine = 4;
-    const int64_t e = eb + lane * 4;
-    const int64_t blk = eb / kQBlock;
-    const uint8_t *S1 = (const uint8_t *)T.s1, *S2 = (const uint8_t *)T.s2, *S3 = (const uint8_t *)T.s3;
+    const uint32_t e = b * kQBlock + lane * 4;
     if (nmine == 4) {
-        f4 pv = sld<f4>(T.p + e);
+        f4 pv = sld<f4>(C.p + e);
         x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
-        load_grad4<GD>(T.g, e, x.g);
-        x.cm = sld<uint32_t>(S1 + e);
-        x.cv = sld<uint32_t>(S2 + e);
-        x.cm2 = OPT == kAdEMAMix ? sld<uint32_t>(S3 + e) : 0u;
+        if (GD == kGradF32) {
+            f4 gv = sld<f4>(C.g + 4 * e);
+            x.g[0] = gv.x; x.g[1] = gv.y; x.g[2] = gv.z; x.g[3] = gv.w;
+        } else {
+            u2 w = sld<u2>(C.g + 2 * e);
+            x.g[0] = bf16_lo(w.x); x.g[1] = bf16_hi(w.x); x.g[2] = bf16_lo(w.y); x.g[3] = bf16_hi(w.y);
+        }
+        x.cm = sld<uint32_t>(C.s1 + e);
+        x.cv = sld<uint32_t>(C.s2 + e);
+        x.cm2 = OPT == kAdEMAMix ? sld<uint32_t>(C.s3 + e) : 0u;
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) { x.p[i] = 0.0f; x.g[i] = 0.0f; }
@@ -263,30 +296,29 @@ __device__ __forceinline__ void q8_load(const DevTensor &T, int64_t eb, int nmin
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (i < nmine) {
-                x.p[i] = gld<float>(T.p + e + i);
-                x.g[i] = load_grad1<GD>(T.g, e + i);
-                x.cm |= (uint32_t)gld<uint8_t>(S1 + e + i) << (8 * i);
-                x.cv |= (uint32_t)gld<uint8_t>(S2 + e + i) << (8 * i);
-                if (OPT == kAdEMAMix) x.cm2 |= (uint32_t)gld<uint8_t>(S3 + e + i) << (8 * i);
+                x.p[i] = gld<float>(C.p + e + i);
+                x.g[i] = GD == kGradF32 ? gld<float>(C.g + 4 * (e + i)) : bf16_lo(gld<uint16_t>(C.g + 2 * (e + i)));
+                x.cm |= (uint32_t)gld<uint8_t>(C.s1 + e + i) << (8 * i);
+                x.cv |= (uint32_t)gld<uint8_t>(C.s2 + e + i) << (8 * i);
+                if (OPT == kAdEMAMix) x.cm2 |= (uint32_t)gld<uint8_t>(C.s3 + e + i) << (8 * i);
             }
         }
     }
-    x.A1 = gld<float>(T.a1 + blk);
-    x.A2 = gld<float>(T.a2 + blk);
-    x.A3 = OPT == kAdEMAMix ? gld<float>(T.a3 + blk) : 0.0f;
+    x.A1 = gld<float>(C.a1 + b);
+    x.A2 = gld<float>(C.a2 + b);
+    x.A3 = OPT == kAdEMAMix ? gld<float>(C.a3 + b) : 0.0f;
 }
 
 // FULL: every lane holds four elements (all blocks but a tensor's short last one).
 template <int OPT, bool FULL>
-__device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
-                                          const uint32_t *lds, int64_t eb, int nmine, int lane, float lam,
+__device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const QChunk &C,
+                                          const uint32_t *lds, uint32_t b, int nmine, int lane, float lam,
                                           const QIn &x)
 {
     if (FULL) nmine = 4;
     const float *TS = (const float *)lds;
     const float *TU = TS + 256;
-    const int64_t e = eb + lane * 4;
-    const int64_t blk = eb / kQBlock;
+    const uint32_t e = b * kQBlock + lane * 4;
     float m_in[4], v_in[4], m2_in[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -316,46 +348,35 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
         vo[i] = valid ? r[i].v : 0.0f;
         m2o[i] = valid ? r[i].m2 : 0.0f;
     }
-    const QTabParams PS = a.q.s, PU = a.q.u;
     const float Am = block_absmax(mo), Av = block_absmax(vo);
-    const bool fm = div_by_ok(Am), fv = div_by_ok(Av);
-    const float ym = fm ? 1.0f / Am : 0.0f, yv = fv ? 1.0f / Av : 0.0f;
-    uint32_t om = 0, ov = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        om |= quant<true>(mo[i], Am, ym, fm, lds, PS) << (8 * i);
-        ov |= quant<false>(vo[i], Av, yv, fv, lds, PU) << (8 * i);
-    }
+    const uint32_t om = quant4<true>(mo, Am, lds, a.q.s);
+    const uint32_t ov = quant4<false>(vo, Av, lds, a.q.u);
     uint32_t om2 = 0;
     float Am2 = 0.0f;
     if (OPT == kAdEMAMix) {
         Am2 = block_absmax(m2o);
-        const bool f2 = div_by_ok(Am2);
-        const float y2 = f2 ? 1.0f / Am2 : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) om2 |= quant<true>(m2o[i], Am2, y2, f2, lds, PS) << (8 * i);
+        om2 = quant4<true>(m2o, Am2, lds, a.q.s);
     }
-    uint8_t *W1 = (uint8_t *)T.s1, *W2 = (uint8_t *)T.s2, *W3 = (uint8_t *)T.s3;
     if (nmine == 4) {
-        sst<f4>(T.p + e, f4{p[0], p[1], p[2], p[3]});
-        sst<uint32_t>(W1 + e, om);
-        sst<uint32_t>(W2 + e, ov);
-        if (OPT == kAdEMAMix) sst<uint32_t>(W3 + e, om2);
+        sst<f4>(C.p + e, f4{p[0], p[1], p[2], p[3]});
+        sst<uint32_t>(C.s1 + e, om);
+        sst<uint32_t>(C.s2 + e, ov);
+        if (OPT == kAdEMAMix) sst<uint32_t>(C.s3 + e, om2);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (i < nmine) {
-                gst<float>(T.p + e + i, p[i]);
-                gst<uint8_t>(W1 + e + i, (uint8_t)(om >> (8 * i)));
-                gst<uint8_t>(W2 + e + i, (uint8_t)(ov >> (8 * i)));
-                if (OPT == kAdEMAMix) gst<uint8_t>(W3 + e + i, (uint8_t)(om2 >> (8 * i)));
+                gst<float>(C.p + e + i, p[i]);
+                gst<uint8_t>(C.s1 + e + i, (uint8_t)(om >> (8 * i)));
+                gst<uint8_t>(C.s2 + e + i, (uint8_t)(ov >> (8 * i)));
+                if (OPT == kAdEMAMix) gst<uint8_t>(C.s3 + e + i, (uint8_t)(om2 >> (8 * i)));
             }
         }
     }
     if (lane == 0) {
-        gst<float>(T.a1 + blk, Am);
-        gst<float>(T.a2 + blk, Av);
-        if (OPT == kAdEMAMix) gst<float>(T.a3 + blk, Am2);
+        gst<float>(C.a1 + b, Am);
+        gst<float>(C.a2 + b, Av);
+        if (OPT == kAdEMAMix) gst<float>(C.a3 + b, Am2);
     }
 }
 
@@ -366,15 +387,27 @@ __device__ __forceinline__ int q8_mine(const DevTensor &T, int64_t eb, int lane)
     return max(0, min(4, nvalid - lane * 4));
 }
 
+#ifndef OPT_Q8_THREADS
+#define OPT_Q8_THREADS 512
+#endif
+#ifndef OPT_Q8_BLOCKS
+#define OPT_Q8_BLOCKS 2
+#endif
+// Workgroup size of the 8-bit kernel (one LDS copy of the tables per
+// workgroup) and full blocks in flight per wave.
+constexpr int kQ8Threads = OPT_Q8_THREADS;
+constexpr int kQ8Waves = kQ8Threads / 64;
+constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
+
 template <int OPT, int GD>
-__global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__restrict__ tens,
-                                                           const int32_t *__restrict__ ctab,
-                                                           const uint32_t *__restrict__ qwords,
-                                                           StepArgs a)
+__global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__restrict__ tens,
+                                                             const int32_t *__restrict__ ctab,
+                                                             const uint32_t *__restrict__ qwords,
+                                                             StepArgs a)
 {
     extern __shared__ uint32_t lds[];
     __shared__ Scalars sh;
-    for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kThreads) lds[i] = qwords[i];
+    for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
@@ -386,30 +419,28 @@ __global__ __launch_bounds__(kThreads) void step_q8_kernel(const DevTensor *__re
         const int64_t e0 = (c - T.chunk_begin) * a.chunk;
         const int64_t len = min(a.chunk, T.numel - e0);
         const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
-        const int64_t nblk = (len + kQBlock - 1) / kQBlock;
-        const int64_t nfull = len / kQBlock;
-        int64_t b = wave;
-#if OPT_Q8_PAIR
-        // two full blocks per wave per iteration: both blocks' loads first
-        for (; b + kWaves < nfull; b += 2 * kWaves) {
-            QIn x0, x1;
-            q8_load<OPT, GD, true>(T, e0 + b * kQBlock, 4, lane, x0);
-            q8_load<OPT, GD, true>(T, e0 + (b + kWaves) * kQBlock, 4, lane, x1);
-            q8_finish<OPT, true>(a, s, T, lds, e0 + b * kQBlock, 4, lane, lam, x0);
-            q8_finish<OPT, true>(a, s, T, lds, e0 + (b + kWaves) * kQBlock, 4, lane, lam, x1);
+        const uint32_t nblk = (uint32_t)((len + kQBlock - 1) / kQBlock);
+        const uint32_t nfull = (uint32_t)(len / kQBlock);
+        const QChunk C = q8_chunk<GD>(T, e0);
+        uint32_t b = wave;
+        // kQ8Blocks full blocks per iteration: all their loads before any math
+        for (; b + (kQ8Blocks - 1) * kQ8Waves < nfull; b += kQ8Blocks * kQ8Waves) {
+            QIn x[kQ8Blocks];
+#pragma unroll
+            for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, true>(C, b + u * kQ8Waves, 4, lane, x[u]);
+#pragma unroll
+            for (int u = 0; u < kQ8Blocks; ++u) q8_finish<OPT, true>(a, s, C, lds, b + u * kQ8Waves, 4, lane, lam, x[u]);
         }
-#endif
-        for (; b < nfull; b += kWaves) {
+        for (; b < nfull; b += kQ8Waves) {
             QIn x0;
-            q8_load<OPT, GD, true>(T, e0 + b * kQBlock, 4, lane, x0);
-            q8_finish<OPT, true>(a, s, T, lds, e0 + b * kQBlock, 4, lane, lam, x0);
+            q8_load<OPT, GD, true>(C, b, 4, lane, x0);
+            q8_finish<OPT, true>(a, s, C, lds, b, 4, lane, lam, x0);
         }
         if (b < nblk) {   // the tensor's short last block
-            const int64_t eb = e0 + b * kQBlock;
-            const int nm = q8_mine(T, eb, lane);
+            const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
             QIn x0;
-            q8_load<OPT, GD, false>(T, eb, nm, lane, x0);
-            q8_finish<OPT, false>(a, s, T, lds, eb, nm, lane, lam, x0);
+            q8_load<OPT, GD, false>(C, b, nm, lane, x0);
+            q8_finish<OPT, false>(a, s, C, lds, b, nm, lane, lam, x0);
         }
     }
 }
@@ -584,7 +615,7 @@ __global__ void debug_quantize_kernel(QTabs q, int is_signed, const float *x, ui
 }
 
 template <class K>
-static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks);
+static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, int threads);
 
 // Calibration stream: dst[j][i] = sum_k src[k][i] over fp32 arrays, 4 per
 // lane per access, grid-stride.  With nsrc reads and ndst writes it moves the
@@ -644,7 +675,7 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
     a.ndst = ndst;
     a.n = n;
     const int64_t groups = (n / 4 + kThreads - 1) / kThreads;
-    const int grid = grid_size(debug_stream_kernel, 0, lg, groups);
+    const int grid = grid_size(debug_stream_kernel, 0, lg, groups, kThreads);
     hipLaunchKernelGGL(debug_stream_kernel, dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -656,12 +687,12 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
 // kernel's occupancy times the compute units), unless the caller fixed a
 // per-CU count; never more workgroups than chunks.
 template <class K>
-static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks)
+static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, int threads)
 {
     int per_cu = lg.wgs_per_cu;
     if (per_cu <= 0) {
         int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, lds) != hipSuccess || occ < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds) != hipSuccess || occ < 1)
             occ = 1;
         per_cu = occ;
     }
@@ -672,8 +703,17 @@ template <class K, class... Args>
 static hipError_t launch_persistent(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, hipStream_t st,
                                     Args... args)
 {
-    const int grid = grid_size(kernel, lds, lg, nchunks);
+    const int grid = grid_size(kernel, lds, lg, nchunks, kThreads);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, st, args...);
+    return hipGetLastError();
+}
+
+template <class K, class... Args>
+static hipError_t launch_persistent_q8(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks,
+                                       hipStream_t st, Args... args)
+{
+    const int grid = grid_size(kernel, lds, lg, nchunks, kQ8Threads);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kQ8Threads), lds, st, args...);
     return hipGetLastError();
 }
 
@@ -685,7 +725,7 @@ static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg
     case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
     case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
     case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kQ8: return launch_persistent(step_q8_kernel<OPT, GD>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kQ8: return launch_persistent_q8(step_q8_kernel<OPT, GD>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     default: return hipErrorInvalidValue;
     }
 }
