@@ -29,6 +29,20 @@ def hipcc():
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
+# The host pass of hipcc does not know the packed-fp32 target feature (it is
+# a device feature) and says so once per compile; that line is dropped.
+_HARMLESS = "'-packed-fp32-ops' is not a recognized feature for this target"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    text = "\n".join(l for l in r.stdout.splitlines() if _HARMLESS not in l)
+    if text.strip():
+        print(text, flush=True)
+    if r.returncode != 0:
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+
+
 def build(verbose=False, out=LIB, extra_flags=()):
     tmpdir = tempfile.mkdtemp(prefix="optstep_build_")
     try:
@@ -39,7 +53,7 @@ def build(verbose=False, out=LIB, extra_flags=()):
             cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True)
+            _run(cmd)
             objs.append(obj)
         tmp = out + ".tmp%d" % os.getpid()
         cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]

@@ -170,9 +170,18 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
     if (OPT == kAdEMAMix) store_state1<SF>(T.s3, e, r.m2, rm2);
 }
 
+#ifndef OPT_EW_WAVES_PER_EU
+#define OPT_EW_WAVES_PER_EU 0
+#endif
+#if OPT_EW_WAVES_PER_EU
+#define OPT_EW_ATTR __attribute__((amdgpu_waves_per_eu(OPT_EW_WAVES_PER_EU)))
+#else
+#define OPT_EW_ATTR
+#endif
+
 template <int OPT, int GD, int SF>
-__global__ __launch_bounds__(kThreads) void step_ew_kernel(const DevTensor *__restrict__ tens,
-                                                           const int32_t *__restrict__ ctab, StepArgs a)
+__global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
+                                                                       const int32_t *__restrict__ ctab, StepArgs a)
 {
     __shared__ Scalars sh;
     if (threadIdx.x == 0) sh = make_scalars(a);

@@ -35,6 +35,7 @@ class HP(ctypes.Structure):
         ("weight_decay", ctypes.c_float), ("max_unorm", ctypes.c_float),
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64), ("index_base", ctypes.c_int64),
         ("tensor_index", ctypes.c_int32), ("decay_after", ctypes.c_int32),
+        ("grad_scale", ctypes.c_float),
     ]
 
 
@@ -73,6 +74,10 @@ def lib():
         L.orc_sr_words.argtypes = [ctypes.c_uint64, i64, i32, i64, i64, i32, vp]
         for fn in (L.orc_bf16_rne_array, L.orc_bf16_sr_array, L.orc_quantize_array, L.orc_sr_words):
             fn.restype = None
+        L.orc_grad_norm.argtypes = [vp, i64, vp]
+        L.orc_grad_norm.restype = None
+        L.orc_clip_coef.argtypes = [ctypes.c_double, f32]
+        L.orc_clip_coef.restype = f32
         _lib = L
     return _lib
 
@@ -95,10 +100,10 @@ def widen_bf16(words):
 
 def make_hp(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
             weight_decay=0.0, max_unorm=0.0, step=1, seed=0, index_base=0,
-            tensor_index=0, decay_after=False):
+            tensor_index=0, decay_after=False, grad_scale=1.0):
     return HP(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
               int(step), int(seed) & (2**64 - 1), int(index_base), int(tensor_index),
-              1 if decay_after else 0)
+              1 if decay_after else 0, grad_scale)
 
 
 def _grad_f32(g):
@@ -251,3 +256,32 @@ def state_zeros(fmt, n, opt="adamw", qs=None, qu=None):
         for i in range(1, nst + 1):
             st[f"s{i}"] = np.zeros(n, dtype=dt)
     return st
+
+
+def grad_norm(g):
+    """(sum g^2, max |g|) of one gradient tensor, binary64; g is float32 or
+    BF16 words (widened exactly)."""
+    g = _grad_f32(g)
+    out = np.zeros(2, dtype=np.float64)
+    lib().orc_grad_norm(_ptr(g), g.size, _ptr(out))
+    return float(out[0]), float(out[1])
+
+
+def grad_norm_list(grads):
+    """Norms of a list: per-tensor (sum g^2, max|g|), then the list totals
+    (sums of the per-tensor sums in list order, compensated; max of maxes,
+    NaN if any is NaN)."""
+    per = [grad_norm(g) for g in grads]
+    s, c = 0.0, 0.0
+    for x, _ in per:        # Neumaier over the per-tensor sums, in list order
+        t = s + x
+        c += ((s - t) + x) if abs(s) >= abs(x) else ((x - t) + s)
+        s = t
+    maxes = [m for _, m in per]
+    mx = float("nan") if any(m != m for m in maxes) else max(maxes, default=0.0)
+    total = s + c if np.isfinite(s) else s
+    return (total, mx), per
+
+
+def clip_coef(norm, max_norm):
+    return float(lib().orc_clip_coef(float(norm), float(max_norm)))

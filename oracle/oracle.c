@@ -65,6 +65,8 @@ typedef struct {
     int32_t decay_after;  /* 0: decay-first (the method).  1: the decay-after
                              ordering that [PR] removes; a planted mistake that
                              tests use to show their checks are not vacuous.  */
+    float grad_scale;     /* gradient clipping fused into the step: the step
+                             uses fl(g * grad_scale); 1 leaves g unchanged   */
 } orc_hp;
 
 /* ------------------------------------------------------------------ */
@@ -234,6 +236,9 @@ static moments_t moments_and_direction(int opt, const orc_hp *hp, const scalars_
                                        float g, float m, float v, float m2)
 {
     moments_t r;
+    /* A clipping coefficient ([GN]) scales the gradient before it enters the
+     * step; a scale of 1 is exact. */
+    g = g * hp->grad_scale;
     /* EMAs ([SU] Sec. 1.1):  m' = b1 m + (1-b1) g,  v' = b2 v + (1-b2) g^2,
      * AdEMAMix adds the slow EMA m2' = b3 m2 + (1-b3) g.  g^2 is formed in
      * fp32 from the widened gradient. */
@@ -410,6 +415,13 @@ int orc_step(int opt, int fmt, const orc_hp *hp, float scale, int64_t n,
 
 typedef struct { double s, c; } nsum_t;
 
+/* The compensated total; once the running sum is infinite or NaN the
+ * compensation term is meaningless (inf - inf), and the sum itself is it. */
+static double nsum_total(const nsum_t *a)
+{
+    return isfinite(a->s) ? a->s + a->c : a->s;
+}
+
 static void nsum_add(nsum_t *a, double x)
 {
     double t = a->s + x;
@@ -447,8 +459,8 @@ int orc_unorm(int opt, int fmt, const orc_hp *hp, int64_t n, const float *p, con
         nsum_add(&su, (double)r.u * (double)r.u);
         nsum_add(&sp, (double)p[j] * (double)p[j]);
     }
-    out[0] = su.s + su.c;
-    out[1] = sp.s + sp.c;
+    out[0] = nsum_total(&su);
+    out[1] = nsum_total(&sp);
     return 0;
 }
 
@@ -485,4 +497,38 @@ void orc_sr_words(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, in
                   uint32_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = sr_word(seed, t, k, j0 + i, stream);
+}
+
+/* ------------------------------------------------------------------ */
+/* Gradient norms for clipping ([GN] What and Numerics: the 2-norm and the
+ * inf-norm of a list of gradients, accumulated in binary64, with NaN
+ * propagating into both).  For one tensor: out[0] = sum_j g_j^2 (binary64,
+ * element order, Neumaier compensation; each g_j^2 is exact in binary64),
+ * out[1] = max_j |g_j|, NaN if any g_j is NaN ("tl.maximum follows IEEE
+ * maxNum and ignores NaN ... the kernel counts NaNs and poisons the
+ * partial").                                                             */
+void orc_grad_norm(const float *g, int64_t n, double out[2])
+{
+    nsum_t s = {0.0, 0.0};
+    double mx = 0.0;
+    int nan_seen = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        double x = (double)g[j];
+        nsum_add(&s, x * x);
+        if (isnan(x)) nan_seen = 1;
+        else if (fabs(x) > mx) mx = fabs(x);
+    }
+    out[0] = nsum_total(&s);
+    out[1] = nan_seen ? NAN : mx;
+}
+
+/* The clipping coefficient for a total norm: max_norm / (norm + 1e-6),
+ * capped at 1, formed in binary64 and rounded to binary32 (reading: the
+ * formula of torch.nn.utils.clip_grad_norm_, which the clipping in [GN]
+ * reimplements).  A NaN norm gives NaN.                                  */
+float orc_clip_coef(double norm, float max_norm)
+{
+    double c = (double)max_norm / (norm + 1e-6);
+    if (isnan(c)) return NAN;
+    return (float)(c < 1.0 ? c : 1.0);
 }
