@@ -86,6 +86,10 @@ def build_workload(name, torch, osa, synth):
         tensors.append(d)
         off += n
     bpe = synth.bytes_per_element(opt, fmt, w["grad_bf16"])
+    if w.get("norm_only"):
+        bpe = 2 if w["grad_bf16"] else 4
+    elif w.get("clip"):
+        bpe += 2 if w["grad_bf16"] else 4       # the norm reads g once more
     hp = dict(w["hp"])
     keep = (P, G, states, qs, qu)
     return tensors, fmt, opt, hp, total, bpe, keep
@@ -94,15 +98,25 @@ def build_workload(name, torch, osa, synth):
 def time_workload(name, steps, warmup, torch, osa, synth):
     tensors, fmt, opt, hp, total, bpe, keep = build_workload(name, torch, osa, synth)
     qs, qu = keep[3], keep[4]
+    w = synth.WORKLOADS[name]
     tl = osa.TensorList(tensors)
     step_fn = osa.opt_step_adamw if opt == "adamw" else osa.opt_step_ademamix
     unorm = None
     if hp.get("max_unorm", 0) > 0:
         unorm = torch.empty(2 * len(tensors), dtype=torch.float64, device="cuda")
     stream = torch.cuda.current_stream()
+    clip = w.get("clip")
+    grads = [d["g"] for d in tensors]
+    gnorm = torch.empty(2 + 2 * len(tensors), dtype=torch.float64, device="cuda")
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
 
     def one(t):
-        h = osa.hparams(step=t, seed=synth.SR_SEED, qmap_signed=qs, qmap_unsigned=qu, **hp)
+        if clip:
+            osa.opt_grad_norm(grads, gnorm, clip[0], clip[1], coef, stream=stream)
+            if w.get("norm_only"):
+                return
+        h = osa.hparams(step=t, seed=synth.SR_SEED, qmap_signed=qs, qmap_unsigned=qu,
+                        grad_scale=coef if clip else None, **hp)
         if unorm is not None:
             osa.opt_precondition_unorm(opt, tl, fmt, h, unorm, stream=stream)
         step_fn(tl, fmt, h, unorm, stream=stream)
@@ -134,7 +148,9 @@ def time_workload(name, steps, warmup, torch, osa, synth):
     if unorm is not None:
         gbytes += 16 * total / 1e9      # the pre-pass reads p, g, m, v once more
     row = {
-        "workload": name, "format": fmt, "optimizer": opt, "elements": total, "tensors": len(tensors),
+        "workload": name, "format": "-" if w.get("norm_only") else fmt,
+        "optimizer": "grad-norm" if w.get("norm_only") else opt + ("+clip" if clip else ""),
+        "elements": total, "tensors": len(tensors),
         "bytes_per_element": bpe + (16 if unorm is not None else 0),
         "ms_per_step": ms, "ms_median": q(0.5), "ms_p10": q(0.1), "ms_p90": q(0.9),
         "gelem_per_s": total / (ms * 1e-3) / 1e9,
@@ -304,7 +320,8 @@ def main():
           file=sys.stderr, flush=True)
 
     rows = []
-    others = ["adamw_q8_1g", "ademamix_f32_268m", "adamw_f32_unorm_268m", "adamw_bf16_1g", "adamw_bf16_sr_1g"]
+    others = ["adamw_q8_1g", "ademamix_f32_268m", "adamw_f32_unorm_268m", "adamw_bf16_1g", "adamw_bf16_sr_1g",
+              "gradnorm_bf16_llama7b", "adamw_f32_clip_llama7b"]
     if args.rows == "none":
         others = []
     elif args.rows != "all":

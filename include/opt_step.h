@@ -121,6 +121,11 @@ typedef struct {
     uint64_t seed;
     const float *qmap_signed;
     const float *qmap_unsigned;
+    const float *grad_scale;    /* DEVICE pointer to one float, or NULL: the step
+                                   uses fl(g * (*grad_scale)) in place of g, read
+                                   when the kernel runs (so a clipping coefficient
+                                   that opt_grad_norm writes earlier on the same
+                                   stream fuses into the step); NULL means 1. */
 } opt_hparams;
 
 /* One AdamW step over the n tensors of `tensors` (host array, read during the
@@ -145,6 +150,29 @@ int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
 int opt_precondition_unorm(int32_t optimizer, const opt_tensor *tensors, int64_t n,
                            int32_t state_fmt, const opt_hparams *hp, double *unorm_out,
                            void *stream);
+
+/* ---- gradient norms for clipping --------------------------------------
+ * NeMo Automodel PR "perf(training): fused multi-tensor gradient-norm
+ * reduction": the 2-norm and the inf-norm of a list of gradients in one
+ * launch per dtype, accumulated in binary64 after widening in registers,
+ * deterministic (fixed tiles and reduction order, no atomics), with NaN
+ * poisoning the inf-norm as well as the 2-norm. */
+typedef struct {
+    const void *g;      /* device, numel gradients in dtype, read      */
+    int64_t numel;      /* >= 0                                         */
+    int32_t dtype;      /* OPT_F32 or OPT_BF16                          */
+    int32_t reserved;   /* 0                                            */
+} opt_grad;
+
+/* out: device double[2 + 2n].  out[0] = sum of g^2 over every element of
+ * every tensor, out[1] = max |g| over all of them (NaN if any g is NaN);
+ * out[2 + 2k], out[3 + 2k]: the same for tensor k alone.  If coef_out is not
+ * NULL (device float[1]) it receives the clipping coefficient
+ * min(1, max_norm / (norm + 1e-6)) with norm = sqrt(out[0]) for norm_type 2
+ * or out[1] for norm_type 0 (the inf-norm); pass it as hp->grad_scale of a
+ * later step on the same stream.  g must be 16-byte aligned. */
+int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm, int32_t norm_type,
+                  float *coef_out, void *stream);
 
 /* Text of the last failure on the calling thread ("" if none). */
 const char *opt_last_error(void);

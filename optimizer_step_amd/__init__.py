@@ -46,7 +46,13 @@ class OptHparams(ctypes.Structure):
         ("weight_decay", ctypes.c_float), ("max_unorm", ctypes.c_float),
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64),
         ("qmap_signed", ctypes.c_void_p), ("qmap_unsigned", ctypes.c_void_p),
+        ("grad_scale", ctypes.c_void_p),
     ]
+
+
+class OptGrad(ctypes.Structure):
+    _fields_ = [("g", ctypes.c_void_p), ("numel", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -77,6 +83,7 @@ def lib():
             "opt_debug_div_by": ([vp, vp, vp, i64], i32),
             "opt_debug_set_launch": ([i64, i32], i32),
             "opt_debug_stream": ([vp, i32, vp, i32, i64, vp], i32),
+            "opt_grad_norm": ([ctypes.POINTER(OptGrad), i64, vp, ctypes.c_float, i32, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -133,18 +140,31 @@ def _as_list(tensors):
 
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
-            weight_decay=0.0, max_unorm=0.0, step=1, seed=0, qmap_signed=None, qmap_unsigned=None):
+            weight_decay=0.0, max_unorm=0.0, step=1, seed=0, qmap_signed=None, qmap_unsigned=None,
+            grad_scale=None):
     """An OptHparams record.  qmap_* are host float32 arrays (numpy or CPU
     torch tensors) of 256 entries; they are referenced, not copied, so keep
-    them alive for the call."""
+    them alive for the call.  grad_scale is a CUDA float tensor of one element
+    (for instance the clipping coefficient opt_grad_norm wrote), or None."""
     h = OptHparams(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
-                   int(step), int(seed) & (2**64 - 1), None, None)
+                   int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale))
     for field, q in (("qmap_signed", qmap_signed), ("qmap_unsigned", qmap_unsigned)):
         if q is not None:
             addr = q.ctypes.data if hasattr(q, "ctypes") else q.data_ptr()
             setattr(h, field, addr)
-    h._keep = (qmap_signed, qmap_unsigned)
+    h._keep = (qmap_signed, qmap_unsigned, grad_scale)
     return h
+
+
+def opt_grad_norm(grads, out, max_norm=0.0, norm_type=2, coef_out=None, stream=None):
+    """Norms of a list of CUDA gradient tensors into out (CUDA float64 tensor
+    of 2 + 2n): totals then per-tensor {sum g^2, max |g|}; optionally the
+    clipping coefficient into coef_out (CUDA float32 tensor of 1)."""
+    arr = (OptGrad * max(1, len(grads)))()
+    for i, g in enumerate(grads):
+        arr[i] = OptGrad(_ptr(g), g.numel(), _dtype_code(g), 0)
+    return _check(lib().opt_grad_norm(arr, len(grads), _ptr(out), float(max_norm), int(norm_type),
+                                      _ptr(coef_out), _stream(stream)))
 
 
 def opt_step_adamw(tensors, state_fmt, hp, unorm=None, stream=None):

@@ -21,6 +21,8 @@ hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const Launch
                        hipStream_t st);
 hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, int ntens,
                         double *out, hipStream_t st);
+hipError_t launch_gnorm(int gd, const StepArgs &a, const LaunchGeom &lg, int ntens, double *out, hipStream_t st);
+hipError_t launch_gnorm_total(int64_t n, double *out, float max_norm, int norm_type, float *coef, hipStream_t st);
 hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, uint32_t *out,
                                hipStream_t st);
 hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, int64_t n, hipStream_t st);
@@ -315,6 +317,7 @@ int check_hparams(const opt_hparams *hp, int fmt)
     if (!(hp->beta3 >= 0.0f && hp->beta3 <= 1.0f)) return fail(OPT_EINVAL, "beta3 must lie in [0, 1]");
     if (fmt == kQ8 && (!hp->qmap_signed || !hp->qmap_unsigned))
         return fail(OPT_EINVAL, "8-bit states need qmap_signed and qmap_unsigned");
+    if (hp->grad_scale && !aligned(hp->grad_scale, 4)) return fail(OPT_EALIGN, "grad_scale must be 4-byte aligned");
     return OPT_OK;
 }
 
@@ -417,6 +420,7 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     a.alpha = hp->alpha; a.eps = hp->eps; a.wd = hp->weight_decay; a.max_unorm = hp->max_unorm;
     a.step = hp->step;
     a.seed = hp->seed;
+    a.grad_scale = hp->grad_scale;
     return a;
 }
 
@@ -517,6 +521,72 @@ int opt_precondition_unorm(int32_t optimizer, const opt_tensor *tensors, int64_t
     if (optimizer != kAdamW && optimizer != kAdEMAMix) return fail(OPT_EINVAL, "unknown optimizer %d", optimizer);
     if (!unorm_out) return fail(OPT_EINVAL, "unorm_out is NULL");
     return run(optimizer, tensors, n, state_fmt, hp, nullptr, unorm_out, stream);
+}
+
+int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm, int32_t norm_type,
+                  float *coef_out, void *stream)
+{
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (n > 0 && !grads) return fail(OPT_EINVAL, "grads is NULL");
+    if (n > INT32_MAX) return fail(OPT_EINVAL, "too many tensors");
+    if (!out) return fail(OPT_EINVAL, "out is NULL");
+    if (!aligned(out, 8)) return fail(OPT_EALIGN, "out must be 8-byte aligned");
+    if (coef_out) {
+        if (norm_type != 2 && norm_type != 0) return fail(OPT_EINVAL, "norm_type must be 2 or 0 (inf)");
+        if (!(max_norm > 0.0f) || !std::isfinite(max_norm)) return fail(OPT_EINVAL, "max_norm must be finite and > 0");
+        if (!aligned(coef_out, 4)) return fail(OPT_EALIGN, "coef_out must be 4-byte aligned");
+    }
+    std::vector<opt_tensor> t((size_t)n);
+    for (int64_t k = 0; k < n; ++k) {
+        const opt_grad &x = grads[k];
+        if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
+        if (x.dtype != OPT_F32 && x.dtype != OPT_BF16)
+            return fail(OPT_EINVAL, "tensor %lld: unknown dtype %d", (long long)k, x.dtype);
+        if (x.numel > 0 && !x.g) return fail(OPT_EINVAL, "tensor %lld: g is NULL", (long long)k);
+        if (x.numel > 0 && !aligned(x.g, 16)) return fail(OPT_EALIGN, "tensor %lld: g must be 16-byte aligned", (long long)k);
+        t[k] = opt_tensor{};
+        t[k].g = x.g;
+        t[k].numel = x.numel;
+        t[k].p_dtype = OPT_F32;
+        t[k].g_dtype = x.dtype;
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace *w;
+    int rc;
+    if ((rc = workspace(w)) != OPT_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t chunk = g_chunk;
+    Bucket b[2];
+    plan_bucket(t.data(), n, kGradF32, chunk, b[0]);
+    plan_bucket(t.data(), n, kGradBF16, chunk, b[1]);
+    size_t need = 0;
+    for (auto &bk : b) need = std::max(need, bk.chunk_tensor.size() * (size_t)(chunk / kUTile) * 2);
+    if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
+    hipError_t e;
+    for (int gd = 0; gd < 2; ++gd) {
+        Bucket &bk = b[gd];
+        if (bk.tens.empty()) continue;
+        std::vector<unsigned char> blob;
+        size_t off_ct, off_q;
+        make_blob(bk, nullptr, blob, off_ct, off_q);
+        Slot *s;
+        if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+        StepArgs a{};
+        a.tens = (const DevTensor *)s->dev;
+        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
+        a.nchunks = (int64_t)bk.chunk_tensor.size();
+        a.chunk = chunk;
+        a.partials = w->partials;
+        e = launch_gnorm(gd, a, geom(*w), (int)bk.tens.size(), out, st);
+        if (e != hipSuccess) return hip_fail(e, "gradient norm launch");
+        if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
+    }
+    e = launch_gnorm_total(n, out, max_norm, norm_type, coef_out, st);
+    if (e != hipSuccess) return hip_fail(e, "gradient norm total launch");
+    w->partials_used = true;
+    w->partials_stream = st;
+    if ((e = hipEventRecord(w->partials_ev, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return OPT_OK;
 }
 
 const char *opt_last_error(void) { return g_err.c_str(); }

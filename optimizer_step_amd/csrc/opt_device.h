@@ -206,6 +206,7 @@ struct Scalars {
     float rc1, rc2;        // RN(1/c1), RN(1/c2)
     float d;               // 1 - lr*wd
     float lam;             // lr (the update-norm scale is applied per tensor)
+    float gs;              // gradient scale (a clipping coefficient), 1 if none
 };
 
 __device__ inline double powi(double b, int64_t t)
@@ -234,6 +235,7 @@ __device__ inline Scalars make_scalars(const StepArgs &a)
     float lrwd = a.lr * a.wd;
     s.d = 1.0f - lrwd;
     s.lam = a.lr;
+    s.gs = a.grad_scale ? *a.grad_scale : 1.0f;
     return s;
 }
 
@@ -257,6 +259,7 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
                                        float v, float m2)
 {
     Mom r;
+    g = g * s.gs;            // clipping fused into the step (exact for a scale of 1)
     float gg = g * g;
     r.m = a.beta1 * m + s.om1 * g;
     r.v = a.beta2 * v + s.om2 * gg;
@@ -286,6 +289,7 @@ __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a,
                                             float v, float m2)
 {
     Mom r;
+    g = g * s.gs;
     float gg = g * g;
     r.m = a.beta1 * m + s.om1 * g;
     r.v = a.beta2 * v + s.om2 * gg;

@@ -591,6 +591,131 @@ __global__ __launch_bounds__(kThreads) void unorm_reduce_kernel(const DevTensor 
 }
 
 // ---------------------------------------------------------------------------
+// Gradient norms (the NeMo PR's fused multi-tensor reduction): per tile of
+// kUTile elements one wave forms {sum g^2 in binary64, max |g| as bits}, then
+// one workgroup per tensor sums its tiles, then one workgroup totals the list
+// in tensor order.  Fixed orders, no atomics.  The tile partials reuse the
+// update-norm partials buffer; slot 2t+1 carries the max as a double.
+
+template <int GD>
+__global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTensor *__restrict__ tens,
+                                                                  const int32_t *__restrict__ ctab,
+                                                                  StepArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tiles_per_chunk = a.chunk / kUTile;
+    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
+        const DevTensor T = tens[ctab[c]];
+        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
+        const int64_t len = min(a.chunk, T.numel - e0);
+        const int64_t ntile = (len + kUTile - 1) / kUTile;
+        for (int64_t tt = wave; tt < ntile; tt += kWaves) {
+            double sq = 0.0;
+            uint32_t mx = 0;
+            if ((tt + 1) * kUTile <= len) {
+                float g[4][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) load_grad4<GD>(T.g, e0 + tt * kUTile + q * 256 + lane * 4, g[q]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const double x = (double)g[q][j];
+                        sq += x * x;
+                        mx = max(mx, fbits(g[q][j]) & 0x7FFFFFFFu);
+                    }
+            } else {
+                for (int q = 0; q < kUTile / 256; ++q) {
+                    const int64_t i0 = tt * kUTile + q * 256 + lane * 4;
+                    const int n = (int)max((int64_t)0, min((int64_t)4, len - i0));
+                    for (int j = 0; j < n; ++j) {
+                        const float gv = load_grad1<GD>(T.g, e0 + i0 + j);
+                        const double x = (double)gv;
+                        sq += x * x;
+                        mx = max(mx, fbits(gv) & 0x7FFFFFFFu);
+                    }
+                }
+            }
+            sq = wave_sum(sq);
+            mx = wave_max_u32(mx);
+            if (lane == 0) {
+                const int64_t slot = c * tiles_per_chunk + tt;
+                gst<double>(a.partials + 2 * slot, sq);
+                gst<double>(a.partials + 2 * slot + 1, (double)bitsf(mx));
+            }
+        }
+    }
+}
+
+// Max of doubles in which any NaN wins.
+__device__ __forceinline__ double nanmax(double x, double y)
+{
+    return (x != x || y != y) ? __builtin_nan("") : fmax(x, y);
+}
+
+__device__ __forceinline__ double wave_nanmax(double x)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x = nanmax(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void gnorm_reduce_kernel(const DevTensor *__restrict__ tens, int64_t chunk,
+                                                              const double *partials, double *out)
+{
+    __shared__ double red[kWaves][2];
+    const DevTensor T = tens[blockIdx.x];
+    const int64_t first = T.chunk_begin * (chunk / kUTile);
+    const int64_t nt = (T.numel + kUTile - 1) / kUTile;
+    double sq = 0.0, mx = 0.0;
+    for (int64_t i = threadIdx.x; i < nt; i += kThreads) {
+        sq += gld<double>(partials + 2 * (first + i));
+        mx = nanmax(mx, gld<double>(partials + 2 * (first + i) + 1));
+    }
+    sq = wave_sum(sq);
+    mx = wave_nanmax(mx);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { red[wave][0] = sq; red[wave][1] = mx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double S = red[0][0], M = red[0][1];
+        for (int w = 1; w < kWaves; ++w) { S += red[w][0]; M = nanmax(M, red[w][1]); }
+        gst<double>(out + 2 + 2 * (int64_t)T.k, S);
+        gst<double>(out + 3 + 2 * (int64_t)T.k, M);
+    }
+}
+
+// List totals in tensor order (lane-strided, fixed butterfly, waves in
+// order) and, if asked, the clipping coefficient.
+__global__ __launch_bounds__(kThreads) void gnorm_total_kernel(int64_t n, double *out, float max_norm,
+                                                             int norm_type, float *coef)
+{
+    __shared__ double red[kWaves][2];
+    double sq = 0.0, mx = 0.0;
+    for (int64_t k = threadIdx.x; k < n; k += kThreads) {
+        sq += gld<double>(out + 2 + 2 * k);
+        mx = nanmax(mx, gld<double>(out + 3 + 2 * k));
+    }
+    sq = wave_sum(sq);
+    mx = wave_nanmax(mx);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { red[wave][0] = sq; red[wave][1] = mx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double S = red[0][0], M = red[0][1];
+        for (int w = 1; w < kWaves; ++w) { S += red[w][0]; M = nanmax(M, red[w][1]); }
+        gst<double>(out, S);
+        gst<double>(out + 1, M);
+        if (coef) {
+            const double norm = norm_type == 2 ? sqrt(S) : M;
+            const double cf = (double)max_norm / (norm + 1e-6);
+            gst<float>(coef, cf != cf ? __builtin_nanf("") : (float)(cf < 1.0 ? cf : 1.0));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // test hooks
 
 __global__ void debug_philox_kernel(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n,
@@ -773,6 +898,24 @@ hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const Launc
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(unorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
                        (const double *)a.partials, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gnorm(int gd, const StepArgs &a, const LaunchGeom &lg, int ntens, double *out, hipStream_t st)
+{
+    hipError_t e = hipSuccess;
+    if (a.nchunks > 0)
+        e = gd == kGradF32 ? launch_persistent(gnorm_partials_kernel<kGradF32>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a)
+                           : launch_persistent(gnorm_partials_kernel<kGradBF16>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gnorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
+                       (const double *)a.partials, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gnorm_total(int64_t n, double *out, float max_norm, int norm_type, float *coef, hipStream_t st)
+{
+    hipLaunchKernelGGL(gnorm_total_kernel, dim3(1), dim3(kThreads), 0, st, n, out, max_norm, norm_type, coef);
     return hipGetLastError();
 }
 

@@ -70,6 +70,7 @@ struct StepArgs {
     float lr, beta1, beta2, beta3, alpha, eps, wd, max_unorm;
     int64_t step;
     uint64_t seed;
+    const float *grad_scale;       // device float or null (1)
 };
 
 }  // namespace optstep

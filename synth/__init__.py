@@ -91,6 +91,19 @@ def grads(n, t, k=0, std=1e-2, bf16=False, mask_scale=None):
     return bf16_words(g) if bf16 else g
 
 
+def grid_grads(n, t, k=0, bf16=False):
+    """Gradients on a coarse grid, so that every square and every partial sum
+    of squares is exact in binary64 whatever the summation order: integers
+    |i| <= 255 times 2^-10 for BF16 (8 significant bits), |i| <= 4095 times
+    2^-12 for float32; about N(0, 0.04) before clipping to the grid."""
+    z = _rng(GRAD_SEED, k, t, 7).standard_normal(n)
+    if bf16:
+        i = np.clip(np.rint(z * 40.0), -255, 255)
+        return bf16_words((i * 2.0**-10).astype(np.float32))
+    i = np.clip(np.rint(z * 160.0), -4095, 4095)
+    return (i * 2.0**-12).astype(np.float32)
+
+
 # --------------------------------------------------------------------------
 # device draws (large workloads)
 
@@ -185,6 +198,15 @@ WORKLOADS = {
     "adamw_bf16_sr_1g": dict(opt="adamw", fmt="bf16_sr", sizes=[2**30], grad_bf16=True,
                              p_std=0.02, g_std="decay", steps=200,
                              hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)),
+    # gradient 2-norm of the Llama-7B-shaped bf16 gradient list alone
+    "gradnorm_bf16_llama7b": dict(opt="adamw", fmt="f32", sizes=[n for _, n in llama7b_shapes()],
+                                  grad_bf16=True, p_std=0.02, g_std=1e-3, steps=5, norm_only=True,
+                                  clip=(1.0, 2), hp=dict()),
+    # the headline step preceded by the fused gradient norm, the clipping
+    # coefficient handed to the step in device memory
+    "adamw_f32_clip_llama7b": dict(opt="adamw", fmt="f32", sizes=[n for _, n in llama7b_shapes()],
+                                   grad_bf16=True, p_std=0.02, g_std=1e-3, steps=5, clip=(1.0, 2),
+                                   hp=dict(lr=3e-4, weight_decay=0.1, beta1=0.9, beta2=0.999, eps=1e-8)),
 }
 
 

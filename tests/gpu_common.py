@@ -78,8 +78,11 @@ class Case:
     """One optimizer run: a list of tensors (host inputs) and how to step it."""
 
     def __init__(self, opt, fmt, sizes, grad_bf16, steps, hp, seed=synth.SR_SEED,
-                 g_std=1e-2, mask_scale=None, grad_override=None):
+                 g_std=1e-2, mask_scale=None, grad_override=None, clip=None):
+        """clip=(max_norm, norm_type): before each step, the gradient norms of
+        the list give a clipping coefficient that the step applies to g."""
         self.opt, self.fmt, self.sizes, self.steps, self.hp = opt, fmt, list(sizes), steps, dict(hp)
+        self.clip = clip
         self.grad_bf16 = grad_bf16 if isinstance(grad_bf16, (list, tuple)) else [grad_bf16] * len(self.sizes)
         self.seed = seed
         self.g_std = g_std
@@ -106,10 +109,17 @@ class Case:
               if start is None else [{k: v.copy() for k, v in s.items()} for s in start[1]])
         t0 = 0 if start is None else start[2]
         norms = []
+        self.oracle_coefs = []
         for t in range(t0 + 1, t0 + steps + 1):
+            extra = {}
+            if self.clip is not None:
+                (s2, mx), _ = oracle.grad_norm_list([self.grad(t, k) for k in range(len(self.sizes))])
+                coef = oracle.clip_coef(np.sqrt(s2) if self.clip[1] == 2 else mx, self.clip[0])
+                self.oracle_coefs.append(coef)
+                extra = {"grad_scale": coef}
             for k, n in enumerate(self.sizes):
                 g = self.grad(t, k)
-                hp = oracle.make_hp(step=t, seed=self.seed, tensor_index=k, **self.hp)
+                hp = oracle.make_hp(step=t, seed=self.seed, tensor_index=k, **self.hp, **extra)
                 scale = 1.0
                 if self.hp.get("max_unorm", 0.0) > 0:
                     u2, p2 = oracle.unorm(self.opt, self.fmt, hp, ps[k], g, qs=self.qs, qu=self.qu, **st[k])
@@ -143,11 +153,19 @@ class Case:
         tl = osa.TensorList(dev)
         fn = osa.opt_step_adamw if self.opt == "adamw" else osa.opt_step_ademamix
         norms = []
+        self.gpu_coefs = []
         for t in range(t0 + 1, t0 + steps + 1):
             for k in range(len(self.sizes)):
                 g = self.grad(t, k)
                 dev[k]["g"].copy_(to_dev(g))
-            hp = osa.hparams(step=t, seed=self.seed, qmap_signed=self.qs, qmap_unsigned=self.qu, **self.hp)
+            coef = None
+            if self.clip is not None:
+                gn = T.empty(2 + 2 * len(self.sizes), dtype=T.float64, device="cuda")
+                coef = T.empty(1, dtype=T.float32, device="cuda")
+                osa.opt_grad_norm([d["g"] for d in dev], gn, self.clip[0], self.clip[1], coef, stream=stream)
+                self.gpu_coefs.append((gn, coef))    # alive until the synchronize below
+            hp = osa.hparams(step=t, seed=self.seed, qmap_signed=self.qs, qmap_unsigned=self.qu,
+                             grad_scale=coef, **self.hp)
             unorm = None
             if self.hp.get("max_unorm", 0.0) > 0:
                 unorm = T.empty(2 * len(self.sizes), dtype=T.float64, device="cuda")
@@ -155,6 +173,7 @@ class Case:
                 norms.append(unorm.cpu().numpy().copy())
             fn(tl, self.fmt, hp, unorm, stream=stream)
         T.cuda.synchronize()
+        self.gpu_coefs = [float(c.cpu().numpy()[0]) for _, c in self.gpu_coefs]
         return dev, norms
 
     @staticmethod

@@ -159,3 +159,33 @@ def test_reused_reciprocal_division_is_correctly_rounded(L):
     ref = (a / b).astype(np.float32)
     normal = np.abs(ref) >= np.float32(2.0 ** -126)
     assert np.array_equal(got[normal].view(np.uint32), ref[normal].view(np.uint32))
+
+
+def _gn(L, grads, out=8192, max_norm=1.0, norm_type=2, coef=None, n=None):
+    arr = (L.OptGrad * max(1, len(grads)))(*[L.OptGrad(*g) for g in grads])
+    return L.lib().opt_grad_norm(arr, len(grads) if n is None else n, out, max_norm, norm_type, coef, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(n=-1), -1),
+    (dict(out=None), -1),
+    (dict(out=8196), -3),
+    (dict(grads=[(4096, 16, 5, 0)]), -1),            # unknown dtype
+    (dict(grads=[(None, 16, 0, 0)]), -1),            # NULL data with elements
+    (dict(grads=[(4100, 16, 0, 0)]), -3),            # misaligned data
+    (dict(grads=[(4096, -1, 0, 0)]), -1),
+    (dict(coef=4096, norm_type=1), -1),              # only 2 and 0 (inf)
+    (dict(coef=4096, max_norm=0.0), -1),
+    (dict(coef=4096, max_norm=float("inf")), -1),
+    (dict(coef=4098), -3),
+])
+def test_grad_norm_bad_arguments(L, case, status):
+    grads = case.pop("grads", [(4096, 16, 0, 0)])
+    assert _gn(L, grads, **case) == status
+    assert L.opt_last_error() != ""
+
+
+def test_step_rejects_misaligned_grad_scale(L):
+    hp = L.hparams()
+    hp.grad_scale = 4098
+    assert _call(L, "opt_step_adamw", _tensor(L), 0, hp) == -3
