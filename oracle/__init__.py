@@ -10,9 +10,10 @@ arrays on the host:
 
 * ``p``: float32 parameters, updated in place;
 * ``g``: float32 gradients, or uint16 BF16 words (widened exactly, bits << 16);
-* states: float32 (fp32 storage), uint16 (BF16 words) or uint8 (8-bit codes),
-  updated in place; 8-bit storage also takes float32 absmax arrays of
-  ceil(n/256) entries per state and the two 256-entry codebooks.
+* states: float32 (fp32 storage), uint16 (BF16 words) or uint8 (8-bit codes,
+  FP8 codes, or two FP4 codes per byte), updated in place; 8-bit, FP8 and FP4
+  storage also take float32 absmax arrays of ceil(n/256) entries per state,
+  and 8-bit storage the two 256-entry codebooks.
 """
 import ctypes
 import os
@@ -23,7 +24,11 @@ from . import build as _build
 
 ADAMW, ADEMAMIX = 0, 1
 F32, BF16_RN, BF16_SR, Q8 = 0, 1, 2, 3
-FORMATS = {"f32": F32, "bf16_rn": BF16_RN, "bf16_sr": BF16_SR, "q8": Q8}
+FP8_RN, FP8_SR, FP4_RN, FP4_SR = 4, 5, 6, 7
+FORMATS = {"f32": F32, "bf16_rn": BF16_RN, "bf16_sr": BF16_SR, "q8": Q8,
+           "fp8_rn": FP8_RN, "fp8_sr": FP8_SR, "fp4_rn": FP4_RN, "fp4_sr": FP4_SR}
+BLOCKED = (Q8, FP8_RN, FP8_SR, FP4_RN, FP4_SR)
+E4M3, E2M1, E2M2U = 0, 1, 2          # element formats of the FP8/FP4 states
 OPTIMIZERS = {"adamw": ADAMW, "ademamix": ADEMAMIX}
 BLOCK = 256
 
@@ -35,7 +40,7 @@ class HP(ctypes.Structure):
         ("weight_decay", ctypes.c_float), ("max_unorm", ctypes.c_float),
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64), ("index_base", ctypes.c_int64),
         ("tensor_index", ctypes.c_int32), ("decay_after", ctypes.c_int32),
-        ("grad_scale", ctypes.c_float),
+        ("grad_scale", ctypes.c_float), ("reset_interval", ctypes.c_int64),
     ]
 
 
@@ -78,6 +83,18 @@ def lib():
         L.orc_grad_norm.restype = None
         L.orc_clip_coef.argtypes = [ctypes.c_double, f32]
         L.orc_clip_coef.restype = f32
+        L.orc_mini_value.argtypes = [i32, i32]
+        L.orc_mini_value.restype = ctypes.c_double
+        L.orc_mini_round.argtypes = [i32, ctypes.c_double, i32]
+        L.orc_mini_round.restype = i32
+        L.orc_mini_encode.argtypes = [i32, f32, f32, i32]
+        L.orc_mini_encode.restype = i32
+        L.orc_mini_decode.argtypes = [i32, i32, f32]
+        L.orc_mini_decode.restype = f32
+        L.orc_mini_scale_exp.argtypes = [i32, f32]
+        L.orc_mini_scale_exp.restype = i32
+        L.orc_mini_round_array.argtypes = [i32, vp, vp, vp, i64]
+        L.orc_mini_round_array.restype = None
         _lib = L
     return _lib
 
@@ -100,10 +117,10 @@ def widen_bf16(words):
 
 def make_hp(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
             weight_decay=0.0, max_unorm=0.0, step=1, seed=0, index_base=0,
-            tensor_index=0, decay_after=False, grad_scale=1.0):
+            tensor_index=0, decay_after=False, grad_scale=1.0, reset_interval=0):
     return HP(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
               int(step), int(seed) & (2**64 - 1), int(index_base), int(tensor_index),
-              1 if decay_after else 0, grad_scale)
+              1 if decay_after else 0, grad_scale, int(reset_interval))
 
 
 def _grad_f32(g):
@@ -113,7 +130,12 @@ def _grad_f32(g):
 
 
 def _state_dtype(fmt):
-    return {F32: np.float32, BF16_RN: np.uint16, BF16_SR: np.uint16, Q8: np.uint8}[fmt]
+    return {F32: np.float32, BF16_RN: np.uint16, BF16_SR: np.uint16}.get(fmt, np.uint8)
+
+
+def state_len(fmt, n):
+    """Entries of one state array for n elements (FP4: two codes per byte)."""
+    return (n + 1) // 2 if fmt in (FP4_RN, FP4_SR) else n
 
 
 def _check(opt, fmt, p, g, s1, s2, s3, a1, a2, a3, qs, qu):
@@ -121,16 +143,18 @@ def _check(opt, fmt, p, g, s1, s2, s3, a1, a2, a3, qs, qu):
     _need(p, np.float32, n, "p")
     _need(g, np.float32, n, "g")
     sd = _state_dtype(fmt)
-    _need(s1, sd, n, "s1")
-    _need(s2, sd, n, "s2")
+    ns = state_len(fmt, n)
+    _need(s1, sd, ns, "s1")
+    _need(s2, sd, ns, "s2")
     if opt == ADEMAMIX:
-        _need(s3, sd, n, "s3")
-    if fmt == Q8:
+        _need(s3, sd, ns, "s3")
+    if fmt in BLOCKED:
         nb = (n + BLOCK - 1) // BLOCK
         _need(a1, np.float32, nb, "a1")
         _need(a2, np.float32, nb, "a2")
         if opt == ADEMAMIX:
             _need(a3, np.float32, nb, "a3")
+    if fmt == Q8:
         _need(qs, np.float32, 256, "qs")
         _need(qu, np.float32, 256, "qu")
 
@@ -251,11 +275,59 @@ def state_zeros(fmt, n, opt="adamw", qs=None, qu=None):
         if nst == 3:
             st["s3"] = np.full(n, cs, dtype=np.uint8)
             st["a3"] = np.zeros(nb, dtype=np.float32)
+    elif fmt in BLOCKED:
+        # code 0 is +0 in every FP8/FP4 element format; absmax 0 reads back 0
+        nb = (n + BLOCK - 1) // BLOCK
+        for i in range(1, nst + 1):
+            st[f"s{i}"] = np.zeros(state_len(fmt, n), dtype=np.uint8)
+            st[f"a{i}"] = np.zeros(nb, dtype=np.float32)
     else:
         dt = _state_dtype(fmt)
         for i in range(1, nst + 1):
             st[f"s{i}"] = np.zeros(n, dtype=dt)
     return st
+
+
+# --------------------------------------------------------------------------
+# FP8 / FP4 element codecs (format ids E4M3, E2M1, E2M2U)
+
+def mini_value(f, mag):
+    return float(lib().orc_mini_value(f, int(mag)))
+
+
+def mini_round(f, y, r=-1):
+    """Magnitude code of y >= 0 (already divided by the block scale); r < 0 is
+    nearest rounding, else stochastic with the 16-bit integer r."""
+    return int(lib().orc_mini_round(f, float(y), int(r)))
+
+
+def mini_round_array(f, y, r=None):
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    rr = None if r is None else np.ascontiguousarray(np.broadcast_to(np.asarray(r, dtype=np.int32), y.shape))
+    out = np.empty(y.size, dtype=np.int32)
+    lib().orc_mini_round_array(f, _ptr(y), _ptr(rr), _ptr(out), y.size)
+    return out
+
+
+def mini_encode(f, x, A, r=-1):
+    return int(lib().orc_mini_encode(f, float(np.float32(x)), float(np.float32(A)), int(r)))
+
+
+def mini_decode(f, code, A):
+    return float(np.float32(lib().orc_mini_decode(f, int(code), float(np.float32(A)))))
+
+
+def mini_scale_exp(f, A):
+    return int(lib().orc_mini_scale_exp(f, float(np.float32(A))))
+
+
+def unpack_fp4(codes, n):
+    """FP4 state bytes -> one code per element (element 2i in the low nibble)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(2 * c.size, dtype=np.uint8)
+    out[0::2] = c & 0xF
+    out[1::2] = c >> 4
+    return out[:n]
 
 
 def grad_norm(g):

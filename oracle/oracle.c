@@ -44,7 +44,10 @@
  *    ([GN] Correctness properties); a zero absmax gives x = 0;
  *  - stochastic rounding draws r from Philox4x32-10 (Salmon, Moraes, Dror,
  *    Shaw, SC'11) keyed by the seed, with counter (j>>2, j>>34, t, k);
- *    the low 16 bits of word j mod 4 round m, the high 16 bits round v.
+ *    the low 16 bits of word j mod 4 round m, the high 16 bits round v;
+ *  - FP8/FP4 states: see the block-scaled section below;
+ *  - a state reset ([SU] Sec. 5) restarts the moments from zero and the
+ *    bias-correction count from 1; the random stream keeps the absolute t.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,7 +57,8 @@
 /* public enums and hyper-parameter record (oracle-private definitions) */
 
 enum { ORC_ADAMW = 0, ORC_ADEMAMIX = 1 };
-enum { ORC_F32 = 0, ORC_BF16_RN = 1, ORC_BF16_SR = 2, ORC_Q8 = 3 };
+enum { ORC_F32 = 0, ORC_BF16_RN = 1, ORC_BF16_SR = 2, ORC_Q8 = 3,
+       ORC_FP8_RN = 4, ORC_FP8_SR = 5, ORC_FP4_RN = 6, ORC_FP4_SR = 7 };
 
 typedef struct {
     float lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm;
@@ -67,6 +71,8 @@ typedef struct {
                              tests use to show their checks are not vacuous.  */
     float grad_scale;     /* gradient clipping fused into the step: the step
                              uses fl(g * grad_scale); 1 leaves g unchanged   */
+    int64_t reset_interval; /* R > 0: the moments restart from zero at steps
+                             1, R+1, 2R+1, ... ([SU] Sec. 5); 0: never        */
 } orc_hp;
 
 /* ------------------------------------------------------------------ */
@@ -204,14 +210,28 @@ typedef struct {
     float lam;             /* lr, times the update-norm scale    */
 } scalars_t;
 
+/* Steps since the moments last started from zero (1 on the step that
+ * starts them), and whether this step starts them. */
+static int64_t cycle_step(const orc_hp *hp)
+{
+    if (hp->reset_interval > 0) return (hp->step - 1) % hp->reset_interval + 1;
+    return hp->step;
+}
+
+static int fresh_states(const orc_hp *hp)
+{
+    return hp->reset_interval > 0 && cycle_step(hp) == 1;
+}
+
 static scalars_t make_scalars(const orc_hp *hp, float scale)
 {
     scalars_t s;
+    int64_t t = cycle_step(hp);
     s.om1 = 1.0f - hp->beta1;
     s.om2 = 1.0f - hp->beta2;
     s.om3 = 1.0f - hp->beta3;
-    s.c1 = (float)(1.0 - pow((double)hp->beta1, (double)hp->step));
-    s.c2 = (float)(1.0 - pow((double)hp->beta2, (double)hp->step));
+    s.c1 = (float)(1.0 - pow((double)hp->beta1, (double)t));
+    s.c2 = (float)(1.0 - pow((double)hp->beta2, (double)t));
     float lrwd = hp->lr * hp->weight_decay;
     s.d = 1.0f - lrwd;
     s.lam = hp->lr * scale;   /* exact when scale is 1 */
@@ -282,9 +302,12 @@ static int step_f32(int opt, const orc_hp *hp, float scale, int64_t n,
                     float *p, const float *g, float *m, float *v, float *m2)
 {
     scalars_t s = make_scalars(hp, scale);
+    int fresh = fresh_states(hp);
     for (int64_t j = 0; j < n; ++j) {
-        moments_t r = moments_and_direction(opt, hp, &s, g[j], m[j], v[j],
-                                            opt == ORC_ADEMAMIX ? m2[j] : 0.0f);
+        float m_old = fresh ? 0.0f : m[j];
+        float v_old = fresh ? 0.0f : v[j];
+        float m2_old = (opt == ORC_ADEMAMIX && !fresh) ? m2[j] : 0.0f;
+        moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
         p[j] = apply_update(hp, &s, p[j], r.u);
         m[j] = r.m;
         v[j] = r.v;
@@ -297,10 +320,11 @@ static int step_bf16(int opt, int stochastic, const orc_hp *hp, float scale, int
                      float *p, const float *g, uint16_t *m, uint16_t *v, uint16_t *m2)
 {
     scalars_t s = make_scalars(hp, scale);
+    int fresh = fresh_states(hp);
     for (int64_t j = 0; j < n; ++j) {
-        float m_old = orc_bf16_to_f32(m[j]);
-        float v_old = orc_bf16_to_f32(v[j]);
-        float m2_old = (opt == ORC_ADEMAMIX) ? orc_bf16_to_f32(m2[j]) : 0.0f;
+        float m_old = fresh ? 0.0f : orc_bf16_to_f32(m[j]);
+        float v_old = fresh ? 0.0f : orc_bf16_to_f32(v[j]);
+        float m2_old = (opt == ORC_ADEMAMIX && !fresh) ? orc_bf16_to_f32(m2[j]) : 0.0f;
         moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
         /* The parameter update uses the unrounded fp32 moments; rounding
          * happens only at write-back ([SU] Sec. 1.1). */
@@ -357,14 +381,15 @@ static int step_q8(int opt, const orc_hp *hp, float scale, int64_t n,
                    float *a1, float *a2, float *a3, const float *qs, const float *qu)
 {
     scalars_t s = make_scalars(hp, scale);
+    int fresh = fresh_states(hp);
     float bm[Q8_BLOCK], bv[Q8_BLOCK], bm2[Q8_BLOCK];
     for (int64_t b0 = 0, blk = 0; b0 < n; b0 += Q8_BLOCK, ++blk) {
         int64_t len = (n - b0 < Q8_BLOCK) ? n - b0 : Q8_BLOCK;
         for (int64_t i = 0; i < len; ++i) {
             int64_t j = b0 + i;
-            float m_old = qs[c1[j]] * a1[blk];
-            float v_old = qu[c2[j]] * a2[blk];
-            float m2_old = (opt == ORC_ADEMAMIX) ? qs[c3[j]] * a3[blk] : 0.0f;
+            float m_old = fresh ? 0.0f : qs[c1[j]] * a1[blk];
+            float v_old = fresh ? 0.0f : qu[c2[j]] * a2[blk];
+            float m2_old = (opt == ORC_ADEMAMIX && !fresh) ? qs[c3[j]] * a3[blk] : 0.0f;
             moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
             p[j] = apply_update(hp, &s, p[j], r.u);
             bm[i] = r.m; bv[i] = r.v; bm2[i] = r.m2;
@@ -382,6 +407,188 @@ static int step_q8(int opt, const orc_hp *hp, float scale, int64_t n,
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* FP8 and FP4 block-scaled states ([SU] Sec. 2.1: an FP8 grid with three
+ * fraction bits, 16 times coarser than BF16 at the same scale, and an
+ * unsigned FP4 grid E2M2, 32 times coarser, for a state that is never
+ * negative; Sec. 5: both formats, with nearest or stochastic rounding).
+ *
+ * Readings (the pages give the grids and nothing else):
+ *  - FP8 is OCP E4M3 (bias 7, no infinities, magnitude 1111.111 is NaN,
+ *    largest finite 448) for m, v and m2.
+ *  - FP4 keeps v in unsigned E2M2 (bias 1: 0, 1/4, ..., 7/4, 2, ..., 7) and
+ *    the signed m and m2 in OCP E2M1 (bias 1: 0, 1/2, 1, 3/2, 2, 3, 4, 6),
+ *    the signed 4-bit format the page contrasts E2M2 with.  Two codes share a
+ *    byte, element 2i in the low nibble; the high nibble after an odd
+ *    tensor's last element is 0.
+ *  - Neither grid can hold gradient-sized moments as they are, so every
+ *    256-element block is scaled by a power of two taken from its absmax A,
+ *    as in the OCP microscaling rule: X = 2^(floor(log2 A) - emax), emax the
+ *    exponent of the format's top binade.  A stored element is the rounding
+ *    of x / X on the format's grid, clamped to the largest finite value, and
+ *    reads back as value(code) * X rounded to binary32.  A power-of-two X
+ *    leaves the grid's relative spacing unchanged, which is what the pages'
+ *    stall analysis depends on.  The block keeps A itself (fp32), like the
+ *    8-bit format.
+ *  - Nearest rounding breaks ties to the even code.  Stochastic rounding
+ *    takes the element's 16-bit random integer r (as BF16 stochastic
+ *    rounding does) and goes up iff floor(f * 2^16) + r >= 2^16, f in [0, 1)
+ *    the position of the value across the gap between its two neighbours:
+ *    the carry rule of [SU] Sec. 6.1 with the dropped part cut to 16 bits.
+ *  - A = 0 reads back as signed zeros; a block whose A is NaN or infinite
+ *    stores codes 0 and reads back as NaN.  An E4M3 NaN code reads as NaN.
+ */
+
+typedef struct {
+    int mbits, bias, maxcode, nan_code, sign;   /* sign: the sign bit, or 0 */
+} mini_t;
+
+static const mini_t MINI_E4M3 = {3, 7, 0x7E, 0x7F, 0x80};
+static const mini_t MINI_E2M1 = {1, 1, 0x7, -1, 0x8};
+static const mini_t MINI_E2M2U = {2, 1, 0xF, -1, 0};
+
+static const mini_t *mini_fmt(int id)
+{
+    return id == 0 ? &MINI_E4M3 : id == 1 ? &MINI_E2M1 : &MINI_E2M2U;
+}
+
+/* The value of a magnitude code: exponent field e, fraction field f. */
+static double mini_value(const mini_t *F, int c)
+{
+    int e = c >> F->mbits, f = c & ((1 << F->mbits) - 1);
+    if (e == 0) return ldexp((double)f, 1 - F->bias - F->mbits);
+    return ldexp((double)((1 << F->mbits) + f), e - F->bias - F->mbits);
+}
+
+static int mini_emax(const mini_t *F) { return (F->maxcode >> F->mbits) - F->bias; }
+
+/* Magnitude code of y >= 0 on the format's grid.  r < 0: nearest, ties to the
+ * even code; else stochastic with the 16-bit integer r.  Values at or above
+ * the largest finite value take it.  Found by walking the grid from 0. */
+static int mini_round(const mini_t *F, double y, int32_t r)
+{
+    if (!(y > 0.0)) return 0;
+    if (y >= mini_value(F, F->maxcode)) return F->maxcode;
+    int c = 0;
+    while (mini_value(F, c + 1) <= y) ++c;
+    double lo = mini_value(F, c), hi = mini_value(F, c + 1);
+    if (r < 0) {
+        double dl = y - lo, dh = hi - y;
+        if (dl < dh) return c;
+        if (dh < dl) return c + 1;
+        return (c & 1) ? c + 1 : c;
+    }
+    /* y - lo is exact (y and lo are within a factor of two, or lo = 0) and
+     * hi - lo is a power of two, so the product is exact before the floor. */
+    uint32_t l = (uint32_t)floor((y - lo) / (hi - lo) * 65536.0);
+    return (l + (uint32_t)r >= 65536u) ? c + 1 : c;
+}
+
+/* floor(log2 A) - emax, for finite A > 0. */
+static int mini_scale_exp(const mini_t *F, float A)
+{
+    int E;
+    frexp((double)A, &E);          /* A = f 2^E with f in [1/2, 1) */
+    return (E - 1) - mini_emax(F);
+}
+
+static int mini_encode(const mini_t *F, float x, float A, int32_t r)
+{
+    if (!isfinite(A)) return 0;
+    int s = A > 0.0f ? mini_scale_exp(F, A) : 0;
+    int c = mini_round(F, ldexp(fabs((double)x), -s), r);
+    if (F->sign && signbit(x)) c |= F->sign;
+    return c;
+}
+
+static float mini_decode(const mini_t *F, int code, float A)
+{
+    if (!isfinite(A)) return NAN;
+    int neg = F->sign && (code & F->sign);
+    int mag = F->sign ? (code & (F->sign - 1)) : code;
+    if (mag == F->nan_code) return NAN;
+    if (A == 0.0f) return neg ? -0.0f : 0.0f;
+    float x = (float)ldexp(mini_value(F, mag), mini_scale_exp(F, A));
+    return neg ? -x : x;
+}
+
+static int mini_get(int nib, const uint8_t *s, int64_t j)
+{
+    return nib ? (s[j >> 1] >> (4 * (j & 1))) & 0xF : s[j];
+}
+
+static void mini_put(int nib, uint8_t *s, int64_t j, int c)
+{
+    if (!nib) { s[j] = (uint8_t)c; return; }
+    int sh = 4 * (int)(j & 1);
+    s[j >> 1] = (uint8_t)((s[j >> 1] & ~(0xF << sh)) | (c << sh));
+}
+
+/* The 16-bit random integer of element j for state `which`: 0 = m (low half
+ * of the element's word), 1 = v (high half), 2 = m2 (low half of the word of
+ * the second stream). */
+static int32_t rand16(const orc_hp *hp, int64_t j, int which)
+{
+    uint32_t w = sr_word(hp->seed, hp->step, hp->tensor_index, hp->index_base + j, which == 2);
+    return (int32_t)(which == 1 ? w >> 16 : w & 0xFFFFu);
+}
+
+static void mini_store_block(const mini_t *F, int nib, int sr, int which, const orc_hp *hp,
+                             const float *x, int64_t len, int64_t b0, uint8_t *codes, float *A_out)
+{
+    float A = block_absmax(x, len);
+    *A_out = A;
+    for (int64_t i = 0; i < len; ++i)
+        mini_put(nib, codes, b0 + i, mini_encode(F, x[i], A, sr ? rand16(hp, b0 + i, which) : -1));
+}
+
+static int step_mini(int opt, int fp4, int sr, const orc_hp *hp, float scale, int64_t n,
+                     float *p, const float *g, uint8_t *c1, uint8_t *c2, uint8_t *c3,
+                     float *a1, float *a2, float *a3)
+{
+    const mini_t *Fm = fp4 ? &MINI_E2M1 : &MINI_E4M3;
+    const mini_t *Fv = fp4 ? &MINI_E2M2U : &MINI_E4M3;
+    scalars_t s = make_scalars(hp, scale);
+    int fresh = fresh_states(hp);
+    float bm[Q8_BLOCK], bv[Q8_BLOCK], bm2[Q8_BLOCK];
+    for (int64_t b0 = 0, blk = 0; b0 < n; b0 += Q8_BLOCK, ++blk) {
+        int64_t len = (n - b0 < Q8_BLOCK) ? n - b0 : Q8_BLOCK;
+        for (int64_t i = 0; i < len; ++i) {
+            int64_t j = b0 + i;
+            float m_old = 0.0f, v_old = 0.0f, m2_old = 0.0f;
+            if (!fresh) {
+                m_old = mini_decode(Fm, mini_get(fp4, c1, j), a1[blk]);
+                v_old = mini_decode(Fv, mini_get(fp4, c2, j), a2[blk]);
+                if (opt == ORC_ADEMAMIX) m2_old = mini_decode(Fm, mini_get(fp4, c3, j), a3[blk]);
+            }
+            moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
+            p[j] = apply_update(hp, &s, p[j], r.u);
+            bm[i] = r.m; bv[i] = r.v; bm2[i] = r.m2;
+        }
+        mini_store_block(Fm, fp4, sr, 0, hp, bm, len, b0, c1, &a1[blk]);
+        mini_store_block(Fv, fp4, sr, 1, hp, bv, len, b0, c2, &a2[blk]);
+        if (opt == ORC_ADEMAMIX) mini_store_block(Fm, fp4, sr, 2, hp, bm2, len, b0, c3, &a3[blk]);
+    }
+    if (fp4 && (n & 1)) {
+        c1[n >> 1] &= 0x0F;
+        c2[n >> 1] &= 0x0F;
+        if (opt == ORC_ADEMAMIX) c3[n >> 1] &= 0x0F;
+    }
+    return 0;
+}
+
+/* Exported for tests: format id 0 = E4M3, 1 = E2M1, 2 = unsigned E2M2. */
+double orc_mini_value(int32_t f, int32_t mag) { return mini_value(mini_fmt(f), mag); }
+int32_t orc_mini_round(int32_t f, double y, int32_t r) { return mini_round(mini_fmt(f), y, r); }
+int32_t orc_mini_encode(int32_t f, float x, float A, int32_t r) { return mini_encode(mini_fmt(f), x, A, r); }
+float orc_mini_decode(int32_t f, int32_t code, float A) { return mini_decode(mini_fmt(f), code, A); }
+int32_t orc_mini_scale_exp(int32_t f, float A) { return mini_scale_exp(mini_fmt(f), A); }
+
+void orc_mini_round_array(int32_t f, const double *y, const int32_t *r, int32_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = mini_round(mini_fmt(f), y[i], r ? r[i] : -1);
 }
 
 /* One optimizer step over one tensor.  s1/s2/s3 are m (m1 for AdEMAMix), v,
@@ -402,6 +609,9 @@ int orc_step(int opt, int fmt, const orc_hp *hp, float scale, int64_t n,
     case ORC_Q8:
         return step_q8(opt, hp, scale, n, p, g, (uint8_t *)s1, (uint8_t *)s2, (uint8_t *)s3,
                        a1, a2, a3, qs, qu);
+    case ORC_FP8_RN: case ORC_FP8_SR: case ORC_FP4_RN: case ORC_FP4_SR:
+        return step_mini(opt, fmt >= ORC_FP4_RN, fmt == ORC_FP8_SR || fmt == ORC_FP4_SR, hp, scale, n,
+                         p, g, (uint8_t *)s1, (uint8_t *)s2, (uint8_t *)s3, a1, a2, a3);
     }
     return -1;
 }
@@ -436,12 +646,23 @@ int orc_unorm(int opt, int fmt, const orc_hp *hp, int64_t n, const float *p, con
               const float *qs, const float *qu, double out[2])
 {
     if (opt != ORC_ADAMW && opt != ORC_ADEMAMIX) return -1;
-    if (fmt < ORC_F32 || fmt > ORC_Q8) return -1;
+    if (fmt < ORC_F32 || fmt > ORC_FP4_SR) return -1;
     scalars_t s = make_scalars(hp, 1.0f);
+    int fresh = fresh_states(hp);
+    int fp4 = fmt >= ORC_FP4_RN;
+    const mini_t *Fm = fp4 ? &MINI_E2M1 : &MINI_E4M3;
+    const mini_t *Fv = fp4 ? &MINI_E2M2U : &MINI_E4M3;
     nsum_t su = {0.0, 0.0}, sp = {0.0, 0.0};
     for (int64_t j = 0; j < n; ++j) {
         float m, v, m2 = 0.0f;
-        if (fmt == ORC_F32) {
+        if (fresh) {
+            m = v = 0.0f;
+        } else if (fmt >= ORC_FP8_RN) {
+            int64_t blk = j / Q8_BLOCK;
+            m = mini_decode(Fm, mini_get(fp4, (const uint8_t *)s1, j), a1[blk]);
+            v = mini_decode(Fv, mini_get(fp4, (const uint8_t *)s2, j), a2[blk]);
+            if (opt == ORC_ADEMAMIX) m2 = mini_decode(Fm, mini_get(fp4, (const uint8_t *)s3, j), a3[blk]);
+        } else if (fmt == ORC_F32) {
             m = ((const float *)s1)[j];
             v = ((const float *)s2)[j];
             if (opt == ORC_ADEMAMIX) m2 = ((const float *)s3)[j];
