@@ -16,6 +16,9 @@
  *    Sec. 1.1, 3, 6.1 and 8.1 (the fused step with BF16 moments);
  *  - 8-bit blockwise states, one absmax per 256-element block: the blockwise
  *    8-bit kernel of the bitsandbytes PR;
+ *  - FP8 and FP4 states with nearest or stochastic rounding, and periodic
+ *    state resets: "When Small Updates Disappear", Sec. 2.1 (an FP8 grid with
+ *    three fraction bits, an unsigned E2M2 FP4 grid) and Sec. 5 (both fixes);
  *  - the max_unorm precondition pass and its per-tensor norm buffer: issue
  *    "Investigate SM103 bias-correction broadcast in 32-bit optimizers",
  *    Problem and Result (here without atomics, so bit-reproducible).
@@ -61,7 +64,13 @@ typedef enum {
     OPT_STATE_F32 = 0,      /* fp32 words                                          */
     OPT_STATE_BF16_RN = 1,  /* BF16 words, round to nearest even on store          */
     OPT_STATE_BF16_SR = 2,  /* BF16 words, stochastic rounding with Philox4x32-10  */
-    OPT_STATE_Q8 = 3        /* 8-bit codes + one fp32 absmax per 256 elements      */
+    OPT_STATE_Q8 = 3,       /* 8-bit codes + one fp32 absmax per 256 elements      */
+    OPT_STATE_FP8_RN = 4,   /* E4M3 codes + one fp32 absmax per 256 elements,
+                               nearest-even                                        */
+    OPT_STATE_FP8_SR = 5,   /* the same, stochastic rounding                       */
+    OPT_STATE_FP4_RN = 6,   /* 4-bit codes (m, m2: E2M1; v: unsigned E2M2), two
+                               per byte, + one fp32 absmax per 256 elements        */
+    OPT_STATE_FP4_SR = 7    /* the same, stochastic rounding                       */
 } opt_state_fmt;
 
 typedef enum { OPT_ADAMW = 0, OPT_ADEMAMIX = 1 } opt_optimizer;
@@ -74,16 +83,25 @@ typedef enum { OPT_ADAMW = 0, OPT_ADEMAMIX = 1 } opt_optimizer;
  *   s2       second moment v, read and written.
  *   s3       AdEMAMix's slow EMA m2, read and written; NULL for AdamW.
  *            State storage: OPT_STATE_F32 -> float[numel]; BF16 formats ->
- *            uint16_t[numel] BF16 words; OPT_STATE_Q8 -> uint8_t[numel] codes.
- *   absmax1..3  OPT_STATE_Q8 only: float[ceil(numel/256)] per-block absmax of
- *            s1..s3; NULL otherwise.  Blocks are 256 consecutive elements from
- *            element 0 of the tensor; the last block may be short.
+ *            uint16_t[numel] BF16 words; OPT_STATE_Q8 and FP8 -> uint8_t[numel]
+ *            codes; FP4 -> uint8_t[ceil(numel/2)], element 2i in the low
+ *            nibble of byte i (after an odd tensor's last element the high
+ *            nibble is written as 0).
+ *   absmax1..3  Q8, FP8 and FP4 only: float[ceil(numel/256)] per-block absmax
+ *            of s1..s3; NULL otherwise.  Blocks are 256 consecutive elements
+ *            from element 0 of the tensor; the last block may be short.
+ *            FP8/FP4 code a block's values as x / X, X = 2^(floor(log2 A) -
+ *            emax) with A its absmax and emax 8 (E4M3) or 2 (E2M1, E2M2),
+ *            clamped to the largest finite value (448, 6, 7); they read back
+ *            as value(code) * X.  A block whose A is 0 reads back as zeros,
+ *            one whose A is NaN or infinite as NaN.
  *   numel    element count, >= 0 (0 is a no-op).
  * Alignment: p, g, s1, s2, s3 must be 16-byte aligned (any PyTorch allocation
  * is); absmax arrays 4-byte aligned.  Buffers of different tensors must not
  * overlap.  The tensor's position k in the list keys its stochastic rounding.
  * A fresh 8-bit state is every code set to the code of 0 (127 for a signed
- * table whose entry 127 is 0, 0 for an unsigned table) and absmax 0.
+ * table whose entry 127 is 0, 0 for an unsigned table) and absmax 0; a fresh
+ * FP8 or FP4 state is all-zero bytes and absmax 0.
  */
 typedef struct {
     void *p;
@@ -104,10 +122,13 @@ typedef struct {
  *                      s_k = min(1, max_unorm*||p_k|| / ||u_k||), from the norms
  *                      opt_precondition_unorm wrote; <= 0: off (s_k = 1).
  *   step               t >= 1; the bias corrections are 1 - beta1^t, 1 - beta2^t.
- *   seed               Philox key for OPT_STATE_BF16_SR: element j of tensor k
- *                      at step t draws word j%4 of Philox4x32-10 with counter
- *                      (j>>2 low, j>>34, t, k) [k | 2^31 for m2]; the low 16 bits
- *                      round m (and m2), the high 16 bits round v.
+ *   seed               Philox key of the stochastic-rounding formats: element j
+ *                      of tensor k at step t draws word j%4 of Philox4x32-10 with
+ *                      counter (j>>2 low, j>>34, t, k) [k | 2^31 for m2]; the low
+ *                      16 bits r round m (and m2), the high 16 bits round v.
+ *                      BF16: add r to the fp32 word, keep the high half.  FP8/FP4:
+ *                      up to the next grid value iff floor(f * 2^16) + r >= 2^16,
+ *                      f the position of x / X across its grid gap.
  *   qmap_signed        OPT_STATE_Q8 only: HOST pointer to 256 floats, strictly
  *                      increasing, finite, within [-1, 1]; codebook of m and m2.
  *   qmap_unsigned      OPT_STATE_Q8 only: HOST pointer to 256 floats as above,
@@ -126,6 +147,12 @@ typedef struct {
                                    when the kernel runs (so a clipping coefficient
                                    that opt_grad_norm writes earlier on the same
                                    stream fuses into the step); NULL means 1. */
+    int64_t reset_interval;     /* R > 0: the moments restart from zero at
+                                   steps 1, R+1, 2R+1, ... (the stored states are
+                                   not read on those steps) and the bias
+                                   corrections count from there: 1 - beta^t'
+                                   with t' = (t-1) mod R + 1; the random stream
+                                   keeps the absolute t.  0: never.          */
 } opt_hparams;
 
 /* One AdamW step over the n tensors of `tensors` (host array, read during the
@@ -138,7 +165,7 @@ int opt_step_adamw(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
                    const opt_hparams *hp, const double *unorm, void *stream);
 
 /* One AdEMAMix step; arguments as opt_step_adamw, with s3 (and absmax3 for
- * OPT_STATE_Q8) required for every tensor. */
+ * the blockwise formats) required for every tensor. */
 int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
                       const opt_hparams *hp, const double *unorm, void *stream);
 
@@ -173,6 +200,18 @@ typedef struct {
  * later step on the same stream.  g must be 16-byte aligned. */
 int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm, int32_t norm_type,
                   float *coef_out, void *stream);
+
+/* Test hook: the FP8/FP4 element codec of the state formats.  elem 0 = E4M3,
+ * 1 = E2M1, 2 = unsigned E2M2.  For i < n: codes[i] = the code of x[i] in a
+ * block whose absmax is A (A >= 0 or NaN), nearest-even if r is NULL, else
+ * stochastic with the 16-bit integer r[i] & 0xFFFF; decoded[i] = the value
+ * that code reads back as.  Device arrays, asynchronous on `stream`. */
+int opt_debug_mini(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
+                   int64_t n, void *stream);
+
+/* The same, computed on the host from the same source (host arrays). */
+int opt_debug_mini_host(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes,
+                        float *decoded, int64_t n);
 
 /* Text of the last failure on the calling thread ("" if none). */
 const char *opt_last_error(void);

@@ -18,8 +18,12 @@ LIB_PATH = os.path.join(HERE, "libopt_step.so")
 OPT_OK, OPT_EINVAL, OPT_EUNSUPPORTED, OPT_EALIGN, OPT_EHIP = 0, -1, -2, -3, -4
 OPT_F32, OPT_BF16 = 0, 1
 STATE_F32, STATE_BF16_RN, STATE_BF16_SR, STATE_Q8 = 0, 1, 2, 3
+STATE_FP8_RN, STATE_FP8_SR, STATE_FP4_RN, STATE_FP4_SR = 4, 5, 6, 7
 ADAMW, ADEMAMIX = 0, 1
-FORMATS = {"f32": STATE_F32, "bf16_rn": STATE_BF16_RN, "bf16_sr": STATE_BF16_SR, "q8": STATE_Q8}
+FORMATS = {"f32": STATE_F32, "bf16_rn": STATE_BF16_RN, "bf16_sr": STATE_BF16_SR, "q8": STATE_Q8,
+           "fp8_rn": STATE_FP8_RN, "fp8_sr": STATE_FP8_SR, "fp4_rn": STATE_FP4_RN, "fp4_sr": STATE_FP4_SR}
+BLOCKED = (STATE_Q8, STATE_FP8_RN, STATE_FP8_SR, STATE_FP4_RN, STATE_FP4_SR)
+ELEM_E4M3, ELEM_E2M1, ELEM_E2M2U = 0, 1, 2
 OPTIMIZERS = {"adamw": ADAMW, "ademamix": ADEMAMIX}
 BLOCK = 256
 
@@ -46,7 +50,7 @@ class OptHparams(ctypes.Structure):
         ("weight_decay", ctypes.c_float), ("max_unorm", ctypes.c_float),
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64),
         ("qmap_signed", ctypes.c_void_p), ("qmap_unsigned", ctypes.c_void_p),
-        ("grad_scale", ctypes.c_void_p),
+        ("grad_scale", ctypes.c_void_p), ("reset_interval", ctypes.c_int64),
     ]
 
 
@@ -84,6 +88,8 @@ def lib():
             "opt_debug_set_launch": ([i64, i32], i32),
             "opt_debug_stream": ([vp, i32, vp, i32, i64, vp], i32),
             "opt_grad_norm": ([ctypes.POINTER(OptGrad), i64, vp, ctypes.c_float, i32, vp, vp], i32),
+            "opt_debug_mini": ([i32, ctypes.c_float, vp, vp, vp, vp, i64, vp], i32),
+            "opt_debug_mini_host": ([i32, ctypes.c_float, vp, vp, vp, vp, i64], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -141,13 +147,14 @@ def _as_list(tensors):
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
             weight_decay=0.0, max_unorm=0.0, step=1, seed=0, qmap_signed=None, qmap_unsigned=None,
-            grad_scale=None):
+            grad_scale=None, reset_interval=0):
     """An OptHparams record.  qmap_* are host float32 arrays (numpy or CPU
     torch tensors) of 256 entries; they are referenced, not copied, so keep
     them alive for the call.  grad_scale is a CUDA float tensor of one element
-    (for instance the clipping coefficient opt_grad_norm wrote), or None."""
+    (for instance the clipping coefficient opt_grad_norm wrote), or None.
+    reset_interval R > 0 restarts the moments from zero every R steps."""
     h = OptHparams(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
-                   int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale))
+                   int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale), int(reset_interval))
     for field, q in (("qmap_signed", qmap_signed), ("qmap_unsigned", qmap_unsigned)):
         if q is not None:
             addr = q.ctypes.data if hasattr(q, "ctypes") else q.data_ptr()
@@ -244,6 +251,22 @@ def opt_debug_stream(srcs, dsts, stream=None):
     return _check(lib().opt_debug_stream(S, len(srcs), D, len(dsts), n, _stream(stream)))
 
 
+def opt_debug_mini(elem, A, x, r, codes, decoded, stream=None):
+    return _check(lib().opt_debug_mini(int(elem), float(A), _ptr(x), _ptr(r), _ptr(codes), _ptr(decoded),
+                                       x.numel(), _stream(stream)))
+
+
+def opt_debug_mini_host(elem, A, x, r=None):
+    import numpy as np
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rr = None if r is None else np.ascontiguousarray(np.broadcast_to(np.asarray(r, dtype=np.uint32), x.shape))
+    codes = np.zeros(x.size, dtype=np.uint8)
+    dec = np.zeros(x.size, dtype=np.float32)
+    _check(lib().opt_debug_mini_host(int(elem), float(A), x.ctypes.data, None if rr is None else rr.ctypes.data,
+                                     codes.ctypes.data, dec.ctypes.data, x.size))
+    return codes, dec
+
+
 def opt_debug_set_launch(chunk, wgs_per_cu):
     return _check(lib().opt_debug_set_launch(int(chunk), int(wgs_per_cu)))
 
@@ -251,7 +274,8 @@ def opt_debug_set_launch(chunk, wgs_per_cu):
 def state_buffers(fmt, numel, optimizer="adamw", device="cuda", qmap_signed=None, qmap_unsigned=None):
     """Fresh (zero) optimizer state on the device for one tensor, as a dict of
     s1, s2[, s3][, absmax1, absmax2[, absmax3]].  8-bit codes start at the
-    code of 0 in each codebook (the index of its 0 entry) with absmax 0."""
+    code of 0 in each codebook (the index of its 0 entry) with absmax 0; FP8
+    and FP4 codes at 0 (FP4: two per byte) with absmax 0."""
     import torch
     import numpy as np
     fmt = FORMATS.get(fmt, fmt)
@@ -263,6 +287,12 @@ def state_buffers(fmt, numel, optimizer="adamw", device="cuda", qmap_signed=None
         zu = int(np.argmin(np.abs(np.asarray(qmap_unsigned, dtype=np.float64))))
         for i in range(1, nst + 1):
             out[f"s{i}"] = torch.full((numel,), zu if i == 2 else zs, dtype=torch.uint8, device=device)
+            out[f"absmax{i}"] = torch.zeros(nb, dtype=torch.float32, device=device)
+    elif fmt in BLOCKED:
+        nb = (numel + BLOCK - 1) // BLOCK
+        nbytes = (numel + 1) // 2 if fmt in (STATE_FP4_RN, STATE_FP4_SR) else numel
+        for i in range(1, nst + 1):
+            out[f"s{i}"] = torch.zeros(nbytes, dtype=torch.uint8, device=device)
             out[f"absmax{i}"] = torch.zeros(nb, dtype=torch.float32, device=device)
     else:
         dt = torch.float32 if fmt == STATE_F32 else torch.bfloat16

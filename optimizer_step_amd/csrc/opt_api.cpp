@@ -28,6 +28,8 @@ hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, 
 hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, int64_t n, hipStream_t st);
 hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, uint8_t *out, int64_t n,
                                  hipStream_t st);
+hipError_t launch_debug_mini(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
+                             int64_t n, hipStream_t st);
 hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *dst, int ndst, int64_t n,
                                const LaunchGeom &lg, hipStream_t st);
 
@@ -318,6 +320,7 @@ int check_hparams(const opt_hparams *hp, int fmt)
     if (fmt == kQ8 && (!hp->qmap_signed || !hp->qmap_unsigned))
         return fail(OPT_EINVAL, "8-bit states need qmap_signed and qmap_unsigned");
     if (hp->grad_scale && !aligned(hp->grad_scale, 4)) return fail(OPT_EALIGN, "grad_scale must be 4-byte aligned");
+    if (hp->reset_interval < 0) return fail(OPT_EINVAL, "reset_interval must be >= 0");
     return OPT_OK;
 }
 
@@ -326,7 +329,7 @@ int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
     if (n < 0) return fail(OPT_EINVAL, "n < 0");
     if (n > 0 && !t) return fail(OPT_EINVAL, "tensors is NULL");
     if (n > INT32_MAX) return fail(OPT_EINVAL, "too many tensors");
-    if (fmt < kF32 || fmt > kQ8) return fail(OPT_EINVAL, "unknown state format %d", fmt);
+    if (fmt < kF32 || fmt > kFP4SR) return fail(OPT_EINVAL, "unknown state format %d", fmt);
     for (int64_t k = 0; k < n; ++k) {
         const opt_tensor &x = t[k];
         if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
@@ -337,7 +340,7 @@ int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
         if (x.p_dtype != OPT_F32)
             return fail(OPT_EUNSUPPORTED, "tensor %lld: only fp32 parameters are provided", (long long)k);
         if (x.numel == 0) continue;
-        const bool q8 = fmt == kQ8, m2 = opt == kAdEMAMix;
+        const bool q8 = blocked(fmt), m2 = opt == kAdEMAMix;
         if (!x.p || !x.g || !x.s1 || !x.s2 || (m2 && !x.s3))
             return fail(OPT_EINVAL, "tensor %lld: missing p, g or a state", (long long)k);
         if (q8 && (!x.absmax1 || !x.absmax2 || (m2 && !x.absmax3)))
@@ -419,6 +422,10 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     a.lr = hp->lr; a.beta1 = hp->beta1; a.beta2 = hp->beta2; a.beta3 = hp->beta3;
     a.alpha = hp->alpha; a.eps = hp->eps; a.wd = hp->weight_decay; a.max_unorm = hp->max_unorm;
     a.step = hp->step;
+    // a reset every R steps restarts the moments at steps 1, R+1, 2R+1, ...
+    const int64_t R = hp->reset_interval;
+    a.bc_step = R > 0 ? (hp->step - 1) % R + 1 : hp->step;
+    a.fresh = R > 0 && a.bc_step == 1;
     a.seed = hp->seed;
     a.grad_scale = hp->grad_scale;
     return a;
@@ -493,6 +500,26 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
         if (e != hipSuccess) return hip_fail(e, pre ? "norm pre-pass launch" : "step launch");
         if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
     }
+    return OPT_OK;
+}
+
+template <class F>
+void mini_host_one(float A, float x, const uint32_t *r, int64_t i, uint8_t *codes, float *decoded)
+{
+    uint32_t c = 0;
+    if (finite_f(A)) {
+        const int nsc = mini_enc_shift<F>(A);
+        c = r ? mini_encode<F, true>(x, nsc, r[i] & 0xFFFFu) : mini_encode<F, false>(x, nsc, 0u);
+    }
+    codes[i] = (uint8_t)c;
+    decoded[i] = finite_f(A) ? mini_decode<F>(c, mini_dec_shift<F>(A)) : bitsf(0x7FC00000u);
+}
+
+int check_mini(int32_t elem, float A, const float *x, uint8_t *codes, float *decoded, int64_t n)
+{
+    if (elem < 0 || elem > 2) return fail(OPT_EINVAL, "elem must be 0 (E4M3), 1 (E2M1) or 2 (unsigned E2M2)");
+    if (n < 0 || (n > 0 && (!x || !codes || !decoded))) return fail(OPT_EINVAL, "bad arguments");
+    if (A == A && A < 0.0f) return fail(OPT_EINVAL, "A must not be negative");
     return OPT_OK;
 }
 
@@ -681,6 +708,29 @@ int opt_debug_quantize_host(const float *qmap, int32_t is_signed, const float *x
         out[i] = (uint8_t)q8_lookup(v, B.entries.data(), P, is_signed != 0);
     }
     return OPT_OK;
+}
+
+
+int opt_debug_mini_host(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
+                        int64_t n)
+{
+    int rc = check_mini(elem, A, x, codes, decoded, n);
+    if (rc != OPT_OK) return rc;
+    for (int64_t i = 0; i < n; ++i) {
+        if (elem == 0) mini_host_one<E4M3>(A, x[i], r, i, codes, decoded);
+        else if (elem == 1) mini_host_one<E2M1>(A, x[i], r, i, codes, decoded);
+        else mini_host_one<E2M2U>(A, x[i], r, i, codes, decoded);
+    }
+    return OPT_OK;
+}
+
+int opt_debug_mini(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
+                   int64_t n, void *stream)
+{
+    int rc = check_mini(elem, A, x, codes, decoded, n);
+    if (rc != OPT_OK || n == 0) return rc;
+    hipError_t e = launch_debug_mini(elem, A, x, r, codes, decoded, n, (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "debug mini launch");
 }
 
 int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n)

@@ -141,8 +141,10 @@ __host__ __device__ inline uint32_t philox_word(const PhiloxOut &o, int i)
 // (r = a - b*q exactly by fma, q += r*y) makes it faithful, and a second
 // correction then yields the correctly rounded quotient (Markstein's theorem:
 // y within half an ulp of 1/b and q faithful => RN(q + r*y) = RN(a/b)).
-// Requires b and 1/b normal and a/b not below the normal range; callers check
-// b and treat tiny quotients as described where they use it.
+// Requires b and 1/b normal, a/b not below the normal range, and |a| >= 2^-100
+// or a = 0: the residual is exact only while ulp(b)*ulp(q) >= 2^-149, which
+// holds for e(a) >= -102 since e(a) is e(b) + e(q) within one.  Callers check
+// b and the dividends as described where they use it.
 __host__ __device__ inline float div_by(float a, float b, float y)
 {
     float q = a * y;
@@ -195,6 +197,112 @@ __host__ __device__ inline uint32_t q8_lookup(float x, const uint32_t *tab, cons
 }
 
 // ---------------------------------------------------------------------------
+// FP8 and FP4 state elements ("When Small Updates Disappear", Sec. 2.1: grids
+// with three and two fraction bits; Sec. 5: such states with nearest or
+// stochastic rounding).  FP8 is OCP E4M3 (no infinities, magnitude 0x7F is
+// NaN); FP4 stores m and m2 as OCP E2M1 and v, which is never negative, as
+// unsigned E2M2.  A 256-element block keeps its absmax A; its elements are
+// coded as x / X with X = 2^(floor(log2 A) - EMAX), EMAX the exponent of the
+// format's top binade, so the block maximum lands in the top binade and the
+// grid keeps its relative spacing.  Codes come straight from the binary32
+// bits of x / X: exponent and top fraction bits give the code below, and the
+// dropped bits decide nearest-even or stochastic rounding (up iff the top 16
+// dropped bits plus the element's 16-bit random integer carry, the rule of
+// Sec. 6.1); values past the largest finite one take it.
+
+template <int MB, int BIAS, uint32_t MAXC, uint32_t SIGN, int NANC>
+struct MiniFmt {
+    static constexpr int kMB = MB;                      // fraction bits
+    static constexpr int kBias = BIAS;
+    static constexpr int kEmin = 1 - BIAS;              // exponent of the smallest normal
+    static constexpr int kEmax = (int)(MAXC >> MB) - BIAS;
+    static constexpr uint32_t kMaxC = MAXC;             // largest finite magnitude code
+    static constexpr uint32_t kSign = SIGN;             // sign bit of a code, 0 if unsigned
+    static constexpr int kNan = NANC;                   // NaN magnitude code, -1 if none
+};
+using E4M3 = MiniFmt<3, 7, 0x7Eu, 0x80u, 0x7F>;
+using E2M1 = MiniFmt<1, 1, 0x7u, 0x8u, -1>;
+using E2M2U = MiniFmt<2, 1, 0xFu, 0u, -1>;
+
+// floor(log2 A) for finite A > 0 (binary32 subnormals included).
+__host__ __device__ inline int floor_log2(float A)
+{
+    const uint32_t u = fbits(A) & 0x7FFFFFFFu;
+    const int ef = (int)(u >> 23);
+    return ef ? ef - 127 : -118 - __builtin_clz(u);
+}
+
+__host__ __device__ inline bool finite_f(float A) { return (fbits(A) & 0x7F800000u) != 0x7F800000u; }
+
+// Exponent shift that takes a block's values to its grid (x * 2^nsc), from
+// the block absmax: 0 if A is 0 (all elements are zeros).
+template <class F>
+__host__ __device__ inline int mini_enc_shift(float A)
+{
+    return A > 0.0f ? F::kEmax - floor_log2(A) : 0;
+}
+
+// Exponent that takes grid values back (v * 2^sc); a zero absmax reads every
+// element as a zero of its sign (2^-400 flushes any grid value to zero).
+template <class F>
+__host__ __device__ inline int mini_dec_shift(float A)
+{
+    return A > 0.0f ? floor_log2(A) - F::kEmax : -400;
+}
+
+// Magnitude code of y >= 0 on F's grid; SR with the 16-bit integer r.
+template <class F, bool SR>
+__host__ __device__ inline uint32_t mini_mag(float y, uint32_t r)
+{
+    const uint32_t u = fbits(y) & 0x7FFFFFFFu;
+    const int ef = (int)(u >> 23);
+    const uint32_t M = (u & 0x7FFFFFu) | (ef ? 0x800000u : 0u);   // y = M * 2^(e - 23)
+    const int e = ef ? ef - 127 : -126;
+    const int eg = e > F::kEmin ? e : F::kEmin;                   // binade of the grid step
+    int sh = 23 - F::kMB + (eg - e);                              // y / step = M >> sh, rest below
+    if (sh > 40) sh = 40;                                         // y / step < 2^-16: code 0, no carry
+    uint32_t code = ((uint32_t)(eg - F::kEmin) << F::kMB) + (sh < 32 ? M >> sh : 0u);
+    const uint32_t rem = sh < 32 ? (M & ((1u << sh) - 1u)) : M;
+    bool up;
+    if (SR) {
+        up = (rem >> (sh - 16)) + r >= 65536u;
+    } else {
+        const uint32_t half = sh <= 24 ? 1u << (sh - 1) : 0u;     // sh > 24: below half a step
+        up = sh <= 24 && (rem > half || (rem == half && (code & 1u)));
+    }
+    code += up ? 1u : 0u;
+    return code < F::kMaxC ? code : F::kMaxC;
+}
+
+template <class F, bool SR>
+__host__ __device__ inline uint32_t mini_encode(float x, int nsc, uint32_t r)
+{
+    // exact unless x * 2^nsc falls below the binary32 normal range, where it
+    // is far below the grid's smallest step and codes as 0 either way
+    uint32_t c = mini_mag<F, SR>(ldexpf(x, nsc), r);
+    if (F::kSign && (fbits(x) >> 31)) c |= F::kSign;
+    return c;
+}
+
+// Grid value of a magnitude code (exact in binary32).
+template <class F>
+__host__ __device__ inline float mini_val(uint32_t mag)
+{
+    const uint32_t e = mag >> F::kMB, f = mag & ((1u << F::kMB) - 1u);
+    if (e == 0) return ldexpf((float)f, 1 - F::kBias - F::kMB);
+    return bitsf(((e + 127u - (uint32_t)F::kBias) << 23) | (f << (23 - F::kMB)));
+}
+
+template <class F>
+__host__ __device__ inline float mini_decode(uint32_t code, int sc)
+{
+    const uint32_t mag = F::kSign ? code & (F::kSign - 1u) : code;
+    float x = ldexpf(mini_val<F>(mag), sc);
+    if (F::kNan >= 0 && mag == (uint32_t)F::kNan) x = bitsf(0x7FC00000u);
+    return (F::kSign && (code & F::kSign)) ? -x : x;
+}
+
+// ---------------------------------------------------------------------------
 // Bias corrections and the other per-call scalars.  Formed once per
 // workgroup by one lane and published through LDS (the issue "Investigate
 // SM103 bias-correction broadcast in 32-bit optimizers", Problem: they are
@@ -226,10 +334,12 @@ __device__ inline Scalars make_scalars(const StepArgs &a)
     s.om1 = 1.0f - a.beta1;
     s.om2 = 1.0f - a.beta2;
     s.om3 = 1.0f - a.beta3;
-    s.c1 = (float)(1.0 - powi((double)a.beta1, a.step));
-    s.c2 = (float)(1.0 - powi((double)a.beta2, a.step));
+    s.c1 = (float)(1.0 - powi((double)a.beta1, a.bc_step));
+    s.c2 = (float)(1.0 - powi((double)a.beta2, a.bc_step));
     // 0 <= beta < 1 (checked by the host) keeps c in [2^-24, 1], where div_by
-    // by c is exact
+    // by c is correctly rounded for every moment of magnitude >= 2^-100; a
+    // smaller moment's m_hat or v_hat (which only feed the direction u, never
+    // a stored state) may be an ulp off
     s.rc1 = 1.0f / s.c1;
     s.rc2 = 1.0f / s.c2;
     float lrwd = a.lr * a.wd;

@@ -110,15 +110,18 @@ struct Group {
 };
 
 template <int OPT, int GD, int SF>
-__device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, Group &x)
+__device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fresh, Group &x)
 {
     f4 pv = sld<f4>(T.p + e);
     x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
     load_grad4<GD>(T.g, e, x.g);
-    load_state4<SF>(T.s1, e, x.m);
-    load_state4<SF>(T.s2, e, x.v);
-    if (OPT == kAdEMAMix) load_state4<SF>(T.s3, e, x.m2);
-    else x.m2[0] = x.m2[1] = x.m2[2] = x.m2[3] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.m[i] = x.v[i] = x.m2[i] = 0.0f;
+    if (!fresh) {   // a step that restarts the moments from zero reads none
+        load_state4<SF>(T.s1, e, x.m);
+        load_state4<SF>(T.s2, e, x.v);
+        if (OPT == kAdEMAMix) load_state4<SF>(T.s3, e, x.m2);
+    }
 }
 
 template <int OPT, int GD, int SF>
@@ -154,8 +157,12 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
                                           int64_t e, float lam)
 {
     float g = load_grad1<GD>(T.g, e);
-    float m = load_state1<SF>(T.s1, e), v = load_state1<SF>(T.s2, e);
-    float m2 = OPT == kAdEMAMix ? load_state1<SF>(T.s3, e) : 0.0f;
+    float m = 0.0f, v = 0.0f, m2 = 0.0f;
+    if (!a.fresh) {
+        m = load_state1<SF>(T.s1, e);
+        v = load_state1<SF>(T.s2, e);
+        if (OPT == kAdEMAMix) m2 = load_state1<SF>(T.s3, e);
+    }
     Mom r = moments<OPT>(s, a, g, m, v, m2);
     gst<float>(T.p + e, apply_update(gld<float>(T.p + e), s.d, lam, r.u));
     uint32_t rm = 0, rv = 0, rm2 = 0;
@@ -187,6 +194,7 @@ __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const Dev
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
+    const bool fresh = a.fresh != 0;
     for (int64_t c = first_chunk(); c < a.nchunks; c += gridDim.x) {
         const DevTensor T = tens[ctab[c]];
         const int64_t e0 = (c - T.chunk_begin) * a.chunk;
@@ -198,13 +206,13 @@ __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const Dev
         for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
             Group x[kEwGroups];
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF>(T, e0 + 4 * (i + u * kThreads), x[u]);
+            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF>(T, e0 + 4 * (i + u * kThreads), fresh, x[u]);
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
         }
         for (; i < ngroups; i += kThreads) {
             Group x0;
-            ew_load<OPT, GD, SF>(T, e0 + 4 * i, x0);
+            ew_load<OPT, GD, SF>(T, e0 + 4 * i, fresh, x0);
             ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, lam, x0);
         }
         const int64_t tail = len & 3;
@@ -216,14 +224,18 @@ __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const Dev
 // 8-bit blockwise states
 
 // Codes of this lane's four fp32 moments against their block absmax A (a
-// wave-uniform value).  When A and 1/A are normal, div_by gives the correctly
-// rounded x = m'/A (|x| <= 1); otherwise x = 0 for A = 0, else the correctly
-// rounded m'/A, and a NaN quotient (A NaN or infinite) gets code 0.
+// wave-uniform value).  When A and 1/A are normal and no moment of the wave is
+// a nonzero value below 2^-100, div_by gives the correctly rounded x = m'/A
+// (|x| <= 1); otherwise x = 0 for A = 0, else the correctly rounded m'/A, and
+// a NaN quotient (A NaN or infinite) gets code 0.
 template <bool SIGNED>
 __device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint32_t *lds, const QTabParams &P)
 {
     uint32_t out = 0;
-    if (div_by_ok(A)) {
+    bool tiny = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tiny |= (fbits(x[i]) & 0x7FFFFFFFu) - 1u < 0x0D7FFFFFu;   // 0 < |x| < 2^-100
+    if (div_by_ok(A) && !__any(tiny)) {
         const float y = 1.0f / A;
 #pragma unroll
         for (int i = 0; i < 4; ++i) out |= q8_code(div_by(x[i], A, y), lds, P, SIGNED) << (8 * i);
@@ -253,35 +265,84 @@ __device__ __forceinline__ float block_absmax(const float x[4])
 struct QChunk {
     float *p;
     const uint8_t *g;      // bytes
-    uint8_t *s1, *s2, *s3;
+    uint8_t *s1, *s2, *s3; // bytes (FP4: two elements per byte)
     float *a1, *a2, *a3;
+    int64_t e0;            // the chunk's first element within its tensor
+    int32_t k;             // the tensor's position in the caller's list
 };
 
-template <int GD>
+template <int GD, int SF>
 __device__ __forceinline__ QChunk q8_chunk(const DevTensor &T, int64_t e0)
 {
+    const int64_t sb = fp4_fmt(SF) ? e0 / 2 : e0;
     QChunk c;
     c.p = T.p + e0;
     c.g = (const uint8_t *)T.g + e0 * (GD == kGradF32 ? 4 : 2);
-    c.s1 = (uint8_t *)T.s1 + e0;
-    c.s2 = (uint8_t *)T.s2 + e0;
-    c.s3 = (uint8_t *)T.s3 + e0;
+    c.s1 = (uint8_t *)T.s1 + sb;
+    c.s2 = (uint8_t *)T.s2 + sb;
+    c.s3 = (uint8_t *)T.s3 + sb;
     c.a1 = T.a1 + e0 / kQBlock;
     c.a2 = T.a2 + e0 / kQBlock;
     c.a3 = T.a3 + e0 / kQBlock;
+    c.e0 = e0;
+    c.k = T.k;
     return c;
 }
 
-// One lane's four elements of a 256-element block, as loaded.
+// One lane's four elements of a 256-element block, as loaded.  Codes are
+// packed in element order: 8 bits each, or 4 bits each for FP4.
 struct QIn {
     float p[4], g[4];
     uint32_t cm, cv, cm2;
     float A1, A2, A3;
 };
 
-// Block b of the chunk (elements 256*b ..); lanes own 4 elements each.
-template <int OPT, int GD, bool FULL>
-__device__ __forceinline__ void q8_load(const QChunk &C, uint32_t b, int nmine, int lane, QIn &x)
+// Four codes of one state at element e (a multiple of 4) of the chunk.
+template <int SF, bool FULL>
+__device__ __forceinline__ uint32_t load_codes(const uint8_t *s, uint32_t e, int nmine)
+{
+    if (fp4_fmt(SF)) {
+        if (FULL || nmine == 4) return sld<uint16_t>(s + e / 2);
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2)
+            if (i < nmine) c |= (uint32_t)gld<uint8_t>(s + e / 2 + i / 2) << (4 * i);
+        return nmine & 1 ? c & ~(0xFu << (4 * nmine)) : c;
+    }
+    if (FULL || nmine == 4) return sld<uint32_t>(s + e);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i < nmine) c |= (uint32_t)gld<uint8_t>(s + e + i) << (8 * i);
+    return c;
+}
+
+template <int SF, bool FULL>
+__device__ __forceinline__ void store_codes(uint8_t *s, uint32_t e, int nmine, uint32_t c)
+{
+    if (fp4_fmt(SF)) {
+        if (FULL || nmine == 4) { sst<uint16_t>(s + e / 2, (uint16_t)c); return; }
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            if (i < nmine) {
+                // past an odd tensor's last element the high nibble is 0
+                const uint32_t hi = i + 1 < nmine ? (c >> (4 * i + 4)) & 0xFu : 0u;
+                gst<uint8_t>(s + e / 2 + i / 2, (uint8_t)(((c >> (4 * i)) & 0xFu) | (hi << 4)));
+            }
+        }
+        return;
+    }
+    if (FULL || nmine == 4) { sst<uint32_t>(s + e, c); return; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i < nmine) gst<uint8_t>(s + e + i, (uint8_t)(c >> (8 * i)));
+}
+
+// Block b of the chunk (elements 256*b ..); lanes own 4 elements each.  A
+// step that starts the moments from zero reads no state.
+template <int OPT, int GD, int SF, bool FULL>
+__device__ __forceinline__ void q8_load(const StepArgs &a, const QChunk &C, uint32_t b, int nmine, int lane,
+                                        QIn &x)
 {
     if (FULL) nmine = 4;
     const uint32_t e = b * kQBlock + lane * 4;
@@ -295,45 +356,93 @@ __device__ __forceinline__ void q8_load(const QChunk &C, uint32_t b, int nmine, 
             u2 w = sld<u2>(C.g + 2 * e);
             x.g[0] = bf16_lo(w.x); x.g[1] = bf16_hi(w.x); x.g[2] = bf16_lo(w.y); x.g[3] = bf16_hi(w.y);
         }
-        x.cm = sld<uint32_t>(C.s1 + e);
-        x.cv = sld<uint32_t>(C.s2 + e);
-        x.cm2 = OPT == kAdEMAMix ? sld<uint32_t>(C.s3 + e) : 0u;
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { x.p[i] = 0.0f; x.g[i] = 0.0f; }
-        x.cm = x.cv = x.cm2 = 0;
-#pragma unroll
         for (int i = 0; i < 4; ++i) {
+            x.p[i] = 0.0f;
+            x.g[i] = 0.0f;
             if (i < nmine) {
                 x.p[i] = gld<float>(C.p + e + i);
                 x.g[i] = GD == kGradF32 ? gld<float>(C.g + 4 * (e + i)) : bf16_lo(gld<uint16_t>(C.g + 2 * (e + i)));
-                x.cm |= (uint32_t)gld<uint8_t>(C.s1 + e + i) << (8 * i);
-                x.cv |= (uint32_t)gld<uint8_t>(C.s2 + e + i) << (8 * i);
-                if (OPT == kAdEMAMix) x.cm2 |= (uint32_t)gld<uint8_t>(C.s3 + e + i) << (8 * i);
             }
         }
     }
-    x.A1 = gld<float>(C.a1 + b);
-    x.A2 = gld<float>(C.a2 + b);
-    x.A3 = OPT == kAdEMAMix ? gld<float>(C.a3 + b) : 0.0f;
+    x.cm = x.cv = x.cm2 = 0;
+    x.A1 = x.A2 = x.A3 = 0.0f;
+    if (!a.fresh) {
+        x.cm = load_codes<SF, FULL>(C.s1, e, nmine);
+        x.cv = load_codes<SF, FULL>(C.s2, e, nmine);
+        if (OPT == kAdEMAMix) x.cm2 = load_codes<SF, FULL>(C.s3, e, nmine);
+        x.A1 = gld<float>(C.a1 + b);
+        x.A2 = gld<float>(C.a2 + b);
+        if (OPT == kAdEMAMix) x.A3 = gld<float>(C.a3 + b);
+    }
+}
+
+// Four stored values of one state.  WHICH: 0 = m, 1 = v, 2 = m2.
+template <int SF, int WHICH>
+__device__ __forceinline__ void blk_decode4(const uint32_t *lds, uint32_t c, float A, float out[4])
+{
+    if (SF == kQ8) {
+        const float *tab = (const float *)lds + (WHICH == 1 ? 256 : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = tab[(c >> (8 * i)) & 0xFFu] * A;
+    } else if (fp4_fmt(SF) && WHICH == 1) {
+        const int sc = mini_dec_shift<E2M2U>(A);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = mini_decode<E2M2U>((c >> (4 * i)) & 0xFu, sc);
+    } else if (fp4_fmt(SF)) {
+        const int sc = mini_dec_shift<E2M1>(A);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = mini_decode<E2M1>((c >> (4 * i)) & 0xFu, sc);
+    } else {
+        const int sc = mini_dec_shift<E4M3>(A);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = mini_decode<E4M3>((c >> (8 * i)) & 0xFFu, sc);
+    }
+    if (mini_fmt(SF) && !finite_f(A)) {          // a poisoned block reads as NaN
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = bitsf(0x7FC00000u);
+    }
+}
+
+template <class F, bool SR>
+__device__ __forceinline__ uint32_t mini_pack4(const float x[4], float A, const uint32_t r[4])
+{
+    if (!finite_f(A)) return 0u;
+    const int nsc = mini_enc_shift<F>(A);
+    constexpr int W = (F::kSign == 0x80u) ? 8 : 4;
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out |= mini_encode<F, SR>(x[i], nsc, r[i]) << (W * i);
+    return out;
+}
+
+template <int SF, int WHICH>
+__device__ __forceinline__ uint32_t blk_encode4(const uint32_t *lds, const StepArgs &a, const float x[4], float A,
+                                                const uint32_t r[4])
+{
+    constexpr bool SR = sr_fmt(SF);
+    if (SF == kQ8) return WHICH == 1 ? quant4<false>(x, A, lds, a.q.u) : quant4<true>(x, A, lds, a.q.s);
+    if (fp4_fmt(SF)) return WHICH == 1 ? mini_pack4<E2M2U, SR>(x, A, r) : mini_pack4<E2M1, SR>(x, A, r);
+    return mini_pack4<E4M3, SR>(x, A, r);
 }
 
 // FULL: every lane holds four elements (all blocks but a tensor's short last one).
-template <int OPT, bool FULL>
+template <int OPT, int SF, bool FULL>
 __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const QChunk &C,
                                           const uint32_t *lds, uint32_t b, int nmine, int lane, float lam,
                                           const QIn &x)
 {
     if (FULL) nmine = 4;
-    const float *TS = (const float *)lds;
-    const float *TU = TS + 256;
     const uint32_t e = b * kQBlock + lane * 4;
-    float m_in[4], v_in[4], m2_in[4];
+    float m_in[4], v_in[4], m2_in[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    blk_decode4<SF, 0>(lds, x.cm, x.A1, m_in);
+    blk_decode4<SF, 1>(lds, x.cv, x.A2, v_in);
+    if (OPT == kAdEMAMix) blk_decode4<SF, 2>(lds, x.cm2, x.A3, m2_in);
+    if (a.fresh) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m_in[i] = TS[(x.cm >> (8 * i)) & 0xFFu] * x.A1;
-        v_in[i] = TU[(x.cv >> (8 * i)) & 0xFFu] * x.A2;
-        m2_in[i] = OPT == kAdEMAMix ? TS[(x.cm2 >> (8 * i)) & 0xFFu] * x.A3 : 0.0f;
+        for (int i = 0; i < 4; ++i) m_in[i] = v_in[i] = m2_in[i] = 0.0f;
     }
     // The stored moments are exact binary32; only the direction u (for p)
     // takes the fast path, unless some v_hat in the wave is tiny or NaN.
@@ -357,31 +466,38 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
         vo[i] = valid ? r[i].v : 0.0f;
         m2o[i] = valid ? r[i].m2 : 0.0f;
     }
+    // stochastic rounding: the element's Philox word, low half for m, high
+    // half for v, low half of the second stream's word for m2
+    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0};
+    if (sr_fmt(SF)) {
+        const uint64_t q = (uint64_t)(C.e0 + e) >> 2;
+        PhiloxOut w = sr_block(a.seed, a.step, C.k, q, false);
+        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
+        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
+        if (OPT == kAdEMAMix) {
+            PhiloxOut w2 = sr_block(a.seed, a.step, C.k, q, true);
+            rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
+        }
+    }
     const float Am = block_absmax(mo), Av = block_absmax(vo);
-    const uint32_t om = quant4<true>(mo, Am, lds, a.q.s);
-    const uint32_t ov = quant4<false>(vo, Av, lds, a.q.u);
+    const uint32_t om = blk_encode4<SF, 0>(lds, a, mo, Am, rm);
+    const uint32_t ov = blk_encode4<SF, 1>(lds, a, vo, Av, rv);
     uint32_t om2 = 0;
     float Am2 = 0.0f;
     if (OPT == kAdEMAMix) {
         Am2 = block_absmax(m2o);
-        om2 = quant4<true>(m2o, Am2, lds, a.q.s);
+        om2 = blk_encode4<SF, 2>(lds, a, m2o, Am2, rm2);
     }
     if (nmine == 4) {
         sst<f4>(C.p + e, f4{p[0], p[1], p[2], p[3]});
-        sst<uint32_t>(C.s1 + e, om);
-        sst<uint32_t>(C.s2 + e, ov);
-        if (OPT == kAdEMAMix) sst<uint32_t>(C.s3 + e, om2);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < nmine) {
-                gst<float>(C.p + e + i, p[i]);
-                gst<uint8_t>(C.s1 + e + i, (uint8_t)(om >> (8 * i)));
-                gst<uint8_t>(C.s2 + e + i, (uint8_t)(ov >> (8 * i)));
-                if (OPT == kAdEMAMix) gst<uint8_t>(C.s3 + e + i, (uint8_t)(om2 >> (8 * i)));
-            }
-        }
+        for (int i = 0; i < 4; ++i)
+            if (i < nmine) gst<float>(C.p + e + i, p[i]);
     }
+    store_codes<SF, FULL>(C.s1, e, nmine, om);
+    store_codes<SF, FULL>(C.s2, e, nmine, ov);
+    if (OPT == kAdEMAMix) store_codes<SF, FULL>(C.s3, e, nmine, om2);
     if (lane == 0) {
         gst<float>(C.a1 + b, Am);
         gst<float>(C.a2 + b, Av);
@@ -402,13 +518,14 @@ __device__ __forceinline__ int q8_mine(const DevTensor &T, int64_t eb, int lane)
 #ifndef OPT_Q8_BLOCKS
 #define OPT_Q8_BLOCKS 2
 #endif
-// Workgroup size of the 8-bit kernel (one LDS copy of the tables per
-// workgroup) and full blocks in flight per wave.
+// Workgroup size of the blockwise kernel (one LDS copy of the 8-bit tables
+// per workgroup) and full blocks in flight per wave.
 constexpr int kQ8Threads = OPT_Q8_THREADS;
 constexpr int kQ8Waves = kQ8Threads / 64;
 constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
 
-template <int OPT, int GD>
+// Blockwise states (8-bit codebook, FP8, FP4): one 256-element block per wave.
+template <int OPT, int GD, int SF>
 __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__restrict__ tens,
                                                              const int32_t *__restrict__ ctab,
                                                              const uint32_t *__restrict__ qwords,
@@ -416,7 +533,8 @@ __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__
 {
     extern __shared__ uint32_t lds[];
     __shared__ Scalars sh;
-    for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
+    if (SF == kQ8)
+        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
@@ -430,26 +548,27 @@ __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__
         const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
         const uint32_t nblk = (uint32_t)((len + kQBlock - 1) / kQBlock);
         const uint32_t nfull = (uint32_t)(len / kQBlock);
-        const QChunk C = q8_chunk<GD>(T, e0);
+        const QChunk C = q8_chunk<GD, SF>(T, e0);
         uint32_t b = wave;
         // kQ8Blocks full blocks per iteration: all their loads before any math
         for (; b + (kQ8Blocks - 1) * kQ8Waves < nfull; b += kQ8Blocks * kQ8Waves) {
             QIn x[kQ8Blocks];
 #pragma unroll
-            for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, true>(C, b + u * kQ8Waves, 4, lane, x[u]);
+            for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, SF, true>(a, C, b + u * kQ8Waves, 4, lane, x[u]);
 #pragma unroll
-            for (int u = 0; u < kQ8Blocks; ++u) q8_finish<OPT, true>(a, s, C, lds, b + u * kQ8Waves, 4, lane, lam, x[u]);
+            for (int u = 0; u < kQ8Blocks; ++u)
+                q8_finish<OPT, SF, true>(a, s, C, lds, b + u * kQ8Waves, 4, lane, lam, x[u]);
         }
         for (; b < nfull; b += kQ8Waves) {
             QIn x0;
-            q8_load<OPT, GD, true>(C, b, 4, lane, x0);
-            q8_finish<OPT, true>(a, s, C, lds, b, 4, lane, lam, x0);
+            q8_load<OPT, GD, SF, true>(a, C, b, 4, lane, x0);
+            q8_finish<OPT, SF, true>(a, s, C, lds, b, 4, lane, lam, x0);
         }
         if (b < nblk) {   // the tensor's short last block
             const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
             QIn x0;
-            q8_load<OPT, GD, false>(C, b, nm, lane, x0);
-            q8_finish<OPT, false>(a, s, C, lds, b, nm, lane, lam, x0);
+            q8_load<OPT, GD, SF, false>(a, C, b, nm, lane, x0);
+            q8_finish<OPT, SF, false>(a, s, C, lds, b, nm, lane, lam, x0);
         }
     }
 }
@@ -462,32 +581,32 @@ __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__
 // depends on the chunk size, the grid or timing, and there are no atomics, so
 // repeated runs give identical bits.
 
-template <int SF>
-__device__ __forceinline__ float read_state(const uint32_t *lds, const void *s, const float *amax,
-                                            bool is_signed, int64_t e)
+// One stored state value at element e of a tensor.  WHICH: 0 = m, 1 = v, 2 = m2.
+template <int SF, int WHICH>
+__device__ __forceinline__ float read_state(const uint32_t *lds, const void *s, const float *amax, int64_t e)
 {
-    if (SF == kQ8) {
-        const float *tab = (const float *)lds + (is_signed ? 0 : 256);
-        return tab[gld<uint8_t>((const uint8_t *)s + e)] * gld<float>(amax + e / kQBlock);
-    }
-    return load_state1<SF == kF32 ? kF32 : kBF16RN>(s, e);
+    if (SF == kF32 || SF == kBF16RN) return load_state1<SF == kF32 ? kF32 : kBF16RN>(s, e);
+    uint32_t c;
+    if (fp4_fmt(SF)) c = ((uint32_t)gld<uint8_t>((const uint8_t *)s + e / 2) >> (4 * (e & 1))) & 0xFu;
+    else c = gld<uint8_t>((const uint8_t *)s + e);
+    float out[4];
+    blk_decode4<SF, WHICH>(lds, c, gld<float>(amax + e / kQBlock), out);
+    return out[0];
 }
 
-// Four consecutive state values starting at e (a multiple of 4, so one 8-bit
-// block holds all four).
-template <int SF>
-__device__ __forceinline__ void read_state4(const uint32_t *lds, const void *s, const float *amax,
-                                            bool is_signed, int64_t e, float out[4])
+// Four consecutive state values starting at e (a multiple of 4, so one block
+// holds all four).
+template <int SF, int WHICH>
+__device__ __forceinline__ void read_state4(const uint32_t *lds, const void *s, const float *amax, int64_t e,
+                                            float out[4])
 {
-    if (SF == kQ8) {
-        const float *tab = (const float *)lds + (is_signed ? 0 : 256);
-        const uint32_t c = sld<uint32_t>((const uint8_t *)s + e);
-        const float A = gld<float>(amax + e / kQBlock);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = tab[(c >> (8 * i)) & 0xFFu] * A;
-    } else {
+    if (SF == kF32 || SF == kBF16RN) {
         load_state4<SF == kF32 ? kF32 : kBF16RN>(s, e, out);
+        return;
     }
+    const uint32_t c = fp4_fmt(SF) ? (uint32_t)sld<uint16_t>((const uint8_t *)s + e / 2)
+                                   : sld<uint32_t>((const uint8_t *)s + e);
+    blk_decode4<SF, WHICH>(lds, c, gld<float>(amax + e / kQBlock), out);
 }
 
 template <int OPT, int GD, int SF>
@@ -523,10 +642,14 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
                     f4 pv = sld<f4>(T.p + e);
                     p[q][0] = pv.x; p[q][1] = pv.y; p[q][2] = pv.z; p[q][3] = pv.w;
                     load_grad4<GD>(T.g, e, g[q]);
-                    read_state4<SF>(lds, T.s1, T.a1, true, e, m[q]);
-                    read_state4<SF>(lds, T.s2, T.a2, false, e, v[q]);
-                    if (OPT == kAdEMAMix) read_state4<SF>(lds, T.s3, T.a3, true, e, m2[q]);
-                    else m2[q][0] = m2[q][1] = m2[q][2] = m2[q][3] = 0.0f;
+                    m[q][0] = m[q][1] = m[q][2] = m[q][3] = 0.0f;
+                    v[q][0] = v[q][1] = v[q][2] = v[q][3] = 0.0f;
+                    m2[q][0] = m2[q][1] = m2[q][2] = m2[q][3] = 0.0f;
+                    if (!a.fresh) {   // a step that restarts the moments reads none
+                        read_state4<SF, 0>(lds, T.s1, T.a1, e, m[q]);
+                        read_state4<SF, 1>(lds, T.s2, T.a2, e, v[q]);
+                        if (OPT == kAdEMAMix) read_state4<SF, 2>(lds, T.s3, T.a3, e, m2[q]);
+                    }
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -543,9 +666,12 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
                     for (int j = 0; j < n; ++j) {
                         const int64_t e = e0 + i0 + j;
                         float g = load_grad1<GD>(T.g, e);
-                        float m = read_state<SF>(lds, T.s1, T.a1, true, e);
-                        float v = read_state<SF>(lds, T.s2, T.a2, false, e);
-                        float m2 = OPT == kAdEMAMix ? read_state<SF>(lds, T.s3, T.a3, true, e) : 0.0f;
+                        float m = 0.0f, v = 0.0f, m2 = 0.0f;
+                        if (!a.fresh) {
+                            m = read_state<SF, 0>(lds, T.s1, T.a1, e);
+                            v = read_state<SF, 1>(lds, T.s2, T.a2, e);
+                            if (OPT == kAdEMAMix) m2 = read_state<SF, 2>(lds, T.s3, T.a3, e);
+                        }
                         Mom r = moments<OPT>(s, a, g, m, v, m2);
                         float p = gld<float>(T.p + e);
                         su += (double)r.u * (double)r.u;
@@ -748,6 +874,31 @@ __global__ void debug_quantize_kernel(QTabs q, int is_signed, const float *x, ui
     }
 }
 
+// codes[i] = the FP8/FP4 code of x[i] in a block of absmax A (nearest, or
+// stochastic with r[i]); decoded[i] = what that code reads back as.
+template <class F>
+__device__ __forceinline__ void debug_mini_one(float A, float x, const uint32_t *r, int64_t i, uint8_t *codes,
+                                               float *decoded)
+{
+    uint32_t c = 0;
+    if (finite_f(A)) {
+        const int nsc = mini_enc_shift<F>(A);
+        c = r ? mini_encode<F, true>(x, nsc, r[i] & 0xFFFFu) : mini_encode<F, false>(x, nsc, 0u);
+    }
+    codes[i] = (uint8_t)c;
+    decoded[i] = finite_f(A) ? mini_decode<F>(c, mini_dec_shift<F>(A)) : bitsf(0x7FC00000u);
+}
+
+__global__ void debug_mini_kernel(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes,
+                                  float *decoded, int64_t n)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        if (elem == 0) debug_mini_one<E4M3>(A, x[i], r, i, codes, decoded);
+        else if (elem == 1) debug_mini_one<E2M1>(A, x[i], r, i, codes, decoded);
+        else debug_mini_one<E2M2U>(A, x[i], r, i, codes, decoded);
+    }
+}
+
 template <class K>
 static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, int threads);
 
@@ -859,7 +1010,11 @@ static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg
     case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
     case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
     case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kQ8: return launch_persistent_q8(step_q8_kernel<OPT, GD>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kQ8: return launch_persistent_q8(step_q8_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP8RN: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP8RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP8SR: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP8SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP4RN: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP4RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP4SR: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP4SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     default: return hipErrorInvalidValue;
     }
 }
@@ -881,6 +1036,10 @@ static hipError_t launch_unorm_t(int fmt, const StepArgs &a, const LaunchGeom &l
     case kBF16RN:
     case kBF16SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     case kQ8: return launch_persistent(unorm_partials_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP8RN:
+    case kFP8SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kFP8RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP4RN:
+    case kFP4SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kFP4RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     default: return hipErrorInvalidValue;
     }
 }
@@ -933,6 +1092,15 @@ hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, 
     int64_t blocks = min((int64_t)4096, (n + 255) / 256);
     hipLaunchKernelGGL(debug_round_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st,
                        x, r, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_mini(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
+                             int64_t n, hipStream_t st)
+{
+    int64_t blocks = min((int64_t)1024, (n + 255) / 256);
+    hipLaunchKernelGGL(debug_mini_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st, elem, A, x, r,
+                       codes, decoded, n);
     return hipGetLastError();
 }
 

@@ -12,7 +12,13 @@ constexpr int kQBlock = 256;       // elements per 8-bit absmax block
 constexpr int kUTile = 1024;       // elements per update-norm partial
 
 enum Opt : int { kAdamW = 0, kAdEMAMix = 1 };
-enum Fmt : int { kF32 = 0, kBF16RN = 1, kBF16SR = 2, kQ8 = 3 };
+enum Fmt : int { kF32 = 0, kBF16RN = 1, kBF16SR = 2, kQ8 = 3, kFP8RN = 4, kFP8SR = 5, kFP4RN = 6, kFP4SR = 7 };
+
+// Formats stored as blocks of 256 codes with one fp32 absmax per block.
+constexpr bool blocked(int f) { return f >= kQ8; }
+constexpr bool fp4_fmt(int f) { return f == kFP4RN || f == kFP4SR; }
+constexpr bool mini_fmt(int f) { return f >= kFP8RN; }
+constexpr bool sr_fmt(int f) { return f == kBF16SR || f == kFP8SR || f == kFP4SR; }
 enum GradT : int { kGradF32 = 0, kGradBF16 = 1 };
 
 // One tensor of a dtype bucket, as the kernels see it (device memory).
@@ -68,7 +74,9 @@ struct StepArgs {
     double *partials;              // pre-pass: {sum u^2, sum p^2} per kUTile elements
     QTabs q;
     float lr, beta1, beta2, beta3, alpha, eps, wd, max_unorm;
-    int64_t step;
+    int64_t step;                  // t: keys the stochastic-rounding stream
+    int64_t bc_step;               // steps since the moments last started from zero
+    int32_t fresh;                 // 1: this step starts the moments from zero (a reset)
     uint64_t seed;
     const float *grad_scale;       // device float or null (1)
 };

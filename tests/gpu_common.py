@@ -182,6 +182,7 @@ class Case:
 
 
 STATE_KEYS = {"adamw": ("s1", "s2"), "ademamix": ("s1", "s2", "s3")}
+BLOCKED_FMTS = ("q8", "fp8_rn", "fp8_sr", "fp4_rn", "fp4_sr")
 
 
 def compare(case, dev, ps, st, steps=None):
@@ -208,7 +209,7 @@ def compare(case, dev, ps, st, steps=None):
                 assert nan_equal_bits(g, o), f"tensor {k} {key}: SR bits differ"
             else:
                 assert np.array_equal(g, o), f"tensor {k} {key}: codes differ"
-        if case.fmt == "q8":
+        if case.fmt in BLOCKED_FMTS:
             for key in ("absmax1", "absmax2", "absmax3")[:len(STATE_KEYS[case.opt])]:
                 a = key.replace("absmax", "a")
                 assert nan_equal_bits(got[k][key], st[k][a]), f"tensor {k} {key}: absmax differs"

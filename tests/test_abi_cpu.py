@@ -189,3 +189,60 @@ def test_step_rejects_misaligned_grad_scale(L):
     hp = L.hparams()
     hp.grad_scale = 4098
     assert _call(L, "opt_step_adamw", _tensor(L), 0, hp) == -3
+
+
+def _mini_inputs(elem, A, rng):
+    """Values on, between and next to the scaled grid of a block with absmax A,
+    random values below A, signed zeros and tiny values; never NaN or
+    infinite (in a step, such an element makes the absmax NaN or infinite)."""
+    s = oracle.mini_scale_exp(elem, A) if A > 0 else 0
+    top = {0: 0x7E, 1: 7, 2: 15}[elem]
+    V = np.array([oracle.mini_value(elem, c) for c in range(top + 1)]) * 2.0 ** s
+    mids = (V[:-1] + V[1:]) / 2
+    x = np.concatenate([V, mids, rng.uniform(0, 1, 4000) * A, (rng.uniform(0, 1, 2000) ** 8) * A,
+                        [0.0, A, A * 0.999, 1e-45, 2.0 ** -140]]).astype(np.float32)
+    x = np.concatenate([x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(0))])
+    if elem != 2:
+        x = np.concatenate([x, -x])
+    return x[np.isfinite(x)]
+
+
+@pytest.mark.parametrize("elem", [0, 1, 2])
+def test_host_mini_codec_matches_oracle(L, elem):
+    """The library's FP8/FP4 codec (the kernels' source, compiled for the host)
+    against the oracle's grid walk: codes and read-back values bit for bit,
+    for nearest and stochastic rounding, across block scales (subnormal,
+    zero, NaN and infinite absmax included)."""
+    rng = np.random.default_rng(90 + elem)
+    As = [np.float32(x) for x in (1.0, 1.5, 448.0, 7.0, 3e-3, 2.5e-12, 1e30, 3e-39, 1e-44)]
+    for A in As + [np.float32(0.0), np.float32(np.nan), np.float32(np.inf)]:
+        x = _mini_inputs(elem, A, rng) if np.isfinite(A) and A > 0 else np.array([0.0, -0.0, 1.0], np.float32)
+        if A == 0:
+            x = np.array([0.0, -0.0] * 4, np.float32)
+        for sr in (False, True):
+            r = rng.integers(0, 65536, x.size).astype(np.uint32) if sr else None
+            if sr:
+                r[:min(8, r.size)] = [0, 1, 32767, 32768, 65534, 65535, 0, 65535][:r.size]
+            codes, dec = L.opt_debug_mini_host(elem, A, x, r)
+            want = np.array([oracle.mini_encode(elem, v, A, int(r[i]) if sr else -1) for i, v in enumerate(x)])
+            assert np.array_equal(codes, want), (elem, A, sr, x[codes != want][:5])
+            wdec = np.array([oracle.mini_decode(elem, int(c), A) for c in want], dtype=np.float32)
+            nan = np.isnan(wdec)
+            assert np.array_equal(np.isnan(dec), nan)
+            assert np.array_equal(dec[~nan].view(np.uint32), wdec[~nan].view(np.uint32)), (elem, A)
+
+
+def test_host_mini_codec_rejects_bad_arguments(L):
+    x = np.zeros(4, np.float32)
+    for elem, A in ((3, 1.0), (-1, 1.0), (0, -1.0)):
+        with pytest.raises(L.OptError):
+            L.opt_debug_mini_host(elem, A, x)
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 7])
+def test_fp_formats_need_absmax(L, fmt):
+    assert _call(L, "opt_step_adamw", _tensor(L), fmt) == -1
+
+
+def test_negative_reset_interval_is_rejected(L):
+    assert _call(L, "opt_step_adamw", _tensor(L), 0, L.hparams(reset_interval=-1)) == -1
