@@ -77,8 +77,8 @@ def build_workload(name, torch, osa, synth):
         for key, buf in states.items():
             if key.startswith("absmax"):
                 continue
-            d[key] = buf[off:off + n]
-        if fmt == "q8":
+            d[key] = buf[off // 2:(off + n + 1) // 2] if fmt.startswith("fp4") else buf[off:off + n]
+        if fmt in ("q8", "fp8_rn", "fp8_sr", "fp4_rn", "fp4_sr"):
             assert off % 256 == 0
             for key, buf in states.items():
                 if key.startswith("absmax"):
@@ -321,6 +321,7 @@ def main():
 
     rows = []
     others = ["adamw_q8_1g", "ademamix_f32_268m", "adamw_f32_unorm_268m", "adamw_bf16_1g", "adamw_bf16_sr_1g",
+              "adamw_fp8_rn_1g", "adamw_fp8_sr_1g", "adamw_fp4_rn_1g", "adamw_fp4_sr_1g",
               "gradnorm_bf16_llama7b", "adamw_f32_clip_llama7b"]
     if args.rows == "none":
         others = []

@@ -95,6 +95,19 @@ def lib():
         L.orc_mini_scale_exp.restype = i32
         L.orc_mini_round_array.argtypes = [i32, vp, vp, vp, i64]
         L.orc_mini_round_array.restype = None
+        L.orc_f16_rne.argtypes = [f32]
+        L.orc_f16_rne.restype = ctypes.c_uint16
+        L.orc_f16_sr.argtypes = [f32, ctypes.c_uint32]
+        L.orc_f16_sr.restype = ctypes.c_uint16
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f32.restype = f32
+        L.orc_f16_array.argtypes = [vp, vp, vp, i64]
+        L.orc_f16_array.restype = None
+        L.orc_step_p16.argtypes = [i32, i32, ctypes.POINTER(HP), f32, i64, vp, i32, i32, vp, vp, vp, vp,
+                                   vp, vp, vp, vp, vp, vp]
+        L.orc_step_p16.restype = i32
+        L.orc_round_cast.argtypes = [vp, vp, i64, i32, i32, ctypes.c_uint64, ctypes.c_uint64]
+        L.orc_round_cast.restype = None
         _lib = L
     return _lib
 
@@ -124,6 +137,7 @@ def make_hp(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
 
 
 def _grad_f32(g):
+    """BF16 words (uint16) or float16 or float32 -> float32, exactly."""
     if g.dtype == np.uint16:
         return widen_bf16(g)
     return np.ascontiguousarray(g, dtype=np.float32)
@@ -159,12 +173,28 @@ def _check(opt, fmt, p, g, s1, s2, s3, a1, a2, a3, qs, qu):
         _need(qu, np.float32, 256, "qu")
 
 
+P_F32, P_BF16, P_F16 = 0, 1, 2
+
+
 def step(opt, fmt, hp, p, g, s1, s2, s3=None, a1=None, a2=None, a3=None,
-         qs=None, qu=None, scale=1.0):
-    """One optimizer step over one tensor, in place on p and the states."""
+         qs=None, qu=None, scale=1.0, p_dtype=None, p_sr=False):
+    """One optimizer step over one tensor, in place on p and the states.  p is
+    float32, or 16-bit words with p_dtype P_BF16 / P_F16 (stored back rounded
+    to nearest-even, or stochastically if p_sr)."""
     opt = OPTIMIZERS.get(opt, opt)
     fmt = FORMATS.get(fmt, fmt)
     g = _grad_f32(g)
+    if p_dtype in (P_BF16, P_F16):
+        if p.dtype != np.uint16 or not p.flags["C_CONTIGUOUS"]:
+            raise ValueError("16-bit parameters are uint16 words")
+        work = np.zeros(p.size, dtype=np.float32)
+        _check(opt, fmt, work, g, s1, s2, s3, a1, a2, a3, qs, qu)
+        rc = lib().orc_step_p16(opt, fmt, ctypes.byref(hp), scale, p.size, _ptr(p), p_dtype, 1 if p_sr else 0,
+                                _ptr(g), _ptr(s1), _ptr(s2), _ptr(s3), _ptr(a1), _ptr(a2), _ptr(a3),
+                                _ptr(qs), _ptr(qu), _ptr(work))
+        if rc != 0:
+            raise ValueError("orc_step_p16 rejected its arguments")
+        return
     _check(opt, fmt, p, g, s1, s2, s3, a1, a2, a3, qs, qu)
     rc = lib().orc_step(opt, fmt, ctypes.byref(hp), scale, p.size, _ptr(p), _ptr(g),
                         _ptr(s1), _ptr(s2), _ptr(s3), _ptr(a1), _ptr(a2), _ptr(a3),
@@ -357,3 +387,37 @@ def grad_norm_list(grads):
 
 def clip_coef(norm, max_norm):
     return float(lib().orc_clip_coef(float(norm), float(max_norm)))
+
+
+# --------------------------------------------------------------------------
+# FP16 rounding and the standalone cast
+
+def f16_rne(x):
+    return int(lib().orc_f16_rne(float(np.float32(x))))
+
+
+def f16_sr(x, r):
+    return int(lib().orc_f16_sr(float(np.float32(x)), int(r)))
+
+
+def f16_array(x, r=None):
+    """FP16 words of float32 values: nearest-even, or stochastic with r."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rr = None if r is None else np.ascontiguousarray(np.broadcast_to(np.asarray(r, dtype=np.uint32), x.shape))
+    out = np.empty(x.size, dtype=np.uint16)
+    lib().orc_f16_array(_ptr(x), _ptr(rr), _ptr(out), x.size)
+    return out
+
+
+def widen_f16(words):
+    w = np.ascontiguousarray(words, dtype=np.uint16)
+    return np.array([lib().orc_f16_to_f32(int(h)) for h in w], dtype=np.float32)
+
+
+def round_cast(x, dtype, stochastic=False, seed=0, offset=0):
+    """fp32 -> BF16 (dtype P_BF16) or FP16 (P_F16) words, as one pass."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, dtype=np.uint16)
+    lib().orc_round_cast(_ptr(x), _ptr(out), x.size, dtype, 1 if stochastic else 0,
+                         int(seed) & (2**64 - 1), int(offset) & (2**64 - 1))
+    return out

@@ -617,6 +617,135 @@ int orc_step(int opt, int fmt, const orc_hp *hp, float scale, int64_t n,
 }
 
 /* ------------------------------------------------------------------ */
+/* BF16 and FP16 parameters, and the standalone rounding cast ([SU] Sec. 6
+ * and 7: FP32 -> BF16 with stochastic rounding as one pass over the tensor;
+ * Sec. 8.1: the rounding inside the step; [ISS] Correctness oracle: FP16,
+ * BF16 and FP32 parameter storage).
+ *
+ * Readings:
+ *  - a BF16 or FP16 parameter is widened exactly, stepped in fp32 exactly as
+ *    an fp32 parameter, and the new value is stored rounded to nearest-even
+ *    or stochastically;
+ *  - stochastic rounding of a parameter uses the high 16 bits of the word
+ *    that the second Philox stream (counter word 3 = k | 2^31) gives the
+ *    element, the half that no state uses;
+ *  - FP16 stochastic rounding goes up to the next FP16 value iff
+ *    floor(f * 2^16) + r >= 2^16, f the position across the gap (the rule
+ *    the FP8/FP4 states use); past the largest finite value the next value
+ *    is infinity, as for BF16, where the carry of Sec. 6.1 reaches the
+ *    exponent;
+ *  - the cast's random integer for element j is the low 16 bits of word
+ *    j mod 4 of Philox4x32-10 keyed by the seed with counter
+ *    (j>>2 low, j>>34, offset low, offset high): tied to the element, with a
+ *    fresh offset for each cast ([SU] Sec. 7.3).
+ */
+
+/* Positive FP16 magnitude of code c (0 <= c <= 0x7C00; 0x7C00 stands for the
+ * first value past the largest finite one, 2^16, which IEEE rounding treats
+ * as infinity). */
+static double f16_value(int c)
+{
+    int e = c >> 10, f = c & 1023;
+    if (e == 0) return ldexp((double)f, -24);
+    return ldexp((double)(1024 + f), e - 25);
+}
+
+/* Largest code c with f16_value(c) <= y, for 0 <= y < 2^16 (bisection). */
+static int f16_floor_code(double y)
+{
+    int lo = 0, hi = 0x7C00;           /* f16_value(lo) <= y < f16_value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (f16_value(mid) <= y) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+/* FP32 -> FP16 bits; r < 0: nearest-even, else stochastic with the 16-bit r. */
+static uint16_t f16_round(float x, int32_t r)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7E00u);
+    double y = fabs((double)x);
+    if (y >= 65536.0) return (uint16_t)(sign | 0x7C00u);
+    int c = f16_floor_code(y);
+    double lo = f16_value(c), hi = f16_value(c + 1);
+    int up;
+    if (r < 0) {
+        double dl = y - lo, dh = hi - y;
+        up = dl > dh || (dl == dh && (c & 1));
+    } else {
+        uint32_t l = (uint32_t)floor((y - lo) / (hi - lo) * 65536.0);
+        up = l + (uint32_t)r >= 65536u;
+    }
+    return (uint16_t)(sign | (c + up));
+}
+
+uint16_t orc_f16_rne(float x) { return f16_round(x, -1); }
+uint16_t orc_f16_sr(float x, uint32_t r) { return f16_round(x, (int32_t)(r & 0xFFFFu)); }
+
+float orc_f16_to_f32(uint16_t h)
+{
+    int e = (h >> 10) & 31, f = h & 1023;
+    float v;
+    if (e == 31) v = f ? NAN : INFINITY;
+    else v = (float)(e ? ldexp((double)(1024 + f), e - 25) : ldexp((double)f, -24));
+    return (h & 0x8000u) ? -v : v;
+}
+
+enum { ORC_P_F32 = 0, ORC_P_BF16 = 1, ORC_P_F16 = 2 };
+
+static uint16_t round16(int dtype, float x, int32_t r)
+{
+    if (dtype == ORC_P_BF16) return r < 0 ? orc_bf16_rne(x) : orc_bf16_sr(x, (uint32_t)r);
+    return f16_round(x, r);
+}
+
+/* One step over a tensor whose parameters are stored as BF16 or FP16 words:
+ * widen, step as fp32, store rounded (p_sr: stochastically). */
+int orc_step_p16(int opt, int fmt, const orc_hp *hp, float scale, int64_t n, uint16_t *p16,
+                 int32_t p_dtype, int32_t p_sr, const float *g, void *s1, void *s2, void *s3,
+                 float *a1, float *a2, float *a3, const float *qs, const float *qu, float *work)
+{
+    if (p_dtype != ORC_P_BF16 && p_dtype != ORC_P_F16) return -1;
+    for (int64_t j = 0; j < n; ++j)
+        work[j] = p_dtype == ORC_P_BF16 ? orc_bf16_to_f32(p16[j]) : orc_f16_to_f32(p16[j]);
+    int rc = orc_step(opt, fmt, hp, scale, n, work, g, s1, s2, s3, a1, a2, a3, qs, qu);
+    if (rc) return rc;
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t r = -1;
+        if (p_sr) r = (int32_t)(sr_word(hp->seed, hp->step, hp->tensor_index, hp->index_base + j, 1) >> 16);
+        p16[j] = round16(p_dtype, work[j], r);
+    }
+    return 0;
+}
+
+/* The standalone cast of n fp32 values to BF16 or FP16 words. */
+void orc_round_cast(const float *x, uint16_t *out, int64_t n, int32_t dtype, int32_t stochastic,
+                    uint64_t seed, uint64_t offset)
+{
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t r = -1;
+        if (stochastic) {
+            uint32_t ctr[4], key[2], w[4];
+            uint64_t q = (uint64_t)j >> 2;
+            ctr[0] = (uint32_t)q; ctr[1] = (uint32_t)(q >> 32);
+            ctr[2] = (uint32_t)offset; ctr[3] = (uint32_t)(offset >> 32);
+            key[0] = (uint32_t)seed; key[1] = (uint32_t)(seed >> 32);
+            orc_philox4x32_10(ctr, key, w);
+            r = (int32_t)(w[j & 3] & 0xFFFFu);
+        }
+        out[j] = round16(dtype, x[j], r);
+    }
+}
+
+void orc_f16_array(const float *x, const uint32_t *r, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_round(x[i], r ? (int32_t)(r[i] & 0xFFFFu) : -1);
+}
+
+/* ------------------------------------------------------------------ */
 /* Update-norm pre-pass ([ISS] Problem: the precondition kernel used when
  * max_unorm > 0 recomputes the would-be update and accumulates its norm).
  * U2 = sum_j u_j^2 and P2 = sum_j p_j^2 for one tensor, with u the direction

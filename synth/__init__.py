@@ -198,6 +198,11 @@ WORKLOADS = {
     "adamw_bf16_sr_1g": dict(opt="adamw", fmt="bf16_sr", sizes=[2**30], grad_bf16=True,
                              p_std=0.02, g_std="decay", steps=200,
                              hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)),
+    # FP8 / FP4 block-scaled m/v, nearest or stochastic rounding, 2^30 elements
+    **{f"adamw_{f}_1g": dict(opt="adamw", fmt=f, sizes=[2**30], grad_bf16=True, p_std=0.02, g_std=1e-3,
+                             mask_scale=(0.1, 100.0), steps=5,
+                             hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8))
+       for f in ("fp8_rn", "fp8_sr", "fp4_rn", "fp4_sr")},
     # gradient 2-norm of the Llama-7B-shaped bf16 gradient list alone
     "gradnorm_bf16_llama7b": dict(opt="adamw", fmt="f32", sizes=[n for _, n in llama7b_shapes()],
                                   grad_bf16=True, p_std=0.02, g_std=1e-3, steps=5, norm_only=True,
@@ -213,13 +218,16 @@ WORKLOADS = {
 def bytes_per_element(opt, fmt, grad_bf16, p_bytes=4):
     """Algorithmic HBM bytes one step must move per element: read p, g and the
     states, write p and the states (8-bit: codes plus one fp32 absmax per 256
-    elements per state, read and written)."""
+    elements per state, read and written; FP8 the same with E4M3 codes; FP4
+    half a byte per element per state plus the absmax)."""
     nst = 3 if opt == "ademamix" else 2
     g = 2 if grad_bf16 else 4
     if fmt == "f32":
         s = 4
     elif fmt.startswith("bf16"):
         s = 2
+    elif fmt.startswith("fp4"):
+        s = 0.5 + 4 / 256
     else:
         s = 1 + 4 / 256
     return p_bytes * 2 + g + nst * s * 2
