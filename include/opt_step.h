@@ -58,7 +58,7 @@ extern "C" {
 #define OPT_EHIP         (-4)  /* a HIP runtime error; its text is in opt_last_error()         */
 
 /* ---- enumerations -------------------------------------------------------- */
-typedef enum { OPT_F32 = 0, OPT_BF16 = 1 } opt_dtype;
+typedef enum { OPT_F32 = 0, OPT_BF16 = 1, OPT_F16 = 2 } opt_dtype;
 
 typedef enum {
     OPT_STATE_F32 = 0,      /* fp32 words                                          */
@@ -77,8 +77,12 @@ typedef enum { OPT_ADAMW = 0, OPT_ADEMAMIX = 1 } opt_optimizer;
 
 /* ---- one tensor of the multi-tensor list --------------------------------
  * All pointers are device pointers owned by the caller.
- *   p        numel fp32 parameters, read and written (p_dtype must be OPT_F32).
- *   g        numel gradients in g_dtype, read.
+ *   p        numel parameters in p_dtype, read and written.  OPT_F32 always;
+ *            OPT_BF16 or OPT_F16 with the fp32 and BF16 state formats (the
+ *            blockwise formats return OPT_EUNSUPPORTED): the stored value is
+ *            widened exactly, stepped in fp32, and stored back rounded to
+ *            nearest-even or stochastically (hp->p_rounding).
+ *   g        numel gradients in g_dtype (OPT_F32, OPT_BF16 or OPT_F16), read.
  *   s1       first moment m (AdamW) or fast EMA m1 (AdEMAMix), read and written.
  *   s2       second moment v, read and written.
  *   s3       AdEMAMix's slow EMA m2, read and written; NULL for AdamW.
@@ -147,6 +151,14 @@ typedef struct {
                                    when the kernel runs (so a clipping coefficient
                                    that opt_grad_norm writes earlier on the same
                                    stream fuses into the step); NULL means 1. */
+    int32_t p_rounding;         /* BF16/FP16 parameters: 0 nearest-even, 1
+                                   stochastic with the high 16 bits of the
+                                   element's word from the second Philox
+                                   stream (counter word 3 = k | 2^31); FP16
+                                   goes up iff floor(f * 2^16) + r >= 2^16, f
+                                   the position across the gap, infinity
+                                   past 65504.                               */
+    int32_t reserved;           /* 0 */
     int64_t reset_interval;     /* R > 0: the moments restart from zero at
                                    steps 1, R+1, 2R+1, ... (the stored states are
                                    not read on those steps) and the bias
@@ -200,6 +212,18 @@ typedef struct {
  * later step on the same stream.  g must be 16-byte aligned. */
 int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm, int32_t norm_type,
                   float *coef_out, void *stream);
+
+/* The standalone rounding cast ("When Small Updates Disappear", Sec. 6 and 7:
+ * FP32 -> BF16 in one pass, stochastic rounding costing about as much as
+ * nearest).  x: device float[n] (16-byte aligned); out: device uint16_t[n]
+ * (8-byte aligned) of BF16 (out_dtype OPT_BF16) or FP16 (OPT_F16) words.
+ * stochastic 0: nearest-even.  1: element j draws the low 16 bits r of word
+ * j%4 of Philox4x32-10 keyed by `seed` with counter (j>>2 low, j>>34, offset
+ * low, offset high) -- tied to the element, so any launch shape gives the
+ * same words; pass a new offset for each cast.  BF16 adds r to the fp32 word
+ * and keeps the high half (Sec. 6.1); FP16 rounds as for parameters. */
+int opt_round_cast(const float *x, void *out, int64_t n, int32_t out_dtype, int32_t stochastic, uint64_t seed,
+                   uint64_t offset, void *stream);
 
 /* Test hook: the FP8/FP4 element codec of the state formats.  elem 0 = E4M3,
  * 1 = E2M1, 2 = unsigned E2M2.  For i < n: codes[i] = the code of x[i] in a

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libopt_step.so")
 
 OPT_OK, OPT_EINVAL, OPT_EUNSUPPORTED, OPT_EALIGN, OPT_EHIP = 0, -1, -2, -3, -4
-OPT_F32, OPT_BF16 = 0, 1
+OPT_F32, OPT_BF16, OPT_F16 = 0, 1, 2
 STATE_F32, STATE_BF16_RN, STATE_BF16_SR, STATE_Q8 = 0, 1, 2, 3
 STATE_FP8_RN, STATE_FP8_SR, STATE_FP4_RN, STATE_FP4_SR = 4, 5, 6, 7
 ADAMW, ADEMAMIX = 0, 1
@@ -50,7 +50,8 @@ class OptHparams(ctypes.Structure):
         ("weight_decay", ctypes.c_float), ("max_unorm", ctypes.c_float),
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64),
         ("qmap_signed", ctypes.c_void_p), ("qmap_unsigned", ctypes.c_void_p),
-        ("grad_scale", ctypes.c_void_p), ("reset_interval", ctypes.c_int64),
+        ("grad_scale", ctypes.c_void_p), ("p_rounding", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("reset_interval", ctypes.c_int64),
     ]
 
 
@@ -89,6 +90,7 @@ def lib():
             "opt_debug_stream": ([vp, i32, vp, i32, i64, vp], i32),
             "opt_grad_norm": ([ctypes.POINTER(OptGrad), i64, vp, ctypes.c_float, i32, vp, vp], i32),
             "opt_debug_mini": ([i32, ctypes.c_float, vp, vp, vp, vp, i64, vp], i32),
+            "opt_round_cast": ([vp, vp, i64, i32, i32, ctypes.c_uint64, ctypes.c_uint64, vp], i32),
             "opt_debug_mini_host": ([i32, ctypes.c_float, vp, vp, vp, vp, i64], i32),
         }
         for name, (args, res) in sig.items():
@@ -122,6 +124,8 @@ def _dtype_code(t):
         return OPT_F32
     if t.dtype == torch.bfloat16:
         return OPT_BF16
+    if t.dtype == torch.float16:
+        return OPT_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -147,14 +151,16 @@ def _as_list(tensors):
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
             weight_decay=0.0, max_unorm=0.0, step=1, seed=0, qmap_signed=None, qmap_unsigned=None,
-            grad_scale=None, reset_interval=0):
+            grad_scale=None, reset_interval=0, p_rounding=0):
     """An OptHparams record.  qmap_* are host float32 arrays (numpy or CPU
     torch tensors) of 256 entries; they are referenced, not copied, so keep
     them alive for the call.  grad_scale is a CUDA float tensor of one element
     (for instance the clipping coefficient opt_grad_norm wrote), or None.
-    reset_interval R > 0 restarts the moments from zero every R steps."""
+    reset_interval R > 0 restarts the moments from zero every R steps;
+    p_rounding 1 stores BF16/FP16 parameters with stochastic rounding."""
     h = OptHparams(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
-                   int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale), int(reset_interval))
+                   int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale), int(p_rounding), 0,
+                   int(reset_interval))
     for field, q in (("qmap_signed", qmap_signed), ("qmap_unsigned", qmap_unsigned)):
         if q is not None:
             addr = q.ctypes.data if hasattr(q, "ctypes") else q.data_ptr()
@@ -249,6 +255,13 @@ def opt_debug_stream(srcs, dsts, stream=None):
     S = (ctypes.c_void_p * max(1, len(srcs)))(*[t.data_ptr() for t in srcs])
     D = (ctypes.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
     return _check(lib().opt_debug_stream(S, len(srcs), D, len(dsts), n, _stream(stream)))
+
+
+def opt_round_cast(x, out, stochastic=False, seed=0, offset=0, stream=None):
+    """x (CUDA float32) -> out (CUDA bfloat16 or float16), nearest-even or
+    stochastic."""
+    return _check(lib().opt_round_cast(_ptr(x), _ptr(out), x.numel(), _dtype_code(out), 1 if stochastic else 0,
+                                       int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), _stream(stream)))
 
 
 def opt_debug_mini(elem, A, x, r, codes, decoded, stream=None):

@@ -30,6 +30,8 @@ hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, 
                                  hipStream_t st);
 hipError_t launch_debug_mini(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
                              int64_t n, hipStream_t st);
+hipError_t launch_round_cast(const float *x, uint16_t *out, int64_t n, int bf16, int sr, uint64_t seed,
+                             uint64_t offset, const LaunchGeom &lg, hipStream_t st);
 hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *dst, int ndst, int64_t n,
                                const LaunchGeom &lg, hipStream_t st);
 
@@ -321,6 +323,7 @@ int check_hparams(const opt_hparams *hp, int fmt)
         return fail(OPT_EINVAL, "8-bit states need qmap_signed and qmap_unsigned");
     if (hp->grad_scale && !aligned(hp->grad_scale, 4)) return fail(OPT_EALIGN, "grad_scale must be 4-byte aligned");
     if (hp->reset_interval < 0) return fail(OPT_EINVAL, "reset_interval must be >= 0");
+    if (hp->p_rounding != 0 && hp->p_rounding != 1) return fail(OPT_EINVAL, "p_rounding must be 0 or 1");
     return OPT_OK;
 }
 
@@ -333,12 +336,13 @@ int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
     for (int64_t k = 0; k < n; ++k) {
         const opt_tensor &x = t[k];
         if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
-        if (x.p_dtype != OPT_F32 && x.p_dtype != OPT_BF16)
+        if (x.p_dtype != OPT_F32 && x.p_dtype != OPT_BF16 && x.p_dtype != OPT_F16)
             return fail(OPT_EINVAL, "tensor %lld: unknown p_dtype %d", (long long)k, x.p_dtype);
-        if (x.g_dtype != OPT_F32 && x.g_dtype != OPT_BF16)
+        if (x.g_dtype != OPT_F32 && x.g_dtype != OPT_BF16 && x.g_dtype != OPT_F16)
             return fail(OPT_EINVAL, "tensor %lld: unknown g_dtype %d", (long long)k, x.g_dtype);
-        if (x.p_dtype != OPT_F32)
-            return fail(OPT_EUNSUPPORTED, "tensor %lld: only fp32 parameters are provided", (long long)k);
+        if (x.p_dtype != OPT_F32 && blocked(fmt))
+            return fail(OPT_EUNSUPPORTED, "tensor %lld: the blockwise state formats take fp32 parameters",
+                        (long long)k);
         if (x.numel == 0) continue;
         const bool q8 = blocked(fmt), m2 = opt == kAdEMAMix;
         if (!x.p || !x.g || !x.s1 || !x.s2 || (m2 && !x.s3))
@@ -359,14 +363,16 @@ struct Bucket {
     std::vector<int32_t> chunk_tensor;
 };
 
-void plan_bucket(const opt_tensor *t, int64_t n, int gd, int64_t chunk, Bucket &b)
+// The tensors whose (gradient, parameter) storage is (gd, pd); opt_dtype,
+// GradT and ParamT share their numbering.
+void plan_bucket(const opt_tensor *t, int64_t n, int gd, int pd, int64_t chunk, Bucket &b)
 {
     int64_t next = 0;
     for (int64_t k = 0; k < n; ++k) {
         const opt_tensor &x = t[k];
         // empty tensors ride in the first bucket with no chunks, so the norm
-        // pre-pass still writes {0, 0} for them
-        const bool mine = x.numel == 0 ? gd == kGradF32 : x.g_dtype == (gd == kGradF32 ? OPT_F32 : OPT_BF16);
+        // pre-passes still write zeros for them
+        const bool mine = x.numel == 0 ? (gd == kGradF32 && pd == kP32) : (x.g_dtype == gd && x.p_dtype == pd);
         if (!mine) continue;
         DevTensor d{};
         d.p = (float *)x.p;
@@ -428,6 +434,7 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     a.fresh = R > 0 && a.bc_step == 1;
     a.seed = hp->seed;
     a.grad_scale = hp->grad_scale;
+    a.p_sr = hp->p_rounding;
     return a;
 }
 
@@ -454,9 +461,8 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
     if (q8 && (rc = qtables(*w, hp)) != OPT_OK) return rc;
     const int64_t chunk = g_chunk;
 
-    Bucket b[2];
-    plan_bucket(t, n, kGradF32, chunk, b[0]);
-    plan_bucket(t, n, kGradBF16, chunk, b[1]);
+    Bucket b[9];   // (gradient dtype, parameter dtype)
+    for (int i = 0; i < 9; ++i) plan_bucket(t, n, i / 3, i % 3, chunk, b[i]);
 
     if (pre) {
         size_t need = 0;
@@ -464,8 +470,9 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
         if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
     }
 
-    for (int gd = 0; gd < 2; ++gd) {
-        Bucket &bk = b[gd];
+    for (int bi = 0; bi < 9; ++bi) {
+        const int gd = bi / 3;
+        Bucket &bk = b[bi];
         if (bk.tens.empty() || (!pre && bk.chunk_tensor.empty())) continue;
         std::vector<unsigned char> blob;
         size_t off_ct, off_q;
@@ -473,6 +480,7 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
         Slot *s;
         if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
         StepArgs a = base_args(hp, chunk);
+        a.p_dtype = bi % 3;
         a.tens = (const DevTensor *)s->dev;
         a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
         a.nchunks = (int64_t)bk.chunk_tensor.size();
@@ -567,7 +575,7 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     for (int64_t k = 0; k < n; ++k) {
         const opt_grad &x = grads[k];
         if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
-        if (x.dtype != OPT_F32 && x.dtype != OPT_BF16)
+        if (x.dtype != OPT_F32 && x.dtype != OPT_BF16 && x.dtype != OPT_F16)
             return fail(OPT_EINVAL, "tensor %lld: unknown dtype %d", (long long)k, x.dtype);
         if (x.numel > 0 && !x.g) return fail(OPT_EINVAL, "tensor %lld: g is NULL", (long long)k);
         if (x.numel > 0 && !aligned(x.g, 16)) return fail(OPT_EALIGN, "tensor %lld: g must be 16-byte aligned", (long long)k);
@@ -583,14 +591,13 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     if ((rc = workspace(w)) != OPT_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const int64_t chunk = g_chunk;
-    Bucket b[2];
-    plan_bucket(t.data(), n, kGradF32, chunk, b[0]);
-    plan_bucket(t.data(), n, kGradBF16, chunk, b[1]);
+    Bucket b[3];
+    for (int gd = 0; gd < 3; ++gd) plan_bucket(t.data(), n, gd, kP32, chunk, b[gd]);
     size_t need = 0;
     for (auto &bk : b) need = std::max(need, bk.chunk_tensor.size() * (size_t)(chunk / kUTile) * 2);
     if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
     hipError_t e;
-    for (int gd = 0; gd < 2; ++gd) {
+    for (int gd = 0; gd < 3; ++gd) {
         Bucket &bk = b[gd];
         if (bk.tens.empty()) continue;
         std::vector<unsigned char> blob;
@@ -614,6 +621,24 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     w->partials_stream = st;
     if ((e = hipEventRecord(w->partials_ev, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return OPT_OK;
+}
+
+int opt_round_cast(const float *x, void *out, int64_t n, int32_t out_dtype, int32_t stochastic, uint64_t seed,
+                   uint64_t offset, void *stream)
+{
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (out_dtype != OPT_BF16 && out_dtype != OPT_F16) return fail(OPT_EINVAL, "out_dtype must be OPT_BF16 or OPT_F16");
+    if (stochastic != 0 && stochastic != 1) return fail(OPT_EINVAL, "stochastic must be 0 or 1");
+    if (n == 0) return OPT_OK;
+    if (!x || !out) return fail(OPT_EINVAL, "x or out is NULL");
+    if (!aligned(x, 16) || !aligned(out, 8)) return fail(OPT_EALIGN, "x must be 16-byte and out 8-byte aligned");
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace *w;
+    int rc;
+    if ((rc = workspace(w)) != OPT_OK) return rc;
+    hipError_t e = launch_round_cast(x, (uint16_t *)out, n, out_dtype == OPT_BF16, stochastic, seed, offset, geom(*w),
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "round cast launch");
 }
 
 const char *opt_last_error(void) { return g_err.c_str(); }

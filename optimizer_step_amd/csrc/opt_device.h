@@ -265,7 +265,10 @@ __host__ __device__ inline uint32_t mini_mag(float y, uint32_t r)
     const uint32_t rem = sh < 32 ? (M & ((1u << sh) - 1u)) : M;
     bool up;
     if (SR) {
-        up = (rem >> (sh - 16)) + r >= 65536u;
+        // the top 16 bits of the dropped part (fewer bits are dropped only
+        // by formats with more than 7 fraction bits, in their normal range)
+        const uint32_t l16 = (F::kMB <= 7 || sh >= 16) ? rem >> (sh - 16) : rem << (16 - sh);
+        up = l16 + r >= 65536u;
     } else {
         const uint32_t half = sh <= 24 ? 1u << (sh - 1) : 0u;     // sh > 24: below half a step
         up = sh <= 24 && (rem > half || (rem == half && (code & 1u)));
@@ -283,6 +286,24 @@ __host__ __device__ inline uint32_t mini_encode(float x, int nsc, uint32_t r)
     if (F::kSign && (fbits(x) >> 31)) c |= F::kSign;
     return c;
 }
+
+// IEEE binary16 as a grid for stochastic rounding: past the largest finite
+// value (65504) the next value is infinity, as a carry into the exponent gives.
+using F16 = MiniFmt<10, 15, 0x7C00u, 0x8000u, -1>;
+
+// FP32 -> FP16 bits with stochastic rounding by the 16-bit integer r (up iff
+// the top 16 dropped bits plus r carry); NaN stays NaN with its sign.
+__host__ __device__ inline uint32_t f16_sr(float x, uint32_t r)
+{
+    if (x != x) return ((fbits(x) >> 16) & 0x8000u) | 0x7E00u;
+    return mini_encode<F16, true>(x, 0, r);
+}
+
+// FP16 words: widening is exact; nearest-even narrowing is the hardware
+// conversion (v_cvt_f16_f32 under the default round-to-nearest-even mode).
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ uint32_t f16_rne(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
 // Grid value of a magnitude code (exact in binary32).
 template <class F>

@@ -40,6 +40,17 @@ __device__ __forceinline__ int64_t first_chunk()
 // ---------------------------------------------------------------------------
 // element groups of four
 
+// Four 16-bit words (BF16 if BF, else FP16) widened to fp32.
+template <bool BF>
+__device__ __forceinline__ void widen4(u2 w, float out[4])
+{
+    if (BF) {
+        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    } else {
+        out[0] = f16_lo(w.x); out[1] = f16_hi(w.x); out[2] = f16_lo(w.y); out[3] = f16_hi(w.y);
+    }
+}
+
 template <int GD>
 __device__ __forceinline__ void load_grad4(const void *g, int64_t e, float out[4])
 {
@@ -47,9 +58,7 @@ __device__ __forceinline__ void load_grad4(const void *g, int64_t e, float out[4
         f4 x = sld<f4>((const float *)g + e);
         out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
     } else {
-        u2 w = sld<u2>((const uint16_t *)g + e);
-        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
-        out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+        widen4<GD == kGradBF16>(sld<u2>((const uint16_t *)g + e), out);
     }
 }
 
@@ -57,7 +66,56 @@ template <int GD>
 __device__ __forceinline__ float load_grad1(const void *g, int64_t e)
 {
     if (GD == kGradF32) return gld<float>((const float *)g + e);
-    return bf16_lo(gld<uint16_t>((const uint16_t *)g + e));
+    const uint32_t h = gld<uint16_t>((const uint16_t *)g + e);
+    return GD == kGradBF16 ? bf16_lo(h) : f16_lo(h);
+}
+
+// Parameters: fp32, or BF16 / FP16 words widened exactly and stored back
+// rounded to nearest-even or, with sr, stochastically by the 16-bit r.
+template <int PD>
+__device__ __forceinline__ void load_p4(const float *p, int64_t e, float out[4])
+{
+    if (PD == kP32) {
+        f4 x = sld<f4>(p + e);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        widen4<PD == kPBF16>(sld<u2>((const uint16_t *)(const void *)p + e), out);
+    }
+}
+
+template <int PD>
+__device__ __forceinline__ float load_p1(const float *p, int64_t e)
+{
+    if (PD == kP32) return gld<float>(p + e);
+    const uint32_t h = gld<uint16_t>((const uint16_t *)(const void *)p + e);
+    return PD == kPBF16 ? bf16_lo(h) : f16_lo(h);
+}
+
+template <int PD>
+__device__ __forceinline__ uint32_t round_p(float x, bool sr, uint32_t r)
+{
+    if (PD == kPBF16) return sr ? bf16_sr(x, r) : bf16_rne(x);
+    return sr ? f16_sr(x, r) : f16_rne(x);
+}
+
+template <int PD>
+__device__ __forceinline__ void store_p4(float *p, int64_t e, const float x[4], bool sr, const uint32_t r[4])
+{
+    if (PD == kP32) {
+        sst<f4>(p + e, f4{x[0], x[1], x[2], x[3]});
+    } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = round_p<PD>(x[i], sr, r[i]);
+        sst<u2>((uint16_t *)(void *)p + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+    }
+}
+
+template <int PD>
+__device__ __forceinline__ void store_p1(float *p, int64_t e, float x, bool sr, uint32_t r)
+{
+    if (PD == kP32) gst<float>(p + e, x);
+    else gst<uint16_t>((uint16_t *)(void *)p + e, (uint16_t)round_p<PD>(x, sr, r));
 }
 
 template <int SF>
@@ -109,11 +167,10 @@ struct Group {
     float p[4], g[4], m[4], v[4], m2[4];
 };
 
-template <int OPT, int GD, int SF>
+template <int OPT, int GD, int SF, int PD>
 __device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fresh, Group &x)
 {
-    f4 pv = sld<f4>(T.p + e);
-    x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
+    load_p4<PD>(T.p, e, x.p);
     load_grad4<GD>(T.g, e, x.g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x.m[i] = x.v[i] = x.m2[i] = 0.0f;
@@ -124,7 +181,7 @@ __device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fres
     }
 }
 
-template <int OPT, int GD, int SF>
+template <int OPT, int GD, int SF, int PD>
 __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
                                           int64_t e, float lam, Group &x)
 {
@@ -135,24 +192,27 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
         x.p[i] = apply_update(x.p[i], s.d, lam, r.u);
         mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
     }
-    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0};
+    // stochastic rounding: the first stream's word rounds m (low half) and v
+    // (high half), the second stream's m2 (low half) and a 16-bit p (high half)
+    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
     if (SF == kBF16SR) {
         PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
         rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
         rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
-        if (OPT == kAdEMAMix) {
-            PhiloxOut w2 = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true);
-            rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu;
-            rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
-        }
     }
-    sst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
+    const bool psr = PD != kP32 && a.p_sr;
+    if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
+        PhiloxOut w2 = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true);
+        rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
+        rp[0] = w2.w0 >> 16; rp[1] = w2.w1 >> 16; rp[2] = w2.w2 >> 16; rp[3] = w2.w3 >> 16;
+    }
+    store_p4<PD>(T.p, e, x.p, psr, rp);
     store_state4<SF>(T.s1, e, mo, rm);
     store_state4<SF>(T.s2, e, vo, rv);
     if (OPT == kAdEMAMix) store_state4<SF>(T.s3, e, m2o, rm2);
 }
 
-template <int OPT, int GD, int SF>
+template <int OPT, int GD, int SF, int PD>
 __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, const DevTensor &T,
                                           int64_t e, float lam)
 {
@@ -164,14 +224,18 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
         if (OPT == kAdEMAMix) m2 = load_state1<SF>(T.s3, e);
     }
     Mom r = moments<OPT>(s, a, g, m, v, m2);
-    gst<float>(T.p + e, apply_update(gld<float>(T.p + e), s.d, lam, r.u));
-    uint32_t rm = 0, rv = 0, rm2 = 0;
+    const float pn = apply_update(load_p1<PD>(T.p, e), s.d, lam, r.u);
+    uint32_t rm = 0, rv = 0, rm2 = 0, rp = 0;
     if (SF == kBF16SR) {
         uint32_t w = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3));
         rm = w & 0xFFFFu; rv = w >> 16;
-        if (OPT == kAdEMAMix)
-            rm2 = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true), (int)(e & 3)) & 0xFFFFu;
     }
+    const bool psr = PD != kP32 && a.p_sr;
+    if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
+        uint32_t w2 = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true), (int)(e & 3));
+        rm2 = w2 & 0xFFFFu; rp = w2 >> 16;
+    }
+    store_p1<PD>(T.p, e, pn, psr, rp);
     store_state1<SF>(T.s1, e, r.m, rm);
     store_state1<SF>(T.s2, e, r.v, rv);
     if (OPT == kAdEMAMix) store_state1<SF>(T.s3, e, r.m2, rm2);
@@ -186,7 +250,7 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
 #define OPT_EW_ATTR
 #endif
 
-template <int OPT, int GD, int SF>
+template <int OPT, int GD, int SF, int PD>
 __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
                                                                        const int32_t *__restrict__ ctab, StepArgs a)
 {
@@ -206,17 +270,17 @@ __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const Dev
         for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
             Group x[kEwGroups];
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF>(T, e0 + 4 * (i + u * kThreads), fresh, x[u]);
+            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (i + u * kThreads), fresh, x[u]);
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
+            for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
         }
         for (; i < ngroups; i += kThreads) {
             Group x0;
-            ew_load<OPT, GD, SF>(T, e0 + 4 * i, fresh, x0);
-            ew_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, lam, x0);
+            ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
+            ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
         }
         const int64_t tail = len & 3;
-        if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
+        if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
     }
 }
 
@@ -277,7 +341,7 @@ __device__ __forceinline__ QChunk q8_chunk(const DevTensor &T, int64_t e0)
     const int64_t sb = fp4_fmt(SF) ? e0 / 2 : e0;
     QChunk c;
     c.p = T.p + e0;
-    c.g = (const uint8_t *)T.g + e0 * (GD == kGradF32 ? 4 : 2);
+    c.g = (const uint8_t *)T.g + e0 * (GD == kGradF32 ? 4 : 2);   // bytes per gradient
     c.s1 = (uint8_t *)T.s1 + sb;
     c.s2 = (uint8_t *)T.s2 + sb;
     c.s3 = (uint8_t *)T.s3 + sb;
@@ -353,8 +417,7 @@ __device__ __forceinline__ void q8_load(const StepArgs &a, const QChunk &C, uint
             f4 gv = sld<f4>(C.g + 4 * e);
             x.g[0] = gv.x; x.g[1] = gv.y; x.g[2] = gv.z; x.g[3] = gv.w;
         } else {
-            u2 w = sld<u2>(C.g + 2 * e);
-            x.g[0] = bf16_lo(w.x); x.g[1] = bf16_hi(w.x); x.g[2] = bf16_lo(w.y); x.g[3] = bf16_hi(w.y);
+            widen4<GD == kGradBF16>(sld<u2>(C.g + 2 * e), x.g);
         }
     } else {
 #pragma unroll
@@ -363,7 +426,9 @@ __device__ __forceinline__ void q8_load(const StepArgs &a, const QChunk &C, uint
             x.g[i] = 0.0f;
             if (i < nmine) {
                 x.p[i] = gld<float>(C.p + e + i);
-                x.g[i] = GD == kGradF32 ? gld<float>(C.g + 4 * (e + i)) : bf16_lo(gld<uint16_t>(C.g + 2 * (e + i)));
+                x.g[i] = GD == kGradF32    ? gld<float>(C.g + 4 * (e + i))
+                         : GD == kGradBF16 ? bf16_lo(gld<uint16_t>(C.g + 2 * (e + i)))
+                                           : f16_lo(gld<uint16_t>(C.g + 2 * (e + i)));
             }
         }
     }
@@ -639,8 +704,9 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t e = e0 + tt * kUTile + q * 256 + lane * 4;
-                    f4 pv = sld<f4>(T.p + e);
-                    p[q][0] = pv.x; p[q][1] = pv.y; p[q][2] = pv.z; p[q][3] = pv.w;
+                    if (a.p_dtype == kP32) load_p4<kP32>(T.p, e, p[q]);
+                    else if (a.p_dtype == kPBF16) load_p4<kPBF16>(T.p, e, p[q]);
+                    else load_p4<kPF16>(T.p, e, p[q]);
                     load_grad4<GD>(T.g, e, g[q]);
                     m[q][0] = m[q][1] = m[q][2] = m[q][3] = 0.0f;
                     v[q][0] = v[q][1] = v[q][2] = v[q][3] = 0.0f;
@@ -673,7 +739,8 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
                             if (OPT == kAdEMAMix) m2 = read_state<SF, 2>(lds, T.s3, T.a3, e);
                         }
                         Mom r = moments<OPT>(s, a, g, m, v, m2);
-                        float p = gld<float>(T.p + e);
+                        const float p = a.p_dtype == kP32 ? load_p1<kP32>(T.p, e)
+                                      : a.p_dtype == kPBF16 ? load_p1<kPBF16>(T.p, e) : load_p1<kPF16>(T.p, e);
                         su += (double)r.u * (double)r.u;
                         sp += (double)p * (double)p;
                     }
@@ -899,6 +966,46 @@ __global__ void debug_mini_kernel(int elem, float A, const float *x, const uint3
     }
 }
 
+// The standalone rounding cast: n fp32 values to BF16 (BF) or FP16 words,
+// nearest-even or stochastic.  Element j's random integer is the low half of
+// word j%4 of Philox4x32-10 keyed by the seed, counter (j>>2, j>>34, offset):
+// tied to the element, so the grid does not change the result.  Each lane
+// takes groups of 4 elements: 128-bit loads, 64-bit stores.
+template <bool BF, bool SR>
+__global__ __launch_bounds__(256) void round_cast_kernel(const float *__restrict__ x, uint16_t *__restrict__ out,
+                                                         int64_t n, uint64_t seed, uint64_t offset)
+{
+    const int64_t ngroups = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q <= ngroups; q += stride) {
+        const int64_t e = q * 4;
+        const int cnt = (int)min((int64_t)4, n - e);
+        if (cnt <= 0) break;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (cnt == 4) {
+            f4 t = sld<f4>(x + e);
+            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+        } else {
+            for (int i = 0; i < cnt; ++i) v[i] = gld<float>(x + e + i);
+        }
+        uint32_t r[4] = {0, 0, 0, 0};
+        if (SR) {
+            const PhiloxOut w = philox4x32_10((uint32_t)q, (uint32_t)((uint64_t)q >> 32), (uint32_t)offset,
+                                              (uint32_t)(offset >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
+            r[0] = w.w0 & 0xFFFFu; r[1] = w.w1 & 0xFFFFu; r[2] = w.w2 & 0xFFFFu; r[3] = w.w3 & 0xFFFFu;
+        }
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            h[i] = BF ? (SR ? bf16_sr(v[i], r[i]) : bf16_rne(v[i])) : (SR ? f16_sr(v[i], r[i]) : f16_rne(v[i]));
+        if (cnt == 4) {
+            sst<u2>(out + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        } else {
+            for (int i = 0; i < cnt; ++i) gst<uint16_t>(out + e + i, (uint16_t)h[i]);
+        }
+    }
+}
+
 template <class K>
 static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, int threads);
 
@@ -1002,14 +1109,32 @@ static hipError_t launch_persistent_q8(K kernel, size_t lds, const LaunchGeom &l
     return hipGetLastError();
 }
 
+template <int OPT, int GD, int PD>
+static hipError_t launch_ew_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
+{
+    const int64_t nc = a.nchunks;
+    switch (fmt) {
+    case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int OPT, int GD>
 static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
     const int64_t nc = a.nchunks;
+    if (!blocked(fmt)) {
+        switch (a.p_dtype) {
+        case kP32: return launch_ew_t<OPT, GD, kP32>(fmt, a, lg, st);
+        case kPBF16: return launch_ew_t<OPT, GD, kPBF16>(fmt, a, lg, st);
+        case kPF16: return launch_ew_t<OPT, GD, kPF16>(fmt, a, lg, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (a.p_dtype != kP32) return hipErrorInvalidValue;
     switch (fmt) {
-    case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
     case kQ8: return launch_persistent_q8(step_q8_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     case kFP8RN: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP8RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
     case kFP8SR: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP8SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
@@ -1019,12 +1144,21 @@ static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg
     }
 }
 
+template <int OPT>
+static hipError_t launch_step_o(int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
+{
+    switch (gd) {
+    case kGradF32: return launch_step_t<OPT, kGradF32>(fmt, a, lg, lds, st);
+    case kGradBF16: return launch_step_t<OPT, kGradBF16>(fmt, a, lg, lds, st);
+    case kGradF16: return launch_step_t<OPT, kGradF16>(fmt, a, lg, lds, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
-    if (opt == kAdamW) return gd == kGradF32 ? launch_step_t<kAdamW, kGradF32>(fmt, a, lg, lds, st)
-                                             : launch_step_t<kAdamW, kGradBF16>(fmt, a, lg, lds, st);
-    return gd == kGradF32 ? launch_step_t<kAdEMAMix, kGradF32>(fmt, a, lg, lds, st)
-                          : launch_step_t<kAdEMAMix, kGradBF16>(fmt, a, lg, lds, st);
+    return opt == kAdamW ? launch_step_o<kAdamW>(gd, fmt, a, lg, lds, st)
+                         : launch_step_o<kAdEMAMix>(gd, fmt, a, lg, lds, st);
 }
 
 template <int OPT, int GD>
@@ -1049,10 +1183,12 @@ hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const Launc
 {
     hipError_t e = hipSuccess;
     if (a.nchunks > 0) {
-        if (opt == kAdamW) e = gd == kGradF32 ? launch_unorm_t<kAdamW, kGradF32>(fmt, a, lg, lds, st)
-                                              : launch_unorm_t<kAdamW, kGradBF16>(fmt, a, lg, lds, st);
-        else e = gd == kGradF32 ? launch_unorm_t<kAdEMAMix, kGradF32>(fmt, a, lg, lds, st)
-                                : launch_unorm_t<kAdEMAMix, kGradBF16>(fmt, a, lg, lds, st);
+        if (opt == kAdamW) e = gd == kGradF32    ? launch_unorm_t<kAdamW, kGradF32>(fmt, a, lg, lds, st)
+                               : gd == kGradBF16 ? launch_unorm_t<kAdamW, kGradBF16>(fmt, a, lg, lds, st)
+                                                 : launch_unorm_t<kAdamW, kGradF16>(fmt, a, lg, lds, st);
+        else e = gd == kGradF32    ? launch_unorm_t<kAdEMAMix, kGradF32>(fmt, a, lg, lds, st)
+                 : gd == kGradBF16 ? launch_unorm_t<kAdEMAMix, kGradBF16>(fmt, a, lg, lds, st)
+                                   : launch_unorm_t<kAdEMAMix, kGradF16>(fmt, a, lg, lds, st);
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(unorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
@@ -1064,8 +1200,9 @@ hipError_t launch_gnorm(int gd, const StepArgs &a, const LaunchGeom &lg, int nte
 {
     hipError_t e = hipSuccess;
     if (a.nchunks > 0)
-        e = gd == kGradF32 ? launch_persistent(gnorm_partials_kernel<kGradF32>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a)
-                           : launch_persistent(gnorm_partials_kernel<kGradBF16>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a);
+        e = gd == kGradF32    ? launch_persistent(gnorm_partials_kernel<kGradF32>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a)
+            : gd == kGradBF16 ? launch_persistent(gnorm_partials_kernel<kGradBF16>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a)
+                              : launch_persistent(gnorm_partials_kernel<kGradF16>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gnorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
                        (const double *)a.partials, out);
@@ -1092,6 +1229,23 @@ hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, 
     int64_t blocks = min((int64_t)4096, (n + 255) / 256);
     hipLaunchKernelGGL(debug_round_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st,
                        x, r, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_round_cast(const float *x, uint16_t *out, int64_t n, int bf16, int sr, uint64_t seed,
+                             uint64_t offset, const LaunchGeom &lg, hipStream_t st)
+{
+    const int64_t groups = (n + 3) / 4;
+    const int64_t want = (groups + 255) / 256;
+    const int64_t cap = (int64_t)lg.ncu * 8;    // a few waves in flight per SIMD, grid-stride beyond
+    const unsigned grid = (unsigned)max((int64_t)1, min(want, cap));
+    if (bf16) {
+        if (sr) hipLaunchKernelGGL((round_cast_kernel<true, true>), dim3(grid), dim3(256), 0, st, x, out, n, seed, offset);
+        else hipLaunchKernelGGL((round_cast_kernel<true, false>), dim3(grid), dim3(256), 0, st, x, out, n, seed, offset);
+    } else {
+        if (sr) hipLaunchKernelGGL((round_cast_kernel<false, true>), dim3(grid), dim3(256), 0, st, x, out, n, seed, offset);
+        else hipLaunchKernelGGL((round_cast_kernel<false, false>), dim3(grid), dim3(256), 0, st, x, out, n, seed, offset);
+    }
     return hipGetLastError();
 }
 

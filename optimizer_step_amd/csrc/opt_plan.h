@@ -19,11 +19,12 @@ constexpr bool blocked(int f) { return f >= kQ8; }
 constexpr bool fp4_fmt(int f) { return f == kFP4RN || f == kFP4SR; }
 constexpr bool mini_fmt(int f) { return f >= kFP8RN; }
 constexpr bool sr_fmt(int f) { return f == kBF16SR || f == kFP8SR || f == kFP4SR; }
-enum GradT : int { kGradF32 = 0, kGradBF16 = 1 };
+enum GradT : int { kGradF32 = 0, kGradBF16 = 1, kGradF16 = 2 };   // gradient storage
+enum ParamT : int { kP32 = 0, kPBF16 = 1, kPF16 = 2 };             // parameter storage
 
 // One tensor of a dtype bucket, as the kernels see it (device memory).
 struct alignas(16) DevTensor {
-    float *p;
+    float *p;              // fp32, or 16-bit words for BF16/FP16 parameters
     const void *g;
     void *s1, *s2, *s3;
     float *a1, *a2, *a3;
@@ -79,6 +80,8 @@ struct StepArgs {
     int32_t fresh;                 // 1: this step starts the moments from zero (a reset)
     uint64_t seed;
     const float *grad_scale;       // device float or null (1)
+    int32_t p_dtype;               // ParamT of the bucket's parameters
+    int32_t p_sr;                  // 1: 16-bit parameters are stored with stochastic rounding
 };
 
 }  // namespace optstep

@@ -246,3 +246,26 @@ def test_fp_formats_need_absmax(L, fmt):
 
 def test_negative_reset_interval_is_rejected(L):
     assert _call(L, "opt_step_adamw", _tensor(L), 0, L.hparams(reset_interval=-1)) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(n=-1), -1),
+    (dict(dtype=0), -1),
+    (dict(stochastic=2), -1),
+    (dict(x=None), -1),
+    (dict(x=4100), -3),
+    (dict(out=4098), -3),
+])
+def test_round_cast_bad_arguments(L, args, status):
+    a = dict(x=4096, out=8192, n=16, dtype=1, stochastic=1)
+    a.update(args)
+    assert L.lib().opt_round_cast(a["x"], a["out"], a["n"], a["dtype"], a["stochastic"], 0, 0, None) == status
+
+
+def test_p16_rules(L):
+    hp = L.hparams(p_rounding=2)
+    assert _call(L, "opt_step_adamw", _tensor(L), 0, hp) == -1
+    t = [L.OptTensor(4096, 4096, 8192, 12288, None, 16384, 16384, None, 16, 1, 1)]   # BF16 p, FP8 states
+    assert _call(L, "opt_step_adamw", t, 4) == -2
+    t = [L.OptTensor(4096, 4096, 8192, 12288, None, None, None, None, 16, 3, 0)]      # unknown p dtype
+    assert _call(L, "opt_step_adamw", t, 0) == -1

@@ -1,0 +1,217 @@
+"""GPU parity of 16-bit (BF16 / FP16) parameter storage with nearest or
+stochastic rounding, FP16 gradients, and the standalone rounding cast
+("When Small Updates Disappear", Sec. 6-8; the issue "Investigate SM103
+bias-correction broadcast in 32-bit optimizers", Correctness oracle: FP16,
+BF16 and FP32 parameter and gradient storage).
+
+Bars: the cast bit-exact; states to the usual bars; 16-bit parameters within
+one 16-bit step per optimizer step of the oracle's words (the fp32 value
+before rounding follows the same recipe, so nearly every word is identical,
+which is checked as a diagnostic)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import bf16_ulps, fp32_close, nan_equal_bits, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import optimizer_step_amd as osa
+    assert torch.cuda.is_available()
+    osa.lib()
+    osa.opt_debug_set_launch(32768, 0)
+    yield
+
+
+def _special(n, rng):
+    x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-12, 6, n)).astype(np.float32)
+    edge = np.array([0.0, -0.0, np.nan, np.inf, -np.inf, 65504, 65519.99, 65520, 65536, 3.4e38,
+                     2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 1e-40, -1e-45, 1.0 + 2.0 ** -9], np.float32)
+    x[:min(n, edge.size)] = edge[:min(n, edge.size)]
+    return x
+
+
+def _words_equal(a, b, dtype):
+    fa = oracle.widen_bf16(a) if dtype == oracle.P_BF16 else a.view(np.float16).astype(np.float32)
+    fb = oracle.widen_bf16(b) if dtype == oracle.P_BF16 else b.view(np.float16).astype(np.float32)
+    nan = np.isnan(fb)
+    return np.array_equal(np.isnan(fa), nan) and np.array_equal(a[~nan], b[~nan])
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 1023, (1 << 20) + 3])
+@pytest.mark.parametrize("stochastic", [False, True])
+@pytest.mark.parametrize("dtype", [oracle.P_BF16, oracle.P_F16])
+def test_round_cast(dtype, stochastic, n):
+    import torch
+    import optimizer_step_amd as osa
+    x = _special(n, np.random.default_rng(n + 7))
+    out = torch.empty(n, dtype=torch.bfloat16 if dtype == oracle.P_BF16 else torch.float16, device="cuda")
+    seed, offset = 0xDEADBEEF12345678, 41
+    osa.opt_round_cast(to_dev(x), out, stochastic, seed, offset)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = oracle.round_cast(x, dtype, stochastic, seed, offset)
+    assert _words_equal(got, want, dtype)
+    if stochastic and n > 1000:
+        nearest = oracle.round_cast(x, dtype, False)
+        assert np.mean(got != nearest) > 0.05
+
+
+def test_round_cast_nearest_matches_torch():
+    import torch
+    import optimizer_step_amd as osa
+    x = _special(100000, np.random.default_rng(3))
+    xd = to_dev(x)
+    for dt in (torch.bfloat16, torch.float16):
+        out = torch.empty(x.size, dtype=dt, device="cuda")
+        osa.opt_round_cast(xd, out)
+        ref = xd.to(dt)
+        torch.cuda.synchronize()
+        a = out.view(torch.int16).cpu().numpy()
+        b = ref.view(torch.int16).cpu().numpy()
+        nan = np.isnan(ref.float().cpu().numpy())
+        assert np.array_equal(a[~nan], b[~nan])
+
+
+# ---------------------------------------------------------------------------
+# steps with 16-bit parameters
+
+GD = {"f32": np.float32, "bf16": "bf16", "f16": np.float16}
+
+
+def _grad(n, t, k, gd):
+    g = synth.grads(n, t, k, std=1e-2)
+    if gd == "bf16":
+        return synth.bf16_words(g)
+    return g.astype(GD[gd])
+
+
+def _p16(p32, dtype):
+    return synth.bf16_words(p32) if dtype == oracle.P_BF16 else p32.astype(np.float16).view(np.uint16)
+
+
+def _dev_p16(words, dtype):
+    import torch
+    t = torch.from_numpy(words.view(np.int16).copy()).cuda()
+    return t.view(torch.bfloat16 if dtype == oracle.P_BF16 else torch.float16)
+
+
+def _run_p16(opt, fmt, sizes, gds, pdt, p_sr, steps, hp, unorm=False):
+    import torch
+    import optimizer_step_amd as osa
+    p0 = [_p16(synth.params(n, k, std=0.5), pdt) for k, n in enumerate(sizes)]
+    # oracle
+    ps = [p.copy() for p in p0]
+    st = [oracle.state_zeros(fmt, n, opt) for n in sizes]
+    norms_o = []
+    for t in range(1, steps + 1):
+        for k, n in enumerate(sizes):
+            g = _grad(n, t, k, gds[k])
+            h = oracle.make_hp(step=t, seed=synth.SR_SEED, tensor_index=k, **hp)
+            scale = 1.0
+            if unorm:
+                wide = oracle.widen_bf16(ps[k]) if pdt == oracle.P_BF16 else ps[k].view(np.float16).astype(np.float32)
+                u2, p2 = oracle.unorm(opt, fmt, h, wide, g, **st[k])
+                norms_o.append((t, k, u2, p2))
+                scale = oracle.unorm_scale(hp["max_unorm"], u2, p2)
+            oracle.step(opt, fmt, h, ps[k], g, scale=scale, p_dtype=pdt, p_sr=p_sr, **st[k])
+    # GPU
+    dev = []
+    for k, n in enumerate(sizes):
+        d = {"p": _dev_p16(p0[k], pdt), "g": to_dev(_grad(n, 1, k, gds[k]))}
+        d.update(osa.state_buffers(fmt, n, opt))
+        dev.append(d)
+    tl = osa.TensorList(dev)
+    fn = osa.opt_step_adamw if opt == "adamw" else osa.opt_step_ademamix
+    norms_g = []
+    for t in range(1, steps + 1):
+        for k, n in enumerate(sizes):
+            dev[k]["g"].copy_(to_dev(_grad(n, t, k, gds[k])))
+        h = osa.hparams(step=t, seed=synth.SR_SEED, p_rounding=1 if p_sr else 0, **hp)
+        un = None
+        if unorm:
+            un = torch.empty(2 * len(sizes), dtype=torch.float64, device="cuda")
+            osa.opt_precondition_unorm(opt, tl, fmt, h, un)
+            norms_g.append(un.cpu().numpy().copy())
+        fn(tl, fmt, h, un)
+    torch.cuda.synchronize()
+    return ps, st, dev, norms_o, norms_g
+
+
+def _check(ps, st, dev, fmt, opt, pdt, steps):
+    same = total = 0
+    for k in range(len(ps)):
+        got = dev[k]["p"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        want = ps[k]
+        gi = got.astype(np.int64); wi = want.astype(np.int64)
+        gi = np.where(gi & 0x8000, -(gi & 0x7FFF), gi)
+        wi = np.where(wi & 0x8000, -(wi & 0x7FFF), wi)
+        assert int(np.abs(gi - wi).max(initial=0)) <= steps, k
+        same += int(np.sum(got == want))
+        total += got.size
+        for key in ("s1", "s2", "s3")[:3 if opt == "ademamix" else 2]:
+            g, o = to_host(dev[k][key]), st[k][key]
+            if fmt == "f32":
+                assert fp32_close(g, o), (k, key)
+            elif fmt == "bf16_rn":
+                assert int(bf16_ulps(g, o).max(initial=0)) <= steps, (k, key)
+            else:
+                assert nan_equal_bits(g, o), (k, key)
+    assert same / max(total, 1) >= 0.999, same / total
+
+
+@pytest.mark.parametrize("p_sr", [False, True])
+@pytest.mark.parametrize("pdt", [oracle.P_BF16, oracle.P_F16])
+@pytest.mark.parametrize("fmt", ["f32", "bf16_sr"])
+def test_p16_adamw(fmt, pdt, p_sr):
+    sizes = [1, 1001, 4096, 32768 + 77]
+    gds = ["f32", "bf16", "f16", "bf16"] if pdt == oracle.P_BF16 else ["f32", "f16", "f16", "f32"]
+    ps, st, dev, _, _ = _run_p16("adamw", fmt, sizes, gds, pdt, p_sr, 4, dict(lr=1e-2, weight_decay=0.1))
+    _check(ps, st, dev, fmt, "adamw", pdt, 4)
+
+
+@pytest.mark.parametrize("pdt", [oracle.P_BF16, oracle.P_F16])
+def test_p16_ademamix_bf16_rn(pdt):
+    sizes = [777, 32768 * 2 + 5]
+    ps, st, dev, _, _ = _run_p16("ademamix", "bf16_rn", sizes, ["bf16", "f16"], pdt, True, 3,
+                                 dict(lr=1e-2, weight_decay=0.1, beta3=0.999, alpha=5.0))
+    _check(ps, st, dev, "bf16_rn", "ademamix", pdt, 3)
+
+
+def test_p16_with_update_norm():
+    sizes = [3000, 65537]
+    ps, st, dev, no, ng = _run_p16("adamw", "f32", sizes, ["bf16", "f32"], oracle.P_BF16, True, 3,
+                                   dict(lr=1e-2, max_unorm=0.5), unorm=True)
+    _check(ps, st, dev, "f32", "adamw", oracle.P_BF16, 3)
+    for (t, k, u2, p2) in no:
+        g = ng[t - 1]
+        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= 1e-12 * p2, (t, k)
+
+
+def test_blockwise_formats_refuse_p16():
+    import torch
+    import optimizer_step_amd as osa
+    d = {"p": torch.zeros(256, dtype=torch.bfloat16, device="cuda"),
+         "g": torch.zeros(256, dtype=torch.bfloat16, device="cuda")}
+    d.update(osa.state_buffers("fp8_rn", 256))
+    with pytest.raises(osa.OptError) as e:
+        osa.opt_step_adamw(osa.TensorList([d]), osa.STATE_FP8_RN, osa.hparams())
+    assert e.value.status == osa.OPT_EUNSUPPORTED
+
+
+def test_grad_norm_f16():
+    import torch
+    import optimizer_step_amd as osa
+    grads = [synth.grads(n, 1, k, std=3.0).astype(np.float16) for k, n in enumerate([5, 4097, 70001])]
+    out = torch.empty(8, dtype=torch.float64, device="cuda")
+    osa.opt_grad_norm([to_dev(g) for g in grads], out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    (s2, mx), per = oracle.grad_norm_list(grads)
+    for k, (ps, pm) in enumerate(per):
+        assert abs(o[2 + 2 * k] - ps) <= grads[k].size * 2.0 ** -53 * ps and o[3 + 2 * k] == pm
