@@ -23,6 +23,8 @@ import numpy as np
 from . import build as _build
 
 ADAMW, ADEMAMIX = 0, 1
+MOMENTUM, RMSPROP, ADAGRAD, LION = 2, 3, 4, 5
+ONE_STATE = {"momentum": MOMENTUM, "rmsprop": RMSPROP, "adagrad": ADAGRAD, "lion": LION}
 F32, BF16_RN, BF16_SR, Q8 = 0, 1, 2, 3
 FP8_RN, FP8_SR, FP4_RN, FP4_SR = 4, 5, 6, 7
 FORMATS = {"f32": F32, "bf16_rn": BF16_RN, "bf16_sr": BF16_SR, "q8": Q8,
@@ -41,6 +43,7 @@ class HP(ctypes.Structure):
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64), ("index_base", ctypes.c_int64),
         ("tensor_index", ctypes.c_int32), ("decay_after", ctypes.c_int32),
         ("grad_scale", ctypes.c_float), ("reset_interval", ctypes.c_int64),
+        ("skip_zeros", ctypes.c_int32), ("pad_", ctypes.c_int32),
     ]
 
 
@@ -108,6 +111,8 @@ def lib():
         L.orc_step_p16.restype = i32
         L.orc_round_cast.argtypes = [vp, vp, i64, i32, i32, ctypes.c_uint64, ctypes.c_uint64]
         L.orc_round_cast.restype = None
+        L.orc_step_1state.argtypes = [i32, i32, ctypes.POINTER(HP), i64, vp, vp, vp]
+        L.orc_step_1state.restype = i32
         _lib = L
     return _lib
 
@@ -130,10 +135,10 @@ def widen_bf16(words):
 
 def make_hp(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
             weight_decay=0.0, max_unorm=0.0, step=1, seed=0, index_base=0,
-            tensor_index=0, decay_after=False, grad_scale=1.0, reset_interval=0):
+            tensor_index=0, decay_after=False, grad_scale=1.0, reset_interval=0, skip_zeros=False):
     return HP(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
               int(step), int(seed) & (2**64 - 1), int(index_base), int(tensor_index),
-              1 if decay_after else 0, grad_scale, int(reset_interval))
+              1 if decay_after else 0, grad_scale, int(reset_interval), 1 if skip_zeros else 0, 0)
 
 
 def _grad_f32(g):
@@ -421,3 +426,20 @@ def round_cast(x, dtype, stochastic=False, seed=0, offset=0):
     lib().orc_round_cast(_ptr(x), _ptr(out), x.size, dtype, 1 if stochastic else 0,
                          int(seed) & (2**64 - 1), int(offset) & (2**64 - 1))
     return out
+
+
+# --------------------------------------------------------------------------
+# one-state optimizers
+
+def step_1state(opt, fmt, hp, p, g, s1):
+    """One momentum / RMSprop / Adagrad / Lion step over one tensor, in place
+    on p (float32) and s1 (float32, or BF16 words for the BF16 formats)."""
+    opt = ONE_STATE.get(opt, opt)
+    fmt = FORMATS.get(fmt, fmt)
+    g = _grad_f32(g)
+    n = p.size
+    _need(p, np.float32, n, "p")
+    _need(g, np.float32, n, "g")
+    _need(s1, np.float32 if fmt == F32 else np.uint16, n, "s1")
+    if lib().orc_step_1state(opt, fmt, ctypes.byref(hp), n, _ptr(p), _ptr(g), _ptr(s1)) != 0:
+        raise ValueError("orc_step_1state rejected its arguments")

@@ -73,6 +73,10 @@ typedef struct {
                              uses fl(g * grad_scale); 1 leaves g unchanged   */
     int64_t reset_interval; /* R > 0: the moments restart from zero at steps
                              1, R+1, 2R+1, ... ([SU] Sec. 5); 0: never        */
+    int32_t skip_zeros;   /* 1: an element whose gradient is exactly zero keeps
+                             its parameter and its states ([PR] Not covered:
+                             the decay is skipped with the update)           */
+    int32_t pad_;
 } orc_hp;
 
 /* ------------------------------------------------------------------ */
@@ -210,6 +214,8 @@ typedef struct {
     float lam;             /* lr, times the update-norm scale    */
 } scalars_t;
 
+static int skipped(const orc_hp *hp, float g) { return hp->skip_zeros && g == 0.0f; }
+
 /* Steps since the moments last started from zero (1 on the step that
  * starts them), and whether this step starts them. */
 static int64_t cycle_step(const orc_hp *hp)
@@ -307,6 +313,12 @@ static int step_f32(int opt, const orc_hp *hp, float scale, int64_t n,
         float m_old = fresh ? 0.0f : m[j];
         float v_old = fresh ? 0.0f : v[j];
         float m2_old = (opt == ORC_ADEMAMIX && !fresh) ? m2[j] : 0.0f;
+        if (skipped(hp, g[j])) {          /* p and the states as they were */
+            m[j] = m_old;
+            v[j] = v_old;
+            if (opt == ORC_ADEMAMIX) m2[j] = m2_old;
+            continue;
+        }
         moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
         p[j] = apply_update(hp, &s, p[j], r.u);
         m[j] = r.m;
@@ -325,6 +337,12 @@ static int step_bf16(int opt, int stochastic, const orc_hp *hp, float scale, int
         float m_old = fresh ? 0.0f : orc_bf16_to_f32(m[j]);
         float v_old = fresh ? 0.0f : orc_bf16_to_f32(v[j]);
         float m2_old = (opt == ORC_ADEMAMIX && !fresh) ? orc_bf16_to_f32(m2[j]) : 0.0f;
+        if (skipped(hp, g[j])) {          /* a stored BF16 value rounds to itself */
+            m[j] = (uint16_t)(f2u(m_old) >> 16);
+            v[j] = (uint16_t)(f2u(v_old) >> 16);
+            if (opt == ORC_ADEMAMIX) m2[j] = (uint16_t)(f2u(m2_old) >> 16);
+            continue;
+        }
         moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
         /* The parameter update uses the unrounded fp32 moments; rounding
          * happens only at write-back ([SU] Sec. 1.1). */
@@ -390,6 +408,10 @@ static int step_q8(int opt, const orc_hp *hp, float scale, int64_t n,
             float m_old = fresh ? 0.0f : qs[c1[j]] * a1[blk];
             float v_old = fresh ? 0.0f : qu[c2[j]] * a2[blk];
             float m2_old = (opt == ORC_ADEMAMIX && !fresh) ? qs[c3[j]] * a3[blk] : 0.0f;
+            if (skipped(hp, g[j])) {      /* the old values, coded again with the block */
+                bm[i] = m_old; bv[i] = v_old; bm2[i] = m2_old;
+                continue;
+            }
             moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
             p[j] = apply_update(hp, &s, p[j], r.u);
             bm[i] = r.m; bv[i] = r.v; bm2[i] = r.m2;
@@ -562,6 +584,10 @@ static int step_mini(int opt, int fp4, int sr, const orc_hp *hp, float scale, in
                 m_old = mini_decode(Fm, mini_get(fp4, c1, j), a1[blk]);
                 v_old = mini_decode(Fv, mini_get(fp4, c2, j), a2[blk]);
                 if (opt == ORC_ADEMAMIX) m2_old = mini_decode(Fm, mini_get(fp4, c3, j), a3[blk]);
+            }
+            if (skipped(hp, g[j])) {
+                bm[i] = m_old; bv[i] = v_old; bm2[i] = m2_old;
+                continue;
             }
             moments_t r = moments_and_direction(opt, hp, &s, g[j], m_old, v_old, m2_old);
             p[j] = apply_update(hp, &s, p[j], r.u);
@@ -746,6 +772,81 @@ void orc_f16_array(const float *x, const uint32_t *r, uint16_t *out, int64_t n)
 }
 
 /* ------------------------------------------------------------------ */
+/* One-state optimizers ([PR] intro: the 1-state kernels use coupled L2
+ * for momentum, RMSprop and Adagrad, and decoupled decay for Lion).
+ *
+ * Readings (the pages name the family and how each couples the decay):
+ *  - coupled L2: when wd != 0 the gradient becomes g' = g + wd*p before it
+ *    enters the state, and the update carries no separate decay;
+ *  - momentum (heavy ball, as torch.optim.SGD with dampening 0): m' = g' on
+ *    the state's first step, else m' = b1*m + g'; p' = p - lr*m';
+ *  - RMSprop (as torch.optim.RMSprop, alpha = b1):
+ *    v' = b1*v + (1-b1)*g'^2, p' = p - lr*(g'/(sqrt(v') + eps));
+ *  - Adagrad (as torch.optim.Adagrad with no lr decay): v' = v + g'^2,
+ *    p' = p - lr*(g'/(sqrt(v') + eps));
+ *  - Lion (Chen et al., "Symbolic Discovery of Optimization Algorithms"):
+ *    c = b1*m + (1-b1)*g, p' = p*(1 - lr*wd) - lr*sign(c) (sign(0) = 0),
+ *    m' = b2*m + (1-b2)*g;
+ *  - the state is fp32 or BF16 (nearest, or stochastic with the low half of
+ *    the element's first-stream word); grad_scale, skip_zeros and resets act
+ *    as for the two-state optimizers.
+ */
+enum { ORC_MOMENTUM = 2, ORC_RMSPROP = 3, ORC_ADAGRAD = 4, ORC_LION = 5 };
+
+static float sign_f(float c)
+{
+    if (c != c) return c;
+    return c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : 0.0f);
+}
+
+int orc_step_1state(int opt, int fmt, const orc_hp *hp, int64_t n, float *p, const float *g, void *s1)
+{
+    if (opt < ORC_MOMENTUM || opt > ORC_LION) return -1;
+    if (fmt != ORC_F32 && fmt != ORC_BF16_RN && fmt != ORC_BF16_SR) return -1;
+    int fresh = fresh_states(hp);
+    int first = cycle_step(hp) == 1;
+    float om1 = 1.0f - hp->beta1, om2 = 1.0f - hp->beta2;
+    float lrwd = hp->lr * hp->weight_decay;
+    float d = 1.0f - lrwd;
+    for (int64_t j = 0; j < n; ++j) {
+        float s_old;
+        if (fresh) s_old = 0.0f;
+        else if (fmt == ORC_F32) s_old = ((float *)s1)[j];
+        else s_old = orc_bf16_to_f32(((uint16_t *)s1)[j]);
+        float s_new = s_old;
+        if (!skipped(hp, g[j])) {
+            float gs = g[j] * hp->grad_scale;
+            float gp = gs;
+            if (opt != ORC_LION && hp->weight_decay != 0.0f) gp = gs + hp->weight_decay * p[j];
+            if (opt == ORC_MOMENTUM) {
+                s_new = first ? gp : hp->beta1 * s_old + gp;
+                p[j] = p[j] - hp->lr * s_new;
+            } else if (opt == ORC_RMSPROP || opt == ORC_ADAGRAD) {
+                float gg = gp * gp;
+                s_new = opt == ORC_RMSPROP ? hp->beta1 * s_old + om1 * gg : s_old + gg;
+                float den = sqrtf(s_new) + hp->eps;
+                float u = gp / den;
+                p[j] = p[j] - hp->lr * u;
+            } else {
+                float c = hp->beta1 * s_old + om1 * gs;
+                float decayed = p[j] * d;
+                p[j] = decayed - hp->lr * sign_f(c);
+                s_new = hp->beta2 * s_old + om2 * gs;
+            }
+        }
+        if (fmt == ORC_F32) {
+            ((float *)s1)[j] = s_new;
+        } else if (fmt == ORC_BF16_RN || s_new == s_old) {
+            ((uint16_t *)s1)[j] = orc_bf16_rne(s_new);   /* a stored value rounds to itself */
+        } else {
+            uint32_t w = sr_word(hp->seed, hp->step, hp->tensor_index, hp->index_base + j, 0);
+            ((uint16_t *)s1)[j] = orc_bf16_sr(s_new, w & 0xFFFFu);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Update-norm pre-pass ([ISS] Problem: the precondition kernel used when
  * max_unorm > 0 recomputes the would-be update and accumulates its norm).
  * U2 = sum_j u_j^2 and P2 = sum_j p_j^2 for one tensor, with u the direction
@@ -806,6 +907,7 @@ int orc_unorm(int opt, int fmt, const orc_hp *hp, int64_t n, const float *p, con
             if (opt == ORC_ADEMAMIX) m2 = orc_bf16_to_f32(((const uint16_t *)s3)[j]);
         }
         moments_t r = moments_and_direction(opt, hp, &s, g[j], m, v, m2);
+        if (skipped(hp, g[j])) r.u = 0.0f;   /* no update for this element */
         nsum_add(&su, (double)r.u * (double)r.u);
         nsum_add(&sp, (double)p[j] * (double)p[j]);
     }
