@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0
 METRIC = "optimizer-step Gelem/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "step_counters.json")
-KERNEL_SOURCES = ["opt_kernels.hip", "opt_device.h", "opt_plan.h"]
+KERNEL_SOURCES = ["opt_kernels_ew.hip", "opt_elem.h", "opt_device.h", "opt_plan.h"]   # the headline kernel's
 
 
 def kernel_hash():

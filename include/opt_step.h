@@ -73,7 +73,10 @@ typedef enum {
     OPT_STATE_FP4_SR = 7    /* the same, stochastic rounding                       */
 } opt_state_fmt;
 
-typedef enum { OPT_ADAMW = 0, OPT_ADEMAMIX = 1 } opt_optimizer;
+typedef enum {
+    OPT_ADAMW = 0, OPT_ADEMAMIX = 1,                                  /* two states  */
+    OPT_MOMENTUM = 2, OPT_RMSPROP = 3, OPT_ADAGRAD = 4, OPT_LION = 5  /* one state   */
+} opt_optimizer;
 
 /* ---- one tensor of the multi-tensor list --------------------------------
  * All pointers are device pointers owned by the caller.
@@ -165,6 +168,15 @@ typedef struct {
                                    corrections count from there: 1 - beta^t'
                                    with t' = (t-1) mod R + 1; the random stream
                                    keeps the absolute t.  0: never.          */
+    int32_t skip_zeros;         /* 1: an element whose gradient is exactly 0
+                                   keeps its parameter (no decay either) and
+                                   its stored moments (blockwise formats code
+                                   the old values again against the block's
+                                   new absmax); the update-norm pre-pass
+                                   counts no update for it.  bitsandbytes PR
+                                   "Fix decoupled weight decay ordering ...",
+                                   Not covered.                              */
+    int32_t reserved2;          /* 0 */
 } opt_hparams;
 
 /* One AdamW step over the n tensors of `tensors` (host array, read during the
@@ -180,6 +192,26 @@ int opt_step_adamw(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
  * the blockwise formats) required for every tensor. */
 int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
                       const opt_hparams *hp, const double *unorm, void *stream);
+
+/* One step of a one-state optimizer (bitsandbytes PR "Fix decoupled weight
+ * decay ordering in the CUDA Adam/AdEMAMix kernels", intro: the 1-state
+ * kernels use coupled L2 for momentum, RMSprop and Adagrad and decoupled
+ * decay for Lion).  optimizer: OPT_MOMENTUM, OPT_RMSPROP, OPT_ADAGRAD or
+ * OPT_LION.  Each tensor needs p (fp32), g and s1 (the state; s2, s3 and the
+ * absmax arrays are ignored); state_fmt OPT_STATE_F32, _BF16_RN or _BF16_SR
+ * (others: OPT_EUNSUPPORTED).  Per element, in binary32, g' = g*grad_scale,
+ * plus wd*p for the coupled-L2 three when wd != 0:
+ *   momentum  m' = g' on the state's first step (t = 1 or a reset), else
+ *             b1*m + g';  p' = p - lr*m'
+ *   RMSprop   v' = b1*v + (1-b1)*g'^2;  p' = p - lr*(g'/(sqrt(v') + eps))
+ *   Adagrad   v' = v + g'^2;            p' = p - lr*(g'/(sqrt(v') + eps))
+ *   Lion      c = b1*m + (1-b1)*g';  p' = p*(1 - lr*wd) - lr*sign(c), sign(0) = 0;
+ *             m' = b2*m + (1-b2)*g'
+ * beta1 in [0, 1]; max_unorm must be <= 0; seed, skip_zeros, grad_scale and
+ * reset_interval act as for the two-state steps (SR: the low 16 bits of the
+ * element's first-stream word). */
+int opt_step_1state(int32_t optimizer, const opt_tensor *tensors, int64_t n, int32_t state_fmt,
+                    const opt_hparams *hp, void *stream);
 
 /* The max_unorm pre-pass: for each tensor k, recompute the direction u of the
  * coming step (no lr, no decay) from p, g and the states without writing them,

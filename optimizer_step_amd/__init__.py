@@ -20,6 +20,8 @@ OPT_F32, OPT_BF16, OPT_F16 = 0, 1, 2
 STATE_F32, STATE_BF16_RN, STATE_BF16_SR, STATE_Q8 = 0, 1, 2, 3
 STATE_FP8_RN, STATE_FP8_SR, STATE_FP4_RN, STATE_FP4_SR = 4, 5, 6, 7
 ADAMW, ADEMAMIX = 0, 1
+MOMENTUM, RMSPROP, ADAGRAD, LION = 2, 3, 4, 5
+ONE_STATE = {"momentum": MOMENTUM, "rmsprop": RMSPROP, "adagrad": ADAGRAD, "lion": LION}
 FORMATS = {"f32": STATE_F32, "bf16_rn": STATE_BF16_RN, "bf16_sr": STATE_BF16_SR, "q8": STATE_Q8,
            "fp8_rn": STATE_FP8_RN, "fp8_sr": STATE_FP8_SR, "fp4_rn": STATE_FP4_RN, "fp4_sr": STATE_FP4_SR}
 BLOCKED = (STATE_Q8, STATE_FP8_RN, STATE_FP8_SR, STATE_FP4_RN, STATE_FP4_SR)
@@ -51,7 +53,7 @@ class OptHparams(ctypes.Structure):
         ("step", ctypes.c_int64), ("seed", ctypes.c_uint64),
         ("qmap_signed", ctypes.c_void_p), ("qmap_unsigned", ctypes.c_void_p),
         ("grad_scale", ctypes.c_void_p), ("p_rounding", ctypes.c_int32), ("reserved", ctypes.c_int32),
-        ("reset_interval", ctypes.c_int64),
+        ("reset_interval", ctypes.c_int64), ("skip_zeros", ctypes.c_int32), ("reserved2", ctypes.c_int32),
     ]
 
 
@@ -91,6 +93,7 @@ def lib():
             "opt_grad_norm": ([ctypes.POINTER(OptGrad), i64, vp, ctypes.c_float, i32, vp, vp], i32),
             "opt_debug_mini": ([i32, ctypes.c_float, vp, vp, vp, vp, i64, vp], i32),
             "opt_round_cast": ([vp, vp, i64, i32, i32, ctypes.c_uint64, ctypes.c_uint64, vp], i32),
+            "opt_step_1state": ([i32, T, i64, i32, H, vp], i32),
             "opt_debug_mini_host": ([i32, ctypes.c_float, vp, vp, vp, vp, i64], i32),
         }
         for name, (args, res) in sig.items():
@@ -151,16 +154,17 @@ def _as_list(tensors):
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
             weight_decay=0.0, max_unorm=0.0, step=1, seed=0, qmap_signed=None, qmap_unsigned=None,
-            grad_scale=None, reset_interval=0, p_rounding=0):
+            grad_scale=None, reset_interval=0, p_rounding=0, skip_zeros=False):
     """An OptHparams record.  qmap_* are host float32 arrays (numpy or CPU
     torch tensors) of 256 entries; they are referenced, not copied, so keep
     them alive for the call.  grad_scale is a CUDA float tensor of one element
     (for instance the clipping coefficient opt_grad_norm wrote), or None.
     reset_interval R > 0 restarts the moments from zero every R steps;
-    p_rounding 1 stores BF16/FP16 parameters with stochastic rounding."""
+    p_rounding 1 stores BF16/FP16 parameters with stochastic rounding;
+    skip_zeros leaves elements whose gradient is exactly 0 untouched."""
     h = OptHparams(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
                    int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale), int(p_rounding), 0,
-                   int(reset_interval))
+                   int(reset_interval), 1 if skip_zeros else 0, 0)
     for field, q in (("qmap_signed", qmap_signed), ("qmap_unsigned", qmap_unsigned)):
         if q is not None:
             addr = q.ctypes.data if hasattr(q, "ctypes") else q.data_ptr()
@@ -190,6 +194,13 @@ def opt_step_ademamix(tensors, state_fmt, hp, unorm=None, stream=None):
     tl = _as_list(tensors)
     return _check(lib().opt_step_ademamix(tl.arr, tl.n, FORMATS.get(state_fmt, state_fmt),
                                           ctypes.byref(hp), _ptr(unorm), _stream(stream)))
+
+
+def opt_step_1state(optimizer, tensors, state_fmt, hp, stream=None):
+    """One momentum / RMSprop / Adagrad / Lion step; tensors need p, g, s1."""
+    tl = _as_list(tensors)
+    return _check(lib().opt_step_1state(ONE_STATE.get(optimizer, optimizer), tl.arr, tl.n,
+                                        FORMATS.get(state_fmt, state_fmt), ctypes.byref(hp), _stream(stream)))
 
 
 def opt_precondition_unorm(optimizer, tensors, state_fmt, hp, unorm_out, stream=None):

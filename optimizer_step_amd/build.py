@@ -8,12 +8,13 @@ import os
 import shutil
 import subprocess
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libopt_step.so")
-SOURCES = ["opt_api.cpp", "opt_kernels.hip"]
+SOURCES = ["opt_api.cpp", "opt_kernels.hip", "opt_kernels_ew.hip", "opt_kernels_1s.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -46,15 +47,18 @@ def _run(cmd):
 def build(verbose=False, out=LIB, extra_flags=()):
     tmpdir = tempfile.mkdtemp(prefix="optstep_build_")
     try:
-        objs = []
+        objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmpdir, src + ".o")
-            lang = ["-x", "hip"]
-            cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            _run(cmd)
+            cmds.append(cmd)
             objs.append(obj)
+        # the translation units compile independently: in parallel
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as pool:
+            for f in [pool.submit(_run, c) for c in cmds]:
+                f.result()
         tmp = out + ".tmp%d" % os.getpid()
         cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
         if verbose:

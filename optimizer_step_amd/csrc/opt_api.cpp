@@ -22,6 +22,7 @@ hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const Launch
 hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, int ntens,
                         double *out, hipStream_t st);
 hipError_t launch_gnorm(int gd, const StepArgs &a, const LaunchGeom &lg, int ntens, double *out, hipStream_t st);
+hipError_t launch_step_1state(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st);
 hipError_t launch_gnorm_total(int64_t n, double *out, float max_norm, int norm_type, float *coef, hipStream_t st);
 hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, uint32_t *out,
                                hipStream_t st);
@@ -324,6 +325,7 @@ int check_hparams(const opt_hparams *hp, int fmt)
     if (hp->grad_scale && !aligned(hp->grad_scale, 4)) return fail(OPT_EALIGN, "grad_scale must be 4-byte aligned");
     if (hp->reset_interval < 0) return fail(OPT_EINVAL, "reset_interval must be >= 0");
     if (hp->p_rounding != 0 && hp->p_rounding != 1) return fail(OPT_EINVAL, "p_rounding must be 0 or 1");
+    if (hp->skip_zeros != 0 && hp->skip_zeros != 1) return fail(OPT_EINVAL, "skip_zeros must be 0 or 1");
     return OPT_OK;
 }
 
@@ -435,6 +437,7 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     a.seed = hp->seed;
     a.grad_scale = hp->grad_scale;
     a.p_sr = hp->p_rounding;
+    a.skip_zeros = hp->skip_zeros;
     return a;
 }
 
@@ -620,6 +623,58 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     w->partials_used = true;
     w->partials_stream = st;
     if ((e = hipEventRecord(w->partials_ev, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return OPT_OK;
+}
+
+int opt_step_1state(int32_t optimizer, const opt_tensor *t, int64_t n, int32_t state_fmt, const opt_hparams *hp,
+                    void *stream)
+{
+    int rc;
+    if (optimizer < OPT_MOMENTUM || optimizer > OPT_LION) return fail(OPT_EINVAL, "unknown one-state optimizer %d", optimizer);
+    if (state_fmt < kF32 || state_fmt > kFP4SR) return fail(OPT_EINVAL, "unknown state format %d", state_fmt);
+    if (blocked(state_fmt))
+        return fail(OPT_EUNSUPPORTED, "the one-state optimizers take fp32 or BF16 states");
+    if ((rc = check_hparams(hp, state_fmt)) != OPT_OK) return rc;
+    if (hp->max_unorm > 0.0f) return fail(OPT_EUNSUPPORTED, "max_unorm is provided for the two-state optimizers only");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 <= 1.0f)) return fail(OPT_EINVAL, "beta1 must lie in [0, 1]");
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (n > 0 && !t) return fail(OPT_EINVAL, "tensors is NULL");
+    if (n > INT32_MAX) return fail(OPT_EINVAL, "too many tensors");
+    for (int64_t k = 0; k < n; ++k) {
+        const opt_tensor &x = t[k];
+        if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
+        if (x.g_dtype != OPT_F32 && x.g_dtype != OPT_BF16 && x.g_dtype != OPT_F16)
+            return fail(OPT_EINVAL, "tensor %lld: unknown g_dtype %d", (long long)k, x.g_dtype);
+        if (x.p_dtype != OPT_F32)
+            return fail(OPT_EUNSUPPORTED, "tensor %lld: the one-state optimizers take fp32 parameters", (long long)k);
+        if (x.numel == 0) continue;
+        if (!x.p || !x.g || !x.s1) return fail(OPT_EINVAL, "tensor %lld: missing p, g or s1", (long long)k);
+        if (!aligned(x.p, 16) || !aligned(x.g, 16) || !aligned(x.s1, 16))
+            return fail(OPT_EALIGN, "tensor %lld: p, g and s1 must be 16-byte aligned", (long long)k);
+    }
+    if (n == 0) return OPT_OK;
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace *w;
+    if ((rc = workspace(w)) != OPT_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t chunk = g_chunk;
+    for (int gd = 0; gd < 3; ++gd) {
+        Bucket bk;
+        plan_bucket(t, n, gd, kP32, chunk, bk);
+        if (bk.chunk_tensor.empty()) continue;
+        std::vector<unsigned char> blob;
+        size_t off_ct, off_q;
+        make_blob(bk, nullptr, blob, off_ct, off_q);
+        Slot *s;
+        if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+        StepArgs a = base_args(hp, chunk);
+        a.tens = (const DevTensor *)s->dev;
+        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
+        a.nchunks = (int64_t)bk.chunk_tensor.size();
+        hipError_t e = launch_step_1state(optimizer, gd, state_fmt, a, geom(*w), st);
+        if (e != hipSuccess) return hip_fail(e, "one-state step launch");
+        if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
+    }
     return OPT_OK;
 }
 

@@ -1,288 +1,17 @@
-// opt_kernels.hip -- gfx950 kernels of the fused element-wise optimizer step.
+// opt_kernels.hip -- gfx950 kernels of the blockwise-state step (8-bit
+// codebook, FP8 and FP4 states), the deterministic update-norm pre-pass, the
+// fused multi-tensor gradient norm, the standalone rounding cast and the test
+// hooks.  (The element-wise two-state step is in opt_kernels_ew.hip, the
+// one-state optimizers in opt_kernels_1s.hip.)
 //
-// Layout of the work: the host flattens a dtype bucket of tensors into a
-// chunk space (each tensor split into chunks of `chunk` elements, a multiple
-// of 1024), and a persistent grid of 256-thread workgroups walks the chunks
-// with a grid stride.  Inside a chunk every lane owns groups of 4 consecutive
-// elements, so p, m, v (fp32) move as 128-bit accesses, bf16 gradients and
-// BF16 states as 64-bit ones, and 8-bit codes as 32-bit ones; consecutive
-// lanes own consecutive groups, so every access instruction of a wave64 is
-// fully coalesced.  The 8-bit format hands one 256-element block to one wave
-// (64 lanes x 4), which makes the block absmax a wave reduction.
-//
-// The step is HBM-bound (no dense contraction, so no MFMA): every byte is read
-// or written once per step and no intermediate leaves registers.
-#include "opt_device.h"
+// The blockwise formats hand one 256-element block to one wave (64 lanes x 4
+// consecutive elements), which makes the block absmax a wave reduction; codes
+// move as 32-bit (8-bit formats) or 16-bit (FP4) accesses per lane, fully
+// coalesced.  Every kernel here is HBM-bound or close to it (no dense
+// contraction, so no MFMA): each byte is read or written once per call.
+#include "opt_elem.h"
 
 namespace optstep {
-
-#ifndef OPT_EW_GROUPS
-#define OPT_EW_GROUPS 4
-#endif
-constexpr int kEwGroups = OPT_EW_GROUPS;   // groups of four in flight per lane
-
-#ifndef OPT_XCD_REMAP
-#define OPT_XCD_REMAP 0
-#endif
-
-// The chunk a workgroup starts at.  Workgroups are dealt to the 8 XCDs in
-// turn; with the remap, the workgroups of one XCD take a contiguous run of
-// each round's chunks instead of every 8th chunk.
-__device__ __forceinline__ int64_t first_chunk()
-{
-#if OPT_XCD_REMAP
-    const unsigned g = gridDim.x, b = blockIdx.x;
-    if (g % 8 == 0) return (int64_t)(b % 8) * (g / 8) + b / 8;
-#endif
-    return blockIdx.x;
-}
-
-// ---------------------------------------------------------------------------
-// element groups of four
-
-// Four 16-bit words (BF16 if BF, else FP16) widened to fp32.
-template <bool BF>
-__device__ __forceinline__ void widen4(u2 w, float out[4])
-{
-    if (BF) {
-        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    } else {
-        out[0] = f16_lo(w.x); out[1] = f16_hi(w.x); out[2] = f16_lo(w.y); out[3] = f16_hi(w.y);
-    }
-}
-
-template <int GD>
-__device__ __forceinline__ void load_grad4(const void *g, int64_t e, float out[4])
-{
-    if (GD == kGradF32) {
-        f4 x = sld<f4>((const float *)g + e);
-        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
-    } else {
-        widen4<GD == kGradBF16>(sld<u2>((const uint16_t *)g + e), out);
-    }
-}
-
-template <int GD>
-__device__ __forceinline__ float load_grad1(const void *g, int64_t e)
-{
-    if (GD == kGradF32) return gld<float>((const float *)g + e);
-    const uint32_t h = gld<uint16_t>((const uint16_t *)g + e);
-    return GD == kGradBF16 ? bf16_lo(h) : f16_lo(h);
-}
-
-// Parameters: fp32, or BF16 / FP16 words widened exactly and stored back
-// rounded to nearest-even or, with sr, stochastically by the 16-bit r.
-template <int PD>
-__device__ __forceinline__ void load_p4(const float *p, int64_t e, float out[4])
-{
-    if (PD == kP32) {
-        f4 x = sld<f4>(p + e);
-        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
-    } else {
-        widen4<PD == kPBF16>(sld<u2>((const uint16_t *)(const void *)p + e), out);
-    }
-}
-
-template <int PD>
-__device__ __forceinline__ float load_p1(const float *p, int64_t e)
-{
-    if (PD == kP32) return gld<float>(p + e);
-    const uint32_t h = gld<uint16_t>((const uint16_t *)(const void *)p + e);
-    return PD == kPBF16 ? bf16_lo(h) : f16_lo(h);
-}
-
-template <int PD>
-__device__ __forceinline__ uint32_t round_p(float x, bool sr, uint32_t r)
-{
-    if (PD == kPBF16) return sr ? bf16_sr(x, r) : bf16_rne(x);
-    return sr ? f16_sr(x, r) : f16_rne(x);
-}
-
-template <int PD>
-__device__ __forceinline__ void store_p4(float *p, int64_t e, const float x[4], bool sr, const uint32_t r[4])
-{
-    if (PD == kP32) {
-        sst<f4>(p + e, f4{x[0], x[1], x[2], x[3]});
-    } else {
-        uint32_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = round_p<PD>(x[i], sr, r[i]);
-        sst<u2>((uint16_t *)(void *)p + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-    }
-}
-
-template <int PD>
-__device__ __forceinline__ void store_p1(float *p, int64_t e, float x, bool sr, uint32_t r)
-{
-    if (PD == kP32) gst<float>(p + e, x);
-    else gst<uint16_t>((uint16_t *)(void *)p + e, (uint16_t)round_p<PD>(x, sr, r));
-}
-
-template <int SF>
-__device__ __forceinline__ void load_state4(const void *s, int64_t e, float out[4])
-{
-    if (SF == kF32) {
-        f4 x = sld<f4>((const float *)s + e);
-        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
-    } else {
-        u2 w = sld<u2>((const uint16_t *)s + e);
-        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
-        out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    }
-}
-
-template <int SF>
-__device__ __forceinline__ float load_state1(const void *s, int64_t e)
-{
-    if (SF == kF32) return gld<float>((const float *)s + e);
-    return bf16_lo(gld<uint16_t>((const uint16_t *)s + e));
-}
-
-// Store four fp32 moments in format SF; r[i] are the 16-bit random integers of
-// stochastic rounding (ignored otherwise).
-template <int SF>
-__device__ __forceinline__ void store_state4(void *s, int64_t e, const float x[4], const uint32_t r[4])
-{
-    if (SF == kF32) {
-        sst<f4>((float *)s + e, f4{x[0], x[1], x[2], x[3]});
-    } else {
-        uint32_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = SF == kBF16SR ? bf16_sr(x[i], r[i]) : bf16_rne(x[i]);
-        sst<u2>((uint16_t *)s + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-    }
-}
-
-template <int SF>
-__device__ __forceinline__ void store_state1(void *s, int64_t e, float x, uint32_t r)
-{
-    if (SF == kF32) gst<float>((float *)s + e, x);
-    else gst<uint16_t>((uint16_t *)s + e, (uint16_t)(SF == kBF16SR ? bf16_sr(x, r) : bf16_rne(x)));
-}
-
-// ---------------------------------------------------------------------------
-// fp32 and BF16 states
-
-struct Group {
-    float p[4], g[4], m[4], v[4], m2[4];
-};
-
-template <int OPT, int GD, int SF, int PD>
-__device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fresh, Group &x)
-{
-    load_p4<PD>(T.p, e, x.p);
-    load_grad4<GD>(T.g, e, x.g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x.m[i] = x.v[i] = x.m2[i] = 0.0f;
-    if (!fresh) {   // a step that restarts the moments from zero reads none
-        load_state4<SF>(T.s1, e, x.m);
-        load_state4<SF>(T.s2, e, x.v);
-        if (OPT == kAdEMAMix) load_state4<SF>(T.s3, e, x.m2);
-    }
-}
-
-template <int OPT, int GD, int SF, int PD>
-__device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
-                                          int64_t e, float lam, Group &x)
-{
-    float mo[4], vo[4], m2o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        Mom r = moments<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
-        x.p[i] = apply_update(x.p[i], s.d, lam, r.u);
-        mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
-    }
-    // stochastic rounding: the first stream's word rounds m (low half) and v
-    // (high half), the second stream's m2 (low half) and a 16-bit p (high half)
-    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
-    if (SF == kBF16SR) {
-        PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
-        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
-        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
-    }
-    const bool psr = PD != kP32 && a.p_sr;
-    if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
-        PhiloxOut w2 = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true);
-        rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
-        rp[0] = w2.w0 >> 16; rp[1] = w2.w1 >> 16; rp[2] = w2.w2 >> 16; rp[3] = w2.w3 >> 16;
-    }
-    store_p4<PD>(T.p, e, x.p, psr, rp);
-    store_state4<SF>(T.s1, e, mo, rm);
-    store_state4<SF>(T.s2, e, vo, rv);
-    if (OPT == kAdEMAMix) store_state4<SF>(T.s3, e, m2o, rm2);
-}
-
-template <int OPT, int GD, int SF, int PD>
-__device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, const DevTensor &T,
-                                          int64_t e, float lam)
-{
-    float g = load_grad1<GD>(T.g, e);
-    float m = 0.0f, v = 0.0f, m2 = 0.0f;
-    if (!a.fresh) {
-        m = load_state1<SF>(T.s1, e);
-        v = load_state1<SF>(T.s2, e);
-        if (OPT == kAdEMAMix) m2 = load_state1<SF>(T.s3, e);
-    }
-    Mom r = moments<OPT>(s, a, g, m, v, m2);
-    const float pn = apply_update(load_p1<PD>(T.p, e), s.d, lam, r.u);
-    uint32_t rm = 0, rv = 0, rm2 = 0, rp = 0;
-    if (SF == kBF16SR) {
-        uint32_t w = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3));
-        rm = w & 0xFFFFu; rv = w >> 16;
-    }
-    const bool psr = PD != kP32 && a.p_sr;
-    if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
-        uint32_t w2 = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true), (int)(e & 3));
-        rm2 = w2 & 0xFFFFu; rp = w2 >> 16;
-    }
-    store_p1<PD>(T.p, e, pn, psr, rp);
-    store_state1<SF>(T.s1, e, r.m, rm);
-    store_state1<SF>(T.s2, e, r.v, rv);
-    if (OPT == kAdEMAMix) store_state1<SF>(T.s3, e, r.m2, rm2);
-}
-
-#ifndef OPT_EW_WAVES_PER_EU
-#define OPT_EW_WAVES_PER_EU 0
-#endif
-#if OPT_EW_WAVES_PER_EU
-#define OPT_EW_ATTR __attribute__((amdgpu_waves_per_eu(OPT_EW_WAVES_PER_EU)))
-#else
-#define OPT_EW_ATTR
-#endif
-
-template <int OPT, int GD, int SF, int PD>
-__global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
-                                                                       const int32_t *__restrict__ ctab, StepArgs a)
-{
-    __shared__ Scalars sh;
-    if (threadIdx.x == 0) sh = make_scalars(a);
-    __syncthreads();
-    const Scalars s = sh;
-    const bool fresh = a.fresh != 0;
-    for (int64_t c = first_chunk(); c < a.nchunks; c += gridDim.x) {
-        const DevTensor T = tens[ctab[c]];
-        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
-        const int64_t len = min(a.chunk, T.numel - e0);
-        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
-        const int64_t ngroups = len >> 2;
-        int64_t i = threadIdx.x;
-        // kEwGroups groups per iteration: all their loads are issued before any math
-        for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
-            Group x[kEwGroups];
-#pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (i + u * kThreads), fresh, x[u]);
-#pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
-        }
-        for (; i < ngroups; i += kThreads) {
-            Group x0;
-            ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
-            ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
-        }
-        const int64_t tail = len & 3;
-        if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // 8-bit blockwise states
@@ -526,10 +255,11 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const bool valid = i < nmine;
-        p[i] = apply_update(x.p[i], s.d, lam, r[i].u);
-        mo[i] = valid ? r[i].m : 0.0f;
-        vo[i] = valid ? r[i].v : 0.0f;
-        m2o[i] = valid ? r[i].m2 : 0.0f;
+        const bool skip = a.skip_zeros && x.g[i] == 0.0f;   // keep p; code the old moments again
+        p[i] = skip ? x.p[i] : apply_update(x.p[i], s.d, lam, r[i].u);
+        mo[i] = valid ? (skip ? m_in[i] : r[i].m) : 0.0f;
+        vo[i] = valid ? (skip ? v_in[i] : r[i].v) : 0.0f;
+        m2o[i] = valid ? (skip ? m2_in[i] : r[i].m2) : 0.0f;
     }
     // stochastic rounding: the element's Philox word, low half for m, high
     // half for v, low half of the second stream's word for m2
@@ -722,6 +452,7 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         Mom r = moments<OPT>(s, a, g[q][j], m[q][j], v[q][j], m2[q][j]);
+                        if (a.skip_zeros && g[q][j] == 0.0f) r.u = 0.0f;   // no update there
                         su += (double)r.u * (double)r.u;
                         sp += (double)p[q][j] * (double)p[q][j];
                     }
@@ -739,6 +470,7 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
                             if (OPT == kAdEMAMix) m2 = read_state<SF, 2>(lds, T.s3, T.a3, e);
                         }
                         Mom r = moments<OPT>(s, a, g, m, v, m2);
+                        if (a.skip_zeros && g == 0.0f) r.u = 0.0f;
                         const float p = a.p_dtype == kP32 ? load_p1<kP32>(T.p, e)
                                       : a.p_dtype == kPBF16 ? load_p1<kPBF16>(T.p, e) : load_p1<kPF16>(T.p, e);
                         su += (double)r.u * (double)r.u;
@@ -1006,8 +738,6 @@ __global__ __launch_bounds__(256) void round_cast_kernel(const float *__restrict
     }
 }
 
-template <class K>
-static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, int threads);
 
 // Calibration stream: dst[j][i] = sum_k src[k][i] over fp32 arrays, 4 per
 // lane per access, grid-stride.  With nsrc reads and ndst writes it moves the
@@ -1078,28 +808,6 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
 // Persistent grid: the workgroups that fit on the device at once (the
 // kernel's occupancy times the compute units), unless the caller fixed a
 // per-CU count; never more workgroups than chunks.
-template <class K>
-static int grid_size(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, int threads)
-{
-    int per_cu = lg.wgs_per_cu;
-    if (per_cu <= 0) {
-        int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds) != hipSuccess || occ < 1)
-            occ = 1;
-        per_cu = occ;
-    }
-    return (int)std::max<int64_t>(1, std::min<int64_t>(nchunks, (int64_t)lg.ncu * per_cu));
-}
-
-template <class K, class... Args>
-static hipError_t launch_persistent(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks, hipStream_t st,
-                                    Args... args)
-{
-    const int grid = grid_size(kernel, lds, lg, nchunks, kThreads);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, st, args...);
-    return hipGetLastError();
-}
-
 template <class K, class... Args>
 static hipError_t launch_persistent_q8(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks,
                                        hipStream_t st, Args... args)
@@ -1109,30 +817,13 @@ static hipError_t launch_persistent_q8(K kernel, size_t lds, const LaunchGeom &l
     return hipGetLastError();
 }
 
-template <int OPT, int GD, int PD>
-static hipError_t launch_ew_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
-{
-    const int64_t nc = a.nchunks;
-    switch (fmt) {
-    case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    default: return hipErrorInvalidValue;
-    }
-}
+hipError_t launch_step_ew(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st);
 
 template <int OPT, int GD>
 static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
     const int64_t nc = a.nchunks;
-    if (!blocked(fmt)) {
-        switch (a.p_dtype) {
-        case kP32: return launch_ew_t<OPT, GD, kP32>(fmt, a, lg, st);
-        case kPBF16: return launch_ew_t<OPT, GD, kPBF16>(fmt, a, lg, st);
-        case kPF16: return launch_ew_t<OPT, GD, kPF16>(fmt, a, lg, st);
-        default: return hipErrorInvalidValue;
-        }
-    }
+    if (!blocked(fmt)) return launch_step_ew(OPT, GD, fmt, a, lg, st);
     if (a.p_dtype != kP32) return hipErrorInvalidValue;
     switch (fmt) {
     case kQ8: return launch_persistent_q8(step_q8_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);

@@ -1,0 +1,188 @@
+// opt_kernels_ew.hip -- gfx950 kernel of the element-wise two-state step
+// with fp32 or BF16 states (AdamW, AdEMAMix), for fp32, BF16 or FP16
+// parameters and gradients.
+//
+// A persistent grid of 256-thread workgroups walks the bucket's chunk table
+// with a grid stride; inside a chunk every lane owns groups of 4 consecutive
+// elements, so fp32 arrays move as 128-bit accesses and 16-bit ones as 64-bit
+// accesses, every access instruction of a wave64 fully coalesced.  kEwGroups
+// groups are loaded before any arithmetic.  HBM-bound: every byte is read or
+// written once per step and no intermediate leaves registers.
+#include "opt_elem.h"
+
+namespace optstep {
+
+// ---------------------------------------------------------------------------
+// fp32 and BF16 states
+
+struct Group {
+    float p[4], g[4], m[4], v[4], m2[4];
+};
+
+template <int OPT, int GD, int SF, int PD>
+__device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fresh, Group &x)
+{
+    load_p4<PD>(T.p, e, x.p);
+    load_grad4<GD>(T.g, e, x.g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.m[i] = x.v[i] = x.m2[i] = 0.0f;
+    if (!fresh) {   // a step that restarts the moments from zero reads none
+        load_state4<SF>(T.s1, e, x.m);
+        load_state4<SF>(T.s2, e, x.v);
+        if (OPT == kAdEMAMix) load_state4<SF>(T.s3, e, x.m2);
+    }
+}
+
+template <int OPT, int GD, int SF, int PD>
+__device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
+                                          int64_t e, float lam, Group &x)
+{
+    float mo[4], vo[4], m2o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        Mom r = moments<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
+        const float pn = apply_update(x.p[i], s.d, lam, r.u);
+        mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
+        if (a.skip_zeros && x.g[i] == 0.0f) {   // p (decay included) and the states as they were
+            mo[i] = x.m[i]; vo[i] = x.v[i]; m2o[i] = x.m2[i];
+        } else {
+            x.p[i] = pn;
+        }
+    }
+    // stochastic rounding: the first stream's word rounds m (low half) and v
+    // (high half), the second stream's m2 (low half) and a 16-bit p (high half)
+    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
+    if (SF == kBF16SR) {
+        PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
+        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
+        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
+    }
+    const bool psr = PD != kP32 && a.p_sr;
+    if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
+        PhiloxOut w2 = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true);
+        rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
+        rp[0] = w2.w0 >> 16; rp[1] = w2.w1 >> 16; rp[2] = w2.w2 >> 16; rp[3] = w2.w3 >> 16;
+    }
+    store_p4<PD>(T.p, e, x.p, psr, rp);
+    store_state4<SF>(T.s1, e, mo, rm);
+    store_state4<SF>(T.s2, e, vo, rv);
+    if (OPT == kAdEMAMix) store_state4<SF>(T.s3, e, m2o, rm2);
+}
+
+template <int OPT, int GD, int SF, int PD>
+__device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, const DevTensor &T,
+                                          int64_t e, float lam)
+{
+    float g = load_grad1<GD>(T.g, e);
+    float m = 0.0f, v = 0.0f, m2 = 0.0f;
+    if (!a.fresh) {
+        m = load_state1<SF>(T.s1, e);
+        v = load_state1<SF>(T.s2, e);
+        if (OPT == kAdEMAMix) m2 = load_state1<SF>(T.s3, e);
+    }
+    Mom r = moments<OPT>(s, a, g, m, v, m2);
+    const float p_old = load_p1<PD>(T.p, e);
+    float pn = apply_update(p_old, s.d, lam, r.u);
+    if (a.skip_zeros && g == 0.0f) {
+        pn = p_old;
+        r.m = m; r.v = v; r.m2 = m2;
+    }
+    uint32_t rm = 0, rv = 0, rm2 = 0, rp = 0;
+    if (SF == kBF16SR) {
+        uint32_t w = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3));
+        rm = w & 0xFFFFu; rv = w >> 16;
+    }
+    const bool psr = PD != kP32 && a.p_sr;
+    if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
+        uint32_t w2 = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true), (int)(e & 3));
+        rm2 = w2 & 0xFFFFu; rp = w2 >> 16;
+    }
+    store_p1<PD>(T.p, e, pn, psr, rp);
+    store_state1<SF>(T.s1, e, r.m, rm);
+    store_state1<SF>(T.s2, e, r.v, rv);
+    if (OPT == kAdEMAMix) store_state1<SF>(T.s3, e, r.m2, rm2);
+}
+
+#ifndef OPT_EW_WAVES_PER_EU
+#define OPT_EW_WAVES_PER_EU 0
+#endif
+#if OPT_EW_WAVES_PER_EU
+#define OPT_EW_ATTR __attribute__((amdgpu_waves_per_eu(OPT_EW_WAVES_PER_EU)))
+#else
+#define OPT_EW_ATTR
+#endif
+
+template <int OPT, int GD, int SF, int PD>
+__global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
+                                                                       const int32_t *__restrict__ ctab, StepArgs a)
+{
+    __shared__ Scalars sh;
+    if (threadIdx.x == 0) sh = make_scalars(a);
+    __syncthreads();
+    const Scalars s = sh;
+    const bool fresh = a.fresh != 0;
+    for (int64_t c = first_chunk(); c < a.nchunks; c += gridDim.x) {
+        const DevTensor T = tens[ctab[c]];
+        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
+        const int64_t len = min(a.chunk, T.numel - e0);
+        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
+        const int64_t ngroups = len >> 2;
+        int64_t i = threadIdx.x;
+        // kEwGroups groups per iteration: all their loads are issued before any math
+        for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
+            Group x[kEwGroups];
+#pragma unroll
+            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (i + u * kThreads), fresh, x[u]);
+#pragma unroll
+            for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
+        }
+        for (; i < ngroups; i += kThreads) {
+            Group x0;
+            ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
+            ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
+        }
+        const int64_t tail = len & 3;
+        if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
+    }
+}
+
+template <int OPT, int GD, int PD>
+static hipError_t launch_ew_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
+{
+    const int64_t nc = a.nchunks;
+    switch (fmt) {
+    case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OPT, int GD>
+static hipError_t launch_ew_g(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
+{
+    switch (a.p_dtype) {
+    case kP32: return launch_ew_t<OPT, GD, kP32>(fmt, a, lg, st);
+    case kPBF16: return launch_ew_t<OPT, GD, kPBF16>(fmt, a, lg, st);
+    case kPF16: return launch_ew_t<OPT, GD, kPF16>(fmt, a, lg, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OPT>
+static hipError_t launch_ew_o(int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
+{
+    switch (gd) {
+    case kGradF32: return launch_ew_g<OPT, kGradF32>(fmt, a, lg, st);
+    case kGradBF16: return launch_ew_g<OPT, kGradBF16>(fmt, a, lg, st);
+    case kGradF16: return launch_ew_g<OPT, kGradF16>(fmt, a, lg, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_step_ew(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
+{
+    return opt == kAdamW ? launch_ew_o<kAdamW>(gd, fmt, a, lg, st) : launch_ew_o<kAdEMAMix>(gd, fmt, a, lg, st);
+}
+
+}  // namespace optstep

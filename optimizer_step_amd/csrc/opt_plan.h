@@ -11,7 +11,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kQBlock = 256;       // elements per 8-bit absmax block
 constexpr int kUTile = 1024;       // elements per update-norm partial
 
-enum Opt : int { kAdamW = 0, kAdEMAMix = 1 };
+enum Opt : int { kAdamW = 0, kAdEMAMix = 1, kMomentum = 2, kRMSprop = 3, kAdagrad = 4, kLion = 5 };
 enum Fmt : int { kF32 = 0, kBF16RN = 1, kBF16SR = 2, kQ8 = 3, kFP8RN = 4, kFP8SR = 5, kFP4RN = 6, kFP4SR = 7 };
 
 // Formats stored as blocks of 256 codes with one fp32 absmax per block.
@@ -82,6 +82,7 @@ struct StepArgs {
     const float *grad_scale;       // device float or null (1)
     int32_t p_dtype;               // ParamT of the bucket's parameters
     int32_t p_sr;                  // 1: 16-bit parameters are stored with stochastic rounding
+    int32_t skip_zeros;            // 1: elements whose gradient is exactly 0 keep p and their states
 };
 
 }  // namespace optstep

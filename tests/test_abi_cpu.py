@@ -269,3 +269,15 @@ def test_p16_rules(L):
     assert _call(L, "opt_step_adamw", t, 4) == -2
     t = [L.OptTensor(4096, 4096, 8192, 12288, None, None, None, None, 16, 3, 0)]      # unknown p dtype
     assert _call(L, "opt_step_adamw", t, 0) == -1
+
+
+def test_one_state_argument_checks(L):
+    lib = L.lib()
+    arr = (L.OptTensor * 1)(*_tensor(L))
+    assert lib.opt_step_1state(9, arr, 1, 0, L.hparams(), None) == -1          # unknown optimizer
+    assert lib.opt_step_1state(5, arr, 1, 3, L.hparams(), None) == -2          # blockwise states
+    assert lib.opt_step_1state(5, arr, 1, 0, L.hparams(max_unorm=1.0), None) == -2
+    assert lib.opt_step_1state(2, arr, 1, 0, L.hparams(skip_zeros=True, beta1=1.5), None) == -1
+    bad = (L.OptTensor * 1)(L.OptTensor(4096, 4096, 0, 0, None, None, None, None, 16, 0, 0))
+    assert lib.opt_step_1state(2, bad, 1, 0, L.hparams(), None) == -1         # no s1
+    assert lib.opt_step_1state(2, None, 0, 0, L.hparams(), None) == 0

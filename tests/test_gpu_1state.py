@@ -1,0 +1,139 @@
+"""GPU parity of the one-state optimizers (momentum, RMSprop, Adagrad with
+coupled L2; Lion with decoupled decay) and of skip_zeros in every step
+(bitsandbytes PR "Fix decoupled weight decay ordering in the CUDA
+Adam/AdEMAMix kernels": intro and Not covered) against the oracle.
+
+Bars: fp32 states and p within 1e-6 relative; BF16 nearest states within one
+BF16 step per step; stochastic-rounding states bit-exact; blockwise codes and
+absmax bit-exact; skipped elements bit-identical to their inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import Case, bf16_ulps, compare, fp32_close, nan_equal_bits, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 1000, 4099, 32768 + 333]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import optimizer_step_amd as osa
+    assert torch.cuda.is_available()
+    osa.lib()
+    osa.opt_debug_set_launch(32768, 0)
+    yield
+
+
+def _grad(n, t, k, gd, zeros=False):
+    g = synth.grads(n, t, k, std=1e-1)
+    if zeros:
+        g[(t + k) % 5::5] = 0.0
+        g[:1] = 0.0
+    if gd == "bf16":
+        return synth.bf16_words(g)
+    return g.astype(np.float16) if gd == "f16" else g
+
+
+def _run_1s(name, fmt, gds, steps, hp, zeros=False):
+    import torch
+    import optimizer_step_amd as osa
+    ps = [synth.params(n, k, std=0.5) for k, n in enumerate(SIZES)]
+    p0 = [p.copy() for p in ps]
+    ss = [np.zeros(n, np.float32 if fmt == "f32" else np.uint16) for n in SIZES]
+    for t in range(1, steps + 1):
+        for k, n in enumerate(SIZES):
+            h = oracle.make_hp(step=t, seed=synth.SR_SEED, tensor_index=k, **hp)
+            oracle.step_1state(name, fmt, h, ps[k], _grad(n, t, k, gds[k], zeros), ss[k])
+    dev = []
+    for k, n in enumerate(SIZES):
+        d = {"p": to_dev(p0[k].copy()), "g": to_dev(_grad(n, 1, k, gds[k], zeros))}
+        d["s1"] = torch.zeros(n, dtype=torch.float32 if fmt == "f32" else torch.bfloat16, device="cuda")
+        dev.append(d)
+    tl = osa.TensorList(dev)
+    for t in range(1, steps + 1):
+        for k, n in enumerate(SIZES):
+            dev[k]["g"].copy_(to_dev(_grad(n, t, k, gds[k], zeros)))
+        osa.opt_step_1state(name, tl, fmt, osa.hparams(step=t, seed=synth.SR_SEED, **hp))
+    torch.cuda.synchronize()
+    return ps, ss, dev
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16_rn", "bf16_sr"])
+@pytest.mark.parametrize("name", ["momentum", "rmsprop", "adagrad", "lion"])
+def test_one_state_parity(name, fmt):
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.05)
+    steps = 4
+    ps, ss, dev = _run_1s(name, fmt, ["f32", "bf16", "f16", "bf16"], steps, hp)
+    for k in range(len(SIZES)):
+        assert fp32_close(to_host(dev[k]["p"]), ps[k]), k
+        g = to_host(dev[k]["s1"])
+        if fmt == "f32":
+            assert fp32_close(g, ss[k]), k
+        elif fmt == "bf16_rn":
+            assert int(bf16_ulps(g, ss[k]).max(initial=0)) <= steps, k
+        else:
+            assert nan_equal_bits(g, ss[k]), k
+
+
+@pytest.mark.parametrize("name", ["momentum", "lion"])
+def test_one_state_skip_zeros_and_reset(name):
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.99, weight_decay=0.05, skip_zeros=True, reset_interval=2)
+    ps, ss, dev = _run_1s(name, "bf16_sr", ["bf16", "f32", "f16", "f32"], 5, hp, zeros=True)
+    for k in range(len(SIZES)):
+        assert fp32_close(to_host(dev[k]["p"]), ps[k]), k
+        assert nan_equal_bits(to_host(dev[k]["s1"]), ss[k]), k
+
+
+def test_one_state_rejections():
+    import torch
+    import optimizer_step_amd as osa
+    d = {"p": torch.zeros(16, device="cuda"), "g": torch.zeros(16, device="cuda"),
+         "s1": torch.zeros(16, device="cuda")}
+    for fmt, hp, status in (("q8", osa.hparams(), osa.OPT_EUNSUPPORTED),
+                            ("f32", osa.hparams(max_unorm=1.0), osa.OPT_EUNSUPPORTED)):
+        with pytest.raises(osa.OptError) as e:
+            osa.opt_step_1state("lion", [d], fmt, hp)
+        assert e.value.status == status
+    with pytest.raises(osa.OptError):
+        osa.opt_step_1state(1, [d], "f32", osa.hparams())
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16_rn", "bf16_sr", "q8", "fp8_sr", "fp4_rn"])
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+def test_two_state_skip_zeros(opt, fmt):
+    """Exact-zero gradients (a fifth of the elements, moving each step) keep
+    their p and moments; with resets every 3 steps as well."""
+    hp = dict(lr=1e-3, weight_decay=0.1, skip_zeros=True, reset_interval=3)
+    if opt == "ademamix":
+        hp.update(beta3=0.999, alpha=5.0)
+
+    bf = [False, True, False, True]
+
+    def g_of(t, k, n):
+        g = synth.grads(n, t, k, std=1e-2)
+        g[(t + k) % 5::5] = 0.0
+        return synth.bf16_words(g) if bf[k] else g
+    case = Case(opt, fmt, SIZES, bf, 5, hp, grad_override=g_of)
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+
+
+def test_two_state_skip_zeros_prepass():
+    hp = dict(lr=1e-3, weight_decay=0.1, skip_zeros=True, max_unorm=0.5)
+
+    def g_of(t, k, n):
+        g = synth.grads(n, t, k, std=1e-2)
+        g[::3] = 0.0
+        return g
+    case = Case("adamw", "f32", [5000, 65537], False, 3, hp, grad_override=g_of)
+    ps, st, no = case.run_oracle()
+    dev, ng = case.run_gpu()
+    compare(case, dev, ps, st)
+    for (t, k, u2, p2) in no:
+        g = ng[t - 1]
+        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= 1e-12 * p2, (t, k)
