@@ -55,21 +55,62 @@ def counter_traffic(workload, launches_elems):
 # ---------------------------------------------------------------------------
 # workloads on the device
 
+def carve(torch, arrays, device):
+    """One device allocation holding every per-element array of a workload
+    (p, g, states, absmax), each starting on a 256-byte boundary; returns
+    views.  Flat buffers like this are how training frameworks hold a bucket
+    of parameters and optimizer states.  (Measured on MI355X: the step's
+    bandwidth over the same arrays varies from process to process, 5.1 to
+    6.1 TB/s, with neither the launch shape nor the offsets between the
+    arrays changing it within a process; on one box one allocation ran at
+    6.09-6.16 TB/s in every process where four separate ones ran at
+    5.2-5.6.)"""
+    sizes = {}
+    off = 0
+    for name, dtype, n in arrays:
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        sizes[name] = (off, dtype, n, nbytes)
+        off += (nbytes + 255) // 256 * 256
+    arena = torch.empty(max(off, 256), dtype=torch.uint8, device=device)
+    return {name: arena[o:o + nb].view(dt) for name, (o, dt, n, nb) in sizes.items()}, arena
+
+
 def build_workload(name, torch, osa, synth):
     """Allocate and fill one workload; returns (tensor list, fmt, opt, hp kwargs,
-    elements, bytes per element, description)."""
+    elements, bytes per element, what to keep alive)."""
     w = synth.WORKLOADS[name]
     sizes = w["sizes"]
     total = sum(sizes)
     dev = torch.device("cuda")
     fmt = w["fmt"]
     opt = w["opt"]
-    P = torch.empty(total, dtype=torch.float32, device=dev)
+    qs, qu = synth.codebook_signed(), synth.codebook_unsigned()
+    nst = 3 if opt == "ademamix" else (2 if opt == "adamw" else 1)
+    nb = (total + 255) // 256
+    arrays = [("p", torch.float32, total), ("g", torch.bfloat16 if w["grad_bf16"] else torch.float32, total)]
+    for i in range(1, nst + 1):
+        if fmt == "f32":
+            arrays.append((f"s{i}", torch.float32, total))
+        elif fmt.startswith("bf16"):
+            arrays.append((f"s{i}", torch.bfloat16, total))
+        else:
+            arrays.append((f"s{i}", torch.uint8, (total + 1) // 2 if fmt.startswith("fp4") else total))
+            arrays.append((f"absmax{i}", torch.float32, nb))
+    views, arena = carve(torch, arrays, dev)
+    P, G = views["p"], views["g"]
     synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
     g_std = w["g_std"] if w["g_std"] != "decay" else 1e-2
-    G = synth.device_grads(total, dev, g_std, 1, bf16=w["grad_bf16"], mask_scale=w.get("mask_scale"))
-    qs, qu = synth.codebook_signed(), synth.codebook_unsigned()
-    states = osa.state_buffers(fmt, total, opt, device=dev, qmap_signed=qs, qmap_unsigned=qu)
+    G.copy_(synth.device_grads(total, dev, g_std, 1, bf16=w["grad_bf16"], mask_scale=w.get("mask_scale")))
+    torch.cuda.empty_cache()
+    # fresh states: zeros; 8-bit codes at the code of 0 in each codebook
+    fresh = osa.state_buffers(fmt, 1, opt, device=dev, qmap_signed=qs, qmap_unsigned=qu)
+    states = {}
+    for key in fresh:
+        if key.startswith("absmax"):
+            views[key].zero_()
+        else:
+            views[key].copy_(fresh[key][:1].expand(views[key].numel()))
+        states[key] = views[key]
     tensors = []
     off = 0
     for n in sizes:
@@ -91,16 +132,63 @@ def build_workload(name, torch, osa, synth):
     elif w.get("clip"):
         bpe += 2 if w["grad_bf16"] else 4       # the norm reads g once more
     hp = dict(w["hp"])
-    keep = (P, G, states, qs, qu)
+    keep = (arena, None, states, qs, qu)
     return tensors, fmt, opt, hp, total, bpe, keep
 
 
+def time_cast(name, steps, warmup, torch, osa, synth):
+    """The standalone FP32 -> BF16 rounding cast: 4 B read + 2 B written."""
+    w = synth.WORKLOADS[name]
+    n = w["sizes"][0]
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(x, synth.PARAM_SEED, w["p_std"])
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sr = w["fmt"].endswith("sr")
+    for i in range(warmup):
+        osa.opt_round_cast(x, out, sr, synth.SR_SEED, i, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        osa.opt_round_cast(x, out, sr, synth.SR_SEED, warmup + i, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sum(per) / steps
+    # torch's built-in nearest cast over the same array, for comparison
+    for _ in range(warmup):
+        x.to(torch.bfloat16)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        x.to(torch.bfloat16)
+    b.record(stream)
+    torch.cuda.synchronize()
+    torch_ms = a.elapsed_time(b) / steps
+    gb = 6 * n / 1e9
+    row = {"workload": name, "format": "bf16_sr" if sr else "bf16_rn", "optimizer": "cast", "elements": n,
+           "tensors": 1, "bytes_per_element": 6, "ms_per_step": ms, "ms_median": per[len(per) // 2],
+           "gelem_per_s": n / (ms * 1e-3) / 1e9, "achieved_GBps": gb / (ms * 1e-3),
+           "frac_of_peak": gb / (ms * 1e-3) / PEAK_GBPS, "launch_ms": ms,
+           "torch_nearest_cast_ms": torch_ms}
+    del x, out
+    torch.cuda.empty_cache()
+    return row
+
+
 def time_workload(name, steps, warmup, torch, osa, synth):
+    if synth.WORKLOADS[name]["opt"] == "cast":
+        return time_cast(name, steps, warmup, torch, osa, synth)
     tensors, fmt, opt, hp, total, bpe, keep = build_workload(name, torch, osa, synth)
     qs, qu = keep[3], keep[4]
     w = synth.WORKLOADS[name]
     tl = osa.TensorList(tensors)
-    step_fn = osa.opt_step_adamw if opt == "adamw" else osa.opt_step_ademamix
+    if opt in osa.ONE_STATE:
+        step_fn = lambda tl_, fmt_, h_, un_, stream=None: osa.opt_step_1state(opt, tl_, fmt_, h_, stream=stream)
+    else:
+        step_fn = osa.opt_step_adamw if opt == "adamw" else osa.opt_step_ademamix
     unorm = None
     if hp.get("max_unorm", 0) > 0:
         unorm = torch.empty(2 * len(tensors), dtype=torch.float64, device="cuda")
@@ -210,7 +298,7 @@ def calibrate(torch, osa, n=1 << 30, reps=3):
 # ---------------------------------------------------------------------------
 # profile summaries (from rocprofv3 csv output)
 
-HEADLINE_KERNEL = "step_ew_kernel<0, 1, 0>"
+HEADLINE_KERNEL = "step_ew_kernel<0, 1, 0, 0>"
 CALIB_KERNEL = "debug_stream_kernel"
 
 
@@ -232,7 +320,14 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd_trace, cmd_fetch, cm
 
     stats = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
     head = [r for r in stats if HEADLINE_KERNEL in r["Name"]][0]
-    calib = [r for r in stats if CALIB_KERNEL in r["Name"]][0]
+    calib = [r for r in stats if CALIB_KERNEL in r["Name"]]
+    # the bench line the traced run printed, if kept next to the trace
+    live = None
+    for cand in glob.glob(os.path.join(trace_dir, "..", "trace_bench.json")):
+        try:
+            live = json.loads(open(cand).read().strip().splitlines()[-1])
+        except (ValueError, IndexError):
+            live = None
 
     def counters(d, name):
         rows = list(csv.DictReader(open(one(os.path.join(d, "**", "*counter_collection.csv")))))
@@ -254,15 +349,20 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd_trace, cmd_fetch, cm
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_trace.txt"), "w") as f:
         f.write("rocprofv3 kernel statistics: AdamW step over the Llama-7B-shaped list (290 tensors,\n"
-                f"6,738,411,520 elements; fp32 p/m/v, bf16 g), plus the calibration copy kernel.\n"
+                f"6,738,411,520 elements; fp32 p/m/v, bf16 g), and the calibration copy kernel if it ran.\n"
                 f"command: {cmd_trace}\n\n")
         f.write(f"{'kernel':48s} {'calls':>6s} {'avg ms':>10s} {'min ms':>10s} {'max ms':>10s}\n")
-        for r in (head, calib):
+        for r in [head] + calib:
             nm = HEADLINE_KERNEL if r is head else CALIB_KERNEL
             f.write(f"{nm:48s} {r['Calls']:>6s} {float(r['AverageNs'])/1e6:10.3f} "
                     f"{float(r['MinNs'])/1e6:10.3f} {float(r['MaxNs'])/1e6:10.3f}\n")
         f.write(f"\nstep kernel: {alg_r + alg_w:.4e} algorithmic bytes per launch / {avg_ms:.3f} ms = "
                 f"{(alg_r + alg_w) / avg_ms / 1e6:.0f} GB/s ({(alg_r + alg_w) / avg_ms / 1e6 / PEAK_GBPS:.1%} of 8 TB/s)\n")
+        if live is not None:
+            lm = live["roofline"]["launch_ms"]
+            f.write(f"the same run's bench line (HIP events on the launch stream, timed steps only): "
+                    f"{lm:.3f} ms per launch, {live['roofline']['achieved']:.0f} GB/s, "
+                    f"value {live['value']:.1f} Gelem/s\n")
     with open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_counters.txt"), "w") as f:
         f.write("rocprofv3 HBM byte counters (KiB per dispatch), one counter per run.\n"
                 f"commands:\n  {cmd_fetch}\n  {cmd_write}\n\n")
@@ -283,6 +383,31 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd_trace, cmd_fetch, cm
     print(open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_counters.txt")).read())
 
 
+def summarize_rows_trace(trace_dir, cmd):
+    """profiles/bench_rows_kernel_stats.txt: per-kernel time statistics of a
+    rocprofv3 --kernel-trace --stats run over every bench row."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = os.path.join(ROOT, "profiles", "bench_rows_kernel_stats.txt")
+    with open(out, "w") as f:
+        f.write("rocprofv3 kernel statistics over every bench row (template arguments: optimizer\n"
+                "0 AdamW 1 AdEMAMix 2 momentum 5 Lion; gradient 0 fp32 1 bf16 2 fp16; state format 0 fp32\n"
+                "1 BF16-RN 2 BF16-SR 3 8-bit 4 FP8-RN 5 FP8-SR 6 FP4-RN 7 FP4-SR; parameter 0 fp32).\n"
+                f"command: {cmd}\n\n")
+        f.write(f"{'kernel':70s} {'calls':>6s} {'avg ms':>9s} {'min ms':>9s} {'max ms':>9s}\n")
+        for r in rows:
+            nm = r["Name"].replace("optstep::", "")
+            nm = nm.split("(")[0] if len(nm) > 70 else nm
+            f.write(f"{nm[:70]:70s} {r['Calls']:>6s} {float(r['AverageNs'])/1e6:9.3f} "
+                    f"{float(r['MinNs'])/1e6:9.3f} {float(r['MaxNs'])/1e6:9.3f}\n")
+    print(open(out).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,12 +420,19 @@ def main():
                          "HBM counters scale the step kernel's")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from three rocprofv3 output folders and exit")
+    ap.add_argument("--summarize-rows-trace", metavar="TRACE_DIR",
+                    help="write profiles/bench_rows_kernel_stats.txt from a rocprofv3 run over all rows and exit")
     args = ap.parse_args()
+    if args.summarize_rows_trace:
+        summarize_rows_trace(args.summarize_rows_trace,
+                             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace "
+                             "-- python bench.py > gpurun_out/trace_bench.json")
+        return
     if args.summarize_profiles:
         base = "python bench.py --rows none --no-cpu --calibrate"
         summarize_profiles(*args.summarize_profiles,
                            cmd_trace="rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
-                                     f"{base} --steps 10 --warmup 3",
+                                     "python bench.py > gpurun_out/trace_bench.json",
                            cmd_fetch=f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- {base} --steps 2 --warmup 1",
                            cmd_write=f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- {base} --steps 2 --warmup 1")
         return
@@ -322,7 +454,8 @@ def main():
     rows = []
     others = ["adamw_q8_1g", "ademamix_f32_268m", "adamw_f32_unorm_268m", "adamw_bf16_1g", "adamw_bf16_sr_1g",
               "adamw_fp8_rn_1g", "adamw_fp8_sr_1g", "adamw_fp4_rn_1g", "adamw_fp4_sr_1g",
-              "gradnorm_bf16_llama7b", "adamw_f32_clip_llama7b"]
+              "gradnorm_bf16_llama7b", "adamw_f32_clip_llama7b", "momentum_f32_1g", "lion_f32_1g",
+              "cast_bf16_sr_1g"]
     if args.rows == "none":
         others = []
     elif args.rows != "all":

@@ -303,7 +303,8 @@ def state_buffers(fmt, numel, optimizer="adamw", device="cuda", qmap_signed=None
     import torch
     import numpy as np
     fmt = FORMATS.get(fmt, fmt)
-    nst = 3 if OPTIMIZERS.get(optimizer, optimizer) == ADEMAMIX else 2
+    o = OPTIMIZERS.get(optimizer, ONE_STATE.get(optimizer, optimizer))
+    nst = 3 if o == ADEMAMIX else (2 if o == ADAMW else 1)
     out = {}
     if fmt == STATE_Q8:
         nb = (numel + BLOCK - 1) // BLOCK

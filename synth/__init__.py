@@ -203,6 +203,13 @@ WORKLOADS = {
                              mask_scale=(0.1, 100.0), steps=5,
                              hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8))
        for f in ("fp8_rn", "fp8_sr", "fp4_rn", "fp4_sr")},
+    # one-state optimizers, bf16 gradients, fp32 state, 2^30 elements
+    **{f"{o}_f32_1g": dict(opt=o, fmt="f32", sizes=[2**30], grad_bf16=True, p_std=0.02, g_std=1e-3, steps=5,
+                          hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.99, eps=1e-8))
+       for o in ("momentum", "lion")},
+    # the standalone FP32 -> BF16 stochastic-rounding cast of 2^30 values
+    "cast_bf16_sr_1g": dict(opt="cast", fmt="bf16_sr", sizes=[2**30], grad_bf16=False, p_std=1.0, g_std=1e-3,
+                            steps=5, hp=dict()),
     # gradient 2-norm of the Llama-7B-shaped bf16 gradient list alone
     "gradnorm_bf16_llama7b": dict(opt="adamw", fmt="f32", sizes=[n for _, n in llama7b_shapes()],
                                   grad_bf16=True, p_std=0.02, g_std=1e-3, steps=5, norm_only=True,
@@ -220,7 +227,7 @@ def bytes_per_element(opt, fmt, grad_bf16, p_bytes=4):
     states, write p and the states (8-bit: codes plus one fp32 absmax per 256
     elements per state, read and written; FP8 the same with E4M3 codes; FP4
     half a byte per element per state plus the absmax)."""
-    nst = 3 if opt == "ademamix" else 2
+    nst = 3 if opt == "ademamix" else (2 if opt == "adamw" else 1)
     g = 2 if grad_bf16 else 4
     if fmt == "f32":
         s = 4
