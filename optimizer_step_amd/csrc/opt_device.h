@@ -250,30 +250,39 @@ __host__ __device__ inline int mini_dec_shift(float A)
     return A > 0.0f ? floor_log2(A) - F::kEmax : -400;
 }
 
-// Magnitude code of y >= 0 on F's grid; SR with the 16-bit integer r.
+// Magnitude code of y >= 0 on F's grid; SR with the 16-bit integer r.  In
+// the format's normal range (y >= 2^Emin) the binary32 exponent and top MB
+// fraction bits are the code below y, less a constant, and the other
+// `drop` = 23 - MB fraction bits decide the rounding (nearest-even: the usual
+// add-and-shift; SR: their top 16 bits plus r carry).  Below 2^Emin the grid
+// step is 2^(Emin - MB): t = y / step is exact, its integer part is the code
+// below and its fraction decides.  A carry moves to the next code, which is
+// the next grid value across binades too; codes past the largest finite one
+// take it.
 template <class F, bool SR>
 __host__ __device__ inline uint32_t mini_mag(float y, uint32_t r)
 {
+    constexpr int drop = 23 - F::kMB;
+    constexpr uint32_t K = (uint32_t)(127 + F::kEmin - 1) << F::kMB;   // code = (bits >> drop) - K
     const uint32_t u = fbits(y) & 0x7FFFFFFFu;
-    const int ef = (int)(u >> 23);
-    const uint32_t M = (u & 0x7FFFFFu) | (ef ? 0x800000u : 0u);   // y = M * 2^(e - 23)
-    const int e = ef ? ef - 127 : -126;
-    const int eg = e > F::kEmin ? e : F::kEmin;                   // binade of the grid step
-    int sh = 23 - F::kMB + (eg - e);                              // y / step = M >> sh, rest below
-    if (sh > 40) sh = 40;                                         // y / step < 2^-16: code 0, no carry
-    uint32_t code = ((uint32_t)(eg - F::kEmin) << F::kMB) + (sh < 32 ? M >> sh : 0u);
-    const uint32_t rem = sh < 32 ? (M & ((1u << sh) - 1u)) : M;
-    bool up;
+    uint32_t cn;
     if (SR) {
-        // the top 16 bits of the dropped part (fewer bits are dropped only
-        // by formats with more than 7 fraction bits, in their normal range)
-        const uint32_t l16 = (F::kMB <= 7 || sh >= 16) ? rem >> (sh - 16) : rem << (16 - sh);
-        up = l16 + r >= 65536u;
+        const uint32_t l16 = drop >= 16 ? (u >> (drop >= 16 ? drop - 16 : 0)) & 0xFFFFu
+                                        : (u << (drop >= 16 ? 0 : 16 - drop)) & 0xFFFFu;
+        cn = (u >> drop) - K + ((l16 + r) >> 16);
     } else {
-        const uint32_t half = sh <= 24 ? 1u << (sh - 1) : 0u;     // sh > 24: below half a step
-        up = sh <= 24 && (rem > half || (rem == half && (code & 1u)));
+        cn = ((u + (1u << (drop - 1)) - 1u + ((u >> drop) & 1u)) >> drop) - K;
     }
-    code += up ? 1u : 0u;
+    const float t = bitsf(fbits(y) & 0x7FFFFFFFu) * (float)(1u << (F::kMB - F::kEmin));   // exact
+    uint32_t cs;
+    if (SR) {
+        const float fl = floorf(t);
+        const uint32_t l16 = (uint32_t)((t - fl) * 65536.0f);   // exact: floor(frac * 2^16)
+        cs = (uint32_t)fl + ((l16 + r) >> 16);
+    } else {
+        cs = (uint32_t)rintf(t);                                // ties to even
+    }
+    const uint32_t code = u < ((uint32_t)(127 + F::kEmin) << 23) ? cs : cn;
     return code < F::kMaxC ? code : F::kMaxC;
 }
 

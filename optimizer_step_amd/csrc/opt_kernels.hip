@@ -174,8 +174,25 @@ __device__ __forceinline__ void q8_load(const StepArgs &a, const QChunk &C, uint
 }
 
 // Four stored values of one state.  WHICH: 0 = m, 1 = v, 2 = m2.
+// Grid values of every FP8/FP4 code (scale 1), one copy per workgroup in LDS:
+// E4M3 codes 0..255, or E2M1 codes 0..15 then unsigned E2M2 codes 0..15.
+constexpr int kMiniTab = 256;
+
+template <int SF>
+__device__ __forceinline__ void fill_mini_tab(float *tab, int tid, int nthreads)
+{
+    for (int i = tid; i < (fp4_fmt(SF) ? 32 : 256); i += nthreads)
+        tab[i] = fp4_fmt(SF) ? (i < 16 ? mini_decode<E2M1>((uint32_t)i, 0) : mini_decode<E2M2U>((uint32_t)(i - 16), 0))
+                             : mini_decode<E4M3>((uint32_t)i, 0);
+}
+
+// Four stored values of one state.  WHICH: 0 = m, 1 = v, 2 = m2.  FP8/FP4
+// codes read their grid value from `mtab` (fill_mini_tab) when it is given,
+// else decode it arithmetically; either way value(code) * 2^(floor(log2 A) -
+// emax) rounded to binary32.
 template <int SF, int WHICH>
-__device__ __forceinline__ void blk_decode4(const uint32_t *lds, uint32_t c, float A, float out[4])
+__device__ __forceinline__ void blk_decode4(const uint32_t *lds, uint32_t c, float A, float out[4],
+                                            const float *mtab = nullptr)
 {
     if (SF == kQ8) {
         const float *tab = (const float *)lds + (WHICH == 1 ? 256 : 0);
@@ -184,15 +201,18 @@ __device__ __forceinline__ void blk_decode4(const uint32_t *lds, uint32_t c, flo
     } else if (fp4_fmt(SF) && WHICH == 1) {
         const int sc = mini_dec_shift<E2M2U>(A);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = mini_decode<E2M2U>((c >> (4 * i)) & 0xFu, sc);
+        for (int i = 0; i < 4; ++i)
+            out[i] = mtab ? ldexpf(mtab[16 + ((c >> (4 * i)) & 0xFu)], sc) : mini_decode<E2M2U>((c >> (4 * i)) & 0xFu, sc);
     } else if (fp4_fmt(SF)) {
         const int sc = mini_dec_shift<E2M1>(A);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = mini_decode<E2M1>((c >> (4 * i)) & 0xFu, sc);
+        for (int i = 0; i < 4; ++i)
+            out[i] = mtab ? ldexpf(mtab[(c >> (4 * i)) & 0xFu], sc) : mini_decode<E2M1>((c >> (4 * i)) & 0xFu, sc);
     } else {
         const int sc = mini_dec_shift<E4M3>(A);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = mini_decode<E4M3>((c >> (8 * i)) & 0xFFu, sc);
+        for (int i = 0; i < 4; ++i)
+            out[i] = mtab ? ldexpf(mtab[(c >> (8 * i)) & 0xFFu], sc) : mini_decode<E4M3>((c >> (8 * i)) & 0xFFu, sc);
     }
     if (mini_fmt(SF) && !finite_f(A)) {          // a poisoned block reads as NaN
 #pragma unroll
@@ -225,15 +245,15 @@ __device__ __forceinline__ uint32_t blk_encode4(const uint32_t *lds, const StepA
 // FULL: every lane holds four elements (all blocks but a tensor's short last one).
 template <int OPT, int SF, bool FULL>
 __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const QChunk &C,
-                                          const uint32_t *lds, uint32_t b, int nmine, int lane, float lam,
-                                          const QIn &x)
+                                          const uint32_t *lds, const float *mtab, uint32_t b, int nmine,
+                                          int lane, float lam, const QIn &x)
 {
     if (FULL) nmine = 4;
     const uint32_t e = b * kQBlock + lane * 4;
     float m_in[4], v_in[4], m2_in[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    blk_decode4<SF, 0>(lds, x.cm, x.A1, m_in);
-    blk_decode4<SF, 1>(lds, x.cv, x.A2, v_in);
-    if (OPT == kAdEMAMix) blk_decode4<SF, 2>(lds, x.cm2, x.A3, m2_in);
+    blk_decode4<SF, 0>(lds, x.cm, x.A1, m_in, mtab);
+    blk_decode4<SF, 1>(lds, x.cv, x.A2, v_in, mtab);
+    if (OPT == kAdEMAMix) blk_decode4<SF, 2>(lds, x.cm2, x.A3, m2_in, mtab);
     if (a.fresh) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) m_in[i] = v_in[i] = m2_in[i] = 0.0f;
@@ -328,8 +348,11 @@ __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__
 {
     extern __shared__ uint32_t lds[];
     __shared__ Scalars sh;
+    __shared__ float mtab_s[mini_fmt(SF) ? kMiniTab : 1];
     if (SF == kQ8)
         for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
+    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
+    const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
@@ -352,18 +375,18 @@ __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__
             for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, SF, true>(a, C, b + u * kQ8Waves, 4, lane, x[u]);
 #pragma unroll
             for (int u = 0; u < kQ8Blocks; ++u)
-                q8_finish<OPT, SF, true>(a, s, C, lds, b + u * kQ8Waves, 4, lane, lam, x[u]);
+                q8_finish<OPT, SF, true>(a, s, C, lds, mtab, b + u * kQ8Waves, 4, lane, lam, x[u]);
         }
         for (; b < nfull; b += kQ8Waves) {
             QIn x0;
             q8_load<OPT, GD, SF, true>(a, C, b, 4, lane, x0);
-            q8_finish<OPT, SF, true>(a, s, C, lds, b, 4, lane, lam, x0);
+            q8_finish<OPT, SF, true>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
         }
         if (b < nblk) {   // the tensor's short last block
             const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
             QIn x0;
             q8_load<OPT, GD, SF, false>(a, C, b, nm, lane, x0);
-            q8_finish<OPT, SF, false>(a, s, C, lds, b, nm, lane, lam, x0);
+            q8_finish<OPT, SF, false>(a, s, C, lds, mtab, b, nm, lane, lam, x0);
         }
     }
 }
@@ -522,6 +545,29 @@ __global__ __launch_bounds__(kThreads) void unorm_reduce_kernel(const DevTensor 
 // in tensor order.  Fixed orders, no atomics.  The tile partials reuse the
 // update-norm partials buffer; slot 2t+1 carries the max as a double.
 
+// One full tile's contribution from this lane: its 16 elements in order.
+__device__ __forceinline__ void gnorm_acc(const float g[4][4], double &sq, uint32_t &mx)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double x = (double)g[q][j];
+            sq += x * x;
+            mx = max(mx, fbits(g[q][j]) & 0x7FFFFFFFu);
+        }
+}
+
+__device__ __forceinline__ void gnorm_store(const StepArgs &a, int64_t slot, int lane, double sq, uint32_t mx)
+{
+    sq = wave_sum(sq);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        gst<double>(a.partials + 2 * slot, sq);
+        gst<double>(a.partials + 2 * slot + 1, (double)bitsf(mx));
+    }
+}
+
 template <int GD>
 __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTensor *__restrict__ tens,
                                                                   const int32_t *__restrict__ ctab,
@@ -535,21 +581,31 @@ __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTenso
         const int64_t e0 = (c - T.chunk_begin) * a.chunk;
         const int64_t len = min(a.chunk, T.numel - e0);
         const int64_t ntile = (len + kUTile - 1) / kUTile;
-        for (int64_t tt = wave; tt < ntile; tt += kWaves) {
+        const int64_t nfull = len / kUTile;
+        int64_t tt = wave;
+        // two full tiles per wave at a time: all 8 loads before the sums
+        for (; tt + kWaves < nfull; tt += 2 * kWaves) {
+            float g0[4][4], g1[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                load_grad4<GD>(T.g, e0 + tt * kUTile + q * 256 + lane * 4, g0[q]);
+                load_grad4<GD>(T.g, e0 + (tt + kWaves) * kUTile + q * 256 + lane * 4, g1[q]);
+            }
+            double sq0 = 0.0, sq1 = 0.0;
+            uint32_t mx0 = 0, mx1 = 0;
+            gnorm_acc(g0, sq0, mx0);
+            gnorm_acc(g1, sq1, mx1);
+            gnorm_store(a, c * tiles_per_chunk + tt, lane, sq0, mx0);
+            gnorm_store(a, c * tiles_per_chunk + tt + kWaves, lane, sq1, mx1);
+        }
+        for (; tt < ntile; tt += kWaves) {
             double sq = 0.0;
             uint32_t mx = 0;
-            if ((tt + 1) * kUTile <= len) {
+            if (tt < nfull) {
                 float g[4][4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) load_grad4<GD>(T.g, e0 + tt * kUTile + q * 256 + lane * 4, g[q]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const double x = (double)g[q][j];
-                        sq += x * x;
-                        mx = max(mx, fbits(g[q][j]) & 0x7FFFFFFFu);
-                    }
+                gnorm_acc(g, sq, mx);
             } else {
                 for (int q = 0; q < kUTile / 256; ++q) {
                     const int64_t i0 = tt * kUTile + q * 256 + lane * 4;
@@ -562,13 +618,7 @@ __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTenso
                     }
                 }
             }
-            sq = wave_sum(sq);
-            mx = wave_max_u32(mx);
-            if (lane == 0) {
-                const int64_t slot = c * tiles_per_chunk + tt;
-                gst<double>(a.partials + 2 * slot, sq);
-                gst<double>(a.partials + 2 * slot + 1, (double)bitsf(mx));
-            }
+            gnorm_store(a, c * tiles_per_chunk + tt, lane, sq, mx);
         }
     }
 }
@@ -704,37 +754,61 @@ __global__ void debug_mini_kernel(int elem, float A, const float *x, const uint3
 // tied to the element, so the grid does not change the result.  Each lane
 // takes groups of 4 elements: 128-bit loads, 64-bit stores.
 template <bool BF, bool SR>
+__device__ __forceinline__ void cast_group(const float v[4], uint16_t *out, int64_t q, int cnt, uint64_t seed,
+                                           uint64_t offset)
+{
+    uint32_t r[4] = {0, 0, 0, 0};
+    if (SR) {
+        const PhiloxOut w = philox4x32_10((uint32_t)q, (uint32_t)((uint64_t)q >> 32), (uint32_t)offset,
+                                          (uint32_t)(offset >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
+        r[0] = w.w0 & 0xFFFFu; r[1] = w.w1 & 0xFFFFu; r[2] = w.w2 & 0xFFFFu; r[3] = w.w3 & 0xFFFFu;
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h[i] = BF ? (SR ? bf16_sr(v[i], r[i]) : bf16_rne(v[i])) : (SR ? f16_sr(v[i], r[i]) : f16_rne(v[i]));
+    if (cnt == 4) {
+        sst<u2>(out + 4 * q, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+    } else {
+        for (int i = 0; i < cnt; ++i) gst<uint16_t>(out + 4 * q + i, (uint16_t)h[i]);
+    }
+}
+
+// The standalone rounding cast: n fp32 values to BF16 (BF) or FP16 words,
+// nearest-even or stochastic.  Element j's random integer is the low half of
+// word j%4 of Philox4x32-10 keyed by the seed, counter (j>>2, j>>34, offset):
+// tied to the element, so the grid does not change the result.  Lanes take
+// groups of 4 elements (128-bit loads, 64-bit stores), four groups loaded
+// before any rounding.
+template <bool BF, bool SR>
 __global__ __launch_bounds__(256) void round_cast_kernel(const float *__restrict__ x, uint16_t *__restrict__ out,
                                                          int64_t n, uint64_t seed, uint64_t offset)
 {
-    const int64_t ngroups = n >> 2;
+    constexpr int U = 4;
+    const int64_t nfull = n >> 2;                       // groups of exactly 4
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q <= ngroups; q += stride) {
-        const int64_t e = q * 4;
-        const int cnt = (int)min((int64_t)4, n - e);
+    int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    for (; q + (U - 1) * stride < nfull; q += U * stride) {
+        float v[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const f4 t = sld<f4>(x + 4 * (q + u * stride));
+            v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) cast_group<BF, SR>(v[u], out, q + u * stride, 4, seed, offset);
+    }
+    for (; q <= nfull; q += stride) {
+        const int cnt = (int)min((int64_t)4, n - 4 * q);
         if (cnt <= 0) break;
         float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (cnt == 4) {
-            f4 t = sld<f4>(x + e);
+            const f4 t = sld<f4>(x + 4 * q);
             v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
         } else {
-            for (int i = 0; i < cnt; ++i) v[i] = gld<float>(x + e + i);
+            for (int i = 0; i < cnt; ++i) v[i] = gld<float>(x + 4 * q + i);
         }
-        uint32_t r[4] = {0, 0, 0, 0};
-        if (SR) {
-            const PhiloxOut w = philox4x32_10((uint32_t)q, (uint32_t)((uint64_t)q >> 32), (uint32_t)offset,
-                                              (uint32_t)(offset >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
-            r[0] = w.w0 & 0xFFFFu; r[1] = w.w1 & 0xFFFFu; r[2] = w.w2 & 0xFFFFu; r[3] = w.w3 & 0xFFFFu;
-        }
-        uint32_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            h[i] = BF ? (SR ? bf16_sr(v[i], r[i]) : bf16_rne(v[i])) : (SR ? f16_sr(v[i], r[i]) : f16_rne(v[i]));
-        if (cnt == 4) {
-            sst<u2>(out + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-        } else {
-            for (int i = 0; i < cnt; ++i) gst<uint16_t>(out + e + i, (uint16_t)h[i]);
-        }
+        cast_group<BF, SR>(v, out, q, cnt, seed, offset);
     }
 }
 
