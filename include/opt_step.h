@@ -319,10 +319,12 @@ int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n);
 int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, int32_t ndst, int64_t n,
                      void *stream);
 
-/* Launch geometry for all later calls in this process: elements per chunk (a
- * positive multiple of 1024, at most 2^24) and persistent workgroups per compute unit
- * (1..64, or 0 for as many as fit, the default).  Results do not depend on
- * either. */
+/* Launch geometry for all later calls in this process: elements per chunk of
+ * the host's chunk table (a power of two in [1024, 2^24]; default 32768) and
+ * workgroups per compute unit: 0 (the default) launches one workgroup per
+ * tile (whole chunks for the blockwise step), 1..64 a persistent grid of that
+ * many per compute unit walking the same tiles with a grid stride.  Results
+ * do not depend on either.  OPT_EINVAL for other values. */
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);
 
 #ifdef __cplusplus

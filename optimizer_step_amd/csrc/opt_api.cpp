@@ -59,8 +59,8 @@ int hip_fail(hipError_t e, const char *what)
 // ---------------------------------------------------------------------------
 // launch configuration
 
-int64_t g_chunk = 32768;      // elements per chunk; multiple of 1024
-int g_wgs_per_cu = 0;         // persistent workgroups per compute unit (0: occupancy)
+int64_t g_chunk = 32768;      // elements per chunk; a power of two >= 1024
+int g_wgs_per_cu = 0;         // workgroups per compute unit (0: one per tile, or occupancy)
 
 constexpr int kMaxDevices = 64;
 constexpr int kSlots = 16;
@@ -856,8 +856,8 @@ int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, i
 
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu)
 {
-    if (chunk <= 0 || chunk % 1024 != 0 || chunk > (1 << 24))
-        return fail(OPT_EINVAL, "chunk must be a positive multiple of 1024, at most 2^24");
+    if (chunk < 1024 || chunk > (1 << 24) || (chunk & (chunk - 1)) != 0)
+        return fail(OPT_EINVAL, "chunk must be a power of two in [1024, 2^24]");
     if (wgs_per_cu < 0 || wgs_per_cu > 64) return fail(OPT_EINVAL, "wgs_per_cu must be in [0, 64]");
     std::lock_guard<std::mutex> lock(g_mu);
     g_chunk = chunk;

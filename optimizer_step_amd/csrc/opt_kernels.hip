@@ -339,7 +339,17 @@ constexpr int kQ8Threads = OPT_Q8_THREADS;
 constexpr int kQ8Waves = kQ8Threads / 64;
 constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
 
-// Blockwise states (8-bit codebook, FP8, FP4): one 256-element block per wave.
+#ifndef OPT_Q8_TILE
+#define OPT_Q8_TILE 32768
+#endif
+// Elements per tile of the blockwise step (a power of two, a multiple of the
+// 8 x 256 elements one pass of the workgroup's waves covers).
+constexpr int64_t kQ8Tile = OPT_Q8_TILE;
+static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
+
+// Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
+// tile scheduling of opt_elem.h), one 256-element block per wave at a time,
+// kQ8Blocks blocks in flight per wave.
 template <int OPT, int GD, int SF>
 __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__restrict__ tens,
                                                              const int32_t *__restrict__ ctab,
@@ -359,10 +369,10 @@ __global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
-        const DevTensor T = tens[ctab[c]];
-        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
-        const int64_t len = min(a.chunk, T.numel - e0);
+    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
+        DevTensor T;
+        int64_t e0, len;
+        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
         const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
         const uint32_t nblk = (uint32_t)((len + kQBlock - 1) / kQBlock);
         const uint32_t nfull = (uint32_t)(len / kQBlock);
@@ -442,11 +452,11 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
     const Scalars s = sh;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t tiles_per_chunk = a.chunk / kUTile;
-    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
-        const DevTensor T = tens[ctab[c]];
-        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
-        const int64_t len = min(a.chunk, T.numel - e0);
+    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
+        DevTensor T;
+        int64_t e0, len;
+        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
+        const int64_t slot0 = w * a.tile / kUTile;   // the tile's first partial in the chunk space
         const int64_t ntile = (len + kUTile - 1) / kUTile;
         for (int64_t tt = wave; tt < ntile; tt += kWaves) {
             double su = 0.0, sp = 0.0;
@@ -504,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
             su = wave_sum(su);
             sp = wave_sum(sp);
             if (lane == 0) {
-                const int64_t slot = c * tiles_per_chunk + tt;
+                const int64_t slot = slot0 + tt;
                 gst<double>(a.partials + 2 * slot, su);
                 gst<double>(a.partials + 2 * slot + 1, sp);
             }
@@ -568,6 +578,13 @@ __device__ __forceinline__ void gnorm_store(const StepArgs &a, int64_t slot, int
     }
 }
 
+#ifndef OPT_GN_UNITS
+#define OPT_GN_UNITS 2
+#endif
+// One workgroup per tile of kGnTile gradient elements: OPT_GN_UNITS partials
+// of 1024 elements per wave.
+constexpr int64_t kGnTile = (int64_t)kWaves * OPT_GN_UNITS * kUTile;
+
 template <int GD>
 __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTensor *__restrict__ tens,
                                                                   const int32_t *__restrict__ ctab,
@@ -575,11 +592,11 @@ __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTenso
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t tiles_per_chunk = a.chunk / kUTile;
-    for (int64_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
-        const DevTensor T = tens[ctab[c]];
-        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
-        const int64_t len = min(a.chunk, T.numel - e0);
+    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
+        DevTensor T;
+        int64_t e0, len;
+        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
+        const int64_t slot0 = w * a.tile / kUTile;   // the tile's first partial in the chunk space
         const int64_t ntile = (len + kUTile - 1) / kUTile;
         const int64_t nfull = len / kUTile;
         int64_t tt = wave;
@@ -595,8 +612,8 @@ __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTenso
             uint32_t mx0 = 0, mx1 = 0;
             gnorm_acc(g0, sq0, mx0);
             gnorm_acc(g1, sq1, mx1);
-            gnorm_store(a, c * tiles_per_chunk + tt, lane, sq0, mx0);
-            gnorm_store(a, c * tiles_per_chunk + tt + kWaves, lane, sq1, mx1);
+            gnorm_store(a, slot0 + tt, lane, sq0, mx0);
+            gnorm_store(a, slot0 + tt + kWaves, lane, sq1, mx1);
         }
         for (; tt < ntile; tt += kWaves) {
             double sq = 0.0;
@@ -618,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTenso
                     }
                 }
             }
-            gnorm_store(a, c * tiles_per_chunk + tt, lane, sq, mx);
+            gnorm_store(a, slot0 + tt, lane, sq, mx);
         }
     }
 }
@@ -780,35 +797,40 @@ __device__ __forceinline__ void cast_group(const float v[4], uint16_t *out, int6
 // tied to the element, so the grid does not change the result.  Lanes take
 // groups of 4 elements (128-bit loads, 64-bit stores), four groups loaded
 // before any rounding.
+// One workgroup per tile of kCastTile values (kCastGroups groups of four per
+// lane), dispatched in order as workgroups retire.
+constexpr int kCastGroups = 2;
+constexpr int64_t kCastTile = 256 * kCastGroups * 4;
+
 template <bool BF, bool SR>
 __global__ __launch_bounds__(256) void round_cast_kernel(const float *__restrict__ x, uint16_t *__restrict__ out,
                                                          int64_t n, uint64_t seed, uint64_t offset)
 {
-    constexpr int U = 4;
-    const int64_t nfull = n >> 2;                       // groups of exactly 4
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    for (; q + (U - 1) * stride < nfull; q += U * stride) {
-        float v[U][4];
+    const int64_t ntiles = (n + kCastTile - 1) / kCastTile;
+    for (int64_t w = blockIdx.x; w < ntiles; w += gridDim.x) {
+        const int64_t q0 = w * (kCastTile / 4);   // the tile's first group of four
+        if ((w + 1) * kCastTile <= n) {
+            float v[kCastGroups][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const f4 t = sld<f4>(x + 4 * (q + u * stride));
-            v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
-        }
+            for (int u = 0; u < kCastGroups; ++u) {
+                const f4 t = sld<f4>(x + 4 * (q0 + threadIdx.x + u * 256));
+                v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
+            }
 #pragma unroll
-        for (int u = 0; u < U; ++u) cast_group<BF, SR>(v[u], out, q + u * stride, 4, seed, offset);
-    }
-    for (; q <= nfull; q += stride) {
-        const int cnt = (int)min((int64_t)4, n - 4 * q);
-        if (cnt <= 0) break;
-        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (cnt == 4) {
-            const f4 t = sld<f4>(x + 4 * q);
-            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-        } else {
-            for (int i = 0; i < cnt; ++i) v[i] = gld<float>(x + 4 * q + i);
+            for (int u = 0; u < kCastGroups; ++u) cast_group<BF, SR>(v[u], out, q0 + threadIdx.x + u * 256, 4, seed, offset);
+        } else {   // the short last tile
+            for (int64_t q = q0 + threadIdx.x; 4 * q < n; q += 256) {
+                const int cnt = (int)min((int64_t)4, n - 4 * q);
+                float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (cnt == 4) {
+                    const f4 t = sld<f4>(x + 4 * q);
+                    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+                } else {
+                    for (int i = 0; i < cnt; ++i) v[i] = gld<float>(x + 4 * q + i);
+                }
+                cast_group<BF, SR>(v, out, q, cnt, seed, offset);
+            }
         }
-        cast_group<BF, SR>(v, out, q, cnt, seed, offset);
     }
 }
 
@@ -830,34 +852,38 @@ struct StreamArgs {
 __global__ __launch_bounds__(kThreads) void debug_stream_kernel(StreamArgs a)
 {
     constexpr int U = OPT_STREAM_UNROLL;
+    constexpr int64_t kTileG = (int64_t)kThreads * U;   // groups of four per tile
     const int64_t ng = a.n >> 2;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
-    for (; i + (U - 1) * stride < ng; i += U * stride) {
-        f4 acc[U];
+    const int64_t ntiles = (ng + kTileG - 1) / kTileG;
+    for (int64_t w = blockIdx.x; w < ntiles; w += gridDim.x) {
+        const int64_t i0 = w * kTileG + threadIdx.x;
+        if ((w + 1) * kTileG <= ng) {
+            f4 acc[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < U; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 6; ++k)
-            if (k < a.nsrc) {
+            for (int k = 0; k < 6; ++k)
+                if (k < a.nsrc) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc[u] += sld<f4>(a.src[k] + 4 * (i + u * stride));
+                    for (int u = 0; u < U; ++u) acc[u] += sld<f4>(a.src[k] + 4 * (i0 + u * kThreads));
+                }
+#pragma unroll
+            for (int k = 0; k < 6; ++k)
+                if (k < a.ndst) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) sst<f4>(a.dst[k] + 4 * (i0 + u * kThreads), acc[u]);
+                }
+        } else {
+            for (int64_t i = i0; i < ng; i += kThreads) {
+                f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < 6; ++k)
+                    if (k < a.nsrc) acc += sld<f4>(a.src[k] + 4 * i);
+#pragma unroll
+                for (int k = 0; k < 6; ++k)
+                    if (k < a.ndst) sst<f4>(a.dst[k] + 4 * i, acc);
             }
-#pragma unroll
-        for (int k = 0; k < 6; ++k)
-            if (k < a.ndst) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) sst<f4>(a.dst[k] + 4 * (i + u * stride), acc[u]);
-            }
-    }
-    for (; i < ng; i += stride) {
-        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 6; ++k)
-            if (k < a.nsrc) acc += sld<f4>(a.src[k] + 4 * i);
-#pragma unroll
-        for (int k = 0; k < 6; ++k)
-            if (k < a.ndst) sst<f4>(a.dst[k] + 4 * i, acc);
+        }
     }
 }
 
@@ -870,8 +896,10 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
     a.nsrc = nsrc;
     a.ndst = ndst;
     a.n = n;
-    const int64_t groups = (n / 4 + kThreads - 1) / kThreads;
-    const int grid = grid_size(debug_stream_kernel, 0, lg, groups, kThreads);
+    const int64_t tile_g = (int64_t)kThreads * OPT_STREAM_UNROLL;
+    int64_t want = (n / 4 + tile_g - 1) / tile_g;
+    if (lg.wgs_per_cu > 0) want = min(want, (int64_t)lg.ncu * lg.wgs_per_cu);
+    const unsigned grid = (unsigned)max((int64_t)1, min(want, kMaxGrid));
     hipLaunchKernelGGL(debug_stream_kernel, dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -879,15 +907,13 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
 // ---------------------------------------------------------------------------
 // launchers (called by opt_api.cpp)
 
-// Persistent grid: the workgroups that fit on the device at once (the
-// kernel's occupancy times the compute units), unless the caller fixed a
-// per-CU count; never more workgroups than chunks.
-template <class K, class... Args>
-static hipError_t launch_persistent_q8(K kernel, size_t lds, const LaunchGeom &lg, int64_t nchunks,
-                                       hipStream_t st, Args... args)
+// The blockwise step over tiles of kQ8Tile elements (opt_elem.h).
+template <class K>
+static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
 {
-    const int grid = grid_size(kernel, lds, lg, nchunks, kQ8Threads);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kQ8Threads), lds, st, args...);
+    set_tiles(a, kQ8Tile);
+    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kQ8Threads), lds, st, a.tens, a.chunk_tensor,
+                       a.q.words, a);
     return hipGetLastError();
 }
 
@@ -896,15 +922,14 @@ hipError_t launch_step_ew(int opt, int gd, int fmt, const StepArgs &a, const Lau
 template <int OPT, int GD>
 static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
-    const int64_t nc = a.nchunks;
     if (!blocked(fmt)) return launch_step_ew(OPT, GD, fmt, a, lg, st);
     if (a.p_dtype != kP32) return hipErrorInvalidValue;
     switch (fmt) {
-    case kQ8: return launch_persistent_q8(step_q8_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
-    case kFP8RN: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP8RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
-    case kFP8SR: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP8SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
-    case kFP4RN: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP4RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
-    case kFP4SR: return launch_persistent_q8(step_q8_kernel<OPT, GD, kFP4SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kQ8: return launch_q8_tiles(step_q8_kernel<OPT, GD, kQ8>, lds, lg, a, st);
+    case kFP8RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8RN>, 0, lg, a, st);
+    case kFP8SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8SR>, 0, lg, a, st);
+    case kFP4RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4RN>, 0, lg, a, st);
+    case kFP4SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4SR>, 0, lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -926,19 +951,29 @@ hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const Launch
                          : launch_step_o<kAdEMAMix>(gd, fmt, a, lg, lds, st);
 }
 
+// The update-norm pre-pass over tiles of one 1024-element partial per wave.
+constexpr int64_t kUnTile = (int64_t)kWaves * kUTile;
+
+template <class K>
+static hipError_t launch_unorm_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
+{
+    set_tiles(a, kUnTile);
+    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kThreads), lds, st, a.tens, a.chunk_tensor, a.q.words, a);
+    return hipGetLastError();
+}
+
 template <int OPT, int GD>
 static hipError_t launch_unorm_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
-    const int64_t nc = a.nchunks;
     switch (fmt) {
-    case kF32: return launch_persistent(unorm_partials_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kF32: return launch_unorm_tiles(unorm_partials_kernel<OPT, GD, kF32>, 0, lg, a, st);
     case kBF16RN:
-    case kBF16SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
-    case kQ8: return launch_persistent(unorm_partials_kernel<OPT, GD, kQ8>, lds, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kBF16SR: return launch_unorm_tiles(unorm_partials_kernel<OPT, GD, kBF16RN>, 0, lg, a, st);
+    case kQ8: return launch_unorm_tiles(unorm_partials_kernel<OPT, GD, kQ8>, lds, lg, a, st);
     case kFP8RN:
-    case kFP8SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kFP8RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP8SR: return launch_unorm_tiles(unorm_partials_kernel<OPT, GD, kFP8RN>, 0, lg, a, st);
     case kFP4RN:
-    case kFP4SR: return launch_persistent(unorm_partials_kernel<OPT, GD, kFP4RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a.q.words, a);
+    case kFP4SR: return launch_unorm_tiles(unorm_partials_kernel<OPT, GD, kFP4RN>, 0, lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -965,9 +1000,9 @@ hipError_t launch_gnorm(int gd, const StepArgs &a, const LaunchGeom &lg, int nte
 {
     hipError_t e = hipSuccess;
     if (a.nchunks > 0)
-        e = gd == kGradF32    ? launch_persistent(gnorm_partials_kernel<kGradF32>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a)
-            : gd == kGradBF16 ? launch_persistent(gnorm_partials_kernel<kGradBF16>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a)
-                              : launch_persistent(gnorm_partials_kernel<kGradF16>, 0, lg, a.nchunks, st, a.tens, a.chunk_tensor, a);
+        e = gd == kGradF32    ? launch_tiles(gnorm_partials_kernel<kGradF32>, kGnTile, 0, lg, a, st)
+            : gd == kGradBF16 ? launch_tiles(gnorm_partials_kernel<kGradBF16>, kGnTile, 0, lg, a, st)
+                              : launch_tiles(gnorm_partials_kernel<kGradF16>, kGnTile, 0, lg, a, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gnorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
                        (const double *)a.partials, out);
@@ -1000,10 +1035,9 @@ hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, 
 hipError_t launch_round_cast(const float *x, uint16_t *out, int64_t n, int bf16, int sr, uint64_t seed,
                              uint64_t offset, const LaunchGeom &lg, hipStream_t st)
 {
-    const int64_t groups = (n + 3) / 4;
-    const int64_t want = (groups + 255) / 256;
-    const int64_t cap = (int64_t)lg.ncu * 8;    // a few waves in flight per SIMD, grid-stride beyond
-    const unsigned grid = (unsigned)max((int64_t)1, min(want, cap));
+    int64_t want = (n + kCastTile - 1) / kCastTile;
+    if (lg.wgs_per_cu > 0) want = min(want, (int64_t)lg.ncu * lg.wgs_per_cu);
+    const unsigned grid = (unsigned)max((int64_t)1, min(want, kMaxGrid));
     if (bf16) {
         if (sr) hipLaunchKernelGGL((round_cast_kernel<true, true>), dim3(grid), dim3(256), 0, st, x, out, n, seed, offset);
         else hipLaunchKernelGGL((round_cast_kernel<true, false>), dim3(grid), dim3(256), 0, st, x, out, n, seed, offset);

@@ -3,9 +3,10 @@
 // (bitsandbytes PR "Fix decoupled weight decay ordering in the CUDA
 // Adam/AdEMAMix kernels", intro: how the 1-state kernels couple the decay).
 //
-// Same layout as the two-state element-wise step: a persistent grid walks
-// the bucket's chunk table; lanes own groups of four consecutive elements,
-// kEwGroups groups loaded before any arithmetic.  Per element, in binary32
+// Same layout as the two-state element-wise step: one workgroup per tile of
+// kEwTile1 elements (the tile scheduling of opt_elem.h); lanes own groups of
+// four consecutive elements, kEwGroups groups loaded before the scalars are
+// formed and before any arithmetic.  Per element, in binary32
 // with no contraction:
 //   g' = g*scale (+ wd*p for the coupled-L2 three when wd != 0)
 //   momentum  m' = g' on the state's first step, else b1*m + g';  p' = p - lr*m'
@@ -62,11 +63,10 @@ struct Group1 {
     float p[4], g[4], s[4];
 };
 
-template <int OPT, int GD, int SF>
-__global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__restrict__ tens,
-                                                           const int32_t *__restrict__ ctab, StepArgs a)
+constexpr int64_t kEwTile1 = (int64_t)kThreads * kEwGroups * 4;
+
+__device__ __forceinline__ Scalars1 publish_scalars1(const StepArgs &a, Scalars1 &sh)
 {
-    __shared__ Scalars1 sh;
     if (threadIdx.x == 0) {
         Scalars1 s;
         s.om1 = 1.0f - a.beta1;
@@ -78,69 +78,91 @@ __global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__re
         sh = s;
     }
     __syncthreads();
-    const Scalars1 s = sh;
-    const bool fresh = a.fresh != 0;
-    for (int64_t c = first_chunk(); c < a.nchunks; c += gridDim.x) {
-        const DevTensor T = tens[ctab[c]];
-        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
-        const int64_t len = min(a.chunk, T.numel - e0);
-        const int64_t ngroups = len >> 2;
-        int64_t i = threadIdx.x;
-        auto finish = [&](int64_t e, Group1 &x) {
-            float sn[4];
-            uint32_t r[4] = {0, 0, 0, 0};
+    return sh;
+}
+
+template <int OPT, int GD, int SF>
+__device__ __forceinline__ void s1_load(const DevTensor &T, int64_t e, bool fresh, Group1 &x)
+{
+    f4 pv = sld<f4>(T.p + e);
+    x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
+    load_grad4<GD>(T.g, e, x.g);
+    x.s[0] = x.s[1] = x.s[2] = x.s[3] = 0.0f;
+    if (!fresh) load_state4<SF>(T.s1, e, x.s);
+}
+
+template <int OPT, int GD, int SF>
+__device__ __forceinline__ void s1_finish(const StepArgs &a, const Scalars1 &s, const DevTensor &T, int64_t e,
+                                          Group1 &x)
+{
+    float sn[4];
+    uint32_t r[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float p_old = x.p[j];
-                sn[j] = one_state<OPT>(a, s, x.g[j], x.p[j], x.s[j]);
-                if (a.skip_zeros && x.g[j] == 0.0f) {   // p and the state as they were
-                    x.p[j] = p_old;
-                    sn[j] = x.s[j];
-                }
-            }
-            if (SF == kBF16SR) {
-                const PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
-                r[0] = w.w0 & 0xFFFFu; r[1] = w.w1 & 0xFFFFu; r[2] = w.w2 & 0xFFFFu; r[3] = w.w3 & 0xFFFFu;
-            }
-            sst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
-            store_state4<SF>(T.s1, e, sn, r);
-        };
-        auto load = [&](int64_t e, Group1 &x) {
-            f4 pv = sld<f4>(T.p + e);
-            x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
-            load_grad4<GD>(T.g, e, x.g);
-            x.s[0] = x.s[1] = x.s[2] = x.s[3] = 0.0f;
-            if (!fresh) load_state4<SF>(T.s1, e, x.s);
-        };
-        for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
+    for (int j = 0; j < 4; ++j) {
+        const float p_old = x.p[j];
+        sn[j] = one_state<OPT>(a, s, x.g[j], x.p[j], x.s[j]);
+        if (a.skip_zeros && x.g[j] == 0.0f) {   // p and the state as they were
+            x.p[j] = p_old;
+            sn[j] = x.s[j];
+        }
+    }
+    if (SF == kBF16SR) {
+        const PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
+        r[0] = w.w0 & 0xFFFFu; r[1] = w.w1 & 0xFFFFu; r[2] = w.w2 & 0xFFFFu; r[3] = w.w3 & 0xFFFFu;
+    }
+    sst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
+    store_state4<SF>(T.s1, e, sn, r);
+}
+
+template <int OPT, int GD, int SF>
+__device__ __forceinline__ void s1_single(const StepArgs &a, const Scalars1 &s, const DevTensor &T, int64_t e,
+                                          bool fresh)
+{
+    float p = gld<float>(T.p + e);
+    const float g = load_grad1<GD>(T.g, e);
+    const float st = fresh ? 0.0f : load_state1<SF>(T.s1, e);
+    const float p_old = p;
+    float sn = one_state<OPT>(a, s, g, p, st);
+    if (a.skip_zeros && g == 0.0f) {
+        p = p_old;
+        sn = st;
+    }
+    uint32_t r = 0;
+    if (SF == kBF16SR)
+        r = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3)) & 0xFFFFu;
+    gst<float>(T.p + e, p);
+    store_state1<SF>(T.s1, e, sn, r);
+}
+
+template <int OPT, int GD, int SF>
+__global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__restrict__ tens,
+                                                           const int32_t *__restrict__ ctab, StepArgs a)
+{
+    __shared__ Scalars1 sh;
+    Scalars1 s;
+    bool have_s = false;
+    const bool fresh = a.fresh != 0;
+    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
+        DevTensor T;
+        int64_t e0, len;
+        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
+        if (len == kEwTile1) {
             Group1 x[kEwGroups];
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) load(e0 + 4 * (i + u * kThreads), x[u]);
+            for (int u = 0; u < kEwGroups; ++u) s1_load<OPT, GD, SF>(T, e0 + 4 * (threadIdx.x + u * kThreads), fresh, x[u]);
+            if (!have_s) { s = publish_scalars1(a, sh); have_s = true; }
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) finish(e0 + 4 * (i + u * kThreads), x[u]);
-        }
-        for (; i < ngroups; i += kThreads) {
-            Group1 x0;
-            load(e0 + 4 * i, x0);
-            finish(e0 + 4 * i, x0);
-        }
-        const int64_t tail = len & 3;
-        if ((int64_t)threadIdx.x < tail) {
-            const int64_t e = e0 + 4 * ngroups + threadIdx.x;
-            float p = gld<float>(T.p + e);
-            const float g = load_grad1<GD>(T.g, e);
-            const float st = fresh ? 0.0f : load_state1<SF>(T.s1, e);
-            const float p_old = p;
-            float sn = one_state<OPT>(a, s, g, p, st);
-            if (a.skip_zeros && g == 0.0f) {
-                p = p_old;
-                sn = st;
+            for (int u = 0; u < kEwGroups; ++u) s1_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (threadIdx.x + u * kThreads), x[u]);
+        } else {   // a tensor's last, short tile
+            if (!have_s) { s = publish_scalars1(a, sh); have_s = true; }
+            const int64_t ngroups = len >> 2;
+            for (int64_t i = threadIdx.x; i < ngroups; i += kThreads) {
+                Group1 x0;
+                s1_load<OPT, GD, SF>(T, e0 + 4 * i, fresh, x0);
+                s1_finish<OPT, GD, SF>(a, s, T, e0 + 4 * i, x0);
             }
-            uint32_t r = 0;
-            if (SF == kBF16SR)
-                r = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3)) & 0xFFFFu;
-            gst<float>(T.p + e, p);
-            store_state1<SF>(T.s1, e, sn, r);
+            const int64_t tail = len & 3;
+            if ((int64_t)threadIdx.x < tail) s1_single<OPT, GD, SF>(a, s, T, e0 + 4 * ngroups + threadIdx.x, fresh);
         }
     }
 }
@@ -148,11 +170,10 @@ __global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__re
 template <int OPT, int GD>
 static hipError_t launch_1s_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
 {
-    const int64_t nc = a.nchunks;
     switch (fmt) {
-    case kF32: return launch_persistent(step_1s_kernel<OPT, GD, kF32>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16RN: return launch_persistent(step_1s_kernel<OPT, GD, kBF16RN>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16SR: return launch_persistent(step_1s_kernel<OPT, GD, kBF16SR>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kF32: return launch_tiles(step_1s_kernel<OPT, GD, kF32>, kEwTile1, 0, lg, a, st);
+    case kBF16RN: return launch_tiles(step_1s_kernel<OPT, GD, kBF16RN>, kEwTile1, 0, lg, a, st);
+    case kBF16SR: return launch_tiles(step_1s_kernel<OPT, GD, kBF16SR>, kEwTile1, 0, lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -2,12 +2,13 @@
 // with fp32 or BF16 states (AdamW, AdEMAMix), for fp32, BF16 or FP16
 // parameters and gradients.
 //
-// A persistent grid of 256-thread workgroups walks the bucket's chunk table
-// with a grid stride; inside a chunk every lane owns groups of 4 consecutive
-// elements, so fp32 arrays move as 128-bit accesses and 16-bit ones as 64-bit
-// accesses, every access instruction of a wave64 fully coalesced.  kEwGroups
-// groups are loaded before any arithmetic.  HBM-bound: every byte is read or
-// written once per step and no intermediate leaves registers.
+// One 256-thread workgroup per tile of kEwTile consecutive elements of one
+// tensor (the tile scheduling of opt_elem.h).  Inside a tile every lane owns
+// kEwGroups groups of 4 consecutive elements, so fp32 arrays move as 128-bit
+// accesses and 16-bit ones as 64-bit accesses, every access instruction of a
+// wave64 fully coalesced; a full tile issues all its loads before the
+// per-call scalars are formed and before any arithmetic.  HBM-bound: every
+// byte is read or written once per step and no intermediate leaves registers.
 #include "opt_elem.h"
 
 namespace optstep {
@@ -112,48 +113,52 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
 #define OPT_EW_ATTR
 #endif
 
+constexpr int64_t kEwTile = (int64_t)kThreads * kEwGroups * 4;
+
 template <int OPT, int GD, int SF, int PD>
 __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
                                                                        const int32_t *__restrict__ ctab, StepArgs a)
 {
     __shared__ Scalars sh;
-    if (threadIdx.x == 0) sh = make_scalars(a);
-    __syncthreads();
-    const Scalars s = sh;
+    Scalars s;
+    bool have_s = false;
     const bool fresh = a.fresh != 0;
-    for (int64_t c = first_chunk(); c < a.nchunks; c += gridDim.x) {
-        const DevTensor T = tens[ctab[c]];
-        const int64_t e0 = (c - T.chunk_begin) * a.chunk;
-        const int64_t len = min(a.chunk, T.numel - e0);
-        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
-        const int64_t ngroups = len >> 2;
-        int64_t i = threadIdx.x;
-        // kEwGroups groups per iteration: all their loads are issued before any math
-        for (; i + (kEwGroups - 1) * kThreads < ngroups; i += kEwGroups * kThreads) {
+    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
+        DevTensor T;
+        int64_t e0, len;
+        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
+        if (len == kEwTile) {
             Group x[kEwGroups];
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (i + u * kThreads), fresh, x[u]);
+            for (int u = 0; u < kEwGroups; ++u)
+                ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (threadIdx.x + u * kThreads), fresh, x[u]);
+            if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
+            const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u) ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (i + u * kThreads), lam, x[u]);
+            for (int u = 0; u < kEwGroups; ++u)
+                ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (threadIdx.x + u * kThreads), lam, x[u]);
+        } else {   // a tensor's last, short tile
+            if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
+            const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
+            const int64_t ngroups = len >> 2;
+            for (int64_t i = threadIdx.x; i < ngroups; i += kThreads) {
+                Group x0;
+                ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
+                ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
+            }
+            const int64_t tail = len & 3;
+            if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
         }
-        for (; i < ngroups; i += kThreads) {
-            Group x0;
-            ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
-            ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
-        }
-        const int64_t tail = len & 3;
-        if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
     }
 }
 
 template <int OPT, int GD, int PD>
 static hipError_t launch_ew_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
 {
-    const int64_t nc = a.nchunks;
     switch (fmt) {
-    case kF32: return launch_persistent(step_ew_kernel<OPT, GD, kF32, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16RN: return launch_persistent(step_ew_kernel<OPT, GD, kBF16RN, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
-    case kBF16SR: return launch_persistent(step_ew_kernel<OPT, GD, kBF16SR, PD>, 0, lg, nc, st, a.tens, a.chunk_tensor, a);
+    case kF32: return launch_tiles(step_ew_kernel<OPT, GD, kF32, PD>, kEwTile, 0, lg, a, st);
+    case kBF16RN: return launch_tiles(step_ew_kernel<OPT, GD, kBF16RN, PD>, kEwTile, 0, lg, a, st);
+    case kBF16SR: return launch_tiles(step_ew_kernel<OPT, GD, kBF16SR, PD>, kEwTile, 0, lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -58,8 +58,8 @@ struct QTabs {
     QTabParams s, u;
 };
 
-// Launch geometry: compute units, and persistent workgroups per compute unit
-// (0: as many as the kernel's occupancy allows).
+// Launch geometry: compute units, and workgroups per compute unit (0: one
+// workgroup per tile; k > 0: a persistent grid of k per compute unit).
 struct LaunchGeom {
     int ncu;
     int wgs_per_cu;
@@ -83,6 +83,11 @@ struct StepArgs {
     int32_t p_dtype;               // ParamT of the bucket's parameters
     int32_t p_sr;                  // 1: 16-bit parameters are stored with stochastic rounding
     int32_t skip_zeros;            // 1: elements whose gradient is exactly 0 keep p and their states
+    // tile space of the launch (set by the launcher from the kernel's tile):
+    // chunk c holds tiles [c << tile_sh, (c + 1) << tile_sh) of tile elements each
+    int64_t tile;
+    int64_t ntiles;
+    int32_t tile_sh;
 };
 
 }  // namespace optstep
