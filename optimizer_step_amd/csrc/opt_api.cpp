@@ -363,6 +363,11 @@ int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
 struct Bucket {
     std::vector<DevTensor> tens;
     std::vector<int32_t> chunk_tensor;
+    int64_t ngroups = 0;   // norm-sum groups of kRGroup partials, over the bucket's tensors
+
+    // doubles of workspace the norm passes use: a pair per partial, then a pair per group
+    size_t partial_doubles(int64_t chunk) const { return chunk_tensor.size() * (size_t)(chunk / kUTile) * 2; }
+    size_t norm_doubles(int64_t chunk) const { return partial_doubles(chunk) + 2 * (size_t)ngroups; }
 };
 
 // The tensors whose (gradient, parameter) storage is (gd, pd); opt_dtype,
@@ -384,6 +389,8 @@ void plan_bucket(const opt_tensor *t, int64_t n, int gd, int pd, int64_t chunk, 
         d.numel = x.numel;
         d.chunk_begin = next;
         d.k = (int32_t)k;
+        d.rg_begin = b.ngroups;
+        b.ngroups += norm_groups(x.numel);
         const int64_t nc = (x.numel + chunk - 1) / chunk;
         const int32_t idx = (int32_t)b.tens.size();
         b.tens.push_back(d);
@@ -469,7 +476,7 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
 
     if (pre) {
         size_t need = 0;
-        for (auto &bk : b) need = std::max(need, bk.chunk_tensor.size() * (size_t)(chunk / kUTile) * 2);
+        for (auto &bk : b) need = std::max(need, bk.norm_doubles(chunk));
         if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
     }
 
@@ -499,6 +506,8 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
         hipError_t e;
         if (pre) {
             a.partials = w->partials;
+            a.groups = w->partials + bk.partial_doubles(chunk);
+            a.ngroups = bk.ngroups;
             e = launch_unorm(opt, gd, fmt, a, geom(*w), q8 ? 2048 : 0, (int)bk.tens.size(), unorm_out, st);
             if (e == hipSuccess) {
                 w->partials_used = true;
@@ -597,7 +606,7 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     Bucket b[3];
     for (int gd = 0; gd < 3; ++gd) plan_bucket(t.data(), n, gd, kP32, chunk, b[gd]);
     size_t need = 0;
-    for (auto &bk : b) need = std::max(need, bk.chunk_tensor.size() * (size_t)(chunk / kUTile) * 2);
+    for (auto &bk : b) need = std::max(need, bk.norm_doubles(chunk));
     if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
     hipError_t e;
     for (int gd = 0; gd < 3; ++gd) {
@@ -614,6 +623,8 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
         a.nchunks = (int64_t)bk.chunk_tensor.size();
         a.chunk = chunk;
         a.partials = w->partials;
+        a.groups = w->partials + bk.partial_doubles(chunk);
+        a.ngroups = bk.ngroups;
         e = launch_gnorm(gd, a, geom(*w), (int)bk.tens.size(), out, st);
         if (e != hipSuccess) return hip_fail(e, "gradient norm launch");
         if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;

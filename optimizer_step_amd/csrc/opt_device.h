@@ -14,6 +14,7 @@ namespace optstep {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // Accesses through the global address space, so the compiler emits global_*
 // (not flat_*) instructions for pointers it reads out of the tensor table.

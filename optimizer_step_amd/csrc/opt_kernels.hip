@@ -523,17 +523,15 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
 }
 
 __global__ __launch_bounds__(kThreads) void unorm_reduce_kernel(const DevTensor *__restrict__ tens,
-                                                              int64_t chunk, const double *partials,
-                                                              double *out)
+                                                              const double *groups, double *out)
 {
     __shared__ double red[kWaves][2];
     const DevTensor T = tens[blockIdx.x];
-    const int64_t first = T.chunk_begin * (chunk / kUTile);
-    const int64_t nt = (T.numel + kUTile - 1) / kUTile;
+    const int64_t ng = norm_groups(T.numel);
     double su = 0.0, sp = 0.0;
-    for (int64_t i = threadIdx.x; i < nt; i += kThreads) {
-        su += gld<double>(partials + 2 * (first + i));
-        sp += gld<double>(partials + 2 * (first + i) + 1);
+    for (int64_t i = threadIdx.x; i < ng; i += kThreads) {
+        su += gld<double>(groups + 2 * (T.rg_begin + i));
+        sp += gld<double>(groups + 2 * (T.rg_begin + i) + 1);
     }
     su = wave_sum(su);
     sp = wave_sum(sp);
@@ -556,18 +554,63 @@ __global__ __launch_bounds__(kThreads) void unorm_reduce_kernel(const DevTensor 
 // update-norm partials buffer; slot 2t+1 carries the max as a double.
 
 // One full tile's contribution from this lane: its 16 elements in order.
-__device__ __forceinline__ void gnorm_acc(const float g[4][4], double &sq, uint32_t &mx)
+// The 16 gradients one lane holds of a full 1024-element partial unit, as
+// raw 16-byte loads: elements q*256 + 4*lane + j (fp32, q < 4) or q*512 +
+// 8*lane + j (16-bit, q < 2), summed by the lane in that order.
+template <int GD>
+struct GnRaw {
+    u4 w[GD == kGradF32 ? 4 : 2];
+};
+
+template <int GD>
+__device__ __forceinline__ void gnorm_load_unit(const void *g, int64_t e, int lane, GnRaw<GD> &r)
 {
+    if (GD == kGradF32) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q) r.w[q] = sld<u4>((const float *)g + e + q * 256 + lane * 4);
+    } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double x = (double)g[q][j];
-            sq += x * x;
-            mx = max(mx, fbits(g[q][j]) & 0x7FFFFFFFu);
-        }
+        for (int q = 0; q < 2; ++q) r.w[q] = sld<u4>((const uint16_t *)g + e + q * 512 + lane * 8);
+    }
 }
 
+typedef uint16_t h2 __attribute__((ext_vector_type(2)));
+
+// sq += x*x in binary64 for the unit's 16 values and mx = max |x| as an fp32
+// bit pattern.  x*x is exact in binary64 for any fp32 or 16-bit x (at most 48
+// significant bits, no overflow or underflow), so the fused multiply-add
+// rounds exactly as the separate product and sum.  16-bit magnitudes are
+// compared as packed 16-bit integers (their bit order is their numeric order,
+// NaN above infinity), then widened exactly.
+template <int GD>
+__device__ __forceinline__ void gnorm_acc(const GnRaw<GD> &r, double &sq, uint32_t &mx)
+{
+    if (GD == kGradF32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double x = (double)bitsf(r.w[q][j]);
+                sq = __builtin_fma(x, x, sq);
+                mx = max(mx, r.w[q][j] & 0x7FFFFFFFu);
+            }
+    } else {
+        h2 m = {0, 0};
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t wd = r.w[q][j];
+                const double lo = (double)(GD == kGradBF16 ? bf16_lo(wd) : f16_lo(wd));
+                const double hi = (double)(GD == kGradBF16 ? bf16_hi(wd) : f16_hi(wd));
+                sq = __builtin_fma(lo, lo, sq);
+                sq = __builtin_fma(hi, hi, sq);
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(h2, wd & 0x7FFF7FFFu));
+            }
+        const uint32_t h = max((uint32_t)m.x, (uint32_t)m.y);
+        mx = max(mx, GD == kGradBF16 ? h << 16 : fbits(f16_lo(h)));
+    }
+}
 __device__ __forceinline__ void gnorm_store(const StepArgs &a, int64_t slot, int lane, double sq, uint32_t mx)
 {
     sq = wave_sum(sq);
@@ -579,11 +622,12 @@ __device__ __forceinline__ void gnorm_store(const StepArgs &a, int64_t slot, int
 }
 
 #ifndef OPT_GN_UNITS
-#define OPT_GN_UNITS 2
+#define OPT_GN_UNITS 4
 #endif
-// One workgroup per tile of kGnTile gradient elements: OPT_GN_UNITS partials
+// One workgroup per tile of kGnTile gradient elements: kGnUnits partial units
 // of 1024 elements per wave.
-constexpr int64_t kGnTile = (int64_t)kWaves * OPT_GN_UNITS * kUTile;
+constexpr int kGnUnits = OPT_GN_UNITS;
+constexpr int64_t kGnTile = (int64_t)kWaves * kGnUnits * kUTile;
 
 template <int GD>
 __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTensor *__restrict__ tens,
@@ -597,33 +641,30 @@ __global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTenso
         int64_t e0, len;
         if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
         const int64_t slot0 = w * a.tile / kUTile;   // the tile's first partial in the chunk space
+        if (len == kGnTile) {
+            // a full tile: every load of the wave's kGnUnits units before the sums
+            GnRaw<GD> g[kGnUnits];
+#pragma unroll
+            for (int u = 0; u < kGnUnits; ++u) gnorm_load_unit<GD>(T.g, e0 + (wave + u * kWaves) * kUTile, lane, g[u]);
+#pragma unroll
+            for (int u = 0; u < kGnUnits; ++u) {
+                double sq = 0.0;
+                uint32_t mx = 0;
+                gnorm_acc<GD>(g[u], sq, mx);
+                gnorm_store(a, slot0 + wave + u * kWaves, lane, sq, mx);
+            }
+            continue;
+        }
         const int64_t ntile = (len + kUTile - 1) / kUTile;
         const int64_t nfull = len / kUTile;
-        int64_t tt = wave;
-        // two full tiles per wave at a time: all 8 loads before the sums
-        for (; tt + kWaves < nfull; tt += 2 * kWaves) {
-            float g0[4][4], g1[4][4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                load_grad4<GD>(T.g, e0 + tt * kUTile + q * 256 + lane * 4, g0[q]);
-                load_grad4<GD>(T.g, e0 + (tt + kWaves) * kUTile + q * 256 + lane * 4, g1[q]);
-            }
-            double sq0 = 0.0, sq1 = 0.0;
-            uint32_t mx0 = 0, mx1 = 0;
-            gnorm_acc(g0, sq0, mx0);
-            gnorm_acc(g1, sq1, mx1);
-            gnorm_store(a, slot0 + tt, lane, sq0, mx0);
-            gnorm_store(a, slot0 + tt + kWaves, lane, sq1, mx1);
-        }
-        for (; tt < ntile; tt += kWaves) {
+        for (int64_t tt = wave; tt < ntile; tt += kWaves) {
             double sq = 0.0;
             uint32_t mx = 0;
             if (tt < nfull) {
-                float g[4][4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) load_grad4<GD>(T.g, e0 + tt * kUTile + q * 256 + lane * 4, g[q]);
-                gnorm_acc(g, sq, mx);
-            } else {
+                GnRaw<GD> g;
+                gnorm_load_unit<GD>(T.g, e0 + tt * kUTile, lane, g);
+                gnorm_acc<GD>(g, sq, mx);
+            } else {   // the tensor's short last unit: elements q*256 + 4*lane + j, one at a time
                 for (int q = 0; q < kUTile / 256; ++q) {
                     const int64_t i0 = tt * kUTile + q * 256 + lane * 4;
                     const int n = (int)max((int64_t)0, min((int64_t)4, len - i0));
@@ -653,17 +694,68 @@ __device__ __forceinline__ double wave_nanmax(double x)
     return x;
 }
 
-__global__ __launch_bounds__(kThreads) void gnorm_reduce_kernel(const DevTensor *__restrict__ tens, int64_t chunk,
-                                                              const double *partials, double *out)
+// ---------------------------------------------------------------------------
+// Per-tensor sums of the norm partials, in two fixed-order levels so that no
+// tensor's sum rests on one workgroup: group j of a tensor holds its partials
+// [j*kRGroup, (j+1)*kRGroup) counted from its first; one workgroup sums a
+// group (each lane four consecutive partials in order, then the wave
+// butterfly, then the waves in order), and one workgroup per tensor then sums
+// its groups (strided lanes, butterfly, waves in order).  Which partials meet
+// in which order depends on the tensor's length alone.
+
+// MAX: the second value of a pair is combined by a NaN-poisoning max (the
+// gradient norm's max |g|), else summed (the update norm's sum of p^2).
+template <bool MAX>
+__global__ __launch_bounds__(kThreads) void norm_group_kernel(const DevTensor *__restrict__ tens, int ntens,
+                                                            int64_t chunk, int64_t ngroups,
+                                                            const double *partials, double *groups)
+{
+    static_assert(kRGroup == 4 * kThreads, "four partials per lane");
+    __shared__ double red[kWaves][2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t gid = blockIdx.x; gid < ngroups; gid += gridDim.x) {
+        // the tensor holding group gid: the last whose first group is <= gid
+        int lo = 0, hi = ntens - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tens[mid].rg_begin <= gid) lo = mid;
+            else hi = mid - 1;
+        }
+        const DevTensor T = tens[lo];
+        const int64_t first = T.chunk_begin * (chunk / kUTile);
+        const int64_t nt = (T.numel + kUTile - 1) / kUTile;
+        const int64_t i0 = (gid - T.rg_begin) * kRGroup + 4 * threadIdx.x;
+        const int64_t i1 = min(nt, i0 + 4);
+        double a = 0.0, b = 0.0;
+        for (int64_t i = i0; i < i1; ++i) {
+            a += gld<double>(partials + 2 * (first + i));
+            const double y = gld<double>(partials + 2 * (first + i) + 1);
+            b = MAX ? nanmax(b, y) : b + y;
+        }
+        a = wave_sum(a);
+        b = MAX ? wave_nanmax(b) : wave_sum(b);
+        if (lane == 0) { red[wave][0] = a; red[wave][1] = b; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double A = red[0][0], B = red[0][1];
+            for (int w = 1; w < kWaves; ++w) { A += red[w][0]; B = MAX ? nanmax(B, red[w][1]) : B + red[w][1]; }
+            gst<double>(groups + 2 * gid, A);
+            gst<double>(groups + 2 * gid + 1, B);
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void gnorm_reduce_kernel(const DevTensor *__restrict__ tens,
+                                                              const double *groups, double *out)
 {
     __shared__ double red[kWaves][2];
     const DevTensor T = tens[blockIdx.x];
-    const int64_t first = T.chunk_begin * (chunk / kUTile);
-    const int64_t nt = (T.numel + kUTile - 1) / kUTile;
+    const int64_t ng = norm_groups(T.numel);
     double sq = 0.0, mx = 0.0;
-    for (int64_t i = threadIdx.x; i < nt; i += kThreads) {
-        sq += gld<double>(partials + 2 * (first + i));
-        mx = nanmax(mx, gld<double>(partials + 2 * (first + i) + 1));
+    for (int64_t i = threadIdx.x; i < ng; i += kThreads) {
+        sq += gld<double>(groups + 2 * (T.rg_begin + i));
+        mx = nanmax(mx, gld<double>(groups + 2 * (T.rg_begin + i) + 1));
     }
     sq = wave_sum(sq);
     mx = wave_nanmax(mx);
@@ -991,8 +1083,12 @@ hipError_t launch_unorm(int opt, int gd, int fmt, const StepArgs &a, const Launc
                                    : launch_unorm_t<kAdEMAMix, kGradF16>(fmt, a, lg, lds, st);
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(unorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
-                       (const double *)a.partials, out);
+    if (a.ngroups > 0) {
+        hipLaunchKernelGGL(norm_group_kernel<false>, dim3((unsigned)min(a.ngroups, kMaxGrid)), dim3(kThreads), 0, st,
+                           a.tens, ntens, a.chunk, a.ngroups, (const double *)a.partials, a.groups);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(unorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, (const double *)a.groups, out);
     return hipGetLastError();
 }
 
@@ -1004,8 +1100,12 @@ hipError_t launch_gnorm(int gd, const StepArgs &a, const LaunchGeom &lg, int nte
             : gd == kGradBF16 ? launch_tiles(gnorm_partials_kernel<kGradBF16>, kGnTile, 0, lg, a, st)
                               : launch_tiles(gnorm_partials_kernel<kGradF16>, kGnTile, 0, lg, a, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gnorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, a.chunk,
-                       (const double *)a.partials, out);
+    if (a.ngroups > 0) {
+        hipLaunchKernelGGL(norm_group_kernel<true>, dim3((unsigned)min(a.ngroups, kMaxGrid)), dim3(kThreads), 0, st,
+                           a.tens, ntens, a.chunk, a.ngroups, (const double *)a.partials, a.groups);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(gnorm_reduce_kernel, dim3(ntens), dim3(kThreads), 0, st, a.tens, (const double *)a.groups, out);
     return hipGetLastError();
 }
 

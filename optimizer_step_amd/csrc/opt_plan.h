@@ -9,7 +9,8 @@ namespace optstep {
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kQBlock = 256;       // elements per 8-bit absmax block
-constexpr int kUTile = 1024;       // elements per update-norm partial
+constexpr int kUTile = 1024;       // elements per norm partial (update norm, gradient norm)
+constexpr int kRGroup = 1024;      // partials per first-level group of the per-tensor norm sums
 
 enum Opt : int { kAdamW = 0, kAdEMAMix = 1, kMomentum = 2, kRMSprop = 3, kAdagrad = 4, kLion = 5 };
 enum Fmt : int { kF32 = 0, kBF16RN = 1, kBF16SR = 2, kQ8 = 3, kFP8RN = 4, kFP8SR = 5, kFP4RN = 6, kFP4SR = 7 };
@@ -31,9 +32,14 @@ struct alignas(16) DevTensor {
     int64_t numel;
     int64_t chunk_begin;   // first chunk of this tensor in the bucket's chunk space
     int32_t k;             // position in the caller's list
-    int32_t pad_[3];
+    int32_t pad_;
+    int64_t rg_begin;      // first norm-sum group of this tensor in the bucket (groups of kRGroup partials)
 };
 static_assert(sizeof(DevTensor) == 96, "DevTensor layout");
+
+// Norm-sum groups of a tensor of numel elements: kRGroup partials of kUTile
+// elements each, the last group possibly short.
+constexpr int64_t norm_groups(int64_t numel) { return ((numel + kUTile - 1) / kUTile + kRGroup - 1) / kRGroup; }
 
 // 8-bit codebook lookup-table parameters (see opt_qtable in opt_api.cpp).
 // For |x| <= 1 the magnitude bits a = bits(max(|x|, lo_f)) give the bucket
@@ -72,7 +78,9 @@ struct StepArgs {
     int64_t nchunks;
     int64_t chunk;                 // elements per chunk (multiple of 1024)
     const double *unorm;           // caller's {sum u^2, sum p^2} per tensor k, or null
-    double *partials;              // pre-pass: {sum u^2, sum p^2} per kUTile elements
+    double *partials;              // norm passes: {sum u^2, sum p^2} or {sum g^2, max |g|} per kUTile elements
+    double *groups;                // norm passes: the same pairs summed over groups of kRGroup partials
+    int64_t ngroups;               // groups in the bucket
     QTabs q;
     float lr, beta1, beta2, beta3, alpha, eps, wd, max_unorm;
     int64_t step;                  // t: keys the stochastic-rounding stream

@@ -143,6 +143,57 @@ def test_deterministic_across_launch_geometry():
     osa.opt_debug_set_launch(32768, 0)
 
 
+BIG = [3 * 2**20 + 7, 0, 5, 2**20, 2 * 2**20 + 1024, 2**20 + 1]
+
+
+def _big_list(gdt, grid=False):
+    out = []
+    for k, n in enumerate(BIG):
+        if grid:
+            out.append(synth.grid_grads(n, 1, k, bf16=(gdt == "bf16")))
+        else:
+            g = synth.grads(n, 1, k, std=1e-2)
+            out.append(synth.bf16_words(g) if gdt == "bf16" else g.astype(np.float16) if gdt == "f16" else g)
+    return out
+
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16", "f16"])
+def test_tensors_spanning_several_sum_groups(gdt):
+    """Tensors of more than 1024 partials (2^20 elements) are summed over
+    several first-level groups, one workgroup each, then in order: sums
+    within the summation bound, maxima exact, and no dependence on the launch
+    geometry."""
+    import optimizer_step_amd as osa
+    grads = _big_list(gdt)
+    out, _ = _gpu_norms(grads, with_coef=False)
+    host = [g.astype(np.float32) if g.dtype == np.float16 else g for g in grads]
+    (s2, mx), per = oracle.grad_norm_list(host)
+    for k, (ps, pm) in enumerate(per):
+        _assert_sum(out[2 + 2 * k], ps, BIG[k])
+        assert out[3 + 2 * k] == pm, (k, out[3 + 2 * k], pm)
+    _assert_sum(out[0], s2, sum(BIG))
+    assert out[1] == mx
+    try:
+        for chunk, wgs in [(1024, 0), (65536, 3)]:
+            osa.opt_debug_set_launch(chunk, wgs)
+            again, _ = _gpu_norms(grads, with_coef=False)
+            assert np.array_equal(again.view(np.uint64), out.view(np.uint64)), (chunk, wgs)
+    finally:
+        osa.opt_debug_set_launch(32768, 0)
+
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+def test_several_sum_groups_grid_values_bit_exact(gdt):
+    grads = _big_list(gdt, grid=True)
+    out, coef = _gpu_norms(grads, 0.5, 2)
+    (s2, mx), per = oracle.grad_norm_list(grads)
+    for k, (ps, pm) in enumerate(per):
+        assert out[2 + 2 * k] == ps and out[3 + 2 * k] == pm, k
+    assert out[0] == s2 and out[1] == mx
+    want = oracle.clip_coef(np.sqrt(s2), 0.5)
+    assert np.float32(coef).view(np.uint32) == np.float32(want).view(np.uint32), (coef, want)
+
+
 CLIP_FORMATS = [("adamw", "f32"), ("adamw", "bf16_rn"), ("adamw", "bf16_sr"), ("adamw", "q8"),
                 ("ademamix", "f32"), ("ademamix", "bf16_sr"), ("ademamix", "q8")]
 

@@ -150,6 +150,24 @@ def test_update_norm_prepass(opt, fmt):
     assert s < 0.1
 
 
+@pytest.mark.parametrize("fmt", ["f32", "bf16_sr", "fp8_rn"])
+def test_update_norm_spans_sum_groups(fmt):
+    """Tensors of more than 1024 partials (2^20 elements) have their norms
+    summed over several first-level groups, one workgroup each, then in
+    order; an empty and a small tensor sit between them in the list."""
+    hp = dict(_hp("adamw"), max_unorm=1.0, lr=1e-3)
+    sizes = [2 * 2**20 + 3001, 0, 1000, 2**20, 3 * 2**20]
+    case = Case("adamw", fmt, sizes, [False, False, True, True, False], 2, hp)
+    ps, st, norms_o = case.run_oracle()
+    dev, norms_g = case.run_gpu()
+    compare(case, dev, ps, st)
+    for (t, k, u2, p2) in norms_o:
+        g = norms_g[t - 1]
+        tol_p = 1e-12 if (t == 1 or fmt == "f32") else 1e-7
+        assert abs(g[2 * k] - u2) <= 1e-12 * abs(u2), (t, k, g[2 * k], u2)
+        assert abs(g[2 * k + 1] - p2) <= tol_p * abs(p2), (t, k, g[2 * k + 1], p2)
+
+
 def test_update_norm_is_deterministic():
     """Ten pre-pass runs over a multi-chunk tensor give identical bits."""
     import torch
