@@ -422,9 +422,10 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
 // update, never a stored moment, code or rounding bit) formed with the
 // hardware reciprocal and square root (each within 1 ulp) instead of
 // correctly rounded division and square root: u is within a few ulp of the
-// exact recipe, far inside the parameter tolerance.  v_hat below 2^-96 (where
-// the hardware square root loses accuracy) or NaN falls back to the exact
-// recipe for the whole wave.
+// exact recipe, far inside the parameter tolerance.  Callers fall back to the
+// exact recipe for the whole wave where some v_hat is below 2^-96 (where the
+// hardware square root loses accuracy); NaN and infinite moments give the
+// same u either way.
 template <int OPT>
 __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a, float g, float m,
                                             float v, float m2)

@@ -194,12 +194,12 @@ __device__ __forceinline__ Scalars publish_scalars(const StepArgs &a, Scalars &s
     return sh;
 }
 
-// One launch of a tile kernel taking (tens, ctab, a).
-template <class K>
+// One launch of a tile kernel taking (tens, ctab, a), THREADS per workgroup.
+template <int THREADS = kThreads, class K>
 static hipError_t launch_tiles(K kernel, int64_t ktile, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
 {
     set_tiles(a, ktile);
-    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kThreads), lds, st, a.tens, a.chunk_tensor, a);
+    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(THREADS), lds, st, a.tens, a.chunk_tensor, a);
     return hipGetLastError();
 }
 

@@ -7,7 +7,10 @@
 // kEwGroups groups of 4 consecutive elements, so fp32 arrays move as 128-bit
 // accesses and 16-bit ones as 64-bit accesses, every access instruction of a
 // wave64 fully coalesced; a full tile issues all its loads before the
-// per-call scalars are formed and before any arithmetic.  HBM-bound: every
+// per-call scalars are formed and before any arithmetic.  The moments are
+// formed exactly (fixed binary32 order); the direction u, which only feeds
+// p, uses the hardware reciprocal and square root (measured on MI355X: +2 %
+// on the 290-tensor AdamW step, +5-6 % with BF16 states).  HBM-bound: every
 // byte is read or written once per step and no intermediate leaves registers.
 #include "opt_elem.h"
 
@@ -39,9 +42,23 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
                                           int64_t e, float lam, Group &x)
 {
     float mo[4], vo[4], m2o[4];
+    // the direction with the hardware reciprocal and square root; the exact
+    // recipe for the whole wave where some v_hat is below 2^-96 (a NaN or
+    // infinite moment gives the same u either way)
+    Mom rr[4];
+    float vmin = INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        Mom r = moments<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
+        rr[i] = moments_fast<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
+        vmin = fminf(vmin, rr[i].v * s.rc2);
+    }
+    if (__any(!(vmin >= 0x1p-96f))) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rr[i] = moments<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const Mom &r = rr[i];
         const float pn = apply_update(x.p[i], s.d, lam, r.u);
         mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
         if (a.skip_zeros && x.g[i] == 0.0f) {   // p (decay included) and the states as they were
@@ -113,10 +130,14 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
 #define OPT_EW_ATTR
 #endif
 
-constexpr int64_t kEwTile = (int64_t)kThreads * kEwGroups * 4;
+#ifndef OPT_EW_THREADS
+#define OPT_EW_THREADS 256
+#endif
+constexpr int kEwThreads = OPT_EW_THREADS;
+constexpr int64_t kEwTile = (int64_t)kEwThreads * kEwGroups * 4;
 
 template <int OPT, int GD, int SF, int PD>
-__global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
+__global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
                                                                        const int32_t *__restrict__ ctab, StepArgs a)
 {
     __shared__ Scalars sh;
@@ -131,17 +152,17 @@ __global__ __launch_bounds__(kThreads) OPT_EW_ATTR void step_ew_kernel(const Dev
             Group x[kEwGroups];
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
-                ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (threadIdx.x + u * kThreads), fresh, x[u]);
+                ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (threadIdx.x + u * kEwThreads), fresh, x[u]);
             if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
-                ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (threadIdx.x + u * kThreads), lam, x[u]);
+                ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (threadIdx.x + u * kEwThreads), lam, x[u]);
         } else {   // a tensor's last, short tile
             if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
             const int64_t ngroups = len >> 2;
-            for (int64_t i = threadIdx.x; i < ngroups; i += kThreads) {
+            for (int64_t i = threadIdx.x; i < ngroups; i += kEwThreads) {
                 Group x0;
                 ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
                 ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
@@ -156,9 +177,9 @@ template <int OPT, int GD, int PD>
 static hipError_t launch_ew_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
 {
     switch (fmt) {
-    case kF32: return launch_tiles(step_ew_kernel<OPT, GD, kF32, PD>, kEwTile, 0, lg, a, st);
-    case kBF16RN: return launch_tiles(step_ew_kernel<OPT, GD, kBF16RN, PD>, kEwTile, 0, lg, a, st);
-    case kBF16SR: return launch_tiles(step_ew_kernel<OPT, GD, kBF16SR, PD>, kEwTile, 0, lg, a, st);
+    case kF32: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD>, kEwTile, 0, lg, a, st);
+    case kBF16RN: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD>, kEwTile, 0, lg, a, st);
+    case kBF16SR: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD>, kEwTile, 0, lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }

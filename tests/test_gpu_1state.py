@@ -136,4 +136,7 @@ def test_two_state_skip_zeros_prepass():
     compare(case, dev, ps, st)
     for (t, k, u2, p2) in no:
         g = ng[t - 1]
-        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= 1e-12 * p2, (t, k)
+        # after step 1, p already differs within its bar (the direction is
+        # formed with hardware rcp/sqrt): sum p^2 within ~1e-7 relative
+        tol_p = 1e-12 if t == 1 else 1e-7
+        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= tol_p * p2, (t, k)

@@ -190,7 +190,12 @@ def test_p16_with_update_norm():
     _check(ps, st, dev, "f32", "adamw", oracle.P_BF16, 3)
     for (t, k, u2, p2) in no:
         g = ng[t - 1]
-        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= 1e-12 * p2, (t, k)
+        # after step 1 a few 16-bit p words may sit one 16-bit step from the
+        # oracle's (the direction's few-ulp difference moves a rounding): at
+        # most 0.1 % of words, each moving its p^2 by <= 2*2^-8 relative, so
+        # sum p^2 moves by < 1e-5 relative
+        tol_p = 1e-12 if t == 1 else 1e-5
+        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= tol_p * p2, (t, k)
 
 
 def test_blockwise_formats_refuse_p16():
