@@ -60,11 +60,11 @@ def carve(torch, arrays, device):
     (p, g, states, absmax), each starting on a 256-byte boundary; returns
     views.  Flat buffers like this are how training frameworks hold a bucket
     of parameters and optimizer states.  (Measured on MI355X: the step's
-    bandwidth over the same arrays varies from process to process, 5.1 to
-    6.1 TB/s, with neither the launch shape nor the offsets between the
-    arrays changing it within a process; on one box one allocation ran at
-    6.09-6.16 TB/s in every process where four separate ones ran at
-    5.2-5.6.)"""
+    bandwidth depends on where an allocation lands physically.  Eighteen
+    14 GB arenas allocated in a row in one process ran the same 2^30-element
+    step at 5.4 to 6.5 TB/s, each arena at its own steady rate, and the same
+    virtual addresses in another process at other rates; DRAM-credit stall
+    counters moved with the rate, translation misses did not.)"""
     sizes = {}
     off = 0
     for name, dtype, n in arrays:
