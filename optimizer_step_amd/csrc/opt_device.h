@@ -107,6 +107,16 @@ __host__ __device__ inline uint32_t bf16_sr(float x, uint32_t r16)
 
 struct PhiloxOut { uint32_t w0, w1, w2, w3; };
 
+// a ^ b ^ c; one three-input bitwise instruction on gfx950 (truth table 0x96)
+__host__ __device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+#else
+    return a ^ b ^ c;
+#endif
+}
+
 __host__ __device__ inline PhiloxOut philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                    uint32_t c3, uint32_t k0, uint32_t k1)
 {
@@ -114,8 +124,8 @@ __host__ __device__ inline PhiloxOut philox4x32_10(uint32_t c0, uint32_t c1, uin
     for (int r = 0; r < 10; ++r) {
         uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
     }
@@ -287,12 +297,42 @@ __host__ __device__ inline uint32_t mini_mag(float y, uint32_t r)
     return code < F::kMaxC ? code : F::kMaxC;
 }
 
+// Code of x * 2^nsc.  When nsc < Emin + 126 (the block's absmax is not far
+// below the binary32 normal range; uniform over a block), every x whose
+// binary32 exponent field is 0 lies below the grid's normal range, so the
+// grid binade of y = |x| * 2^nsc is E = max(field - 127 + nsc, Emin) and its
+// step is 2^(E - MB).  Then q = |x| * 2^(nsc + MB - E) in [0, 2^(MB+1)) is
+// exact (a power-of-two scaling; a q below 2^-126 is far below one step and
+// codes as 0 either way), the code below y is ((E - Emin) << MB) + floor(q),
+// and rounding q to an integer (nearest-even, or up iff the top 16 bits of
+// its fraction plus r carry) gives the code; a carry to 2^(MB+1) lands on the
+// next binade's first code.  Other blocks take mini_mag on x * 2^nsc.
 template <class F, bool SR>
 __host__ __device__ inline uint32_t mini_encode(float x, int nsc, uint32_t r)
 {
-    // exact unless x * 2^nsc falls below the binary32 normal range, where it
-    // is far below the grid's smallest step and codes as 0 either way
-    uint32_t c = mini_mag<F, SR>(ldexpf(x, nsc), r);
+    uint32_t c;
+    if (nsc < F::kEmin + 126) {
+        // infinities and NaNs as the largest finite binary32, which codes as
+        // the largest code like any value past the grid's end
+        const uint32_t u = min(fbits(x) & 0x7FFFFFFFu, 0x7F7FFFFFu);
+        const int e = (int)(u >> 23) - 127 + nsc;
+        const int E = e > F::kEmin ? e : F::kEmin;
+        const float q = ldexpf(bitsf(u), nsc + F::kMB - E);
+        uint32_t k;
+        if (SR) {
+            const float fl = floorf(q);
+            const uint32_t l16 = (uint32_t)((q - fl) * 65536.0f);   // exact: floor(frac * 2^16)
+            k = (uint32_t)fl + ((l16 + r) >> 16);
+        } else {
+            k = (uint32_t)rintf(q);                                 // ties to even
+        }
+        c = ((uint32_t)(E - F::kEmin) << F::kMB) + k;
+        c = c < F::kMaxC ? c : F::kMaxC;
+    } else {
+        // exact unless x * 2^nsc falls below the binary32 normal range, where
+        // it is far below the grid's smallest step and codes as 0 either way
+        c = mini_mag<F, SR>(ldexpf(x, nsc), r);
+    }
     if (F::kSign && (fbits(x) >> 31)) c |= F::kSign;
     return c;
 }

@@ -215,6 +215,10 @@ def test_host_mini_codec_matches_oracle(L, elem):
     zero, NaN and infinite absmax included)."""
     rng = np.random.default_rng(90 + elem)
     As = [np.float32(x) for x in (1.0, 1.5, 448.0, 7.0, 3e-3, 2.5e-12, 1e30, 3e-39, 1e-44)]
+    # block scales around the switch between the codec's two paths: the
+    # scaling exponent nsc = emax - floor(log2 A) at Emin + 125, 126 and 127
+    emax, emin = {0: (8, -6), 1: (2, 0), 2: (2, 0)}[elem]
+    As += [np.float32(1.3 * 2.0 ** (emax - (emin + d))) for d in (125, 126, 127)]
     for A in As + [np.float32(0.0), np.float32(np.nan), np.float32(np.inf)]:
         x = _mini_inputs(elem, A, rng) if np.isfinite(A) and A > 0 else np.array([0.0, -0.0, 1.0], np.float32)
         if A == 0:
