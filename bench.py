@@ -245,6 +245,7 @@ def time_workload(name, steps, warmup, torch, osa, synth):
         "achieved_GBps": gbytes / (launch_ms * 1e-3),
         "frac_of_peak": gbytes / (launch_ms * 1e-3) / PEAK_GBPS,
         "launch_ms": launch_ms, "wall_s": wall,
+        "samples_ms": [round(x, 4) for x in per],
     }
     del tensors, tl, keep
     torch.cuda.empty_cache()
@@ -412,7 +413,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rows", default="all", help="'all', 'none', or comma-separated workload names")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--calibrate", action="store_true",
@@ -496,6 +497,7 @@ def main():
         "gbps_achieved": main_row["achieved_GBps"],
         "frac_of_peak": main_row["frac_of_peak"],
         "ms_median": main_row["ms_median"], "ms_p10": main_row["ms_p10"], "ms_p90": main_row["ms_p90"],
+        "samples_ms": main_row["samples_ms"],
         "rows": rows,
     }
     if calib is not None:
