@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_common import Case, compare, to_dev, to_host
+from tests.gpu_common import Case, compare, states_bit_identical, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -133,6 +133,25 @@ def test_update_norm_prepass(fmt):
         tol_p = 1e-12 if t == 1 else 1e-7
         assert abs(g[2 * k] - u2) <= 1e-12 * abs(u2), (t, k)
         assert abs(g[2 * k + 1] - p2) <= tol_p * abs(p2), (t, k)
+
+
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+def test_q8_tiny_moments_in_normal_blocks(opt):
+    """Moments below 2^-100 (gradients of 1e-35 and binary32 subnormals) in
+    blocks whose absmax is normal: the 8-bit quotient of such a moment may miss
+    the correctly rounded one by an ulp, and its code must still be the
+    oracle's (the quotient lies far below every codebook midpoint)."""
+    def g_of(t, k, n):
+        g = synth.grads(n, t, k, std=1e-2)
+        rng = np.random.default_rng([11, t, k])
+        pick = rng.random(n) < 0.05
+        tiny = rng.choice(np.array([1e-35, -1e-35, 3e-38, -2e-40, 1e-44], np.float32), n)
+        return np.where(pick, tiny, g).astype(np.float32)
+    case = Case(opt, "q8", [4096, 1000], False, 3, _hp(opt), grad_override=g_of)
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+    states_bit_identical(case, dev, st)
 
 
 @pytest.mark.parametrize("fmt", FP_FMTS + ["q8"])
