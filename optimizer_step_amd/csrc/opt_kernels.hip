@@ -331,7 +331,7 @@ __device__ __forceinline__ int q8_mine(const DevTensor &T, int64_t eb, int lane)
 #define OPT_Q8_THREADS 512
 #endif
 #ifndef OPT_Q8_BLOCKS
-#define OPT_Q8_BLOCKS 2
+#define OPT_Q8_BLOCKS 1
 #endif
 // Workgroup size of the blockwise kernel (one LDS copy of the 8-bit tables
 // per workgroup) and full blocks in flight per wave.
@@ -350,8 +350,13 @@ static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 // Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
 // tile scheduling of opt_elem.h), one 256-element block per wave at a time,
 // kQ8Blocks blocks in flight per wave.
+// Waves per SIMD the AdamW instantiations are held to (their registers fit
+// 7 without spilling; AdEMAMix's third state does not, and is left free).
+constexpr int kQ8WavesAdamW = 7;
+
 template <int OPT, int GD, int SF>
-__global__ __launch_bounds__(kQ8Threads) void step_q8_kernel(const DevTensor *__restrict__ tens,
+__global__ __launch_bounds__(kQ8Threads)
+__attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
                                                              const int32_t *__restrict__ ctab,
                                                              const uint32_t *__restrict__ qwords,
                                                              StepArgs a)
