@@ -105,7 +105,10 @@ typedef enum {
  *   numel    element count, >= 0 (0 is a no-op).
  * Alignment: p, g, s1, s2, s3 must be 16-byte aligned (any PyTorch allocation
  * is); absmax arrays 4-byte aligned.  Buffers of different tensors must not
- * overlap.  The tensor's position k in the list keys its stochastic rounding.
+ * overlap.  The tensor's position k in the list keys its stochastic rounding
+ * unless sr_tensor_set says otherwise; element j of the record is element
+ * index_base + j of its tensor for that purpose.  A zero-initialised record
+ * (index_base 0, sr_tensor_set 0) is a whole tensor keyed by its position.
  * A fresh 8-bit state is every code set to the code of 0 (127 for a signed
  * table whose entry 127 is 0, 0 for an unsigned table) and absmax 0; a fresh
  * FP8 or FP4 state is all-zero bytes and absmax 0.
@@ -118,6 +121,16 @@ typedef struct {
     int64_t numel;
     int32_t p_dtype;
     int32_t g_dtype;
+    int64_t index_base;     /* index, within the whole tensor, of this record's element 0 (0 for a
+                               whole tensor).  A record that holds a slice of a tensor (one rank's
+                               shard) steps exactly as that part of the whole tensor would: the
+                               stochastic-rounding counter takes index_base + j as the element
+                               index.  >= 0 and a multiple of 4; a multiple of 256 for the 8-bit,
+                               FP8 and FP4 formats, so the slice's blocks are the tensor's.      */
+    int32_t sr_tensor;      /* the tensor number k of the stochastic-rounding counter when
+                               sr_tensor_set is 1 (0 <= sr_tensor < 2^31), so that a slice keeps
+                               its tensor's stream whatever its position in this list           */
+    int32_t sr_tensor_set;  /* 0: k is the record's position in the list; 1: k is sr_tensor     */
 } opt_tensor;
 
 /* ---- hyper-parameters -----------------------------------------------------

@@ -42,6 +42,7 @@ class OptTensor(ctypes.Structure):
         ("s1", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("s3", ctypes.c_void_p),
         ("absmax1", ctypes.c_void_p), ("absmax2", ctypes.c_void_p), ("absmax3", ctypes.c_void_p),
         ("numel", ctypes.c_int64), ("p_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32),
+        ("index_base", ctypes.c_int64), ("sr_tensor", ctypes.c_int32), ("sr_tensor_set", ctypes.c_int32),
     ]
 
 
@@ -134,7 +135,9 @@ def _dtype_code(t):
 
 class TensorList:
     """The C array of opt_tensor for a list of tensor dicts; build it once and
-    pass it to every step when the buffers do not change."""
+    pass it to every step when the buffers do not change.  A dict may carry
+    "index_base" (the slice's first element within its whole tensor) and
+    "sr_tensor" (the tensor number of its stochastic-rounding stream)."""
 
     def __init__(self, tensors):
         self.keep = list(tensors)
@@ -144,7 +147,8 @@ class TensorList:
             self.arr[i] = OptTensor(
                 _ptr(p), _ptr(d["g"]), _ptr(d.get("s1")), _ptr(d.get("s2")), _ptr(d.get("s3")),
                 _ptr(d.get("absmax1")), _ptr(d.get("absmax2")), _ptr(d.get("absmax3")),
-                p.numel(), _dtype_code(p), _dtype_code(d["g"]))
+                p.numel(), _dtype_code(p), _dtype_code(d["g"]), int(d.get("index_base", 0)),
+                int(d.get("sr_tensor", 0)), 1 if d.get("sr_tensor") is not None else 0)
         self.n = len(self.keep)
 
 

@@ -329,8 +329,20 @@ int check_hparams(const opt_hparams *hp, int fmt)
     return OPT_OK;
 }
 
+// index_base and the stochastic-rounding tensor number of one record.
+int check_slice(const opt_tensor &x, int64_t k, int64_t align)
+{
+    if (x.index_base < 0 || x.index_base % align != 0)
+        return fail(OPT_EINVAL, "tensor %lld: index_base must be >= 0 and a multiple of %lld", (long long)k,
+                    (long long)align);
+    if (x.sr_tensor_set != 0 && x.sr_tensor_set != 1) return fail(OPT_EINVAL, "tensor %lld: sr_tensor_set must be 0 or 1", (long long)k);
+    if (x.sr_tensor_set && x.sr_tensor < 0) return fail(OPT_EINVAL, "tensor %lld: sr_tensor must be >= 0", (long long)k);
+    return OPT_OK;
+}
+
 int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
 {
+    int rc;
     if (n < 0) return fail(OPT_EINVAL, "n < 0");
     if (n > 0 && !t) return fail(OPT_EINVAL, "tensors is NULL");
     if (n > INT32_MAX) return fail(OPT_EINVAL, "too many tensors");
@@ -345,6 +357,7 @@ int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
         if (x.p_dtype != OPT_F32 && blocked(fmt))
             return fail(OPT_EUNSUPPORTED, "tensor %lld: the blockwise state formats take fp32 parameters",
                         (long long)k);
+        if ((rc = check_slice(x, k, blocked(fmt) ? kQBlock : 4)) != OPT_OK) return rc;
         if (x.numel == 0) continue;
         const bool q8 = blocked(fmt), m2 = opt == kAdEMAMix;
         if (!x.p || !x.g || !x.s1 || !x.s2 || (m2 && !x.s3))
@@ -389,6 +402,8 @@ void plan_bucket(const opt_tensor *t, int64_t n, int gd, int pd, int64_t chunk, 
         d.numel = x.numel;
         d.chunk_begin = next;
         d.k = (int32_t)k;
+        d.rk = x.sr_tensor_set ? (uint32_t)x.sr_tensor : (uint32_t)k;
+        d.jbase = x.index_base;
         d.rg_begin = b.ngroups;
         b.ngroups += norm_groups(x.numel);
         const int64_t nc = (x.numel + chunk - 1) / chunk;
@@ -658,6 +673,7 @@ int opt_step_1state(int32_t optimizer, const opt_tensor *t, int64_t n, int32_t s
             return fail(OPT_EINVAL, "tensor %lld: unknown g_dtype %d", (long long)k, x.g_dtype);
         if (x.p_dtype != OPT_F32)
             return fail(OPT_EUNSUPPORTED, "tensor %lld: the one-state optimizers take fp32 parameters", (long long)k);
+        if ((rc = check_slice(x, k, 4)) != OPT_OK) return rc;
         if (x.numel == 0) continue;
         if (!x.p || !x.g || !x.s1) return fail(OPT_EINVAL, "tensor %lld: missing p, g or s1", (long long)k);
         if (!aligned(x.p, 16) || !aligned(x.g, 16) || !aligned(x.s1, 16))

@@ -60,8 +60,8 @@ struct QChunk {
     const uint8_t *g;      // bytes
     uint8_t *s1, *s2, *s3; // bytes (FP4: two elements per byte)
     float *a1, *a2, *a3;
-    int64_t e0;            // the chunk's first element within its tensor
-    int32_t k;             // the tensor's position in the caller's list
+    int64_t e0;            // the chunk's first element within its whole tensor (index_base included)
+    int32_t k;             // the tensor number of its stochastic-rounding stream
 };
 
 template <int GD, int SF>
@@ -77,8 +77,8 @@ __device__ __forceinline__ QChunk q8_chunk(const DevTensor &T, int64_t e0)
     c.a1 = T.a1 + e0 / kQBlock;
     c.a2 = T.a2 + e0 / kQBlock;
     c.a3 = T.a3 + e0 / kQBlock;
-    c.e0 = e0;
-    c.k = T.k;
+    c.e0 = T.jbase + e0;
+    c.k = (int32_t)T.rk;
     return c;
 }
 

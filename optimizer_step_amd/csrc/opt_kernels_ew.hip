@@ -71,13 +71,13 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
     // (high half), the second stream's m2 (low half) and a 16-bit p (high half)
     uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
     if (SF == kBF16SR) {
-        PhiloxOut w = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false);
+        PhiloxOut w = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false);
         rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
         rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
     }
     const bool psr = PD != kP32 && a.p_sr;
     if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
-        PhiloxOut w2 = sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true);
+        PhiloxOut w2 = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, true);
         rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
         rp[0] = w2.w0 >> 16; rp[1] = w2.w1 >> 16; rp[2] = w2.w2 >> 16; rp[3] = w2.w3 >> 16;
     }
@@ -107,12 +107,12 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
     }
     uint32_t rm = 0, rv = 0, rm2 = 0, rp = 0;
     if (SF == kBF16SR) {
-        uint32_t w = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, false), (int)(e & 3));
+        uint32_t w = philox_word(sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false), (int)(e & 3));
         rm = w & 0xFFFFu; rv = w >> 16;
     }
     const bool psr = PD != kP32 && a.p_sr;
     if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
-        uint32_t w2 = philox_word(sr_block(a.seed, a.step, T.k, (uint64_t)e >> 2, true), (int)(e & 3));
+        uint32_t w2 = philox_word(sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, true), (int)(e & 3));
         rm2 = w2 & 0xFFFFu; rp = w2 >> 16;
     }
     store_p1<PD>(T.p, e, pn, psr, rp);

@@ -31,11 +31,13 @@ struct alignas(16) DevTensor {
     float *a1, *a2, *a3;
     int64_t numel;
     int64_t chunk_begin;   // first chunk of this tensor in the bucket's chunk space
-    int32_t k;             // position in the caller's list
-    int32_t pad_;
+    int32_t k;             // position in the caller's list (norm output slot)
+    uint32_t rk;           // tensor number of the stochastic-rounding counter
     int64_t rg_begin;      // first norm-sum group of this tensor in the bucket (groups of kRGroup partials)
+    int64_t jbase;         // element index of element 0 within the whole tensor (stochastic rounding)
+    int64_t pad_;
 };
-static_assert(sizeof(DevTensor) == 96, "DevTensor layout");
+static_assert(sizeof(DevTensor) == 112, "DevTensor layout");
 
 // Norm-sum groups of a tensor of numel elements: kRGroup partials of kUTile
 // elements each, the last group possibly short.

@@ -285,3 +285,23 @@ def test_one_state_argument_checks(L):
     bad = (L.OptTensor * 1)(L.OptTensor(4096, 4096, 0, 0, None, None, None, None, 16, 0, 0))
     assert lib.opt_step_1state(2, bad, 1, 0, L.hparams(), None) == -1         # no s1
     assert lib.opt_step_1state(2, None, 0, 0, L.hparams(), None) == 0
+
+
+def test_index_base_and_stream_tensor_checks(L):
+    """index_base must be >= 0 and a multiple of 4 (256 for the blockwise
+    formats); sr_tensor_set must be 0 or 1, and sr_tensor >= 0 when set.
+    Arguments that pass the checks go on to need a GPU (any other status)."""
+    hp = L.hparams()
+    for fmt, base, bad in ((0, 4, False), (0, 2, True), (0, -4, True), (2, 1 << 40, False),
+                           (5, 128, True), (5, 512, False), (4, 256, False), (6, 100, True)):
+        blk = fmt >= 3
+        t = L.OptTensor(4096, 4096, 8192, 12288, None, 16384 if blk else None, 20480 if blk else None, None,
+                        16, 0, 0)
+        t.index_base = base
+        rc = _call(L, "opt_step_adamw", [t], fmt, hp)
+        assert (rc == -1) == bad, (fmt, base, rc, L.opt_last_error())
+    for set_, k, bad in ((2, 0, True), (1, -1, True), (1, 0, False), (1, 7, False), (0, -5, False)):
+        t = L.OptTensor(4096, 4096, 8192, 12288, None, None, None, None, 16, 0, 0)
+        t.sr_tensor, t.sr_tensor_set = k, set_
+        rc = _call(L, "opt_step_adamw", [t], 0, hp)
+        assert (rc == -1) == bad, (set_, k, rc, L.opt_last_error())
