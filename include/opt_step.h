@@ -80,9 +80,9 @@ typedef enum {
 
 /* ---- one tensor of the multi-tensor list --------------------------------
  * All pointers are device pointers owned by the caller.
- *   p        numel parameters in p_dtype, read and written.  OPT_F32 always;
- *            OPT_BF16 or OPT_F16 with the fp32 and BF16 state formats (the
- *            blockwise formats return OPT_EUNSUPPORTED): the stored value is
+ *   p        numel parameters in p_dtype, read and written: OPT_F32, or
+ *            OPT_BF16 / OPT_F16 with any state format (the two-state steps;
+ *            the one-state optimizers take OPT_F32 only).  A 16-bit value is
  *            widened exactly, stepped in fp32, and stored back rounded to
  *            nearest-even or stochastically (hp->p_rounding).
  *   g        numel gradients in g_dtype (OPT_F32, OPT_BF16 or OPT_F16), read.
@@ -335,7 +335,7 @@ int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, i
 /* Launch geometry for all later calls in this process: elements per chunk of
  * the host's chunk table (a power of two in [1024, 2^24]; default 32768) and
  * workgroups per compute unit: 0 (the default) launches one workgroup per
- * tile (whole chunks for the blockwise step), 1..64 a persistent grid of that
+ * tile (of each kernel's size, at most one chunk), 1..64 a persistent grid of that
  * many per compute unit walking the same tiles with a grid stride.  Results
  * do not depend on either.  OPT_EINVAL for other values. */
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);

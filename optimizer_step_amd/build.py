@@ -14,7 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libopt_step.so")
-SOURCES = ["opt_api.cpp", "opt_kernels.hip", "opt_kernels_ew.hip", "opt_kernels_1s.hip"]
+# (source, extra flags): the blockwise step compiles once per parameter storage
+SOURCES = [("opt_api.cpp", []), ("opt_kernels.hip", []), ("opt_kernels_ew.hip", []), ("opt_kernels_1s.hip", []),
+           ("opt_kernels_q8.hip", ["-DOPT_Q8_PD=0"]), ("opt_kernels_q8.hip", ["-DOPT_Q8_PD=1"]),
+           ("opt_kernels_q8.hip", ["-DOPT_Q8_PD=2"])]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -48,9 +51,9 @@ def build(verbose=False, out=LIB, extra_flags=()):
     tmpdir = tempfile.mkdtemp(prefix="optstep_build_")
     try:
         objs, cmds = [], []
-        for src in SOURCES:
-            obj = os.path.join(tmpdir, src + ".o")
-            cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        for i, (src, flags) in enumerate(SOURCES):
+            obj = os.path.join(tmpdir, f"{i}_{src}.o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *flags, *extra_flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             cmds.append(cmd)

@@ -354,9 +354,6 @@ int check_tensors(const opt_tensor *t, int64_t n, int opt, int fmt)
             return fail(OPT_EINVAL, "tensor %lld: unknown p_dtype %d", (long long)k, x.p_dtype);
         if (x.g_dtype != OPT_F32 && x.g_dtype != OPT_BF16 && x.g_dtype != OPT_F16)
             return fail(OPT_EINVAL, "tensor %lld: unknown g_dtype %d", (long long)k, x.g_dtype);
-        if (x.p_dtype != OPT_F32 && blocked(fmt))
-            return fail(OPT_EUNSUPPORTED, "tensor %lld: the blockwise state formats take fp32 parameters",
-                        (long long)k);
         if ((rc = check_slice(x, k, blocked(fmt) ? kQBlock : 4)) != OPT_OK) return rc;
         if (x.numel == 0) continue;
         const bool q8 = blocked(fmt), m2 = opt == kAdEMAMix;

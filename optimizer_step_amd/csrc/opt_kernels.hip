@@ -1,410 +1,13 @@
-// opt_kernels.hip -- gfx950 kernels of the blockwise-state step (8-bit
-// codebook, FP8 and FP4 states), the deterministic update-norm pre-pass, the
-// fused multi-tensor gradient norm, the standalone rounding cast and the test
-// hooks.  (The element-wise two-state step is in opt_kernels_ew.hip, the
-// one-state optimizers in opt_kernels_1s.hip.)
-//
-// The blockwise formats hand one 256-element block to one wave (64 lanes x 4
-// consecutive elements), which makes the block absmax a wave reduction; codes
-// move as 32-bit (8-bit formats) or 16-bit (FP4) accesses per lane, fully
-// coalesced.  Every kernel here is HBM-bound or close to it (no dense
-// contraction, so no MFMA): each byte is read or written once per call.
-#include "opt_elem.h"
+// opt_kernels.hip -- gfx950 kernels of the deterministic update-norm
+// pre-pass, the fused multi-tensor gradient norm, the standalone rounding
+// cast and the test hooks.  (The element-wise two-state step is in
+// opt_kernels_ew.hip, the blockwise-state step in opt_kernels_q8.hip, the
+// one-state optimizers in opt_kernels_1s.hip.)  Every kernel here is
+// HBM-bound or close to it (no dense contraction, so no MFMA): each byte is
+// read or written once per call.
+#include "opt_blk.h"
 
 namespace optstep {
-
-// ---------------------------------------------------------------------------
-// 8-bit blockwise states
-
-// Codes of this lane's four fp32 moments against their block absmax A (a
-// wave-uniform value).  When A and 1/A are normal and no moment of the wave is
-// a nonzero value below 2^-100, div_by gives the correctly rounded x = m'/A
-// (|x| <= 1); otherwise x = 0 for A = 0, else the correctly rounded m'/A, and
-// a NaN quotient (A NaN or infinite) gets code 0.
-template <bool SIGNED>
-__device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint32_t *lds, const QTabParams &P)
-{
-    uint32_t out = 0;
-    bool tiny = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tiny |= (fbits(x[i]) & 0x7FFFFFFFu) - 1u < 0x0D7FFFFFu;   // 0 < |x| < 2^-100
-    if (div_by_ok(A) && !__any(tiny)) {
-        const float y = 1.0f / A;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out |= q8_code(div_by(x[i], A, y), lds, P, SIGNED) << (8 * i);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float q = A == 0.0f ? 0.0f : x[i] / A;
-            out |= (q != q ? 0u : q8_lookup(q, lds, P, SIGNED)) << (8 * i);
-        }
-    }
-    return out;
-}
-
-// The block absmax from this lane's four values: max |x| as unsigned bit
-// patterns across the wave, so NaN poisons it.  Values of lanes past the end
-// of a short block are passed as 0.
-__device__ __forceinline__ float block_absmax(const float x[4])
-{
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
-    return bitsf(wave_max_u32(m));
-}
-
-// One chunk's arrays, offset to the chunk's first element (absmax to its
-// first block): wave-uniform base pointers, indexed with 32-bit offsets.
-struct QChunk {
-    float *p;
-    const uint8_t *g;      // bytes
-    uint8_t *s1, *s2, *s3; // bytes (FP4: two elements per byte)
-    float *a1, *a2, *a3;
-    int64_t e0;            // the chunk's first element within its whole tensor (index_base included)
-    int32_t k;             // the tensor number of its stochastic-rounding stream
-};
-
-template <int GD, int SF>
-__device__ __forceinline__ QChunk q8_chunk(const DevTensor &T, int64_t e0)
-{
-    const int64_t sb = fp4_fmt(SF) ? e0 / 2 : e0;
-    QChunk c;
-    c.p = T.p + e0;
-    c.g = (const uint8_t *)T.g + e0 * (GD == kGradF32 ? 4 : 2);   // bytes per gradient
-    c.s1 = (uint8_t *)T.s1 + sb;
-    c.s2 = (uint8_t *)T.s2 + sb;
-    c.s3 = (uint8_t *)T.s3 + sb;
-    c.a1 = T.a1 + e0 / kQBlock;
-    c.a2 = T.a2 + e0 / kQBlock;
-    c.a3 = T.a3 + e0 / kQBlock;
-    c.e0 = T.jbase + e0;
-    c.k = (int32_t)T.rk;
-    return c;
-}
-
-// One lane's four elements of a 256-element block, as loaded.  Codes are
-// packed in element order: 8 bits each, or 4 bits each for FP4.
-struct QIn {
-    float p[4], g[4];
-    uint32_t cm, cv, cm2;
-    float A1, A2, A3;
-};
-
-// Four codes of one state at element e (a multiple of 4) of the chunk.
-template <int SF, bool FULL>
-__device__ __forceinline__ uint32_t load_codes(const uint8_t *s, uint32_t e, int nmine)
-{
-    if (fp4_fmt(SF)) {
-        if (FULL || nmine == 4) return sld<uint16_t>(s + e / 2);
-        uint32_t c = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i += 2)
-            if (i < nmine) c |= (uint32_t)gld<uint8_t>(s + e / 2 + i / 2) << (4 * i);
-        return nmine & 1 ? c & ~(0xFu << (4 * nmine)) : c;
-    }
-    if (FULL || nmine == 4) return sld<uint32_t>(s + e);
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (i < nmine) c |= (uint32_t)gld<uint8_t>(s + e + i) << (8 * i);
-    return c;
-}
-
-template <int SF, bool FULL>
-__device__ __forceinline__ void store_codes(uint8_t *s, uint32_t e, int nmine, uint32_t c)
-{
-    if (fp4_fmt(SF)) {
-        if (FULL || nmine == 4) { sst<uint16_t>(s + e / 2, (uint16_t)c); return; }
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-            if (i < nmine) {
-                // past an odd tensor's last element the high nibble is 0
-                const uint32_t hi = i + 1 < nmine ? (c >> (4 * i + 4)) & 0xFu : 0u;
-                gst<uint8_t>(s + e / 2 + i / 2, (uint8_t)(((c >> (4 * i)) & 0xFu) | (hi << 4)));
-            }
-        }
-        return;
-    }
-    if (FULL || nmine == 4) { sst<uint32_t>(s + e, c); return; }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (i < nmine) gst<uint8_t>(s + e + i, (uint8_t)(c >> (8 * i)));
-}
-
-// Block b of the chunk (elements 256*b ..); lanes own 4 elements each.  A
-// step that starts the moments from zero reads no state.
-template <int OPT, int GD, int SF, bool FULL>
-__device__ __forceinline__ void q8_load(const StepArgs &a, const QChunk &C, uint32_t b, int nmine, int lane,
-                                        QIn &x)
-{
-    if (FULL) nmine = 4;
-    const uint32_t e = b * kQBlock + lane * 4;
-    if (nmine == 4) {
-        f4 pv = sld<f4>(C.p + e);
-        x.p[0] = pv.x; x.p[1] = pv.y; x.p[2] = pv.z; x.p[3] = pv.w;
-        if (GD == kGradF32) {
-            f4 gv = sld<f4>(C.g + 4 * e);
-            x.g[0] = gv.x; x.g[1] = gv.y; x.g[2] = gv.z; x.g[3] = gv.w;
-        } else {
-            widen4<GD == kGradBF16>(sld<u2>(C.g + 2 * e), x.g);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x.p[i] = 0.0f;
-            x.g[i] = 0.0f;
-            if (i < nmine) {
-                x.p[i] = gld<float>(C.p + e + i);
-                x.g[i] = GD == kGradF32    ? gld<float>(C.g + 4 * (e + i))
-                         : GD == kGradBF16 ? bf16_lo(gld<uint16_t>(C.g + 2 * (e + i)))
-                                           : f16_lo(gld<uint16_t>(C.g + 2 * (e + i)));
-            }
-        }
-    }
-    x.cm = x.cv = x.cm2 = 0;
-    x.A1 = x.A2 = x.A3 = 0.0f;
-    if (!a.fresh) {
-        x.cm = load_codes<SF, FULL>(C.s1, e, nmine);
-        x.cv = load_codes<SF, FULL>(C.s2, e, nmine);
-        if (OPT == kAdEMAMix) x.cm2 = load_codes<SF, FULL>(C.s3, e, nmine);
-        x.A1 = gld<float>(C.a1 + b);
-        x.A2 = gld<float>(C.a2 + b);
-        if (OPT == kAdEMAMix) x.A3 = gld<float>(C.a3 + b);
-    }
-}
-
-// Four stored values of one state.  WHICH: 0 = m, 1 = v, 2 = m2.
-// Grid values of every FP8/FP4 code (scale 1), one copy per workgroup in LDS:
-// E4M3 codes 0..255, or E2M1 codes 0..15 then unsigned E2M2 codes 0..15.
-constexpr int kMiniTab = 256;
-
-template <int SF>
-__device__ __forceinline__ void fill_mini_tab(float *tab, int tid, int nthreads)
-{
-    for (int i = tid; i < (fp4_fmt(SF) ? 32 : 256); i += nthreads)
-        tab[i] = fp4_fmt(SF) ? (i < 16 ? mini_decode<E2M1>((uint32_t)i, 0) : mini_decode<E2M2U>((uint32_t)(i - 16), 0))
-                             : mini_decode<E4M3>((uint32_t)i, 0);
-}
-
-// Four stored values of one state.  WHICH: 0 = m, 1 = v, 2 = m2.  FP8/FP4
-// codes read their grid value from `mtab` (fill_mini_tab) when it is given,
-// else decode it arithmetically; either way value(code) * 2^(floor(log2 A) -
-// emax) rounded to binary32.
-template <int SF, int WHICH>
-__device__ __forceinline__ void blk_decode4(const uint32_t *lds, uint32_t c, float A, float out[4],
-                                            const float *mtab = nullptr)
-{
-    if (SF == kQ8) {
-        const float *tab = (const float *)lds + (WHICH == 1 ? 256 : 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = tab[(c >> (8 * i)) & 0xFFu] * A;
-    } else if (fp4_fmt(SF) && WHICH == 1) {
-        const int sc = mini_dec_shift<E2M2U>(A);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out[i] = mtab ? ldexpf(mtab[16 + ((c >> (4 * i)) & 0xFu)], sc) : mini_decode<E2M2U>((c >> (4 * i)) & 0xFu, sc);
-    } else if (fp4_fmt(SF)) {
-        const int sc = mini_dec_shift<E2M1>(A);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out[i] = mtab ? ldexpf(mtab[(c >> (4 * i)) & 0xFu], sc) : mini_decode<E2M1>((c >> (4 * i)) & 0xFu, sc);
-    } else {
-        const int sc = mini_dec_shift<E4M3>(A);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out[i] = mtab ? ldexpf(mtab[(c >> (8 * i)) & 0xFFu], sc) : mini_decode<E4M3>((c >> (8 * i)) & 0xFFu, sc);
-    }
-    if (mini_fmt(SF) && !finite_f(A)) {          // a poisoned block reads as NaN
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = bitsf(0x7FC00000u);
-    }
-}
-
-template <class F, bool SR>
-__device__ __forceinline__ uint32_t mini_pack4(const float x[4], float A, const uint32_t r[4])
-{
-    if (!finite_f(A)) return 0u;
-    const int nsc = mini_enc_shift<F>(A);
-    constexpr int W = (F::kSign == 0x80u) ? 8 : 4;
-    uint32_t out = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out |= mini_encode<F, SR>(x[i], nsc, r[i]) << (W * i);
-    return out;
-}
-
-template <int SF, int WHICH>
-__device__ __forceinline__ uint32_t blk_encode4(const uint32_t *lds, const StepArgs &a, const float x[4], float A,
-                                                const uint32_t r[4])
-{
-    constexpr bool SR = sr_fmt(SF);
-    if (SF == kQ8) return WHICH == 1 ? quant4<false>(x, A, lds, a.q.u) : quant4<true>(x, A, lds, a.q.s);
-    if (fp4_fmt(SF)) return WHICH == 1 ? mini_pack4<E2M2U, SR>(x, A, r) : mini_pack4<E2M1, SR>(x, A, r);
-    return mini_pack4<E4M3, SR>(x, A, r);
-}
-
-// FULL: every lane holds four elements (all blocks but a tensor's short last one).
-template <int OPT, int SF, bool FULL>
-__device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const QChunk &C,
-                                          const uint32_t *lds, const float *mtab, uint32_t b, int nmine,
-                                          int lane, float lam, const QIn &x)
-{
-    if (FULL) nmine = 4;
-    const uint32_t e = b * kQBlock + lane * 4;
-    float m_in[4], v_in[4], m2_in[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    blk_decode4<SF, 0>(lds, x.cm, x.A1, m_in, mtab);
-    blk_decode4<SF, 1>(lds, x.cv, x.A2, v_in, mtab);
-    if (OPT == kAdEMAMix) blk_decode4<SF, 2>(lds, x.cm2, x.A3, m2_in, mtab);
-    if (a.fresh) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m_in[i] = v_in[i] = m2_in[i] = 0.0f;
-    }
-    // The stored moments are exact binary32; only the direction u (for p)
-    // takes the fast path, unless some v_hat in the wave is tiny or NaN.
-    float p[4], mo[4], vo[4], m2o[4];
-    float vmin = 1.0f;
-    Mom r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = moments_fast<OPT>(s, a, x.g[i], m_in[i], v_in[i], m2_in[i]);
-        vmin = fminf(vmin, r[i].v * s.rc2);
-    }
-    if (__any(!(vmin >= 0x1p-96f))) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = moments<OPT>(s, a, x.g[i], m_in[i], v_in[i], m2_in[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool valid = i < nmine;
-        const bool skip = a.skip_zeros && x.g[i] == 0.0f;   // keep p; code the old moments again
-        p[i] = skip ? x.p[i] : apply_update(x.p[i], s.d, lam, r[i].u);
-        mo[i] = valid ? (skip ? m_in[i] : r[i].m) : 0.0f;
-        vo[i] = valid ? (skip ? v_in[i] : r[i].v) : 0.0f;
-        m2o[i] = valid ? (skip ? m2_in[i] : r[i].m2) : 0.0f;
-    }
-    // stochastic rounding: the element's Philox word, low half for m, high
-    // half for v, low half of the second stream's word for m2
-    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0};
-    if (sr_fmt(SF)) {
-        const uint64_t q = (uint64_t)(C.e0 + e) >> 2;
-        PhiloxOut w = sr_block(a.seed, a.step, C.k, q, false);
-        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
-        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
-        if (OPT == kAdEMAMix) {
-            PhiloxOut w2 = sr_block(a.seed, a.step, C.k, q, true);
-            rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
-        }
-    }
-    const float Am = block_absmax(mo), Av = block_absmax(vo);
-    const uint32_t om = blk_encode4<SF, 0>(lds, a, mo, Am, rm);
-    const uint32_t ov = blk_encode4<SF, 1>(lds, a, vo, Av, rv);
-    uint32_t om2 = 0;
-    float Am2 = 0.0f;
-    if (OPT == kAdEMAMix) {
-        Am2 = block_absmax(m2o);
-        om2 = blk_encode4<SF, 2>(lds, a, m2o, Am2, rm2);
-    }
-    if (nmine == 4) {
-        sst<f4>(C.p + e, f4{p[0], p[1], p[2], p[3]});
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (i < nmine) gst<float>(C.p + e + i, p[i]);
-    }
-    store_codes<SF, FULL>(C.s1, e, nmine, om);
-    store_codes<SF, FULL>(C.s2, e, nmine, ov);
-    if (OPT == kAdEMAMix) store_codes<SF, FULL>(C.s3, e, nmine, om2);
-    if (lane == 0) {
-        gst<float>(C.a1 + b, Am);
-        gst<float>(C.a2 + b, Av);
-        if (OPT == kAdEMAMix) gst<float>(C.a3 + b, Am2);
-    }
-}
-
-// Lanes of this wave that hold elements of the block starting at eb.
-__device__ __forceinline__ int q8_mine(const DevTensor &T, int64_t eb, int lane)
-{
-    const int nvalid = (int)min((int64_t)kQBlock, T.numel - eb);
-    return max(0, min(4, nvalid - lane * 4));
-}
-
-#ifndef OPT_Q8_THREADS
-#define OPT_Q8_THREADS 512
-#endif
-#ifndef OPT_Q8_BLOCKS
-#define OPT_Q8_BLOCKS 1
-#endif
-// Workgroup size of the blockwise kernel (one LDS copy of the 8-bit tables
-// per workgroup) and full blocks in flight per wave.
-constexpr int kQ8Threads = OPT_Q8_THREADS;
-constexpr int kQ8Waves = kQ8Threads / 64;
-constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
-
-#ifndef OPT_Q8_TILE
-#define OPT_Q8_TILE 32768
-#endif
-// Elements per tile of the blockwise step (a power of two, a multiple of the
-// 8 x 256 elements one pass of the workgroup's waves covers).
-constexpr int64_t kQ8Tile = OPT_Q8_TILE;
-static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
-
-// Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
-// tile scheduling of opt_elem.h), one 256-element block per wave at a time,
-// kQ8Blocks blocks in flight per wave.
-// Waves per SIMD the AdamW instantiations are held to (their registers fit
-// 7 without spilling; AdEMAMix's third state does not, and is left free).
-constexpr int kQ8WavesAdamW = 7;
-
-template <int OPT, int GD, int SF>
-__global__ __launch_bounds__(kQ8Threads)
-__attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
-                                                             const int32_t *__restrict__ ctab,
-                                                             const uint32_t *__restrict__ qwords,
-                                                             StepArgs a)
-{
-    extern __shared__ uint32_t lds[];
-    __shared__ Scalars sh;
-    __shared__ float mtab_s[mini_fmt(SF) ? kMiniTab : 1];
-    if (SF == kQ8)
-        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
-    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
-    const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
-    if (threadIdx.x == 0) sh = make_scalars(a);
-    __syncthreads();
-    const Scalars s = sh;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
-        DevTensor T;
-        int64_t e0, len;
-        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
-        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
-        const uint32_t nblk = (uint32_t)((len + kQBlock - 1) / kQBlock);
-        const uint32_t nfull = (uint32_t)(len / kQBlock);
-        const QChunk C = q8_chunk<GD, SF>(T, e0);
-        uint32_t b = wave;
-        // kQ8Blocks full blocks per iteration: all their loads before any math
-        for (; b + (kQ8Blocks - 1) * kQ8Waves < nfull; b += kQ8Blocks * kQ8Waves) {
-            QIn x[kQ8Blocks];
-#pragma unroll
-            for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, SF, true>(a, C, b + u * kQ8Waves, 4, lane, x[u]);
-#pragma unroll
-            for (int u = 0; u < kQ8Blocks; ++u)
-                q8_finish<OPT, SF, true>(a, s, C, lds, mtab, b + u * kQ8Waves, 4, lane, lam, x[u]);
-        }
-        for (; b < nfull; b += kQ8Waves) {
-            QIn x0;
-            q8_load<OPT, GD, SF, true>(a, C, b, 4, lane, x0);
-            q8_finish<OPT, SF, true>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
-        }
-        if (b < nblk) {   // the tensor's short last block
-            const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
-            QIn x0;
-            q8_load<OPT, GD, SF, false>(a, C, b, nm, lane, x0);
-            q8_finish<OPT, SF, false>(a, s, C, lds, mtab, b, nm, lane, lam, x0);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // max_unorm pre-pass.  The tensor is cut into tiles of kUTile elements from
@@ -1003,50 +606,6 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
 
 // ---------------------------------------------------------------------------
 // launchers (called by opt_api.cpp)
-
-// The blockwise step over tiles of kQ8Tile elements (opt_elem.h).
-template <class K>
-static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
-{
-    set_tiles(a, kQ8Tile);
-    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kQ8Threads), lds, st, a.tens, a.chunk_tensor,
-                       a.q.words, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_step_ew(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st);
-
-template <int OPT, int GD>
-static hipError_t launch_step_t(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
-{
-    if (!blocked(fmt)) return launch_step_ew(OPT, GD, fmt, a, lg, st);
-    if (a.p_dtype != kP32) return hipErrorInvalidValue;
-    switch (fmt) {
-    case kQ8: return launch_q8_tiles(step_q8_kernel<OPT, GD, kQ8>, lds, lg, a, st);
-    case kFP8RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8RN>, 0, lg, a, st);
-    case kFP8SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8SR>, 0, lg, a, st);
-    case kFP4RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4RN>, 0, lg, a, st);
-    case kFP4SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4SR>, 0, lg, a, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int OPT>
-static hipError_t launch_step_o(int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
-{
-    switch (gd) {
-    case kGradF32: return launch_step_t<OPT, kGradF32>(fmt, a, lg, lds, st);
-    case kGradBF16: return launch_step_t<OPT, kGradBF16>(fmt, a, lg, lds, st);
-    case kGradF16: return launch_step_t<OPT, kGradF16>(fmt, a, lg, lds, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
-{
-    return opt == kAdamW ? launch_step_o<kAdamW>(gd, fmt, a, lg, lds, st)
-                         : launch_step_o<kAdEMAMix>(gd, fmt, a, lg, lds, st);
-}
 
 // The update-norm pre-pass over tiles of one 1024-element partial per wave.
 constexpr int64_t kUnTile = (int64_t)kWaves * kUTile;

@@ -1,0 +1,164 @@
+// opt_kernels_q8.hip -- gfx950 kernel of the blockwise-state step (8-bit
+// codebook, FP8 and FP4 states) for AdamW and AdEMAMix, fp32, BF16 or FP16
+// parameters and gradients, and the step's launcher (the element-wise formats
+// go to opt_kernels_ew.hip).  HBM-bound, with the codecs' VALU work close
+// behind: each byte is read or written once per step.
+#include "opt_blk.h"
+
+namespace optstep {
+
+#ifndef OPT_Q8_THREADS
+#define OPT_Q8_THREADS 512
+#endif
+#ifndef OPT_Q8_BLOCKS
+#define OPT_Q8_BLOCKS 1
+#endif
+// Workgroup size of the blockwise kernel (one LDS copy of the 8-bit tables
+// per workgroup) and full blocks in flight per wave.
+constexpr int kQ8Threads = OPT_Q8_THREADS;
+constexpr int kQ8Waves = kQ8Threads / 64;
+constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
+
+#ifndef OPT_Q8_TILE
+#define OPT_Q8_TILE 32768
+#endif
+// Elements per tile of the blockwise step (a power of two, a multiple of the
+// 8 x 256 elements one pass of the workgroup's waves covers).
+constexpr int64_t kQ8Tile = OPT_Q8_TILE;
+static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
+
+// Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
+// tile scheduling of opt_elem.h), one 256-element block per wave at a time,
+// kQ8Blocks blocks in flight per wave.
+// Waves per SIMD the AdamW instantiations are held to (their registers fit
+// 7 without spilling; AdEMAMix's third state does not, and is left free).
+constexpr int kQ8WavesAdamW = 7;
+
+template <int OPT, int GD, int SF, int PD>
+__global__ __launch_bounds__(kQ8Threads)
+__attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
+                                                             const int32_t *__restrict__ ctab,
+                                                             const uint32_t *__restrict__ qwords,
+                                                             StepArgs a)
+{
+    extern __shared__ uint32_t lds[];
+    __shared__ Scalars sh;
+    __shared__ float mtab_s[mini_fmt(SF) ? kMiniTab : 1];
+    if (SF == kQ8)
+        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
+    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
+    const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
+    if (threadIdx.x == 0) sh = make_scalars(a);
+    __syncthreads();
+    const Scalars s = sh;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
+        DevTensor T;
+        int64_t e0, len;
+        if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
+        const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
+        const uint32_t nblk = (uint32_t)((len + kQBlock - 1) / kQBlock);
+        const uint32_t nfull = (uint32_t)(len / kQBlock);
+        const QChunk C = q8_chunk<GD, SF, PD>(T, e0);
+        uint32_t b = wave;
+        // kQ8Blocks full blocks per iteration: all their loads before any math
+        for (; b + (kQ8Blocks - 1) * kQ8Waves < nfull; b += kQ8Blocks * kQ8Waves) {
+            QIn x[kQ8Blocks];
+#pragma unroll
+            for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, SF, PD, true>(a, C, b + u * kQ8Waves, 4, lane, x[u]);
+#pragma unroll
+            for (int u = 0; u < kQ8Blocks; ++u)
+                q8_finish<OPT, SF, PD, true>(a, s, C, lds, mtab, b + u * kQ8Waves, 4, lane, lam, x[u]);
+        }
+        for (; b < nfull; b += kQ8Waves) {
+            QIn x0;
+            q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
+            q8_finish<OPT, SF, PD, true>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
+        }
+        if (b < nblk) {   // the tensor's short last block
+            const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
+            QIn x0;
+            q8_load<OPT, GD, SF, PD, false>(a, C, b, nm, lane, x0);
+            q8_finish<OPT, SF, PD, false>(a, s, C, lds, mtab, b, nm, lane, lam, x0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers (called by opt_api.cpp)
+
+// The blockwise step over tiles of kQ8Tile elements (opt_elem.h).
+template <class K>
+static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
+{
+    set_tiles(a, kQ8Tile);
+    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kQ8Threads), lds, st, a.tens, a.chunk_tensor,
+                       a.q.words, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_ew(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st);
+
+template <int OPT, int GD, int PD>
+static hipError_t launch_q8_pd(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
+{
+    switch (fmt) {
+    case kQ8: return launch_q8_tiles(step_q8_kernel<OPT, GD, kQ8, PD>, lds, lg, a, st);
+    case kFP8RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8RN, PD>, 0, lg, a, st);
+    case kFP8SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8SR, PD>, 0, lg, a, st);
+    case kFP4RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4RN, PD>, 0, lg, a, st);
+    case kFP4SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4SR, PD>, 0, lg, a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// This translation unit holds the kernels for one parameter storage,
+// OPT_Q8_PD (0 fp32, 1 BF16, 2 FP16); the library compiles it once for each,
+// and the fp32 unit also holds the step's dispatcher.
+#ifndef OPT_Q8_PD
+#define OPT_Q8_PD 0
+#endif
+#define OPT_Q8_FN_(pd) launch_step_q8_p##pd
+#define OPT_Q8_FN(pd) OPT_Q8_FN_(pd)
+
+hipError_t OPT_Q8_FN(OPT_Q8_PD)(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds,
+                                 hipStream_t st)
+{
+    constexpr int PD = OPT_Q8_PD;
+    if (opt == kAdamW) {
+        switch (gd) {
+        case kGradF32: return launch_q8_pd<kAdamW, kGradF32, PD>(fmt, a, lg, lds, st);
+        case kGradBF16: return launch_q8_pd<kAdamW, kGradBF16, PD>(fmt, a, lg, lds, st);
+        case kGradF16: return launch_q8_pd<kAdamW, kGradF16, PD>(fmt, a, lg, lds, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (gd) {
+    case kGradF32: return launch_q8_pd<kAdEMAMix, kGradF32, PD>(fmt, a, lg, lds, st);
+    case kGradBF16: return launch_q8_pd<kAdEMAMix, kGradBF16, PD>(fmt, a, lg, lds, st);
+    case kGradF16: return launch_q8_pd<kAdEMAMix, kGradF16, PD>(fmt, a, lg, lds, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+#if OPT_Q8_PD == 0
+hipError_t launch_step_q8_p1(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds,
+                             hipStream_t st);
+hipError_t launch_step_q8_p2(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds,
+                             hipStream_t st);
+
+hipError_t launch_step(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
+{
+    if (!blocked(fmt)) return launch_step_ew(opt, gd, fmt, a, lg, st);
+    switch (a.p_dtype) {
+    case kP32: return launch_step_q8_p0(opt, gd, fmt, a, lg, lds, st);
+    case kPBF16: return launch_step_q8_p1(opt, gd, fmt, a, lg, lds, st);
+    case kPF16: return launch_step_q8_p2(opt, gd, fmt, a, lg, lds, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+#endif
+
+}  // namespace optstep

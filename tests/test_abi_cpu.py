@@ -270,7 +270,7 @@ def test_p16_rules(L):
     hp = L.hparams(p_rounding=2)
     assert _call(L, "opt_step_adamw", _tensor(L), 0, hp) == -1
     t = [L.OptTensor(4096, 4096, 8192, 12288, None, 16384, 16384, None, 16, 1, 1)]   # BF16 p, FP8 states
-    assert _call(L, "opt_step_adamw", t, 4) == -2
+    assert _call(L, "opt_step_adamw", t, 4) not in (-1, -2)                           # accepted (needs a GPU)
     t = [L.OptTensor(4096, 4096, 8192, 12288, None, None, None, None, 16, 3, 0)]      # unknown p dtype
     assert _call(L, "opt_step_adamw", t, 0) == -1
 

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_common import bf16_ulps, fp32_close, nan_equal_bits, to_dev, to_host
+from tests.gpu_common import BLOCKED_FMTS, bf16_ulps, fp32_close, nan_equal_bits, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -105,9 +105,12 @@ def _run_p16(opt, fmt, sizes, gds, pdt, p_sr, steps, hp, unorm=False):
     import torch
     import optimizer_step_amd as osa
     p0 = [_p16(synth.params(n, k, std=0.5), pdt) for k, n in enumerate(sizes)]
+    q8 = fmt == "q8"
+    qs, qu = (synth.codebook_signed(), synth.codebook_unsigned()) if q8 else (None, None)
     # oracle
     ps = [p.copy() for p in p0]
-    st = [oracle.state_zeros(fmt, n, opt) for n in sizes]
+    st = [oracle.state_zeros(fmt, n, opt, qs=qs, qu=qu) if q8 else oracle.state_zeros(fmt, n, opt) for n in sizes]
+    qkw = dict(qs=qs, qu=qu) if q8 else {}
     norms_o = []
     for t in range(1, steps + 1):
         for k, n in enumerate(sizes):
@@ -116,15 +119,15 @@ def _run_p16(opt, fmt, sizes, gds, pdt, p_sr, steps, hp, unorm=False):
             scale = 1.0
             if unorm:
                 wide = oracle.widen_bf16(ps[k]) if pdt == oracle.P_BF16 else ps[k].view(np.float16).astype(np.float32)
-                u2, p2 = oracle.unorm(opt, fmt, h, wide, g, **st[k])
+                u2, p2 = oracle.unorm(opt, fmt, h, wide, g, **st[k], **qkw)
                 norms_o.append((t, k, u2, p2))
                 scale = oracle.unorm_scale(hp["max_unorm"], u2, p2)
-            oracle.step(opt, fmt, h, ps[k], g, scale=scale, p_dtype=pdt, p_sr=p_sr, **st[k])
+            oracle.step(opt, fmt, h, ps[k], g, scale=scale, p_dtype=pdt, p_sr=p_sr, **st[k], **qkw)
     # GPU
     dev = []
     for k, n in enumerate(sizes):
         d = {"p": _dev_p16(p0[k], pdt), "g": to_dev(_grad(n, 1, k, gds[k]))}
-        d.update(osa.state_buffers(fmt, n, opt))
+        d.update(osa.state_buffers(fmt, n, opt, qmap_signed=qs, qmap_unsigned=qu))
         dev.append(d)
     tl = osa.TensorList(dev)
     fn = osa.opt_step_adamw if opt == "adamw" else osa.opt_step_ademamix
@@ -132,7 +135,8 @@ def _run_p16(opt, fmt, sizes, gds, pdt, p_sr, steps, hp, unorm=False):
     for t in range(1, steps + 1):
         for k, n in enumerate(sizes):
             dev[k]["g"].copy_(to_dev(_grad(n, t, k, gds[k])))
-        h = osa.hparams(step=t, seed=synth.SR_SEED, p_rounding=1 if p_sr else 0, **hp)
+        h = osa.hparams(step=t, seed=synth.SR_SEED, p_rounding=1 if p_sr else 0, qmap_signed=qs,
+                        qmap_unsigned=qu, **hp)
         un = None
         if unorm:
             un = torch.empty(2 * len(sizes), dtype=torch.float64, device="cuda")
@@ -162,6 +166,9 @@ def _check(ps, st, dev, fmt, opt, pdt, steps):
                 assert int(bf16_ulps(g, o).max(initial=0)) <= steps, (k, key)
             else:
                 assert nan_equal_bits(g, o), (k, key)
+            if fmt in BLOCKED_FMTS:   # codes above, absmax here: bit-exact
+                a = "a" + key[1]
+                assert nan_equal_bits(to_host(dev[k]["absmax" + key[1]]), st[k][a]), (k, a)
     assert same / max(total, 1) >= 0.999, same / total
 
 
@@ -198,14 +205,15 @@ def test_p16_with_update_norm():
         assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= tol_p * p2, (t, k)
 
 
-def test_blockwise_formats_refuse_p16():
+def test_one_state_refuses_p16():
+    """The one-state optimizers take fp32 parameters only."""
     import torch
     import optimizer_step_amd as osa
     d = {"p": torch.zeros(256, dtype=torch.bfloat16, device="cuda"),
-         "g": torch.zeros(256, dtype=torch.bfloat16, device="cuda")}
-    d.update(osa.state_buffers("fp8_rn", 256))
+         "g": torch.zeros(256, dtype=torch.bfloat16, device="cuda"),
+         "s1": torch.zeros(256, dtype=torch.float32, device="cuda")}
     with pytest.raises(osa.OptError) as e:
-        osa.opt_step_adamw(osa.TensorList([d]), osa.STATE_FP8_RN, osa.hparams())
+        osa.opt_step_1state("momentum", osa.TensorList([d]), "f32", osa.hparams())
     assert e.value.status == osa.OPT_EUNSUPPORTED
 
 
@@ -220,3 +228,30 @@ def test_grad_norm_f16():
     (s2, mx), per = oracle.grad_norm_list(grads)
     for k, (ps, pm) in enumerate(per):
         assert abs(o[2 + 2 * k] - ps) <= grads[k].size * 2.0 ** -53 * ps and o[3 + 2 * k] == pm
+
+
+@pytest.mark.parametrize("p_sr", [False, True])
+@pytest.mark.parametrize("pdt", [oracle.P_BF16, oracle.P_F16])
+@pytest.mark.parametrize("fmt", ["q8", "fp8_sr", "fp4_rn"])
+def test_p16_blockwise_states(fmt, pdt, p_sr):
+    """16-bit parameters with the blockwise state formats: codes and absmax
+    bit-exact, p within one 16-bit step per step."""
+    sizes = [1, 1001, 4096, 32768 + 77]
+    gds = ["f32", "bf16", "f16", "bf16"]
+    ps, st, dev, _, _ = _run_p16("adamw", fmt, sizes, gds, pdt, p_sr, 3, dict(lr=1e-2, weight_decay=0.1))
+    _check(ps, st, dev, fmt, "adamw", pdt, 3)
+
+
+@pytest.mark.parametrize("fmt", ["q8", "fp8_sr"])
+def test_p16_blockwise_ademamix_with_update_norm(fmt):
+    sizes = [3000, 65537]
+    ps, st, dev, no, ng = _run_p16("ademamix", fmt, sizes, ["bf16", "f32"], oracle.P_BF16, True, 3,
+                                   dict(lr=1e-2, max_unorm=0.5, beta3=0.999, alpha=5.0), unorm=True)
+    _check(ps, st, dev, fmt, "ademamix", oracle.P_BF16, 3)
+    for (t, k, u2, p2) in no:
+        g = ng[t - 1]
+        tol_p = 1e-12 if t == 1 else 1e-5   # as in test_p16_with_update_norm
+        # the moments differ from the oracle's only where a stored code does
+        # not (never, codes are bit-exact), so sum u^2 differs by summation only
+        assert abs(g[2 * k] - u2) <= 1e-12 * u2 and abs(g[2 * k + 1] - p2) <= tol_p * p2, (t, k)
+
