@@ -274,3 +274,136 @@ def test_bf16_states_one_billion_200_steps(fmt):
         assert abs(stalled[t] - so[t]) < 0.05
     del P, st, v_prev
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["fp8_rn", "fp8_sr", "fp4_rn", "fp4_sr"])
+def test_fp8_fp4_one_billion_elements(fmt):
+    """2^30 elements, FP8 / FP4 block-scaled m and v, 10% of gradients x100,
+    5 steps; 32 sampled blocks (first and last included), each replayed by the
+    oracle at its own element index (the stochastic-rounding stream is tied to
+    it): codes and absmax bit-exact, p within the fp32 bar."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS[f"adamw_{fmt}_1g"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    fp4 = fmt.startswith("fp4")
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = osa.state_buffers(fmt, n, "adamw")
+    nb = n // 256
+    blocks = np.unique(np.concatenate([[0, nb - 1], np.random.default_rng(21).integers(0, nb, 30)]))
+    idx = (blocks[:, None] * 256 + np.arange(256)[None, :]).reshape(-1)
+    cidx = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1) if fp4 else idx
+    p0 = _gather(P, idx)
+    g_hist = []
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", w["g_std"], t, bf16=True, mask_scale=w["mask_scale"])
+        views = {"p": P, "g": G, **st}
+        osa.opt_step_adamw(osa.TensorList([views]), fmt, osa.hparams(step=t, seed=synth.SR_SEED, **hp))
+        g_hist.append(_gather(G, idx))
+        del G
+    torch.cuda.synchronize()
+    gp = _gather(P, idx)
+    gm, gv = _gather(st["s1"], cidx), _gather(st["s2"], cidx)
+    ga1, ga2 = _gather(st["absmax1"], blocks), _gather(st["absmax2"], blocks)
+    cb = 128 if fp4 else 256
+    for i, b in enumerate(blocks):
+        sl = slice(256 * i, 256 * (i + 1))
+        p = p0[sl].copy()
+        s = oracle.state_zeros(fmt, 256, "adamw")
+        for t in range(1, steps + 1):
+            h = oracle.make_hp(step=t, seed=synth.SR_SEED, index_base=int(b) * 256, **hp)
+            oracle.step("adamw", fmt, h, p, g_hist[t - 1][sl], **s)
+        assert fp32_close(gp[sl], p), (fmt, b)
+        assert np.array_equal(gm[cb * i:cb * (i + 1)], s["s1"]), (fmt, b, "m")
+        assert np.array_equal(gv[cb * i:cb * (i + 1)], s["s2"]), (fmt, b, "v")
+        assert nan_equal_bits(ga1[i:i + 1], s["a1"]) and nan_equal_bits(ga2[i:i + 1], s["a2"]), (fmt, b)
+    del P, st
+    torch.cuda.empty_cache()
+
+
+def test_gradient_norm_llama7b_list():
+    """The bf16 gradient norm of the 290-tensor list in one call: four whole
+    tensors (the two 131M-element matrices, a 16M-element one, a norm vector)
+    against the oracle within the summation bound, maxima exact, the total
+    equal to the sum of the per-tensor sums within the bound."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["gradnorm_bf16_llama7b"]
+    sizes = w["sizes"]
+    total = sum(sizes)
+    offs = np.cumsum([0] + sizes[:-1])
+    G = synth.device_grads(total, "cuda", w["g_std"], 1, bf16=True)
+    grads = [G[o:o + n] for o, n in zip(offs, sizes)]
+    out = torch.empty(2 + 2 * len(sizes), dtype=torch.float64, device="cuda")
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
+    osa.opt_grad_norm(grads, out, 1.0, 2, coef)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    U = 2.0 ** -53
+    for k in (0, 1, 8, len(sizes) - 1):
+        ps, pm = oracle.grad_norm(to_host(grads[k]))
+        assert abs(o[2 + 2 * k] - ps) <= (sizes[k] - 1) * U * ps, (k, o[2 + 2 * k], ps)
+        assert o[3 + 2 * k] == pm, k
+    per = o[2::2]
+    assert abs(o[0] - per.sum()) <= len(sizes) * U * o[0]
+    assert o[1] == o[3::2].max()
+    want = np.float32(oracle.clip_coef(np.sqrt(o[0]), 1.0)).view(np.int32)
+    assert abs(int(coef.cpu().numpy().view(np.int32)[0]) - int(want)) <= 1
+    del G, grads
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("opt", ["momentum", "lion"])
+def test_one_state_one_billion_elements(opt):
+    """2^30 elements, bf16 gradients, fp32 state, 5 steps; 4096 sampled
+    elements (first and last included) against the oracle."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS[f"{opt}_f32_1g"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    S = torch.zeros(n, dtype=torch.float32, device="cuda")
+    idx = _sample_idx(n, 4096, 33)
+    p0 = _gather(P, idx)
+    g_hist = []
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", w["g_std"], t, bf16=True)
+        osa.opt_step_1state(opt, osa.TensorList([{"p": P, "g": G, "s1": S}]), "f32", osa.hparams(step=t, **hp))
+        g_hist.append(_gather(G, idx))
+        del G
+    torch.cuda.synchronize()
+    p, s1 = p0.copy(), np.zeros(idx.size, np.float32)
+    for t in range(1, steps + 1):
+        oracle.step_1state(opt, "f32", oracle.make_hp(step=t, **hp), p, g_hist[t - 1], s1)
+    assert fp32_close(_gather(P, idx), p)
+    assert fp32_close(_gather(S, idx), s1)
+    del P, S
+    torch.cuda.empty_cache()
+
+
+def test_round_cast_one_billion_values():
+    """The stochastic BF16 cast of 2^30 values in one launch: the first 2^24
+    outputs bit-exact against the oracle, and every output one of the two
+    BF16 neighbours of its input (the rounding never leaves its gap)."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["cast_bf16_sr_1g"]
+    n = w["sizes"][0]
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(x, synth.PARAM_SEED, w["p_std"])
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    osa.opt_round_cast(x, out, True, synth.SR_SEED, 7)
+    torch.cuda.synchronize()
+    m = 1 << 24
+    xh = to_host(x[:m])
+    assert np.array_equal(to_host(out[:m]), oracle.round_cast(xh, oracle.P_BF16, True, synth.SR_SEED, 7))
+    xb = x.view(torch.int32)
+    lo = (xb & ~0xFFFF).view(torch.float32)                # toward zero: the gap's inner end
+    wide = out.float()
+    inner = wide == lo
+    outer = (wide.view(torch.int32) == ((xb & ~0xFFFF) + 0x10000)) & ((xb & 0xFFFF) != 0)
+    assert bool((inner | outer).all())
+    del x, out, xb, lo, wide
+    torch.cuda.empty_cache()
