@@ -82,6 +82,14 @@ static float bf(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
 // tau_i the smallest float above t_i: the nearest entry, ties to the lower
 // index.  The table splits [lo, 1] into buckets of 2^shift ulps (one sign at
 // a time) holding at most one tau each, so one comparison finishes the code.
+// The comparison is folded into the entry (opt_plan.h): with base taus at or
+// below the bucket and the bucket's tau at in-bucket key K, x > 0 takes
+// E = ((base + 1) << 24) - K, so E + k carries into the top byte iff k >= K;
+// x = -m (m's key k) takes E = ((base + 1) << 24) + K', K' the key of -tau,
+// so E + ~k = E - k - 1 keeps base + 1 iff k <= K' - 1.  A bucket with no tau
+// uses K = 2^shift and K' = 0 (never and always past).  Sums stay within 2^24
+// of the top byte's boundary because k and K are below 2^18, and arithmetic
+// is modulo 2^32, which is what the device does.
 int build_search(const float *T, bool is_signed, BuiltTable &out)
 {
     for (int i = 0; i < 256; ++i) {
@@ -116,22 +124,22 @@ int build_search(const float *T, bool is_signed, BuiltTable &out)
         for (uint32_t b = 0; b < nb && ok; ++b) {
             const uint32_t L = lo + (b << shift), H = L + (1u << shift) - 1u;
             const float xl = bf(L), xh = bf(H);
-            // x >= 0 with magnitude bits in [L, H]
-            uint32_t base = 0, nin = 0, thr = 1u << shift;
+            // x > 0 with magnitude bits in [L, H]: past the tau at key K
+            uint32_t base = 0, nin = 0, K = 1u << shift;
             for (int i = 0; i < 255; ++i) {
                 if (tau[i] <= xl) ++base;
-                else if (tau[i] <= xh) { ++nin; thr = fb(tau[i]) - L; }
+                else if (tau[i] <= xh) { ++nin; K = fb(tau[i]) - L; }
             }
-            ent[b] = base | (thr << 8);
+            ent[sides * b] = ((base + 1u) << 24) - K;
             ok = nin <= 1;
             if (is_signed && ok) {
-                // x = -m, m in [xl, xh]
-                base = 0; nin = 0; thr = 1u << shift;
+                // x = -m, m in [xl, xh]: one more code while m's key <= key(-tau)
+                base = 0; nin = 0; K = 0;
                 for (int i = 0; i < 255; ++i) {
                     if (tau[i] <= -xh) ++base;
-                    else if (tau[i] <= -xl) { ++nin; thr = ((1u << shift) - 1u) - (fb(-tau[i]) - L); }
+                    else if (tau[i] <= -xl) { ++nin; K = fb(-tau[i]) - L + 1u; }
                 }
-                ent[nb + b] = base | (thr << 8);
+                ent[2 * b + 1] = ((base + 1u) << 24) + K;
                 ok = nin <= 1;
             }
         }

@@ -16,22 +16,55 @@ namespace optstep {
 // ---------------------------------------------------------------------------
 // 8-bit blockwise states
 
+// The top bytes of four words, packed low to high (two byte permutes and an
+// or): the codes q8_code_hi leaves there.
+__device__ __forceinline__ uint32_t pack_top_bytes(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3)
+{
+    // selector bytes 0-3 pick from the second operand, 4-7 from the first,
+    // 0x0C gives a zero byte
+    return __builtin_amdgcn_perm(h1, h0, 0x0C0C0703u) | __builtin_amdgcn_perm(h3, h2, 0x07030C0Cu);
+}
+
+// q8_code_hi for the step's fast path, x normal or 0 with |x| <= 1, the table
+// in LDS: the same entry and sum with byte-offset addressing.  s is all ones
+// iff x <= +0 as a signed integer (a saturating b - 1 keeps -0 negative), and
+// picks the odd entry through its bit 2 (the table starts 8-byte aligned).
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t q8_code_hi_lds(float x, const uint32_t *tab, const QTabParams &P)
+{
+    const uint32_t b = fbits(x);
+    const uint32_t a = b & 0x7FFFFFFFu;
+    const uint32_t d = a > P.lo ? a - P.lo : 0u;
+    const uint32_t k = d & ((1u << P.shift) - 1u);
+    const uint32_t j = d >> P.shift;
+    typedef __attribute__((address_space(3))) const uint32_t lds_word;
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_word *)(tab + P.offset);   // LDS byte address
+    if (!SIGNED) return *(lds_word *)(uintptr_t)(base + (j << 2)) + k;
+    const uint32_t s = (uint32_t)(__builtin_elementwise_sub_sat((int32_t)b, 1) >> 31);
+    const uint32_t e = *(lds_word *)(uintptr_t)((j << 3) + ((s & 4u) | base));
+    return e + (k ^ s);
+}
+
 // Codes of this lane's four fp32 moments against their block absmax A (a
-// wave-uniform value).  When A and 1/A are normal and no moment of the wave is
-// a nonzero value below 2^-100, div_by gives the correctly rounded x = m'/A
-// (|x| <= 1); otherwise x = 0 for A = 0, else the correctly rounded m'/A, and
-// a NaN quotient (A NaN or infinite) gets code 0.
+// wave-uniform value).  When div_by_ok(A) and no moment of the wave is a
+// nonzero value below 2^-100, div_by gives the correctly rounded x = m'/A
+// (|x| <= 1, normal or 0); otherwise x = 0 for A = 0, else the correctly
+// rounded m'/A, and a NaN quotient (A NaN or infinite) gets code 0.
 template <bool SIGNED>
 __device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint32_t *lds, const QTabParams &P)
 {
     uint32_t out = 0;
-    bool tiny = false;
+    // 0 < |x| < 2^-100 for some x: |x| - 1 (as unsigned, 0 wraps to the top)
+    // below the bits of 2^-100 - 1
+    uint32_t t = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tiny |= (fbits(x[i]) & 0x7FFFFFFFu) - 1u < 0x0D7FFFFFu;   // 0 < |x| < 2^-100
-    if (div_by_ok(A) && !__any(tiny)) {
+    for (int i = 0; i < 4; ++i) t = min(t, (fbits(x[i]) & 0x7FFFFFFFu) - 1u);
+    if (div_by_ok(A) && !__any(t < 0x0D7FFFFFu)) {
         const float y = 1.0f / A;
+        uint32_t h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out |= q8_code(div_by(x[i], A, y), lds, P, SIGNED) << (8 * i);
+        for (int i = 0; i < 4; ++i) h[i] = q8_code_hi_lds<SIGNED>(div_by(x[i], A, y), lds, P);
+        out = pack_top_bytes(h[0], h[1], h[2], h[3]);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -273,12 +306,25 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const bool valid = i < nmine;
-        const bool skip = a.skip_zeros && x.g[i] == 0.0f;   // keep p; code the old moments again
-        p[i] = skip ? x.p[i] : apply_update(x.p[i], s.d, lam, r[i].u);
-        mo[i] = valid ? (skip ? m_in[i] : r[i].m) : 0.0f;
-        vo[i] = valid ? (skip ? v_in[i] : r[i].v) : 0.0f;
-        m2o[i] = valid ? (skip ? m2_in[i] : r[i].m2) : 0.0f;
+        p[i] = apply_update(x.p[i], s.d, lam, r[i].u);
+        mo[i] = r[i].m;
+        vo[i] = r[i].v;
+        m2o[i] = r[i].m2;
+    }
+    if (a.skip_zeros) {   // a zero gradient keeps p and codes the old moments again
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (x.g[i] == 0.0f) {
+                p[i] = x.p[i];
+                mo[i] = m_in[i];
+                vo[i] = v_in[i];
+                m2o[i] = m2_in[i];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i >= nmine) mo[i] = vo[i] = m2o[i] = 0.0f;   // past the end of a short block
     }
     // stochastic rounding: the element's Philox word, low half for m, high
     // half for v; the second stream's word, low half for m2 and high half

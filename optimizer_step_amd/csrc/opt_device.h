@@ -165,33 +165,41 @@ __host__ __device__ inline float div_by(float a, float b, float y)
     return fmaf(r, y, q);
 }
 
-// b for which div_by is exact: b and 1/b both well inside the normal range.
+// b for which div_by is exact for every dividend a with |a| >= 2^-100 or
+// a = 0 and |a| <= |b|: 2^-124 <= |b| <= 2^26 keeps b and 1/b normal and the
+// quotient at or above 2^-126.  An integer test of the bits, so a wave-uniform
+// b is checked on the scalar unit.
 __host__ __device__ inline bool div_by_ok(float b)
 {
-    float ab = b < 0 ? -b : b;
-    return ab >= 0x1p-124f && ab <= 0x1p124f;
+    return (fbits(b) & 0x7FFFFFFFu) - 0x01800000u <= 0x4C800000u - 0x01800000u;
 }
 
 // ---------------------------------------------------------------------------
 // 8-bit code of x against a codebook's lookup table (layout in opt_plan.h),
 // for x with |x| <= 1 that is not NaN (and, for an unsigned table, x >= 0 or
-// -0).  The magnitude max(|x|, lo) picks a bucket that holds at most one
-// threshold, so the code is the bucket's base plus one comparison.  +0 reads
-// the x < 0 half: a midpoint of exactly 0 sits between +0 and the smallest
-// positive float, and that half holds code(0) for m -> 0.  For x < 0 the
-// in-bucket key is mirrored (xor with the bucket mask flips only the low
-// bits, so the bucket index is unchanged).
+// -0), returned in the top byte of the word (the low bits are noise).  The
+// magnitude max(|x|, lo) picks a bucket that holds at most one threshold, so
+// the code is the bucket's entry plus the in-bucket key.  +0 reads the x <= 0
+// side: a midpoint of exactly 0 sits between +0 and the smallest positive
+// float, and that side holds code(0) for m -> 0.  On the x <= 0 side the key
+// enters complemented (s = all ones), which the entries expect.
+__host__ __device__ inline uint32_t q8_code_hi(float x, const uint32_t *tab, const QTabParams &P,
+                                               bool is_signed)
+{
+    const uint32_t b = fbits(x);
+    const uint32_t a = b & 0x7FFFFFFFu;
+    const uint32_t d = a > P.lo ? a - P.lo : 0u;       // all |x| < lo share one code
+    const uint32_t k = d & ((1u << P.shift) - 1u);
+    const uint32_t j = d >> P.shift;
+    if (!is_signed) return tab[P.offset + j] + k;
+    const uint32_t s = (int32_t)b <= 0 ? ~0u : 0u;
+    return tab[P.offset + 2u * j + (s & 1u)] + (k ^ s);
+}
+
 __host__ __device__ inline uint32_t q8_code(float x, const uint32_t *tab, const QTabParams &P,
                                             bool is_signed)
 {
-    const uint32_t b = fbits(x);
-    uint32_t mag = b & 0x7FFFFFFFu;
-    mag = mag > P.lo ? mag : P.lo;                     // all |x| < lo share one code
-    const uint32_t mask = (1u << P.shift) - 1u;
-    const bool neg = is_signed && (int32_t)b <= 0;
-    const uint32_t off = (mag - P.lo) ^ (neg ? mask : 0u);
-    const uint32_t e = tab[(neg ? P.offset + P.nb : P.offset) + (off >> P.shift)];
-    return (e & 0xFFu) + ((off & mask) >= (e >> 8) ? 1u : 0u);
+    return q8_code_hi(x, tab, P, is_signed) >> 24;
 }
 
 // The same for any x that is not NaN (callers map NaN to code 0): magnitudes
@@ -511,9 +519,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    return __builtin_amdgcn_readfirstlane(max(max(r0, r1), max(r2, r3)));
+    // row_bcast:15 into rows 1 and 3 (row 1 = rows 0-1, row 3 = rows 2-3), then
+    // row_bcast:31 into rows 2 and 3: lane 63 ends with the wave max; rows
+    // outside a step's row mask see 0, the identity of the max
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum over the 64 lanes in a fixed butterfly order; every lane ends with the

@@ -10,14 +10,10 @@ namespace optstep {
 #ifndef OPT_Q8_THREADS
 #define OPT_Q8_THREADS 512
 #endif
-#ifndef OPT_Q8_BLOCKS
-#define OPT_Q8_BLOCKS 1
-#endif
 // Workgroup size of the blockwise kernel (one LDS copy of the 8-bit tables
-// per workgroup) and full blocks in flight per wave.
+// per workgroup).
 constexpr int kQ8Threads = OPT_Q8_THREADS;
 constexpr int kQ8Waves = kQ8Threads / 64;
-constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
 
 #ifndef OPT_Q8_TILE
 #define OPT_Q8_TILE 32768
@@ -27,33 +23,19 @@ constexpr int kQ8Blocks = OPT_Q8_BLOCKS;
 constexpr int64_t kQ8Tile = OPT_Q8_TILE;
 static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 
-// Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
-// tile scheduling of opt_elem.h), one 256-element block per wave at a time,
-// kQ8Blocks blocks in flight per wave.
+#ifndef OPT_Q8_WAVES
+#define OPT_Q8_WAVES 7
+#endif
 // Waves per SIMD the AdamW instantiations are held to (their registers fit
 // 7 without spilling; AdEMAMix's third state does not, and is left free).
-constexpr int kQ8WavesAdamW = 7;
+constexpr int kQ8WavesAdamW = OPT_Q8_WAVES;
 
+// The tiles of one workgroup: one 256-element block per wave at a time.
 template <int OPT, int GD, int SF, int PD>
-__global__ __launch_bounds__(kQ8Threads)
-__attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
-                                                             const int32_t *__restrict__ ctab,
-                                                             const uint32_t *__restrict__ qwords,
-                                                             StepArgs a)
+__device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, const int32_t *__restrict__ ctab,
+                                         const StepArgs &a, const Scalars &s, const uint32_t *lds,
+                                         const float *mtab, int lane, int wave)
 {
-    extern __shared__ uint32_t lds[];
-    __shared__ Scalars sh;
-    __shared__ float mtab_s[mini_fmt(SF) ? kMiniTab : 1];
-    if (SF == kQ8)
-        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
-    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
-    const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
-    if (threadIdx.x == 0) sh = make_scalars(a);
-    __syncthreads();
-    const Scalars s = sh;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
     for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
         DevTensor T;
         int64_t e0, len;
@@ -63,15 +45,6 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
         const uint32_t nfull = (uint32_t)(len / kQBlock);
         const QChunk C = q8_chunk<GD, SF, PD>(T, e0);
         uint32_t b = wave;
-        // kQ8Blocks full blocks per iteration: all their loads before any math
-        for (; b + (kQ8Blocks - 1) * kQ8Waves < nfull; b += kQ8Blocks * kQ8Waves) {
-            QIn x[kQ8Blocks];
-#pragma unroll
-            for (int u = 0; u < kQ8Blocks; ++u) q8_load<OPT, GD, SF, PD, true>(a, C, b + u * kQ8Waves, 4, lane, x[u]);
-#pragma unroll
-            for (int u = 0; u < kQ8Blocks; ++u)
-                q8_finish<OPT, SF, PD, true>(a, s, C, lds, mtab, b + u * kQ8Waves, 4, lane, lam, x[u]);
-        }
         for (; b < nfull; b += kQ8Waves) {
             QIn x0;
             q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
@@ -84,6 +57,30 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
             q8_finish<OPT, SF, PD, false>(a, s, C, lds, mtab, b, nm, lane, lam, x0);
         }
     }
+}
+
+// Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
+// tile scheduling of opt_elem.h).
+template <int OPT, int GD, int SF, int PD>
+__global__ __launch_bounds__(kQ8Threads)
+__attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
+                                                             const int32_t *__restrict__ ctab,
+                                                             const uint32_t *__restrict__ qwords,
+                                                             StepArgs a)
+{
+    extern __shared__ uint32_t lds[];
+    __shared__ Scalars sh;
+    __shared__ float mtab_s[mini_fmt(SF) ? kMiniTab : 1];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (SF == kQ8)
+        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
+    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
+    const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
+    if (threadIdx.x == 0) sh = make_scalars(a);
+    __syncthreads();
+    const Scalars s = sh;
+    q8_tiles<OPT, GD, SF, PD>(tens, ctab, a, s, lds, mtab, lane, wave);
 }
 
 // ---------------------------------------------------------------------------

@@ -43,12 +43,14 @@ static_assert(sizeof(DevTensor) == 112, "DevTensor layout");
 // elements each, the last group possibly short.
 constexpr int64_t norm_groups(int64_t numel) { return ((numel + kUTile - 1) / kUTile + kRGroup - 1) / kRGroup; }
 
-// 8-bit codebook lookup-table parameters (see opt_qtable in opt_api.cpp).
+// 8-bit codebook lookup-table parameters (see build_search in opt_api.cpp).
 // For |x| <= 1 the magnitude bits a = bits(max(|x|, lo_f)) give the bucket
-// b = (a - lo) >> shift and the in-bucket key (a - lo) & mask; a signed table
-// holds nb buckets for x >= 0 followed by nb for x < 0.  Each 32-bit entry is
-// base | thr << 8: code = base + (key' >= thr), key' = key for x >= 0 and
-// mask - key for x < 0.
+// b = (a - lo) >> shift and the in-bucket key k = (a - lo) & mask (shift is
+// at most 17, so k < 2^17).  An unsigned table holds one entry per bucket; a
+// signed table two, interleaved: entry 2b for x > 0, 2b + 1 for x <= 0.  An
+// entry E carries the code in its top byte after one 32-bit add:
+// code = (E + k) >> 24 for x > 0 and (E + ~k) >> 24 for x <= 0, i.e. the
+// bucket's base code plus one when k is past the bucket's threshold.
 struct QTabParams {
     uint32_t lo;       // bit pattern of the smallest magnitude kept apart
     uint32_t shift;    // log2 of the bucket width in ulps
