@@ -255,27 +255,57 @@ def time_workload(name, steps, warmup, torch, osa, synth):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the headline workload
 
-def cpu_baseline(budget_s=12.0):
-    import numpy as np
+_start_barrier = None
+
+
+def _set_barrier(b):
+    global _start_barrier
+    _start_barrier = b
+    import torch
+    torch.set_num_threads(1)      # the inputs' BF16 cast, one thread per worker
+
+
+def _oracle_steps(k, budget_s, n=1 << 24):
+    """AdamW steps of the C oracle (fp32 p/m/v, bf16 g) over n elements of
+    tensor k's synthetic inputs for about budget_s seconds: (steps, elements
+    stepped, seconds).  Workers of a pool start timing together."""
     import oracle
     import synth
-    n = 1 << 24
-    p = synth.params(n)
-    g = synth.grads(n, 1, std=1e-3, bf16=True)
+    p = synth.params(n, k)
+    g = synth.grads(n, 1, k, std=1e-3, bf16=True)
     st = oracle.state_zeros("f32", n)
+    if _start_barrier is not None:
+        _start_barrier.wait(timeout=300)   # a lost worker fails the pool, not hangs it
     done = 0
-    t0 = time.perf_counter()
     t = 0
+    t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         t += 1
-        hp = oracle.make_hp(lr=3e-4, weight_decay=0.1, step=t)
-        oracle.step("adamw", "f32", hp, p, g, **st)
+        oracle.step("adamw", "f32", oracle.make_hp(lr=3e-4, weight_decay=0.1, step=t), p, g, **st)
         done += n
-    dt = time.perf_counter() - t0
-    return {"value": done / dt / 1e9, "unit": "Gelem/s", "cores": 1, "kind": "oracle",
-            "sample": f"{t} steps of AdamW (fp32 p/m/v, bf16 g) over the first 2^24 elements of the "
-                      f"Llama-7B-shaped list, single-threaded C oracle, {dt:.1f} s",
-            "bytes_per_element": 26, "GBps": done * 26 / dt / 1e9}
+    return t, done, time.perf_counter() - t0
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle on the host: one process per core of this process's CPU
+    share (at most 16), each on its own 2^24-element slice, then one process
+    alone.  The workers are forked, so this runs before the process touches
+    the GPU, and before it uses torch's CPU thread pool (the inputs' BF16
+    cast), which a forked child could not use."""
+    import multiprocessing
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers, initializer=_set_barrier, initargs=(ctx.Barrier(workers),)) as pool:
+        res = pool.starmap(_oracle_steps, [(k, budget_s) for k in range(workers)], chunksize=1)
+    steps, done, dt = _oracle_steps(0, budget_s)
+    single = done / dt / 1e9
+    rate = sum(d / s for _, d, s in res) / 1e9          # the workers' intervals overlap
+    return {"value": rate, "unit": "Gelem/s", "cores": workers, "kind": "oracle",
+            "sample": f"AdamW (fp32 p/m/v, bf16 g) on 2^24-element slices of the Llama-7B-shaped list's "
+                      f"synthetic inputs, C oracle: {workers} processes x ~{budget_s:.0f} s "
+                      f"({sum(r[0] for r in res)} steps); one process alone: {steps} steps in {dt:.1f} s",
+            "bytes_per_element": 26, "GBps": rate * 26,
+            "single_core": {"value": single, "unit": "Gelem/s", "cores": 1, "GBps": single * 26}}
 
 
 def calibrate(torch, osa, n=1 << 30, reps=3):
@@ -427,13 +457,13 @@ def main():
     if args.summarize_rows_trace:
         summarize_rows_trace(args.summarize_rows_trace,
                              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace "
-                             "-- python bench.py > gpurun_out/trace_bench.json")
+                             "-- python bench.py --no-cpu > gpurun_out/trace_bench.json")
         return
     if args.summarize_profiles:
         base = "python bench.py --rows none --no-cpu --calibrate"
         summarize_profiles(*args.summarize_profiles,
                            cmd_trace="rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
-                                     "python bench.py > gpurun_out/trace_bench.json",
+                                     "python bench.py --no-cpu > gpurun_out/trace_bench.json",
                            cmd_fetch=f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- {base} --steps 2 --warmup 1",
                            cmd_write=f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- {base} --steps 2 --warmup 1")
         return
@@ -441,6 +471,13 @@ def main():
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the step shards with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baseline first: its workers are forked, which must happen
+    # before this process initialises the GPU
+    cpu = None if args.no_cpu else cpu_baseline()
+    if cpu is not None:
+        print(f"[bench] CPU oracle: {cpu['value']:.3f} Gelem/s on {cpu['cores']} cores, "
+              f"{cpu['single_core']['value']:.3f} on 1", file=sys.stderr, flush=True)
 
     import torch
     import optimizer_step_amd as osa
@@ -468,7 +505,6 @@ def main():
         rows.append(r)
 
     calib = calibrate(torch, osa) if args.calibrate else None
-    cpu = None if args.no_cpu else cpu_baseline()
     traffic = counter_traffic(head, main_row["elements"])
     gb_launch = main_row["bytes_per_element"] * main_row["elements"]
     out = {

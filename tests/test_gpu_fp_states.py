@@ -154,6 +154,54 @@ def test_q8_tiny_moments_in_normal_blocks(opt):
     states_bit_identical(case, dev, st)
 
 
+def _linear_signed():
+    # entries +-1/255, +-3/255, ...: the middle midpoint is exactly 0
+    return np.linspace(-1, 1, 256).astype(np.float32)
+
+
+def test_q8_huge_absmax_with_tiny_moments():
+    """Blocks whose absmax is 1e10..1e13 holding moments of 1e-30..1e-25:
+    their quotients m'/A fall below the normal range, where the reused
+    reciprocal is not covered, so such blocks take true division.  The
+    linear codebook's zero midpoint makes a flushed or misrounded tiny
+    quotient change its code."""
+    def g_of(t, k, n):
+        g = synth.grads(n, t, k, std=1e-2)
+        rng = np.random.default_rng([23, t, k])
+        for b, big in ((0, 1e11), (1, -3e12), (3, 1e13), (6, 2e10)):
+            sl = slice(256 * b, 256 * (b + 1))
+            g[sl] = (rng.choice([-1.0, 1.0], 256) * 10.0 ** rng.uniform(-29, -24, 256)).astype(np.float32)
+            g[256 * b + 7 * (t + k) % 256] = np.float32(big)
+        return g.astype(np.float32)
+    case = Case("adamw", "q8", [2048, 1800], False, 3, _hp("adamw"), grad_override=g_of)
+    case.qs = _linear_signed()
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+    states_bit_identical(case, dev, st)
+    assert st[0]["a1"][3] > 2.0 ** 26                  # the fallback's range exercised
+
+
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+def test_q8_signed_zero_moments(opt):
+    """Exact +-0 gradients at step 1 give moments of +0 and -0 (a fresh
+    state decodes to -0 for a negative zero code): both must take the code of
+    x <= 0 on the linear codebook, whose midpoint between -1/255 and +1/255 is
+    exactly 0, while the smallest positive quotients take the one above."""
+    def g_of(t, k, n):
+        g = synth.grads(n, t, k, std=1e-2)
+        rng = np.random.default_rng([29, t, k])
+        z = rng.random(n) < 0.3
+        g[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+        return g.astype(np.float32)
+    case = Case(opt, "q8", [4096, 777], False, 3, _hp(opt), grad_override=g_of)
+    case.qs = _linear_signed()
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+    states_bit_identical(case, dev, st)
+
+
 @pytest.mark.parametrize("fmt", FP_FMTS + ["q8"])
 def test_nan_and_tiny_gradients(fmt):
     """A NaN gradient poisons its block's absmax (the block then reads back as
