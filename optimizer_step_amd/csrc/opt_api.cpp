@@ -191,7 +191,9 @@ struct Slot {
     void *host = nullptr;           // pinned staging copy
     size_t cap = 0;
     std::vector<unsigned char> content;
-    hipEvent_t ev = nullptr;
+    hipEvent_t ev = nullptr;        // after the last kernel that read the slot
+    hipEvent_t ready = nullptr;     // after the copy that filled it
+    hipStream_t upload_stream = nullptr;
     hipStream_t last_stream = nullptr;
     bool multi_stream = false;
     bool used = false;
@@ -227,6 +229,8 @@ int workspace(Workspace *&out)
         for (Slot &s : w.slots) {
             e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
             if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+            e = hipEventCreateWithFlags(&s.ready, hipEventDisableTiming);
+            if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
         }
         e = hipEventCreateWithFlags(&w.partials_ev, hipEventDisableTiming);
         if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
@@ -236,9 +240,14 @@ int workspace(Workspace *&out)
     return OPT_OK;
 }
 
-// Wait until no queued kernel still reads the slot.
+// Wait until neither the copy that filled the slot (which reads its pinned
+// staging buffer) nor a queued kernel that reads the slot is pending.
 int slot_quiesce(Slot &s)
 {
+    if (s.upload_stream || !s.content.empty()) {
+        hipError_t e = hipEventSynchronize(s.ready);
+        if (e != hipSuccess) return hip_fail(e, "waiting for a workspace copy");
+    }
     if (!s.used) return OPT_OK;
     hipError_t e = s.multi_stream ? hipDeviceSynchronize() : hipEventSynchronize(s.ev);
     if (e != hipSuccess) return hip_fail(e, "waiting for a workspace slot");
@@ -248,11 +257,17 @@ int slot_quiesce(Slot &s)
 }
 
 // Device copy of `blob`, reusing a slot that already holds the same bytes.
+// A slot filled on another stream is reused after that stream's copy: the
+// caller's stream waits on the copy's event (no wait on the filling stream).
 int upload(Workspace &w, const std::vector<unsigned char> &blob, hipStream_t st, Slot *&out)
 {
     ++w.tick;
     for (Slot &s : w.slots) {
         if (s.dev && s.content.size() == blob.size() && memcmp(s.content.data(), blob.data(), blob.size()) == 0) {
+            if (s.upload_stream != st) {
+                hipError_t e = hipStreamWaitEvent(st, s.ready, 0);
+                if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (tables)");
+            }
             s.tick = w.tick;
             out = &s;
             return OPT_OK;
@@ -279,6 +294,11 @@ int upload(Workspace &w, const std::vector<unsigned char> &blob, hipStream_t st,
         v->content.clear();
         return hip_fail(e, "hipMemcpyAsync (tables)");
     }
+    if ((e = hipEventRecord(v->ready, st)) != hipSuccess) {
+        v->content.clear();
+        return hip_fail(e, "hipEventRecord (tables)");
+    }
+    v->upload_stream = st;
     v->tick = w.tick;
     out = v;
     return OPT_OK;
@@ -744,6 +764,7 @@ int opt_shutdown(void)
             if (s.dev) (void)hipFree(s.dev);
             if (s.host) (void)hipHostFree(s.host);
             if (s.ev) (void)hipEventDestroy(s.ev);
+            if (s.ready) (void)hipEventDestroy(s.ready);
             s = Slot();
         }
         if (w.partials) (void)hipFree(w.partials);

@@ -238,6 +238,36 @@ def test_streams_other_than_the_default():
     compare(case, dev, ps, st)
 
 
+def test_steps_alternating_between_two_streams():
+    """The same tensor list stepped on two streams in turn, each ordered after
+    the other as a caller would: every call after the first finds the list's
+    tables already uploaded from the other stream (and the pre-pass partials
+    last written there), and the results are the oracle's."""
+    import torch
+    import optimizer_step_amd as osa
+    hp = dict(HP_ADAMW, max_unorm=1.0)
+    case = Case("adamw", "q8", [5000, 70_000], True, 4, hp)
+    ps, st, _ = case.run_oracle()
+    dev = case.alloc_gpu()
+    tl = osa.TensorList(dev)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for t in range(1, case.steps + 1):
+        s, other = streams[t % 2], streams[(t + 1) % 2]
+        s.wait_stream(other)
+        with torch.cuda.stream(s):
+            for k in range(len(case.sizes)):
+                dev[k]["g"].copy_(to_dev(case.grad(t, k)))
+            h = osa.hparams(step=t, seed=case.seed, qmap_signed=case.qs, qmap_unsigned=case.qu, **hp)
+            unorm = torch.empty(2 * len(case.sizes), dtype=torch.float64, device="cuda")
+            osa.opt_precondition_unorm("adamw", tl, "q8", h, unorm, stream=s)
+            osa.opt_step_adamw(tl, "q8", h, unorm, stream=s)
+            unorm.record_stream(s)
+    torch.cuda.synchronize()
+    compare(case, dev, ps, st)
+    states_bit_identical(case, dev, st)
+
+
 # ---------------------------------------------------------------------------
 # test hooks: the device functions the kernels use
 
