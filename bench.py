@@ -454,18 +454,25 @@ def main():
     ap.add_argument("--summarize-rows-trace", metavar="TRACE_DIR",
                     help="write profiles/bench_rows_kernel_stats.txt from a rocprofv3 run over all rows and exit")
     args = ap.parse_args()
+
+    # the commands the summaries record: the profiling runs that wrote the
+    # folders given (the trace run's bench line sits beside its folder)
+    def trace_cmd(d):
+        line = os.path.join(os.path.dirname(os.path.normpath(d)), "trace_bench.json")
+        return (f"rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o trace -- "
+                f"python bench.py --no-cpu > {line}")
+
+    def pmc_cmd(counter, d, name):
+        return (f"rocprofv3 --pmc {counter} --output-format csv -d {d} -o {name} -- "
+                "python bench.py --rows none --no-cpu --calibrate --steps 2 --warmup 1")
+
     if args.summarize_rows_trace:
-        summarize_rows_trace(args.summarize_rows_trace,
-                             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace "
-                             "-- python bench.py --no-cpu > gpurun_out/trace_bench.json")
+        summarize_rows_trace(args.summarize_rows_trace, trace_cmd(args.summarize_rows_trace))
         return
     if args.summarize_profiles:
-        base = "python bench.py --rows none --no-cpu --calibrate"
-        summarize_profiles(*args.summarize_profiles,
-                           cmd_trace="rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o trace -- "
-                                     "python bench.py --no-cpu > gpurun_out/trace_bench.json",
-                           cmd_fetch=f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o fetch -- {base} --steps 2 --warmup 1",
-                           cmd_write=f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o write -- {base} --steps 2 --warmup 1")
+        tdir, fdir, wdir = args.summarize_profiles
+        summarize_profiles(tdir, fdir, wdir, cmd_trace=trace_cmd(tdir), cmd_fetch=pmc_cmd("FETCH_SIZE", fdir, "fetch"),
+                           cmd_write=pmc_cmd("WRITE_SIZE", wdir, "write"))
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
