@@ -102,7 +102,8 @@ typedef enum {
  *            clamped to the largest finite value (448, 6, 7); they read back
  *            as value(code) * X.  A block whose A is 0 reads back as zeros,
  *            one whose A is NaN or infinite as NaN.
- *   numel    element count, >= 0 (0 is a no-op).
+ *   numel    element count, 0 <= numel <= 2^46 (0 is a no-op); index_base +
+ *            numel <= 2^60.
  * Alignment: p, g, s1, s2, s3 must be 16-byte aligned (any PyTorch allocation
  * is); absmax arrays 4-byte aligned.  Buffers of different tensors must not
  * overlap.  The tensor's position k in the list keys its stochastic rounding
@@ -243,7 +244,7 @@ int opt_precondition_unorm(int32_t optimizer, const opt_tensor *tensors, int64_t
  * poisoning the inf-norm as well as the 2-norm. */
 typedef struct {
     const void *g;      /* device, numel gradients in dtype, read      */
-    int64_t numel;      /* >= 0                                         */
+    int64_t numel;      /* 0 <= numel <= 2^46                           */
     int32_t dtype;      /* OPT_F32 or OPT_BF16                          */
     int32_t reserved;   /* 0                                            */
 } opt_grad;

@@ -64,6 +64,10 @@ int g_wgs_per_cu = 0;         // workgroups per compute unit (0: one per tile, o
 
 constexpr int kMaxDevices = 64;
 constexpr int kSlots = 16;
+// Size limits, far beyond any device's memory, that keep the host's chunk
+// arithmetic and the element indices of the random streams in range.
+constexpr int64_t kMaxNumel = (int64_t)1 << 46;
+constexpr int64_t kMaxIndex = (int64_t)1 << 60;
 constexpr uint32_t kMaxSearchWords = 15000;   // LDS budget of the search tables
 
 // ---------------------------------------------------------------------------
@@ -360,6 +364,9 @@ int check_hparams(const opt_hparams *hp, int fmt)
 // index_base and the stochastic-rounding tensor number of one record.
 int check_slice(const opt_tensor &x, int64_t k, int64_t align)
 {
+    if (x.numel > kMaxNumel) return fail(OPT_EINVAL, "tensor %lld: numel above 2^46", (long long)k);
+    if (x.index_base > kMaxIndex - x.numel)
+        return fail(OPT_EINVAL, "tensor %lld: index_base + numel above 2^60", (long long)k);
     if (x.index_base < 0 || x.index_base % align != 0)
         return fail(OPT_EINVAL, "tensor %lld: index_base must be >= 0 and a multiple of %lld", (long long)k,
                     (long long)align);
@@ -627,6 +634,7 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     for (int64_t k = 0; k < n; ++k) {
         const opt_grad &x = grads[k];
         if (x.numel < 0) return fail(OPT_EINVAL, "tensor %lld: numel < 0", (long long)k);
+        if (x.numel > kMaxNumel) return fail(OPT_EINVAL, "tensor %lld: numel above 2^46", (long long)k);
         if (x.dtype != OPT_F32 && x.dtype != OPT_BF16 && x.dtype != OPT_F16)
             return fail(OPT_EINVAL, "tensor %lld: unknown dtype %d", (long long)k, x.dtype);
         if (x.numel > 0 && !x.g) return fail(OPT_EINVAL, "tensor %lld: g is NULL", (long long)k);
@@ -734,6 +742,7 @@ int opt_round_cast(const float *x, void *out, int64_t n, int32_t out_dtype, int3
                    uint64_t offset, void *stream)
 {
     if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (n > kMaxNumel) return fail(OPT_EINVAL, "n above 2^46");
     if (out_dtype != OPT_BF16 && out_dtype != OPT_F16) return fail(OPT_EINVAL, "out_dtype must be OPT_BF16 or OPT_F16");
     if (stochastic != 0 && stochastic != 1) return fail(OPT_EINVAL, "stochastic must be 0 or 1");
     if (n == 0) return OPT_OK;

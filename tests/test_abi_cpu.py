@@ -16,6 +16,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 QS, QU = synth.codebook_signed(), synth.codebook_unsigned()
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0      # counts without initialising the device
+    except Exception:
+        return False
+
+
+# Calls that pass the argument checks go on to launch work on the made-up
+# device addresses these tests use, so such tests run only with no GPU.
+no_device = pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses would reach a kernel")
+
+
 @pytest.fixture(scope="module")
 def L():
     import optimizer_step_amd as osa
@@ -266,6 +279,7 @@ def test_round_cast_bad_arguments(L, args, status):
     assert L.lib().opt_round_cast(a["x"], a["out"], a["n"], a["dtype"], a["stochastic"], 0, 0, None) == status
 
 
+@no_device
 def test_p16_rules(L):
     hp = L.hparams(p_rounding=2)
     assert _call(L, "opt_step_adamw", _tensor(L), 0, hp) == -1
@@ -287,6 +301,25 @@ def test_one_state_argument_checks(L):
     assert lib.opt_step_1state(2, None, 0, 0, L.hparams(), None) == 0
 
 
+@no_device
+def test_size_limits(L):
+    """numel above 2^46, or index_base + numel above 2^60, is refused before
+    any work (the host's chunk arithmetic and the stream indices stay in
+    range); sizes at the limits pass the checks and go on to need a GPU."""
+    hp = L.hparams()
+    for numel, base, bad in ((1 << 46, 0, False), ((1 << 46) + 4, 0, True),
+                             (4096, (1 << 60) - 4096, False), (4096, (1 << 60) - 4092, True)):
+        t = L.OptTensor(4096, 4096, 8192, 12288, None, None, None, None, numel, 0, 0)
+        t.index_base = base
+        rc = _call(L, "opt_step_adamw", [t], 0, hp)
+        assert (rc == -1) == bad, (numel, base, rc, L.opt_last_error())
+    g = L.OptGrad(4096, (1 << 46) + 1, 0, 0)
+    arr = (L.OptGrad * 1)(g)
+    assert L.lib().opt_grad_norm(arr, 1, 8192, 0.0, 2, None, None) == -1
+    assert L.lib().opt_round_cast(4096, 8192, (1 << 46) + 1, 1, 0, 0, 0, None) == -1
+
+
+@no_device
 def test_index_base_and_stream_tensor_checks(L):
     """index_base must be >= 0 and a multiple of 4 (256 for the blockwise
     formats); sr_tensor_set must be 0 or 1, and sr_tensor >= 0 when set.
