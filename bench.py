@@ -414,6 +414,71 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd_trace, cmd_fetch, cm
     print(open(os.path.join(ROOT, "profiles", "step_ew_adamw_llama7b_counters.txt")).read())
 
 
+OUR_KERNELS = ("step_", "gnorm_", "unorm_", "norm_group", "round_cast")
+
+
+def summarize_rows_counters(base):
+    """profiles/bench_rows_counters.txt: HBM bytes per step of each bench row
+    from two rocprofv3 runs per row (--pmc FETCH_SIZE, then WRITE_SIZE; KiB
+    per dispatch), scaled by the same run's calibration copy, against the
+    row's algorithmic bytes per step.  A row's kernels are this library's
+    kernels in its run (the rows run one per process), each dispatched once
+    per step."""
+    import csv
+    import glob
+    import statistics
+    kib = 1024.0
+    cal_bytes = 4.0 * (1 << 30)
+    lines = []
+    for rdir in sorted(glob.glob(os.path.join(base, "*", ""))):
+        row = os.path.basename(os.path.normpath(rdir))
+        try:
+            info = json.loads(open(os.path.join(rdir, "bench.json")).read().strip().splitlines()[-1])["rows"][0]
+        except (OSError, ValueError, IndexError, KeyError):
+            continue
+        per = {}
+        for counter, sub_ in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            files = glob.glob(os.path.join(rdir, sub_, "**", "*counter_collection.csv"), recursive=True)
+            if not files:
+                break
+            vals = {}
+            for r in csv.DictReader(open(files[0])):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].replace("void ", "").replace("optstep::", "")
+                name = name[:name.index(">(") + 1] if ">(" in name else name.split("(")[0]
+                vals.setdefault(name, []).append(float(r["Counter_Value"]))
+            cal = [v for k, v in vals.items() if CALIB_KERNEL in k]
+            if not cal:
+                break
+            scale = cal_bytes / (statistics.median(cal[0]) * kib)
+            per[counter] = {k: statistics.median(v) * kib * scale for k, v in vals.items()
+                            if k.startswith(OUR_KERNELS)}
+        if len(per) != 2:
+            continue
+        rd, wr = sum(per["FETCH_SIZE"].values()), sum(per["WRITE_SIZE"].values())
+        alg = info["bytes_per_element"] * info["elements"]
+        kernels = ", ".join(sorted(set(per["FETCH_SIZE"]) | set(per["WRITE_SIZE"])))
+        lines.append((row, info["elements"], info["bytes_per_element"], alg, rd, wr, kernels))
+    if not lines:
+        raise SystemExit(f"no complete row under {base}")
+    with open(os.path.join(ROOT, "profiles", "bench_rows_counters.txt"), "w") as f:
+        f.write("rocprofv3 HBM byte counters per bench row: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each\n"
+                "scaled by what it reads for the calibration copy in the same run (2^30 fp32 read + written),\n"
+                "summed over this library's kernels of one step, against the row's algorithmic bytes per step.\n"
+                f"commands, per row R (each a process of its own):\n"
+                f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d {base}/R/fetch -o c -- python bench.py "
+                "--rows-only --rows R --no-cpu --calibrate --steps 2 --warmup 1 > " f"{base}/R/bench.json\n"
+                f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d {base}/R/write -o c -- python bench.py "
+                "--rows-only --rows R --no-cpu --calibrate --steps 2 --warmup 1\n\n")
+        f.write(f"{'row':26s} {'elements':>14s} {'B/elem':>8s} {'algorithmic':>12s} {'read':>12s} {'written':>12s} "
+                f"{'ratio':>7s}  kernels\n")
+        for row, n, bpe, alg, rd, wr, kernels in lines:
+            f.write(f"{row:26s} {n:14,d} {bpe:8.4g} {alg:12.4e} {rd:12.4e} {wr:12.4e} {(rd + wr) / alg:7.4f}  "
+                    f"{kernels}\n")
+    print(f"wrote profiles/bench_rows_counters.txt ({len(lines)} rows)")
+
+
 def summarize_rows_trace(trace_dir, cmd):
     """profiles/bench_rows_kernel_stats.txt: per-kernel time statistics of a
     rocprofv3 --kernel-trace --stats run over every bench row."""
@@ -451,6 +516,12 @@ def main():
                          "HBM counters scale the step kernel's")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from three rocprofv3 output folders and exit")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time only the rows given by --rows (no headline, no CPU leg) and print them as one "
+                         "JSON line; for per-row profiling runs")
+    ap.add_argument("--summarize-rows-counters", metavar="DIR",
+                    help="write profiles/bench_rows_counters.txt from per-row rocprofv3 counter runs under DIR "
+                         "(DIR/<row>/{fetch,write}/ and DIR/<row>/bench.json) and exit")
     ap.add_argument("--summarize-rows-trace", metavar="TRACE_DIR",
                     help="write profiles/bench_rows_kernel_stats.txt from a rocprofv3 run over all rows and exit")
     args = ap.parse_args()
@@ -469,6 +540,9 @@ def main():
     if args.summarize_rows_trace:
         summarize_rows_trace(args.summarize_rows_trace, trace_cmd(args.summarize_rows_trace))
         return
+    if args.summarize_rows_counters:
+        summarize_rows_counters(args.summarize_rows_counters)
+        return
     if args.summarize_profiles:
         tdir, fdir, wdir = args.summarize_profiles
         summarize_profiles(tdir, fdir, wdir, cmd_trace=trace_cmd(tdir), cmd_fetch=pmc_cmd("FETCH_SIZE", fdir, "fetch"),
@@ -478,6 +552,19 @@ def main():
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the step shards with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+
+    if args.rows_only:
+        import torch
+        import optimizer_step_amd as osa
+        import synth
+        osa.lib()
+        rows = [time_workload(name, max(args.steps, 20), max(args.warmup, 5), torch, osa, synth)
+                for name in (r for r in args.rows.split(",") if r and r not in ("all", "none"))]
+        out = {"rows": rows}
+        if args.calibrate:
+            out["calibration"] = calibrate(torch, osa)
+        print(json.dumps(out), flush=True)
+        return
 
     # the CPU baseline first: its workers are forked, which must happen
     # before this process initialises the GPU
