@@ -323,7 +323,10 @@ int opt_debug_quantize_host(const float *qmap, int32_t is_signed, const float *x
 
 /* Host only: out[i] = a[i] / b[i] by the kernels' division with a reused
  * reciprocal (two residual corrections of a[i] * RN(1/b[i])), on the CPU.
- * Each b[i] must have |b|, 1/|b| in [2^-124, 2^124] (OPT_EINVAL otherwise). */
+ * Each b[i] must have 2^-124 <= |b[i]| <= 2^26, the range in which the
+ * kernels take this division (OPT_EINVAL otherwise); the quotient is the
+ * correctly rounded one when |a[i]| <= |b[i]| and a[i] is 0 or at least
+ * 2^-100 in magnitude. */
 int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n);
 
 /* Calibration: dst[j][i] = sum_k src[k][i] for i < n over fp32 device arrays

@@ -85,7 +85,7 @@ static float bf(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
 // binary64) that x lies strictly above, i.e. the count of tau_i <= x with
 // tau_i the smallest float above t_i: the nearest entry, ties to the lower
 // index.  The table splits [lo, 1] into buckets of 2^shift ulps (one sign at
-// a time) holding at most one tau each, so one comparison finishes the code.
+// a time) holding at most one tau each, so one add finishes the code.
 // The comparison is folded into the entry (opt_plan.h): with base taus at or
 // below the bucket and the bucket's tau at in-bucket key K, x > 0 takes
 // E = ((base + 1) << 24) - K, so E + k carries into the top byte iff k >= K;
