@@ -133,7 +133,9 @@ def device_grads(n, device, std, t, k=0, bf16=False, mask_scale=None):
     device_normal_(g, GRAD_SEED, std, k, t)
     if mask_scale is not None:
         frac, factor = mask_scale
-        g[device_mask(n, device, frac, k)] *= factor
+        # elementwise select (the same fp32 product as indexing in place);
+        # boolean-mask indexing fails past 2^32 elements
+        g = torch.where(device_mask(n, device, frac, k), g * factor, g)
     return g.to(torch.bfloat16) if bf16 else g
 
 
