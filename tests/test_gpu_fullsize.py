@@ -407,3 +407,54 @@ def test_round_cast_one_billion_values():
     assert bool((inner | outer).all())
     del x, out, xb, lo, wide
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["f32", "q8"])
+def test_one_tensor_past_2_to_32(fmt):
+    """One tensor of 2^32 + 1027 elements (a ragged last block), bf16
+    gradients, 2 steps: elements and whole 8-bit blocks around 2^31 and 2^32
+    and in the tail against the oracle, so that no element offset, block
+    index or stream index wraps at 32 bits."""
+    import torch
+    import optimizer_step_amd as osa
+    n = (1 << 32) + 1027
+    hp = dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)
+    qs, qu = synth.codebook_signed(), synth.codebook_unsigned()
+    print(f"one tensor of {n} elements, {fmt} states", flush=True)
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, 0.02)
+    st = _flat_states(fmt, n, "adamw", qs if fmt == "q8" else None, qu if fmt == "q8" else None)
+    nb = (n + 255) // 256
+    blocks = np.array([0, (1 << 23) - 1, 1 << 23, (1 << 24) - 1, nb - 2, nb - 1])   # 2^31 and 2^32 edges
+    idx = np.concatenate([np.arange(256 * b, min(256 * (b + 1), n)) for b in blocks])
+    p0 = _gather(P, idx)
+    g_hist = []
+    for t in (1, 2):
+        G = synth.device_grads(n, "cuda", 1e-3, t, bf16=True)
+        tl = osa.TensorList(_views(P, G, st, [n], fmt))
+        osa.opt_step_adamw(tl, fmt, osa.hparams(step=t, qmap_signed=qs, qmap_unsigned=qu, **hp))
+        g_hist.append(_gather(G, idx))
+        del G, tl
+    torch.cuda.synchronize()
+    gp = _gather(P, idx)
+    pos = 0
+    for b in blocks:
+        m = min(256 * (b + 1), n) - 256 * b
+        sl = slice(pos, pos + m)
+        p = p0[sl].copy()
+        s = oracle.state_zeros(fmt, m, "adamw", qs, qu)
+        for t in (1, 2):
+            oracle.step("adamw", fmt, oracle.make_hp(step=t, index_base=256 * int(b), **hp), p, g_hist[t - 1][sl],
+                        qs=qs, qu=qu, **s)
+        assert fp32_close(gp[sl], p), (fmt, b)
+        if fmt == "q8":
+            assert np.array_equal(_gather(st["s1"], idx[sl]), s["s1"]), (fmt, b)
+            assert np.array_equal(_gather(st["s2"], idx[sl]), s["s2"]), (fmt, b)
+            assert nan_equal_bits(_gather(st["absmax1"], np.array([b])), s["a1"]), (fmt, b)
+            assert nan_equal_bits(_gather(st["absmax2"], np.array([b])), s["a2"]), (fmt, b)
+        else:
+            assert fp32_close(_gather(st["s1"], idx[sl]), s["s1"]), (fmt, b)
+            assert fp32_close(_gather(st["s2"], idx[sl]), s["s2"]), (fmt, b)
+        pos += m
+    del P, st
+    torch.cuda.empty_cache()
