@@ -458,3 +458,48 @@ def test_one_tensor_past_2_to_32(fmt):
         pos += m
     del P, st
     torch.cuda.empty_cache()
+
+
+def test_gradient_norm_one_tensor_past_2_to_32():
+    """One bf16 gradient of 2^32 + 5 elements: 2^-10 everywhere but 1.0 in
+    the last five, so the sum of squares is exactly 2^32 * 2^-20 + 5 = 4101
+    and the maximum 1.0; a unit index that wrapped at 32 bits would drop or
+    repeat the tail."""
+    import torch
+    import optimizer_step_amd as osa
+    n = (1 << 32) + 5
+    G = torch.full((n,), 2.0 ** -10, dtype=torch.bfloat16, device="cuda")
+    G[1 << 32:] = 1.0
+    out = torch.empty(4, dtype=torch.float64, device="cuda")
+    osa.opt_grad_norm([G], out)
+    o = out.cpu().numpy()
+    assert o[0] == 4101.0 and o[2] == 4101.0, o
+    assert o[1] == 1.0 and o[3] == 1.0, o
+    del G
+    torch.cuda.empty_cache()
+
+
+def test_round_cast_past_2_to_34():
+    """The stochastic BF16 cast of 2^34 + 4099 values: the element index
+    enters the Philox counter as (j >> 2) low word and j >> 34, so values past
+    2^34 use the second word; sampled outputs around 2^32, 2^34 and the tail
+    against the oracle's rounding with the words formed from that layout."""
+    import torch
+    import optimizer_step_amd as osa
+    n = (1 << 34) + 4099
+    seed, offset = synth.SR_SEED, 0x0000_0005_0000_0009
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(x, synth.PARAM_SEED, 1.0)
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    osa.opt_round_cast(x, out, True, seed, offset)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.arange(0, 8), (1 << 32) + np.arange(-8, 8), (1 << 34) + np.arange(-8, 8),
+                                    np.arange(n - 13, n)]))
+    xs, got = _gather(x, idx), _gather(out, idx)
+    for j, xj, gj in zip(idx, xs, got):
+        q = int(j) >> 2
+        w = oracle.philox([q & 0xFFFFFFFF, q >> 32, offset & 0xFFFFFFFF, offset >> 32],
+                          [seed & 0xFFFFFFFF, seed >> 32])
+        assert int(gj) == oracle.bf16_sr(xj, int(w[int(j) & 3]) & 0xFFFF), j
+    del x, out
+    torch.cuda.empty_cache()
