@@ -38,8 +38,10 @@
  * demand and releases in opt_shutdown.  Calls from several host threads are
  * serialized inside the library.
  *
- * Errors.  Every entry point returns OPT_OK (0) or a negative status and, on
- * error, enqueues nothing; opt_last_error() then describes the failure.
+ * Errors.  Every entry point returns OPT_OK (0) or a negative status, and
+ * opt_last_error() then describes the failure.  Invalid arguments are found
+ * before anything is enqueued.  A HIP error while enqueuing (OPT_EHIP) may
+ * leave the launches of earlier storage buckets of the same call queued.
  */
 #ifndef OPT_STEP_H
 #define OPT_STEP_H
