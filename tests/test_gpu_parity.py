@@ -268,6 +268,51 @@ def test_steps_alternating_between_two_streams():
     states_bit_identical(case, dev, st)
 
 
+def test_two_host_threads_two_streams():
+    """Two host threads step two different tensor lists at the same time, each
+    on a stream of its own (8-bit states with the pre-pass on one, BF16-SR on
+    the other): the calls serialize inside the library, each list keeps its
+    own tables, and both results are the oracle's."""
+    import threading
+    import torch
+    import optimizer_step_amd as osa
+    cases = [Case("adamw", "q8", [5000, 70_000], True, 4, dict(HP_ADAMW, max_unorm=1.0)),
+             Case("ademamix", "bf16_sr", [33_333, 1024], False, 4, HP_ADEMAMIX)]
+    want = [c.run_oracle() for c in cases]
+    devs = [c.alloc_gpu() for c in cases]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(c, dev):
+        try:
+            s = torch.cuda.Stream()
+            tl = osa.TensorList(dev)
+            fn = osa.opt_step_adamw if c.opt == "adamw" else osa.opt_step_ademamix
+            with torch.cuda.stream(s):
+                for t in range(1, c.steps + 1):
+                    for k in range(len(c.sizes)):
+                        dev[k]["g"].copy_(to_dev(c.grad(t, k)))
+                    h = osa.hparams(step=t, seed=c.seed, qmap_signed=c.qs, qmap_unsigned=c.qu, **c.hp)
+                    unorm = None
+                    if c.hp.get("max_unorm", 0.0) > 0:
+                        unorm = torch.empty(2 * len(c.sizes), dtype=torch.float64, device="cuda")
+                        osa.opt_precondition_unorm(c.opt, tl, c.fmt, h, unorm, stream=s)
+                    fn(tl, c.fmt, h, unorm, stream=s)
+                s.synchronize()
+        except Exception as e:     # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(c, d)) for c, d in zip(cases, devs)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads) and not errors, errors
+    for c, dev, (ps, st, _) in zip(cases, devs, want):
+        compare(c, dev, ps, st)
+        states_bit_identical(c, dev, st)
+
+
 # ---------------------------------------------------------------------------
 # test hooks: the device functions the kernels use
 
