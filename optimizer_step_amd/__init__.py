@@ -150,6 +150,35 @@ class TensorList:
                 p.numel(), _dtype_code(p), _dtype_code(d["g"]), int(d.get("index_base", 0)),
                 int(d.get("sr_tensor", 0)), 1 if d.get("sr_tensor") is not None else 0)
         self.n = len(self.keep)
+        self._checked = set()
+
+    def check(self, state_fmt, nstates):
+        """Raise ValueError unless every tensor given is a contiguous CUDA
+        tensor, g has p's element count, and each of the first nstates states
+        (and, for the blockwise formats, its absmax array) holds at least the
+        bytes the format needs: the library sees only pointers, so a short or
+        strided buffer would be read out of bounds.  Checked once per format."""
+        key = (state_fmt, nstates)
+        if key in self._checked:
+            return
+        per = {STATE_F32: 8, STATE_BF16_RN: 4, STATE_BF16_SR: 4}.get(state_fmt, 2)   # half-bytes per element
+        if state_fmt in (STATE_FP4_RN, STATE_FP4_SR):
+            per = 1
+        for i, d in enumerate(self.keep):
+            n = d["p"].numel()
+            for name, t in d.items():
+                if hasattr(t, "is_cuda") and (not t.is_cuda or not t.is_contiguous()):
+                    raise ValueError(f"tensor {i}: {name} must be a contiguous CUDA tensor")
+            if d["g"].numel() != n:
+                raise ValueError(f"tensor {i}: g has {d['g'].numel()} elements, p has {n}")
+            for j in range(1, nstates + 1):
+                s = d.get(f"s{j}")
+                if s is not None and 2 * s.numel() * s.element_size() < per * n:
+                    raise ValueError(f"tensor {i}: s{j} is shorter than {n} elements of this state format")
+                a = d.get(f"absmax{j}")
+                if state_fmt in BLOCKED and a is not None and a.numel() * a.element_size() < 4 * ((n + BLOCK - 1) // BLOCK):
+                    raise ValueError(f"tensor {i}: absmax{j} holds fewer than ceil({n}/256) floats")
+        self._checked.add(key)
 
 
 def _as_list(tensors):
@@ -188,30 +217,45 @@ def opt_grad_norm(grads, out, max_norm=0.0, norm_type=2, coef_out=None, stream=N
                                       _ptr(coef_out), _stream(stream)))
 
 
+def _norm_buffer(t, n):
+    """The per-tensor {sum u^2, sum p^2} buffer: CUDA float64, 2n entries."""
+    if t is not None and (not t.is_cuda or not t.is_contiguous() or t.element_size() != 8 or t.numel() < 2 * n):
+        raise ValueError(f"the update-norm buffer must be a contiguous CUDA float64 tensor of >= {2 * n} entries")
+    return _ptr(t)
+
+
 def opt_step_adamw(tensors, state_fmt, hp, unorm=None, stream=None):
     tl = _as_list(tensors)
-    return _check(lib().opt_step_adamw(tl.arr, tl.n, FORMATS.get(state_fmt, state_fmt),
-                                       ctypes.byref(hp), _ptr(unorm), _stream(stream)))
+    fmt = FORMATS.get(state_fmt, state_fmt)
+    tl.check(fmt, 2)
+    return _check(lib().opt_step_adamw(tl.arr, tl.n, fmt, ctypes.byref(hp), _norm_buffer(unorm, tl.n),
+                                       _stream(stream)))
 
 
 def opt_step_ademamix(tensors, state_fmt, hp, unorm=None, stream=None):
     tl = _as_list(tensors)
-    return _check(lib().opt_step_ademamix(tl.arr, tl.n, FORMATS.get(state_fmt, state_fmt),
-                                          ctypes.byref(hp), _ptr(unorm), _stream(stream)))
+    fmt = FORMATS.get(state_fmt, state_fmt)
+    tl.check(fmt, 3)
+    return _check(lib().opt_step_ademamix(tl.arr, tl.n, fmt, ctypes.byref(hp), _norm_buffer(unorm, tl.n),
+                                          _stream(stream)))
 
 
 def opt_step_1state(optimizer, tensors, state_fmt, hp, stream=None):
     """One momentum / RMSprop / Adagrad / Lion step; tensors need p, g, s1."""
     tl = _as_list(tensors)
-    return _check(lib().opt_step_1state(ONE_STATE.get(optimizer, optimizer), tl.arr, tl.n,
-                                        FORMATS.get(state_fmt, state_fmt), ctypes.byref(hp), _stream(stream)))
+    fmt = FORMATS.get(state_fmt, state_fmt)
+    tl.check(fmt, 1)
+    return _check(lib().opt_step_1state(ONE_STATE.get(optimizer, optimizer), tl.arr, tl.n, fmt, ctypes.byref(hp),
+                                        _stream(stream)))
 
 
 def opt_precondition_unorm(optimizer, tensors, state_fmt, hp, unorm_out, stream=None):
     tl = _as_list(tensors)
-    return _check(lib().opt_precondition_unorm(OPTIMIZERS.get(optimizer, optimizer), tl.arr, tl.n,
-                                               FORMATS.get(state_fmt, state_fmt), ctypes.byref(hp),
-                                               _ptr(unorm_out), _stream(stream)))
+    fmt = FORMATS.get(state_fmt, state_fmt)
+    opt = OPTIMIZERS.get(optimizer, optimizer)
+    tl.check(fmt, 3 if opt == ADEMAMIX else 2)
+    return _check(lib().opt_precondition_unorm(opt, tl.arr, tl.n, fmt, ctypes.byref(hp),
+                                               _norm_buffer(unorm_out, tl.n), _stream(stream)))
 
 
 def opt_last_error():

@@ -301,6 +301,15 @@ def test_one_state_argument_checks(L):
     assert lib.opt_step_1state(2, None, 0, 0, L.hparams(), None) == 0
 
 
+def test_binding_refuses_host_tensors(L):
+    """The binding checks what the library cannot see: tensors that are not
+    on the GPU are refused before any call."""
+    import torch
+    t = L.TensorList([{"p": torch.zeros(16), "g": torch.zeros(16), "s1": torch.zeros(16), "s2": torch.zeros(16)}])
+    with pytest.raises(ValueError):
+        t.check(L.STATE_F32, 2)
+
+
 @no_device
 def test_size_limits(L):
     """numel above 2^46, or index_base + numel above 2^60, is refused before

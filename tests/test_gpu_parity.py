@@ -268,6 +268,33 @@ def test_steps_alternating_between_two_streams():
     states_bit_identical(case, dev, st)
 
 
+def test_binding_refuses_short_or_strided_buffers():
+    """The library sees pointers only, so the binding refuses buffers it
+    would read out of bounds: a strided view, a state shorter than the
+    format needs, a short absmax array, a short update-norm buffer."""
+    import torch
+    import optimizer_step_amd as osa
+    n = 1000
+    f = lambda k, dt=torch.float32: torch.zeros(k, dtype=dt, device="cuda")
+    ok = {"p": f(n), "g": f(n), "s1": f(n), "s2": f(n)}
+    osa.opt_step_adamw([ok], "f32", osa.hparams())
+    bad = [dict(ok, p=f(2 * n)[::2]), dict(ok, s2=f(n - 1)), dict(ok, g=f(n + 4))]
+    for d in bad:
+        with pytest.raises(ValueError):
+            osa.opt_step_adamw([d], "f32", osa.hparams())
+    fp4 = {"p": f(n), "g": f(n), "s1": f(n // 2, torch.uint8), "s2": f(n // 2 - 1, torch.uint8),
+           "absmax1": f(4), "absmax2": f(4)}
+    with pytest.raises(ValueError):
+        osa.opt_step_adamw([fp4], "fp4_rn", osa.hparams())
+    fp4["s2"] = f(n // 2, torch.uint8)
+    fp4["absmax2"] = f(3)
+    with pytest.raises(ValueError):
+        osa.opt_step_adamw([fp4], "fp4_rn", osa.hparams())
+    with pytest.raises(ValueError):
+        osa.opt_precondition_unorm("adamw", [ok], "f32", osa.hparams(max_unorm=1.0), f(1, torch.float64))
+    torch.cuda.synchronize()
+
+
 def test_two_host_threads_two_streams():
     """Two host threads step two different tensor lists at the same time, each
     on a stream of its own (8-bit states with the pre-pass on one, BF16-SR on
