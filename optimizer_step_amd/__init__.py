@@ -210,11 +210,22 @@ def opt_grad_norm(grads, out, max_norm=0.0, norm_type=2, coef_out=None, stream=N
     """Norms of a list of CUDA gradient tensors into out (CUDA float64 tensor
     of 2 + 2n): totals then per-tensor {sum g^2, max |g|}; optionally the
     clipping coefficient into coef_out (CUDA float32 tensor of 1)."""
+    _device_buffer(out, 8, 2 + 2 * len(grads), "out")
+    _device_buffer(coef_out, 4, 1, "coef_out")
     arr = (OptGrad * max(1, len(grads)))()
     for i, g in enumerate(grads):
+        _device_buffer(g, g.element_size(), g.numel(), f"gradient {i}")
         arr[i] = OptGrad(_ptr(g), g.numel(), _dtype_code(g), 0)
     return _check(lib().opt_grad_norm(arr, len(grads), _ptr(out), float(max_norm), int(norm_type),
                                       _ptr(coef_out), _stream(stream)))
+
+
+def _device_buffer(t, itemsize, count, what):
+    """Raise ValueError unless t (if given) is a contiguous CUDA tensor of
+    `itemsize`-byte elements holding at least `count` of them."""
+    if t is not None and (not t.is_cuda or not t.is_contiguous() or t.element_size() != itemsize
+                          or t.numel() < count):
+        raise ValueError(f"{what} must be a contiguous CUDA tensor of >= {count} {itemsize}-byte elements")
 
 
 def _norm_buffer(t, n):
@@ -319,6 +330,8 @@ def opt_debug_stream(srcs, dsts, stream=None):
 def opt_round_cast(x, out, stochastic=False, seed=0, offset=0, stream=None):
     """x (CUDA float32) -> out (CUDA bfloat16 or float16), nearest-even or
     stochastic."""
+    _device_buffer(x, 4, x.numel(), "x")
+    _device_buffer(out, 2, x.numel(), "out")
     return _check(lib().opt_round_cast(_ptr(x), _ptr(out), x.numel(), _dtype_code(out), 1 if stochastic else 0,
                                        int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), _stream(stream)))
 
