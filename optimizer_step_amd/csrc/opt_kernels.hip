@@ -230,15 +230,21 @@ __device__ __forceinline__ void gnorm_store(const StepArgs &a, int64_t slot, int
 }
 
 #ifndef OPT_GN_UNITS
-#define OPT_GN_UNITS 4
+#define OPT_GN_UNITS 2
+#endif
+#ifndef OPT_GN_WAVES
+#define OPT_GN_WAVES 8
 #endif
 // One workgroup per tile of kGnTile gradient elements: kGnUnits partial units
-// of 1024 elements per wave.
+// of 1024 elements per wave (16 KB of bf16 per workgroup), held to OPT_GN_WAVES
+// waves per SIMD (56-64 registers, no spills).  A read-only stream wants bytes
+// in flight: on the 290-tensor bf16 list this reads at 6.34-6.45 TB/s,
+// against 6.19-6.25 with four units and no cap (92 registers, 5 waves).
 constexpr int kGnUnits = OPT_GN_UNITS;
 constexpr int64_t kGnTile = (int64_t)kWaves * kGnUnits * kUTile;
-
+#define OPT_GN_ATTR __attribute__((amdgpu_waves_per_eu(OPT_GN_WAVES)))
 template <int GD>
-__global__ __launch_bounds__(kThreads) void gnorm_partials_kernel(const DevTensor *__restrict__ tens,
+__global__ __launch_bounds__(kThreads) OPT_GN_ATTR void gnorm_partials_kernel(const DevTensor *__restrict__ tens,
                                                                   const int32_t *__restrict__ ctab,
                                                                   StepArgs a)
 {
