@@ -268,6 +268,32 @@ def test_steps_alternating_between_two_streams():
     states_bit_identical(case, dev, st)
 
 
+def test_refused_call_leaves_everything_unchanged():
+    """An argument the library refuses (here a codebook too dense for its
+    lookup table) returns an error before anything is enqueued: p and the
+    states keep their bits, and the next valid call steps as usual."""
+    import torch
+    import optimizer_step_amd as osa
+    case = Case("adamw", "q8", [3000], True, 1, HP_ADAMW)
+    dev = case.alloc_gpu()
+    dev[0]["g"].copy_(to_dev(case.grad(1, 0)))
+    before = {k: v.clone() for k, v in dev[0].items()}
+    dense = np.linspace(-1, 1, 256).astype(np.float32)
+    dense[200] = np.nextafter(dense[201], np.float32(-1))
+    dense[199] = np.nextafter(dense[200], np.float32(-1))
+    with pytest.raises(osa.OptError) as e:
+        osa.opt_step_adamw(osa.TensorList(dev), "q8",
+                           osa.hparams(step=1, qmap_signed=dense, qmap_unsigned=case.qu, **HP_ADAMW))
+    assert e.value.status == osa.OPT_EUNSUPPORTED
+    torch.cuda.synchronize()
+    for k, v in dev[0].items():
+        assert torch.equal(v.view(torch.uint8) if v.dtype != torch.uint8 else v,
+                           before[k].view(torch.uint8) if v.dtype != torch.uint8 else before[k]), k
+    ps, st, _ = case.run_oracle()
+    dev2, _ = case.run_gpu(dev=dev)
+    compare(case, dev2, ps, st)
+
+
 def test_binding_refuses_short_or_strided_buffers():
     """The library sees pointers only, so the binding refuses buffers it
     would read out of bounds: a strided view, a state shorter than the
