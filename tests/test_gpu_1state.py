@@ -38,26 +38,30 @@ def _grad(n, t, k, gd, zeros=False):
     return g.astype(np.float16) if gd == "f16" else g
 
 
-def _run_1s(name, fmt, gds, steps, hp, zeros=False):
+def _run_1s(name, fmt, gds, steps, hp, zeros=False, sizes=SIZES, grad=None, seed=synth.SR_SEED):
+    """Steps the list of `sizes` on both sides; grad(n, t, k, gd) overrides
+    the gradients (default: normal draws, with a moving fifth of zeros if
+    `zeros`)."""
     import torch
     import optimizer_step_amd as osa
-    ps = [synth.params(n, k, std=0.5) for k, n in enumerate(SIZES)]
+    gfun = grad or (lambda n, t, k, gd: _grad(n, t, k, gd, zeros))
+    ps = [synth.params(n, k, std=0.5) for k, n in enumerate(sizes)]
     p0 = [p.copy() for p in ps]
-    ss = [np.zeros(n, np.float32 if fmt == "f32" else np.uint16) for n in SIZES]
+    ss = [np.zeros(n, np.float32 if fmt == "f32" else np.uint16) for n in sizes]
     for t in range(1, steps + 1):
-        for k, n in enumerate(SIZES):
-            h = oracle.make_hp(step=t, seed=synth.SR_SEED, tensor_index=k, **hp)
-            oracle.step_1state(name, fmt, h, ps[k], _grad(n, t, k, gds[k], zeros), ss[k])
+        for k, n in enumerate(sizes):
+            h = oracle.make_hp(step=t, seed=seed, tensor_index=k, **hp)
+            oracle.step_1state(name, fmt, h, ps[k], gfun(n, t, k, gds[k]), ss[k])
     dev = []
-    for k, n in enumerate(SIZES):
-        d = {"p": to_dev(p0[k].copy()), "g": to_dev(_grad(n, 1, k, gds[k], zeros))}
+    for k, n in enumerate(sizes):
+        d = {"p": to_dev(p0[k].copy()), "g": to_dev(gfun(n, 1, k, gds[k]))}
         d["s1"] = torch.zeros(n, dtype=torch.float32 if fmt == "f32" else torch.bfloat16, device="cuda")
         dev.append(d)
     tl = osa.TensorList(dev)
     for t in range(1, steps + 1):
-        for k, n in enumerate(SIZES):
-            dev[k]["g"].copy_(to_dev(_grad(n, t, k, gds[k], zeros)))
-        osa.opt_step_1state(name, tl, fmt, osa.hparams(step=t, seed=synth.SR_SEED, **hp))
+        for k, n in enumerate(sizes):
+            dev[k]["g"].copy_(to_dev(gfun(n, t, k, gds[k])))
+        osa.opt_step_1state(name, tl, fmt, osa.hparams(step=t, seed=seed, **hp))
     torch.cuda.synchronize()
     return ps, ss, dev
 

@@ -133,3 +133,133 @@ def test_sweep_covers_every_format_and_feature():
     assert any(c["t0"] for c in cases)
     assert any(0 in c["sizes"] for c in cases)
     assert any(c["geometry"] != (32768, 0) for c in cases)
+
+
+# ---------------------------------------------------------------------------
+# 16-bit parameters and the one-state optimizers
+
+P16_CASES = 48
+ONE_STATE_CASES = 48
+GRAD_DTYPES = ["f32", "bf16", "f16"]
+
+
+def _features(rng, hp):
+    if rng.random() < 0.3:
+        hp["skip_zeros"] = True
+    if rng.random() < 0.3:
+        hp["reset_interval"] = int(rng.integers(2, 4))
+    return float(rng.choice([0.0, 0.05, 0.3]))
+
+
+def _sizes(rng, cap=MAX_TOTAL):
+    sizes = []
+    for _ in range(int(rng.integers(1, 6))):
+        n = int(SIZE_POOL[int(rng.integers(len(SIZE_POOL)))])
+        if sum(sizes) + n <= cap:
+            sizes.append(n)
+    return sizes
+
+
+def draw_p16(i):
+    """A two-state step on BF16 / FP16 parameters, nearest or stochastic."""
+    rng = np.random.default_rng([0x9161, i])
+    opt = ["adamw", "ademamix"][int(rng.integers(2))]
+    fmt = FORMATS[i % len(FORMATS)]
+    sizes = _sizes(rng)
+    hp = dict(lr=float(10.0 ** rng.uniform(-4, -1.5)), weight_decay=float(rng.choice([0.0, 0.01, 0.1])),
+              beta1=float(rng.uniform(0.8, 0.95)), beta2=float(rng.choice([0.99, 0.999])))
+    if opt == "ademamix":
+        hp.update(beta3=float(rng.choice([0.999, 0.9999])), alpha=float(rng.uniform(2.0, 8.0)))
+    if rng.random() < 0.3:
+        hp["max_unorm"] = float(rng.choice([0.5, 1.0]))
+    zero_frac = _features(rng, hp)
+    return dict(opt=opt, fmt=fmt, sizes=sizes, hp=hp, zero_frac=zero_frac,
+                pdt=int(rng.choice([oracle.P_BF16, oracle.P_F16])), p_sr=bool(rng.integers(2)),
+                gds=[GRAD_DTYPES[int(j)] for j in rng.integers(0, 3, len(sizes))],
+                steps=int(rng.integers(2, 5)), seed=int(rng.integers(1, 2**63)))
+
+
+def draw_1s(i):
+    """A momentum / RMSprop / Adagrad / Lion step."""
+    rng = np.random.default_rng([0x1575, i])
+    name = ["momentum", "rmsprop", "adagrad", "lion"][i % 4]
+    fmt = ["f32", "bf16_rn", "bf16_sr"][(i // 4) % 3]
+    sizes = _sizes(rng)
+    hp = dict(lr=float(10.0 ** rng.uniform(-4, -1.5)), weight_decay=float(rng.choice([0.0, 0.01, 0.05])),
+              beta1=float(rng.uniform(0.8, 0.99)), beta2=float(rng.choice([0.9, 0.99, 0.999])),
+              eps=float(rng.choice([1e-8, 1e-6])))
+    zero_frac = _features(rng, hp)
+    return dict(name=name, fmt=fmt, sizes=sizes, hp=hp, zero_frac=zero_frac,
+                gds=[GRAD_DTYPES[int(j)] for j in rng.integers(0, 3, len(sizes))],
+                steps=int(rng.integers(2, 5)), seed=int(rng.integers(1, 2**63)))
+
+
+def _typed_grads(c, std):
+    """Gradients of dtype gd (float32, BF16 words or float16) with a seeded
+    share of exact zeros of both signs."""
+    def g_of(n, t, k, gd):
+        g = synth.grads(n, t, k, std=std)
+        if c["zero_frac"] > 0 and n:
+            rng = np.random.default_rng([c["seed"] & 0xFFFFFFFF, t, k])
+            z = rng.random(n) < c["zero_frac"]
+            neg = rng.random(n) < 0.5
+            g[z & ~neg] = np.float32(0.0)
+            g[z & neg] = np.float32(-0.0)
+        if gd == "bf16":
+            return synth.bf16_words(g)
+        return g.astype(np.float16) if gd == "f16" else g
+    return g_of
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(P16_CASES))
+def test_sweep_p16(i, gpu):
+    from tests.test_gpu_p16 import _check, _run_p16
+    c = draw_p16(i)
+    print(f"p16 sweep case {i}: {c}", flush=True)
+    ps, st, dev, _, _ = _run_p16(c["opt"], c["fmt"], c["sizes"], c["gds"], c["pdt"], c["p_sr"], c["steps"],
+                                 c["hp"], unorm="max_unorm" in c["hp"], grad=_typed_grads(c, 1e-2),
+                                 seed=c["seed"])
+    # the share of identical 16-bit words is a diagnostic on large lists only
+    _check(ps, st, dev, c["fmt"], c["opt"], c["pdt"], c["steps"],
+           min_same=0.999 if sum(c["sizes"]) >= 20000 else 0.0)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(ONE_STATE_CASES))
+def test_sweep_one_state(i, gpu):
+    from tests.gpu_common import bf16_ulps, fp32_close, nan_equal_bits, to_host
+    from tests.test_gpu_1state import _run_1s
+    c = draw_1s(i)
+    print(f"one-state sweep case {i}: {c}", flush=True)
+    ps, ss, dev = _run_1s(c["name"], c["fmt"], c["gds"], c["steps"], c["hp"], sizes=c["sizes"],
+                          grad=_typed_grads(c, 1e-1), seed=c["seed"])
+    for k in range(len(c["sizes"])):
+        assert fp32_close(to_host(dev[k]["p"]), ps[k]), k
+        g = to_host(dev[k]["s1"])
+        if c["fmt"] == "f32":
+            assert fp32_close(g, ss[k]), k
+        elif c["fmt"] == "bf16_rn":
+            assert int(bf16_ulps(g, ss[k]).max(initial=0)) <= c["steps"], k
+        else:
+            assert nan_equal_bits(g, ss[k]), k
+
+
+def test_sweeps_of_p16_and_one_state_cover_their_space():
+    """Host-side check of the two draws: every format, parameter dtype and
+    rounding, optimizer, gradient dtype, and each feature on and off."""
+    p = [draw_p16(i) for i in range(P16_CASES)]
+    assert {c["fmt"] for c in p} == set(FORMATS)
+    assert {(c["pdt"], c["p_sr"]) for c in p} == {(d, r) for d in (oracle.P_BF16, oracle.P_F16)
+                                                  for r in (False, True)}
+    assert {c["opt"] for c in p} == {"adamw", "ademamix"}
+    o = [draw_1s(i) for i in range(ONE_STATE_CASES)]
+    assert {(c["name"], c["fmt"]) for c in o} == {(n, f) for n in ("momentum", "rmsprop", "adagrad", "lion")
+                                                  for f in ("f32", "bf16_rn", "bf16_sr")}
+    for cases in (p, o):
+        assert {g for c in cases for g in c["gds"]} == set(GRAD_DTYPES)
+        for key in ("skip_zeros", "reset_interval"):
+            on = [key in c["hp"] for c in cases]
+            assert any(on) and not all(on), key
+    on = ["max_unorm" in c["hp"] for c in p]
+    assert any(on) and not all(on)
