@@ -282,6 +282,10 @@ int upload(Workspace &w, const std::vector<unsigned char> &blob, hipStream_t st,
     int rc = slot_quiesce(*v);
     if (rc != OPT_OK) return rc;
     hipError_t e;
+    // The slot holds nothing valid until the copy below is queued, so a
+    // failure from here on can never let a later call reuse it.
+    v->content.clear();
+    v->upload_stream = nullptr;
     if (v->cap < blob.size()) {
         if (v->dev) { (void)hipFree(v->dev); v->dev = nullptr; }
         if (v->host) { (void)hipHostFree(v->host); v->host = nullptr; }
@@ -299,7 +303,10 @@ int upload(Workspace &w, const std::vector<unsigned char> &blob, hipStream_t st,
         return hip_fail(e, "hipMemcpyAsync (tables)");
     }
     if ((e = hipEventRecord(v->ready, st)) != hipSuccess) {
+        // with no event to wait on later, let the queued copy finish reading
+        // the staging buffer before a later fill may overwrite it
         v->content.clear();
+        (void)hipStreamSynchronize(st);
         return hip_fail(e, "hipEventRecord (tables)");
     }
     v->upload_stream = st;
