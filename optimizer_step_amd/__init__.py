@@ -133,11 +133,37 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _current_device(tensors):
+    """The current CUDA device index if any tensor given is a CUDA tensor
+    (else None: the per-tensor checks then refuse the host tensors)."""
+    for d in tensors:
+        for t in d.values():
+            if getattr(t, "is_cuda", False):
+                import torch
+                return torch.cuda.current_device()
+    return None
+
+
+def _host_qmap(q, name):
+    """Address of a 256-entry float32 codebook in host memory (numpy array or
+    CPU torch tensor), which the library reads on the host."""
+    if hasattr(q, "data_ptr"):
+        import torch
+        if q.is_cuda or q.dtype != torch.float32 or not q.is_contiguous() or q.numel() != 256:
+            raise ValueError(f"{name} must be a contiguous CPU float32 tensor of 256 entries")
+        return q.data_ptr()
+    import numpy as np
+    if not isinstance(q, np.ndarray) or q.dtype != np.float32 or not q.flags["C_CONTIGUOUS"] or q.size != 256:
+        raise ValueError(f"{name} must be a C-contiguous float32 numpy array of 256 entries")
+    return q.ctypes.data
+
+
 class TensorList:
     """The C array of opt_tensor for a list of tensor dicts; build it once and
     pass it to every step when the buffers do not change.  A dict may carry
     "index_base" (the slice's first element within its whole tensor) and
-    "sr_tensor" (the tensor number of its stochastic-rounding stream)."""
+    "sr_tensor" (the tensor number of its stochastic-rounding stream).  All
+    tensors must sit on the current CUDA device, whose stream runs the step."""
 
     def __init__(self, tensors):
         self.keep = list(tensors)
@@ -158,7 +184,8 @@ class TensorList:
         (and, for the blockwise formats, its absmax array) holds at least the
         bytes the format needs: the library sees only pointers, so a short or
         strided buffer would be read out of bounds.  Checked once per format."""
-        key = (state_fmt, nstates)
+        dev = _current_device(self.keep)
+        key = (state_fmt, nstates, dev)
         if key in self._checked:
             return
         per = {STATE_F32: 8, STATE_BF16_RN: 4, STATE_BF16_SR: 4}.get(state_fmt, 2)   # half-bytes per element
@@ -169,6 +196,8 @@ class TensorList:
             for name, t in d.items():
                 if hasattr(t, "is_cuda") and (not t.is_cuda or not t.is_contiguous()):
                     raise ValueError(f"tensor {i}: {name} must be a contiguous CUDA tensor")
+                if hasattr(t, "is_cuda") and t.device.index != dev:
+                    raise ValueError(f"tensor {i}: {name} is on {t.device}, not on the current device cuda:{dev}")
             if d["g"].numel() != n:
                 raise ValueError(f"tensor {i}: g has {d['g'].numel()} elements, p has {n}")
             for j in range(1, nstates + 1):
@@ -195,13 +224,17 @@ def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
     reset_interval R > 0 restarts the moments from zero every R steps;
     p_rounding 1 stores BF16/FP16 parameters with stochastic rounding;
     skip_zeros leaves elements whose gradient is exactly 0 untouched."""
+    if grad_scale is not None:
+        import torch
+        _device_buffer(grad_scale, 4, 1, "grad_scale")
+        if grad_scale.dtype != torch.float32:
+            raise ValueError("grad_scale must be a CUDA float32 tensor")
     h = OptHparams(lr, beta1, beta2, beta3, alpha, eps, weight_decay, max_unorm,
                    int(step), int(seed) & (2**64 - 1), None, None, _ptr(grad_scale), int(p_rounding), 0,
                    int(reset_interval), 1 if skip_zeros else 0, 0)
     for field, q in (("qmap_signed", qmap_signed), ("qmap_unsigned", qmap_unsigned)):
         if q is not None:
-            addr = q.ctypes.data if hasattr(q, "ctypes") else q.data_ptr()
-            setattr(h, field, addr)
+            setattr(h, field, _host_qmap(q, field))
     h._keep = (qmap_signed, qmap_unsigned, grad_scale)
     return h
 
@@ -226,12 +259,21 @@ def _device_buffer(t, itemsize, count, what):
     if t is not None and (not t.is_cuda or not t.is_contiguous() or t.element_size() != itemsize
                           or t.numel() < count):
         raise ValueError(f"{what} must be a contiguous CUDA tensor of >= {count} {itemsize}-byte elements")
+    _same_device(t, what)
+
+
+def _same_device(t, what):
+    if t is not None:
+        import torch
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{what} is on {t.device}, not on the current device")
 
 
 def _norm_buffer(t, n):
     """The per-tensor {sum u^2, sum p^2} buffer: CUDA float64, 2n entries."""
     if t is not None and (not t.is_cuda or not t.is_contiguous() or t.element_size() != 8 or t.numel() < 2 * n):
         raise ValueError(f"the update-norm buffer must be a contiguous CUDA float64 tensor of >= {2 * n} entries")
+    _same_device(t, "the update-norm buffer")
     return _ptr(t)
 
 

@@ -310,6 +310,23 @@ def test_binding_refuses_host_tensors(L):
         t.check(L.STATE_F32, 2)
 
 
+def test_binding_refuses_bad_grad_scale_and_codebooks(L):
+    """grad_scale is read by the kernels, so a host tensor (or another dtype)
+    is refused; the codebooks are read on the host, so they must be float32
+    host arrays of exactly 256 entries."""
+    import torch
+    with pytest.raises(ValueError):
+        L.hparams(grad_scale=torch.ones(1))                       # host memory
+    qs = np.asarray(QS, dtype=np.float32)
+    for bad in (qs.astype(np.float64), qs[:255].copy(), np.concatenate([qs, qs[:1]]), qs[::-1],
+                torch.from_numpy(qs.astype(np.float64)), list(qs)):
+        with pytest.raises(ValueError):
+            L.hparams(qmap_signed=bad, qmap_unsigned=QU)
+    # float32 arrays of 256 in host memory, numpy or torch, are taken as they are
+    h = L.hparams(qmap_signed=qs, qmap_unsigned=torch.from_numpy(np.asarray(QU, dtype=np.float32)))
+    assert h.qmap_signed == qs.ctypes.data
+
+
 @no_device
 def test_size_limits(L):
     """numel above 2^46, or index_base + numel above 2^60, is refused before
