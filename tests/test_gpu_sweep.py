@@ -263,3 +263,99 @@ def test_sweeps_of_p16_and_one_state_cover_their_space():
             assert any(on) and not all(on), key
     on = ["max_unorm" in c["hp"] for c in p]
     assert any(on) and not all(on)
+
+
+# ---------------------------------------------------------------------------
+# the gradient norm
+
+GN_CASES = 32
+U53 = 2.0 ** -53
+
+
+def draw_gn(i):
+    """A gradient list: 1..40 tensors of pool sizes and mixed dtypes, one
+    magnitude per case, maybe one non-finite value, a norm type and maybe a
+    clipping coefficient."""
+    rng = np.random.default_rng([0x6E0, i])
+    ntens = int(rng.integers(1, 41))
+    sizes = [int(SIZE_POOL[int(j)]) for j in rng.integers(0, len(SIZE_POOL), ntens)]
+    while sum(sizes) > MAX_TOTAL:
+        sizes.pop()
+    return dict(sizes=sizes, gds=[GRAD_DTYPES[int(j)] for j in rng.integers(0, 3, len(sizes))],
+                std=float(10.0 ** rng.choice([-6, -3, -1, 0, 2])),
+                norm_type=int(rng.choice([2, 0])),
+                max_norm=float(10.0 ** rng.uniform(-2, 3)) if rng.random() < 0.7 else None,
+                poison=str(rng.choice(["none", "none", "none", "nan", "inf"])),
+                geometry=GEOMETRY[int(rng.integers(len(GEOMETRY)))], t=int(i + 1))
+
+
+def _gn_inputs(c):
+    """Per tensor: the device-side array (float32, BF16 words or float16) and
+    the oracle's view of the same values (float32 or BF16 words; float16
+    widens exactly)."""
+    dev, host = [], []
+    for k, (n, gd) in enumerate(zip(c["sizes"], c["gds"])):
+        g = synth.grads(n, c["t"], k, std=c["std"])
+        if gd == "f16":
+            g = np.clip(g, -65504, 65504).astype(np.float16)
+        if c["poison"] != "none" and k == len(c["sizes"]) // 2 and n:
+            g[n // 2] = np.nan if c["poison"] == "nan" else -np.inf
+        g = synth.bf16_words(g) if gd == "bf16" else g
+        dev.append(g)
+        host.append(g.astype(np.float32) if gd == "f16" else g)
+    return dev, host
+
+
+def _same_or_both_nan(a, b):
+    return (np.isnan(a) and np.isnan(b)) or a == b
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(GN_CASES))
+def test_sweep_grad_norm(i, gpu):
+    import torch
+    import optimizer_step_amd as osa
+    c = draw_gn(i)
+    print(f"grad-norm sweep case {i}: {dict(c, sizes=len(c['sizes']), gds=None)} "
+          f"sizes={c['sizes']} gds={c['gds']}", flush=True)
+    dev_in, host_in = _gn_inputs(c)
+    (s2, mx), per = oracle.grad_norm_list(host_in)
+    from tests.gpu_common import to_dev
+    dev = [to_dev(g) for g in dev_in]
+    out = torch.full((2 + 2 * len(dev),), -1.0, dtype=torch.float64, device="cuda")
+    coef = torch.full((1,), -1.0, dtype=torch.float32, device="cuda") if c["max_norm"] else None
+    try:
+        osa.opt_debug_set_launch(*c["geometry"])
+        osa.opt_grad_norm(dev, out, c["max_norm"] or 0.0, c["norm_type"], coef)
+    finally:
+        osa.opt_debug_set_launch(32768, 0)
+        torch.cuda.synchronize()
+    got = out.cpu().numpy()
+
+    def within(gv, ov, n):       # summation error of n non-negative terms
+        if not np.isfinite(ov):
+            return _same_or_both_nan(gv, ov)
+        return abs(gv - ov) <= max(n - 1, 0) * U53 * ov
+
+    for k, (ps, pm) in enumerate(per):
+        assert within(got[2 + 2 * k], ps, c["sizes"][k]), (k, got[2 + 2 * k], ps)
+        assert _same_or_both_nan(got[3 + 2 * k], pm), (k, got[3 + 2 * k], pm)
+    assert within(got[0], s2, sum(c["sizes"])), (got[0], s2)
+    assert _same_or_both_nan(got[1], mx)
+    if coef is not None:
+        cg = float(coef.cpu().numpy()[0])
+        want = oracle.clip_coef(np.sqrt(s2) if c["norm_type"] == 2 else mx, c["max_norm"])
+        if np.isnan(want):
+            assert np.isnan(cg)
+        else:
+            d = abs(int(np.float32(cg).view(np.int32)) - int(np.float32(want).view(np.int32)))
+            assert d <= (0 if c["norm_type"] == 0 else 1), (cg, want)
+
+
+def test_grad_norm_sweep_covers_its_space():
+    cases = [draw_gn(i) for i in range(GN_CASES)]
+    assert {g for c in cases for g in c["gds"]} == set(GRAD_DTYPES)
+    assert {c["norm_type"] for c in cases} == {2, 0}
+    assert {c["poison"] for c in cases} == {"none", "nan", "inf"}
+    assert any(c["max_norm"] is None for c in cases) and any(c["max_norm"] for c in cases)
+    assert max(len(c["sizes"]) for c in cases) >= 20
