@@ -549,8 +549,9 @@ def main():
                            cmd_write=pmc_cmd("WRITE_SIZE", wdir, "write"))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the step shards with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the step is "
+              "element-wise: each GPU would run this same launch on its own shard, with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.rows_only:
