@@ -359,3 +359,35 @@ def test_grad_norm_sweep_covers_its_space():
     assert {c["poison"] for c in cases} == {"none", "nan", "inf"}
     assert any(c["max_norm"] is None for c in cases) and any(c["max_norm"] for c in cases)
     assert max(len(c["sizes"]) for c in cases) >= 20
+
+
+# ---------------------------------------------------------------------------
+# thousands of tensors in one call
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("opt,fmt", [("adamw", "f32"), ("adamw", "q8"), ("ademamix", "bf16_sr"), ("adamw", "fp4_sr")])
+def test_thousands_of_small_tensors(opt, fmt, gpu):
+    """3000 ragged tensors (empty to a few thousand elements, mixed gradient
+    dtypes) in one call: a chunk table of thousands of entries, per-tensor
+    update norms and clipping over the whole list, and skip_zeros."""
+    rng = np.random.default_rng(3000)
+    sizes = [int(x) for x in rng.choice([0, 1, 3, 17, 255, 256, 257, 1000, 1025, 4097], 3000)]
+    bf = [bool(b) for b in rng.integers(0, 2, len(sizes))]
+    hp = dict(lr=1e-3, weight_decay=0.1, max_unorm=1.0, skip_zeros=True)
+    if opt == "ademamix":
+        hp.update(beta3=0.999, alpha=5.0)
+    case = Case(opt, fmt, sizes, bf, 2, hp, grad_override=lambda t, k, n: synth.grid_grads(n, t, k, bf16=bf[k]),
+                clip=(0.5, 2))
+    print(f"{len(sizes)} tensors, {sum(sizes)} elements, {opt} {fmt}", flush=True)
+    ps, st, norms_o = case.run_oracle()
+    dev, norms_g = case.run_gpu()
+    assert [np.float32(x).view(np.uint32) for x in case.gpu_coefs] == \
+           [np.float32(x).view(np.uint32) for x in case.oracle_coefs]
+    assert all(c < 1.0 for c in case.oracle_coefs)
+    compare(case, dev, ps, st)
+    states_bit_identical(case, dev, st)
+    # the first step's per-tensor norms see identical inputs on both sides
+    for (t, k, u2, p2) in norms_o:
+        if t == 1:
+            assert abs(norms_g[0][2 * k] - u2) <= 1e-12 * abs(u2), (k, norms_g[0][2 * k], u2)
+            assert abs(norms_g[0][2 * k + 1] - p2) <= 1e-12 * abs(p2), (k, norms_g[0][2 * k + 1], p2)
