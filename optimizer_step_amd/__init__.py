@@ -239,17 +239,34 @@ def hparams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
     return h
 
 
+class GradList:
+    """The C array of opt_grad for a list of gradient tensors, each checked
+    once (a contiguous CUDA tensor on the current device); pass it to
+    opt_grad_norm in place of the list while the buffers do not change."""
+
+    def __init__(self, grads):
+        import torch
+        self.keep = list(grads)
+        self.arr = (OptGrad * max(1, len(self.keep)))()
+        dev = torch.cuda.current_device() if any(getattr(g, "is_cuda", False) for g in self.keep) else None
+        for i, g in enumerate(self.keep):
+            if not g.is_cuda or not g.is_contiguous():
+                raise ValueError(f"gradient {i} must be a contiguous CUDA tensor")
+            if g.device.index != dev:
+                raise ValueError(f"gradient {i} is on {g.device}, not on the current device")
+            self.arr[i] = OptGrad(_ptr(g), g.numel(), _dtype_code(g), 0)
+        self.n = len(self.keep)
+
+
 def opt_grad_norm(grads, out, max_norm=0.0, norm_type=2, coef_out=None, stream=None):
-    """Norms of a list of CUDA gradient tensors into out (CUDA float64 tensor
-    of 2 + 2n): totals then per-tensor {sum g^2, max |g|}; optionally the
-    clipping coefficient into coef_out (CUDA float32 tensor of 1)."""
-    _device_buffer(out, 8, 2 + 2 * len(grads), "out")
+    """Norms of a list of CUDA gradient tensors (or a GradList) into out (CUDA
+    float64 tensor of 2 + 2n): totals then per-tensor {sum g^2, max |g|};
+    optionally the clipping coefficient into coef_out (CUDA float32 tensor of
+    1)."""
+    gl = grads if isinstance(grads, GradList) else GradList(grads)
+    _device_buffer(out, 8, 2 + 2 * gl.n, "out")
     _device_buffer(coef_out, 4, 1, "coef_out")
-    arr = (OptGrad * max(1, len(grads)))()
-    for i, g in enumerate(grads):
-        _device_buffer(g, g.element_size(), g.numel(), f"gradient {i}")
-        arr[i] = OptGrad(_ptr(g), g.numel(), _dtype_code(g), 0)
-    return _check(lib().opt_grad_norm(arr, len(grads), _ptr(out), float(max_norm), int(norm_type),
+    return _check(lib().opt_grad_norm(gl.arr, gl.n, _ptr(out), float(max_norm), int(norm_type),
                                       _ptr(coef_out), _stream(stream)))
 
 

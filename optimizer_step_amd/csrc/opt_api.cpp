@@ -64,6 +64,8 @@ int g_wgs_per_cu = 0;         // workgroups per compute unit (0: one per tile, o
 
 constexpr int kMaxDevices = 64;
 constexpr int kSlots = 16;
+constexpr int kPlans = 8;                  // planned calls remembered per device
+constexpr int64_t kPlanMaxTensors = 1 << 16;
 // Size limits, far beyond any device's memory, that keep the host's chunk
 // arithmetic and the element indices of the random streams in range.
 constexpr int64_t kMaxNumel = (int64_t)1 << 46;
@@ -185,6 +187,7 @@ struct QCache {
     std::vector<uint32_t> words;
     QTabParams ps, pu;
     bool valid = false;
+    uint64_t gen = 0;               // bumped whenever the tables change
 };
 
 // ---------------------------------------------------------------------------
@@ -202,6 +205,29 @@ struct Slot {
     bool multi_stream = false;
     bool used = false;
     uint64_t tick = 0;
+    uint64_t gen = 0;               // bumped whenever the contents are replaced
+};
+
+// One bucket's launch in a planned call: its tables' slot and offsets.
+struct PlanItem {
+    int bi = 0;                     // bucket: (gradient dtype, parameter dtype) index
+    Slot *slot = nullptr;
+    uint64_t gen = 0;               // the slot's generation when the tables went in
+    size_t off_ct = 0, off_q = 0;
+    int64_t nchunks = 0;
+    int ntens = 0;
+    size_t partial_doubles = 0;
+    int64_t ngroups = 0;
+};
+
+// A planned call, keyed by the raw tensor records and everything else the
+// tables depend on (kind of call, optimizer, format, chunk size, codebook
+// tables); valid while every slot it names still holds its tables.
+struct PlanEntry {
+    std::vector<unsigned char> key;
+    std::vector<PlanItem> items;
+    size_t need = 0;                // doubles of norm workspace
+    uint64_t tick = 0;
 };
 
 struct Workspace {
@@ -215,6 +241,7 @@ struct Workspace {
     hipStream_t partials_stream = nullptr;
     bool partials_used = false;
     QCache q;
+    PlanEntry plans[kPlans];
 };
 
 std::mutex g_mu;
@@ -286,6 +313,7 @@ int upload(Workspace &w, const std::vector<unsigned char> &blob, hipStream_t st,
     // failure from here on can never let a later call reuse it.
     v->content.clear();
     v->upload_stream = nullptr;
+    ++v->gen;
     if (v->cap < blob.size()) {
         if (v->dev) { (void)hipFree(v->dev); v->dev = nullptr; }
         if (v->host) { (void)hipHostFree(v->host); v->host = nullptr; }
@@ -481,6 +509,7 @@ int qtables(Workspace &w, const opt_hparams *hp)
     memcpy(q.qs, hp->qmap_signed, 1024);
     memcpy(q.qu, hp->qmap_unsigned, 1024);
     q.valid = true;
+    ++q.gen;
     return OPT_OK;
 }
 
@@ -504,6 +533,79 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
 
 LaunchGeom geom(const Workspace &w) { return LaunchGeom{w.ncu, g_wgs_per_cu}; }
 
+// The device tables of a call's buckets (bucket bi = 3 * gradient dtype +
+// parameter dtype).  A call whose tensor records, kind, optimizer, format,
+// chunk size and codebook tables equal those of a remembered call, and whose
+// tables are all still in their slots, reuses that plan; otherwise the
+// buckets are planned and their tables uploaded (or found) now.  Buckets
+// whose tensors are all empty are kept only if keep_chunkless (the norm
+// passes write zeros for them).
+int plan_call(Workspace &w, int kind, int opt, int fmt, bool keep_chunkless, const opt_tensor *t, int64_t n,
+              const std::vector<uint32_t> *qw, hipStream_t st, std::vector<PlanItem> &items, size_t &need)
+{
+    const int64_t chunk = g_chunk;
+    const bool cache = n <= kPlanMaxTensors;
+    std::vector<unsigned char> key;
+    if (cache) {
+        const int64_t head[6] = {kind, opt, fmt, keep_chunkless ? 1 : 0, chunk, qw ? (int64_t)w.q.gen : -1};
+        key.resize(sizeof head + (size_t)n * sizeof(opt_tensor));
+        memcpy(key.data(), head, sizeof head);
+        if (n) memcpy(key.data() + sizeof head, t, (size_t)n * sizeof(opt_tensor));
+        for (PlanEntry &e : w.plans) {
+            if (e.key.size() != key.size() || memcmp(e.key.data(), key.data(), key.size()) != 0) continue;
+            bool live = true;
+            for (const PlanItem &it : e.items) live = live && it.slot->gen == it.gen;
+            if (!live) {            // a table was evicted since: plan afresh
+                e = PlanEntry();
+                break;
+            }
+            for (const PlanItem &it : e.items) {
+                Slot &s = *it.slot;
+                if (s.upload_stream != st) {    // as in upload(): order after the copy
+                    hipError_t er = hipStreamWaitEvent(st, s.ready, 0);
+                    if (er != hipSuccess) return hip_fail(er, "hipStreamWaitEvent (tables)");
+                }
+                s.tick = ++w.tick;
+            }
+            e.tick = ++w.tick;
+            items = e.items;
+            need = e.need;
+            return OPT_OK;
+        }
+    }
+    items.clear();
+    need = 0;
+    for (int bi = 0; bi < 9; ++bi) {
+        Bucket bk;
+        plan_bucket(t, n, bi / 3, bi % 3, chunk, bk);
+        if (bk.tens.empty() || (!keep_chunkless && bk.chunk_tensor.empty())) continue;
+        std::vector<unsigned char> blob;
+        PlanItem it;
+        it.bi = bi;
+        make_blob(bk, qw, blob, it.off_ct, it.off_q);
+        Slot *s;
+        int rc = upload(w, blob, st, s);
+        if (rc != OPT_OK) return rc;
+        it.slot = s;
+        it.gen = s->gen;
+        it.nchunks = (int64_t)bk.chunk_tensor.size();
+        it.ntens = (int)bk.tens.size();
+        it.partial_doubles = bk.partial_doubles(chunk);
+        it.ngroups = bk.ngroups;
+        need = std::max(need, bk.norm_doubles(chunk));
+        items.push_back(it);
+    }
+    if (cache) {
+        PlanEntry *v = &w.plans[0];
+        for (PlanEntry &e : w.plans) if (e.tick < v->tick) v = &e;
+        v->key = std::move(key);
+        v->items = items;
+        v->need = need;
+        v->tick = ++w.tick;
+    }
+    return OPT_OK;
+}
+
 // The shared body of the step and the pre-pass.
 int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp, const double *unorm,
         double *unorm_out, void *stream)
@@ -525,33 +627,24 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
     if (q8 && (rc = qtables(*w, hp)) != OPT_OK) return rc;
     const int64_t chunk = g_chunk;
 
-    Bucket b[9];   // (gradient dtype, parameter dtype)
-    for (int i = 0; i < 9; ++i) plan_bucket(t, n, i / 3, i % 3, chunk, b[i]);
+    std::vector<PlanItem> items;
+    size_t need = 0;
+    if ((rc = plan_call(*w, 0, opt, fmt, pre, t, n, q8 ? &w->q.words : nullptr, st, items, need)) != OPT_OK)
+        return rc;
+    if (pre && (rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
 
-    if (pre) {
-        size_t need = 0;
-        for (auto &bk : b) need = std::max(need, bk.norm_doubles(chunk));
-        if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
-    }
-
-    for (int bi = 0; bi < 9; ++bi) {
-        const int gd = bi / 3;
-        Bucket &bk = b[bi];
-        if (bk.tens.empty() || (!pre && bk.chunk_tensor.empty())) continue;
-        std::vector<unsigned char> blob;
-        size_t off_ct, off_q;
-        make_blob(bk, q8 ? &w->q.words : nullptr, blob, off_ct, off_q);
-        Slot *s;
-        if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+    for (const PlanItem &it : items) {
+        const int gd = it.bi / 3;
+        Slot *s = it.slot;
         StepArgs a = base_args(hp, chunk);
-        a.p_dtype = bi % 3;
+        a.p_dtype = it.bi % 3;
         a.tens = (const DevTensor *)s->dev;
-        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
-        a.nchunks = (int64_t)bk.chunk_tensor.size();
+        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + it.off_ct);
+        a.nchunks = it.nchunks;
         a.unorm = (!pre && hp->max_unorm > 0.0f) ? unorm : nullptr;
         size_t lds = 0;
         if (q8) {
-            a.q.words = (const uint32_t *)((unsigned char *)s->dev + off_q);
+            a.q.words = (const uint32_t *)((unsigned char *)s->dev + it.off_q);
             a.q.nwords = (uint32_t)w->q.words.size();
             a.q.s = w->q.ps;
             a.q.u = w->q.pu;
@@ -560,9 +653,9 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
         hipError_t e;
         if (pre) {
             a.partials = w->partials;
-            a.groups = w->partials + bk.partial_doubles(chunk);
-            a.ngroups = bk.ngroups;
-            e = launch_unorm(opt, gd, fmt, a, geom(*w), q8 ? 2048 : 0, (int)bk.tens.size(), unorm_out, st);
+            a.groups = w->partials + it.partial_doubles;
+            a.ngroups = it.ngroups;
+            e = launch_unorm(opt, gd, fmt, a, geom(*w), q8 ? 2048 : 0, it.ntens, unorm_out, st);
             if (e == hipSuccess) {
                 w->partials_used = true;
                 w->partials_stream = st;
@@ -658,29 +751,22 @@ int opt_grad_norm(const opt_grad *grads, int64_t n, double *out, float max_norm,
     if ((rc = workspace(w)) != OPT_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const int64_t chunk = g_chunk;
-    Bucket b[3];
-    for (int gd = 0; gd < 3; ++gd) plan_bucket(t.data(), n, gd, kP32, chunk, b[gd]);
+    std::vector<PlanItem> items;
     size_t need = 0;
-    for (auto &bk : b) need = std::max(need, bk.norm_doubles(chunk));
+    if ((rc = plan_call(*w, 1, 0, 0, true, t.data(), n, nullptr, st, items, need)) != OPT_OK) return rc;
     if ((rc = partials_reserve(*w, need, st)) != OPT_OK) return rc;
     hipError_t e;
-    for (int gd = 0; gd < 3; ++gd) {
-        Bucket &bk = b[gd];
-        if (bk.tens.empty()) continue;
-        std::vector<unsigned char> blob;
-        size_t off_ct, off_q;
-        make_blob(bk, nullptr, blob, off_ct, off_q);
-        Slot *s;
-        if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+    for (const PlanItem &it : items) {
+        Slot *s = it.slot;
         StepArgs a{};
         a.tens = (const DevTensor *)s->dev;
-        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
-        a.nchunks = (int64_t)bk.chunk_tensor.size();
+        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + it.off_ct);
+        a.nchunks = it.nchunks;
         a.chunk = chunk;
         a.partials = w->partials;
-        a.groups = w->partials + bk.partial_doubles(chunk);
-        a.ngroups = bk.ngroups;
-        e = launch_gnorm(gd, a, geom(*w), (int)bk.tens.size(), out, st);
+        a.groups = w->partials + it.partial_doubles;
+        a.ngroups = it.ngroups;
+        e = launch_gnorm(it.bi / 3, a, geom(*w), it.ntens, out, st);
         if (e != hipSuccess) return hip_fail(e, "gradient norm launch");
         if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
     }
@@ -725,20 +811,16 @@ int opt_step_1state(int32_t optimizer, const opt_tensor *t, int64_t n, int32_t s
     if ((rc = workspace(w)) != OPT_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     const int64_t chunk = g_chunk;
-    for (int gd = 0; gd < 3; ++gd) {
-        Bucket bk;
-        plan_bucket(t, n, gd, kP32, chunk, bk);
-        if (bk.chunk_tensor.empty()) continue;
-        std::vector<unsigned char> blob;
-        size_t off_ct, off_q;
-        make_blob(bk, nullptr, blob, off_ct, off_q);
-        Slot *s;
-        if ((rc = upload(*w, blob, st, s)) != OPT_OK) return rc;
+    std::vector<PlanItem> items;
+    size_t need = 0;
+    if ((rc = plan_call(*w, 2, optimizer, state_fmt, false, t, n, nullptr, st, items, need)) != OPT_OK) return rc;
+    for (const PlanItem &it : items) {
+        Slot *s = it.slot;
         StepArgs a = base_args(hp, chunk);
         a.tens = (const DevTensor *)s->dev;
-        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + off_ct);
-        a.nchunks = (int64_t)bk.chunk_tensor.size();
-        hipError_t e = launch_step_1state(optimizer, gd, state_fmt, a, geom(*w), st);
+        a.chunk_tensor = (const int32_t *)((unsigned char *)s->dev + it.off_ct);
+        a.nchunks = it.nchunks;
+        hipError_t e = launch_step_1state(optimizer, it.bi / 3, state_fmt, a, geom(*w), st);
         if (e != hipSuccess) return hip_fail(e, "one-state step launch");
         if ((rc = slot_mark_used(*s, st)) != OPT_OK) return rc;
     }

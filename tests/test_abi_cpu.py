@@ -308,6 +308,8 @@ def test_binding_refuses_host_tensors(L):
     t = L.TensorList([{"p": torch.zeros(16), "g": torch.zeros(16), "s1": torch.zeros(16), "s2": torch.zeros(16)}])
     with pytest.raises(ValueError):
         t.check(L.STATE_F32, 2)
+    with pytest.raises(ValueError):
+        L.GradList([torch.zeros(16)])
 
 
 def test_binding_refuses_bad_grad_scale_and_codebooks(L):
