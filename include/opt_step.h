@@ -32,10 +32,12 @@
  *
  * Calls and memory.  Every call is asynchronous on `stream` (a hipStream_t
  * passed as void*; NULL is the null stream).  All tensors, states and the
- * unorm buffer are caller-owned device memory; the library keeps no pointer
- * after a call returns.  The library owns a small per-device workspace
- * (tensor tables, codebook search tables, norm partials) that it grows on
- * demand and releases in opt_shutdown.  Calls from several host threads are
+ * unorm buffer are caller-owned device memory; the library touches them
+ * only through the work a call enqueues.  It owns a small per-device
+ * workspace (tensor tables, codebook search tables, norm partials) that it
+ * grows on demand and releases in opt_shutdown, and it remembers the tensor
+ * records (pointers and sizes) of recent calls to recognise a repeated call
+ * and reuse its device tables.  Calls from several host threads are
  * serialized inside the library.
  *
  * Errors.  Every entry point returns OPT_OK (0) or a negative status, and
