@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
             if (full) {
                 // the whole tile is in range: 4 groups of 4 per lane, loads first
                 float p[4][4], g[4][4], m[4][4], v[4][4], m2[4][4];
+                load_prio_hi();
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t e = e0 + tt * kUTile + q * 256 + lane * 4;
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
                         if (OPT == kAdEMAMix) read_state4<SF, 2>(lds, T.s3, T.a3, e, m2[q]);
                     }
                 }
+                load_prio_lo();
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -258,8 +260,10 @@ __global__ __launch_bounds__(kThreads) OPT_GN_ATTR void gnorm_partials_kernel(co
         if (len == kGnTile) {
             // a full tile: every load of the wave's kGnUnits units before the sums
             GnRaw<GD> g[kGnUnits];
+            load_prio_hi();
 #pragma unroll
             for (int u = 0; u < kGnUnits; ++u) gnorm_load_unit<GD>(T.g, e0 + (wave + u * kWaves) * kUTile, lane, g[u]);
+            load_prio_lo();
 #pragma unroll
             for (int u = 0; u < kGnUnits; ++u) {
                 double sq = 0.0;
@@ -517,11 +521,13 @@ __global__ __launch_bounds__(256) void round_cast_kernel(const float *__restrict
         const int64_t q0 = w * (kCastTile / 4);   // the tile's first group of four
         if ((w + 1) * kCastTile <= n) {
             float v[kCastGroups][4];
+            load_prio_hi();
 #pragma unroll
             for (int u = 0; u < kCastGroups; ++u) {
                 const f4 t = sld<f4>(x + 4 * (q0 + threadIdx.x + u * 256));
                 v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
             }
+            load_prio_lo();
 #pragma unroll
             for (int u = 0; u < kCastGroups; ++u) cast_group<BF, SR>(v[u], out, q0 + threadIdx.x + u * 256, 4, seed, offset);
         } else {   // the short last tile

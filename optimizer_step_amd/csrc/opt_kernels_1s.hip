@@ -148,8 +148,10 @@ __global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__re
         if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
         if (len == kEwTile1) {
             Group1 x[kEwGroups];
+            load_prio_hi();
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u) s1_load<OPT, GD, SF>(T, e0 + 4 * (threadIdx.x + u * kThreads), fresh, x[u]);
+            load_prio_lo();
             if (!have_s) { s = publish_scalars1(a, sh); have_s = true; }
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u) s1_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (threadIdx.x + u * kThreads), x[u]);

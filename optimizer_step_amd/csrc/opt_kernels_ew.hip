@@ -150,9 +150,11 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
         if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
         if (len == kEwTile) {
             Group x[kEwGroups];
+            load_prio_hi(SF != kBF16RN);
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
                 ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (threadIdx.x + u * kEwThreads), fresh, x[u]);
+            load_prio_lo(SF != kBF16RN);
             if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll

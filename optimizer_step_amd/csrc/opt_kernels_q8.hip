@@ -47,7 +47,9 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
         uint32_t b = wave;
         for (; b < nfull; b += kQ8Waves) {
             QIn x0;
+            load_prio_hi();
             q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
+            load_prio_lo();
             q8_finish<OPT, SF, PD, true>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
         }
         if (b < nblk) {   // the tensor's short last block
