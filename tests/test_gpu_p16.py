@@ -117,8 +117,8 @@ def _step16(x, dtype):
     2^(floor(log2|x|) - fraction bits), and the subnormal spacing below the
     normal range."""
     frac, emin = (7, -126) if dtype == oracle.P_BF16 else (10, -14)
-    _, e = np.frexp(np.abs(x))
-    return np.ldexp(1.0, np.maximum(e - 1, emin) - frac)
+    _, e = np.frexp(np.abs(x))                  # |x| = m 2^e, m in [0.5, 1); e = 0 for x = 0
+    return np.ldexp(1.0, np.where(x != 0, np.maximum(e - 1, emin), emin) - frac)
 
 
 def _run_p16(opt, fmt, sizes, gds, pdt, p_sr, steps, hp, unorm=False, grad=_grad, seed=synth.SR_SEED):
