@@ -127,3 +127,59 @@ def test_chunk_size_change_on_the_same_list():
         osa.opt_debug_set_launch(32768, 0)
         torch.cuda.synchronize()
     _check(case, dev)
+
+
+def test_random_schedule_over_two_streams():
+    """A seeded schedule of 80 steps over 10 lists (some alike but for their
+    buffers), each step on one of two streams under one of three chunk
+    sizes, with a pre-pass on the lists that bound the update norm.  The
+    caller orders its own data across the streams; the library orders its
+    tables.  Every list ends where the oracle's steps take it."""
+    import torch
+    import optimizer_step_amd as osa
+    rng = np.random.default_rng(2024)
+    shapes = [[5000, 3], [70000], [257, 4097, 1], [5000, 3], [32768 + 9, 100]]
+    cases, devs, tls, ts = [], [], [], []
+    for i in range(10):
+        sizes = shapes[i % len(shapes)]
+        hp = dict(lr=1e-3, weight_decay=0.1, beta3=0.999, alpha=5.0)
+        if i % 4 == 1:
+            hp["max_unorm"] = 1.0
+        c = Case("ademamix" if i % 3 == 0 else "adamw", ["f32", "bf16_sr", "q8", "fp8_rn", "fp4_sr"][i % 5],
+                 sizes, [bool(b) for b in rng.integers(0, 2, len(sizes))], 0, hp, seed=500 + i)
+        d = c.alloc_gpu()
+        cases.append(c)
+        devs.append(d)
+        tls.append(osa.TensorList(d))
+        ts.append(0)
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    try:
+        for _ in range(80):
+            i = int(rng.integers(len(cases)))
+            s = streams[int(rng.integers(2))]
+            osa.opt_debug_set_launch(int(rng.choice([32768, 1024, 65536])), 0)
+            for other in streams:
+                if other is not s:
+                    s.wait_stream(other)
+            c, d, tl = cases[i], devs[i], tls[i]
+            ts[i] += 1
+            t = ts[i]
+            with torch.cuda.stream(s):
+                for k in range(len(c.sizes)):
+                    d[k]["g"].copy_(to_dev(c.grad(t, k)))
+                hp = osa.hparams(step=t, seed=c.seed, qmap_signed=c.qs, qmap_unsigned=c.qu, **c.hp)
+                un = None
+                if c.hp.get("max_unorm", 0) > 0:
+                    un = torch.empty(2 * len(c.sizes), dtype=torch.float64, device="cuda")
+                    osa.opt_precondition_unorm(c.opt, tl, c.fmt, hp, un, stream=s)
+                fn = osa.opt_step_adamw if c.opt == "adamw" else osa.opt_step_ademamix
+                fn(tl, c.fmt, hp, un, stream=s)
+                if un is not None:
+                    un.record_stream(s)
+    finally:
+        osa.opt_debug_set_launch(32768, 0)
+        torch.cuda.synchronize()
+    assert min(ts) >= 3
+    for c, d, n in zip(cases, devs, ts):
+        c.steps = n
+        _check(c, d)
