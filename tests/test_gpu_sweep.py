@@ -1,10 +1,12 @@
-"""A seeded sweep over combinations the focused tests take one at a time:
-optimizer x state format x list shape (empty, one-element, block- and
-tile-edge sizes, mixed gradient dtypes) x hyper-parameters x the features
-around the step (update-norm bound, gradient clipping, skip_zeros with exact
-+-0 gradients, state resets, a late first step) x launch geometry.  Each case
-is drawn from its own seed and printed before it runs, so a failure names the
-case to rerun on its own.
+"""Seeded sweeps over combinations the focused tests take one at a time.
+The two-state sweep draws optimizer x state format x list shape (empty,
+one-element, block- and tile-edge sizes, mixed gradient dtypes) x
+hyper-parameters x the features around the step (update-norm bound, gradient
+clipping, skip_zeros with exact +-0 gradients, state resets, a late first
+step) x launch geometry.  Further sweeps draw steps on BF16/FP16 parameters,
+the one-state optimizers and the gradient norm; one test steps 3000 ragged
+tensors in one call.  Each case is drawn from its own seed and printed
+before it runs, so a failure names the case to rerun on its own.
 
 Bars, as in the focused tests: p within 1e-6 relative; fp32 states within
 1e-6 relative, BF16-nearest states within one BF16 step per step, every other
