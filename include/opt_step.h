@@ -198,16 +198,28 @@ typedef struct {
 } opt_hparams;
 
 /* One AdamW step over the n tensors of `tensors` (host array, read during the
- * call only).  Tensors are grouped by gradient dtype and each group runs as
- * one kernel launch over a host-built chunk table.
+ * call only), with decoupled weight decay applied decay-first: per element,
+ * in binary32, m' = b1*m + (1-b1)*g, v' = b2*v + (1-b2)*g^2 ("When Small
+ * Updates Disappear", Sec. 1.1), u = (m'/c1)/(sqrt(v'/c2) + eps) with
+ * c = 1 - beta^t, and p' = p*(1 - lr*wd) - lr*s_k*u, both terms from the old
+ * p (bitsandbytes PR "Fix decoupled weight decay ordering in the CUDA
+ * Adam/AdEMAMix kernels", intro); s_k is the update-norm scale (1 unless
+ * max_unorm > 0).  Tensors are grouped by gradient and parameter storage and
+ * each group runs as one kernel launch over a host-built chunk table (NeMo
+ * Automodel PR "perf(training): fused multi-tensor gradient-norm
+ * reduction", What).  Errors: negative status, nothing enqueued.
  * unorm: device double[2*n] written by opt_precondition_unorm with the same
  * tensors, format and hyper-parameters, on the same stream, before this call;
  * required when hp->max_unorm > 0 and ignored otherwise. */
 int opt_step_adamw(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
                    const opt_hparams *hp, const double *unorm, void *stream);
 
-/* One AdEMAMix step; arguments as opt_step_adamw, with s3 (and absmax3 for
- * the blockwise formats) required for every tensor. */
+/* One AdEMAMix step (the rule the bitsandbytes PR "Fix decoupled weight
+ * decay ordering in the CUDA Adam/AdEMAMix kernels" intro cites, Pagliardini
+ * et al.): as opt_step_adamw plus the slow EMA m2' = b3*m2 + (1-b3)*g, kept in
+ * s3, and u = (m1'/c1 + alpha*m2')/(sqrt(v'/c2) + eps) (m2 is not
+ * bias-corrected).  Arguments as opt_step_adamw, with s3 (and absmax3 for the
+ * blockwise formats) required for every tensor. */
 int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
                       const opt_hparams *hp, const double *unorm, void *stream);
 

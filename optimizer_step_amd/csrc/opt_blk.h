@@ -290,20 +290,11 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) m_in[i] = v_in[i] = m2_in[i] = 0.0f;
     }
-    // The stored moments are exact binary32; only the direction u (for p)
-    // takes the fast path, unless some v_hat in the wave is tiny or NaN.
+    // The stored moments are exact binary32; only the direction u (for an
+    // fp32 p) takes the fast path, per element (moments4).
     float p[4], mo[4], vo[4], m2o[4];
-    float vmin = 1.0f;
     Mom r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = moments_fast<OPT>(s, a, x.g[i], m_in[i], v_in[i], m2_in[i]);
-        vmin = fminf(vmin, r[i].v * s.rc2);
-    }
-    if (__any(!(vmin >= 0x1p-96f))) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = moments<OPT>(s, a, x.g[i], m_in[i], v_in[i], m2_in[i]);
-    }
+    moments4<OPT, PD == kP32>(s, a, x.g, m_in, v_in, m2_in, r);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         p[i] = apply_update(x.p[i], s.d, lam, r[i].u);

@@ -174,6 +174,15 @@ __host__ __device__ inline bool div_by_ok(float b)
     return (fbits(b) & 0x7FFFFFFFu) - 0x01800000u <= 0x4C800000u - 0x01800000u;
 }
 
+// Dividends for which div_by is correctly rounded (with a divisor that passes
+// div_by_ok): zero, or a finite magnitude of at least 2^-100.  Others (tiny,
+// infinite, NaN) take the plain division.
+__host__ __device__ inline bool div_by_arg(float a)
+{
+    const uint32_t m = fbits(a) & 0x7FFFFFFFu;
+    return m == 0u || m - 0x0D800000u < 0x7F800000u - 0x0D800000u;
+}
+
 // ---------------------------------------------------------------------------
 // 8-bit code of x against a codebook's lookup table (layout in opt_plan.h),
 // for x with |x| <= 1 that is not NaN (and, for an unsigned table, x >= 0 or
@@ -416,9 +425,7 @@ __device__ inline Scalars make_scalars(const StepArgs &a)
     s.c1 = (float)(1.0 - powi((double)a.beta1, a.bc_step));
     s.c2 = (float)(1.0 - powi((double)a.beta2, a.bc_step));
     // 0 <= beta < 1 (checked by the host) keeps c in [2^-24, 1], where div_by
-    // by c is correctly rounded for every moment of magnitude >= 2^-100; a
-    // smaller moment's m_hat or v_hat (which only feed the direction u, never
-    // a stored state) may be an ulp off
+    // by c is correctly rounded for every moment that passes div_by_arg
     s.rc1 = 1.0f / s.c1;
     s.rc2 = 1.0f / s.c2;
     float lrwd = a.lr * a.wd;
@@ -454,6 +461,10 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
     r.v = a.beta2 * v + s.om2 * gg;
     float mh = div_by(r.m, s.c1, s.rc1);
     float vh = div_by(r.v, s.c2, s.rc2);
+    if (!(div_by_arg(r.m) && div_by_arg(r.v))) {   // rare: the plain correctly rounded division
+        mh = r.m / s.c1;
+        vh = r.v / s.c2;
+    }
     float den = __builtin_sqrtf(vh) + a.eps;
     if (OPT == kAdEMAMix) {
         r.m2 = a.beta3 * m2 + s.om3 * g;
@@ -470,10 +481,11 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
 // update, never a stored moment, code or rounding bit) formed with the
 // hardware reciprocal and square root (each within 1 ulp) instead of
 // correctly rounded division and square root: u is within a few ulp of the
-// exact recipe, far inside the parameter tolerance.  Callers fall back to the
-// exact recipe for the whole wave where some v_hat is below 2^-96 (where the
-// hardware square root loses accuracy); NaN and infinite moments give the
-// same u either way.
+// exact recipe, far inside the fp32 parameter tolerance.  Used for fp32
+// parameters only; an element whose own v_hat is below 2^-96 (where the
+// hardware square root loses accuracy) takes the exact recipe (fast_ok), so
+// every element's result depends on its own inputs alone.  NaN and infinite
+// moments give the same u either way.
 template <int OPT>
 __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a, float g, float m,
                                             float v, float m2)
@@ -494,6 +506,41 @@ __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a,
         r.u = mh * rden;
     }
     return r;
+}
+
+// Whether moments_fast's direction is used for this element (else the exact
+// recipe): its fast v_hat is at least 2^-96, or NaN.
+template <int OPT>
+__device__ __forceinline__ bool fast_ok(const Scalars &s, const Mom &r)
+{
+    return !(r.v * s.rc2 < 0x1p-96f);
+}
+
+// The moments and direction of four elements: the fast direction (FAST, fp32
+// parameters) with the exact recipe for the elements fast_ok rejects, or the
+// exact recipe throughout (16-bit parameters, whose rounded store must see
+// exactly the oracle's binary32 value).  The wave skips the exact pass when
+// no lane needs it; the result of an element never depends on other lanes.
+template <int OPT, bool FAST>
+__device__ __forceinline__ void moments4(const Scalars &s, const StepArgs &a, const float g[4],
+                                         const float m[4], const float v[4], const float m2[4], Mom r[4])
+{
+    if (!FAST) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = moments<OPT>(s, a, g[i], m[i], v[i], m2[i]);
+        return;
+    }
+    bool slow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = moments_fast<OPT>(s, a, g[i], m[i], v[i], m2[i]);
+        slow[i] = !fast_ok<OPT>(s, r[i]);
+    }
+    if (__any(slow[0] || slow[1] || slow[2] || slow[3])) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (slow[i]) r[i] = moments<OPT>(s, a, g[i], m[i], v[i], m2[i]);
+    }
 }
 
 // Decay-first: both terms from the previous p (bitsandbytes PR "Fix decoupled

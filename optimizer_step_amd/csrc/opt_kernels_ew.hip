@@ -8,9 +8,10 @@
 // accesses and 16-bit ones as 64-bit accesses, every access instruction of a
 // wave64 fully coalesced; a full tile issues all its loads before the
 // per-call scalars are formed and before any arithmetic.  The moments are
-// formed exactly (fixed binary32 order); the direction u, which only feeds
-// p, uses the hardware reciprocal and square root (measured on MI355X: +2 %
-// on the 290-tensor AdamW step, +5-6 % with BF16 states).  HBM-bound: every
+// formed exactly (fixed binary32 order); for fp32 parameters the direction
+// u, which only feeds p, uses the hardware reciprocal and square root
+// (measured on MI355X: +2 % on the 290-tensor AdamW step, +5-6 % with BF16
+// states), and 16-bit parameters take the exact recipe.  HBM-bound: every
 // byte is read or written once per step and no intermediate leaves registers.
 #include "opt_elem.h"
 
@@ -42,20 +43,11 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
                                           int64_t e, float lam, Group &x)
 {
     float mo[4], vo[4], m2o[4];
-    // the direction with the hardware reciprocal and square root; the exact
-    // recipe for the whole wave where some v_hat is below 2^-96 (a NaN or
-    // infinite moment gives the same u either way)
+    // fp32 parameters: the direction with the hardware reciprocal and square
+    // root (exact recipe for an element with a tiny v_hat); 16-bit
+    // parameters: the exact recipe
     Mom rr[4];
-    float vmin = INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        rr[i] = moments_fast<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
-        vmin = fminf(vmin, rr[i].v * s.rc2);
-    }
-    if (__any(!(vmin >= 0x1p-96f))) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rr[i] = moments<OPT>(s, a, x.g[i], x.m[i], x.v[i], x.m2[i]);
-    }
+    moments4<OPT, PD == kP32>(s, a, x.g, x.m, x.v, x.m2, rr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const Mom &r = rr[i];

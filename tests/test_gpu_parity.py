@@ -136,17 +136,67 @@ def test_update_norm_prepass(opt, fmt):
     for (t, k, u2, p2) in norms_o:
         g = norms_g[t - 1]
         # Step 1 sees identical inputs on both sides: 1e-12.  Later steps see
-        # p that already differs within its bar: the kernels form the
-        # direction with the hardware reciprocal and square root, so p moves
-        # by a few ulp of lr*|u| per step, which shifts sum p^2 by at most
-        # ~2*max|dp|/rms(p) ~ 1e-7 relative.  The moments, and so sum u^2,
-        # are exact.
+        # an fp32 p that differs from the oracle's within the fp32 bar (the
+        # direction u of an fp32 p uses the hardware reciprocal and square
+        # root), which shifts sum p^2 by at most ~2*max|dp|/rms(p) ~ 1e-7
+        # relative.  The moments, and so sum u^2, are exact.  The pre-pass
+        # itself is held to 1e-12 at every step on the oracle's own inputs
+        # (test_update_norm_prepass_on_oracle_inputs).
         tol_p = 1e-12 if t == 1 else 1e-7
         assert abs(g[2 * k] - u2) <= 1e-12 * abs(u2), (t, k, g[2 * k], u2)
         assert abs(g[2 * k + 1] - p2) <= tol_p * abs(p2), (t, k, g[2 * k + 1], p2)
     # clipping is active: the scale at step 1 is well below 1
     s = oracle.unorm_scale(1.0, norms_o[0][2], norms_o[0][3])
     assert s < 0.1
+
+
+def _prepass_on_oracle_inputs(case):
+    """At every step t, the pre-pass over the oracle's own p and stored states
+    (uploaded to the device) against the oracle's sums over the same inputs:
+    both sums within 1e-12 relative (the oracle sums with compensation, the
+    kernels in a fixed fp64 order).  Then the oracle takes the step."""
+    import torch
+    import optimizer_step_amd as osa
+    ps = [p.copy() for p in case.p0]
+    st = [oracle.state_zeros(case.fmt, n, case.opt, case.qs, case.qu) for n in case.sizes]
+    checked = 0
+    for t in range(1, case.steps + 1):
+        grads = [case.grad(t, k) for k in range(len(case.sizes))]
+        dev = [{"p": to_dev(ps[k].copy()), "g": to_dev(grads[k]),
+                **{key.replace("a", "absmax"): to_dev(v.copy()) for key, v in st[k].items()}}
+               for k in range(len(case.sizes))]
+        h = osa.hparams(step=t, seed=case.seed, qmap_signed=case.qs, qmap_unsigned=case.qu, **case.hp)
+        un = torch.empty(2 * len(case.sizes), dtype=torch.float64, device="cuda")
+        osa.opt_precondition_unorm(case.opt, dev, case.fmt, h, un)
+        got = un.cpu().numpy()
+        for k in range(len(case.sizes)):
+            hp = oracle.make_hp(step=t, seed=case.seed, tensor_index=k, **case.hp)
+            u2, p2 = oracle.unorm(case.opt, case.fmt, hp, ps[k], grads[k], qs=case.qs, qu=case.qu, **st[k])
+            assert abs(got[2 * k] - u2) <= 1e-12 * abs(u2), (t, k, got[2 * k], u2)
+            assert abs(got[2 * k + 1] - p2) <= 1e-12 * abs(p2), (t, k, got[2 * k + 1], p2)
+            checked += int(u2 > 0)
+            scale = oracle.unorm_scale(case.hp["max_unorm"], u2, p2)
+            oracle.step(case.opt, case.fmt, hp, ps[k], grads[k], qs=case.qs, qu=case.qu, scale=scale, **st[k])
+    assert checked >= case.steps
+
+
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_update_norm_prepass_on_oracle_inputs(opt, fmt):
+    hp = dict(_hp(opt), max_unorm=1.0, lr=1e-3)
+    _prepass_on_oracle_inputs(Case(opt, fmt, [65537, 0, 3000], [False, False, True], 4, hp))
+
+
+@pytest.mark.parametrize("fmt", ["f32", "q8", "fp4_sr"])
+def test_update_norm_prepass_on_oracle_inputs_skip_zeros(fmt):
+    """skip_zeros: an element with a zero gradient counts no update."""
+    def grads(t, k, n):
+        g = synth.grads(n, t, k)
+        g[::7] = 0.0
+        g[100:400] = -0.0
+        return g
+    hp = dict(_hp("adamw"), max_unorm=1.0, lr=1e-3, skip_zeros=True)
+    _prepass_on_oracle_inputs(Case("adamw", fmt, [4097, 1500], False, 3, hp, grad_override=grads))
 
 
 @pytest.mark.parametrize("fmt", ["f32", "bf16_sr", "fp8_rn"])
@@ -165,6 +215,7 @@ def test_update_norm_spans_sum_groups(fmt):
         tol_p = 1e-12 if t == 1 else 1e-7   # as in test_update_norm_prepass
         assert abs(g[2 * k] - u2) <= 1e-12 * abs(u2), (t, k, g[2 * k], u2)
         assert abs(g[2 * k + 1] - p2) <= tol_p * abs(p2), (t, k, g[2 * k + 1], p2)
+    _prepass_on_oracle_inputs(case)
 
 
 def test_update_norm_is_deterministic():

@@ -20,6 +20,10 @@ pytestmark = pytest.mark.gpu
 
 N = 300_001
 CUTS = [0, 65536 + 3 * 256, 200_192, N]      # slice boundaries, multiples of 256
+# element-wise formats: slices on multiples of 4 (fp32 arrays) or 8 (16-bit
+# arrays: every pointer must be 16-byte aligned) that are not multiples of 256
+CUTS4 = [0, 1028, 70_004, 200_196, N]
+CUTS8 = [0, 1032, 70_008, 200_200, N]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -57,7 +61,21 @@ def _slice(d, a, b, fmt):
     return out
 
 
-def _run(opt, fmt, p16=None, steps=3):
+def _grads(t, zeros, cuts=CUTS, f32=False):
+    g = synth.grads(N, t, 5, std=1e-2)
+    if zeros:
+        # exact zeros of both signs on both sides of every cut (v = 0 at step
+        # 1); before each element's direction was chosen on its own, such an
+        # element sent its whole wave to the exact recipe, and the waves of a
+        # slice that starts off a 256-element boundary group other elements
+        for c in cuts[1:-1]:
+            g[c - 9:c + 7:3] = 0.0
+            g[c - 2:c + 2:2] = -0.0
+        g[::997] = 0.0
+    return to_dev(g) if f32 else to_dev(synth.bf16_words(g))
+
+
+def _run(opt, fmt, p16=None, steps=3, cuts=CUTS, zeros=False):
     import torch
     import optimizer_step_amd as osa
     one_state = opt in osa.ONE_STATE
@@ -72,10 +90,10 @@ def _run(opt, fmt, p16=None, steps=3):
     results = []
     for sharded, p, st in ((False, p_w, st_w), (True, p_s, st_s)):
         for t in range(1, steps + 1):
-            g = to_dev(synth.grads(N, t, 5, std=1e-2, bf16=True))
+            g = _grads(t, zeros, cuts, f32=fmt == "f32" and cuts is CUTS4)
             if sharded:
                 tl = [other]
-                for a, b in zip(CUTS[:-1], CUTS[1:]):
+                for a, b in zip(cuts[:-1], cuts[1:]):
                     tl.append({"p": p[a:b], "g": g[a:b], **_slice(st, a, b, fmt), "index_base": a, "sr_tensor": 1})
             else:
                 tl = [other, {"p": p, "g": g, **st}]
@@ -96,6 +114,16 @@ def test_slices_step_as_the_whole_tensor(opt, fmt):
     _run(opt, fmt)
 
 
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16_rn", "bf16_sr"])
+def test_unaligned_slices_with_zero_gradients(opt, fmt):
+    """Element-wise formats accept slices on any 16-byte-aligned element (a
+    multiple of 4 for fp32 arrays, here with fp32 gradients; of 8 with BF16
+    words); elements whose gradient is exactly zero sit on both sides of each
+    cut, and every element's result depends on its own inputs only."""
+    _run(opt, fmt, cuts=CUTS4 if fmt == "f32" else CUTS8, zeros=True)
+
+
 @pytest.mark.parametrize("p16", ["bf16", "f16"])
 def test_slices_with_stochastic_16bit_parameters(p16):
     _run("adamw", "bf16_sr", p16=p16)
@@ -113,7 +141,7 @@ def test_shifted_base_changes_the_stream():
     import optimizer_step_amd as osa
     p, st, qs, qu = _fresh("adamw", "bf16_sr", N)
     p2, st2 = p.clone(), {k: v.clone() for k, v in st.items()}
-    g = to_dev(synth.grads(N, 1, 5, std=1e-2, bf16=True))
+    g = _grads(1, False)
     a, b = CUTS[1], CUTS[2]
     h = osa.hparams(step=1, seed=synth.SR_SEED)
     osa.opt_step_adamw(osa.TensorList([{"p": p[a:b], "g": g[a:b], **_slice(st, a, b, "bf16_sr"),

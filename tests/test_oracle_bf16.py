@@ -49,7 +49,9 @@ ALL_R = np.arange(65536, dtype=np.uint32)
 
 
 def test_sr_keeps_representable_values():
-    """A value that is already representable stays as it is, for every r."""
+    """SR of an exactly representable BF16 value returns that same word for
+    each of the 2^16 random integers ("When Small Updates Disappear", Sec. 3:
+    no dropped bits, so no carry)."""
     rng = np.random.default_rng(3)
     words = np.concatenate([rng.integers(0, 65536, 300), [0, 0x8000, 0x7F7F, 0xFF7F, 1, 0x8001, 0x3F80]])
     for w in words.astype(np.uint16):
