@@ -25,15 +25,16 @@ __device__ __forceinline__ uint32_t pack_top_bytes(uint32_t h0, uint32_t h1, uin
     return __builtin_amdgcn_perm(h1, h0, 0x0C0C0703u) | __builtin_amdgcn_perm(h3, h2, 0x07030C0Cu);
 }
 
-// q8_code_hi for the step's fast path, x normal or 0 with |x| <= 1, the table
-// in LDS: the same entry and sum with byte-offset addressing.  s is all ones
-// iff x <= +0 as a signed integer (a saturating b - 1 keeps -0 negative), and
-// picks the odd entry through its bit 2 (the table starts 8-byte aligned).
+// q8_code_hi for the step's fast path, x normal or 0 with |x| <= 1 (for the
+// unsigned table x >= +0, as every v is), the table in LDS: the same entry
+// and sum with byte-offset addressing.  s is all ones iff x <= +0 as a signed
+// integer (a saturating b - 1 keeps -0 negative), and picks the odd entry
+// through its bit 2 (the table starts 8-byte aligned).
 template <bool SIGNED>
 __device__ __forceinline__ uint32_t q8_code_hi_lds(float x, const uint32_t *tab, const QTabParams &P)
 {
     const uint32_t b = fbits(x);
-    const uint32_t a = b & 0x7FFFFFFFu;
+    const uint32_t a = SIGNED ? b & 0x7FFFFFFFu : b;
     const uint32_t d = a > P.lo ? a - P.lo : 0u;
     const uint32_t k = d & ((1u << P.shift) - 1u);
     const uint32_t j = d >> P.shift;
@@ -60,7 +61,7 @@ __device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint
 #pragma unroll
     for (int i = 0; i < 4; ++i) t = min(t, (fbits(x[i]) & 0x7FFFFFFFu) - 1u);
     if (div_by_ok(A) && !__any(t < 0x0D7FFFFFu)) {
-        const float y = 1.0f / A;
+        const float y = recip_rn(A);
         uint32_t h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) h[i] = q8_code_hi_lds<SIGNED>(div_by(x[i], A, y), lds, P);
@@ -274,8 +275,9 @@ __device__ __forceinline__ uint32_t blk_encode4(const uint32_t *lds, const StepA
     return mini_pack4<E4M3, SR>(x, A, r);
 }
 
-// FULL: every lane holds four elements (all blocks but a tensor's short last one).
-template <int OPT, int SF, int PD, bool FULL>
+// FULL: every lane holds four elements (all blocks but a tensor's short last
+// one).  PLAIN: no gradient scale and no skip_zeros in this call.
+template <int OPT, int SF, int PD, bool FULL, bool PLAIN = false>
 __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, const QChunk &C,
                                           const uint32_t *lds, const float *mtab, uint32_t b, int nmine,
                                           int lane, float lam, const QIn &x)
@@ -286,7 +288,7 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
     blk_decode4<SF, 0>(lds, x.cm, x.A1, m_in, mtab);
     blk_decode4<SF, 1>(lds, x.cv, x.A2, v_in, mtab);
     if (OPT == kAdEMAMix) blk_decode4<SF, 2>(lds, x.cm2, x.A3, m2_in, mtab);
-    if (a.fresh) {
+    if (!PLAIN && a.fresh) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) m_in[i] = v_in[i] = m2_in[i] = 0.0f;
     }
@@ -294,7 +296,7 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
     // fp32 p) takes the fast path, per element (moments4).
     float p[4], mo[4], vo[4], m2o[4];
     Mom r[4];
-    moments4<OPT, PD == kP32>(s, a, x.g, m_in, v_in, m2_in, r);
+    moments4<OPT, PD == kP32, !PLAIN>(s, a, x.g, m_in, v_in, m2_in, r);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         p[i] = apply_update(x.p[i], s.d, lam, r[i].u);
@@ -302,7 +304,7 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
         vo[i] = r[i].v;
         m2o[i] = r[i].m2;
     }
-    if (a.skip_zeros) {   // a zero gradient keeps p and codes the old moments again
+    if (!PLAIN && a.skip_zeros) {   // a zero gradient keeps p and codes the old moments again
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (x.g[i] == 0.0f) {
@@ -319,7 +321,8 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
     }
     // stochastic rounding: the element's Philox word, low half for m, high
     // half for v; the second stream's word, low half for m2 and high half
-    // for a 16-bit parameter stored stochastically
+    // for a 16-bit parameter stored stochastically (rm, rv, rm2: the 16 bits
+    // as an integer; rp: the whole word, as the parameter store takes them)
     uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
     const bool psr = PD != kP32 && a.p_sr;
     const uint64_t q = (uint64_t)(C.e0 + e) >> 2;
@@ -331,7 +334,7 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
     if ((sr_fmt(SF) && OPT == kAdEMAMix) || psr) {
         PhiloxOut w2 = sr_block(a.seed, a.step, C.k, q, true);
         rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
-        rp[0] = w2.w0 >> 16; rp[1] = w2.w1 >> 16; rp[2] = w2.w2 >> 16; rp[3] = w2.w3 >> 16;
+        rp[0] = w2.w0; rp[1] = w2.w1; rp[2] = w2.w2; rp[3] = w2.w3;
     }
     const float Am = block_absmax(mo), Av = block_absmax(vo);
     const uint32_t om = blk_encode4<SF, 0>(lds, a, mo, Am, rm);

@@ -100,6 +100,29 @@ __host__ __device__ inline uint32_t bf16_sr(float x, uint32_t r16)
     return (b + r16) >> 16;
 }
 
+// The same two roundings for a pair of values, by gfx950's conversion
+// instructions (x0 in the low half of the result).  Nearest-even is the IEEE
+// conversion; it equals bf16_rne on every non-NaN binary32 word (all 2^32
+// checked on MI355X), and NaNs stay NaNs.  The stochastic conversion adds the
+// HIGH 16 bits of its random operand to the dropped bits: it equals
+// bf16_sr(x, r >> 16) (checked on 2^28 hashed words and random operands);
+// callers pass the element's 16 random bits in the high half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float x0, float x1)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){x0, x1}, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t bf16x2_sr_hi(float x0, uint32_t rh0, float x1, uint32_t rh1)
+{
+    bf16x2_t o = {};
+    o = __builtin_amdgcn_cvt_sr_bf16_f32(o, x0, rh0, false);
+    o = __builtin_amdgcn_cvt_sr_bf16_f32(o, x1, rh1, true);
+    return __builtin_bit_cast(uint32_t, o);
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies and a key-dependent exchange, the key bumped by the
@@ -172,6 +195,24 @@ __host__ __device__ inline float div_by(float a, float b, float y)
 __host__ __device__ inline bool div_by_ok(float b)
 {
     return (fbits(b) & 0x7FFFFFFFu) - 0x01800000u <= 0x4C800000u - 0x01800000u;
+}
+
+// RN(1/b) for b with 2^-126 <= |b| <= 2^126 (the range div_by_ok admits).
+// The hardware reciprocal in binary64 refined by two Newton steps is 1/b to
+// within 2^-52 relative, and 1/b is never that close to a binary32 rounding
+// boundary: a midpoint m of 25 significant bits has |1 - b*m| >= 2^-49 unless
+// b*m = 1, which needs b and m powers of two (m is then no midpoint), so the
+// one rounding to binary32 gives the correctly rounded reciprocal.  Seven
+// instructions, against about a dozen for the IEEE division sequence.
+__device__ __forceinline__ float recip_rn(float b)
+{
+    const double d = (double)b;
+    double r = __builtin_amdgcn_rcp(d);
+    double e = __builtin_fma(-d, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-d, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    return (float)r;
 }
 
 // Dividends for which div_by is correctly rounded (with a divisor that passes
@@ -450,12 +491,12 @@ __device__ inline float lam_for(const StepArgs &a, int32_t k)
 
 struct Mom { float m, v, m2, u; };
 
-template <int OPT>
+template <int OPT, bool GS = true>
 __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, float g, float m,
                                        float v, float m2)
 {
     Mom r;
-    g = g * s.gs;            // clipping fused into the step (exact for a scale of 1)
+    if (GS) g = g * s.gs;    // clipping fused into the step (GS false: no scale given)
     float gg = g * g;
     r.m = a.beta1 * m + s.om1 * g;
     r.v = a.beta2 * v + s.om2 * gg;
@@ -486,12 +527,12 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
 // hardware square root loses accuracy) takes the exact recipe (fast_ok), so
 // every element's result depends on its own inputs alone.  NaN and infinite
 // moments give the same u either way.
-template <int OPT>
+template <int OPT, bool GS = true>
 __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a, float g, float m,
                                             float v, float m2)
 {
     Mom r;
-    g = g * s.gs;
+    if (GS) g = g * s.gs;
     float gg = g * g;
     r.m = a.beta1 * m + s.om1 * g;
     r.v = a.beta2 * v + s.om2 * gg;
@@ -521,25 +562,25 @@ __device__ __forceinline__ bool fast_ok(const Scalars &s, const Mom &r)
 // exact recipe throughout (16-bit parameters, whose rounded store must see
 // exactly the oracle's binary32 value).  The wave skips the exact pass when
 // no lane needs it; the result of an element never depends on other lanes.
-template <int OPT, bool FAST>
+template <int OPT, bool FAST, bool GS = true>
 __device__ __forceinline__ void moments4(const Scalars &s, const StepArgs &a, const float g[4],
                                          const float m[4], const float v[4], const float m2[4], Mom r[4])
 {
     if (!FAST) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = moments<OPT>(s, a, g[i], m[i], v[i], m2[i]);
+        for (int i = 0; i < 4; ++i) r[i] = moments<OPT, GS>(s, a, g[i], m[i], v[i], m2[i]);
         return;
     }
     bool slow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        r[i] = moments_fast<OPT>(s, a, g[i], m[i], v[i], m2[i]);
+        r[i] = moments_fast<OPT, GS>(s, a, g[i], m[i], v[i], m2[i]);
         slow[i] = !fast_ok<OPT>(s, r[i]);
     }
     if (__any(slow[0] || slow[1] || slow[2] || slow[3])) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (slow[i]) r[i] = moments<OPT>(s, a, g[i], m[i], v[i], m2[i]);
+            if (slow[i]) r[i] = moments<OPT, GS>(s, a, g[i], m[i], v[i], m2[i]);
     }
 }
 

@@ -74,7 +74,10 @@ __device__ __forceinline__ float load_grad1(const void *g, int64_t e)
 }
 
 // Parameters: fp32, or BF16 / FP16 words widened exactly and stored back
-// rounded to nearest-even or, with sr, stochastically by the 16-bit r.
+// rounded to nearest-even or, with sr, stochastically.  Every random operand
+// of the stores below carries the element's 16 random bits in its HIGH half
+// (the low half is ignored), the convention of gfx950's stochastic BF16
+// conversion.
 template <int PD>
 __device__ __forceinline__ void load_p4(const float *p, int64_t e, float out[4])
 {
@@ -95,30 +98,34 @@ __device__ __forceinline__ float load_p1(const float *p, int64_t e)
 }
 
 template <int PD>
-__device__ __forceinline__ uint32_t round_p(float x, bool sr, uint32_t r)
+__device__ __forceinline__ uint32_t round_p(float x, bool sr, uint32_t rh)
 {
-    if (PD == kPBF16) return sr ? bf16_sr(x, r) : bf16_rne(x);
-    return sr ? f16_sr(x, r) : f16_rne(x);
+    if (PD == kPBF16) return sr ? bf16_sr(x, rh >> 16) : bf16_rne(x);
+    return sr ? f16_sr(x, rh >> 16) : f16_rne(x);
 }
 
 template <int PD>
-__device__ __forceinline__ void store_p4(float *p, int64_t e, const float x[4], bool sr, const uint32_t r[4])
+__device__ __forceinline__ void store_p4(float *p, int64_t e, const float x[4], bool sr, const uint32_t rh[4])
 {
     if (PD == kP32) {
         sst<f4>(p + e, f4{x[0], x[1], x[2], x[3]});
+    } else if (PD == kPBF16) {
+        u2 w = sr ? u2{bf16x2_sr_hi(x[0], rh[0], x[1], rh[1]), bf16x2_sr_hi(x[2], rh[2], x[3], rh[3])}
+                  : u2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])};
+        sst<u2>((uint16_t *)(void *)p + e, w);
     } else {
         uint32_t h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = round_p<PD>(x[i], sr, r[i]);
+        for (int i = 0; i < 4; ++i) h[i] = round_p<PD>(x[i], sr, rh[i]);
         sst<u2>((uint16_t *)(void *)p + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
     }
 }
 
 template <int PD>
-__device__ __forceinline__ void store_p1(float *p, int64_t e, float x, bool sr, uint32_t r)
+__device__ __forceinline__ void store_p1(float *p, int64_t e, float x, bool sr, uint32_t rh)
 {
     if (PD == kP32) gst<float>(p + e, x);
-    else gst<uint16_t>((uint16_t *)(void *)p + e, (uint16_t)round_p<PD>(x, sr, r));
+    else gst<uint16_t>((uint16_t *)(void *)p + e, (uint16_t)round_p<PD>(x, sr, rh));
 }
 
 template <int SF>
@@ -141,26 +148,25 @@ __device__ __forceinline__ float load_state1(const void *s, int64_t e)
     return bf16_lo(gld<uint16_t>((const uint16_t *)s + e));
 }
 
-// Store four fp32 moments in format SF; r[i] are the 16-bit random integers of
-// stochastic rounding (ignored otherwise).
+// Store four fp32 moments in format SF; rh[i] hold the 16 random bits of
+// stochastic rounding in their high half (ignored by the other formats).
 template <int SF>
-__device__ __forceinline__ void store_state4(void *s, int64_t e, const float x[4], const uint32_t r[4])
+__device__ __forceinline__ void store_state4(void *s, int64_t e, const float x[4], const uint32_t rh[4])
 {
     if (SF == kF32) {
         sst<f4>((float *)s + e, f4{x[0], x[1], x[2], x[3]});
+    } else if (SF == kBF16SR) {
+        sst<u2>((uint16_t *)s + e, u2{bf16x2_sr_hi(x[0], rh[0], x[1], rh[1]), bf16x2_sr_hi(x[2], rh[2], x[3], rh[3])});
     } else {
-        uint32_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = SF == kBF16SR ? bf16_sr(x[i], r[i]) : bf16_rne(x[i]);
-        sst<u2>((uint16_t *)s + e, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        sst<u2>((uint16_t *)s + e, u2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])});
     }
 }
 
 template <int SF>
-__device__ __forceinline__ void store_state1(void *s, int64_t e, float x, uint32_t r)
+__device__ __forceinline__ void store_state1(void *s, int64_t e, float x, uint32_t rh)
 {
     if (SF == kF32) gst<float>((float *)s + e, x);
-    else gst<uint16_t>((uint16_t *)s + e, (uint16_t)(SF == kBF16SR ? bf16_sr(x, r) : bf16_rne(x)));
+    else gst<uint16_t>((uint16_t *)s + e, (uint16_t)(SF == kBF16SR ? bf16_sr(x, rh >> 16) : bf16_rne(x)));
 }
 
 // ---------------------------------------------------------------------------
@@ -204,6 +210,10 @@ __device__ __forceinline__ bool locate_tile(const DevTensor *__restrict__ tens, 
     len = min(a.tile, T.numel - e0);
     return len > 0;
 }
+
+// A call with no gradient scale, no skip_zeros and no state reset on this
+// step: the step kernels have a variant that spends no instruction on any.
+__host__ inline bool plain_call(const StepArgs &a) { return a.grad_scale == nullptr && !a.skip_zeros && !a.fresh; }
 
 // The per-call scalars, formed by lane 0 and read by every lane after the
 // workgroup's barrier.

@@ -437,6 +437,9 @@ __global__ void debug_round_kernel(const float *x, const uint32_t *r, uint16_t *
         out[i] = (uint16_t)(r ? bf16_sr(x[i], r[i] & 0xFFFFu) : bf16_rne(x[i]));
 }
 
+// codes[i] of x[i] against one codebook's table in LDS.  Inputs in the step's
+// fast-path domain (|x| <= 1, normal or zero; for the unsigned table x >= +0)
+// take the step's own lookup (q8_code_hi_lds); other inputs the general one.
 __global__ void debug_quantize_kernel(QTabs q, int is_signed, const float *x, uint8_t *out, int64_t n)
 {
     extern __shared__ uint32_t lds[];
@@ -445,8 +448,14 @@ __global__ void debug_quantize_kernel(QTabs q, int is_signed, const float *x, ui
     const QTabParams P = is_signed ? q.s : q.u;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
-        float v = x[i];
-        out[i] = (uint8_t)(v != v ? 0u : q8_lookup(v, lds, P, is_signed != 0));
+        const float v = x[i];
+        const uint32_t b = fbits(v), a = b & 0x7FFFFFFFu;
+        const bool step_domain = a <= 0x3F800000u && (a == 0u || a >= 0x00800000u) && (is_signed || (b >> 31) == 0u);
+        uint32_t c;
+        if (v != v) c = 0u;
+        else if (step_domain) c = (is_signed ? q8_code_hi_lds<true>(v, lds, P) : q8_code_hi_lds<false>(v, lds, P)) >> 24;
+        else c = q8_lookup(v, lds, P, is_signed != 0);
+        out[i] = (uint8_t)c;
     }
 }
 

@@ -108,7 +108,7 @@ __device__ __forceinline__ void s1_finish(const StepArgs &a, const Scalars1 &s, 
     }
     if (SF == kBF16SR) {
         const PhiloxOut w = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false);
-        r[0] = w.w0 & 0xFFFFu; r[1] = w.w1 & 0xFFFFu; r[2] = w.w2 & 0xFFFFu; r[3] = w.w3 & 0xFFFFu;
+        r[0] = w.w0 << 16; r[1] = w.w1 << 16; r[2] = w.w2 << 16; r[3] = w.w3 << 16;   // low halves, moved up
     }
     sst<f4>(T.p + e, f4{x.p[0], x.p[1], x.p[2], x.p[3]});
     store_state4<SF>(T.s1, e, sn, r);
@@ -129,7 +129,7 @@ __device__ __forceinline__ void s1_single(const StepArgs &a, const Scalars1 &s, 
     }
     uint32_t r = 0;
     if (SF == kBF16SR)
-        r = philox_word(sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false), (int)(e & 3)) & 0xFFFFu;
+        r = philox_word(sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false), (int)(e & 3)) << 16;
     gst<float>(T.p + e, p);
     store_state1<SF>(T.s1, e, sn, r);
 }

@@ -38,7 +38,9 @@ __device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fres
     }
 }
 
-template <int OPT, int GD, int SF, int PD>
+// PLAIN: no gradient scale and no skip_zeros in this call (a uniform choice
+// made by the launcher), so neither costs an instruction per element.
+template <int OPT, int GD, int SF, int PD, bool PLAIN>
 __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
                                           int64_t e, float lam, Group &x)
 {
@@ -47,31 +49,32 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
     // root (exact recipe for an element with a tiny v_hat); 16-bit
     // parameters: the exact recipe
     Mom rr[4];
-    moments4<OPT, PD == kP32>(s, a, x.g, x.m, x.v, x.m2, rr);
+    moments4<OPT, PD == kP32, !PLAIN>(s, a, x.g, x.m, x.v, x.m2, rr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const Mom &r = rr[i];
         const float pn = apply_update(x.p[i], s.d, lam, r.u);
         mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
-        if (a.skip_zeros && x.g[i] == 0.0f) {   // p (decay included) and the states as they were
+        if (!PLAIN && a.skip_zeros && x.g[i] == 0.0f) {   // p (decay included) and the states as they were
             mo[i] = x.m[i]; vo[i] = x.v[i]; m2o[i] = x.m2[i];
         } else {
             x.p[i] = pn;
         }
     }
-    // stochastic rounding: the first stream's word rounds m (low half) and v
-    // (high half), the second stream's m2 (low half) and a 16-bit p (high half)
+    // stochastic rounding: the first stream's word rounds m (its low half) and
+    // v (its high half), the second stream's m2 (low half) and a 16-bit p
+    // (high half); the stores take the 16 bits in the high half of a word
     uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
     if (SF == kBF16SR) {
         PhiloxOut w = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false);
-        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
-        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
+        rm[0] = w.w0 << 16; rm[1] = w.w1 << 16; rm[2] = w.w2 << 16; rm[3] = w.w3 << 16;
+        rv[0] = w.w0; rv[1] = w.w1; rv[2] = w.w2; rv[3] = w.w3;
     }
     const bool psr = PD != kP32 && a.p_sr;
     if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
         PhiloxOut w2 = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, true);
-        rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
-        rp[0] = w2.w0 >> 16; rp[1] = w2.w1 >> 16; rp[2] = w2.w2 >> 16; rp[3] = w2.w3 >> 16;
+        rm2[0] = w2.w0 << 16; rm2[1] = w2.w1 << 16; rm2[2] = w2.w2 << 16; rm2[3] = w2.w3 << 16;
+        rp[0] = w2.w0; rp[1] = w2.w1; rp[2] = w2.w2; rp[3] = w2.w3;
     }
     store_p4<PD>(T.p, e, x.p, psr, rp);
     store_state4<SF>(T.s1, e, mo, rm);
@@ -97,15 +100,15 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
         pn = p_old;
         r.m = m; r.v = v; r.m2 = m2;
     }
-    uint32_t rm = 0, rv = 0, rm2 = 0, rp = 0;
+    uint32_t rm = 0, rv = 0, rm2 = 0, rp = 0;   // random bits in the high half, as in ew_finish
     if (SF == kBF16SR) {
         uint32_t w = philox_word(sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false), (int)(e & 3));
-        rm = w & 0xFFFFu; rv = w >> 16;
+        rm = w << 16; rv = w;
     }
     const bool psr = PD != kP32 && a.p_sr;
     if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
         uint32_t w2 = philox_word(sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, true), (int)(e & 3));
-        rm2 = w2 & 0xFFFFu; rp = w2 >> 16;
+        rm2 = w2 << 16; rp = w2;
     }
     store_p1<PD>(T.p, e, pn, psr, rp);
     store_state1<SF>(T.s1, e, r.m, rm);
@@ -128,7 +131,7 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
 constexpr int kEwThreads = OPT_EW_THREADS;
 constexpr int64_t kEwTile = (int64_t)kEwThreads * kEwGroups * 4;
 
-template <int OPT, int GD, int SF, int PD>
+template <int OPT, int GD, int SF, int PD, bool PLAIN>
 __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
                                                                        const int32_t *__restrict__ ctab, StepArgs a)
 {
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
-                ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * (threadIdx.x + u * kEwThreads), lam, x[u]);
+                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, T, e0 + 4 * (threadIdx.x + u * kEwThreads), lam, x[u]);
         } else {   // a tensor's last, short tile
             if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
             for (int64_t i = threadIdx.x; i < ngroups; i += kEwThreads) {
                 Group x0;
                 ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
-                ew_finish<OPT, GD, SF, PD>(a, s, T, e0 + 4 * i, lam, x0);
+                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, T, e0 + 4 * i, lam, x0);
             }
             const int64_t tail = len & 3;
             if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);
@@ -167,15 +170,21 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
     }
 }
 
+template <int OPT, int GD, int PD, bool PLAIN>
+static hipError_t launch_ew_p(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
+{
+    switch (fmt) {
+    case kF32: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD, PLAIN>, kEwTile, 0, lg, a, st);
+    case kBF16RN: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, kEwTile, 0, lg, a, st);
+    case kBF16SR: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, kEwTile, 0, lg, a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int OPT, int GD, int PD>
 static hipError_t launch_ew_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
 {
-    switch (fmt) {
-    case kF32: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD>, kEwTile, 0, lg, a, st);
-    case kBF16RN: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD>, kEwTile, 0, lg, a, st);
-    case kBF16SR: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD>, kEwTile, 0, lg, a, st);
-    default: return hipErrorInvalidValue;
-    }
+    return plain_call(a) ? launch_ew_p<OPT, GD, PD, true>(fmt, a, lg, st) : launch_ew_p<OPT, GD, PD, false>(fmt, a, lg, st);
 }
 
 template <int OPT, int GD>

@@ -23,6 +23,17 @@ constexpr int kQ8Waves = kQ8Threads / 64;
 constexpr int64_t kQ8Tile = OPT_Q8_TILE;
 static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 
+#ifndef OPT_MINI_TILE
+#define OPT_MINI_TILE 8192
+#endif
+// Elements per tile of the FP8/FP4 formats, which load no lookup table: four
+// passes of the workgroup's waves.  Measured on MI355X, FP8 nearest: 8 K and
+// 4 K tiles 2.70 ms, 16 K 2.83 ms, 32 K 2.80 ms, 2 K 3.09 ms per 2^30
+// elements; the 8-bit format, whose tables every workgroup copies into LDS,
+// keeps 32 K (16 K 2.84, 8 K 2.91, 4 K 3.14, 2 K 4.06 ms against 2.80).
+constexpr int64_t kMiniTile = OPT_MINI_TILE;
+static_assert(kMiniTile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
+
 #ifndef OPT_Q8_WAVES
 #define OPT_Q8_WAVES 7
 #endif
@@ -31,7 +42,7 @@ static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 constexpr int kQ8WavesAdamW = OPT_Q8_WAVES;
 
 // The tiles of one workgroup: one 256-element block per wave at a time.
-template <int OPT, int GD, int SF, int PD>
+template <int OPT, int GD, int SF, int PD, bool PLAIN>
 __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, const int32_t *__restrict__ ctab,
                                          const StepArgs &a, const Scalars &s, const uint32_t *lds,
                                          const float *mtab, int lane, int wave)
@@ -50,20 +61,20 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
             load_prio_hi();
             q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
             load_prio_lo();
-            q8_finish<OPT, SF, PD, true>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
+            q8_finish<OPT, SF, PD, true, PLAIN>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
         }
         if (b < nblk) {   // the tensor's short last block
             const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
             QIn x0;
             q8_load<OPT, GD, SF, PD, false>(a, C, b, nm, lane, x0);
-            q8_finish<OPT, SF, PD, false>(a, s, C, lds, mtab, b, nm, lane, lam, x0);
+            q8_finish<OPT, SF, PD, false, PLAIN>(a, s, C, lds, mtab, b, nm, lane, lam, x0);
         }
     }
 }
 
 // Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
 // tile scheduling of opt_elem.h).
-template <int OPT, int GD, int SF, int PD>
+template <int OPT, int GD, int SF, int PD, bool PLAIN>
 __global__ __launch_bounds__(kQ8Threads)
 __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
                                                              const int32_t *__restrict__ ctab,
@@ -82,17 +93,18 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
     if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
     const Scalars s = sh;
-    q8_tiles<OPT, GD, SF, PD>(tens, ctab, a, s, lds, mtab, lane, wave);
+    q8_tiles<OPT, GD, SF, PD, PLAIN>(tens, ctab, a, s, lds, mtab, lane, wave);
 }
 
 // ---------------------------------------------------------------------------
 // launchers (called by opt_api.cpp)
 
-// The blockwise step over tiles of kQ8Tile elements (opt_elem.h).
+// The blockwise step over tiles of `tile` elements (opt_elem.h).
 template <class K>
-static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
+static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st,
+                                  int64_t tile = kQ8Tile)
 {
-    set_tiles(a, kQ8Tile);
+    set_tiles(a, tile);
     hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kQ8Threads), lds, st, a.tens, a.chunk_tensor,
                        a.q.words, a);
     return hipGetLastError();
@@ -100,17 +112,24 @@ static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, St
 
 hipError_t launch_step_ew(int opt, int gd, int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st);
 
+template <int OPT, int GD, int PD, bool PLAIN>
+static hipError_t launch_q8_pl(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
+{
+    switch (fmt) {
+    case kQ8: return launch_q8_tiles(step_q8_kernel<OPT, GD, kQ8, PD, PLAIN>, lds, lg, a, st);
+    case kFP8RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8RN, PD, PLAIN>, 0, lg, a, st, kMiniTile);
+    case kFP8SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8SR, PD, PLAIN>, 0, lg, a, st, kMiniTile);
+    case kFP4RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4RN, PD, PLAIN>, 0, lg, a, st, kMiniTile);
+    case kFP4SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4SR, PD, PLAIN>, 0, lg, a, st, kMiniTile);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int OPT, int GD, int PD>
 static hipError_t launch_q8_pd(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
-    switch (fmt) {
-    case kQ8: return launch_q8_tiles(step_q8_kernel<OPT, GD, kQ8, PD>, lds, lg, a, st);
-    case kFP8RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8RN, PD>, 0, lg, a, st);
-    case kFP8SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8SR, PD>, 0, lg, a, st);
-    case kFP4RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4RN, PD>, 0, lg, a, st);
-    case kFP4SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4SR, PD>, 0, lg, a, st);
-    default: return hipErrorInvalidValue;
-    }
+    return plain_call(a) ? launch_q8_pl<OPT, GD, PD, true>(fmt, a, lg, lds, st)
+                         : launch_q8_pl<OPT, GD, PD, false>(fmt, a, lg, lds, st);
 }
 
 // This translation unit holds the kernels for one parameter storage,

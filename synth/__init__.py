@@ -209,6 +209,15 @@ WORKLOADS = {
     **{f"{o}_f32_1g": dict(opt=o, fmt="f32", sizes=[2**30], grad_bf16=True, p_std=0.02, g_std=1e-3, steps=5,
                           hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.99, eps=1e-8))
        for o in ("momentum", "lion")},
+    # BF16 parameters (a mixed-precision model without fp32 master weights):
+    # stored with stochastic rounding next to BF16-SR states, or to nearest
+    # next to fp32 states; the direction is then formed exactly
+    "adamw_bf16p_bf16_sr_1g": dict(opt="adamw", fmt="bf16_sr", sizes=[2**30], grad_bf16=True, p_dtype="bf16",
+                                   p_sr=True, p_std=0.02, g_std=1e-3, steps=5,
+                                   hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)),
+    "adamw_bf16p_f32_1g": dict(opt="adamw", fmt="f32", sizes=[2**30], grad_bf16=True, p_dtype="bf16",
+                               p_std=0.02, g_std=1e-3, steps=5,
+                               hp=dict(lr=1e-3, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8)),
     # the standalone FP32 -> BF16 stochastic-rounding cast of 2^30 values
     "cast_bf16_sr_1g": dict(opt="cast", fmt="bf16_sr", sizes=[2**30], grad_bf16=False, p_std=1.0, g_std=1e-3,
                             steps=5, hp=dict()),

@@ -467,3 +467,40 @@ def test_quantizer_matches_oracle(signed):
     out = torch.empty(x.size, dtype=torch.uint8, device="cuda")
     osa.opt_debug_quantize(T, signed, to_dev(x), out)
     assert np.array_equal(out.cpu().numpy(), oracle.quantize_array(T, x))
+
+
+@pytest.mark.parametrize("signed", [True, False], ids=["signed", "unsigned"])
+def test_device_lookup_on_every_value_in_unit_interval(signed):
+    """The step's 8-bit lookup on the device, on every binary32 word in
+    [-1, 1] (inputs generated on the device, 2^28 words a launch).  Expected:
+    the count of thresholds tau_i <= x, tau_i the smallest binary32 above the
+    binary64 midpoint (T_i + T_{i+1})/2 -- the nearest entry, ties to the
+    lower index; an unsigned table gives 0 to every x <= 0."""
+    import torch
+    import optimizer_step_amd as osa
+    T = synth.codebook_signed() if signed else synth.codebook_unsigned()
+    t = (T[:-1].astype(np.float64) + T[1:].astype(np.float64)) / 2
+    tau = t.astype(np.float32)
+    tau[tau.astype(np.float64) <= t] = np.nextafter(tau[tau.astype(np.float64) <= t], np.float32(np.inf))
+    tau_d = torch.from_numpy(tau).cuda()
+    one, chunk = 0x3F800000, 1 << 28
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    checked = 0
+    for neg in (False, True):
+        for lo in range(0, one + 1, chunk):
+            hi = min(lo + chunk, one + 1)
+            w = torch.arange(lo, hi, dtype=torch.int64, device="cuda")
+            if neg:
+                w = w - 2**31                        # the same magnitudes with the sign bit set (int32 view)
+            x = w.to(torch.int32).view(torch.float32)
+            o = out[:hi - lo]
+            osa.opt_debug_quantize(T, signed, x, o)
+            want = torch.searchsorted(tau_d, x, right=True).to(torch.uint8)
+            if not signed and neg:
+                want.zero_()
+            bad = int((o != want).sum())
+            assert bad == 0, (signed, neg, lo, bad)
+            checked += hi - lo
+            del w, x, want
+    assert checked == 2 * (one + 1)
+    torch.cuda.synchronize()
