@@ -193,15 +193,23 @@ uint32_t orc_sr_word(uint64_t seed, int64_t t, int32_t k, int64_t j, int32_t str
  * the nearest entry, ties to the lower index.  Written as a count of the
  * midpoints x lies strictly above; each midpoint is formed in binary64, where
  * (T[i] + T[i+1]) / 2 is exact for entries of similar size.  NaN lies above
- * no midpoint and gets code 0.                                            */
+ * no midpoint and gets code 0.  The midpoints never decrease with i (a
+ * rounded sum is monotone), so those below x are a prefix of them and the
+ * count is found by bisection: the first midpoint not below x.          */
+static double q8_mid(const float *T, int i)
+{
+    return ((double)T[i] + (double)T[i + 1]) / 2.0;
+}
+
 int orc_quantize(const float *T, float x)
 {
-    int code = 0;
-    for (int i = 0; i < 255; ++i) {
-        double mid = ((double)T[i] + (double)T[i + 1]) / 2.0;
-        if ((double)x > mid) ++code;
+    int lo = 0, hi = 255;            /* the count lies in [lo, hi] */
+    while (lo < hi) {
+        int m = (lo + hi) / 2;
+        if ((double)x > q8_mid(T, m)) lo = m + 1;
+        else hi = m;
     }
-    return code;
+    return lo;
 }
 
 /* ------------------------------------------------------------------ */
