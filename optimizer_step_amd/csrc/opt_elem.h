@@ -170,6 +170,102 @@ __device__ __forceinline__ void store_state1(void *s, int64_t e, float x, uint32
 }
 
 // ---------------------------------------------------------------------------
+// The same group loads and stores addressed as a wave-uniform base pointer
+// plus a 32-bit byte offset per lane (base + zero-extended offset: the
+// global_* saddr form, one VGPR per address instead of two).  i is the
+// element index within the run that starts at the base (i * 4 < 2^32).
+
+template <class V>
+__device__ __forceinline__ V sld_at(const void *base, uint32_t off)
+{
+    return sld<V>((const char *)base + off);
+}
+
+// Stores of the element-wise steps: the global store with the non-temporal
+// hint, or (SC1) a buffer store with the system-coherence bit and no
+// non-temporal hint.  Paired on MI355X in one process over one arena, on two
+// boxes: the 290-tensor AdamW step (fp32 p, m, v; BF16 g) 30.01 -> 29.29 ms
+// and 30.02 -> 29.31 ms with SC1 on its 16-byte stores; the same policy cost
+// 2.7 % on AdEMAMix (fp32 g) and 0.8-1.3 % on BF16-state and BF16-parameter
+// steps, so only that configuration takes it.  The buffer resource spans
+// 2^32 - 1 bytes from the tile's base; every offset here is below a tile's
+// bytes.
+template <bool SC1, class V>
+__device__ __forceinline__ void sst_at(void *base, uint32_t off, V v)
+{
+    if constexpr (SC1 && sizeof(V) == 16) {
+        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, -1, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 16 /* sc1 */);
+    } else {
+        sst<V>((char *)base + off, v);
+    }
+}
+
+template <int PD>
+__device__ __forceinline__ void load_p4_at(const void *p, uint32_t i, float out[4])
+{
+    if (PD == kP32) {
+        f4 x = sld_at<f4>(p, i * 4u);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        widen4<PD == kPBF16>(sld_at<u2>(p, i * 2u), out);
+    }
+}
+
+template <int GD>
+__device__ __forceinline__ void load_grad4_at(const void *g, uint32_t i, float out[4])
+{
+    if (GD == kGradF32) {
+        f4 x = sld_at<f4>(g, i * 4u);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        widen4<GD == kGradBF16>(sld_at<u2>(g, i * 2u), out);
+    }
+}
+
+template <int SF>
+__device__ __forceinline__ void load_state4_at(const void *s, uint32_t i, float out[4])
+{
+    if (SF == kF32) {
+        f4 x = sld_at<f4>(s, i * 4u);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        u2 w = sld_at<u2>(s, i * 2u);
+        out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+        out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    }
+}
+
+template <int PD, bool SC1 = false>
+__device__ __forceinline__ void store_p4_at(void *p, uint32_t i, const float x[4], bool sr, const uint32_t rh[4])
+{
+    if (PD == kP32) {
+        sst_at<SC1, f4>(p, i * 4u, f4{x[0], x[1], x[2], x[3]});
+    } else if (PD == kPBF16) {
+        u2 w = sr ? u2{bf16x2_sr_hi(x[0], rh[0], x[1], rh[1]), bf16x2_sr_hi(x[2], rh[2], x[3], rh[3])}
+                  : u2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])};
+        sst_at<false, u2>(p, i * 2u, w);
+    } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[k] = round_p<PD>(x[k], sr, rh[k]);
+        sst_at<false, u2>(p, i * 2u, u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+    }
+}
+
+template <int SF, bool SC1 = false>
+__device__ __forceinline__ void store_state4_at(void *s, uint32_t i, const float x[4], const uint32_t rh[4])
+{
+    if (SF == kF32) {
+        sst_at<SC1, f4>(s, i * 4u, f4{x[0], x[1], x[2], x[3]});
+    } else if (SF == kBF16SR) {
+        sst_at<false, u2>(s, i * 2u, u2{bf16x2_sr_hi(x[0], rh[0], x[1], rh[1]), bf16x2_sr_hi(x[2], rh[2], x[3], rh[3])});
+    } else {
+        sst_at<false, u2>(s, i * 2u, u2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])});
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tile scheduling.  A launch covers its bucket's chunk space in tiles of
 // consecutive elements of one tensor; a chunk of the host's table (a power of
 // two, as is the kernel's tile) holds chunk/tile of them.  By default the grid

@@ -24,25 +24,49 @@ struct Group {
     float p[4], g[4], m[4], v[4], m2[4];
 };
 
+// One tile's arrays: the tensor's arrays advanced to the tile's first element
+// (wave-uniform), addressed by a 32-bit element index within the tile.
+struct TileRef {
+    void *p, *s1, *s2, *s3;
+    const void *g;
+    int64_t j0;      // element index of the tile's first element within the whole tensor
+    uint32_t rk;     // the tensor number of its stochastic-rounding stream
+};
+
 template <int OPT, int GD, int SF, int PD>
-__device__ __forceinline__ void ew_load(const DevTensor &T, int64_t e, bool fresh, Group &x)
+__device__ __forceinline__ TileRef tile_ref(const DevTensor &T, int64_t e0)
 {
-    load_p4<PD>(T.p, e, x.p);
-    load_grad4<GD>(T.g, e, x.g);
+    constexpr int pb = PD == kP32 ? 4 : 2, gb = GD == kGradF32 ? 4 : 2, sb = SF == kF32 ? 4 : 2;
+    TileRef r;
+    r.p = (char *)(void *)T.p + e0 * pb;
+    r.g = (const char *)T.g + e0 * gb;
+    r.s1 = (char *)T.s1 + e0 * sb;
+    r.s2 = (char *)T.s2 + e0 * sb;
+    r.s3 = OPT == kAdEMAMix ? (void *)((char *)T.s3 + e0 * sb) : nullptr;
+    r.j0 = T.jbase + e0;
+    r.rk = T.rk;
+    return r;
+}
+
+template <int OPT, int GD, int SF, int PD>
+__device__ __forceinline__ void ew_load(const TileRef &R, uint32_t i, bool fresh, Group &x)
+{
+    load_p4_at<PD>(R.p, i, x.p);
+    load_grad4_at<GD>(R.g, i, x.g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x.m[i] = x.v[i] = x.m2[i] = 0.0f;
+    for (int k = 0; k < 4; ++k) x.m[k] = x.v[k] = x.m2[k] = 0.0f;
     if (!fresh) {   // a step that restarts the moments from zero reads none
-        load_state4<SF>(T.s1, e, x.m);
-        load_state4<SF>(T.s2, e, x.v);
-        if (OPT == kAdEMAMix) load_state4<SF>(T.s3, e, x.m2);
+        load_state4_at<SF>(R.s1, i, x.m);
+        load_state4_at<SF>(R.s2, i, x.v);
+        if (OPT == kAdEMAMix) load_state4_at<SF>(R.s3, i, x.m2);
     }
 }
 
 // PLAIN: no gradient scale and no skip_zeros in this call (a uniform choice
 // made by the launcher), so neither costs an instruction per element.
 template <int OPT, int GD, int SF, int PD, bool PLAIN>
-__device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const DevTensor &T,
-                                          int64_t e, float lam, Group &x)
+__device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, const TileRef &R,
+                                          uint32_t i, float lam, Group &x)
 {
     float mo[4], vo[4], m2o[4];
     // fp32 parameters: the direction with the hardware reciprocal and square
@@ -65,21 +89,24 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
     // v (its high half), the second stream's m2 (low half) and a 16-bit p
     // (high half); the stores take the 16 bits in the high half of a word
     uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
+    const uint64_t q = (uint64_t)(R.j0 + i) >> 2;
     if (SF == kBF16SR) {
-        PhiloxOut w = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, false);
+        PhiloxOut w = sr_block(a.seed, a.step, R.rk, q, false);
         rm[0] = w.w0 << 16; rm[1] = w.w1 << 16; rm[2] = w.w2 << 16; rm[3] = w.w3 << 16;
         rv[0] = w.w0; rv[1] = w.w1; rv[2] = w.w2; rv[3] = w.w3;
     }
     const bool psr = PD != kP32 && a.p_sr;
     if ((SF == kBF16SR && OPT == kAdEMAMix) || psr) {
-        PhiloxOut w2 = sr_block(a.seed, a.step, T.rk, (uint64_t)(T.jbase + e) >> 2, true);
+        PhiloxOut w2 = sr_block(a.seed, a.step, R.rk, q, true);
         rm2[0] = w2.w0 << 16; rm2[1] = w2.w1 << 16; rm2[2] = w2.w2 << 16; rm2[3] = w2.w3 << 16;
         rp[0] = w2.w0; rp[1] = w2.w1; rp[2] = w2.w2; rp[3] = w2.w3;
     }
-    store_p4<PD>(T.p, e, x.p, psr, rp);
-    store_state4<SF>(T.s1, e, mo, rm);
-    store_state4<SF>(T.s2, e, vo, rv);
-    if (OPT == kAdEMAMix) store_state4<SF>(T.s3, e, m2o, rm2);
+    // the store policy measured fastest for this configuration (opt_elem.h)
+    constexpr bool sc1 = OPT == kAdamW && GD != kGradF32 && SF == kF32 && PD == kP32;
+    store_p4_at<PD, sc1>(R.p, i, x.p, psr, rp);
+    store_state4_at<SF, sc1>(R.s1, i, mo, rm);
+    store_state4_at<SF, sc1>(R.s2, i, vo, rv);
+    if (OPT == kAdEMAMix) store_state4_at<SF>(R.s3, i, m2o, rm2);
 }
 
 template <int OPT, int GD, int SF, int PD>
@@ -143,26 +170,27 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
         DevTensor T;
         int64_t e0, len;
         if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
+        const TileRef R = tile_ref<OPT, GD, SF, PD>(T, e0);
         if (len == kEwTile) {
             Group x[kEwGroups];
             load_prio_hi(SF != kBF16RN);
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
-                ew_load<OPT, GD, SF, PD>(T, e0 + 4 * (threadIdx.x + u * kEwThreads), fresh, x[u]);
+                ew_load<OPT, GD, SF, PD>(R, 4u * (threadIdx.x + u * kEwThreads), fresh, x[u]);
             load_prio_lo(SF != kBF16RN);
             if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
-                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, T, e0 + 4 * (threadIdx.x + u * kEwThreads), lam, x[u]);
+                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, R, 4u * (threadIdx.x + u * kEwThreads), lam, x[u]);
         } else {   // a tensor's last, short tile
             if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
-            const int64_t ngroups = len >> 2;
-            for (int64_t i = threadIdx.x; i < ngroups; i += kEwThreads) {
+            const uint32_t ngroups = (uint32_t)(len >> 2);
+            for (uint32_t i = threadIdx.x; i < ngroups; i += kEwThreads) {
                 Group x0;
-                ew_load<OPT, GD, SF, PD>(T, e0 + 4 * i, fresh, x0);
-                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, T, e0 + 4 * i, lam, x0);
+                ew_load<OPT, GD, SF, PD>(R, 4u * i, fresh, x0);
+                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, R, 4u * i, lam, x0);
             }
             const int64_t tail = len & 3;
             if ((int64_t)threadIdx.x < tail) ew_single<OPT, GD, SF, PD>(a, s, T, e0 + 4 * ngroups + threadIdx.x, lam);

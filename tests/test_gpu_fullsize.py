@@ -503,3 +503,117 @@ def test_round_cast_past_2_to_34():
         assert int(gj) == oracle.bf16_sr(xj, int(w[int(j) & 3]) & 0xFFFF), j
     del x, out
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# whole-buffer checks: the oracle replays every element of the workload from
+# the same seeded inputs, in slices that host threads step in parallel (each
+# oracle call is one C call that releases the interpreter lock; the blockwise
+# formats and the element-wise step make slices independent)
+
+def _pool():
+    from concurrent.futures import ThreadPoolExecutor
+    return ThreadPoolExecutor(max_workers=max(1, min(16, len(__import__("os").sched_getaffinity(0)))))
+
+
+def test_q8_one_billion_every_block():
+    """2^30 elements, 8-bit blockwise m and v, 10% of gradients x100, 5 steps,
+    in the benchmark's launch configuration: all 4,194,304 blocks' codes and
+    absmax bit-exact and every p within the fp32 bar, the oracle replaying all
+    five steps over 2^24-element slices from the same seeded inputs."""
+    import time
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["adamw_q8_1g"]
+    n, hp, steps = w["sizes"][0], w["hp"], w["steps"]
+    qs, qu = synth.codebook_signed(), synth.codebook_unsigned()
+    P = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    p_host = to_host(P).copy()
+    st = _flat_states("q8", n, "adamw", qs, qu)
+    g_host = []
+    for t in range(1, steps + 1):
+        G = synth.device_grads(n, "cuda", w["g_std"], t, bf16=True, mask_scale=w["mask_scale"])
+        tl = osa.TensorList(_views(P, G, st, [n], "q8"))
+        osa.opt_step_adamw(tl, "q8", osa.hparams(step=t, qmap_signed=qs, qmap_unsigned=qu, **hp))
+        g_host.append(to_host(G).copy())
+        del G, tl
+    torch.cuda.synchronize()
+    got = {"p": to_host(P), "s1": to_host(st["s1"]), "s2": to_host(st["s2"]),
+           "a1": to_host(st["absmax1"]), "a2": to_host(st["absmax2"])}
+    del P, st
+    torch.cuda.empty_cache()
+    S = 1 << 24
+    t0 = time.time()
+
+    def check(lo):
+        hi = min(n, lo + S)
+        p = p_host[lo:hi].copy()
+        s = oracle.state_zeros("q8", hi - lo, "adamw", qs, qu)
+        for t in range(1, steps + 1):
+            oracle.step("adamw", "q8", oracle.make_hp(step=t, index_base=lo, **hp), p, g_host[t - 1][lo:hi],
+                        qs=qs, qu=qu, **s)
+        b0, b1 = lo // 256, (hi + 255) // 256
+        bad = {"s1": int(np.sum(got["s1"][lo:hi] != s["s1"])), "s2": int(np.sum(got["s2"][lo:hi] != s["s2"])),
+               "a1": not nan_equal_bits(got["a1"][b0:b1], s["a1"]), "a2": not nan_equal_bits(got["a2"][b0:b1], s["a2"]),
+               "p": not fp32_close(got["p"][lo:hi], p)}
+        print(f"q8 slice {lo // S}: {bad} ({time.time() - t0:.0f} s)", flush=True)
+        return lo, bad
+
+    with _pool() as pool:
+        results = list(pool.map(check, range(0, n, S)))
+    failed = [(lo, b) for lo, b in results if any(b.values())]
+    assert not failed, failed[:4]
+    assert len(results) == n // S
+
+
+def test_llama7b_whole_tensors_of_every_shape():
+    """The 290-tensor list stepped 5 times in one launch per step; the oracle
+    replays every element of one tensor of each shape (embed, an attention
+    projection, an MLP projection, a norm vector, lm_head): p within the fp32
+    bar, m and v bit-exact (the moments follow the oracle's binary32 order)."""
+    import torch
+    import optimizer_step_amd as osa
+    w = synth.WORKLOADS["adamw_f32_llama7b"]
+    sizes, hp, steps = w["sizes"], w["hp"], w["steps"]
+    names = [nm for nm, _ in synth.llama7b_shapes()]
+    pick = [names.index(x) for x in ("embed", "l0.q", "l17.gate", "l31.mlp_norm", "lm_head")]
+    total = sum(sizes)
+    offs = np.cumsum([0] + sizes[:-1])
+    P = torch.empty(total, dtype=torch.float32, device="cuda")
+    synth.device_normal_(P, synth.PARAM_SEED, w["p_std"])
+    st = _flat_states("f32", total, "adamw", None, None)
+    p0 = {k: to_host(P[offs[k]:offs[k] + sizes[k]]).copy() for k in pick}
+    g_hist = {k: [] for k in pick}
+    for t in range(1, steps + 1):
+        G = synth.device_grads(total, "cuda", w["g_std"], t, bf16=True)
+        tl = osa.TensorList(_views(P, G, st, sizes, "f32"))
+        osa.opt_step_adamw(tl, "f32", osa.hparams(step=t, **hp))
+        for k in pick:
+            g_hist[k].append(to_host(G[offs[k]:offs[k] + sizes[k]]).copy())
+        del G, tl
+    torch.cuda.synchronize()
+    got = {k: {key: to_host(buf[offs[k]:offs[k] + sizes[k]]) for key, buf in (("p", P), ("s1", st["s1"]),
+                                                                                  ("s2", st["s2"]))} for k in pick}
+    del P, st
+    torch.cuda.empty_cache()
+    S = 1 << 24
+
+    def check(job):
+        k, lo = job
+        hi = min(sizes[k], lo + S)
+        p = p0[k][lo:hi].copy()
+        s = oracle.state_zeros("f32", hi - lo)
+        for t in range(1, steps + 1):
+            oracle.step("adamw", "f32", oracle.make_hp(step=t, tensor_index=k, index_base=lo, **hp), p,
+                        g_hist[k][t - 1][lo:hi], **s)
+        return (k, lo, fp32_close(got[k]["p"][lo:hi], p), nan_equal_bits(got[k]["s1"][lo:hi], s["s1"]),
+                nan_equal_bits(got[k]["s2"][lo:hi], s["s2"]))
+
+    jobs = [(k, lo) for k in pick for lo in range(0, sizes[k], S)]
+    with _pool() as pool:
+        results = list(pool.map(check, jobs))
+    for k in pick:
+        print(f"{names[k]} ({sizes[k]} elements): whole tensor checked", flush=True)
+    failed = [r for r in results if not all(r[2:])]
+    assert not failed, failed[:4]
