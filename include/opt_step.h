@@ -214,6 +214,21 @@ typedef struct {
 int opt_step_adamw(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
                    const opt_hparams *hp, const double *unorm, void *stream);
 
+/* opt_step_adamw for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results, with the call's tables (tensor
+ * records, chunk table, 8-bit lookup tables) copied into one fixed 2 MiB
+ * device array that each GPU the library runs on holds until the process
+ * ends, instead of the library's grown workspace.  It calls no hipMalloc,
+ * hipFree or other allocating routine.  A list whose tables exceed 2 MiB
+ * (about 500,000 chunks of the current chunk size, with the tensor records)
+ * returns OPT_EUNSUPPORTED before anything is enqueued.  Every call on a GPU
+ * rewrites that GPU's array: calls in order on one stream are safe; calls
+ * that overlap on one GPU (other streams or threads) race, and the caller
+ * must order them. */
+int opt_step_adamw_noalloc(const opt_tensor *tensors, int64_t n, int32_t state_fmt,
+                           const opt_hparams *hp, const double *unorm, void *stream);
+
 /* One AdEMAMix step (the rule the bitsandbytes PR "Fix decoupled weight
  * decay ordering in the CUDA Adam/AdEMAMix kernels" intro cites, Pagliardini
  * et al.): as opt_step_adamw plus the slow EMA m2' = b3*m2 + (1-b3)*g, kept in

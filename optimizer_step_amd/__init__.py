@@ -80,6 +80,7 @@ def lib():
         sig = {
             "opt_step_adamw": ([T, i64, i32, H, vp, vp], i32),
             "opt_step_ademamix": ([T, i64, i32, H, vp, vp], i32),
+            "opt_step_adamw_noalloc": ([T, i64, i32, H, vp, vp], i32),
             "opt_precondition_unorm": ([i32, T, i64, i32, H, vp, vp], i32),
             "opt_last_error": ([], ctypes.c_char_p),
             "opt_shutdown": ([], i32),
@@ -300,6 +301,17 @@ def opt_step_adamw(tensors, state_fmt, hp, unorm=None, stream=None):
     tl.check(fmt, 2)
     return _check(lib().opt_step_adamw(tl.arr, tl.n, fmt, ctypes.byref(hp), _norm_buffer(unorm, tl.n),
                                        _stream(stream)))
+
+
+def opt_step_adamw_noalloc(tensors, state_fmt, hp, unorm=None, stream=None):
+    """opt_step_adamw that allocates no device memory (the library's fixed
+    2 MiB table array instead of its workspace); calls that overlap on one
+    GPU race."""
+    tl = _as_list(tensors)
+    fmt = FORMATS.get(state_fmt, state_fmt)
+    tl.check(fmt, 2)
+    return _check(lib().opt_step_adamw_noalloc(tl.arr, tl.n, fmt, ctypes.byref(hp), _norm_buffer(unorm, tl.n),
+                                               _stream(stream)))
 
 
 def opt_step_ademamix(tensors, state_fmt, hp, unorm=None, stream=None):

@@ -670,6 +670,122 @@ int run(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp,
     return OPT_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free AdamW step.  Its tables (DevTensor records, chunk
+// table, 8-bit lookup tables) go into a fixed device array instead of the
+// grown workspace: one copy per device of kScratchBytes, which the device
+// holds until the process ends.  On the host only its address, taken once per
+// device with hipGetSymbolAddress, is ever used (the array's own name in host
+// code is not a device address).
+
+constexpr size_t kScratchBytes = (size_t)2 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchDev {
+    bool init = false;
+    unsigned char *ptr = nullptr;   // device address of `scratch` on this device
+    int ncu = 0;
+    hipEvent_t copied = nullptr;    // after the last call's table copy
+    bool pending = false;
+    std::vector<unsigned char> host;   // host image of the tables (pageable)
+};
+ScratchDev g_scratch[kMaxDevices];
+
+// The current device's scratch record, set up on its first use (with g_mu held).
+int scratch_dev(ScratchDev *&out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(OPT_EUNSUPPORTED, "device %d out of range", dev);
+    ScratchDev &d = g_scratch[dev];
+    if (!d.init) {
+        if ((e = hipGetSymbolAddress((void **)&d.ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress (scratch)");
+        if ((e = hipDeviceGetAttribute(&d.ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return hip_fail(e, "hipDeviceGetAttribute");
+        if ((e = hipEventCreateWithFlags(&d.copied, hipEventDisableTiming)) != hipSuccess)
+            return hip_fail(e, "hipEventCreate");
+        d.init = true;
+    }
+    out = &d;
+    return OPT_OK;
+}
+
+int run_noalloc(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hparams *hp, const double *unorm,
+                void *stream)
+{
+    int rc;
+    if ((rc = check_hparams(hp, fmt)) != OPT_OK) return rc;
+    if ((rc = check_tensors(t, n, opt, fmt)) != OPT_OK) return rc;
+    if (hp->max_unorm > 0.0f && !unorm)
+        return fail(OPT_EINVAL, "max_unorm > 0 needs the norms from opt_precondition_unorm");
+    if (n == 0) return OPT_OK;
+    std::lock_guard<std::mutex> lock(g_mu);
+    const bool q8 = fmt == kQ8;
+    std::vector<uint32_t> qw;
+    QTabParams ps{}, pu{};
+    if (q8 && (rc = build_qwords(hp->qmap_signed, hp->qmap_unsigned, qw, ps, pu)) != OPT_OK) return rc;
+    const int64_t chunk = g_chunk;
+    // every bucket's tables, one after another, each on a 256-byte boundary
+    struct Item { int bi; size_t off, off_ct, off_q; int64_t nchunks; };
+    std::vector<Item> items;
+    std::vector<unsigned char> image;
+    for (int bi = 0; bi < 9; ++bi) {
+        Bucket bk;
+        plan_bucket(t, n, bi / 3, bi % 3, chunk, bk);
+        if (bk.chunk_tensor.empty()) continue;
+        std::vector<unsigned char> blob;
+        Item it{bi, (image.size() + 255) & ~(size_t)255, 0, 0, (int64_t)bk.chunk_tensor.size()};
+        make_blob(bk, q8 ? &qw : nullptr, blob, it.off_ct, it.off_q);
+        if (it.off + blob.size() > kScratchBytes)
+            return fail(OPT_EUNSUPPORTED, "the tensor list needs more than the %zu bytes of tables the "
+                        "allocation-free step holds (%zu tensors, %lld chunks so far)", kScratchBytes,
+                        (size_t)n, (long long)it.nchunks);
+        image.resize(it.off + blob.size(), 0);
+        memcpy(image.data() + it.off, blob.data(), blob.size());
+        items.push_back(it);
+    }
+    if (items.empty()) return OPT_OK;
+
+    ScratchDev *d;
+    if ((rc = scratch_dev(d)) != OPT_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    // the host image of the previous call must have been read before it is
+    // overwritten (a pageable source is staged when the copy is queued; the
+    // wait covers the case where it is read later)
+    if (d->pending && (e = hipEventSynchronize(d->copied)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    d->pending = false;
+    d->host.swap(image);
+    if ((e = hipMemcpyAsync(d->ptr, d->host.data(), d->host.size(), hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync (tables into scratch)");
+    if ((e = hipEventRecord(d->copied, st)) != hipSuccess) {
+        (void)hipStreamSynchronize(st);
+        return hip_fail(e, "hipEventRecord");
+    }
+    d->pending = true;
+    for (const Item &it : items) {
+        StepArgs a = base_args(hp, chunk);
+        a.p_dtype = it.bi % 3;
+        a.tens = (const DevTensor *)(d->ptr + it.off);
+        a.chunk_tensor = (const int32_t *)(d->ptr + it.off + it.off_ct);
+        a.nchunks = it.nchunks;
+        a.unorm = hp->max_unorm > 0.0f ? unorm : nullptr;
+        size_t lds = 0;
+        if (q8) {
+            a.q.words = (const uint32_t *)(d->ptr + it.off + it.off_q);
+            a.q.nwords = (uint32_t)qw.size();
+            a.q.s = ps;
+            a.q.u = pu;
+            lds = (size_t)a.q.nwords * 4;
+        }
+        e = launch_step(opt, it.bi / 3, fmt, a, LaunchGeom{d->ncu, g_wgs_per_cu}, lds, st);
+        if (e != hipSuccess) return hip_fail(e, "step launch");
+    }
+    return OPT_OK;
+}
+
 template <class F>
 void mini_host_one(float A, float x, const uint32_t *r, int64_t i, uint8_t *codes, float *decoded)
 {
@@ -707,6 +823,12 @@ int opt_step_ademamix(const opt_tensor *tensors, int64_t n, int32_t state_fmt, c
                       const double *unorm, void *stream)
 {
     return run(kAdEMAMix, tensors, n, state_fmt, hp, unorm, nullptr, stream);
+}
+
+int opt_step_adamw_noalloc(const opt_tensor *tensors, int64_t n, int32_t state_fmt, const opt_hparams *hp,
+                           const double *unorm, void *stream)
+{
+    return run_noalloc(kAdamW, tensors, n, state_fmt, hp, unorm, stream);
 }
 
 int opt_precondition_unorm(int32_t optimizer, const opt_tensor *tensors, int64_t n, int32_t state_fmt,

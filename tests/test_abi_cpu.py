@@ -85,6 +85,24 @@ def test_bad_arguments_are_rejected_before_device_work(L, case, status):
     assert L.opt_last_error() != ""
 
 
+@pytest.mark.parametrize("case,status", [
+    (dict(hp=dict(step=0)), -1),
+    (dict(tensor=dict(p=4100)), -3),
+    (dict(hp=dict(max_unorm=1.0)), -1),
+])
+def test_no_alloc_step_checks_its_arguments(L, case, status):
+    hp = L.hparams(**case.get("hp", {}))
+    assert _call(L, "opt_step_adamw_noalloc", _tensor(L, **case.get("tensor", {})), 0, hp) == status
+
+
+def test_no_alloc_step_refuses_tables_beyond_its_array(L):
+    """20,000 tensor records (2.2 MB of tables) exceed the fixed 2 MiB array:
+    OPT_EUNSUPPORTED, decided on the host before any device work."""
+    recs = [L.OptTensor(4096 * (i + 1), 4096, 8192, 12288, None, None, None, None, 4, 0, 0) for i in range(20000)]
+    assert _call(L, "opt_step_adamw_noalloc", recs) == -2
+    assert "2097152" in L.opt_last_error()
+
+
 def test_ademamix_needs_slow_ema(L):
     assert _call(L, "opt_step_ademamix", _tensor(L)) == -1
 
