@@ -72,15 +72,11 @@ def test_one_state_parity(name, fmt):
     hp = dict(lr=1e-2, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.05)
     steps = 4
     ps, ss, dev = _run_1s(name, fmt, ["f32", "bf16", "f16", "bf16"], steps, hp)
+    # the one-state recipes use correctly rounded division and square root in
+    # the oracle's binary32 order: p and the stored state are the oracle's bits
     for k in range(len(SIZES)):
-        assert fp32_close(to_host(dev[k]["p"]), ps[k]), k
-        g = to_host(dev[k]["s1"])
-        if fmt == "f32":
-            assert fp32_close(g, ss[k]), k
-        elif fmt == "bf16_rn":
-            assert int(bf16_ulps(g, ss[k]).max(initial=0)) <= steps, k
-        else:
-            assert nan_equal_bits(g, ss[k]), k
+        assert nan_equal_bits(to_host(dev[k]["p"]), ps[k]), k
+        assert nan_equal_bits(to_host(dev[k]["s1"]), ss[k]), k
 
 
 @pytest.mark.parametrize("name", ["momentum", "lion"])
@@ -88,7 +84,7 @@ def test_one_state_skip_zeros_and_reset(name):
     hp = dict(lr=1e-2, beta1=0.9, beta2=0.99, weight_decay=0.05, skip_zeros=True, reset_interval=2)
     ps, ss, dev = _run_1s(name, "bf16_sr", ["bf16", "f32", "f16", "f32"], 5, hp, zeros=True)
     for k in range(len(SIZES)):
-        assert fp32_close(to_host(dev[k]["p"]), ps[k]), k
+        assert nan_equal_bits(to_host(dev[k]["p"]), ps[k]), k
         assert nan_equal_bits(to_host(dev[k]["s1"]), ss[k]), k
 
 

@@ -235,14 +235,8 @@ def test_sweep_one_state(i, gpu):
     ps, ss, dev = _run_1s(c["name"], c["fmt"], c["gds"], c["steps"], c["hp"], sizes=c["sizes"],
                           grad=_typed_grads(c, 1e-1), seed=c["seed"])
     for k in range(len(c["sizes"])):
-        assert fp32_close(to_host(dev[k]["p"]), ps[k]), k
-        g = to_host(dev[k]["s1"])
-        if c["fmt"] == "f32":
-            assert fp32_close(g, ss[k]), k
-        elif c["fmt"] == "bf16_rn":
-            assert int(bf16_ulps(g, ss[k]).max(initial=0)) <= c["steps"], k
-        else:
-            assert nan_equal_bits(g, ss[k]), k
+        assert nan_equal_bits(to_host(dev[k]["p"]), ps[k]), k
+        assert nan_equal_bits(to_host(dev[k]["s1"]), ss[k]), k
 
 
 def test_sweeps_of_p16_and_one_state_cover_their_space():
