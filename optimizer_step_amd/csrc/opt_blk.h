@@ -253,11 +253,70 @@ __device__ __forceinline__ void blk_decode4(const uint32_t *lds, uint32_t c, flo
     }
 }
 
+typedef short s2_t __attribute__((ext_vector_type(2)));
+
+// Codes of four values of one block by gfx950's scaled conversions, for
+// E4M3 and E2M1 when the block scale 2^-nsc is a normal binary32 value (the
+// caller's uniform test).  Each value is first clamped to the grid's largest
+// finite value times the scale (past it the conversion gives NaN; our rule
+// takes the largest value, and clamping first gives the same code).  The
+// nearest conversions are IEEE; the stochastic ones add their random
+// operand's top bits to the dropped bits, so the element's 16 random bits go
+// in the high half, which makes them round up exactly when the top 16 dropped
+// bits plus r carry.  The packed FP4 stochastic conversion draws its second
+// element's bits elsewhere, so each element gets a conversion of its own.
+// Checked on MI355X against mini_encode: 33.5 M hashed values and 33.5 M edge
+// cases (zeros of both signs, binary32 subnormals, values at the clamp, every
+// normal scale), no difference in any of the four conversions.
+template <class F, bool SR>
+__device__ __forceinline__ uint32_t mini_pack4_hw(const float x[4], int nsc, const uint32_t r[4])
+{
+    const float scale = ldexpf(1.0f, -nsc);
+    const float lim = (F::kSign == 0x80u ? 448.0f : 6.0f) * scale;
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(x[i], -lim, lim);
+    if (F::kSign == 0x80u) {                     // E4M3, a byte each
+        if (!SR) {
+            s2_t w = {};
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c[0], c[1], scale, false);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c[2], c[3], scale, true);
+            return __builtin_bit_cast(uint32_t, w);
+        }
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, c[0], r[0] << 16, scale, 0);
+        w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, c[1], r[1] << 16, scale, 1);
+        w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, c[2], r[2] << 16, scale, 2);
+        w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, c[3], r[3] << 16, scale, 3);
+        return w;
+    }
+    if (!SR) {                                   // E2M1, two nibbles a byte
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[0], c[1], scale, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], scale, 1);
+        return w & 0xFFFFu;
+    }
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t b = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (f2v){c[i], c[i]}, r[i] << 16, scale, 0);
+        out |= (b & 0xFu) << (4 * i);
+    }
+    return out;
+}
+
 template <class F, bool SR>
 __device__ __forceinline__ uint32_t mini_pack4(const float x[4], float A, const uint32_t r[4])
 {
     if (!finite_f(A)) return 0u;
     const int nsc = mini_enc_shift<F>(A);
+    // E4M3 stochastic, E2M1 both ways (not the unsigned E2M2, which has no
+    // hardware format).  Paired on MI355X, 2^30 elements: FP8-SR 2.89 ->
+    // 2.72 ms, FP4-SR 2.65 -> 2.51, FP4-RN 2.32 -> 2.29; FP8 nearest, whose
+    // integer rounding is a few instructions, lost 1.2 % and keeps it.
+    constexpr bool hw = (F::kSign == 0x80u && SR) || F::kMB == 1;
+    if (hw && nsc >= -127 && nsc <= 126) return mini_pack4_hw<F, SR>(x, nsc, r);
     constexpr int W = (F::kSign == 0x80u) ? 8 : 4;
     uint32_t out = 0;
 #pragma unroll
