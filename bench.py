@@ -508,6 +508,74 @@ def summarize_rows_counters(base):
     print(f"wrote profiles/bench_rows_counters.txt ({len(lines)} rows)")
 
 
+ACTIVITY_PASSES = {
+    "A": "VALUBusy LDSBankConflict OccupancyPercent MemUnitStalled",
+    "B": "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_BUSY_CYCLES "
+         "SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE",
+}
+
+
+ACTIVITY_REGEX = "step_|gnorm_|round_cast|norm_group"
+
+
+def summarize_rows_activity(base):
+    """profiles/bench_rows_activity.txt: per bench row, what the step kernel
+    keeps busy -- VALU issue (VALUBusy: share of the kernel's cycles the SIMDs
+    issue vector ALU work), VALU instructions per element, LDS bank-conflict
+    stall share, occupancy, memory-unit stall share -- from two rocprofv3
+    counter passes per row (A and B), medians over the row's dispatches of
+    its dominant kernel (the one the shader sequencers are busy longest in)."""
+    import csv
+    import glob
+    import statistics
+    lines = []
+    for rdir in sorted(glob.glob(os.path.join(base, "*", ""))):
+        row = os.path.basename(os.path.normpath(rdir))
+        try:
+            info = json.loads(open(os.path.join(rdir, "bench.json")).read().strip().splitlines()[-1])["rows"][0]
+        except (OSError, ValueError, IndexError, KeyError):
+            continue
+        per = {}
+        for p in ACTIVITY_PASSES:
+            files = glob.glob(os.path.join(rdir, p, "**", "*counter_collection.csv"), recursive=True)
+            if not files:
+                break
+            for r in csv.DictReader(open(files[0])):
+                name = r["Kernel_Name"].replace("void ", "").replace("optstep::", "")
+                if not name.startswith(OUR_KERNELS):
+                    continue
+                name = name[:name.index(">(") + 1] if ">(" in name else name.split("(")[0]
+                per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        need = ("VALUBusy", "SQ_INSTS_VALU", "SQ_WAVES", "SQ_BUSY_CYCLES")
+        per = {k: v for k, v in per.items() if all(c in v for c in need)}
+        if not per:
+            continue
+        # the row's dominant kernel: the one its SQs are busy longest in
+        kname = max(per, key=lambda k: statistics.median(per[k]["SQ_BUSY_CYCLES"]))
+        m = {c: statistics.median(v) for c, v in per[kname].items()}
+        lines.append((row, kname, info["elements"], m))
+    if not lines:
+        raise SystemExit(f"no complete row under {base}")
+    with open(os.path.join(ROOT, "profiles", "bench_rows_activity.txt"), "w") as f:
+        f.write("rocprofv3 activity counters of each bench row's dominant kernel (medians over its dispatches).\n"
+                "VALUBusy: % of the kernel's cycles the SIMDs spend issuing vector ALU work; VALU/elem: vector\n"
+                "instructions (each for 64 lanes) x 64 / elements, i.e. per-element VALU work; LDSconfl: % of\n"
+                "cycles LDS is stalled on bank conflicts; Occ: % of the maximum waves resident; MemStall: % of\n"
+                "cycles the memory unit is stalled.\n"
+                "commands, per row R (each a process of its own):\n")
+        for p, ctr in ACTIVITY_PASSES.items():
+            f.write(f"  rocprofv3 --pmc {ctr} --kernel-include-regex '{ACTIVITY_REGEX}' --output-format csv -d {base}/R/{p} -o c "
+                    f"-- python bench.py --rows-only --rows R --no-cpu --steps 2 --warmup 1 > {base}/R/bench.json\n")
+        f.write(f"\n{'row':24s} {'VALUBusy':>8s} {'VALU/elem':>9s} {'LDS/elem':>8s} {'LDSconfl':>8s} {'Occ':>6s} "
+                f"{'MemStall':>8s}  kernel\n")
+        for row, kname, n, m in lines:
+            valu = m["SQ_INSTS_VALU"] * 64 / n
+            lds = m.get("SQ_INSTS_LDS", 0.0) * 64 / n
+            f.write(f"{row:24s} {m['VALUBusy']:8.1f} {valu:9.1f} {lds:8.2f} {m.get('LDSBankConflict', 0.0):8.2f} "
+                    f"{m.get('OccupancyPercent', 0.0):6.1f} {m.get('MemUnitStalled', 0.0):8.2f}  {kname}\n")
+    print(open(os.path.join(ROOT, "profiles", "bench_rows_activity.txt")).read())
+
+
 def summarize_rows_trace(trace_dir, cmd):
     """profiles/bench_rows_kernel_stats.txt: per-kernel time statistics of a
     rocprofv3 --kernel-trace --stats run over every bench row."""
@@ -536,8 +604,12 @@ def summarize_rows_trace(trace_dir, cmd):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    # the warmup also lets the device leave its idle clocks: on MI355X the
+    # step runs about 2 % slower for the first 1-2 s of sustained load
+    # (Llama-7B-shaped AdamW 28.01 ms per step in the first second, 27.38
+    # from the second on); 100 steps of the headline take about 2.7 s
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--rows", default="all", help="'all', 'none', or comma-separated workload names")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--calibrate", action="store_true",
@@ -554,6 +626,9 @@ def main():
     ap.add_argument("--summarize-rows-counters", metavar="DIR",
                     help="write profiles/bench_rows_counters.txt from per-row rocprofv3 counter runs under DIR "
                          "(DIR/<row>/{fetch,write}/ and DIR/<row>/bench.json) and exit")
+    ap.add_argument("--summarize-rows-activity", metavar="DIR",
+                    help="write profiles/bench_rows_activity.txt from per-row rocprofv3 activity-counter runs under "
+                         "DIR (DIR/<row>/{A,B}/ and DIR/<row>/bench.json) and exit")
     ap.add_argument("--summarize-rows-trace", metavar="TRACE_DIR",
                     help="write profiles/bench_rows_kernel_stats.txt from a rocprofv3 run over all rows and exit")
     args = ap.parse_args()
@@ -574,6 +649,9 @@ def main():
         return
     if args.summarize_rows_counters:
         summarize_rows_counters(args.summarize_rows_counters)
+        return
+    if args.summarize_rows_activity:
+        summarize_rows_activity(args.summarize_rows_activity)
         return
     if args.summarize_profiles:
         tdir, fdir, wdir = args.summarize_profiles

@@ -375,6 +375,14 @@ int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, i
  * do not depend on either.  OPT_EINVAL for other values. */
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);
 
+/* Cap on the workgroups each compute unit holds at once for the element-wise
+ * and one-state step kernels, for all later calls in this process: -1 (the
+ * default) lets each kernel configuration take its own measured choice, 0
+ * sets no cap, 2..32 caps at that many (a launch-time LDS reservation that
+ * the kernels do not use).  Results do not depend on it.  OPT_EINVAL for
+ * other values. */
+int opt_debug_set_wg_cap(int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

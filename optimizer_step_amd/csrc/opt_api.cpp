@@ -61,6 +61,7 @@ int hip_fail(hipError_t e, const char *what)
 
 int64_t g_chunk = 32768;      // elements per chunk; a power of two >= 1024
 int g_wgs_per_cu = 0;         // workgroups per compute unit (0: one per tile, or occupancy)
+int g_wg_cap = -1;            // resident workgroups per compute unit (-1: per kernel, 0: no cap)
 
 constexpr int kMaxDevices = 64;
 constexpr int kSlots = 16;
@@ -531,7 +532,7 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     return a;
 }
 
-LaunchGeom geom(const Workspace &w) { return LaunchGeom{w.ncu, g_wgs_per_cu}; }
+LaunchGeom geom(const Workspace &w) { return LaunchGeom{w.ncu, g_wgs_per_cu, g_wg_cap}; }
 
 // The device tables of a call's buckets (bucket bi = 3 * gradient dtype +
 // parameter dtype).  A call whose tensor records, kind, optimizer, format,
@@ -780,7 +781,7 @@ int run_noalloc(int opt, const opt_tensor *t, int64_t n, int fmt, const opt_hpar
             a.q.u = pu;
             lds = (size_t)a.q.nwords * 4;
         }
-        e = launch_step(opt, it.bi / 3, fmt, a, LaunchGeom{d->ncu, g_wgs_per_cu}, lds, st);
+        e = launch_step(opt, it.bi / 3, fmt, a, LaunchGeom{d->ncu, g_wgs_per_cu, g_wg_cap}, lds, st);
         if (e != hipSuccess) return hip_fail(e, "step launch");
     }
     return OPT_OK;
@@ -1135,6 +1136,14 @@ int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu)
     std::lock_guard<std::mutex> lock(g_mu);
     g_chunk = chunk;
     g_wgs_per_cu = wgs_per_cu;
+    return OPT_OK;
+}
+
+int opt_debug_set_wg_cap(int32_t cap)
+{
+    if (cap != -1 && (cap < 0 || cap == 1 || cap > 32)) return fail(OPT_EINVAL, "cap must be -1, 0 or in [2, 32]");
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_wg_cap = cap;
     return OPT_OK;
 }
 

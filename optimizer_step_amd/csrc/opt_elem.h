@@ -320,6 +320,21 @@ __device__ __forceinline__ Scalars publish_scalars(const StepArgs &a, Scalars &s
     return sh;
 }
 
+// Occupancy cap.  A 256-thread tile kernel is held to `cap` resident
+// workgroups per compute unit (cap waves per SIMD) by reserving, at launch,
+// LDS it never touches: 1 KiB under a cap-th of the 160 KiB each gfx950
+// compute unit holds, which leaves room for the kernels' few bytes of static
+// LDS and keeps cap + 1 workgroups from fitting.  Measured on MI355X, some
+// element-wise configurations run faster with fewer waves in flight than
+// their registers allow (the launchers name them).
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+__host__ inline size_t cap_lds(const LaunchGeom &lg, int dflt)
+{
+    const int cap = lg.wg_cap >= 0 ? lg.wg_cap : dflt;
+    return cap >= 2 ? kLdsPerCu / cap - 1024 : 0;
+}
+
 // One launch of a tile kernel taking (tens, ctab, a), THREADS per workgroup.
 template <int THREADS = kThreads, class K>
 static hipError_t launch_tiles(K kernel, int64_t ktile, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)

@@ -198,13 +198,36 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
     }
 }
 
+// Resident workgroups per compute unit of the fp32-state AdamW step with
+// 16-bit gradients (0: as many as registers allow, 7 for the plain kernel).
+// Measured on MI355X in paired runs over one arena (fp32 p, m, v; BF16 g),
+// caps 0 / 3 / 4 / 5 / 6: 290-tensor Llama-7B-shaped list 29.41 / 27.45 /
+// 27.71 / 28.56 / 29.41 ms, and with a gradient scale (the kernel that also
+// reads it) 29.0 / 28.4 / 27.7 / 29.0 / 29.0 ms; 3 x 2^30 elements 13.83 /
+// 12.73 / 12.89 / 13.42 / 13.83 ms; one 2^30 tensor 4.69 / 4.59 / 4.60 /
+// 4.59 / 4.69 ms; 2^29 elements 2.32 / 2.40 / 2.31 / 2.28 / 2.32 ms; 2^28
+// elements 1.17 / 1.22 / 1.17 / 1.16 / 1.17 ms.  BF16 parameters (2^30):
+// 3.85 / 4.31 / 3.82 / 3.73 / 3.84 ms.  The BF16 state formats and AdEMAMix
+// gain nothing (BF16 states lose up to 15 % at 4), so keep the default.
+template <int OPT, int GD, int SF, int PD, bool PLAIN>
+static int ew_wg_cap(const StepArgs &a)
+{
+    if (OPT != kAdamW || GD == kGradF32 || SF != kF32) return 0;
+    if (PD != kP32 || a.nchunks * a.chunk < ((int64_t)1 << 30)) return 5;
+    return PLAIN ? 3 : 4;
+}
+
 template <int OPT, int GD, int PD, bool PLAIN>
 static hipError_t launch_ew_p(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
 {
     switch (fmt) {
-    case kF32: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD, PLAIN>, kEwTile, 0, lg, a, st);
-    case kBF16RN: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, kEwTile, 0, lg, a, st);
-    case kBF16SR: return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, kEwTile, 0, lg, a, st);
+    case kF32:
+        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD, PLAIN>, kEwTile,
+                                        cap_lds(lg, ew_wg_cap<OPT, GD, kF32, PD, PLAIN>(a)), lg, a, st);
+    case kBF16RN:
+        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, kEwTile, cap_lds(lg, 0), lg, a, st);
+    case kBF16SR:
+        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, kEwTile, cap_lds(lg, 0), lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -68,11 +68,14 @@ struct QTabs {
     QTabParams s, u;
 };
 
-// Launch geometry: compute units, and workgroups per compute unit (0: one
-// workgroup per tile; k > 0: a persistent grid of k per compute unit).
+// Launch geometry: compute units, workgroups per compute unit (0: one
+// workgroup per tile; k > 0: a persistent grid of k per compute unit), and
+// the cap on workgroups resident per compute unit of the element-wise tile
+// kernels (-1: each kernel's own choice; 0: none; k: at most k).
 struct LaunchGeom {
     int ncu;
     int wgs_per_cu;
+    int wg_cap = -1;
 };
 
 // Kernel arguments (passed by value).

@@ -384,3 +384,11 @@ def test_index_base_and_stream_tensor_checks(L):
         t.sr_tensor, t.sr_tensor_set = k, set_
         rc = _call(L, "opt_step_adamw", [t], 0, hp)
         assert (rc == -1) == bad, (set_, k, rc, L.opt_last_error())
+
+
+def test_wg_cap_values(L):
+    lib = L.lib()
+    for bad in (-2, 1, 33, 1 << 20):
+        assert lib.opt_debug_set_wg_cap(bad) == -1, bad
+    for ok in (0, 2, 3, 32, -1):
+        assert lib.opt_debug_set_wg_cap(ok) == 0, ok
