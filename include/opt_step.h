@@ -334,6 +334,18 @@ int opt_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t co
 int opt_debug_round_bf16(const float *x, const uint32_t *r, uint16_t *out, int64_t n,
                          void *stream);
 
+/* The step's two directions for n elements with inputs g, m, v (and m2 for
+ * AdEMAMix; NULL for AdamW), the moments formed from them with hp's betas,
+ * alpha, eps and bias-correction step (no gradient scale): out[i] = the
+ * direction with the hardware reciprocal and square root, out[n+i] = its
+ * error bound against the exact recipe (infinite where the step would take
+ * the exact recipe for that element anyway), out[2n+i] = the exact recipe's
+ * direction (correctly rounded division and square root).  Device arrays;
+ * out is float[3n].  OPT_EINVAL for another optimizer, NULL arrays, betas
+ * outside [0, 1) or step < 1. */
+int opt_debug_direction(int32_t optimizer, const opt_hparams *hp, const float *g, const float *m,
+                        const float *v, const float *m2, float *out, int64_t n, void *stream);
+
 /* out[i] = code of x[i] against the host codebook qmap (256 floats, as
  * qmap_signed; pass is_signed = 0 for a table of non-negative entries, which
  * must hold 0 <= x <= 1), using the lookup tables the 8-bit step builds.

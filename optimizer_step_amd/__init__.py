@@ -86,6 +86,7 @@ def lib():
             "opt_shutdown": ([], i32),
             "opt_debug_philox": ([ctypes.c_uint64, i64, i32, i64, i64, vp, vp], i32),
             "opt_debug_round_bf16": ([vp, vp, vp, i64, vp], i32),
+            "opt_debug_direction": ([i32, vp, vp, vp, vp, vp, vp, i64, vp], i32),
             "opt_debug_quantize": ([vp, i32, vp, vp, i64, vp], i32),
             "opt_debug_plan": ([vp, i64, vp], i64),
             "opt_debug_quantize_host": ([vp, i32, vp, vp, i64], i32),
@@ -352,6 +353,15 @@ def opt_shutdown():
 def opt_debug_philox(seed, t, k, j0, out, stream=None):
     return _check(lib().opt_debug_philox(int(seed) & (2**64 - 1), t, k, j0, out.numel(), _ptr(out),
                                          _stream(stream)))
+
+
+def opt_debug_direction(optimizer, hp, g, m, v, m2, out, stream=None):
+    """out (device float[3n]): the fast direction, its error bound and the
+    exact recipe's direction of each element (m2 unused for AdamW)."""
+    code = ADEMAMIX if optimizer == "ademamix" else ADAMW
+    return _check(lib().opt_debug_direction(code, ctypes.byref(hp), _ptr(g), _ptr(m), _ptr(v),
+                                            _ptr(m2) if m2 is not None else None, _ptr(out), g.numel(),
+                                            _stream(stream)))
 
 
 def opt_debug_round_bf16(x, r, out, stream=None):

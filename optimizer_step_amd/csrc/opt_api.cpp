@@ -27,6 +27,8 @@ hipError_t launch_gnorm_total(int64_t n, double *out, float max_norm, int norm_t
 hipError_t launch_debug_philox(uint64_t seed, int64_t t, int32_t k, int64_t j0, int64_t n, uint32_t *out,
                                hipStream_t st);
 hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, int64_t n, hipStream_t st);
+hipError_t launch_debug_direction(int opt, const StepArgs &a, const float *g, const float *m, const float *v,
+                                  const float *m2, float *out, int64_t n, hipStream_t st);
 hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, uint8_t *out, int64_t n,
                                  hipStream_t st);
 hipError_t launch_debug_mini(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
@@ -529,6 +531,7 @@ StepArgs base_args(const opt_hparams *hp, int64_t chunk)
     a.grad_scale = hp->grad_scale;
     a.p_sr = hp->p_rounding;
     a.skip_zeros = hp->skip_zeros;
+    a.sc = make_scalars(a);
     return a;
 }
 
@@ -1013,6 +1016,32 @@ int opt_debug_round_bf16(const float *x, const uint32_t *r, uint16_t *out, int64
     if (!x || !out) return fail(OPT_EINVAL, "x or out is NULL");
     hipError_t e = launch_debug_round(x, r, out, n, (hipStream_t)stream);
     return e == hipSuccess ? OPT_OK : hip_fail(e, "debug round launch");
+}
+
+int opt_debug_direction(int32_t optimizer, const opt_hparams *hp, const float *g, const float *m, const float *v,
+                        const float *m2, float *out, int64_t n, void *stream)
+{
+    if (optimizer != OPT_ADAMW && optimizer != OPT_ADEMAMIX) return fail(OPT_EINVAL, "optimizer must be AdamW or AdEMAMix");
+    if (!hp) return fail(OPT_EINVAL, "hp is NULL");
+    if (n < 0) return fail(OPT_EINVAL, "n < 0");
+    if (n == 0) return OPT_OK;
+    if (!g || !m || !v || !out || (optimizer == OPT_ADEMAMIX && !m2)) return fail(OPT_EINVAL, "NULL array");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || hp->step < 1)
+        return fail(OPT_EINVAL, "betas must be in [0, 1) and step >= 1");
+    StepArgs a{};
+    a.lr = hp->lr;
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.beta3 = hp->beta3;
+    a.alpha = hp->alpha;
+    a.eps = hp->eps;
+    a.wd = hp->weight_decay;
+    a.bc_step = hp->step;
+    a.grad_scale = nullptr;
+    a.sc = make_scalars(a);
+    hipError_t e = launch_debug_direction(optimizer == OPT_ADEMAMIX ? kAdEMAMix : kAdamW, a, g, m, v, m2, out, n,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "debug direction launch");
 }
 
 int opt_debug_quantize(const float *qmap, int32_t is_signed, const float *x, uint8_t *out, int64_t n,

@@ -351,14 +351,37 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) m_in[i] = v_in[i] = m2_in[i] = 0.0f;
     }
-    // The stored moments are exact binary32; only the direction u (for an
-    // fp32 p) takes the fast path, per element (moments4).
+    // stochastic rounding: the element's Philox word, low half for m, high
+    // half for v; the second stream's word, low half for m2 and high half
+    // for a 16-bit parameter stored stochastically (rm, rv, rm2: the 16 bits
+    // as an integer; rp: the whole word, as the parameter store takes them)
+    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
+    const bool psr = PD != kP32 && a.p_sr;
+    const uint64_t q = (uint64_t)(C.e0 + e) >> 2;
+    if (sr_fmt(SF)) {
+        PhiloxOut w = sr_block(a.seed, a.step, C.k, q, false);
+        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
+        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
+    }
+    if ((sr_fmt(SF) && OPT == kAdEMAMix) || psr) {
+        PhiloxOut w2 = sr_block(a.seed, a.step, C.k, q, true);
+        rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
+        rp[0] = w2.w0; rp[1] = w2.w1; rp[2] = w2.w2; rp[3] = w2.w3;
+    }
+    // The stored moments are exact binary32; only the direction u takes the
+    // fast path, per element: for an fp32 p (moments4), and for a 16-bit p
+    // where it provably stores the exact recipe's word (moments16).
     float p[4], mo[4], vo[4], m2o[4];
     Mom r[4];
-    moments4<OPT, PD == kP32, !PLAIN>(s, a, x.g, m_in, v_in, m2_in, r);
+    if (PD == kP32) {
+        moments4<OPT, !PLAIN>(s, a, x.g, m_in, v_in, m2_in, r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = apply_update(x.p[i], s.d, lam, r[i].u);
+    } else {
+        moments16<OPT, PD, !PLAIN>(s, a, x.p, x.g, m_in, v_in, m2_in, lam, psr, rp, r, p);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[i] = apply_update(x.p[i], s.d, lam, r[i].u);
         mo[i] = r[i].m;
         vo[i] = r[i].v;
         m2o[i] = r[i].m2;
@@ -377,23 +400,6 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (i >= nmine) mo[i] = vo[i] = m2o[i] = 0.0f;   // past the end of a short block
-    }
-    // stochastic rounding: the element's Philox word, low half for m, high
-    // half for v; the second stream's word, low half for m2 and high half
-    // for a 16-bit parameter stored stochastically (rm, rv, rm2: the 16 bits
-    // as an integer; rp: the whole word, as the parameter store takes them)
-    uint32_t rm[4] = {0, 0, 0, 0}, rv[4] = {0, 0, 0, 0}, rm2[4] = {0, 0, 0, 0}, rp[4] = {0, 0, 0, 0};
-    const bool psr = PD != kP32 && a.p_sr;
-    const uint64_t q = (uint64_t)(C.e0 + e) >> 2;
-    if (sr_fmt(SF)) {
-        PhiloxOut w = sr_block(a.seed, a.step, C.k, q, false);
-        rm[0] = w.w0 & 0xFFFFu; rm[1] = w.w1 & 0xFFFFu; rm[2] = w.w2 & 0xFFFFu; rm[3] = w.w3 & 0xFFFFu;
-        rv[0] = w.w0 >> 16; rv[1] = w.w1 >> 16; rv[2] = w.w2 >> 16; rv[3] = w.w3 >> 16;
-    }
-    if ((sr_fmt(SF) && OPT == kAdEMAMix) || psr) {
-        PhiloxOut w2 = sr_block(a.seed, a.step, C.k, q, true);
-        rm2[0] = w2.w0 & 0xFFFFu; rm2[1] = w2.w1 & 0xFFFFu; rm2[2] = w2.w2 & 0xFFFFu; rm2[3] = w2.w3 & 0xFFFFu;
-        rp[0] = w2.w0; rp[1] = w2.w1; rp[2] = w2.w2; rp[3] = w2.w3;
     }
     const float Am = block_absmax(mo), Av = block_absmax(vo);
     const uint32_t om = blk_encode4<SF, 0>(lds, a, mo, Am, rm);

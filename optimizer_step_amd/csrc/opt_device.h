@@ -437,16 +437,7 @@ __host__ __device__ inline float mini_decode(uint32_t code, int sc)
 // SM103 bias-correction broadcast in 32-bit optimizers", Problem: they are
 // uniform across the workgroup).
 
-struct Scalars {
-    float om1, om2, om3;   // 1 - beta
-    float c1, c2;          // 1 - beta^t, formed in binary64 and rounded once
-    float rc1, rc2;        // RN(1/c1), RN(1/c2)
-    float d;               // 1 - lr*wd
-    float lam;             // lr (the update-norm scale is applied per tensor)
-    float gs;              // gradient scale (a clipping coefficient), 1 if none
-};
-
-__device__ inline double powi(double b, int64_t t)
+__host__ __device__ inline double powi(double b, int64_t t)
 {
     double r = 1.0;
     while (t > 0) {
@@ -457,7 +448,10 @@ __device__ inline double powi(double b, int64_t t)
     return r;
 }
 
-__device__ inline Scalars make_scalars(const StepArgs &a)
+// The call's scalars from its hyperparameters; the host forms them once per
+// call (StepArgs::sc), with IEEE binary64 and binary32 operations only, so
+// they are the same bits on either side.
+__host__ __device__ inline Scalars make_scalars(const StepArgs &a)
 {
     Scalars s;
     s.om1 = 1.0f - a.beta1;
@@ -472,7 +466,16 @@ __device__ inline Scalars make_scalars(const StepArgs &a)
     float lrwd = a.lr * a.wd;
     s.d = 1.0f - lrwd;
     s.lam = a.lr;
-    s.gs = a.grad_scale ? *a.grad_scale : 1.0f;
+    s.gs = 1.0f;
+    return s;
+}
+
+// The scalars a kernel works with: the host's, and the gradient scale from
+// device memory (read when the kernel runs).
+__device__ __forceinline__ Scalars call_scalars(const StepArgs &a)
+{
+    Scalars s = a.sc;
+    if (a.grad_scale) s.gs = *a.grad_scale;
     return s;
 }
 
@@ -523,13 +526,30 @@ __device__ __forceinline__ Mom moments(const Scalars &s, const StepArgs &a, floa
 // hardware reciprocal and square root (each within 1 ulp) instead of
 // correctly rounded division and square root: u is within a few ulp of the
 // exact recipe, far inside the fp32 parameter tolerance.  Used for fp32
-// parameters only; an element whose own v_hat is below 2^-96 (where the
+// parameters, and for a 16-bit parameter where the bound below shows that the
+// stored word is the exact recipe's (moments16); an element whose own v_hat
+// is below 2^-96 (where the
 // hardware square root loses accuracy) takes the exact recipe (fast_ok), so
 // every element's result depends on its own inputs alone.  NaN and infinite
 // moments give the same u either way.
+//
+// With bu given, *bu bounds |u - u_exact| when eps >= 0 and fast_ok holds.
+// Each step's error against the exact recipe's, relative (units of 2^-24):
+// m*RN(1/c1) against RN(m/c1) 3; v_hat likewise 3, its hardware square root
+// (1 ulp) against the correctly rounded one 4.5, so sqrt + eps (eps >= 0
+// only shrinks relative errors) and its rounding 6.5; the hardware
+// reciprocal 2 and the product's rounding 1 against the exact quotient's 1:
+// about 14 for AdamW.  AdEMAMix's numerator mh + alpha*m2 may cancel, so its
+// error is bounded against |mh| + |alpha*m2| instead (3.1 for mh, 2 for the
+// two roundings of the sum, 10.6 for the rest: under 16 in all).  *bu =
+// 2^-19 (|mh| + |alpha*m2|) / den + 2^-140 is twice that, plus room for the
+// absolute error of a direction that falls below the normal range.  The
+// analysis needs mh and 1/den normal (or mh = 0, which only m = 0 gives, and
+// then both directions are the same zero) and (|mh| + |alpha*m2|) / den
+// below 2^126, so that no direction overflows: elsewhere *bu is infinite.
 template <int OPT, bool GS = true>
 __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a, float g, float m,
-                                            float v, float m2)
+                                            float v, float m2, float *bu = nullptr)
 {
     Mom r;
     if (GS) g = g * s.gs;
@@ -539,12 +559,20 @@ __device__ __forceinline__ Mom moments_fast(const Scalars &s, const StepArgs &a,
     const float mh = r.m * s.rc1;
     const float vh = r.v * s.rc2;
     const float rden = __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(vh) + a.eps);
+    float t = 0.0f;
     if (OPT == kAdEMAMix) {
         r.m2 = a.beta3 * m2 + s.om3 * g;
-        r.u = (mh + a.alpha * r.m2) * rden;
+        t = a.alpha * r.m2;
+        r.u = (mh + t) * rden;
     } else {
         r.m2 = 0.0f;
         r.u = mh * rden;
+    }
+    if (bu) {
+        const float amh = __builtin_fabsf(mh);
+        const float mag = (amh + __builtin_fabsf(t)) * rden;
+        const bool ok = (amh >= 0x1p-100f || r.m == 0.0f) && rden >= 0x1p-126f && mag < 0x1p126f;
+        *bu = ok ? __builtin_fmaf(0x1p-19f, mag, 0x1p-140f) : __builtin_inff();
     }
     return r;
 }
@@ -557,20 +585,14 @@ __device__ __forceinline__ bool fast_ok(const Scalars &s, const Mom &r)
     return !(r.v * s.rc2 < 0x1p-96f);
 }
 
-// The moments and direction of four elements: the fast direction (FAST, fp32
-// parameters) with the exact recipe for the elements fast_ok rejects, or the
-// exact recipe throughout (16-bit parameters, whose rounded store must see
-// exactly the oracle's binary32 value).  The wave skips the exact pass when
-// no lane needs it; the result of an element never depends on other lanes.
-template <int OPT, bool FAST, bool GS = true>
+// The moments and direction of four elements with fp32 parameters: the
+// fast direction, with the exact recipe for the elements fast_ok rejects.
+// The wave skips the exact pass when no lane needs it; the result of an
+// element never depends on other lanes.
+template <int OPT, bool GS = true>
 __device__ __forceinline__ void moments4(const Scalars &s, const StepArgs &a, const float g[4],
                                          const float m[4], const float v[4], const float m2[4], Mom r[4])
 {
-    if (!FAST) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = moments<OPT, GS>(s, a, g[i], m[i], v[i], m2[i]);
-        return;
-    }
     bool slow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -104,6 +104,68 @@ __device__ __forceinline__ uint32_t round_p(float x, bool sr, uint32_t rh)
     return sr ? f16_sr(x, rh >> 16) : f16_rne(x);
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit parameters.  Their stored word must be the one the exact recipe's
+// binary32 parameter rounds to.  With the fast direction u and its bound bu
+// (moments_fast), pf = RN(RN(p*d) - step) with step = RN(lam*u), and the
+// exact recipe's pe differs from pf by at most |lam|*bu/2 + 2^-23 (|step| +
+// |pf|) + 2^-148 to first order (the step's and the parameter's roundings;
+// bu already holds a factor two).  B = |lam|*bu + 2^-22 (|step| + |pf|) +
+// 2^-126 covers that twice over, and the rounding of pf -+ B besides, for
+// |lam| <= 2^20 (the caller's test) and with step, pf and B well inside the
+// binary32 range, so that nothing on either path overflows.  Both 16-bit
+// roundings are monotone in |x| for a fixed random operand, so when pf - B
+// and pf + B have one sign and round to one word, pe rounds to it too.
+template <int PD>
+__device__ __forceinline__ bool p16_same(float pf, float step, float bu, float lam, bool sr, uint32_t rh)
+{
+    const float as = __builtin_fabsf(step), ap = __builtin_fabsf(pf);
+    const float B = __builtin_fmaf(__builtin_fabsf(lam), bu, __builtin_fmaf(0x1p-22f, as + ap, 0x1p-126f));
+    const float lo = pf - B, hi = pf + B;
+    if (!(B < 0x1p100f) || !(__builtin_fmaxf(as, ap) < 0x1p126f) || ((fbits(lo) ^ fbits(hi)) >> 31) != 0u)
+        return false;
+    if (PD == kPBF16) {
+        const uint32_t w = sr ? bf16x2_sr_hi(lo, rh, hi, rh) : bf16x2_rne(lo, hi);
+        return (w & 0xFFFFu) == (w >> 16);
+    }
+    // FP16: well inside its range, where its stochastic rounding is plain
+    return __builtin_fabsf(lo) < 0x1p15f && __builtin_fabsf(hi) < 0x1p15f &&
+           round_p<PD>(lo, sr, rh) == round_p<PD>(hi, sr, rh);
+}
+
+// Moments, direction and new binary32 parameter of four elements with a
+// 16-bit parameter (rh: their rounding bits, as the store takes them): the
+// fast direction where p16_same shows that the stored word is the exact
+// recipe's, else (about one element in 2^14 for BF16, 2^11 for FP16, and all
+// of them for eps < 0 or |lam| > 2^20, which the bound does not cover) the
+// exact recipe.  The
+// wave skips the exact pass when no lane needs it; each element's result
+// depends on its own inputs alone.
+template <int OPT, int PD, bool GS>
+__device__ __forceinline__ void moments16(const Scalars &s, const StepArgs &a, const float p[4], const float g[4],
+                                          const float m[4], const float v[4], const float m2[4], float lam, bool sr,
+                                          const uint32_t rh[4], Mom r[4], float pn[4])
+{
+    const bool fast = a.eps >= 0.0f && __builtin_fabsf(lam) <= 0x1p20f;
+    bool slow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float bu;
+        r[i] = moments_fast<OPT, GS>(s, a, g[i], m[i], v[i], m2[i], &bu);
+        pn[i] = apply_update(p[i], s.d, lam, r[i].u);
+        slow[i] = !(fast && fast_ok<OPT>(s, r[i]) && p16_same<PD>(pn[i], lam * r[i].u, bu, lam, sr, rh[i]));
+    }
+    if (__any(slow[0] || slow[1] || slow[2] || slow[3])) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (slow[i]) {
+                r[i] = moments<OPT, GS>(s, a, g[i], m[i], v[i], m2[i]);
+                pn[i] = apply_update(p[i], s.d, lam, r[i].u);
+            }
+        }
+    }
+}
+
 template <int PD>
 __device__ __forceinline__ void store_p4(float *p, int64_t e, const float x[4], bool sr, const uint32_t rh[4])
 {
@@ -310,15 +372,6 @@ __device__ __forceinline__ bool locate_tile(const DevTensor *__restrict__ tens, 
 // A call with no gradient scale, no skip_zeros and no state reset on this
 // step: the step kernels have a variant that spends no instruction on any.
 __host__ inline bool plain_call(const StepArgs &a) { return a.grad_scale == nullptr && !a.skip_zeros && !a.fresh; }
-
-// The per-call scalars, formed by lane 0 and read by every lane after the
-// workgroup's barrier.
-__device__ __forceinline__ Scalars publish_scalars(const StepArgs &a, Scalars &sh)
-{
-    if (threadIdx.x == 0) sh = make_scalars(a);
-    __syncthreads();
-    return sh;
-}
 
 // Occupancy cap.  A 256-thread tile kernel is held to `cap` resident
 // workgroups per compute unit (cap waves per SIMD) by reserving, at launch,

@@ -52,12 +52,10 @@ __global__ __launch_bounds__(kThreads) void unorm_partials_kernel(const DevTenso
                                                                   StepArgs a)
 {
     extern __shared__ uint32_t lds[];
-    __shared__ Scalars sh;
     if (SF == kQ8)
         for (uint32_t i = threadIdx.x; i < 512; i += kThreads) lds[i] = qwords[i];
-    if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
-    const Scalars s = sh;
+    const Scalars s = call_scalars(a);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
@@ -437,6 +435,25 @@ __global__ void debug_round_kernel(const float *x, const uint32_t *r, uint16_t *
         out[i] = (uint16_t)(r ? bf16_sr(x[i], r[i] & 0xFFFFu) : bf16_rne(x[i]));
 }
 
+// For each element: the fast direction, its error bound (infinite where the
+// step takes the exact recipe regardless), and the exact recipe's direction.
+template <int OPT>
+__global__ void debug_direction_kernel(StepArgs a, const float *g, const float *m, const float *v, const float *m2,
+                                       float *out, int64_t n)
+{
+    const Scalars s = call_scalars(a);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float mm2 = OPT == kAdEMAMix ? m2[i] : 0.0f;
+        float bu;
+        const Mom f = moments_fast<OPT, false>(s, a, g[i], m[i], v[i], mm2, &bu);
+        const Mom e = moments<OPT, false>(s, a, g[i], m[i], v[i], mm2);
+        out[i] = f.u;
+        out[n + i] = a.eps >= 0.0f && fast_ok<OPT>(s, f) ? bu : __builtin_inff();
+        out[2 * n + i] = e.u;
+    }
+}
+
 // codes[i] of x[i] against one codebook's table in LDS.  Inputs in the step's
 // fast-path domain (|x| <= 1, normal or zero; for the unsigned table x >= +0)
 // take the step's own lookup (q8_code_hi_lds); other inputs the general one.
@@ -714,6 +731,19 @@ hipError_t launch_debug_round(const float *x, const uint32_t *r, uint16_t *out, 
     int64_t blocks = min((int64_t)4096, (n + 255) / 256);
     hipLaunchKernelGGL(debug_round_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st,
                        x, r, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_direction(int opt, const StepArgs &a, const float *g, const float *m, const float *v,
+                                  const float *m2, float *out, int64_t n, hipStream_t st)
+{
+    int64_t blocks = min((int64_t)4096, (n + 255) / 256);
+    if (opt == kAdEMAMix)
+        hipLaunchKernelGGL(debug_direction_kernel<kAdEMAMix>, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0,
+                           st, a, g, m, v, m2, out, n);
+    else
+        hipLaunchKernelGGL(debug_direction_kernel<kAdamW>, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st,
+                           a, g, m, v, m2, out, n);
     return hipGetLastError();
 }
 

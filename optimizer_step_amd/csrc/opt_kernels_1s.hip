@@ -65,20 +65,17 @@ struct Group1 {
 
 constexpr int64_t kEwTile1 = (int64_t)kThreads * kEwGroups * 4;
 
-__device__ __forceinline__ Scalars1 publish_scalars1(const StepArgs &a, Scalars1 &sh)
+// The call's scalars (uniform: every lane forms the same values).
+__device__ __forceinline__ Scalars1 scalars1(const StepArgs &a)
 {
-    if (threadIdx.x == 0) {
-        Scalars1 s;
-        s.om1 = 1.0f - a.beta1;
-        s.om2 = 1.0f - a.beta2;
-        const float lrwd = a.lr * a.wd;
-        s.d = 1.0f - lrwd;
-        s.gs = a.grad_scale ? *a.grad_scale : 1.0f;
-        s.first = a.bc_step == 1;
-        sh = s;
-    }
-    __syncthreads();
-    return sh;
+    Scalars1 s;
+    s.om1 = 1.0f - a.beta1;
+    s.om2 = 1.0f - a.beta2;
+    const float lrwd = a.lr * a.wd;
+    s.d = 1.0f - lrwd;
+    s.gs = a.grad_scale ? *a.grad_scale : 1.0f;
+    s.first = a.bc_step == 1;
+    return s;
 }
 
 template <int OPT, int GD, int SF>
@@ -138,9 +135,7 @@ template <int OPT, int GD, int SF>
 __global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__restrict__ tens,
                                                            const int32_t *__restrict__ ctab, StepArgs a)
 {
-    __shared__ Scalars1 sh;
-    Scalars1 s;
-    bool have_s = false;
+    const Scalars1 s = scalars1(a);
     const bool fresh = a.fresh != 0;
     for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
         DevTensor T;
@@ -152,11 +147,9 @@ __global__ __launch_bounds__(kThreads) void step_1s_kernel(const DevTensor *__re
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u) s1_load<OPT, GD, SF>(T, e0 + 4 * (threadIdx.x + u * kThreads), fresh, x[u]);
             load_prio_lo();
-            if (!have_s) { s = publish_scalars1(a, sh); have_s = true; }
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u) s1_finish<OPT, GD, SF>(a, s, T, e0 + 4 * (threadIdx.x + u * kThreads), x[u]);
         } else {   // a tensor's last, short tile
-            if (!have_s) { s = publish_scalars1(a, sh); have_s = true; }
             const int64_t ngroups = len >> 2;
             for (int64_t i = threadIdx.x; i < ngroups; i += kThreads) {
                 Group1 x0;

@@ -69,22 +69,6 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
                                           uint32_t i, float lam, Group &x)
 {
     float mo[4], vo[4], m2o[4];
-    // fp32 parameters: the direction with the hardware reciprocal and square
-    // root (exact recipe for an element with a tiny v_hat); 16-bit
-    // parameters: the exact recipe
-    Mom rr[4];
-    moments4<OPT, PD == kP32, !PLAIN>(s, a, x.g, x.m, x.v, x.m2, rr);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const Mom &r = rr[i];
-        const float pn = apply_update(x.p[i], s.d, lam, r.u);
-        mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
-        if (!PLAIN && a.skip_zeros && x.g[i] == 0.0f) {   // p (decay included) and the states as they were
-            mo[i] = x.m[i]; vo[i] = x.v[i]; m2o[i] = x.m2[i];
-        } else {
-            x.p[i] = pn;
-        }
-    }
     // stochastic rounding: the first stream's word rounds m (its low half) and
     // v (its high half), the second stream's m2 (low half) and a 16-bit p
     // (high half); the stores take the 16 bits in the high half of a word
@@ -100,6 +84,28 @@ __device__ __forceinline__ void ew_finish(const StepArgs &a, const Scalars &s, c
         PhiloxOut w2 = sr_block(a.seed, a.step, R.rk, q, true);
         rm2[0] = w2.w0 << 16; rm2[1] = w2.w1 << 16; rm2[2] = w2.w2 << 16; rm2[3] = w2.w3 << 16;
         rp[0] = w2.w0; rp[1] = w2.w1; rp[2] = w2.w2; rp[3] = w2.w3;
+    }
+    // fp32 parameters: the direction with the hardware reciprocal and square
+    // root (exact recipe for an element with a tiny v_hat); 16-bit
+    // parameters: the same where it provably stores the exact recipe's word
+    Mom rr[4];
+    float pn[4];
+    if (PD == kP32) {
+        moments4<OPT, !PLAIN>(s, a, x.g, x.m, x.v, x.m2, rr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pn[i] = apply_update(x.p[i], s.d, lam, rr[i].u);
+    } else {
+        moments16<OPT, PD, !PLAIN>(s, a, x.p, x.g, x.m, x.v, x.m2, lam, psr, rp, rr, pn);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const Mom &r = rr[i];
+        mo[i] = r.m; vo[i] = r.v; m2o[i] = r.m2;
+        if (!PLAIN && a.skip_zeros && x.g[i] == 0.0f) {   // p (decay included) and the states as they were
+            mo[i] = x.m[i]; vo[i] = x.v[i]; m2o[i] = x.m2[i];
+        } else {
+            x.p[i] = pn[i];
+        }
     }
     // the store policy measured fastest for this configuration (opt_elem.h)
     constexpr bool sc1 = OPT == kAdamW && GD != kGradF32 && SF == kF32 && PD == kP32;
@@ -162,9 +168,7 @@ template <int OPT, int GD, int SF, int PD, bool PLAIN>
 __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
                                                                        const int32_t *__restrict__ ctab, StepArgs a)
 {
-    __shared__ Scalars sh;
-    Scalars s;
-    bool have_s = false;
+    const Scalars s = call_scalars(a);
     const bool fresh = a.fresh != 0;
     for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
         DevTensor T;
@@ -178,13 +182,11 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
             for (int u = 0; u < kEwGroups; ++u)
                 ew_load<OPT, GD, SF, PD>(R, 4u * (threadIdx.x + u * kEwThreads), fresh, x[u]);
             load_prio_lo(SF != kBF16RN);
-            if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll
             for (int u = 0; u < kEwGroups; ++u)
                 ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, R, 4u * (threadIdx.x + u * kEwThreads), lam, x[u]);
         } else {   // a tensor's last, short tile
-            if (!have_s) { s = publish_scalars(a, sh); have_s = true; }
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
             const uint32_t ngroups = (uint32_t)(len >> 2);
             for (uint32_t i = threadIdx.x; i < ngroups; i += kEwThreads) {
@@ -198,21 +200,26 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
     }
 }
 
-// Resident workgroups per compute unit of the fp32-state AdamW step with
-// 16-bit gradients (0: as many as registers allow, 7 for the plain kernel).
-// Measured on MI355X in paired runs over one arena (fp32 p, m, v; BF16 g),
-// caps 0 / 3 / 4 / 5 / 6: 290-tensor Llama-7B-shaped list 29.41 / 27.45 /
-// 27.71 / 28.56 / 29.41 ms, and with a gradient scale (the kernel that also
-// reads it) 29.0 / 28.4 / 27.7 / 29.0 / 29.0 ms; 3 x 2^30 elements 13.83 /
-// 12.73 / 12.89 / 13.42 / 13.83 ms; one 2^30 tensor 4.69 / 4.59 / 4.60 /
-// 4.59 / 4.69 ms; 2^29 elements 2.32 / 2.40 / 2.31 / 2.28 / 2.32 ms; 2^28
-// elements 1.17 / 1.22 / 1.17 / 1.16 / 1.17 ms.  BF16 parameters (2^30):
-// 3.85 / 4.31 / 3.82 / 3.73 / 3.84 ms.  The BF16 state formats and AdEMAMix
-// gain nothing (BF16 states lose up to 15 % at 4), so keep the default.
+// Resident workgroups per compute unit of an element-wise step (0: as many
+// as registers allow, 8 for most of them).  Measured on MI355X in paired runs
+// over one arena.  fp32-state AdamW with BF16 g and fp32 p, caps 0 / 3 / 4 /
+// 5 / 6: 290-tensor Llama-7B-shaped list 29.41 / 27.45 / 27.71 / 28.56 /
+// 29.41 ms, and with a gradient scale (the kernel that also reads it) 29.0 /
+// 28.4 / 27.7 / 29.0 / 29.0 ms; 3 x 2^30 elements 13.83 / 12.73 / 12.89 /
+// 13.42 / 13.83 ms; one 2^30 tensor 4.69 / 4.59 / 4.60 / 4.59 / 4.69 ms;
+// 2^29 elements 2.32 / 2.40 / 2.31 / 2.28 / 2.32 ms; 2^28 elements 1.17 /
+// 1.22 / 1.17 / 1.16 / 1.17 ms.  BF16 parameters (2^30): 3.85 / 4.31 /
+// 3.82 / 3.73 / 3.84 ms.  AdEMAMix with fp32 states (2^28), caps 0 / 4 / 5 /
+// 6: 1.735 / 1.685 / 1.701 / 1.736 ms; AdamW with BF16 nearest states (2^30),
+// caps 0 / 5 / 6 / 7: 3.108 / 3.093 / 3.065 / 3.107 ms.  BF16 stochastic
+// states gain nothing from a cap (and lose up to 10 % at 4).
 template <int OPT, int GD, int SF, int PD, bool PLAIN>
 static int ew_wg_cap(const StepArgs &a)
 {
-    if (OPT != kAdamW || GD == kGradF32 || SF != kF32) return 0;
+    if (OPT == kAdEMAMix) return SF == kF32 ? 4 : 0;
+    if (GD == kGradF32) return 0;
+    if (SF == kBF16RN) return PD == kP32 ? 6 : 0;
+    if (SF != kF32) return 0;
     if (PD != kP32 || a.nchunks * a.chunk < ((int64_t)1 << 30)) return 5;
     return PLAIN ? 3 : 4;
 }
@@ -225,9 +232,11 @@ static hipError_t launch_ew_p(int fmt, const StepArgs &a, const LaunchGeom &lg, 
         return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD, PLAIN>, kEwTile,
                                         cap_lds(lg, ew_wg_cap<OPT, GD, kF32, PD, PLAIN>(a)), lg, a, st);
     case kBF16RN:
-        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, kEwTile, cap_lds(lg, 0), lg, a, st);
+        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, kEwTile,
+                                        cap_lds(lg, ew_wg_cap<OPT, GD, kBF16RN, PD, PLAIN>(a)), lg, a, st);
     case kBF16SR:
-        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, kEwTile, cap_lds(lg, 0), lg, a, st);
+        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, kEwTile,
+                                        cap_lds(lg, ew_wg_cap<OPT, GD, kBF16SR, PD, PLAIN>(a)), lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }

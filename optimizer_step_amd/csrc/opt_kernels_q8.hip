@@ -82,7 +82,6 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
                                                              StepArgs a)
 {
     extern __shared__ uint32_t lds[];
-    __shared__ Scalars sh;
     __shared__ float mtab_s[mini_fmt(SF) ? kMiniTab : 1];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,9 +89,8 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
         for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
     if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
     const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
-    if (threadIdx.x == 0) sh = make_scalars(a);
     __syncthreads();
-    const Scalars s = sh;
+    const Scalars s = call_scalars(a);
     q8_tiles<OPT, GD, SF, PD, PLAIN>(tens, ctab, a, s, lds, mtab, lane, wave);
 }
 

@@ -78,6 +78,18 @@ struct LaunchGeom {
     int wg_cap = -1;
 };
 
+// Per-call scalars of the two-state steps, formed once by the host
+// (make_scalars) in the order the element recipe expects; the gradient scale
+// is read from device memory by the kernels.
+struct Scalars {
+    float om1, om2, om3;   // 1 - beta
+    float c1, c2;          // 1 - beta^t, formed in binary64 and rounded once
+    float rc1, rc2;        // RN(1/c1), RN(1/c2)
+    float d;               // 1 - lr*wd
+    float lam;             // lr (the update-norm scale is applied per tensor)
+    float gs;              // gradient scale (a clipping coefficient), 1 if none
+};
+
 // Kernel arguments (passed by value).
 struct StepArgs {
     const DevTensor *tens;
@@ -98,6 +110,7 @@ struct StepArgs {
     int32_t p_dtype;               // ParamT of the bucket's parameters
     int32_t p_sr;                  // 1: 16-bit parameters are stored with stochastic rounding
     int32_t skip_zeros;            // 1: elements whose gradient is exactly 0 keep p and their states
+    Scalars sc;                    // make_scalars of these arguments (gs = 1)
     // tile space of the launch (set by the launcher from the kernel's tile):
     // chunk c holds tiles [c << tile_sh, (c + 1) << tile_sh) of tile elements each
     int64_t tile;

@@ -392,3 +392,18 @@ def test_wg_cap_values(L):
         assert lib.opt_debug_set_wg_cap(bad) == -1, bad
     for ok in (0, 2, 3, 32, -1):
         assert lib.opt_debug_set_wg_cap(ok) == 0, ok
+
+
+@pytest.mark.parametrize("opt,hp,arrays,status", [
+    (2, {}, (4096, 4096, 4096, 0, 4096), -1),                       # a one-state optimizer
+    (0, dict(beta1=1.0), (4096, 4096, 4096, 0, 4096), -1),           # beta outside [0, 1)
+    (0, dict(step=0), (4096, 4096, 4096, 0, 4096), -1),              # step < 1
+    (0, {}, (0, 4096, 4096, 0, 4096), -1),                           # NULL g
+    (1, {}, (4096, 4096, 4096, 0, 4096), -1),                        # AdEMAMix without m2
+])
+def test_debug_direction_checks_its_arguments(L, opt, hp, arrays, status):
+    import ctypes
+    h = L.hparams(**hp)
+    g, m, v, m2, out = (a or None for a in arrays)
+    assert L.lib().opt_debug_direction(opt, ctypes.byref(h), g, m, v, m2, out, 16, None) == status
+    assert L.lib().opt_debug_direction(0, None, 4096, 4096, 4096, None, 4096, 16, None) == -1

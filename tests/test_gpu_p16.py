@@ -5,9 +5,13 @@ bias-correction broadcast in 32-bit optimizers", Correctness oracle: FP16,
 BF16 and FP32 parameter and gradient storage).
 
 Bars: the cast bit-exact; 16-bit parameters and every state bit-exact.  With
-16-bit parameters the kernels form the direction u with correctly rounded
-division and square root in the oracle's binary32 order, so the value
-rounded to 16 bits is the oracle's and so is every stored word."""
+16-bit parameters the kernels take the fast direction u (hardware reciprocal
+and square root) only where its error bound shows that the parameter rounds
+to the word the exact recipe's binary32 value rounds to (one element in
+about 2^14 for BF16, 2^11 for FP16 falls back to the exact recipe, which
+forms u with correctly rounded division and square root in the oracle's
+order), so every stored word is the oracle's.  The bound itself is checked
+in test_gpu_direction_bound.py."""
 import numpy as np
 import pytest
 
@@ -178,6 +182,17 @@ def test_p16_adamw(fmt, pdt, p_sr):
     gds = ["f32", "bf16", "f16", "bf16"] if pdt == oracle.P_BF16 else ["f32", "f16", "f16", "f32"]
     ps, st, dev, _, _, pmax = _run_p16("adamw", fmt, sizes, gds, pdt, p_sr, 4, dict(lr=1e-2, weight_decay=0.1))
     _check(ps, st, dev, fmt, "adamw", pdt, 4, pmax)
+
+
+@pytest.mark.parametrize("p_sr", [False, True])
+@pytest.mark.parametrize("pdt", [oracle.P_BF16, oracle.P_F16])
+def test_p16_many_elements(pdt, p_sr):
+    """2^20 + 5 elements over three steps: a few hundred (BF16) to a few
+    thousand (FP16) of them take the exact fallback, every word bit-exact."""
+    sizes = [(1 << 20) + 5]
+    ps, st, dev, _, _, pmax = _run_p16("adamw", "bf16_sr", sizes, ["bf16"], pdt, p_sr, 3,
+                                       dict(lr=1e-3, weight_decay=0.01))
+    _check(ps, st, dev, "bf16_sr", "adamw", pdt, 3, pmax)
 
 
 @pytest.mark.parametrize("pdt", [oracle.P_BF16, oracle.P_F16])
