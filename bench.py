@@ -268,6 +268,14 @@ def interleaved_rounds(rows, rounds, torch):
     row every sample, the median and p10/p90 over all samples, and the median
     of each round."""
     per_row = {r.name: [] for r in rows}
+    # untimed: every row once, then about 2 s of the first row, so that the
+    # rounds start with the device at its working clocks (building the rows
+    # leaves it idle for a while)
+    for r in rows:
+        r.run(1, 0)
+    warm = rows[0].run(0, 3)
+    k = max(1, int(2000.0 / max(1e-3, sum(warm["samples_ms"]) / 3)))
+    rows[0].run(k, 0)
     for _ in range(rounds):
         for r in rows:
             big = r.elements * r.bpe > 50e9
