@@ -638,7 +638,8 @@ hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *
     int64_t want = (n / 4 + tile_g - 1) / tile_g;
     if (lg.wgs_per_cu > 0) want = min(want, (int64_t)lg.ncu * lg.wgs_per_cu);
     const unsigned grid = (unsigned)max((int64_t)1, min(want, kMaxGrid));
-    hipLaunchKernelGGL(debug_stream_kernel, dim3(grid), dim3(kThreads), 0, st, a);
+    // no cap unless one is set (opt_debug_set_wg_cap), to read a capped stream's rate
+    hipLaunchKernelGGL(debug_stream_kernel, dim3(grid), dim3(kThreads), cap_lds(lg, 0), st, a);
     return hipGetLastError();
 }
 

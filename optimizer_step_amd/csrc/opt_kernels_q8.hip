@@ -34,6 +34,10 @@ static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 constexpr int64_t kMiniTile = OPT_MINI_TILE;
 static_assert(kMiniTile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 
+#ifndef OPT_Q8_PREFETCH
+#define OPT_Q8_PREFETCH 0
+#endif
+
 #ifndef OPT_Q8_WAVES
 #define OPT_Q8_WAVES 7
 #endif
@@ -56,6 +60,29 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
         const uint32_t nfull = (uint32_t)(len / kQBlock);
         const QChunk C = q8_chunk<GD, SF, PD>(T, e0);
         uint32_t b = wave;
+#if OPT_Q8_PREFETCH
+        // the wave's next block is loaded while it finishes this one
+        if (b < nfull) {
+            QIn xa;
+            load_prio_hi();
+            q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, xa);
+            load_prio_lo();
+            for (;;) {
+                const uint32_t bn = b + kQ8Waves;
+                const bool more = bn < nfull;
+                QIn xb;
+                if (more) {
+                    load_prio_hi();
+                    q8_load<OPT, GD, SF, PD, true>(a, C, bn, 4, lane, xb);
+                    load_prio_lo();
+                }
+                q8_finish<OPT, SF, PD, true, PLAIN>(a, s, C, lds, mtab, b, 4, lane, lam, xa);
+                b = bn;
+                if (!more) break;
+                xa = xb;
+            }
+        }
+#else
         for (; b < nfull; b += kQ8Waves) {
             QIn x0;
             load_prio_hi();
@@ -63,6 +90,7 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
             load_prio_lo();
             q8_finish<OPT, SF, PD, true, PLAIN>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
         }
+#endif
         if (b < nblk) {   // the tensor's short last block
             const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
             QIn x0;
