@@ -35,8 +35,11 @@ constexpr int64_t kMiniTile = OPT_MINI_TILE;
 static_assert(kMiniTile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
 
 #ifndef OPT_Q8_PREFETCH
-#define OPT_Q8_PREFETCH 0
+#define OPT_Q8_PREFETCH (-1)
 #endif
+// Whether a wave loads its next block before finishing the current one
+// (OPT_Q8_PREFETCH: -1 per format, 0 never, 1 always).
+constexpr bool q8_prefetch(int sf) { return sf == kFP8RN || sf == kFP4RN; }
 
 #ifndef OPT_Q8_WAVES
 #define OPT_Q8_WAVES 7
@@ -60,14 +63,15 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
         const uint32_t nfull = (uint32_t)(len / kQBlock);
         const QChunk C = q8_chunk<GD, SF, PD>(T, e0);
         uint32_t b = wave;
-#if OPT_Q8_PREFETCH
-        // the wave's next block is loaded while it finishes this one
-        if (b < nfull) {
+        if (OPT_Q8_PREFETCH < 0 ? q8_prefetch(SF) : OPT_Q8_PREFETCH != 0) {
+            // the wave's next block is loaded while it finishes this one
             QIn xa;
-            load_prio_hi();
-            q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, xa);
-            load_prio_lo();
-            for (;;) {
+            if (b < nfull) {
+                load_prio_hi();
+                q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, xa);
+                load_prio_lo();
+            }
+            while (b < nfull) {
                 const uint32_t bn = b + kQ8Waves;
                 const bool more = bn < nfull;
                 QIn xb;
@@ -78,19 +82,17 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
                 }
                 q8_finish<OPT, SF, PD, true, PLAIN>(a, s, C, lds, mtab, b, 4, lane, lam, xa);
                 b = bn;
-                if (!more) break;
-                xa = xb;
+                if (more) xa = xb;
+            }
+        } else {
+            for (; b < nfull; b += kQ8Waves) {
+                QIn x0;
+                load_prio_hi();
+                q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
+                load_prio_lo();
+                q8_finish<OPT, SF, PD, true, PLAIN>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
             }
         }
-#else
-        for (; b < nfull; b += kQ8Waves) {
-            QIn x0;
-            load_prio_hi();
-            q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
-            load_prio_lo();
-            q8_finish<OPT, SF, PD, true, PLAIN>(a, s, C, lds, mtab, b, 4, lane, lam, x0);
-        }
-#endif
         if (b < nblk) {   // the tensor's short last block
             const int nm = q8_mine(T, e0 + (int64_t)b * kQBlock, lane);
             QIn x0;
