@@ -310,6 +310,15 @@ int opt_round_cast(const float *x, void *out, int64_t n, int32_t out_dtype, int3
 int opt_debug_mini(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
                    int64_t n, void *stream);
 
+/* The step's encoder for the same formats: codes[i] for groups of four values
+ * of one block with absmax A, as the blockwise step forms them (gfx950's
+ * scaled conversions for E4M3 stochastic, E2M1, and unsigned E2M2 stochastic
+ * through E5M2; integer rounding otherwise).  n a multiple of 4; r as for
+ * opt_debug_mini.  Device arrays, asynchronous on `stream`.  OPT_EINVAL for a
+ * bad elem, n, A or NULL array. */
+int opt_debug_mini_pack(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes, int64_t n,
+                        void *stream);
+
 /* The same, computed on the host from the same source (host arrays). */
 int opt_debug_mini_host(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes,
                         float *decoded, int64_t n);

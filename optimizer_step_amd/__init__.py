@@ -96,6 +96,7 @@ def lib():
             "opt_debug_stream": ([vp, i32, vp, i32, i64, vp], i32),
             "opt_grad_norm": ([ctypes.POINTER(OptGrad), i64, vp, ctypes.c_float, i32, vp, vp], i32),
             "opt_debug_mini": ([i32, ctypes.c_float, vp, vp, vp, vp, i64, vp], i32),
+            "opt_debug_mini_pack": ([i32, ctypes.c_float, vp, vp, vp, i64, vp], i32),
             "opt_round_cast": ([vp, vp, i64, i32, i32, ctypes.c_uint64, ctypes.c_uint64, vp], i32),
             "opt_step_1state": ([i32, T, i64, i32, H, vp], i32),
             "opt_debug_mini_host": ([i32, ctypes.c_float, vp, vp, vp, vp, i64], i32),
@@ -421,6 +422,13 @@ def opt_round_cast(x, out, stochastic=False, seed=0, offset=0, stream=None):
 def opt_debug_mini(elem, A, x, r, codes, decoded, stream=None):
     return _check(lib().opt_debug_mini(int(elem), float(A), _ptr(x), _ptr(r), _ptr(codes), _ptr(decoded),
                                        x.numel(), _stream(stream)))
+
+
+def opt_debug_mini_pack(elem, A, x, r, codes, stream=None):
+    """The blockwise step's encoder (hardware conversions included) on the
+    device, four values at a time; x.numel() a multiple of 4."""
+    return _check(lib().opt_debug_mini_pack(int(elem), float(A), _ptr(x), _ptr(r) if r is not None else None,
+                                            _ptr(codes), x.numel(), _stream(stream)))
 
 
 def opt_debug_mini_host(elem, A, x, r=None):

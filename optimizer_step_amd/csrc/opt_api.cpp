@@ -33,6 +33,8 @@ hipError_t launch_debug_quantize(const QTabs &q, int is_signed, const float *x, 
                                  hipStream_t st);
 hipError_t launch_debug_mini(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, float *decoded,
                              int64_t n, hipStream_t st);
+hipError_t launch_debug_mini_pack(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, int64_t n,
+                                  hipStream_t st);
 hipError_t launch_round_cast(const float *x, uint16_t *out, int64_t n, int bf16, int sr, uint64_t seed,
                              uint64_t offset, const LaunchGeom &lg, hipStream_t st);
 hipError_t launch_debug_stream(const float *const *src, int nsrc, float *const *dst, int ndst, int64_t n,
@@ -1114,6 +1116,18 @@ int opt_debug_mini(int32_t elem, float A, const float *x, const uint32_t *r, uin
     if (rc != OPT_OK || n == 0) return rc;
     hipError_t e = launch_debug_mini(elem, A, x, r, codes, decoded, n, (hipStream_t)stream);
     return e == hipSuccess ? OPT_OK : hip_fail(e, "debug mini launch");
+}
+
+int opt_debug_mini_pack(int32_t elem, float A, const float *x, const uint32_t *r, uint8_t *codes, int64_t n,
+                        void *stream)
+{
+    if (elem < 0 || elem > 2) return fail(OPT_EINVAL, "elem must be 0 (E4M3), 1 (E2M1) or 2 (unsigned E2M2)");
+    if (n < 0 || n % 4 != 0) return fail(OPT_EINVAL, "n must be a non-negative multiple of 4");
+    if (n > 0 && (!x || !codes)) return fail(OPT_EINVAL, "x or codes is NULL");
+    if (A == A && A < 0.0f) return fail(OPT_EINVAL, "A must not be negative");
+    if (n == 0) return OPT_OK;
+    hipError_t e = launch_debug_mini_pack(elem, A, x, r, codes, n, (hipStream_t)stream);
+    return e == hipSuccess ? OPT_OK : hip_fail(e, "debug mini pack launch");
 }
 
 int opt_debug_div_by(const float *a, const float *b, float *out, int64_t n)

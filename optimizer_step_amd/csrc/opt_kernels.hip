@@ -501,6 +501,37 @@ __global__ void debug_mini_kernel(int elem, float A, const float *x, const uint3
     }
 }
 
+// codes[i] of x[i] as the step's blockwise encoder forms them: four values of
+// a block at a time through mini_pack4 (gfx950's scaled conversions wherever
+// the step uses them), one byte per element on output.
+template <class F, bool SR>
+__device__ __forceinline__ void debug_pack_group(float A, const float *x, const uint32_t *r, uint8_t *codes,
+                                                 int64_t g)
+{
+    float v[4];
+    uint32_t rr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[k] = x[4 * g + k];
+        rr[k] = SR ? (r[4 * g + k] & 0xFFFFu) : 0u;
+    }
+    const uint32_t w = mini_pack4<F, SR>(v, A, rr);
+    constexpr int W = F::kSign == 0x80u ? 8 : 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) codes[4 * g + k] = (uint8_t)((w >> (W * k)) & ((1u << W) - 1u));
+}
+
+__global__ void debug_mini_pack_kernel(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes,
+                                       int64_t ngroups)
+{
+    for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < ngroups;
+         g += (int64_t)gridDim.x * blockDim.x) {
+        if (elem == 0) r ? debug_pack_group<E4M3, true>(A, x, r, codes, g) : debug_pack_group<E4M3, false>(A, x, r, codes, g);
+        else if (elem == 1) r ? debug_pack_group<E2M1, true>(A, x, r, codes, g) : debug_pack_group<E2M1, false>(A, x, r, codes, g);
+        else r ? debug_pack_group<E2M2U, true>(A, x, r, codes, g) : debug_pack_group<E2M2U, false>(A, x, r, codes, g);
+    }
+}
+
 // The standalone rounding cast: n fp32 values to BF16 (BF) or FP16 words,
 // nearest-even or stochastic.  Element j's random integer is the low half of
 // word j%4 of Philox4x32-10 keyed by the seed, counter (j>>2, j>>34, offset):
@@ -770,6 +801,16 @@ hipError_t launch_debug_mini(int elem, float A, const float *x, const uint32_t *
     int64_t blocks = min((int64_t)1024, (n + 255) / 256);
     hipLaunchKernelGGL(debug_mini_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st, elem, A, x, r,
                        codes, decoded, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_mini_pack(int elem, float A, const float *x, const uint32_t *r, uint8_t *codes, int64_t n,
+                                  hipStream_t st)
+{
+    const int64_t ng = n / 4;
+    int64_t blocks = min((int64_t)1024, (ng + 255) / 256);
+    hipLaunchKernelGGL(debug_mini_pack_kernel, dim3((unsigned)max((int64_t)1, blocks)), dim3(256), 0, st, elem, A, x,
+                       r, codes, ng);
     return hipGetLastError();
 }
 

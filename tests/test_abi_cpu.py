@@ -407,3 +407,8 @@ def test_debug_direction_checks_its_arguments(L, opt, hp, arrays, status):
     g, m, v, m2, out = (a or None for a in arrays)
     assert L.lib().opt_debug_direction(opt, ctypes.byref(h), g, m, v, m2, out, 16, None) == status
     assert L.lib().opt_debug_direction(0, None, 4096, 4096, 4096, None, 4096, 16, None) == -1
+
+
+@pytest.mark.parametrize("elem,n,A,status", [(3, 4, 1.0, -1), (0, 6, 1.0, -1), (0, -4, 1.0, -1), (1, 4, -1.0, -1)])
+def test_mini_pack_checks_its_arguments(L, elem, n, A, status):
+    assert L.lib().opt_debug_mini_pack(elem, A, 4096, None, 8192, n, None) == status

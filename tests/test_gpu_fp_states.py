@@ -65,6 +65,40 @@ def test_device_codec_matches_oracle(elem):
             assert np.array_equal(d[~nan].view(np.uint32), wdec[~nan].view(np.uint32)), (elem, A, sr)
 
 
+@pytest.mark.parametrize("elem", [0, 1, 2])
+def test_step_encoder_matches_oracle(elem):
+    """The encoder the blockwise step runs (four values at a time, gfx950's
+    scaled conversions for E4M3 stochastic, E2M1, and unsigned E2M2
+    stochastic through E5M2) against the oracle's grid walk, for both
+    roundings, across block scales: every normal scale the conversions take,
+    the ends of their range and past them (where the step rounds in integer
+    arithmetic), subnormal absmax included."""
+    import torch
+    import optimizer_step_amd as osa
+    from tests.test_abi_cpu import _mini_inputs
+    rng = np.random.default_rng(290 + elem)
+    emax, emin = {0: (8, -6), 1: (2, 0), 2: (2, 0)}[elem]
+    As = [np.float32(v) for v in (1.0, 1.5, 448.0, 7.0, 3e-3, 2.5e-12, 1e30, 3e-39, 1e-44)]
+    # nsc = emax - floor(log2 A) at the conversions' limits (-127 / -113 and 126) and beyond
+    for nsc in (-128, -127, -126, -114, -113, -112, 0, 125, 126, 127):
+        a = 1.3 * 2.0 ** (emax - nsc)
+        if 0 < a < 3.4e38:
+            As.append(np.float32(a))
+    for A in As:
+        x = _mini_inputs(elem, A, rng)
+        x = np.concatenate([x, np.zeros((-x.size) % 4, np.float32)])
+        for sr in (False, True):
+            r = rng.integers(0, 65536, x.size).astype(np.uint32) if sr else None
+            codes = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+            osa.opt_debug_mini_pack(elem, float(A), to_dev(x), None if r is None else torch.from_numpy(r.view(np.int32)).cuda(),
+                                    codes)
+            torch.cuda.synchronize()
+            got = to_host(codes)
+            want = np.array([oracle.mini_encode(elem, v, A, int(r[i]) if sr else -1) for i, v in enumerate(x)])
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, (elem, float(A), sr, x[bad[:4]], got[bad[:4]], want[bad[:4]])
+
+
 @pytest.mark.parametrize("fmt", FP_FMTS)
 @pytest.mark.parametrize("opt", ["adamw", "ademamix"])
 def test_step_parity(opt, fmt):
