@@ -428,11 +428,15 @@ __global__ void debug_philox_kernel(uint64_t seed, int64_t t, int32_t k, int64_t
     }
 }
 
+// The BF16 roundings the step kernels store with (gfx950's pair conversions,
+// the element's 16 random bits in the high half of the operand).
 __global__ void debug_round_kernel(const float *x, const uint32_t *r, uint16_t *out, int64_t n)
 {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        out[i] = (uint16_t)(r ? bf16_sr(x[i], r[i] & 0xFFFFu) : bf16_rne(x[i]));
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t rh = r ? (r[i] & 0xFFFFu) << 16 : 0u;
+        out[i] = (uint16_t)((r ? bf16x2_sr_hi(x[i], rh, x[i], rh) : bf16x2_rne(x[i], x[i])) & 0xFFFFu);
+    }
 }
 
 // For each element: the fast direction, its error bound (infinite where the
