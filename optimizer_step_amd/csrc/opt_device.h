@@ -432,10 +432,10 @@ __host__ __device__ inline float mini_decode(uint32_t code, int sc)
 }
 
 // ---------------------------------------------------------------------------
-// Bias corrections and the other per-call scalars.  Formed once per
-// workgroup by one lane and published through LDS (the issue "Investigate
-// SM103 bias-correction broadcast in 32-bit optimizers", Problem: they are
-// uniform across the workgroup).
+// Bias corrections and the other per-call scalars.  They are uniform across
+// the launch (the issue "Investigate SM103 bias-correction broadcast in
+// 32-bit optimizers", Problem), so the host forms them once per call and the
+// kernels receive them in their arguments (StepArgs::sc).
 
 __host__ __device__ inline double powi(double b, int64_t t)
 {
