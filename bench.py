@@ -29,10 +29,17 @@ KERNEL_SOURCES = ["opt_kernels_ew.hip", "opt_elem.h", "opt_device.h", "opt_plan.
 
 
 def kernel_hash():
+    """Hash of the headline kernel's sources with comments and blank space
+    taken out, so that the committed counters stay valid across edits to
+    comments alone."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "optimizer_step_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "optimizer_step_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
