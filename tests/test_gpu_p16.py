@@ -195,6 +195,21 @@ def test_p16_many_elements(pdt, p_sr):
     _check(ps, st, dev, "bf16_sr", "adamw", pdt, 3, pmax)
 
 
+@pytest.mark.parametrize("eps", [0.0, -1e-3])
+@pytest.mark.parametrize("opt", ["adamw", "ademamix"])
+def test_p16_eps_edges(opt, eps):
+    """eps = 0 keeps the fast direction's bound (tiny v_hat takes the exact
+    recipe per element); a negative eps is outside the bound's analysis, so
+    every element takes the exact recipe (directions that blow up included).
+    Every word bit-exact either way."""
+    sizes = [1000, 32768 + 77]
+    hp = dict(lr=1e-2, weight_decay=0.1, eps=eps)
+    if opt == "ademamix":
+        hp.update(beta3=0.999, alpha=5.0)
+    ps, st, dev, _, _, pmax = _run_p16(opt, "bf16_sr", sizes, ["bf16", "f16"], oracle.P_BF16, True, 3, hp)
+    _check(ps, st, dev, "bf16_sr", opt, oracle.P_BF16, 3, pmax)
+
+
 @pytest.mark.parametrize("pdt", [oracle.P_BF16, oracle.P_F16])
 def test_p16_ademamix_bf16_rn(pdt):
     sizes = [777, 32768 * 2 + 5]
