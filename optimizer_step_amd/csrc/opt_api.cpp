@@ -178,6 +178,11 @@ int build_qwords(const float *qs, const float *qu, std::vector<uint32_t> &words,
     words.resize(512 + S.entries.size() + U.entries.size());
     memcpy(words.data(), qs, 1024);
     memcpy(words.data() + 256, qu, 1024);
+    // The unsigned table's values read back as v, which the kernels keep at
+    // +0 or above (its code lookup and block absmax take the bit pattern with
+    // no sign mask).  A -0 first entry reads back as +0, which codes, scales
+    // and steps exactly as -0 does.
+    if (words[256] == 0x80000000u) words[256] = 0u;
     std::copy(S.entries.begin(), S.entries.end(), words.begin() + 512);
     std::copy(U.entries.begin(), U.entries.end(), words.begin() + 512 + S.entries.size());
     ps = S.P;

@@ -59,7 +59,7 @@ __device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint
     // below the bits of 2^-100 - 1
     uint32_t t = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t = min(t, (fbits(x[i]) & 0x7FFFFFFFu) - 1u);
+    for (int i = 0; i < 4; ++i) t = min(t, (SIGNED ? fbits(x[i]) & 0x7FFFFFFFu : fbits(x[i])) - 1u);
     if (div_by_ok(A) && !__any(t < 0x0D7FFFFFu)) {
         const float y = recip_rn(A);
         uint32_t h[4];
@@ -78,12 +78,16 @@ __device__ __forceinline__ uint32_t quant4(const float x[4], float A, const uint
 
 // The block absmax from this lane's four values: max |x| as unsigned bit
 // patterns across the wave, so NaN poisons it.  Values of lanes past the end
-// of a short block are passed as 0.
+// of a short block are passed as 0.  NONNEG: the values are +0 or positive
+// (v) or NaN, so their bit patterns need no sign mask (a NaN with its sign
+// bit set still exceeds every number, and the absmax reads as NaN either
+// way).
+template <bool NONNEG = false>
 __device__ __forceinline__ float block_absmax(const float x[4])
 {
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+    for (int i = 0; i < 4; ++i) m = max(m, NONNEG ? fbits(x[i]) : fbits(x[i]) & 0x7FFFFFFFu);
     return bitsf(wave_max_u32(m));
 }
 
@@ -426,7 +430,7 @@ __device__ __forceinline__ void q8_finish(const StepArgs &a, const Scalars &s, c
     for (int i = 0; i < 4; ++i) {
         if (i >= nmine) mo[i] = vo[i] = m2o[i] = 0.0f;   // past the end of a short block
     }
-    const float Am = block_absmax(mo), Av = block_absmax(vo);
+    const float Am = block_absmax(mo), Av = block_absmax<true>(vo);
     const uint32_t om = blk_encode4<SF, 0>(lds, a, mo, Am, rm);
     const uint32_t ov = blk_encode4<SF, 1>(lds, a, vo, Av, rv);
     uint32_t om2 = 0;

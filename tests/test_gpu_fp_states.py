@@ -236,6 +236,29 @@ def test_q8_signed_zero_moments(opt):
     states_bit_identical(case, dev, st)
 
 
+def test_q8_unsigned_codebook_starting_at_negative_zero():
+    """An unsigned codebook whose first entry is -0.0: with skip_zeros, a zero
+    gradient codes the old v again, and the oracle reads code 0 back as -0.
+    The library's table reads it as +0 (its lookup takes v's bits with no
+    sign mask); codes, absmax, p and every state word stay the oracle's."""
+    def g_of(t, k, n):
+        g = synth.grads(n, t, k, std=1e-2)
+        rng = np.random.default_rng([31, t, k])
+        g[rng.random(n) < 0.4] = np.float32(0.0)
+        g[::97] = np.float32(3.0)                      # large values: small v code 0 elsewhere
+        return g.astype(np.float32)
+    hp = dict(_hp("adamw"), skip_zeros=True)
+    case = Case("adamw", "q8", [4096, 777], False, 4, hp, grad_override=g_of)
+    qu = synth.codebook_unsigned().copy()
+    assert qu[0] == 0.0
+    qu[0] = np.float32(-0.0)
+    case.qu = qu
+    ps, st, _ = case.run_oracle()
+    dev, _ = case.run_gpu()
+    compare(case, dev, ps, st)
+    states_bit_identical(case, dev, st)
+
+
 @pytest.mark.parametrize("fmt", FP_FMTS + ["q8"])
 def test_nan_and_tiny_gradients(fmt):
     """A NaN gradient poisons its block's absmax (the block then reads back as
