@@ -29,6 +29,12 @@
  * 8-bit results are bit-reproducible.  The update uses these unrounded fp32
  * moments; rounding or quantization happens only when they are stored.
  * Bias corrections c = 1 - beta^t are formed in binary64 and rounded once.
+ * The direction u feeds the parameter alone.  For an fp32 parameter it is
+ * formed with the hardware reciprocal and square root (a few ulp from the
+ * correctly rounded recipe; the recipe itself for a tiny v_hat).  A 16-bit
+ * parameter stores the word the correctly rounded recipe's value rounds to:
+ * the kernels use the fast direction only where its error bound proves that
+ * word (opt_debug_direction exposes both directions and the bound).
  *
  * Calls and memory.  Every call is asynchronous on `stream` (a hipStream_t
  * passed as void*; NULL is the null stream).  All tensors, states and the
