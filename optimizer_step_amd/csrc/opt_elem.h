@@ -138,9 +138,8 @@ __device__ __forceinline__ bool p16_same(float pf, float step, float bu, float l
 // fast direction where p16_same shows that the stored word is the exact
 // recipe's, else (about one element in 2^14 for BF16, 2^11 for FP16, and all
 // of them for eps < 0 or |lam| > 2^20, which the bound does not cover) the
-// exact recipe.  The
-// wave skips the exact pass when no lane needs it; each element's result
-// depends on its own inputs alone.
+// exact recipe.  The wave skips the exact pass when no lane needs it; each
+// element's result depends on its own inputs alone.
 template <int OPT, int PD, bool GS>
 __device__ __forceinline__ void moments16(const Scalars &s, const StepArgs &a, const float p[4], const float g[4],
                                           const float m[4], const float v[4], const float m2[4], float lam, bool sr,
