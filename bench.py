@@ -330,6 +330,17 @@ def _oracle_steps(k, budget_s, n=1 << 24):
     return t, done, time.perf_counter() - t0
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle on the host: one process per core of this process's CPU
     share (at most 16), each on its own 2^24-element slice, then one process
@@ -348,7 +359,7 @@ def cpu_baseline(budget_s=12.0):
             "sample": f"AdamW (fp32 p/m/v, bf16 g) on 2^24-element slices of the Llama-7B-shaped list's "
                       f"synthetic inputs, C oracle: {workers} processes x ~{budget_s:.0f} s "
                       f"({sum(r[0] for r in res)} steps); one process alone: {steps} steps in {dt:.1f} s",
-            "bytes_per_element": 26, "GBps": rate * 26,
+            "bytes_per_element": 26, "GBps": rate * 26, "cpu_model": _cpu_model(),
             "single_core": {"value": single, "unit": "Gelem/s", "cores": 1, "GBps": single * 26}}
 
 
@@ -366,8 +377,19 @@ def calibrate(torch, osa, n=1 << 30, reps=3):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
+    # the runtime's device-to-device copy of the same buffer, beside it
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms_d2d = a.elapsed_time(b) / reps
     return {"kernel": "debug_stream_kernel (1 read, 1 write)", "bytes_read": 4 * n, "bytes_written": 4 * n,
-            "ms": ms, "GBps": 8 * n / ms / 1e6}
+            "ms": ms, "GBps": 8 * n / ms / 1e6,
+            "d2d_copy": {"how": "torch copy_ of the same fp32 buffer (device to device)", "ms": ms_d2d,
+                         "GBps": 8 * n / ms_d2d / 1e6}}
 
 
 # ---------------------------------------------------------------------------
@@ -726,7 +748,8 @@ def main():
         share = head_row.share if synth.WORKLOADS[name]["sizes"] == synth.WORKLOADS[head]["sizes"] else None
         rows.append(Row(name, torch, osa, synth, share=share))
     calib = calibrate(torch, osa)
-    print(f"[bench] calibration copy: {calib['GBps']:.0f} GB/s; {args.rounds} interleaved rounds over "
+    print(f"[bench] calibration copy: {calib['GBps']:.0f} GB/s (runtime D2D copy {calib['d2d_copy']['GBps']:.0f}); "
+          f"{args.rounds} interleaved rounds over "
           f"{len(rows)} rows", file=sys.stderr, flush=True)
     protocol = interleaved_rounds(rows, args.rounds, torch) if args.rounds > 0 else []
     for r in protocol:
