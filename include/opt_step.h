@@ -402,6 +402,13 @@ int opt_debug_stream(const float *const *src, int32_t nsrc, float *const *dst, i
  * do not depend on either.  OPT_EINVAL for other values. */
 int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu);
 
+/* The per-call scalars the host forms for a step with hyper-parameters hp
+ * (host array out[10]): 1-beta1, 1-beta2, 1-beta3, c1 = 1-beta1^t',
+ * c2 = 1-beta2^t' (binary64, rounded once; t' counts from the last state
+ * reset), RN(1/c1), RN(1/c2), 1-lr*wd, lr, and the gradient scale 1 (the
+ * kernels read a given scale from device memory). */
+int opt_debug_scalars(const opt_hparams *hp, float *out);
+
 /* Cap on the workgroups each compute unit holds at once for the element-wise
  * and one-state step kernels, for all later calls in this process: -1 (the
  * default) lets each kernel configuration take its own measured choice, 0

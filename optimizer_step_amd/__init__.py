@@ -93,6 +93,7 @@ def lib():
             "opt_debug_div_by": ([vp, vp, vp, i64], i32),
             "opt_debug_set_launch": ([i64, i32], i32),
             "opt_debug_set_wg_cap": ([i32], i32),
+            "opt_debug_scalars": ([H, vp], i32),
             "opt_debug_stream": ([vp, i32, vp, i32, i64, vp], i32),
             "opt_grad_norm": ([ctypes.POINTER(OptGrad), i64, vp, ctypes.c_float, i32, vp, vp], i32),
             "opt_debug_mini": ([i32, ctypes.c_float, vp, vp, vp, vp, i64, vp], i32),
@@ -444,6 +445,14 @@ def opt_debug_mini_host(elem, A, x, r=None):
 
 def opt_debug_set_launch(chunk, wgs_per_cu):
     return _check(lib().opt_debug_set_launch(int(chunk), int(wgs_per_cu)))
+
+
+def opt_debug_scalars(hp):
+    """The per-call scalars the host forms for hp (numpy float32[10])."""
+    import numpy as np
+    out = np.zeros(10, dtype=np.float32)
+    _check(lib().opt_debug_scalars(ctypes.byref(hp), out.ctypes.data))
+    return out
 
 
 def opt_debug_set_wg_cap(cap):

@@ -1187,6 +1187,16 @@ int opt_debug_set_launch(int64_t chunk, int32_t wgs_per_cu)
     return OPT_OK;
 }
 
+int opt_debug_scalars(const opt_hparams *hp, float *out)
+{
+    if (!hp || !out) return fail(OPT_EINVAL, "hp or out is NULL");
+    const StepArgs a = base_args(hp, 32768);
+    const Scalars &c = a.sc;
+    const float v[10] = {c.om1, c.om2, c.om3, c.c1, c.c2, c.rc1, c.rc2, c.d, c.lam, c.gs};
+    memcpy(out, v, sizeof v);
+    return OPT_OK;
+}
+
 int opt_debug_set_wg_cap(int32_t cap)
 {
     if (cap != -1 && (cap < 0 || cap == 1 || cap > 32)) return fail(OPT_EINVAL, "cap must be -1, 0 or in [2, 32]");
