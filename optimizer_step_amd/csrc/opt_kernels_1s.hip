@@ -5,9 +5,8 @@
 //
 // Same layout as the two-state element-wise step: one workgroup per tile of
 // kEwTile1 elements (the tile scheduling of opt_elem.h); lanes own groups of
-// four consecutive elements, kEwGroups groups loaded before the scalars are
-// formed and before any arithmetic.  Per element, in binary32
-// with no contraction:
+// four consecutive elements, kEwGroups groups loaded before any arithmetic.
+// Per element, in binary32 with no contraction:
 //   g' = g*scale (+ wd*p for the coupled-L2 three when wd != 0)
 //   momentum  m' = g' on the state's first step, else b1*m + g';  p' = p - lr*m'
 //   RMSprop   v' = b1*v + (1-b1)*g'^2;  p' = p - lr*(g'/(sqrt(v') + eps))

@@ -6,13 +6,14 @@
 // tensor (the tile scheduling of opt_elem.h).  Inside a tile every lane owns
 // kEwGroups groups of 4 consecutive elements, so fp32 arrays move as 128-bit
 // accesses and 16-bit ones as 64-bit accesses, every access instruction of a
-// wave64 fully coalesced; a full tile issues all its loads before the
-// per-call scalars are formed and before any arithmetic.  The moments are
-// formed exactly (fixed binary32 order); for fp32 parameters the direction
-// u, which only feeds p, uses the hardware reciprocal and square root
-// (measured on MI355X: +2 % on the 290-tensor AdamW step, +5-6 % with BF16
-// states), and 16-bit parameters take the exact recipe.  HBM-bound: every
-// byte is read or written once per step and no intermediate leaves registers.
+// wave64 fully coalesced; a full tile issues all its loads before any
+// arithmetic (the per-call scalars come formed in the kernel arguments).  The
+// moments are formed exactly (fixed binary32 order); the direction u, which
+// only feeds p, uses the hardware reciprocal and square root (measured on
+// MI355X: +2 % on the 290-tensor AdamW step, +5-6 % with BF16 states), for a
+// 16-bit parameter only where its error bound proves the stored word
+// (moments16 in opt_elem.h).  HBM-bound: every byte is read or written once
+// per step and no intermediate leaves registers.
 #include "opt_elem.h"
 
 namespace optstep {
