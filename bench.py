@@ -627,7 +627,8 @@ def summarize_rows_trace(trace_dir, cmd):
     with open(out, "w") as f:
         f.write("rocprofv3 kernel statistics over every bench row (template arguments: optimizer\n"
                 "0 AdamW 1 AdEMAMix 2 momentum 5 Lion; gradient 0 fp32 1 bf16 2 fp16; state format 0 fp32\n"
-                "1 BF16-RN 2 BF16-SR 3 8-bit 4 FP8-RN 5 FP8-SR 6 FP4-RN 7 FP4-SR; parameter 0 fp32).\n"
+                "1 BF16-RN 2 BF16-SR 3 8-bit 4 FP8-RN 5 FP8-SR 6 FP4-RN 7 FP4-SR; parameter 0 fp32 1 bf16\n"
+                "2 fp16; true: a call with no gradient scale, skip_zeros or state reset).\n"
                 f"command: {cmd}\n\n")
         f.write(f"{'kernel':70s} {'calls':>6s} {'avg ms':>9s} {'min ms':>9s} {'max ms':>9s}\n")
         for r in rows:
