@@ -7,46 +7,35 @@
 
 namespace optstep {
 
-#ifndef OPT_Q8_THREADS
-#define OPT_Q8_THREADS 512
-#endif
-// Workgroup size of the blockwise kernel (one LDS copy of the 8-bit tables
-// per workgroup).
-constexpr int kQ8Threads = OPT_Q8_THREADS;
-constexpr int kQ8Waves = kQ8Threads / 64;
+// Workgroup shape and tile of the blockwise kernel, per state format.  A
+// wave takes one 256-element block at a time; a tile's blocks go to the
+// workgroup's waves in turn.  Measured on MI355X, AdamW over 2^30 elements,
+// paired runs in one process:
+//  * 8-bit: 512 threads over 32 K-element tiles (one LDS copy of the
+//    lookup tables per workgroup, up to 60 KB): 16 K tiles 2.84, 8 K 2.91,
+//    4 K 3.14, 2 K 4.06 ms against 2.80; one-shot tiles of 1-4 K elements
+//    (a workgroup per tile, one or two blocks per wave) 2.84-4.29 ms
+//    against 2.78, the table copy costing more than the tile's traffic.
+//  * FP8 and FP4 nearest: 128 threads over 1 K-element tiles, each wave
+//    loading its second block while it finishes its first: FP8 2.47 and
+//    FP4 2.08 ms against 2.67 and 2.25 with the 512-thread 8 K tiles;
+//    256 threads over 2 K tiles 2.51 / 2.13, 64 over 512 2.53 / 2.17.
+//    AdEMAMix over 2^28 elements is unchanged (0.797 against 0.793 ms).
+//  * FP8 and FP4 stochastic: 512 threads over 8 K tiles, no prefetch; the
+//    shapes above lose 9-17 % there.
+template <int SF>
+struct Q8Shape {
+    static constexpr bool kSmall = SF == kFP8RN || SF == kFP4RN;
+    static constexpr int kThreads = kSmall ? 128 : 512;
+    static constexpr int kWaves = kThreads / 64;
+    static constexpr int64_t kTile = SF == kQ8 ? 32768 : kSmall ? 1024 : 8192;
+    static constexpr bool kPrefetch = kSmall;   // a wave loads its next block before finishing this one
+    static_assert(kTile % (kWaves * kQBlock) == 0, "blockwise tile");
+};
 
-#ifndef OPT_Q8_TILE
-#define OPT_Q8_TILE 32768
-#endif
-// Elements per tile of the blockwise step (a power of two, a multiple of the
-// 8 x 256 elements one pass of the workgroup's waves covers).
-constexpr int64_t kQ8Tile = OPT_Q8_TILE;
-static_assert(kQ8Tile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
-
-#ifndef OPT_MINI_TILE
-#define OPT_MINI_TILE 8192
-#endif
-// Elements per tile of the FP8/FP4 formats, which load no lookup table: four
-// passes of the workgroup's waves.  Measured on MI355X, FP8 nearest: 8 K and
-// 4 K tiles 2.70 ms, 16 K 2.83 ms, 32 K 2.80 ms, 2 K 3.09 ms per 2^30
-// elements; the 8-bit format, whose tables every workgroup copies into LDS,
-// keeps 32 K (16 K 2.84, 8 K 2.91, 4 K 3.14, 2 K 4.06 ms against 2.80).
-constexpr int64_t kMiniTile = OPT_MINI_TILE;
-static_assert(kMiniTile % (kQ8Waves * kQBlock) == 0, "blockwise tile");
-
-#ifndef OPT_Q8_PREFETCH
-#define OPT_Q8_PREFETCH (-1)
-#endif
-// Whether a wave loads its next block before finishing the current one
-// (OPT_Q8_PREFETCH: -1 per format, 0 never, 1 always).
-constexpr bool q8_prefetch(int sf) { return sf == kFP8RN || sf == kFP4RN; }
-
-#ifndef OPT_Q8_WAVES
-#define OPT_Q8_WAVES 7
-#endif
 // Waves per SIMD the AdamW instantiations are held to (their registers fit
 // 7 without spilling; AdEMAMix's third state does not, and is left free).
-constexpr int kQ8WavesAdamW = OPT_Q8_WAVES;
+constexpr int kQ8WavesAdamW = 7;
 
 // The tiles of one workgroup: one 256-element block per wave at a time.
 template <int OPT, int GD, int SF, int PD, bool PLAIN>
@@ -63,7 +52,7 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
         const uint32_t nfull = (uint32_t)(len / kQBlock);
         const QChunk C = q8_chunk<GD, SF, PD>(T, e0);
         uint32_t b = wave;
-        if (OPT_Q8_PREFETCH < 0 ? q8_prefetch(SF) : OPT_Q8_PREFETCH != 0) {
+        if (Q8Shape<SF>::kPrefetch) {
             // the wave's next block is loaded while it finishes this one
             QIn xa;
             if (b < nfull) {
@@ -72,7 +61,7 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
                 load_prio_lo();
             }
             while (b < nfull) {
-                const uint32_t bn = b + kQ8Waves;
+                const uint32_t bn = b + Q8Shape<SF>::kWaves;
                 const bool more = bn < nfull;
                 QIn xb;
                 if (more) {
@@ -85,7 +74,7 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
                 if (more) xa = xb;
             }
         } else {
-            for (; b < nfull; b += kQ8Waves) {
+            for (; b < nfull; b += Q8Shape<SF>::kWaves) {
                 QIn x0;
                 load_prio_hi();
                 q8_load<OPT, GD, SF, PD, true>(a, C, b, 4, lane, x0);
@@ -105,7 +94,7 @@ __device__ __forceinline__ void q8_tiles(const DevTensor *__restrict__ tens, con
 // Blockwise states (8-bit codebook, FP8, FP4): one workgroup per tile (the
 // tile scheduling of opt_elem.h).
 template <int OPT, int GD, int SF, int PD, bool PLAIN>
-__global__ __launch_bounds__(kQ8Threads)
+__global__ __launch_bounds__(Q8Shape<SF>::kThreads)
 __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void step_q8_kernel(const DevTensor *__restrict__ tens,
                                                              const int32_t *__restrict__ ctab,
                                                              const uint32_t *__restrict__ qwords,
@@ -116,8 +105,8 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (SF == kQ8)
-        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += kQ8Threads) lds[i] = qwords[i];
-    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, kQ8Threads);
+        for (uint32_t i = threadIdx.x; i < a.q.nwords; i += Q8Shape<SF>::kThreads) lds[i] = qwords[i];
+    if (mini_fmt(SF)) fill_mini_tab<SF>(mtab_s, threadIdx.x, Q8Shape<SF>::kThreads);
     const float *mtab = mini_fmt(SF) ? mtab_s : nullptr;
     __syncthreads();
     const Scalars s = call_scalars(a);
@@ -127,14 +116,13 @@ __attribute__((amdgpu_waves_per_eu(OPT == kAdamW ? kQ8WavesAdamW : 1))) void ste
 // ---------------------------------------------------------------------------
 // launchers (called by opt_api.cpp)
 
-// The blockwise step over tiles of `tile` elements (opt_elem.h).
-template <class K>
-static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st,
-                                  int64_t tile = kQ8Tile)
+// The blockwise step of state format SF over its tiles (opt_elem.h).
+template <int SF, class K>
+static hipError_t launch_q8_tiles(K kernel, size_t lds, const LaunchGeom &lg, StepArgs a, hipStream_t st)
 {
-    set_tiles(a, tile);
-    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(kQ8Threads), lds, st, a.tens, a.chunk_tensor,
-                       a.q.words, a);
+    set_tiles(a, Q8Shape<SF>::kTile);
+    hipLaunchKernelGGL(kernel, dim3(tile_grid(a, lg)), dim3(Q8Shape<SF>::kThreads), lds, st, a.tens,
+                       a.chunk_tensor, a.q.words, a);
     return hipGetLastError();
 }
 
@@ -144,11 +132,11 @@ template <int OPT, int GD, int PD, bool PLAIN>
 static hipError_t launch_q8_pl(int fmt, const StepArgs &a, const LaunchGeom &lg, size_t lds, hipStream_t st)
 {
     switch (fmt) {
-    case kQ8: return launch_q8_tiles(step_q8_kernel<OPT, GD, kQ8, PD, PLAIN>, lds, lg, a, st);
-    case kFP8RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8RN, PD, PLAIN>, 0, lg, a, st, kMiniTile);
-    case kFP8SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP8SR, PD, PLAIN>, 0, lg, a, st, kMiniTile);
-    case kFP4RN: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4RN, PD, PLAIN>, 0, lg, a, st, kMiniTile);
-    case kFP4SR: return launch_q8_tiles(step_q8_kernel<OPT, GD, kFP4SR, PD, PLAIN>, 0, lg, a, st, kMiniTile);
+    case kQ8: return launch_q8_tiles<kQ8>(step_q8_kernel<OPT, GD, kQ8, PD, PLAIN>, lds, lg, a, st);
+    case kFP8RN: return launch_q8_tiles<kFP8RN>(step_q8_kernel<OPT, GD, kFP8RN, PD, PLAIN>, 0, lg, a, st);
+    case kFP8SR: return launch_q8_tiles<kFP8SR>(step_q8_kernel<OPT, GD, kFP8SR, PD, PLAIN>, 0, lg, a, st);
+    case kFP4RN: return launch_q8_tiles<kFP4RN>(step_q8_kernel<OPT, GD, kFP4RN, PD, PLAIN>, 0, lg, a, st);
+    case kFP4SR: return launch_q8_tiles<kFP4SR>(step_q8_kernel<OPT, GD, kFP4SR, PD, PLAIN>, 0, lg, a, st);
     default: return hipErrorInvalidValue;
     }
 }
