@@ -13,23 +13,27 @@ namespace optstep {
 // paired runs in one process:
 //  * 8-bit: 512 threads over 32 K-element tiles (one LDS copy of the
 //    lookup tables per workgroup, up to 60 KB): 16 K tiles 2.84, 8 K 2.91,
-//    4 K 3.14, 2 K 4.06 ms against 2.80; one-shot tiles of 1-4 K elements
-//    (a workgroup per tile, one or two blocks per wave) 2.84-4.29 ms
-//    against 2.78, the table copy costing more than the tile's traffic.
+//    4 K 3.14, 2 K 4.06 ms against 2.80.  Smaller one-shot shapes lose
+//    even with the table cut to 5 KB (a timing copy whose codes were not
+//    the format's): 128 threads over 1 K 3.03, 256 over 2 K 2.76, 512 over
+//    4 K 2.74 ms against 2.77.
 //  * FP8 and FP4 nearest: 128 threads over 1 K-element tiles, each wave
 //    loading its second block while it finishes its first: FP8 2.47 and
-//    FP4 2.08 ms against 2.67 and 2.25 with the 512-thread 8 K tiles;
+//    FP4 2.08 ms against 2.67 and 2.25 with 512 threads over 8 K tiles;
 //    256 threads over 2 K tiles 2.51 / 2.13, 64 over 512 2.53 / 2.17.
-//    AdEMAMix over 2^28 elements is unchanged (0.797 against 0.793 ms).
-//  * FP8 and FP4 stochastic: 512 threads over 8 K tiles, no prefetch; the
-//    shapes above lose 9-17 % there.
+//  * FP8 stochastic: 128 threads over 2 K-element tiles, four blocks per
+//    wave in turn: 2.60-2.66 ms against 2.75 with 512 threads over 8 K;
+//    256 over 4 K 2.66, 128 over 1 K 2.73, the prefetching shape 3.04.
+//  * FP4 stochastic: 512 threads over 8 K-element tiles; the shapes above
+//    land within 2 % either side of it or lose up to 17 %.
+//  AdEMAMix over 2^28 elements moves within 1 % with any of these shapes.
 template <int SF>
 struct Q8Shape {
-    static constexpr bool kSmall = SF == kFP8RN || SF == kFP4RN;
+    static constexpr bool kPrefetch = SF == kFP8RN || SF == kFP4RN;   // a wave loads its next block before finishing this one
+    static constexpr bool kSmall = kPrefetch || SF == kFP8SR;
     static constexpr int kThreads = kSmall ? 128 : 512;
     static constexpr int kWaves = kThreads / 64;
-    static constexpr int64_t kTile = SF == kQ8 ? 32768 : kSmall ? 1024 : 8192;
-    static constexpr bool kPrefetch = kSmall;   // a wave loads its next block before finishing this one
+    static constexpr int64_t kTile = SF == kQ8 ? 32768 : !kSmall ? 8192 : kPrefetch ? 1024 : 2048;
     static_assert(kTile % (kWaves * kQBlock) == 0, "blockwise tile");
 };
 
