@@ -2,9 +2,10 @@
 // with fp32 or BF16 states (AdamW, AdEMAMix), for fp32, BF16 or FP16
 // parameters and gradients.
 //
-// One 256-thread workgroup per tile of kEwTile consecutive elements of one
-// tensor (the tile scheduling of opt_elem.h).  Inside a tile every lane owns
-// kEwGroups groups of 4 consecutive elements, so fp32 arrays move as 128-bit
+// One workgroup per tile of 1024 consecutive elements of one tensor (the
+// tile scheduling of opt_elem.h): 256 threads, or 128 for 16-bit parameters
+// with BF16 states (EwShape below).  Inside a tile every lane owns one or two
+// groups of 4 consecutive elements, so fp32 arrays move as 128-bit
 // accesses and 16-bit ones as 64-bit accesses, every access instruction of a
 // wave64 fully coalesced; a full tile issues all its loads before any
 // arithmetic (the per-call scalars come formed in the kernel arguments).  The
@@ -162,13 +163,29 @@ __device__ __forceinline__ void ew_single(const StepArgs &a, const Scalars &s, c
 #ifndef OPT_EW_THREADS
 #define OPT_EW_THREADS 256
 #endif
-constexpr int kEwThreads = OPT_EW_THREADS;
-constexpr int64_t kEwTile = (int64_t)kEwThreads * kEwGroups * 4;
+
+// Workgroup shape of the element-wise step: threads, and groups of four
+// elements per lane, all loaded before any arithmetic.  BF16 or FP16
+// parameters with BF16 states take 128 threads with two groups each (the
+// same 1024-element tile).  Measured on MI355X, paired, 2^30 elements,
+// BF16 p with BF16-SR states 2.59 ms against 3.05 (256 x 2: 2.60, 64 x 2:
+// 2.56, 256 x 4: 2.89), with BF16 nearest states 2.36 against 2.82,
+// AdEMAMix (2^28) 0.830 against 0.884; BF16 p with fp32 states loses 3-9 %
+// with any of these, and fp32 p gains nothing (BF16 nearest states 1 %,
+// BF16-SR -2 to -4 %).
+template <int SF, int PD>
+struct EwShape {
+    static constexpr bool kPair = PD != kP32 && SF != kF32;
+    static constexpr int kThreads = kPair ? 128 : OPT_EW_THREADS;
+    static constexpr int kGroups = kPair ? 2 : kEwGroups;
+    static constexpr int64_t kTile = (int64_t)kThreads * kGroups * 4;
+};
 
 template <int OPT, int GD, int SF, int PD, bool PLAIN>
-__global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
+__global__ __launch_bounds__((EwShape<SF, PD>::kThreads)) OPT_EW_ATTR void step_ew_kernel(const DevTensor *__restrict__ tens,
                                                                        const int32_t *__restrict__ ctab, StepArgs a)
 {
+    typedef EwShape<SF, PD> Sh;
     const Scalars s = call_scalars(a);
     const bool fresh = a.fresh != 0;
     for (int64_t w = blockIdx.x; w < a.ntiles; w += gridDim.x) {
@@ -176,21 +193,21 @@ __global__ __launch_bounds__(kEwThreads) OPT_EW_ATTR void step_ew_kernel(const D
         int64_t e0, len;
         if (!locate_tile(tens, ctab, a, w, T, e0, len)) continue;
         const TileRef R = tile_ref<OPT, GD, SF, PD>(T, e0);
-        if (len == kEwTile) {
-            Group x[kEwGroups];
+        if (len == Sh::kTile) {
+            Group x[Sh::kGroups];
             load_prio_hi(SF != kBF16RN);
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u)
-                ew_load<OPT, GD, SF, PD>(R, 4u * (threadIdx.x + u * kEwThreads), fresh, x[u]);
+            for (int u = 0; u < Sh::kGroups; ++u)
+                ew_load<OPT, GD, SF, PD>(R, 4u * (threadIdx.x + u * Sh::kThreads), fresh, x[u]);
             load_prio_lo(SF != kBF16RN);
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
 #pragma unroll
-            for (int u = 0; u < kEwGroups; ++u)
-                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, R, 4u * (threadIdx.x + u * kEwThreads), lam, x[u]);
+            for (int u = 0; u < Sh::kGroups; ++u)
+                ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, R, 4u * (threadIdx.x + u * Sh::kThreads), lam, x[u]);
         } else {   // a tensor's last, short tile
             const float lam = a.unorm ? lam_for(a, T.k) : s.lam;
             const uint32_t ngroups = (uint32_t)(len >> 2);
-            for (uint32_t i = threadIdx.x; i < ngroups; i += kEwThreads) {
+            for (uint32_t i = threadIdx.x; i < ngroups; i += Sh::kThreads) {
                 Group x0;
                 ew_load<OPT, GD, SF, PD>(R, 4u * i, fresh, x0);
                 ew_finish<OPT, GD, SF, PD, PLAIN>(a, s, R, 4u * i, lam, x0);
@@ -230,13 +247,13 @@ static hipError_t launch_ew_p(int fmt, const StepArgs &a, const LaunchGeom &lg, 
 {
     switch (fmt) {
     case kF32:
-        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kF32, PD, PLAIN>, kEwTile,
+        return launch_tiles<EwShape<kF32, PD>::kThreads>(step_ew_kernel<OPT, GD, kF32, PD, PLAIN>, EwShape<kF32, PD>::kTile,
                                         cap_lds(lg, ew_wg_cap<OPT, GD, kF32, PD, PLAIN>(a)), lg, a, st);
     case kBF16RN:
-        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, kEwTile,
+        return launch_tiles<EwShape<kBF16RN, PD>::kThreads>(step_ew_kernel<OPT, GD, kBF16RN, PD, PLAIN>, EwShape<kBF16RN, PD>::kTile,
                                         cap_lds(lg, ew_wg_cap<OPT, GD, kBF16RN, PD, PLAIN>(a)), lg, a, st);
     case kBF16SR:
-        return launch_tiles<kEwThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, kEwTile,
+        return launch_tiles<EwShape<kBF16SR, PD>::kThreads>(step_ew_kernel<OPT, GD, kBF16SR, PD, PLAIN>, EwShape<kBF16SR, PD>::kTile,
                                         cap_lds(lg, ew_wg_cap<OPT, GD, kBF16SR, PD, PLAIN>(a)), lg, a, st);
     default: return hipErrorInvalidValue;
     }
