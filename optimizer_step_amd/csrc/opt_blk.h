@@ -339,12 +339,14 @@ __device__ __forceinline__ uint32_t mini_pack4(const float x[4], float A, const 
 {
     if (!finite_f(A)) return 0u;
     const int nsc = mini_enc_shift<F>(A);
-    // E4M3 stochastic, E2M1 both ways, unsigned E2M2 stochastic (through
-    // E5M2).  Paired on MI355X, 2^30 elements: FP8-SR 2.89 -> 2.72 ms, FP4-SR
-    // 2.65 -> 2.51 (E2M1) -> 2.39 (E2M2 too), FP4-RN 2.32 -> 2.29; the
-    // nearest FP8 and E2M2 roundings, a few integer instructions, lost 0.4-1.2 %
-    // with the conversions and keep them.
-    constexpr bool hw = (F::kSign == 0x80u && SR) || F::kMB == 1 || (F::kSign == 0u && SR);
+    // E4M3 and E2M1 both ways, unsigned E2M2 stochastic (through E5M2).
+    // Paired on MI355X, 2^30 elements: FP8-SR 2.89 -> 2.72 ms, FP4-SR 2.65 ->
+    // 2.51 (E2M1) -> 2.39 (E2M2 too), FP4-RN 2.32 -> 2.29, and, since the
+    // nearest kernels run VALU-bound in their 1 K-element tiles, FP8-RN 2.49
+    // -> 2.39.  Nearest E2M2 keeps its few integer instructions (the
+    // conversion costs FP4-RN 1.4 %).  Decoding by the matching conversions
+    // instead of the LDS grid table measured 0 to -7 %.
+    constexpr bool hw = F::kSign == 0x80u || F::kMB == 1 || (F::kSign == 0u && SR);
     if (hw && nsc >= (F::kSign == 0u ? -113 : -127) && nsc <= 126) return mini_pack4_hw<F, SR>(x, nsc, r);
     constexpr int W = (F::kSign == 0x80u) ? 8 : 4;
     uint32_t out = 0;
