@@ -1,8 +1,9 @@
 // opt_kernels_q8.hip -- gfx950 kernel of the blockwise-state step (8-bit
 // codebook, FP8 and FP4 states) for AdamW and AdEMAMix, fp32, BF16 or FP16
 // parameters and gradients, and the step's launcher (the element-wise formats
-// go to opt_kernels_ew.hip).  HBM-bound, with the codecs' VALU work close
-// behind: each byte is read or written once per step.
+// go to opt_kernels_ew.hip).  Each byte is read or written once per step;
+// what bounds each format (its traffic pattern, or the codec's and the
+// random generator's VALU work) decides its workgroup shape below.
 #include "opt_blk.h"
 
 namespace optstep {
