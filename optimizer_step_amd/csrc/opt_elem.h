@@ -372,8 +372,8 @@ __device__ __forceinline__ bool locate_tile(const DevTensor *__restrict__ tens, 
 // step: the step kernels have a variant that spends no instruction on any.
 __host__ inline bool plain_call(const StepArgs &a) { return a.grad_scale == nullptr && !a.skip_zeros && !a.fresh; }
 
-// Occupancy cap.  A 256-thread tile kernel is held to `cap` resident
-// workgroups per compute unit (cap waves per SIMD) by reserving, at launch,
+// Occupancy cap.  A tile kernel is held to `cap` resident workgroups per
+// compute unit (cap waves per SIMD for 256 threads) by reserving, at launch,
 // LDS it never touches: 1 KiB under a cap-th of the 160 KiB each gfx950
 // compute unit holds, which leaves room for the kernels' few bytes of static
 // LDS and keeps cap + 1 workgroups from fitting.  Measured on MI355X, some
