@@ -230,12 +230,14 @@ __global__ __launch_bounds__((EwShape<SF, PD>::kThreads)) OPT_EW_ATTR void step_
 // 3.82 / 3.73 / 3.84 ms.  AdEMAMix with fp32 states (2^28), caps 0 / 4 / 5 /
 // 6: 1.735 / 1.685 / 1.701 / 1.736 ms; AdamW with BF16 nearest states (2^30),
 // caps 0 / 5 / 6 / 7: 3.108 / 3.093 / 3.065 / 3.107 ms.  BF16 stochastic
-// states gain nothing from a cap (and lose up to 10 % at 4).
+// states gain nothing from a cap (and lose up to 10 % at 4).  AdamW with fp32
+// g and states, caps 0 / 3 / 4 / 5 / 6: 2^28 elements 1.282 / 1.324 / 1.259 /
+// 1.225 / 1.256 ms, 2^30 5.416 / 5.274 / 5.266 / 5.242 / 5.330 ms.
 template <int OPT, int GD, int SF, int PD, bool PLAIN>
 static int ew_wg_cap(const StepArgs &a)
 {
     if (OPT == kAdEMAMix) return SF == kF32 ? 4 : 0;
-    if (GD == kGradF32) return 0;
+    if (GD == kGradF32) return SF == kF32 && PD == kP32 ? 5 : 0;
     if (SF == kBF16RN) return PD == kP32 ? 6 : 0;
     if (SF != kF32) return 0;
     if (PD != kP32 || a.nchunks * a.chunk < ((int64_t)1 << 30)) return 5;
