@@ -165,11 +165,11 @@ template <int OPT, int GD>
 static hipError_t launch_1s_t(int fmt, const StepArgs &a, const LaunchGeom &lg, hipStream_t st)
 {
     switch (fmt) {
-    // fp32 state with 16-bit gradients: at most 5 resident workgroups per
-    // compute unit (measured on MI355X, 2^30 elements, BF16 g: momentum 3.19
-    // -> 3.09 ms, Lion 3.19 -> 3.08 ms)
+    // fp32 state: at most 5 resident workgroups per compute unit (measured on
+    // MI355X, 2^30 elements, BF16 g: momentum 3.19 -> 3.09 ms, Lion 3.19 ->
+    // 3.08 ms; fp32 g: momentum 3.635 -> 3.493 ms)
     case kF32:
-        return launch_tiles(step_1s_kernel<OPT, GD, kF32>, kEwTile1, cap_lds(lg, GD == kGradF32 ? 0 : 5), lg, a, st);
+        return launch_tiles(step_1s_kernel<OPT, GD, kF32>, kEwTile1, cap_lds(lg, 5), lg, a, st);
     case kBF16RN: return launch_tiles(step_1s_kernel<OPT, GD, kBF16RN>, kEwTile1, cap_lds(lg, 0), lg, a, st);
     case kBF16SR: return launch_tiles(step_1s_kernel<OPT, GD, kBF16SR>, kEwTile1, cap_lds(lg, 0), lg, a, st);
     default: return hipErrorInvalidValue;
