@@ -248,7 +248,10 @@ __device__ __forceinline__ V sld_at(const void *base, uint32_t off)
 // boxes: the 290-tensor AdamW step (fp32 p, m, v; BF16 g) 30.01 -> 29.29 ms
 // and 30.02 -> 29.31 ms with SC1 on its 16-byte stores; the same policy cost
 // 2.7 % on AdEMAMix (fp32 g) and 0.8-1.3 % on BF16-state and BF16-parameter
-// steps, so only that configuration takes it.  The buffer resource spans
+// steps, so only that configuration takes it.  Other policy bits on the same
+// buffer store, paired on that step (290-tensor list / 3 x 2^30 elements):
+// SC0|SC1 the same, NT|SC1 and NT|SC0|SC1 0.1-1 % slower, NT and NT|SC0 2-4 %,
+// no bits or SC0 alone 5-15 %.  The buffer resource spans
 // 2^32 - 1 bytes from the tile's base; every offset here is below a tile's
 // bytes.
 template <bool SC1, class V>
