@@ -28,7 +28,9 @@ __device__ __forceinline__ void gst(void *p, V v) { *(OPT_GLOBAL V *)p = v; }
 
 // Streaming accesses of the per-element arrays (p, g, states): each byte is
 // touched once per step, so they carry the non-temporal hint (measured on
-// MI355X: +2-4% step bandwidth over plain accesses).
+// MI355X: +2-4% step bandwidth over plain accesses).  Buffer loads with the
+// same hint, alone or with SC0/SC1, ran within 1 % of these on the headline
+// step; with SC1 and no hint they lost 8-13 %.
 #ifndef OPT_NT_LOAD
 #define OPT_NT_LOAD 1
 #endif
