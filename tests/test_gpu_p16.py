@@ -195,6 +195,33 @@ def test_p16_many_elements(pdt, p_sr):
     _check(ps, st, dev, "bf16_sr", "adamw", pdt, 3, pmax)
 
 
+@pytest.mark.parametrize("fmt", ["bf16_rn", "bf16_sr", "fp8_rn", "fp8_sr"])
+def test_p16_chunk_and_grid_do_not_change_results(fmt):
+    """16-bit parameters with BF16 or FP8 states under several host chunk
+    sizes and grids (one workgroup per tile, and persistent grids walking the
+    tiles): every word the same, and the first launch setting bit-exact
+    against the oracle.  The tiles of these kernels (two groups of four
+    elements per lane, or two blocks per wave) then start and end at other
+    places within each tensor."""
+    import optimizer_step_amd as osa
+    sizes = [300_001, 4097, 1000]
+    hp = dict(lr=1e-2, weight_decay=0.1)
+    runs = []
+    try:
+        for chunk, wgs in ((32768, 0), (1024, 1), (65536, 3), (4096, 64)):
+            osa.opt_debug_set_launch(chunk, wgs)
+            ps, st, dev, _, _, pmax = _run_p16("adamw", fmt, sizes, ["bf16", "f16", "bf16"], oracle.P_BF16, True, 2, hp)
+            if not runs:
+                _check(ps, st, dev, fmt, "adamw", oracle.P_BF16, 2, pmax)
+            runs.append([{k: to_host(v).view(np.uint8).copy() for k, v in d.items() if k != "g"} for d in dev])
+    finally:
+        osa.opt_debug_set_launch(32768, 0)
+    for r in runs[1:]:
+        for x, y in zip(runs[0], r):
+            for key in x:
+                assert np.array_equal(x[key], y[key]), key
+
+
 @pytest.mark.parametrize("eps", [0.0, -1e-3])
 @pytest.mark.parametrize("opt", ["adamw", "ademamix"])
 def test_p16_eps_edges(opt, eps):
