@@ -35,10 +35,11 @@ def _bits(host):
     return [{k: v.view(np.uint8).copy() for k, v in d.items()} for d in host]
 
 
-@pytest.mark.parametrize("fmt,clip", [("f32", None), ("f32", (1.0, 2)), ("bf16_sr", None)])
-def test_two_state_step_independent_of_cap(fmt, clip):
+@pytest.mark.parametrize("fmt,clip,grad_bf16", [("f32", None, True), ("f32", (1.0, 2), True), ("bf16_sr", None, True),
+                                               ("f32", None, False)])
+def test_two_state_step_independent_of_cap(fmt, clip, grad_bf16):
     import optimizer_step_amd as osa
-    case = Case("adamw", fmt, SIZES, True, 2, _hp(), clip=clip)
+    case = Case("adamw", fmt, SIZES, grad_bf16, 2, _hp(), clip=clip)
     try:
         osa.opt_debug_set_wg_cap(0)
         ref = _bits(Case.host(case.run_gpu()[0]))
@@ -57,13 +58,15 @@ def test_two_state_step_independent_of_cap(fmt, clip):
         osa.opt_debug_set_wg_cap(-1)
 
 
+@pytest.mark.parametrize("grad_bf16", [True, False])
 @pytest.mark.parametrize("name", ["momentum", "lion"])
-def test_one_state_step_independent_of_cap(name):
+def test_one_state_step_independent_of_cap(name, grad_bf16):
     import torch
     import optimizer_step_amd as osa
     hp = dict(lr=1e-2, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.05)
     ps = [synth.params(n, k, std=0.5) for k, n in enumerate(SIZES)]
-    gs = [[synth.bf16_words(synth.grads(n, t, k, std=1e-1)) for k, n in enumerate(SIZES)] for t in (1, 2)]
+    gs = [[(synth.bf16_words if grad_bf16 else np.asarray)(synth.grads(n, t, k, std=1e-1)) for k, n in enumerate(SIZES)]
+          for t in (1, 2)]
     ss = [np.zeros(n, np.float32) for n in SIZES]
     for t in (1, 2):
         for k in range(len(SIZES)):
